@@ -42,6 +42,7 @@ Parity pins for every function live in ``tests/test_oracle_*.py``.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -191,34 +192,49 @@ def window_blocks(L: int, n: int, G: int) -> list:
     return [b for b in range(nb) if (b + 1) * G > L - W]
 
 
+EXACT_SHIFT = 149   # every float32 in [0, 1] is an integer multiple of 2**-149
+
+
+def exact_units(x: float) -> int:
+    """A float32 value in [0, 1] as an exact integer count of 2**-149."""
+    f = Fraction(float(np.float32(x))) * (1 << EXACT_SHIFT)
+    assert f.denominator == 1
+    return int(f)
+
+
 def topp_request(scores: np.ndarray, L: int, n: int, G: int, p: float):
     """Top-p cut for one request.
 
     scores: float32 [nb].  Blocks are ordered by descending score, ties by lower
-    block index (reading: a stable sort).  The running sum is taken in float64,
-    sequentially, in that order, against p as a float32 value widened to float64.
-    The cut keeps the shortest prefix whose running sum reaches p (reading:
-    "reaches" is inclusive, >=).  With p >= 1, or if rounding keeps every running
-    sum below p, all blocks are kept.  The window blocks are added afterwards.
+    block index (reading: a stable sort).  The running sum of the sorted scores is
+    compared with p, both as float32 values, and the sum is taken exactly, with no
+    rounding (reading: the plain meaning of "the cumulative sum reaches p"; it also
+    makes the cut independent of summation order).  The cut keeps the shortest
+    prefix whose running sum reaches p ("reaches" read as >=).  With p >= 1, or if
+    every running sum stays below p, all blocks are kept.  The window blocks are
+    added afterwards.
 
-    Returns (keep bool [nb], detail dict with order, cumsum and the cut size).
+    Returns (keep bool [nb], detail dict with order, the float64 running sums for
+    reports, and the cut size).
     """
     nb = n_blocks(L, G)
     s = np.asarray(scores, dtype=np.float32)
     assert s.size == nb
     order = sorted(range(nb), key=lambda b: (-float(s[b]), b))
     p64 = float(np.float32(p))
+    p_units = exact_units(p64) if p64 <= 1.0 else None
     csum = []
     acc = 0.0
+    exact = 0
     kstar = nb
+    found = False
     for r, b in enumerate(order):
         acc = acc + float(s[b])
         csum.append(acc)
-    if p64 < 1.0:
-        for r in range(nb):
-            if csum[r] >= p64:
-                kstar = r + 1
-                break
+        exact += exact_units(float(s[b]))
+        if not found and p64 < 1.0 and exact >= p_units:
+            kstar = r + 1
+            found = True
     keep = np.zeros(nb, dtype=bool)
     for b in order[:kstar]:
         keep[b] = True

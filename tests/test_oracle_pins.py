@@ -240,7 +240,9 @@ def test_one_hot_block_dominates():
 
 @pytest.mark.parametrize("seed", range(12))
 def test_topp_minimal_by_subset_enumeration(seed):
-    """The prefix cut is the smallest block set reaching p, and no equal-size set has more mass."""
+    """The prefix cut is the smallest block set reaching p, and no equal-size set has more mass.
+
+    Sums are exact (Fractions), as the oracle's cut is."""
     rng = np.random.default_rng(100 + seed)
     nb = int(rng.integers(2, 13))
     s = rng.dirichlet(np.full(nb, 0.7)).astype(np.float32)
@@ -248,29 +250,41 @@ def test_topp_minimal_by_subset_enumeration(seed):
     L, G, n = nb * 16, 16, 1                      # window = last token only
     keep, det = O.topp_request(s, L, n, G, p)
     kstar = det["kstar"]
-    p64 = float(np.float32(p))
-    sd = s.astype(np.float64)
+    pf = Fraction(float(np.float32(p)))
+    sf = [Fraction(float(x)) for x in s]
     best_size = None
     for size in range(1, nb + 1):
-        if any(math.fsum(sd[list(c)]) >= p64 for c in itertools.combinations(range(nb), size)):
+        if any(sum(sf[i] for i in c) >= pf for c in itertools.combinations(range(nb), size)):
             best_size = size
             break
     if best_size is None:
-        assert kstar == nb                        # rounding kept every sum below p: keep all
+        assert kstar == nb                        # every sum stays below p: keep all
     else:
-        # float64 sums of distinct orders may differ in the last ulp; the prefix sums are sequential
         assert kstar == best_size
-        pref = math.fsum(sd[det["order"][:kstar]])
-        assert all(pref >= math.fsum(sd[list(c)]) - 1e-15
-                   for c in itertools.combinations(range(nb), kstar))
-    # invariants: reached p at the cut, not one block earlier
-    c = det["cumsum"]
-    if kstar < nb or (best_size is not None):
-        assert c[kstar - 1] >= p64 or kstar == nb
+        pref = sum(sf[i] for i in det["order"][:kstar])
+        assert pref >= pf
+        assert all(pref >= sum(sf[i] for i in c) for c in itertools.combinations(range(nb), kstar))
         if kstar > 1:
-            assert c[kstar - 2] < p64
+            assert sum(sf[i] for i in det["order"][:kstar - 1]) < pf
     # the window block (the last one) is always kept
     assert keep[nb - 1]
+
+
+def test_topp_cut_is_exact_at_the_boundary():
+    """Scores whose float64 running sum rounds differently from the exact one.
+
+    2**-30 added to 1 - 2**-30 ... : sequential float64 rounding is irrelevant to the
+    exact comparison; a running sum that equals p exactly counts as reaching it."""
+    s = np.array([0.5, 0.25, 0.125, 0.125], np.float32)
+    for p, k in ((0.75, 2), (0.875, 3), (0.8750001, 4), (1.0, 4), (0.5, 1)):
+        keep, det = O.topp_request(s, 4 * 16, 1, 16, p)
+        assert det["kstar"] == k, (p, det["kstar"])
+    # many tiny scores after a large one: the exact sum of the tail crosses p
+    tiny = np.float32(2.0 ** -40)
+    s = np.array([np.float32(1.0) - np.float32(2.0 ** -24)] + [tiny] * 2**4 + [np.float32(0)] * 3, np.float32)
+    p = float(np.float32(1.0) - np.float32(2.0 ** -24))
+    keep, det = O.topp_request(s, s.size * 16, 1, 16, p)
+    assert det["kstar"] == 1
 
 
 def test_topp_special_cases_and_nesting():
