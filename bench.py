@@ -1,0 +1,182 @@
+"""Benchmark of one full-attention layer decision on one MI355X.
+
+A step = block scores -> Top-p select -> expand + compact -> compose, over one batch
+of synthetic inputs already resident in HBM (default: the Llama-3.1-8B shape at 128K
+tokens).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--p P]
+                    [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/sec selected+compacted per layer at 128K; % MFMA peak, % HBM BW"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(L: int, W: int) -> int:
+    """(query, key) pairs one head scores: W*(L-W) + W*(W+1)/2."""
+    return W * (L - W) + W * (W + 1) // 2
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama31_8b_128k")
+    ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
+              "multi-GPU path; the per-GPU share is what one GPU measures.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_wise_token_amd as up
+    from workloads import synth
+
+    cfg = synth.WORKLOADS[args.workload]
+    p = cfg["p"] if args.p is None else args.p
+    t0 = time.time()
+    b = synth.make_batch(cfg)
+    hidden = synth.gen_hidden(b.T, cfg["H"], cfg["seed"])
+    pos = synth.positions(b.cu_seqlens)
+    log(f"[bench] generated {args.workload}: T={b.T} in {time.time() - t0:.1f}s")
+
+    dev = torch.device("cuda:0")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    qwin, k, hid = bf16(b.qwin), bf16(b.k), bf16(hidden)
+    cu = torch.from_numpy(b.cu_seqlens).to(dev)
+    posd = torch.from_numpy(pos).to(dev)
+    dec = up.LayerDecision(qwin, k, cu, b.cu_seqlens, hid, posd, b.n, b.G, p)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        dec.run()
+    torch.cuda.synchronize()
+    assert up.device_error() == 0, "device error word set"
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    # Timed region: K steps, nothing instrumented.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        dec.run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
+
+    # Same K steps again with the library's per-kernel HIP events on the launch stream.
+    up.profile_reset()
+    up.profile_enable(True)
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev2.record(stream)
+    for _ in range(args.steps):
+        dec.run()
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    up.profile_enable(False)
+    ms_step_instr = ev2.elapsed_time(ev3) / args.steps
+    kern = {}
+    for name in up.KERNEL_IDS:
+        n, ms = up.profile_read(name)
+        if n:
+            kern[name] = {"launches": n, "avg_us": ms * 1e3 / n}
+    up.profile_reset()
+    assert up.device_error() == 0
+
+    kept = int(dec.cu_out[-1].item())
+    T = b.T
+    row_bytes = cfg["H"] * 2
+    # Algorithmic work per launch.
+    pairs = sum(causal_pairs(int(L), min(b.n, int(L))) for L in np.diff(b.cu_seqlens))
+    score_flops = 2.0 * b.d * b.Hq * pairs                          # one Q K^T over causal pairs
+    gather_bytes = kept * (2 * row_bytes + 12)                        # rows read+written, pos r/w, idx w
+    s_us = kern["score_partial"]["avg_us"]
+    g_us = kern["gather"]["avg_us"]
+    score_tflops = score_flops / (s_us * 1e-6) / 1e12
+    gather_gbs = gather_bytes / (g_us * 1e-6) / 1e9
+    roof_score = {"bound": "mfma", "achieved": round(score_tflops, 2),
+                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(score_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                  "kernel": "up_score_partial_kernel", "avg_us": round(s_us, 2),
+                  "work_per_launch": score_flops}
+    roof_gather = {"bound": "hbm", "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                   "kernel": "up_gather_kernel", "avg_us": round(g_us, 2),
+                   "work_per_launch": gather_bytes}
+    dominant = roof_gather if g_us >= s_us else roof_score
+
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": b.B, "T": T, "Hq": b.Hq, "Hkv": b.Hkv,
+                   "d": b.d, "n": b.n, "G": b.G, "p": p, "H": cfg["H"], "seed": cfg["seed"],
+                   "kept_tokens": kept, "rho": kept / T},
+        "roofline": dominant,
+        "rooflines": {"score": roof_score, "gather": roof_gather},
+        "kernels_avg_us": {k2: round(v["avg_us"], 2) for k2, v in kern.items()},
+        "ms_per_step_instrumented": ms_step_instr,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(b, hidden, pos, p, cfg)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(b, hidden, pos, p, cfg):
+    """The oracle, untuned, timed on this host on one full decision of the same workload."""
+    from oracle import uniprefill_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    log("[bench] cpu baseline: oracle on one full decision ...")
+    t0 = time.perf_counter()
+    O.decide(b.qwin, b.k, b.cu_seqlens, hidden, pos, b.Hq, b.Hkv, b.d, b.n, b.G, p, fast=True)
+    dt = time.perf_counter() - t0
+    log(f"[bench] cpu baseline: {dt:.1f}s")
+    return {"value": b.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full decision of {cfg and 'the same workload'} "
+                      f"({b.T} tokens: scores, Top-p, expand, compact, compose), NumPy float64",
+            "seconds": dt, "cpu": platform.processor() or platform.machine()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,278 @@
+"""ctypes binding of libuniprefill (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libuniprefill.so")
+
+KERNEL_IDS = {
+    "score_partial": 0, "row_stats": 1, "block_mass": 2, "normalize": 3, "select": 4,
+    "select_finalize": 5, "block_dst": 6, "gather": 7, "compose": 8, "score_plan": 9,
+}
+
+_lib = None
+
+
+class UniPrefillError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libuniprefill.so (built in-tree by ``python -m block_wise_token_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise UniPrefillError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m block_wise_token_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32p, u8p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    ci, cf, cs = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.up_status_string.restype = ctypes.c_char_p
+    L.up_status_string.argtypes = [ci]
+    L.up_abi_version.restype = ci
+    L.up_block_scores_workspace.restype = cs
+    L.up_block_scores_workspace.argtypes = [vp, ci, ci, ci, ci, ci, ci]
+    L.up_block_scores.restype = ci
+    L.up_block_scores.argtypes = [vp, vp, i32p, vp, ci, ci, ci, ci, ci, ci, cf, f32p, vp, cs, vp]
+    L.up_topp_select.restype = ci
+    L.up_topp_select.argtypes = [f32p, i32p, vp, ci, ci, ci, cf, u8p, i32p, vp]
+    L.up_topk_select.restype = ci
+    L.up_topk_select.argtypes = [f32p, i32p, vp, ci, ci, ci, ci, u8p, i32p, vp]
+    L.up_expand_compact_workspace.restype = cs
+    L.up_expand_compact_workspace.argtypes = [vp, ci, ci]
+    L.up_expand_compact.restype = ci
+    L.up_expand_compact.argtypes = [vp, ci, ci, i32p, u8p, i32p, i32p, vp, ci, ci, i32p, vp, i32p,
+                                    vp, cs, vp]
+    L.up_compose_drops.restype = ci
+    L.up_compose_drops.argtypes = [i32p, ci, i32p, i32p, ci, i32p, vp]
+    L.up_device_error.restype = ci
+    L.up_device_error.argtypes = [vp, vp]
+    L.up_profile_enable.restype = ci
+    L.up_profile_enable.argtypes = [ci]
+    L.up_profile_read.restype = ci
+    L.up_profile_read.argtypes = [ci, vp, vp]
+    L.up_profile_reset.restype = ci
+    L.up_profile_reset.argtypes = []
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise UniPrefillError(f"{what}: {lib().up_status_string(status).decode()}")
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+class _HostCu:
+    """Host copy of cu_seqlens as a C int32 array (kept alive with its pointer)."""
+
+    def __init__(self, cu_h):
+        a = np.ascontiguousarray(np.asarray(cu_h.cpu() if isinstance(cu_h, torch.Tensor) else cu_h,
+                                            dtype=np.int32))
+        self.arr = a
+        self.B = int(a.size - 1)
+        self.ptr = a.ctypes.data_as(ctypes.c_void_p)
+
+    @property
+    def T(self) -> int:
+        return int(self.arr[-1]) if self.arr.size else 0
+
+    def nb_tot(self, G: int) -> int:
+        return int(sum((int(L) + G - 1) // G for L in np.diff(self.arr)))
+
+
+def block_scores_workspace_bytes(cu_h, Hq, Hkv, d, n, G) -> int:
+    h = _HostCu(cu_h)
+    return int(lib().up_block_scores_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
+
+
+def expand_compact_workspace_bytes(cu_h, G) -> int:
+    h = _HostCu(cu_h)
+    return int(lib().up_expand_compact_workspace(h.ptr, h.B, G))
+
+
+def block_scores(qwin, k, cu_seqlens, cu_h, n, G, scale=0.0, out=None, workspace=None,
+                 stream=None):
+    """Per-block importance scores (float32 [NB_tot]); see up_block_scores."""
+    _dev(qwin, torch.bfloat16, "qwin")
+    _dev(k, torch.bfloat16, "k")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    h = _HostCu(cu_h)
+    Hq, d = int(qwin.shape[1]), int(qwin.shape[2])
+    Hkv = int(k.shape[1])
+    if out is None:
+        out = torch.empty(h.nb_tot(G), dtype=torch.float32, device=qwin.device)
+    need = int(lib().up_block_scores_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qwin.device)
+    st = lib().up_block_scores(_ptr(qwin), _ptr(k), _ptr(cu_seqlens), h.ptr, h.B, Hq, Hkv, d, n,
+                               G, float(scale), _ptr(out), _ptr(workspace),
+                               workspace.numel(), _stream(stream))
+    _check(st, "up_block_scores")
+    return out
+
+
+def _select(fn, scores, cu_seqlens, cu_h, n, G, arg, keep, cu_out, stream, what):
+    _dev(scores, torch.float32, "scores")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    h = _HostCu(cu_h)
+    if keep is None:
+        keep = torch.empty(h.nb_tot(G), dtype=torch.uint8, device=scores.device)
+    if cu_out is None:
+        cu_out = torch.empty(h.B + 1, dtype=torch.int32, device=scores.device)
+    st = fn(_ptr(scores), _ptr(cu_seqlens), h.ptr, h.B, n, G, arg, _ptr(keep), _ptr(cu_out),
+            _stream(stream))
+    _check(st, what)
+    return keep, cu_out
+
+
+def topp_select(scores, cu_seqlens, cu_h, n, G, p, keep=None, cu_out=None, stream=None):
+    """Top-p cut: (keep_blocks uint8 [NB_tot], cu_seqlens_out int32 [B+1])."""
+    return _select(lib().up_topp_select, scores, cu_seqlens, cu_h, n, G, ctypes.c_float(p), keep,
+                   cu_out, stream, "up_topp_select")
+
+
+def topk_select(scores, cu_seqlens, cu_h, n, G, topk, keep=None, cu_out=None, stream=None):
+    """Top-k cut (fixed block count per request) plus the window blocks."""
+    return _select(lib().up_topk_select, scores, cu_seqlens, cu_h, n, G, int(topk), keep, cu_out,
+                   stream, "up_topk_select")
+
+
+def expand_compact(hidden, pos, keep, cu_seqlens, cu_out, cu_h, G, idx_out=None, hidden_out=None,
+                   pos_out=None, workspace=None, stream=None):
+    """Kept-token rows: (idx_out, hidden_out, pos_out), each with capacity T rows."""
+    if not hidden.is_cuda or not hidden.is_contiguous():
+        raise ValueError("hidden must be a contiguous device tensor")
+    _dev(keep, torch.uint8, "keep_blocks")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    _dev(cu_out, torch.int32, "cu_seqlens_out")
+    if pos is not None:
+        _dev(pos, torch.int32, "pos")
+    h = _HostCu(cu_h)
+    T = h.T
+    H = int(hidden.shape[1])
+    eb = hidden.element_size()
+    dev = hidden.device
+    if idx_out is None:
+        idx_out = torch.empty(T, dtype=torch.int32, device=dev)
+    if hidden_out is None:
+        hidden_out = torch.empty((T, H), dtype=hidden.dtype, device=dev)
+    if pos_out is None and pos is not None:
+        pos_out = torch.empty(T, dtype=torch.int32, device=dev)
+    need = int(lib().up_expand_compact_workspace(h.ptr, h.B, G))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().up_expand_compact(_ptr(hidden), H, eb, _ptr(pos), _ptr(keep), _ptr(cu_seqlens),
+                                 _ptr(cu_out), h.ptr, h.B, G, _ptr(idx_out), _ptr(hidden_out),
+                                 _ptr(pos_out), _ptr(workspace), workspace.numel(),
+                                 _stream(stream))
+    _check(st, "up_expand_compact")
+    return idx_out, hidden_out, pos_out
+
+
+def compose_drops(prev_orig, idx, count, capacity=None, out=None, stream=None):
+    """orig[r] = prev_orig[idx[r]] for r < *count (count: device int32 scalar view)."""
+    _dev(prev_orig, torch.int32, "prev_orig")
+    _dev(idx, torch.int32, "idx")
+    _dev(count, torch.int32, "count")
+    cap = int(idx.numel()) if capacity is None else int(capacity)
+    if out is None:
+        out = torch.empty(cap, dtype=torch.int32, device=idx.device)
+    st = lib().up_compose_drops(_ptr(prev_orig), int(prev_orig.numel()), _ptr(idx), _ptr(count),
+                                cap, _ptr(out), _stream(stream))
+    _check(st, "up_compose_drops")
+    return out
+
+
+def device_error(stream=None) -> int:
+    """Read and clear the library's device error word (synchronises)."""
+    v = ctypes.c_int32(0)
+    _check(lib().up_device_error(ctypes.byref(v), _stream(stream)), "up_device_error")
+    return int(v.value)
+
+
+def profile_enable(on: bool = True):
+    _check(lib().up_profile_enable(1 if on else 0), "up_profile_enable")
+
+
+def profile_reset():
+    _check(lib().up_profile_reset(), "up_profile_reset")
+
+
+def profile_read(name: str):
+    """(launches, total milliseconds) recorded for a kernel family."""
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib().up_profile_read(KERNEL_IDS[name], ctypes.byref(n), ctypes.byref(ms)),
+           "up_profile_read")
+    return int(n.value), float(ms.value)
+
+
+class LayerDecision:
+    """One full-attention layer decision with every buffer allocated up front.
+
+    ``run()`` issues the four calls -- scores, Top-p, expand+compact, compose -- on
+    the current stream and allocates nothing.
+    """
+
+    def __init__(self, qwin, k, cu_seqlens, cu_h, hidden, pos, n, G, p, scale=0.0,
+                 prev_orig=None, topk=None):
+        self.qwin, self.k, self.cu, self.hidden, self.pos = qwin, k, cu_seqlens, hidden, pos
+        self.h = _HostCu(cu_h)
+        self.n, self.G, self.p, self.scale, self.topk = n, G, p, scale, topk
+        dev = qwin.device
+        T, B = self.h.T, self.h.B
+        nbt = self.h.nb_tot(G)
+        Hq, d, Hkv = int(qwin.shape[1]), int(qwin.shape[2]), int(k.shape[1])
+        self.scores = torch.empty(nbt, dtype=torch.float32, device=dev)
+        self.ws_scores = torch.empty(max(1, block_scores_workspace_bytes(self.h.arr, Hq, Hkv, d, n, G)),
+                                     dtype=torch.uint8, device=dev)
+        self.keep = torch.empty(nbt, dtype=torch.uint8, device=dev)
+        self.cu_out = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        self.idx = torch.empty(T, dtype=torch.int32, device=dev)
+        self.hidden_out = torch.empty_like(hidden)
+        self.pos_out = torch.empty(T, dtype=torch.int32, device=dev)
+        self.ws_compact = torch.empty(max(1, expand_compact_workspace_bytes(self.h.arr, G)),
+                                      dtype=torch.uint8, device=dev)
+        self.prev_orig = prev_orig if prev_orig is not None else torch.arange(
+            T, dtype=torch.int32, device=dev)
+        self.orig = torch.empty(T, dtype=torch.int32, device=dev)
+
+    def run(self, stream=None):
+        block_scores(self.qwin, self.k, self.cu, self.h.arr, self.n, self.G, self.scale,
+                     out=self.scores, workspace=self.ws_scores, stream=stream)
+        if self.topk is None:
+            topp_select(self.scores, self.cu, self.h.arr, self.n, self.G, self.p, keep=self.keep,
+                        cu_out=self.cu_out, stream=stream)
+        else:
+            topk_select(self.scores, self.cu, self.h.arr, self.n, self.G, self.topk, keep=self.keep,
+                        cu_out=self.cu_out, stream=stream)
+        expand_compact(self.hidden, self.pos, self.keep, self.cu, self.cu_out, self.h.arr, self.G,
+                       idx_out=self.idx, hidden_out=self.hidden_out, pos_out=self.pos_out,
+                       workspace=self.ws_compact, stream=stream)
+        compose_drops(self.prev_orig, self.idx, self.cu_out[self.h.B:self.h.B + 1],
+                      capacity=self.h.T, out=self.orig, stream=stream)

@@ -1,0 +1,346 @@
+// C ABI of libuniprefill: argument validation, grid planning, workspace layout and
+// launches.  The operations and their page citations are documented in
+// include/uniprefill.h.
+#include "uniprefill.h"
+#include "up_internal.h"
+
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+namespace {
+
+using namespace up;
+
+// Device error word: one copy per GPU; its device address is looked up once per
+// device and passed to kernels as a plain pointer.
+__device__ int g_up_error;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+int* g_err_ptr[kMaxDevices] = {};
+
+int* error_word() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_err_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_up_error)) != hipSuccess) return nullptr;
+    g_err_ptr[dev] = static_cast<int*>(p);
+  }
+  return g_err_ptr[dev];
+}
+
+__global__ void up_clear_word_kernel(int* w) { *w = 0; }
+
+// ---- kernel timing (opt-in) ------------------------------------------------
+struct Rec {
+  int which;
+  hipEvent_t a, b;
+};
+bool g_prof = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(int which, hipStream_t st, F&& f) {
+  if (!g_prof) return f();
+  std::lock_guard<std::mutex> lk(g_mu);
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, st);
+  if (e != hipSuccess) return e;
+  e = f();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, st);
+  g_recs.push_back({which, a, b});
+  return e;
+}
+
+// ---- validation ----------------------------------------------------------------
+bool cu_ok(const int32_t* cu_h, int B) {
+  if (B < 0 || (B > 0 && !cu_h)) return false;
+  if (B == 0) return cu_h == nullptr || cu_h[0] == 0;
+  if (cu_h[0] != 0) return false;
+  for (int i = 0; i < B; ++i)
+    if (cu_h[i + 1] < cu_h[i]) return false;
+  return true;
+}
+
+struct SelPlan {
+  int64_t T = 0, nb_tot = 0;
+  int nb_max = 0;
+};
+
+SelPlan sel_plan(const int32_t* cu_h, int B, int G) {
+  SelPlan s;
+  for (int i = 0; i < B; ++i) {
+    const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
+    const int64_t nb = (L + G - 1) / G;
+    s.nb_tot += nb;
+    if (nb > s.nb_max) s.nb_max = (int)nb;
+  }
+  s.T = B > 0 ? cu_h[B] : 0;
+  return s;
+}
+
+bool block_size_supported(int G) { return G >= 32 && G <= 1024 && G % 32 == 0; }
+
+// Plan of the score pass; returns UP_OK or an error status.
+int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G, ScoreShape* s,
+                Totals* t) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || n <= 0 || G <= 0 || d <= 0) return UP_EINVAL;
+  if (Hq % Hkv != 0) return UP_EINVAL;
+  if (!cu_ok(cu_h, B)) return UP_EINVAL;
+  if (d != 64 && d != 128 && d != 256) return UP_EUNSUPPORTED;
+  if (!block_size_supported(G)) return UP_EUNSUPPORTED;
+  s->B = B; s->Hq = Hq; s->Hkv = Hkv; s->d = d; s->n = n; s->G = G;
+  s->qt = (d == 256) ? 1 : 2;
+  s->kt = (d == 256) ? 1 : (G % 64 == 0 ? 2 : 1);
+  s->rows_wg = 8 * s->qt * 32;
+  const int64_t gs = Hq / Hkv;
+  int64_t units = 0;
+  for (int i = 0; i < B; ++i) {
+    const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
+    const int64_t W = L < n ? L : n;
+    const int64_t nb = (L + G - 1) / G;
+    const int64_t nrt = (gs * W + s->rows_wg - 1) / s->rows_wg;
+    units += nb * Hkv * nrt;
+  }
+  // Key-chunk length: aim at about 1024 workgroups (4 per CU) for long inputs.
+  int64_t cb = units / 1024;
+  s->CB = (int)(cb < 1 ? 1 : (cb > 32 ? 32 : cb));
+  *t = Totals{};
+  for (int i = 0; i < B; ++i) {
+    const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
+    const int64_t W = L < n ? L : n;
+    const int64_t nb = (L + G - 1) / G;
+    const int64_t nch = (nb + s->CB - 1) / s->CB;
+    const int64_t R = gs * W;
+    const int64_t nrt = (R + s->rows_wg - 1) / s->rows_wg;
+    t->win_rows += W;
+    t->nb_tot += nb;
+    t->items += nch * Hkv * nrt;
+    t->ml_pairs += nb * Hkv * R;
+    t->cs_pairs += nch * Hkv * R;
+    if (nb > t->nb_max) t->nb_max = (int32_t)nb;
+  }
+  t->T = B > 0 ? cu_h[B] : 0;
+  t->rows = t->win_rows * Hq;
+  if (t->items >= (int64_t)1 << 31 || t->rows >= (int64_t)1 << 31) return UP_EUNSUPPORTED;
+  if ((int64_t)t->win_rows * Hq * d >= ((int64_t)1 << 40)) return UP_EUNSUPPORTED;
+  return UP_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* up_status_string(int status) {
+  switch (status) {
+    case UP_OK: return "UP_OK";
+    case UP_EINVAL: return "UP_EINVAL: invalid argument";
+    case UP_EUNSUPPORTED: return "UP_EUNSUPPORTED: unsupported shape or size";
+    case UP_EWORKSPACE: return "UP_EWORKSPACE: workspace missing, too small or misaligned";
+    case UP_EHIP: return "UP_EHIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int up_abi_version(void) { return 1; }
+
+size_t up_block_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d,
+                                 int n, int G) {
+  ScoreShape s;
+  Totals t;
+  if (plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t) != UP_OK) return 0;
+  return score_ws_layout(B, t).total;
+}
+
+int up_block_scores(const void* qwin, const void* k, const int32_t* cu_seqlens,
+                    const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d, int n, int G,
+                    float scale, float* scores, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  ScoreShape s;
+  Totals t;
+  const int st = plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t);
+  if (st != UP_OK) return st;
+  if (B == 0 || t.T == 0) return UP_OK;
+  if (!qwin || !k || !cu_seqlens || !scores) return UP_EINVAL;
+  if (!aligned(qwin, 16) || !aligned(k, 16)) return UP_EINVAL;
+  const ScoreWs L = score_ws_layout(B, t);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, kWsAlign))
+    return UP_EWORKSPACE;
+  if (!(scale > 0.f) || std::isinf(scale)) scale = (float)(1.0 / std::sqrt((double)d));
+  const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
+  int* err = error_word();
+  if (!err) return UP_EHIP;
+  hipStream_t hs = as_stream(stream);
+  hipError_t e;
+  e = timed(9, hs, [&] { return launch_score_plan(cu_seqlens, s, t, workspace, L, err, hs); });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(0, hs, [&] { return launch_score_partial(qwin, k, s, t, workspace, L, c, hs); });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(1, hs, [&] { return launch_row_stats(s, t, workspace, L, hs); });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(2, hs, [&] { return launch_block_mass(s, t, workspace, L, hs); });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(3, hs, [&] { return launch_normalize(s, t, workspace, L, scores, hs); });
+  if (e != hipSuccess) return UP_EHIP;
+  return UP_OK;
+}
+
+static int select_common(const float* scores, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_h, int B, int n, int G, int mode, float p,
+                         int topk, uint8_t* keep_blocks, int32_t* cu_seqlens_out, void* stream) {
+  if (B < 0 || n <= 0 || G <= 0) return UP_EINVAL;
+  if (!cu_ok(cu_seqlens_h, B)) return UP_EINVAL;
+  if (mode == 0 && !(p > 0.f && p <= 1.f)) return UP_EINVAL;
+  if (mode == 1 && topk < 0) return UP_EINVAL;
+  if (!cu_seqlens_out) return UP_EINVAL;
+  const SelPlan sp = sel_plan(cu_seqlens_h, B, G);
+  if (sp.nb_max > kSelectMaxBlocks) return UP_EUNSUPPORTED;
+  if (B > 0 && (!cu_seqlens || (sp.nb_tot > 0 && (!scores || !keep_blocks)))) return UP_EINVAL;
+  int* err = error_word();
+  if (!err) return UP_EHIP;
+  hipStream_t hs = as_stream(stream);
+  hipError_t e = timed(4, hs, [&] {
+    return launch_select(scores, cu_seqlens, B, n, G, mode, p, topk, sp.nb_max, sp.T, sp.nb_tot,
+                         keep_blocks, cu_seqlens_out, err, hs);
+  });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(5, hs, [&] { return launch_select_finalize(cu_seqlens_out, B, hs); });
+  return e == hipSuccess ? UP_OK : UP_EHIP;
+}
+
+int up_topp_select(const float* scores, const int32_t* cu_seqlens, const int32_t* cu_seqlens_h,
+                   int B, int n, int G, float p, uint8_t* keep_blocks, int32_t* cu_seqlens_out,
+                   void* stream) {
+  return select_common(scores, cu_seqlens, cu_seqlens_h, B, n, G, 0, p, 0, keep_blocks,
+                       cu_seqlens_out, stream);
+}
+
+int up_topk_select(const float* scores, const int32_t* cu_seqlens, const int32_t* cu_seqlens_h,
+                   int B, int n, int G, int topk, uint8_t* keep_blocks, int32_t* cu_seqlens_out,
+                   void* stream) {
+  return select_common(scores, cu_seqlens, cu_seqlens_h, B, n, G, 1, 1.0f, topk, keep_blocks,
+                       cu_seqlens_out, stream);
+}
+
+size_t up_expand_compact_workspace(const int32_t* cu_seqlens_h, int B, int G) {
+  if (G <= 0 || !cu_ok(cu_seqlens_h, B)) return 0;
+  const SelPlan sp = sel_plan(cu_seqlens_h, B, G);
+  return compact_ws_layout(sp.nb_tot).total;
+}
+
+int up_expand_compact(const void* hidden, int H, int elem_bytes, const int32_t* pos,
+                      const uint8_t* keep_blocks, const int32_t* cu_seqlens,
+                      const int32_t* cu_seqlens_out, const int32_t* cu_seqlens_h, int B, int G,
+                      int32_t* idx_out, void* hidden_out, int32_t* pos_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (B < 0 || G <= 0 || H <= 0 || elem_bytes <= 0) return UP_EINVAL;
+  if (!cu_ok(cu_seqlens_h, B)) return UP_EINVAL;
+  const SelPlan sp = sel_plan(cu_seqlens_h, B, G);
+  if (B == 0 || sp.T == 0) return UP_OK;
+  if (!hidden || !keep_blocks || !cu_seqlens || !cu_seqlens_out || !idx_out || !hidden_out)
+    return UP_EINVAL;
+  if (pos_out && !pos) return UP_EINVAL;
+  const int64_t row_bytes = (int64_t)H * elem_bytes;
+  if (sp.T * row_bytes / row_bytes != sp.T) return UP_EUNSUPPORTED;
+  const CompactWs L = compact_ws_layout(sp.nb_tot);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, kWsAlign))
+    return UP_EWORKSPACE;
+  int* err = error_word();
+  if (!err) return UP_EHIP;
+  hipStream_t hs = as_stream(stream);
+  hipError_t e = timed(6, hs, [&] {
+    return launch_block_dst(keep_blocks, cu_seqlens, cu_seqlens_out, B, G, sp.T, sp.nb_tot,
+                            workspace, L, err, hs);
+  });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(7, hs, [&] {
+    return launch_gather(hidden, row_bytes, pos, workspace, L, sp.nb_tot, G, idx_out, hidden_out,
+                         pos_out, hs);
+  });
+  return e == hipSuccess ? UP_OK : UP_EHIP;
+}
+
+int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
+                     const int32_t* count, int capacity, int32_t* orig_out, void* stream) {
+  if (capacity < 0 || prev_len < 0) return UP_EINVAL;
+  if (capacity == 0) return UP_OK;
+  if (!idx || !count || !orig_out || (prev_len > 0 && !prev_orig)) return UP_EINVAL;
+  int* err = error_word();
+  if (!err) return UP_EHIP;
+  hipStream_t hs = as_stream(stream);
+  hipError_t e = timed(8, hs, [&] {
+    return launch_compose(prev_orig, prev_len, idx, count, capacity, orig_out, err, hs);
+  });
+  return e == hipSuccess ? UP_OK : UP_EHIP;
+}
+
+int up_device_error(int32_t* code_h, void* stream) {
+  if (!code_h) return UP_EINVAL;
+  int* err = error_word();
+  if (!err) return UP_EHIP;
+  hipStream_t hs = as_stream(stream);
+  if (hipStreamSynchronize(hs) != hipSuccess) return UP_EHIP;
+  if (hipMemcpy(code_h, err, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return UP_EHIP;
+  hipLaunchKernelGGL(up_clear_word_kernel, dim3(1), dim3(1), 0, hs, err);
+  if (hipGetLastError() != hipSuccess) return UP_EHIP;
+  if (hipStreamSynchronize(hs) != hipSuccess) return UP_EHIP;
+  return UP_OK;
+}
+
+int up_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_prof = on != 0;
+  return UP_OK;
+}
+
+int up_profile_read(int which, int* launches_h, double* total_ms_h) {
+  if (!launches_h || !total_ms_h) return UP_EINVAL;
+  std::lock_guard<std::mutex> lk(g_mu);
+  int cnt = 0;
+  double tot = 0.0;
+  for (const Rec& r : g_recs) {
+    if (r.which != which) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return UP_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return UP_EHIP;
+    tot += ms;
+    ++cnt;
+  }
+  *launches_h = cnt;
+  *total_ms_h = tot;
+  return UP_OK;
+}
+
+int up_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (const Rec& r : g_recs) {
+    (void)hipEventSynchronize(r.b);
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return UP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal declarations shared by the HIP translation units of libuniprefill.
+// Not part of the public ABI (include/uniprefill.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace up {
+
+constexpr size_t kWsAlign = 256;
+
+inline size_t align_up(size_t x, size_t a = kWsAlign) { return (x + a - 1) / a * a; }
+
+// Per-request plan of the score pass.  Built on the host from cu_seqlens_h (to size
+// grids and workspaces) and rebuilt on the device from cu_seqlens by the plan
+// kernel, which checks the two agree before any other kernel touches memory.
+struct ReqPlan {
+  int32_t tok_off;   // first token of the request in the packed batch
+  int32_t L;         // length
+  int32_t W;         // window rows: min(n, L)
+  int32_t win_off;   // first window row of the request in qwin
+  int32_t blk_off;   // first global block
+  int32_t nb;        // blocks: ceil(L / G)
+  int32_t nch;       // key chunks: ceil(nb / CB)
+  int32_t item_end;  // exclusive end of the request's work items of the score kernel
+  int64_t ml_off;    // first (m, l) pair of the request: pairs are [nb][Hkv][R], R = gs * W
+  int64_t cs_off;    // first chunk-statistics pair: [nch][Hkv][R]
+};
+
+// Shape of the score pass, fixed by the host for one call.
+struct ScoreShape {
+  int B, Hq, Hkv, d, n, G;
+  int CB;        // blocks per key chunk (one workgroup's span of keys)
+  int qt;        // 32-query column tiles per wave (1 or 2)
+  int kt;        // 32-key row tiles per LDS stage (1 or 2)
+  int rows_wg;   // query rows per workgroup = 8 waves * qt * 32
+};
+
+struct Totals {
+  int64_t T;         // tokens
+  int64_t win_rows;  // sum of W_i
+  int64_t rows;      // window rows over all query heads: Hq * win_rows
+  int64_t nb_tot;    // blocks
+  int64_t items;     // score work items (workgroups)
+  int64_t ml_pairs;  // (m, l) pairs
+  int64_t cs_pairs;  // chunk-statistics pairs
+  int32_t nb_max;    // largest per-request block count
+};
+
+// Workspace header written by the plan kernel (first 256 bytes of a workspace).
+struct WsHeader {
+  int32_t valid;     // 1 when the device plan matches the host totals
+  int32_t pad[63];
+};
+
+// Score-pass workspace layout (offsets in bytes from the workspace base).
+struct ScoreWs {
+  size_t plan, ml, cs, rs, mass, total;
+};
+
+ScoreWs score_ws_layout(int B, const Totals& t);
+
+// Launchers (score.hip).  Each returns the hipError_t of its launch.
+hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Totals& t,
+                             void* ws, const ScoreWs& L, int* err, hipStream_t st);
+hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShape& s,
+                                const Totals& t, void* ws, const ScoreWs& L, float c_log2,
+                                hipStream_t st);
+hipError_t launch_row_stats(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
+                            hipStream_t st);
+hipError_t launch_block_mass(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
+                             hipStream_t st);
+hipError_t launch_normalize(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
+                            float* scores, hipStream_t st);
+
+// Selection (select.hip).  mode 0: Top-p with threshold p; mode 1: Top-k with k = topk.
+constexpr int kSelectMaxBlocks = 8192;
+hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, int G, int mode,
+                         float p, int topk, int nb_max, int64_t T_host, int64_t nb_tot_host,
+                         uint8_t* keep, int32_t* cu_out, int* err, hipStream_t st);
+hipError_t launch_select_finalize(int32_t* cu_out, int B, hipStream_t st);
+
+// Expand + compact (compact.hip).
+struct CompactWs {
+  size_t hdr, dst, src, len, total;
+};
+CompactWs compact_ws_layout(int64_t nb_tot);
+hipError_t launch_block_dst(const uint8_t* keep, const int32_t* cu, const int32_t* cu_out, int B,
+                            int G, int64_t T_host, int64_t nb_tot_host, void* ws,
+                            const CompactWs& L, int* err, hipStream_t st);
+hipError_t launch_gather(const void* hidden, int64_t row_bytes, const int32_t* pos, void* ws,
+                         const CompactWs& L, int64_t nb_tot, int G, int32_t* idx_out,
+                         void* hidden_out, int32_t* pos_out, hipStream_t st);
+hipError_t launch_compose(const int32_t* prev, int prev_len, const int32_t* idx,
+                          const int32_t* count, int capacity, int32_t* out, int* err,
+                          hipStream_t st);
+
+}  // namespace up

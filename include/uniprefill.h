@@ -1,0 +1,193 @@
+/*
+ * uniprefill.h -- C ABI of the block-wise token-dropping hot path (MI355X / gfx950).
+ *
+ * One full-attention layer decision, as described by the UniPrefill pages:
+ *   1. up_block_scores   : per-block importance from the last n window queries
+ *   2. up_topp_select    : Top-p cut over the sorted block scores
+ *   3. up_expand_compact : kept blocks -> token indices; gather hidden rows and positions
+ *   4. up_compose_drops  : map survivors back to original indices across layers
+ *
+ * Pages cited (by title and paragraph / section):
+ *   [UP]  "UniPrefill: 블록 단위 동적 희소화를 통한 범용적 롱 컨텍스트 프리필 가속화"
+ *         (AI Trends article on UniPrefill)
+ *   [UPA] "UniPrefill: Universal Long-Context Prefill Acceleration via Block-wise
+ *         Dynamic Sparsification" (ChatPaper abstract page)
+ *   [CP]  "Chunked Prefill" (Ultralytics glossary)
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers unless their name ends in _h (host memory).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream), never synchronises, never allocates device memory, and returns an
+ *    up_status (0 = UP_OK, negative = error).  Arguments are validated on the
+ *    host before anything is launched; on error nothing is launched.
+ *  - The caller owns every buffer.  Outputs are sized for the worst case
+ *    (everything kept); the number of valid rows lives on the device, in
+ *    cu_seqlens_out[B].
+ *  - Batches are packed ("varlen", [UPA]: the operator serves continuous
+ *    batching): request i owns tokens [cu_seqlens[i], cu_seqlens[i+1]) and its
+ *    length is L_i.  cu_seqlens_h must hold the same values as the device
+ *    cu_seqlens; it is used to size grids and workspaces.  A kernel that finds
+ *    the device copy inconsistent with the host-derived totals does nothing and
+ *    raises the device error word (up_device_error).
+ *  - Request i has W_i = min(n, L_i) window queries and nb_i = ceil(L_i / G)
+ *    blocks of G tokens counted from its token 0 (the last may be partial).
+ *    Blocks are numbered globally: request i's blocks start at sum_{i'<i} nb_i'.
+ *  - Results are bitwise reproducible run to run: no floating-point atomics,
+ *    every reduction has a fixed order.
+ *  - Thread safety: calls on different streams may overlap as long as their
+ *    buffers and workspaces are distinct.
+ */
+#ifndef UNIPREFILL_H
+#define UNIPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  UP_OK = 0,
+  UP_EINVAL = -1,        /* bad argument (null pointer, bad size, bad cu_seqlens_h, p out of range) */
+  UP_EUNSUPPORTED = -2,  /* valid but not implemented (head dim, block size, too many blocks) */
+  UP_EWORKSPACE = -3,    /* workspace missing, too small or misaligned (needs 256-byte alignment) */
+  UP_EHIP = -4           /* a HIP runtime call failed */
+} up_status;
+
+/* Human-readable name of a status code (static string). */
+const char* up_status_string(int status);
+
+/* ABI version, currently 1. */
+int up_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * 1. Block scores  ([UP] "drop" paragraph: softmax probabilities near zero mark
+ *    droppable tokens; [UP] "block-wise estimation" paragraph: blocks of G tokens,
+ *    the last n queries, per-block average attention normalised into per-block
+ *    importance scores; [UP] "Triton kernels" paragraph: online softmax and block
+ *    reduction on the GPU; [CP] causal mask over absolute positions)
+ *
+ * For request i, window row j (absolute position t = L_i - W_i + j) and query head
+ * h, with kv head g = floor(h / (Hq/Hkv)):
+ *   P[h, j, k] = softmax over keys k <= t of  scale * <q[j, h], K[k, g]>
+ *   mass[b]    = sum_h sum_j sum_{k in block b} P[h, j, k]
+ *   scores[b]  = mass[b] / sum_{b'} mass[b']          (scores of a request sum to 1)
+ *
+ * qwin  : bf16 [sum_i W_i, Hq, d]; request i's last W_i query tokens, in order,
+ *         requests in batch order.  Row (w, h) at ((w * Hq) + h) * d.
+ * k     : bf16 [T, Hkv, d]; T = cu_seqlens[B].  Key (t, g) at ((t * Hkv) + g) * d.
+ * cu_seqlens / cu_seqlens_h : int32 [B+1], cu[0] = 0, non-decreasing.
+ * Hq % Hkv == 0.  d in {64, 128, 256}.  G a multiple of 32 in [32, 1024].  n >= 1.
+ * scale : softmax scale; <= 0 or NaN selects 1/sqrt(d) (as float32).
+ * scores: float32 [NB_tot] output, NB_tot = sum_i nb_i.
+ * workspace: device buffer of at least up_block_scores_workspace(...) bytes,
+ *         256-byte aligned; its contents on entry are ignored.
+ * Precision: bf16 products accumulated in float32 on the matrix cores; softmax and
+ * probabilities in float32 (never rounded to bf16); cross-row sums in float64.
+ * ------------------------------------------------------------------------- */
+size_t up_block_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv,
+                                 int d, int n, int G);
+
+int up_block_scores(const void* qwin, const void* k,
+                    const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B,
+                    int Hq, int Hkv, int d, int n, int G, float scale,
+                    float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 2. Top-p selection  ([UP] "Top-p selection" paragraph: sort blocks by descending
+ *    importance and keep them until the cumulative sum reaches p, e.g. 0.99;
+ *    [UP] "ablation" paragraph: G = 64, n = 128 are the chosen defaults)
+ *
+ * Per request: order its blocks by (score descending, block index ascending);
+ * keep the shortest prefix whose running sum reaches p (>=).  The running sum of
+ * the float32 scores is exact (no rounding; compared with p as float32), so the cut
+ * does not depend on summation order.  p == 1 keeps every block; so does a running
+ * sum that never reaches p.  The blocks holding window tokens ((b+1)*G > L_i - W_i)
+ * are always kept as well.
+ *
+ * scores        : float32 [NB_tot], each request's scores >= 0 (as produced by 1.).
+ * p             : in (0, 1].
+ * keep_blocks   : uint8 [NB_tot] output, 1 = kept, 0 = dropped.
+ * cu_seqlens_out: int32 [B+1] output, packed offsets of the kept tokens.
+ * Limit: nb_i <= 16384 blocks per request (UP_EUNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------- */
+int up_topp_select(const float* scores, const int32_t* cu_seqlens,
+                   const int32_t* cu_seqlens_h, int B, int n, int G, float p,
+                   uint8_t* keep_blocks, int32_t* cu_seqlens_out, void* stream);
+
+/* Same cut with a fixed number of blocks per request instead of a mass threshold:
+ * keep the top `topk` blocks (all if nb_i <= topk) plus the window blocks.
+ * ([UP] "ablation" paragraph compares Top-p against this fixed-count Top-k.) */
+int up_topk_select(const float* scores, const int32_t* cu_seqlens,
+                   const int32_t* cu_seqlens_h, int B, int n, int G, int topk,
+                   uint8_t* keep_blocks, int32_t* cu_seqlens_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 3. Expand + compact  ([UP] "Top-p selection" paragraph: the output is the set of
+ *    token indices to keep; [UP] "propagation" and "Sparsity Propagation"
+ *    paragraphs: later layers receive only the surviving tokens; [UP] "scheduler"
+ *    paragraph: positions of the survivors are carried along)
+ *
+ * For each request, kept blocks in ascending order, tokens in ascending order:
+ *   idx_out[r]    = packed input row of the r-th surviving token
+ *   hidden_out[r] = hidden[idx_out[r]]   (a bit copy of row_bytes = H * elem_bytes)
+ *   pos_out[r]    = pos[idx_out[r]]      (original positions, never renumbered)
+ * Rows r in [cu_seqlens_out[i], cu_seqlens_out[i+1]) belong to request i.
+ *
+ * hidden     : [T, H] rows of elem_bytes each (bf16: elem_bytes = 2).
+ * pos        : int32 [T], or NULL (then pos_out is not written and may be NULL).
+ * keep_blocks, cu_seqlens_out : as produced by up_topp_select.
+ * idx_out    : int32 [T] capacity;  hidden_out: [T, H] capacity;  pos_out: int32 [T].
+ * workspace  : at least up_expand_compact_workspace(...) bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------- */
+size_t up_expand_compact_workspace(const int32_t* cu_seqlens_h, int B, int G);
+
+int up_expand_compact(const void* hidden, int H, int elem_bytes, const int32_t* pos,
+                      const uint8_t* keep_blocks, const int32_t* cu_seqlens,
+                      const int32_t* cu_seqlens_out, const int32_t* cu_seqlens_h, int B,
+                      int G, int32_t* idx_out, void* hidden_out, int32_t* pos_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 4. Drop composition  ([UP] "propagation" paragraph: a drop carries into every
+ *    later layer; [UP] "scheduler" paragraph: the drop history maps survivors to
+ *    their original positions)
+ *
+ *   orig_out[r] = prev_orig[idx[r]]   for r < *count
+ * prev_orig : int32 [prev_len], the original index of every row of the previous
+ *             layer's input (the identity at the first decision).
+ * idx       : int32 [capacity], e.g. idx_out of up_expand_compact.
+ * count     : device int32 scalar, e.g. &cu_seqlens_out[B]; must be <= capacity.
+ * Rows with idx outside [0, prev_len), or a count above capacity, raise the device
+ * error word; such rows get -1.
+ * ------------------------------------------------------------------------- */
+int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
+                     const int32_t* count, int capacity, int32_t* orig_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics (not on the hot path)
+ * ------------------------------------------------------------------------- */
+
+/* Device error word: bit 1 = cu_seqlens inconsistent with the host copy,
+ * bit 2 = index out of range in up_compose_drops, bit 4 = count above capacity.
+ * Synchronises `stream`, copies the word to *code_h and clears it. */
+int up_device_error(int32_t* code_h, void* stream);
+
+/* Kernel timing with HIP events recorded by the library on the launch stream.
+ * up_profile_enable(1) starts recording an event pair around every kernel the
+ * library launches; up_profile_read() synchronises the recorded events and
+ * returns, for kernel family `which` (0 score partials, 1 row statistics,
+ * 2 block masses, 3 normalise, 4 select, 5 select finalise, 6 block
+ * destinations, 7 gather, 8 compose, 9 plan), the number of launches and their
+ * summed duration in milliseconds; up_profile_reset() forgets them.
+ * up_profile_enable(0) stops recording.  Not thread safe. */
+int up_profile_enable(int on);
+int up_profile_read(int which, int* launches_h, double* total_ms_h);
+int up_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UNIPREFILL_H */

@@ -244,6 +244,35 @@ def topp_request(scores: np.ndarray, L: int, n: int, G: int, p: float):
                       kstar=kstar, p64=p64)
 
 
+def topk_request(scores: np.ndarray, L: int, n: int, G: int, k: int):
+    """Fixed-count alternative from the [UP] ablation paragraph: the k highest-scoring
+    blocks (same order and tie rule as Top-p), plus the window blocks."""
+    nb = n_blocks(L, G)
+    s = np.asarray(scores, dtype=np.float32)
+    order = sorted(range(nb), key=lambda b: (-float(s[b]), b))
+    keep = np.zeros(nb, dtype=bool)
+    for b in order[:min(k, nb)]:
+        keep[b] = True
+    for b in window_blocks(L, n, G):
+        keep[b] = True
+    return keep
+
+
+def topk_select(scores: np.ndarray, cu_seqlens: np.ndarray, n: int, G: int, k: int):
+    """Top-k over a packed batch: (keep uint8 [NB_tot], cu_seqlens_out int32 [B+1])."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    keeps, out, boff = [], np.zeros(cu.size, dtype=np.int32), 0
+    for i in range(cu.size - 1):
+        L = int(cu[i + 1] - cu[i])
+        nb = n_blocks(L, G)
+        keep = topk_request(scores[boff:boff + nb], L, n, G, k)
+        boff += nb
+        out[i + 1] = out[i] + sum(min((b + 1) * G, L) - b * G for b in range(nb) if keep[b])
+        keeps.append(keep)
+    keep_all = np.concatenate(keeps).astype(np.uint8) if keeps else np.zeros(0, np.uint8)
+    return keep_all, out
+
+
 def topp_select(scores: np.ndarray, cu_seqlens: np.ndarray, n: int, G: int, p: float):
     """Top-p over a packed batch; each request independently ([UPA]).
 

@@ -1,0 +1,145 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes workspaces on the host, and rejects bad arguments with the
+documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uniprefill.h")
+
+UP_OK, UP_EINVAL, UP_EUNSUPPORTED, UP_EWORKSPACE = 0, -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def L():
+    from block_wise_token_amd import lib
+    return lib()
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(up_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    syms = _declared_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in include/uniprefill.h but not exported"
+
+
+def test_status_strings(L):
+    assert L.up_status_string(UP_OK) == b"UP_OK"
+    for st in (UP_EINVAL, UP_EUNSUPPORTED, UP_EWORKSPACE, -4):
+        assert L.up_status_string(st).startswith(b"UP_E")
+    assert L.up_abi_version() == 1
+
+
+def _cu(lengths):
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return cu
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def test_workspace_sizes(L):
+    cu = _cu([131072])
+    ws = L.up_block_scores_workspace(_p(cu), 1, 32, 8, 128, 128, 64)
+    # at least the per-(row, block) statistics: 2048 blocks x 4096 rows x 8 bytes
+    assert ws >= 2048 * 4096 * 8
+    assert ws % 256 == 0
+    assert L.up_block_scores_workspace(_p(cu), 1, 32, 7, 128, 128, 64) == 0     # Hq % Hkv
+    assert L.up_block_scores_workspace(_p(cu), 1, 32, 8, 96, 128, 64) == 0      # d unsupported
+    assert L.up_block_scores_workspace(_p(cu), 1, 32, 8, 128, 128, 16) == 0     # G unsupported
+    cw = L.up_expand_compact_workspace(_p(cu), 1, 64)
+    assert cw >= 3 * 2048 * 4
+    vl = _cu([8192, 0, 65536, 77])
+    assert L.up_block_scores_workspace(_p(vl), 4, 32, 8, 128, 128, 64) > 0
+    bad = np.array([0, 10, 5], np.int32)
+    assert L.up_expand_compact_workspace(_p(bad), 2, 64) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: validation fails first
+
+
+def test_block_scores_rejects_bad_arguments(L):
+    cu = _cu([4096])
+    f = L.up_block_scores
+
+    def call(cu_h=cu, B=1, Hq=8, Hkv=2, d=64, n=128, G=64, ws=FAKE, wsb=1 << 40, q=FAKE):
+        return f(q, FAKE, FAKE, _p(cu_h), B, Hq, Hkv, d, n, G, ctypes.c_float(0.0), FAKE, ws,
+                 ctypes.c_size_t(wsb), None)
+
+    assert call(Hkv=3) == UP_EINVAL
+    assert call(Hq=0) == UP_EINVAL
+    assert call(n=0) == UP_EINVAL
+    assert call(d=80) == UP_EUNSUPPORTED
+    assert call(G=48) == UP_EUNSUPPORTED
+    assert call(G=2048) == UP_EUNSUPPORTED
+    assert call(cu_h=np.array([0, 5, 3], np.int32), B=2) == UP_EINVAL
+    assert call(cu_h=np.array([1, 5], np.int32)) == UP_EINVAL
+    assert call(q=None) == UP_EINVAL
+    assert call(q=ctypes.c_void_p(0x100002)) == UP_EINVAL           # qwin not 16-byte aligned
+    assert call(wsb=16) == UP_EWORKSPACE
+    assert call(ws=None) == UP_EWORKSPACE
+    assert call(ws=ctypes.c_void_p(0x100010)) == UP_EWORKSPACE      # not 256-byte aligned
+    # nothing to do is not an error
+    assert call(cu_h=np.array([0], np.int32), B=0) == UP_OK
+    assert call(cu_h=np.array([0, 0, 0], np.int32), B=2) == UP_OK
+
+
+def test_select_rejects_bad_arguments(L):
+    cu = _cu([4096])
+    for p in (0.0, -0.5, 1.5, float("nan")):
+        assert L.up_topp_select(FAKE, FAKE, _p(cu), 1, 128, 64, ctypes.c_float(p), FAKE, FAKE,
+                                None) == UP_EINVAL
+    assert L.up_topk_select(FAKE, FAKE, _p(cu), 1, 128, 64, -1, FAKE, FAKE, None) == UP_EINVAL
+    assert L.up_topp_select(FAKE, FAKE, _p(cu), 1, 0, 64, ctypes.c_float(0.9), FAKE, FAKE,
+                            None) == UP_EINVAL
+    assert L.up_topp_select(FAKE, FAKE, _p(cu), 1, 128, 64, ctypes.c_float(0.9), FAKE, None,
+                            None) == UP_EINVAL
+    huge = _cu([64 * 8192 + 1])                                        # 8193 blocks
+    assert L.up_topp_select(FAKE, FAKE, _p(huge), 1, 128, 64, ctypes.c_float(0.9), FAKE, FAKE,
+                            None) == UP_EUNSUPPORTED
+    assert L.up_topp_select(FAKE, FAKE, _p(np.array([0, 3, 2], np.int32)), 2, 128, 64,
+                            ctypes.c_float(0.9), FAKE, FAKE, None) == UP_EINVAL
+
+
+def test_expand_compact_and_compose_reject_bad_arguments(L):
+    cu = _cu([4096])
+    f = L.up_expand_compact
+
+    def call(H=1024, eb=2, ws=FAKE, wsb=1 << 30, hidden=FAKE, pos=FAKE, pos_out=FAKE, G=64):
+        return f(hidden, H, eb, pos, FAKE, FAKE, FAKE, _p(cu), 1, G, FAKE, FAKE, pos_out, ws,
+                 ctypes.c_size_t(wsb), None)
+
+    assert call(H=0) == UP_EINVAL
+    assert call(eb=0) == UP_EINVAL
+    assert call(G=0) == UP_EINVAL
+    assert call(hidden=None) == UP_EINVAL
+    assert call(pos=None) == UP_EINVAL          # pos_out requested without pos
+    assert call(wsb=8) == UP_EWORKSPACE
+    assert call(ws=None) == UP_EWORKSPACE
+    g = L.up_compose_drops
+    assert g(FAKE, 10, FAKE, FAKE, -1, FAKE, None) == UP_EINVAL
+    assert g(FAKE, -1, FAKE, FAKE, 4, FAKE, None) == UP_EINVAL
+    assert g(FAKE, 10, None, FAKE, 4, FAKE, None) == UP_EINVAL
+    assert g(None, 0, None, None, 0, None, None) == UP_OK                # empty: nothing to do
+
+
+def test_no_cpu_fallback_in_the_product_path():
+    """The binding has no route to the oracle or any CPU implementation."""
+    pkg = os.path.join(ROOT, "block_wise_token_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in src, fn
+            assert "uniprefill_oracle" not in src, fn

@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on seeded inputs.
+
+Every test prints the case it is about to run (config, seed, shape) before its GPU
+step.  Tolerances: see tests/gpu_helpers.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_wise_token_amd as up
+from oracle import uniprefill_oracle as O
+from workloads import synth
+from tests.gpu_helpers import (GpuBatch, ambiguous_blocks, bf16_dev, check_compaction, check_keep,
+                               check_scores, i32_dev, run_decision, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _batch(lengths, Hq, Hkv, d, n, G, needles=2, seed=0, recency=0):
+    reqs = [synth.gen_request(L, Hq, Hkv, d, n, G, needles,
+                              np.random.default_rng([seed, synth.TAG_VARLEN_REQUEST, i]),
+                              recency=recency)
+            for i, L in enumerate(lengths)]
+    return synth.pack(reqs, Hq, Hkv, d, n, G)
+
+
+def _full_check(batch, p, H=None, sample_rows=None, topk=None, label=""):
+    say(f"[case] {label} B={batch.B} T={batch.T} Hq={batch.Hq} Hkv={batch.Hkv} d={batch.d} "
+        f"n={batch.n} G={batch.G} p={p} topk={topk} H={H}")
+    gb = GpuBatch(batch, H=H)
+    res = run_decision(gb, p, topk=topk)
+    s32, s64, _ = O.block_scores(batch.qwin, batch.k, batch.cu_seqlens, batch.Hq, batch.Hkv,
+                                 batch.d, batch.n, batch.G)
+    worst = check_scores(res["scores"], s64)
+    if topk is None:
+        ref_keep, ref_cu, _ = O.topp_select(s32, batch.cu_seqlens, batch.n, batch.G, p)
+        amb = ambiguous_blocks(s32, batch.cu_seqlens, batch.n, batch.G, p)
+        ndiff = check_keep(res["keep"], ref_keep, amb)
+        # the GPU's cut is exactly the oracle's cut applied to the GPU's own scores
+        own_keep, own_cu, _ = O.topp_select(res["scores"], batch.cu_seqlens, batch.n, batch.G, p)
+    else:
+        ref_keep, ref_cu = O.topk_select(s32, batch.cu_seqlens, batch.n, batch.G, topk)
+        amb = set()
+        ndiff = int(np.sum(res["keep"] != ref_keep))
+        own_keep, own_cu = O.topk_select(res["scores"], batch.cu_seqlens, batch.n, batch.G, topk)
+    np.testing.assert_array_equal(res["keep"], own_keep)
+    np.testing.assert_array_equal(res["cu_out"], own_cu)
+    check_compaction(gb, res, sample_rows=sample_rows)
+    say(f"[ok] {label} worst score rel err {worst:.2e}; ambiguous {len(amb)}, differing {ndiff}; "
+        f"kept {res['count']}/{batch.T}")
+    return res, gb
+
+
+SMALL_CASES = [
+    # lengths, Hq, Hkv, d, n, G, p
+    ([4096], 8, 2, 64, 128, 64, 0.99),            # the small single-request workload's shape
+    ([1000], 4, 2, 64, 128, 64, 0.9),             # ragged last block
+    ([300], 8, 2, 128, 128, 32, 0.95),            # G = 32: one 32-key stage per block
+    ([2000], 4, 2, 256, 128, 64, 0.99),           # d = 256
+    ([777], 4, 4, 128, 128, 128, 0.8),            # MHA (Hq = Hkv), G = 128
+    ([1500], 8, 1, 64, 64, 96, 0.9),              # MQA, G = 96 (multiple of 32, not of 64)
+    ([50], 4, 2, 64, 128, 64, 0.5),               # L < n: everything kept
+    ([1], 4, 2, 128, 128, 64, 0.99),              # a single token
+    ([129, 0, 3000, 64, 1], 8, 2, 128, 128, 64, 0.97),   # varlen with an empty request
+    ([5000], 16, 2, 128, 256, 64, 0.99),          # 8-query groups, n = 256: two row tiles
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[f"c{i}" for i in range(len(SMALL_CASES))])
+def test_small_cases_match_oracle(case):
+    lengths, Hq, Hkv, d, n, G, p = case
+    batch = _batch(lengths, Hq, Hkv, d, n, G, needles=2, seed=len(lengths) * 131 + d)
+    _full_check(batch, p, H=256, label=f"small {case}")
+
+
+def test_single_4k_workload():
+    cfg = synth.WORKLOADS["single_4k_h8_d64"]
+    _full_check(synth.make_batch(cfg), cfg["p"], H=cfg["H"], label="single_4k_h8_d64")
+
+
+@pytest.mark.parametrize("p", [0.95, 0.99, 0.999, 1.0])
+def test_llama_32k_workload(p):
+    cfg = synth.WORKLOADS["llama31_8b_32k"]
+    _full_check(synth.make_batch(cfg), p, H=cfg["H"], sample_rows=4096,
+                label=f"llama31_8b_32k p={p}")
+
+
+def test_topk_matches_oracle():
+    cfg = synth.WORKLOADS["llama31_8b_32k"]
+    for k in (1, 100, 511, 4096):
+        _full_check(synth.make_batch(cfg), 0.99, H=None, topk=k, label=f"topk k={k}")
+
+
+def test_select_is_bit_exact_on_oracle_scores():
+    """Given identical float32 scores the GPU cut equals the oracle's exactly,
+    including exact ties (zero queries) and p = 1."""
+    rng = np.random.default_rng(8)
+    cases = []
+    lens = [4096, 700, 1, 0, 12000]
+    cu = np.zeros(len(lens) + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    nbt = sum(O.n_blocks(L, 64) for L in lens)
+    s = np.concatenate([rng.dirichlet(np.full(O.n_blocks(L, 64), 0.3)).astype(np.float32)
+                        for L in lens if L > 0])
+    cases.append((s, cu, "dirichlet"))
+    # exact ties everywhere: the zero-query closed form
+    qb = np.zeros((128, 2, 8), np.uint16)
+    kb = synth.f32_to_bf16_bits(rng.standard_normal((4096, 1, 8), dtype=np.float32))
+    cu1 = np.array([0, 4096], np.int32)
+    s1, _, _ = O.block_scores(qb, kb, cu1, 2, 1, 8, 128, 64)
+    cases.append((s1, cu1, "ties"))
+    for s, c, name in cases:
+        for p in (1e-6, 0.3, 0.9, 0.95, 0.99, 0.999, 1.0):
+            say(f"[case] select {name} p={p} nb={s.size}")
+            keep, cu_out = up.topp_select(torch.from_numpy(s).cuda(), i32_dev(c), c, 128, 64, p)
+            torch.cuda.synchronize()
+            ref_keep, ref_cu, _ = O.topp_select(s, c, 128, 64, p)
+            np.testing.assert_array_equal(keep.cpu().numpy(), ref_keep)
+            np.testing.assert_array_equal(cu_out.cpu().numpy(), ref_cu)
+    # exact boundaries: a running sum equal to p counts as reaching it
+    s = np.array([0.5, 0.25, 0.125, 0.125], np.float32)
+    c = np.array([0, 4 * 64], np.int32)
+    for p in (0.5, 0.75, 0.875, 0.8750001):
+        keep, _ = up.topp_select(torch.from_numpy(s).cuda(), i32_dev(c), c, 1, 64, p)
+        ref_keep, _, _ = O.topp_select(s, c, 1, 64, p)
+        np.testing.assert_array_equal(keep.cpu().numpy(), ref_keep)
+    assert up.device_error() == 0
+
+
+def test_zero_queries_give_exact_ties_on_gpu():
+    """Q = 0: early blocks must get bit-identical scores and the cut the closed form's k*."""
+    L, n, G, Hq, p = 4096, 128, 64, 2, 0.95
+    qb = np.zeros((n, Hq, 128), np.uint16)
+    rng = np.random.default_rng(3)
+    kb = synth.f32_to_bf16_bits(rng.standard_normal((L, 1, 128), dtype=np.float32))
+    batch = synth.Batch(cu_seqlens=np.array([0, L], np.int32), qwin=qb, k=kb, Hq=Hq, Hkv=1,
+                        d=128, n=n, G=G)
+    say("[case] zero queries L=4096 d=128")
+    gb = GpuBatch(batch, H=64)
+    res = run_decision(gb, p)
+    s = res["scores"]
+    early = [b for b in range(L // G) if (b + 1) * G - 1 <= L - n]
+    assert len({float(s[b]) for b in early}) == 1
+    s32, s64, _ = O.block_scores(qb, kb, batch.cu_seqlens, Hq, 1, 128, n, G)
+    check_scores(s, s64)
+    ref_keep, _, _ = O.topp_select(s32, batch.cu_seqlens, n, G, p)
+    np.testing.assert_array_equal(res["keep"], ref_keep)
+    check_compaction(gb, res)
+
+
+def test_runs_are_bitwise_reproducible():
+    cfg = synth.WORKLOADS["single_4k_h8_d64"]
+    batch = synth.make_batch(cfg)
+    say("[case] determinism single_4k_h8_d64")
+    gb = GpuBatch(batch, H=cfg["H"])
+    a = run_decision(gb, cfg["p"])
+    b = run_decision(gb, cfg["p"])
+    assert np.array_equal(a["scores"].view(np.uint32), b["scores"].view(np.uint32))
+    assert np.array_equal(a["keep"], b["keep"])
+    assert torch.equal(a["dec"].hidden_out, b["dec"].hidden_out)
+
+
+def test_inconsistent_device_cu_seqlens_raises_error_word():
+    """Device cu_seqlens disagreeing with the host copy: kernels do nothing, error bit 1."""
+    cfg = synth.WORKLOADS["single_4k_h8_d64"]
+    batch = synth.make_batch(cfg)
+    gb = GpuBatch(batch, H=cfg["H"])
+    say("[case] inconsistent cu_seqlens")
+    up.device_error()
+    bad_cu = i32_dev(np.array([0, 4000], np.int32))
+    scores = torch.full((64,), -7.0, device="cuda")
+    up.block_scores(gb.qwin, gb.k, bad_cu, gb.cu_h, batch.n, batch.G, out=scores)
+    torch.cuda.synchronize()
+    assert up.device_error() & 1
+    assert torch.all(scores == -7.0)
+    # compose: out-of-range indices give -1 and raise bit 2
+    prev = i32_dev(np.arange(10, dtype=np.int32))
+    idx = i32_dev(np.array([0, 9, 10, -1], np.int32))
+    cnt = i32_dev(np.array([4], np.int32))
+    out = up.compose_drops(prev, idx, cnt)
+    torch.cuda.synchronize()
+    assert out.cpu().numpy().tolist() == [0, 9, -1, -1]
+    assert up.device_error() & 2

@@ -405,3 +405,18 @@ def test_generator_is_seeded():
     bits = synth.f32_to_bf16_bits(x)
     back = O.bf16_bits_to_f64(bits)
     np.testing.assert_array_equal(back, [1.0, 1.0, 1.0 + 2**-6, 1.0, -2.5])
+
+
+def test_topk_keeps_the_k_best_and_the_window():
+    rng = np.random.default_rng(31)
+    nb = 50
+    s = rng.dirichlet(np.full(nb, 0.4)).astype(np.float32)
+    L, G, n = nb * 64 - 10, 64, 128
+    for k in (0, 1, 7, nb, nb + 5):
+        keep = O.topk_request(s, L, n, G, k)
+        top = set(np.argsort(-s.astype(np.float64), kind="stable")[:min(k, nb)].tolist())
+        assert set(np.nonzero(keep)[0].tolist()) == top | set(O.window_blocks(L, n, G))
+    cu = np.array([0, L, L + 100], np.int32)
+    s2 = np.concatenate([s, np.array([0.5, 0.5], np.float32)])
+    keep, cu_out = O.topk_select(s2, cu, n, G, 3)
+    assert cu_out[-1] - cu_out[-2] == 100           # a short request keeps everything

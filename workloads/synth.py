@@ -31,11 +31,16 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
     For finite inputs the rounding add cannot overflow 32 bits (the largest
     finite pattern is 0xFF7FFFFF), so uint32 arithmetic is exact."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    x = np.ascontiguousarray(x, dtype=np.float32)
     if not np.isfinite(x).all():
         raise ValueError("bf16 rounding expects finite values")
-    u = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-    return (u >> np.uint32(16)).astype(np.uint16)
+    u = x.view(np.uint32)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= np.uint32(16)
+    return t.astype(np.uint16)
 
 
 def _unit_query_direction(q: np.ndarray, Hkv: int) -> np.ndarray:
@@ -63,40 +68,58 @@ class Request:
     sink: bool = True
 
 
+CHUNK_ELEMS = 1 << 20   # values drawn, biased and rounded per step (keeps temporaries small)
+
+
 def gen_request(L: int, Hq: int, Hkv: int, d: int, n: int, G: int,
                 n_needles: int, rng: np.random.Generator,
                 recency: int = 0) -> Request:
     """Sink/needle generator.
 
-    Draw order: window queries [W, Hq, d], keys [L, Hkv, d], then the needle
-    blocks.  With u_g the unit direction of kv head g's window queries:
+    Draw order: window queries [W, Hq, d], the needle blocks, then the keys
+    [L, Hkv, d] in row order.  With u_g the unit direction of kv head g's window
+    queries:
       * key 0 (the sink) gets + 4 sqrt(d) u_g,
       * every key of each needle block gets + 2 sqrt(d) u_g,
       * when ``recency`` > 0, the last ``recency`` keys get + 0.5 sqrt(d) u_g,
-    and only then are the keys rounded to bfloat16.
+    and only then are the keys rounded to bfloat16.  Keys are drawn in chunks of
+    rows; the stream of draws is the same as one draw of the whole array.
     """
     W = min(n, L)
     q = rng.standard_normal((W, Hq, d), dtype=np.float32)
-    k = rng.standard_normal((L, Hkv, d), dtype=np.float32)
-    u = _unit_query_direction(q, Hkv)
+    u = _unit_query_direction(q, Hkv) if W > 0 else np.zeros((Hkv, d), np.float32)
     sd = np.float32(np.sqrt(d))
-    k[0] += np.float32(4.0) * sd * u
     cand = needle_candidates(L, n, G)
     m = min(n_needles, cand.size)
     needles = np.sort(rng.choice(cand, size=m, replace=False)) if m else cand[:0]
-    for b in needles:
-        k[b * G:(b + 1) * G] += np.float32(2.0) * sd * u
-    if recency > 0:
-        k[max(0, L - recency):] += np.float32(0.5) * sd * u
-    return Request(L=L, qwin=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), needles=needles)
+    is_needle = np.zeros((L + G - 1) // G, dtype=bool)
+    is_needle[needles] = True
+    kb = np.empty((L, Hkv, d), dtype=np.uint16)
+    rows_per = max(1, CHUNK_ELEMS // (Hkv * d))
+    for r0 in range(0, L, rows_per):
+        r1 = min(L, r0 + rows_per)
+        kc = rng.standard_normal((r1 - r0, Hkv, d), dtype=np.float32)
+        if r0 == 0:
+            kc[0] += np.float32(4.0) * sd * u
+        rows = np.arange(r0, r1)
+        nrow = is_needle[rows // G]
+        if nrow.any():
+            kc[nrow] += np.float32(2.0) * sd * u
+        if recency > 0:
+            rec = rows >= L - recency
+            if rec.any():
+                kc[rec] += np.float32(0.5) * sd * u
+        kb[r0:r1] = f32_to_bf16_bits(kc)
+    return Request(L=L, qwin=f32_to_bf16_bits(q), k=kb, needles=needles)
 
 
-def gen_hidden(T: int, H: int, seed: int, chunk_rows: int = 8192) -> np.ndarray:
+def gen_hidden(T: int, H: int, seed: int) -> np.ndarray:
     """Hidden states [T, H] as bfloat16 bits, drawn N(0,1) from default_rng(seed + 1)."""
     rng = np.random.default_rng(seed + 1)
     out = np.empty((T, H), dtype=np.uint16)
-    for r0 in range(0, T, chunk_rows):
-        r1 = min(T, r0 + chunk_rows)
+    rows_per = max(1, CHUNK_ELEMS // max(1, H))
+    for r0 in range(0, T, rows_per):
+        r1 = min(T, r0 + rows_per)
         out[r0:r1] = f32_to_bf16_bits(rng.standard_normal((r1 - r0, H), dtype=np.float32))
     return out
 
@@ -207,10 +230,19 @@ def gen_layer(orig: np.ndarray, L0: int, needles: np.ndarray, Hq: int, Hkv: int,
     L = int(orig.size)
     W = min(n, L)
     q = rng.standard_normal((W, Hq, d), dtype=np.float32)
-    k = rng.standard_normal((L, Hkv, d), dtype=np.float32)
-    u = _unit_query_direction(q, Hkv)
+    u = _unit_query_direction(q, Hkv) if W > 0 else np.zeros((Hkv, d), np.float32)
     sd = np.float32(np.sqrt(d))
-    k[orig == 0] += np.float32(4.0) * sd * u
-    is_needle = np.isin(orig // G, needles)
-    k[is_needle] += np.float32(2.0) * sd * u
-    return Request(L=L, qwin=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), needles=needles)
+    is_needle = np.zeros((L0 + G - 1) // G, dtype=bool)
+    is_needle[needles] = True
+    kb = np.empty((L, Hkv, d), dtype=np.uint16)
+    rows_per = max(1, CHUNK_ELEMS // (Hkv * d))
+    for r0 in range(0, L, rows_per):
+        r1 = min(L, r0 + rows_per)
+        kc = rng.standard_normal((r1 - r0, Hkv, d), dtype=np.float32)
+        o = orig[r0:r1]
+        kc[o == 0] += np.float32(4.0) * sd * u
+        nrow = is_needle[o // G]
+        if nrow.any():
+            kc[nrow] += np.float32(2.0) * sd * u
+        kb[r0:r1] = f32_to_bf16_bits(kc)
+    return Request(L=L, qwin=f32_to_bf16_bits(q), k=kb, needles=needles)
