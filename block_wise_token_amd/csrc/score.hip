@@ -96,23 +96,46 @@ __global__ void up_score_plan_kernel(const int32_t* __restrict__ cu, ScoreShape 
 //
 // Workgroup = 8 waves = one (request, kv head g, query-row tile, key chunk).
 // Each wave holds QT tiles of 32 query rows of kv head g's group in VGPRs as the B
-// operand (rows r = j * gs + hh: window row j, head g*gs + hh).  Key tiles of
-// UK = 32*KT keys are staged through LDS (double-buffered, padded rows) and read as
-// the A operand, so S^T = K Q^T lands with one query per lane column: lane l and
-// lane l^32 together hold all keys of a tile for query l%32, and the per-query
-// max and sum over a block are in-lane reductions plus one cross-half exchange.
+// operand (rows r = j * gs + hh: window row j, head g*gs + hh).  Keys are staged
+// through LDS in stages of 32*HPS keys (double-buffered, padded rows; each stage's
+// global loads are issued two stages ahead) and read as the A operand, so
+// S^T = K Q^T lands with one query per lane column: lane l and lane l^32 together
+// hold the 32 keys of a half-stage for query l%32.
+//
+// The keys are processed in halves of 32.  The MFMAs of half h+1 are interleaved
+// (scheduling groups) with the exp/sum work of half h, on two accumulator sets.
+//
+// Softmax statistics per lane: a running reference Rs (log2 units) and the sums
+// l = sum 2^(x - Rs) over the lane's keys of the current block and chunk.  Any
+// reference gives the same (reference, sum) value, so there is no per-block max
+// pass: a half whose sum leaves [0, 2^64] (overflow, or NaN from an unset
+// reference) is redone against its own maximum and the earlier sums rescaled.
+// At a block end the two lanes of a query combine their pairs and one of them
+// stores (m_b, l_b); the chunk sums are combined and stored at the chunk end.
 //
 // The head dimension is contracted in a permuted order that both operands share:
 // lane half h, k-step s holds d-elements [h*D/2 + 8s, h*D/2 + 8s + 8), so every
 // lane reads one contiguous D-byte run per row.
 // ---------------------------------------------------------------------------
-template <int D, int QT, int KT>
+
+// Combine two (reference, sum) pairs of the same quantity into one.
+__device__ __forceinline__ void combine_pair(float m1, float l1, float m2, float l2, float& m,
+                                             float& l) {
+  if (m1 == m2) { m = m1; l = l1 + l2; return; }   // common case, exact
+  m = fmaxf(m1, m2);
+  if (m == kNegInf) { l = 0.f; return; }
+  l = l1 * fast_exp2(m1 - m) + l2 * fast_exp2(m2 - m);
+}
+
+constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
+
+template <int D, int QT, int HPS>
 __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     const uint16_t* __restrict__ qwin, const uint16_t* __restrict__ kmat,
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
     int G, int CB, float c, float2* __restrict__ ml, float2* __restrict__ cs) {
   constexpr int NT = 512;
-  constexpr int UK = KT * 32;          // keys per LDS stage
+  constexpr int UK = 32 * HPS;         // keys per LDS stage
   constexpr int RS = 2 * D + 16;       // LDS bytes per key row (16 B pad against bank conflicts)
   constexpr int SEGS = UK * D / 8;     // 16-byte segments per stage
   constexpr int SPT = (SEGS + NT - 1) / NT;
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     } else {
 #pragma unroll
       for (int s = 0; s < DS; ++s) qreg[t][s] = bf16x8{};
-      qpos[t] = -1;   // inactive row: every key masked in masked stages, never stored
+      qpos[t] = -1;   // inactive row: every key masked in masked halves, never stored
     }
   }
 
@@ -162,127 +185,222 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
   const int b1 = min(pr.nb, b0 + CB);
   const int k0 = b0 * G;
   const int kend = min(b1 * G, pr.L);
-  const int nunits = (kend - k0 + UK - 1) / UK;
-  const int upb = G / UK;
+  const int nh = (kend - k0 + 31) / 32;          // 32-key halves in this chunk
+  const int nst = (nh + HPS - 1) / HPS;          // LDS stages
   const int64_t kstride = (int64_t)Hkv * D;
   const uint16_t* kbase = kmat + ((int64_t)pr.tok_off * Hkv + g) * D;
   const int fast_limit = pr.L - pr.W;   // keys <= this are visible to every window row
 
-  uint4 pre[SPT];
-  auto gload = [&](int u) {
-    const int ks = k0 + u * UK;
+  uint4 pre0[SPT], pre1[SPT];   // stages of even / odd index
+  auto gload = [&](int st, uint4 (&regs)[SPT]) {
+    const int ks = k0 + st * UK;
 #pragma unroll
     for (int q = 0; q < SPT; ++q) {
       const int e = tid + q * NT;
       if (SEGS % NT == 0 || e < SEGS) {
         const int key = e / (D / 8), part = e % (D / 8);
         const int kabs = ks + key;
-        pre[q] = (kabs < pr.L)
-                     ? *reinterpret_cast<const uint4*>(kbase + (int64_t)kabs * kstride + part * 8)
-                     : make_uint4(0, 0, 0, 0);
+        regs[q] = (kabs < pr.L)
+                      ? *reinterpret_cast<const uint4*>(kbase + (int64_t)kabs * kstride + part * 8)
+                      : make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const uint4 (&regs)[SPT]) {
 #pragma unroll
     for (int q = 0; q < SPT; ++q) {
       const int e = tid + q * NT;
       if (SEGS % NT == 0 || e < SEGS) {
         const int key = e / (D / 8), part = e % (D / 8);
-        *reinterpret_cast<uint4*>(lds + buf * UK * RS + key * RS + part * 16) = pre[q];
+        *reinterpret_cast<uint4*>(lds + buf * UK * RS + key * RS + part * 16) = regs[q];
       }
     }
   };
 
-  float mb[QT], lb[QT], Mc[QT], Lc[QT];
+  // Per-lane softmax state (both lanes of a query keep their own).
+  float Rs[QT], lblk[QT], Lch[QT];
 #pragma unroll
-  for (int t = 0; t < QT; ++t) { mb[t] = kNegInf; lb[t] = 0.f; Mc[t] = kNegInf; Lc[t] = 0.f; }
-
+  for (int t = 0; t < QT; ++t) { Rs[t] = kNegInf; lblk[t] = 0.f; Lch[t] = 0.f; }
   const int t_st = (QT == 2) ? half : 0;          // the tile this lane stores
   const int r_st = row0 + t_st * 32 + l32;
   const bool st_ok = (QT == 2 || half == 0) && (r_st < R);
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  f32x16 acc0[QT], acc1[QT];
 
-  for (int u = 0; u < nunits; ++u) {
-    if (u + 1 < nunits) gload(u + 1);
-    const uint8_t* kb = lds + (u & 1) * UK * RS;
-    f32x16 acc[KT][QT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int t = 0; t < QT; ++t) acc[kt][t] = f32x16{};
+  // MFMAs of half h into acc.
+  auto mfma_half = [&](int h, f32x16 (&acc)[QT]) {
+    const int st = h / HPS, hh = h % HPS;
+    const uint8_t* kb = lds + (st & 1) * UK * RS + (hh * 32 + l32) * RS + half * D;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + s * 16);
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(kb + (kt * 32 + l32) * RS + half * D + s * 16);
-#pragma unroll
-        for (int t = 0; t < QT; ++t)
-          acc[kt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][s], acc[kt][t], 0, 0, 0);
-      }
+      for (int t = 0; t < QT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][s], s == 0 ? f32x16{} : acc[t],
+                                                         0, 0, 0);
     }
+  };
 
-    const int ks = k0 + u * UK;
-    const bool masked = (ks + UK - 1 > fast_limit);   // uniform across the workgroup
+  // Sum of 2^(x - Rs) over a lane's 16 values of half h (masked keys give 0).
+  auto half_sums = [&](f32x16 (&acc)[QT], float (&sum)[QT]) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      if (masked) {
+      float a0 = 0.f, a1 = 0.f;   // same order as the interleaved path: even / odd elements
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            // 32x32 MFMA result layout: register e of lane l holds row
-            // 8*(e/4) + 4*(l/32) + e%4 (the key) and column l%32 (the query).
-            const int key = ks + kt * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (key > qpos[t]) acc[kt][t][e] = kNegInf;
-          }
+      for (int e = 0; e < 16; e += 2) {
+        a0 += fast_exp2(fmaf(acc[t][e], c, -Rs[t]));
+        a1 += fast_exp2(fmaf(acc[t][e + 1], c, -Rs[t]));
       }
-      float mx = kNegInf;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[kt][t][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m = mx * c;                          // exact max of the scaled logits
-      const float msub = (mx == kNegInf) ? 0.f : m;    // all masked: every term is 2^-inf = 0
-      float sum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(acc[kt][t][e], c, -msub));
-      sum += __shfl_xor(sum, 32);                      // same value on both halves
-      merge_ml(mb[t], lb[t], m, sum);
+      sum[t] = a0 + a1;
     }
+  };
 
-    const int uu = (ks - k0) / UK;                     // stage index within the chunk
-    const bool block_end = (uu % upb == upb - 1) || (u == nunits - 1);
-    if (block_end) {
-      const int bl = b0 + uu / upb;                    // request-local block
-      if (st_ok) {
-        const float mv = (QT == 2 && t_st) ? mb[QT - 1] : mb[0];
-        const float lv = (QT == 2 && t_st) ? lb[QT - 1] : lb[0];
-        ml[pr.ml_off + ((int64_t)bl * Hkv + g) * R + r_st] = make_float2(mv, lv);
+  // Apply the causal mask to half h's values (keys past a row's position -> -inf).
+  auto mask_half = [&](int h, f32x16 (&acc)[QT]) {
+    const int key0 = k0 + h * 32;
+#pragma unroll
+    for (int t = 0; t < QT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        // 32x32 MFMA result layout: register e of lane l holds row
+        // 8*(e/4) + 4*(l/32) + e%4 (the key) and column l%32 (the query).
+        const int key = key0 + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (key > qpos[t]) acc[t][e] = kNegInf;
       }
+  };
+
+  // Accumulate half h's sums; redo a half whose sum is out of range; handle block ends.
+  auto finish_half = [&](int h, f32x16 (&acc)[QT], float (&sum)[QT]) {
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      float nl = lblk[t] + sum[t];
+      if (!(nl <= kSumLimit)) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[t][e]);
+        if (mx == kNegInf) {
+          nl = lblk[t];                    // no visible key in this half
+        } else {
+          const float rn = fmaxf(Rs[t], mx * c);
+          const float sc = fast_exp2(Rs[t] - rn);   // Rs = -inf gives 0 (sums were 0)
+          lblk[t] *= sc;
+          Lch[t] *= sc;
+          Rs[t] = rn;
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            a0 += fast_exp2(fmaf(acc[t][e], c, -rn));
+            a1 += fast_exp2(fmaf(acc[t][e + 1], c, -rn));
+          }
+          nl = lblk[t] + (a0 + a1);
+        }
+      }
+      lblk[t] = nl;
+    }
+    const int kh_end = k0 + (h + 1) * 32;
+    if (kh_end % G == 0 || h == nh - 1) {
+      const int bl = (k0 + h * 32) / G;   // request-local block
+      float mst = 0.f, lst = 0.f;
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
-        merge_ml(Mc[t], Lc[t], mb[t], lb[t]);
-        mb[t] = kNegInf;
-        lb[t] = 0.f;
+        const float mo = __shfl_xor(Rs[t], 32), lo = __shfl_xor(lblk[t], 32);
+        float m, l;
+        combine_pair(Rs[t], lblk[t], mo, lo, m, l);
+        if (t == t_st) { mst = m; lst = l; }
+        Lch[t] += lblk[t];
+        lblk[t] = 0.f;
       }
+      if (st_ok) ml[pr.ml_off + ((int64_t)bl * Hkv + g) * R + r_st] = make_float2(mst, lst);
     }
-    if (u + 1 < nunits) lstore((u + 1) & 1);
-    __syncthreads();
+  };
+
+  // One pipeline step: MFMAs of half h+1 (if any) interleaved with the sums of half h.
+  // `regs` holds the stage that half h+1 starts, when it starts one (its parity is
+  // static in the unrolled loop below).
+  auto step = [&](int h, f32x16 (&cur)[QT], f32x16 (&nxt)[QT], uint4 (&regs)[SPT]) {
+    const bool more = h + 1 < nh;
+    if (more && (h + 1) % HPS == 0) {
+      // entering stage (h+1)/HPS: publish it, then prefetch two stages ahead
+      const int st = (h + 1) / HPS;
+      lstore(st & 1, regs);
+      __syncthreads();
+      if (st + 2 <= nst - 1) gload(st + 2, regs);
+    }
+    const bool masked = (k0 + h * 32 + 31 > fast_limit);
+    float sum[QT];
+    if (!masked && more) {
+      // Interleaved: k-step s issues the LDS read for s+1, the MFMAs of half h+1
+      // for s, and 16/DS of each tile's exp-and-sum of half h.
+      constexpr int EPS = 16 / DS;   // elements per tile per k-step
+      const int st = (h + 1) / HPS, hh = (h + 1) % HPS;
+      const uint8_t* kb = lds + (st & 1) * UK * RS + (hh * 32 + l32) * RS + half * D;
+      float part[QT][2];
+#pragma unroll
+      for (int t = 0; t < QT; ++t) { part[t][0] = 0.f; part[t][1] = 0.f; }
+      bf16x8 a = *reinterpret_cast<const bf16x8*>(kb);
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks) {
+        bf16x8 an;
+        if (ks + 1 < DS) an = *reinterpret_cast<const bf16x8*>(kb + (ks + 1) * 16);
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+          nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][ks],
+                                                           ks == 0 ? f32x16{} : nxt[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+#pragma unroll
+          for (int q = 0; q < EPS; ++q) {
+            const int e = ks * EPS + q;
+            part[t][e & 1] += fast_exp2(fmaf(cur[t][e], c, -Rs[t]));
+          }
+        if (ks + 1 < DS) a = an;
+      }
+#pragma unroll
+      for (int t = 0; t < QT; ++t) sum[t] = part[t][0] + part[t][1];
+    } else {
+      if (more) mfma_half(h + 1, nxt);
+      if (masked) mask_half(h, cur);
+      half_sums(cur, sum);
+    }
+    finish_half(h, cur, sum);
+  };
+
+  // Prologue: stages 0 and 1 to registers, stage 0 to LDS, stage 2 prefetched.
+  gload(0, pre0);
+  if (nst > 1) gload(1, pre1);
+  lstore(0, pre0);
+  __syncthreads();
+  if (nst > 2) gload(2, pre0);
+  mfma_half(0, acc0);
+
+  if constexpr (HPS == 2) {
+    for (int h = 0; h < nh; h += 4) {   // halves h..h+3 = stages h/2 (even) and h/2+1 (odd)
+      step(h, acc0, acc1, pre1);
+      if (h + 1 >= nh) break;
+      step(h + 1, acc1, acc0, pre1);    // enters stage h/2+1 (odd)
+      if (h + 2 >= nh) break;
+      step(h + 2, acc0, acc1, pre0);
+      if (h + 3 >= nh) break;
+      step(h + 3, acc1, acc0, pre0);    // enters stage h/2+2 (even)
+    }
+  } else {
+    for (int h = 0; h < nh; h += 2) {
+      step(h, acc0, acc1, pre1);        // enters stage h+1 (odd)
+      if (h + 1 >= nh) break;
+      step(h + 1, acc1, acc0, pre0);    // enters stage h+2 (even)
+    }
   }
 
-  if (st_ok) {
-    const float mv = (QT == 2 && t_st) ? Mc[QT - 1] : Mc[0];
-    const float lv = (QT == 2 && t_st) ? Lc[QT - 1] : Lc[0];
-    cs[pr.cs_off + ((int64_t)ch * Hkv + g) * R + r_st] = make_float2(mv, lv);
+  // Chunk statistics: combine the two lanes of each query.
+  float mst = 0.f, lst = 0.f;
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const float mo = __shfl_xor(Rs[t], 32), lo = __shfl_xor(Lch[t], 32);
+    float m, l;
+    combine_pair(Rs[t], Lch[t], mo, lo, m, l);
+    if (t == t_st) { mst = m; lst = l; }
   }
+  if (st_ok) cs[pr.cs_off + ((int64_t)ch * Hkv + g) * R + r_st] = make_float2(mst, lst);
 }
 
 // ---------------------------------------------------------------------------
@@ -299,24 +417,36 @@ __device__ __forceinline__ int request_of_row(const ReqPlan* __restrict__ plan, 
   return lo;
 }
 
-__global__ __launch_bounds__(256) void up_row_stats_kernel(
+// Workgroup = 64 rows (one per lane) x 16 waves; wave w merges chunks w, w+16, ...
+// of its lane's row, then wave 0 merges the 16 partial results in wave order.
+__global__ __launch_bounds__(1024) void up_row_stats_kernel(
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
     const float2* __restrict__ cs, float2* __restrict__ rs, int64_t total_rows) {
+  __shared__ float2 part[16][64];
   if (hdr->valid != 1) return;
-  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (x >= total_rows) return;
-  const int i = request_of_row(plan, B, Hq, x);
-  if (i >= B) return;
-  const ReqPlan pr = plan[i];
-  const int R = (Hq / Hkv) * pr.W;
-  const int64_t local = x - (int64_t)pr.win_off * Hq;   // = g*R + r
-  const int g = (int)(local / R), r = (int)(local % R);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t x = (int64_t)blockIdx.x * 64 + lane;
   float M = kNegInf, S = 0.f;
-  for (int chk = 0; chk < pr.nch; ++chk) {
-    const float2 v = cs[pr.cs_off + ((int64_t)chk * Hkv + g) * R + r];
-    merge_ml(M, S, v.x, v.y);
+  if (x < total_rows) {
+    const int i = request_of_row(plan, B, Hq, x);
+    if (i < B) {
+      const ReqPlan pr = plan[i];
+      const int R = (Hq / Hkv) * pr.W;
+      const int64_t local = x - (int64_t)pr.win_off * Hq;   // = g*R + r
+      const int g = (int)(local / R), r = (int)(local % R);
+      for (int chk = wave; chk < pr.nch; chk += 16) {
+        const float2 v = cs[pr.cs_off + ((int64_t)chk * Hkv + g) * R + r];
+        merge_ml(M, S, v.x, v.y);
+      }
+    }
   }
-  rs[x] = make_float2(M, S);
+  part[wave][lane] = make_float2(M, S);
+  __syncthreads();
+  if (wave == 0 && x < total_rows) {
+    float Mt = kNegInf, St = 0.f;
+    for (int w = 0; w < 16; ++w) merge_ml(Mt, St, part[w][lane].x, part[w][lane].y);
+    rs[x] = make_float2(Mt, St);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -414,11 +544,11 @@ hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Total
   return hipGetLastError();
 }
 
-template <int D, int QT, int KT>
+template <int D, int QT, int HPS>
 static hipError_t launch_partial_t(const void* qwin, const void* k, const ScoreShape& s,
                                    const Totals& t, void* ws, const ScoreWs& L, float c,
                                    hipStream_t st) {
-  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, KT>), dim3((unsigned)t.items), dim3(512), 0,
+  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, HPS>), dim3((unsigned)t.items), dim3(512), 0,
                      st, static_cast<const uint16_t*>(qwin), static_cast<const uint16_t*>(k),
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq, s.Hkv, s.G,
@@ -431,13 +561,10 @@ hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShap
                                 const Totals& t, void* ws, const ScoreWs& L, float c,
                                 hipStream_t st) {
   if (t.items == 0) return hipSuccess;
-  const int key = s.d * 100 + s.qt * 10 + s.kt;
-  switch (key) {
-    case 6421: return launch_partial_t<64, 2, 1>(qwin, k, s, t, ws, L, c, st);
-    case 6422: return launch_partial_t<64, 2, 2>(qwin, k, s, t, ws, L, c, st);
-    case 12821: return launch_partial_t<128, 2, 1>(qwin, k, s, t, ws, L, c, st);
-    case 12822: return launch_partial_t<128, 2, 2>(qwin, k, s, t, ws, L, c, st);
-    case 25611: return launch_partial_t<256, 1, 1>(qwin, k, s, t, ws, L, c, st);
+  switch (s.d) {
+    case 64: return launch_partial_t<64, 2, 2>(qwin, k, s, t, ws, L, c, st);
+    case 128: return launch_partial_t<128, 2, 2>(qwin, k, s, t, ws, L, c, st);
+    case 256: return launch_partial_t<256, 1, 1>(qwin, k, s, t, ws, L, c, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -445,8 +572,8 @@ hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShap
 hipError_t launch_row_stats(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
                             hipStream_t st) {
   if (t.rows == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((t.rows + 255) / 256);
-  hipLaunchKernelGGL(up_row_stats_kernel, dim3(grid), dim3(256), 0, st,
+  const unsigned grid = (unsigned)((t.rows + 63) / 64);
+  hipLaunchKernelGGL(up_row_stats_kernel, dim3(grid), dim3(1024), 0, st,
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq, s.Hkv,
                      reinterpret_cast<const float2*>(wsb(ws) + L.cs),

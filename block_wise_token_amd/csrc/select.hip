@@ -122,32 +122,69 @@ __global__ __launch_bounds__(1024) void up_select_kernel(
   const int64_t W = L < n ? L : n;
   const int64_t wfirst = (L - W) / G;   // first block holding a window token
 
-  // Sort keys.
-  for (int e = tid; e < NP; e += kSelThreads) {
-    uint64_t key = ~0ull;
-    if (e < nb) {
-      const float s = clamp_score(scores[blk_off + e]);
-      key = ((uint64_t)(~__float_as_uint(s)) << 32) | (uint32_t)e;
-    }
-    keys[e] = key;
-  }
-  __syncthreads();
-  for (int k = 2; k <= NP; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int e = tid; e < NP / 2; e += kSelThreads) {
-        const int a = 2 * j * (e / j) + (e % j);
-        const int b = a + j;
-        const uint64_t ka = keys[a], kb = keys[b];
-        const bool up = (a & k) == 0;
-        if ((ka > kb) == up) { keys[a] = kb; keys[b] = ka; }
-      }
-      __syncthreads();
-    }
-  }
-
-  // Each thread owns PER consecutive sorted positions.
+  // Sort keys.  Element a of the bitonic network lives in thread a % 1024, slot
+  // a / 1024: partners at distance j >= 1024 are in the same thread, partners at
+  // 64 <= j < 1024 are exchanged through LDS, partners at j < 64 by wave shuffles.
   const int PER = NP >= kSelThreads ? NP / kSelThreads : 1;
   uint64_t kv[kSelMaxPer];
+#pragma unroll
+  for (int q = 0; q < kSelMaxPer; ++q) {
+    const int a = q * kSelThreads + tid;
+    uint64_t key = ~0ull;
+    if (q < PER && a < nb) {
+      const float s = clamp_score(scores[blk_off + a]);
+      key = ((uint64_t)(~__float_as_uint(s)) << 32) | (uint32_t)a;
+    }
+    kv[q] = key;
+  }
+  for (int k = 2; k <= NP; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= kSelThreads) {
+        const int jj = j / kSelThreads;
+        auto cx = [&](int q, int p) {   // q < p: slots q and p of this thread
+          const bool up = ((q * kSelThreads + tid) & k) == 0;
+          const uint64_t x = kv[q], y = kv[p];
+          if ((x > y) == up) { kv[q] = y; kv[p] = x; }
+        };
+#pragma unroll
+        for (int q = 0; q < kSelMaxPer; ++q) {
+          if (jj == 1 && !(q & 1) && q + 1 < PER) cx(q, q + 1);
+          if (jj == 2 && !(q & 2) && q + 2 < PER) cx(q, q + 2);
+          if (jj == 4 && !(q & 4) && q + 4 < PER) cx(q, q + 4);
+        }
+      } else {
+        uint64_t y[kSelMaxPer];
+        if (j >= 64) {
+#pragma unroll
+          for (int q = 0; q < kSelMaxPer; ++q)
+            if (q < PER) keys[q * kSelThreads + tid] = kv[q];
+          __syncthreads();
+#pragma unroll
+          for (int q = 0; q < kSelMaxPer; ++q)
+            if (q < PER) y[q] = keys[q * kSelThreads + (tid ^ j)];
+          __syncthreads();
+        } else {
+#pragma unroll
+          for (int q = 0; q < kSelMaxPer; ++q)
+            if (q < PER) y[q] = __shfl_xor(kv[q], j);
+        }
+#pragma unroll
+        for (int q = 0; q < kSelMaxPer; ++q) {
+          if (q < PER) {
+            const int a = q * kSelThreads + tid;
+            const bool lower = (a & j) == 0, up = (a & k) == 0;
+            const uint64_t x = kv[q];
+            kv[q] = (lower == up) ? (x < y[q] ? x : y[q]) : (x < y[q] ? y[q] : x);
+          }
+        }
+      }
+    }
+  }
+  // Re-distribute: thread t takes PER consecutive sorted positions.
+#pragma unroll
+  for (int q = 0; q < kSelMaxPer; ++q)
+    if (q < PER) keys[q * kSelThreads + tid] = kv[q];
+  __syncthreads();
   U192 seg = u192_zero();
 #pragma unroll
   for (int q = 0; q < kSelMaxPer; ++q) {
@@ -237,7 +274,7 @@ hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, i
   if (B == 0) return hipSuccess;
   int NP = 1;
   while (NP < nb_max) NP <<= 1;
-  const size_t lds = (size_t)NP * sizeof(uint64_t);
+  const size_t lds = (size_t)(NP > kSelThreads ? NP : kSelThreads) * sizeof(uint64_t);
   hipLaunchKernelGGL(up_select_kernel, dim3(B), dim3(kSelThreads), lds, st, scores, cu, B, n, G,
                      mode, p, topk, NP, T_host, nb_tot_host, keep, cu_out, err);
   return hipGetLastError();

@@ -109,6 +109,13 @@ def test_select_is_bit_exact_on_oracle_scores():
     cu1 = np.array([0, 4096], np.int32)
     s1, _, _ = O.block_scores(qb, kb, cu1, 2, 1, 8, 128, 64)
     cases.append((s1, cu1, "ties"))
+    # block counts that use every exchange kind of the sort network (up to 8192 blocks)
+    big = [131072, 3000 * 64, 8192 * 64 - 5, 64 * 1500]
+    cub = np.zeros(len(big) + 1, np.int32)
+    cub[1:] = np.cumsum(big)
+    sb = np.concatenate([rng.dirichlet(np.full(O.n_blocks(L, 64), 0.5)).astype(np.float32)
+                         for L in big])
+    cases.append((sb, cub, "large"))
     for s, c, name in cases:
         for p in (1e-6, 0.3, 0.9, 0.95, 0.99, 0.999, 1.0):
             say(f"[case] select {name} p={p} nb={s.size}")
