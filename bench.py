@@ -43,6 +43,9 @@ def main():
     ap.add_argument("--workload", default="llama31_8b_128k")
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="BYTES",
+                    help="only time a plain device-to-device copy of BYTES (the reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
@@ -50,6 +53,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_reference:
+        copy_reference(torch, args.copy_reference, args.steps)
+        return
     import block_wise_token_amd as up
     from workloads import synth
 
@@ -157,6 +163,23 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, hidden, pos, p, cfg)
     print(json.dumps(result), flush=True)
+
+
+def copy_reference(torch, nbytes, steps):
+    """Plain copy of a known number of bytes (torch's device-to-device copy kernel)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_reference_bytes": nbytes, "reads": nbytes, "writes": nbytes,
+                      "ms": ms, "GB/s_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}))
 
 
 def cpu_baseline(b, hidden, pos, p, cfg):

@@ -98,6 +98,16 @@ SelPlan sel_plan(const int32_t* cu_h, int B, int G) {
 
 bool block_size_supported(int G) { return G >= 32 && G <= 1024 && G % 32 == 0; }
 
+// Compute units of the current device (256 on MI355X; also the fallback when no
+// device is visible, so host-only size queries agree with the calls).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 // Plan of the score pass; returns UP_OK or an error status.
 int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G, ScoreShape* s,
                 Totals* t) {
@@ -119,9 +129,28 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
     const int64_t nrt = (gs * W + s->rows_wg - 1) / s->rows_wg;
     units += nb * Hkv * nrt;
   }
-  // Key-chunk length: aim at about 1024 workgroups (4 per CU) for long inputs.
-  int64_t cb = units / 1024;
-  s->CB = (int)(cb < 1 ? 1 : (cb > 32 ? 32 : cb));
+  // Key-chunk length (blocks per workgroup).  One 8-wave workgroup fills a CU, so
+  // the score pass takes ceil(items / CUs) rounds of CB blocks each: pick the CB
+  // that minimises that product (ties: the larger CB, fewer workgroups).
+  (void)units;
+  {
+    const int64_t cus = device_cus();
+    int64_t best_cost = -1;
+    int best_cb = 1;
+    for (int cb = 256; cb >= 1; --cb) {
+      int64_t items = 0;
+      for (int i = 0; i < B; ++i) {
+        const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
+        const int64_t W = L < n ? L : n;
+        const int64_t nb = (L + G - 1) / G;
+        const int64_t nrt = (gs * W + s->rows_wg - 1) / s->rows_wg;
+        items += (nb + cb - 1) / cb * Hkv * nrt;
+      }
+      const int64_t cost = (items + cus - 1) / cus * cb;
+      if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_cb = cb; }
+    }
+    s->CB = best_cb;
+  }
   *t = Totals{};
   for (int i = 0; i < B; ++i) {
     const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];

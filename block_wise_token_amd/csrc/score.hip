@@ -129,19 +129,67 @@ __device__ __forceinline__ void combine_pair(float m1, float l1, float m2, float
 
 constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 
-template <int D, int QT, int HPS>
+// K rows live in LDS without padding; 16-byte granules of a row are XOR-swizzled
+// so that the 16 lanes of an LDS read phase (16 consecutive keys, same granule)
+// hit 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_swizzle(int key) {
+  return (D / 8 >= 16) ? (key & 15) : ((key >> 1) & 7);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane i of the wave writes LDS bytes [m0 + 16 i, m0 + 16 i + 16).  Issued from
+// inline assembly so that the compiler does not drain every outstanding load at
+// the next LDS read; completion is awaited explicitly (vmcnt) before the barrier
+// that publishes a stage.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m0)
+               : "memory", "m0");
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding and all
+// LDS operations are done, then barrier.  n is a small constant known per call site.
+__device__ __forceinline__ void wait_vm_lgkm_barrier(int n) {
+  // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+#define UP_WAIT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (0 << 8))
+  switch (n) {
+    case 0: UP_WAIT(0); break;
+    case 1: UP_WAIT(1); break;
+    case 2: UP_WAIT(2); break;
+    case 3: UP_WAIT(3); break;
+    case 4: UP_WAIT(4); break;
+    case 5: UP_WAIT(5); break;
+    case 6: UP_WAIT(6); break;
+    case 7: UP_WAIT(7); break;
+    case 8: UP_WAIT(8); break;
+    case 9: UP_WAIT(9); break;
+    case 10: UP_WAIT(10); break;
+    case 11: UP_WAIT(11); break;
+    case 12: UP_WAIT(12); break;
+    case 13: UP_WAIT(13); break;
+    case 14: UP_WAIT(14); break;
+    case 15: UP_WAIT(15); break;
+    default: UP_WAIT(0); break;
+  }
+#undef UP_WAIT
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int D, int QT, int HPS, int NS>
 __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     const uint16_t* __restrict__ qwin, const uint16_t* __restrict__ kmat,
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
     int G, int CB, float c, float2* __restrict__ ml, float2* __restrict__ cs) {
   constexpr int NT = 512;
   constexpr int UK = 32 * HPS;         // keys per LDS stage
-  constexpr int RS = 2 * D + 16;       // LDS bytes per key row (16 B pad against bank conflicts)
-  constexpr int SEGS = UK * D / 8;     // 16-byte segments per stage
-  constexpr int SPT = (SEGS + NT - 1) / NT;
+  constexpr int RB = 2 * D;            // LDS bytes per key row
+  constexpr int SB = UK * RB;          // LDS bytes per stage
+  constexpr int SPT = SB / (NT * 16);  // 16-byte DMA copies per lane per stage
   constexpr int DS = D / 16;           // MFMA k-steps over the head dimension
   constexpr int ROWS = 8 * QT * 32;    // query rows per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * UK * RS];
+  static_assert(SB % (NT * 16) == 0, "stage must be a whole number of DMA rounds");
+  static_assert((NS - 2) * SPT <= 15, "vmcnt wait range");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
 
   if (hdr->valid != 1) return;
   const int x = blockIdx.x;
@@ -180,6 +228,8 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
       qpos[t] = -1;   // inactive row: every key masked in masked halves, never stored
     }
   }
+  // Q is in registers before any K copy is issued: the waits below count K copies only.
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
 
   const int b0 = ch * CB;
   const int b1 = min(pr.nb, b0 + CB);
@@ -190,31 +240,30 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
   const int64_t kstride = (int64_t)Hkv * D;
   const uint16_t* kbase = kmat + ((int64_t)pr.tok_off * Hkv + g) * D;
   const int fast_limit = pr.L - pr.W;   // keys <= this are visible to every window row
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8*)lds;   // LDS byte address
 
-  uint4 pre0[SPT], pre1[SPT];   // stages of even / odd index
-  auto gload = [&](int st, uint4 (&regs)[SPT]) {
+  // Issue the DMA copies of stage st into ring slot st % NS.  Keys past the request
+  // read its last key instead (they are masked); nothing is read out of bounds.
+  auto stage_issue = [&](int st) {
     const int ks = k0 + st * UK;
+    const uint32_t sbase = lds_base + (uint32_t)((st % NS) * SB);
 #pragma unroll
     for (int q = 0; q < SPT; ++q) {
-      const int e = tid + q * NT;
-      if (SEGS % NT == 0 || e < SEGS) {
-        const int key = e / (D / 8), part = e % (D / 8);
-        const int kabs = ks + key;
-        regs[q] = (kabs < pr.L)
-                      ? *reinterpret_cast<const uint4*>(kbase + (int64_t)kabs * kstride + part * 8)
-                      : make_uint4(0, 0, 0, 0);
-      }
+      const int o = q * NT * 16 + tid * 16;          // byte offset in the stage
+      const int key = o / RB;
+      const int p = ((o % RB) / 16) ^ k_swizzle<D>(key);
+      const int kabs = min(ks + key, pr.L - 1);
+      lds_dma16(kbase + (int64_t)kabs * kstride + p * 8,
+                __builtin_amdgcn_readfirstlane(sbase + q * NT * 16 + wave * 1024));
     }
   };
-  auto lstore = [&](int buf, const uint4 (&regs)[SPT]) {
-#pragma unroll
-    for (int q = 0; q < SPT; ++q) {
-      const int e = tid + q * NT;
-      if (SEGS % NT == 0 || e < SEGS) {
-        const int key = e / (D / 8), part = e % (D / 8);
-        *reinterpret_cast<uint4*>(lds + buf * UK * RS + key * RS + part * 16) = regs[q];
-      }
-    }
+  // Make stage st visible: wait for its copies (later stages may stay in flight),
+  // barrier, then refill the slot freed by stage st-1 with stage st+NS-1.
+  auto stage_enter = [&](int st) {
+    const int later = min(NS - 2, nst - 1 - st);   // stages issued after st
+    wait_vm_lgkm_barrier(later * SPT);
+    if (st + NS - 1 <= nst - 1) stage_issue(st + NS - 1);
   };
 
   // Per-lane softmax state (both lanes of a query keep their own).
@@ -230,10 +279,12 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
   // MFMAs of half h into acc.
   auto mfma_half = [&](int h, f32x16 (&acc)[QT]) {
     const int st = h / HPS, hh = h % HPS;
-    const uint8_t* kb = lds + (st & 1) * UK * RS + (hh * 32 + l32) * RS + half * D;
+    const int key = hh * 32 + l32;
+    const uint8_t* kb = lds + (st % NS) * SB + key * RB;
+    const int sw = k_swizzle<D>(key);
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + s * 16);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + 16 * ((half * DS + s) ^ sw));
 #pragma unroll
       for (int t = 0; t < QT; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][s], s == 0 ? f32x16{} : acc[t],
@@ -317,15 +368,9 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
   // One pipeline step: MFMAs of half h+1 (if any) interleaved with the sums of half h.
   // `regs` holds the stage that half h+1 starts, when it starts one (its parity is
   // static in the unrolled loop below).
-  auto step = [&](int h, f32x16 (&cur)[QT], f32x16 (&nxt)[QT], uint4 (&regs)[SPT]) {
+  auto step = [&](int h, f32x16 (&cur)[QT], f32x16 (&nxt)[QT]) {
     const bool more = h + 1 < nh;
-    if (more && (h + 1) % HPS == 0) {
-      // entering stage (h+1)/HPS: publish it, then prefetch two stages ahead
-      const int st = (h + 1) / HPS;
-      lstore(st & 1, regs);
-      __syncthreads();
-      if (st + 2 <= nst - 1) gload(st + 2, regs);
-    }
+    if (more && (h + 1) % HPS == 0) stage_enter((h + 1) / HPS);
     const bool masked = (k0 + h * 32 + 31 > fast_limit);
     float sum[QT];
     if (!masked && more) {
@@ -333,15 +378,18 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
       // for s, and 16/DS of each tile's exp-and-sum of half h.
       constexpr int EPS = 16 / DS;   // elements per tile per k-step
       const int st = (h + 1) / HPS, hh = (h + 1) % HPS;
-      const uint8_t* kb = lds + (st & 1) * UK * RS + (hh * 32 + l32) * RS + half * D;
+      const int key = hh * 32 + l32;
+      const uint8_t* kb = lds + (st % NS) * SB + key * RB;
+      const int sw = k_swizzle<D>(key);
       float part[QT][2];
 #pragma unroll
       for (int t = 0; t < QT; ++t) { part[t][0] = 0.f; part[t][1] = 0.f; }
-      bf16x8 a = *reinterpret_cast<const bf16x8*>(kb);
+      bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + 16 * ((half * DS) ^ sw));
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks) {
         bf16x8 an;
-        if (ks + 1 < DS) an = *reinterpret_cast<const bf16x8*>(kb + (ks + 1) * 16);
+        if (ks + 1 < DS)
+          an = *reinterpret_cast<const bf16x8*>(kb + 16 * ((half * DS + ks + 1) ^ sw));
 #pragma unroll
         for (int t = 0; t < QT; ++t)
           nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][ks],
@@ -365,30 +413,15 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     finish_half(h, cur, sum);
   };
 
-  // Prologue: stages 0 and 1 to registers, stage 0 to LDS, stage 2 prefetched.
-  gload(0, pre0);
-  if (nst > 1) gload(1, pre1);
-  lstore(0, pre0);
-  __syncthreads();
-  if (nst > 2) gload(2, pre0);
+  // Prologue: stages 0 .. NS-2 in flight, stage 0 published.
+  for (int st = 0; st <= NS - 2 && st < nst; ++st) stage_issue(st);
+  stage_enter(0);
   mfma_half(0, acc0);
 
-  if constexpr (HPS == 2) {
-    for (int h = 0; h < nh; h += 4) {   // halves h..h+3 = stages h/2 (even) and h/2+1 (odd)
-      step(h, acc0, acc1, pre1);
-      if (h + 1 >= nh) break;
-      step(h + 1, acc1, acc0, pre1);    // enters stage h/2+1 (odd)
-      if (h + 2 >= nh) break;
-      step(h + 2, acc0, acc1, pre0);
-      if (h + 3 >= nh) break;
-      step(h + 3, acc1, acc0, pre0);    // enters stage h/2+2 (even)
-    }
-  } else {
-    for (int h = 0; h < nh; h += 2) {
-      step(h, acc0, acc1, pre1);        // enters stage h+1 (odd)
-      if (h + 1 >= nh) break;
-      step(h + 1, acc1, acc0, pre0);    // enters stage h+2 (even)
-    }
+  for (int h = 0; h < nh; h += 2) {
+    step(h, acc0, acc1);
+    if (h + 1 >= nh) break;
+    step(h + 1, acc1, acc0);
   }
 
   // Chunk statistics: combine the two lanes of each query.
@@ -544,11 +577,11 @@ hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Total
   return hipGetLastError();
 }
 
-template <int D, int QT, int HPS>
+template <int D, int QT, int HPS, int NS>
 static hipError_t launch_partial_t(const void* qwin, const void* k, const ScoreShape& s,
                                    const Totals& t, void* ws, const ScoreWs& L, float c,
                                    hipStream_t st) {
-  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, HPS>), dim3((unsigned)t.items), dim3(512), 0,
+  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, HPS, NS>), dim3((unsigned)t.items), dim3(512), 0,
                      st, static_cast<const uint16_t*>(qwin), static_cast<const uint16_t*>(k),
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq, s.Hkv, s.G,
@@ -562,9 +595,9 @@ hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShap
                                 hipStream_t st) {
   if (t.items == 0) return hipSuccess;
   switch (s.d) {
-    case 64: return launch_partial_t<64, 2, 2>(qwin, k, s, t, ws, L, c, st);
-    case 128: return launch_partial_t<128, 2, 2>(qwin, k, s, t, ws, L, c, st);
-    case 256: return launch_partial_t<256, 1, 1>(qwin, k, s, t, ws, L, c, st);
+    case 64: return launch_partial_t<64, 2, 2, 8>(qwin, k, s, t, ws, L, c, st);
+    case 128: return launch_partial_t<128, 2, 2, 6>(qwin, k, s, t, ws, L, c, st);
+    case 256: return launch_partial_t<256, 1, 2, 4>(qwin, k, s, t, ws, L, c, st);
     default: return hipErrorInvalidValue;
   }
 }
