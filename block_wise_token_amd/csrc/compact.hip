@@ -117,7 +117,7 @@ __global__ __launch_bounds__(NT) void up_gather_kernel(
     int32_t* __restrict__ pos_out) {
   if (hdr->valid != 1) return;
   const int64_t blk = blockIdx.x / split;
-  const int part = blockIdx.x % split;
+  const int part = (int)(blockIdx.x % split);
   const int32_t d = dst[blk];
   if (d < 0) return;
   const int64_t s = src[blk];
@@ -194,11 +194,14 @@ hipError_t launch_gather(const void* hidden, int64_t row_bytes, const int32_t* p
                          const CompactWs& L, int64_t nb_tot, int G, int32_t* idx_out,
                          void* hidden_out, int32_t* pos_out, hipStream_t st) {
   if (nb_tot == 0) return hipSuccess;
-  constexpr int NT = 256;
+  // Many small workgroups (4 KiB each, two 16-byte vectors per lane in flight)
+  // stream fastest on MI355X: about 6.5 TB/s read+write for a plain 1 GiB copy.
+  constexpr int NT = 128;
   const int64_t blk_bytes = (int64_t)G * row_bytes;
-  int split = (int)(blk_bytes / 65536);
+  int64_t split = blk_bytes / 4096;
   if (split < 1) split = 1;
-  if (split > 64) split = 64;
+  if (split > 4096) split = 4096;
+  if (split > INT32_MAX / nb_tot) split = INT32_MAX / nb_tot > 0 ? INT32_MAX / nb_tot : 1;
   const dim3 grid((unsigned)(nb_tot * split));
   const auto* h = static_cast<const uint8_t*>(hidden);
   auto* ho = static_cast<uint8_t*>(hidden_out);
@@ -208,7 +211,7 @@ hipError_t launch_gather(const void* hidden, int64_t row_bytes, const int32_t* p
   const auto* len = reinterpret_cast<const int32_t*>(wsb(ws) + L.len);
   const uintptr_t al = reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(hidden_out);
   if (row_bytes % 16 == 0 && al % 16 == 0) {
-    hipLaunchKernelGGL((up_gather_kernel<u32x4, NT, 4>), grid, dim3(NT), 0, st, h, row_bytes, pos,
+    hipLaunchKernelGGL((up_gather_kernel<u32x4, NT, 2>), grid, dim3(NT), 0, st, h, row_bytes, pos,
                        hdr, dst, src, len, split, idx_out, ho, pos_out);
   } else if (row_bytes % 4 == 0 && al % 4 == 0) {
     hipLaunchKernelGGL((up_gather_kernel<uint32_t, NT, 4>), grid, dim3(NT), 0, st, h, row_bytes,

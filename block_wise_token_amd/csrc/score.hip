@@ -175,20 +175,22 @@ __device__ __forceinline__ void wait_vm_lgkm_barrier(int n) {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int D, int QT, int HPS, int NS>
+template <int D, int QT, int NS>
 __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     const uint16_t* __restrict__ qwin, const uint16_t* __restrict__ kmat,
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
     int G, int CB, float c, float2* __restrict__ ml, float2* __restrict__ cs) {
   constexpr int NT = 512;
-  constexpr int UK = 32 * HPS;         // keys per LDS stage
+  constexpr int UK = 64;               // keys per LDS stage (two 32-key halves)
   constexpr int RB = 2 * D;            // LDS bytes per key row
   constexpr int SB = UK * RB;          // LDS bytes per stage
   constexpr int SPT = SB / (NT * 16);  // 16-byte DMA copies per lane per stage
   constexpr int DS = D / 16;           // MFMA k-steps over the head dimension
   constexpr int ROWS = 8 * QT * 32;    // query rows per workgroup
+  constexpr int EPS = 16 / DS;         // softmax elements per tile per k-step
   static_assert(SB % (NT * 16) == 0, "stage must be a whole number of DMA rounds");
   static_assert((NS - 2) * SPT <= 15, "vmcnt wait range");
+  static_assert((NS & (NS - 1)) == 0, "ring length must be a power of two");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
 
   if (hdr->valid != 1) return;
@@ -236,26 +238,48 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
   const int k0 = b0 * G;
   const int kend = min(b1 * G, pr.L);
   const int nh = (kend - k0 + 31) / 32;          // 32-key halves in this chunk
-  const int nst = (nh + HPS - 1) / HPS;          // LDS stages
+  const int nst = (nh + 1) / 2;                  // LDS stages
   const int64_t kstride = (int64_t)Hkv * D;
   const uint16_t* kbase = kmat + ((int64_t)pr.tok_off * Hkv + g) * D;
   const int fast_limit = pr.L - pr.W;   // keys <= this are visible to every window row
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8*)lds;   // LDS byte address
 
-  // Issue the DMA copies of stage st into ring slot st % NS.  Keys past the request
-  // read its last key instead (they are masked); nothing is read out of bounds.
+  // Per-lane constants: where this lane's DMA copies come from and land, and where its
+  // A-operand reads are (granule half*DS+s of key l32, swizzled; key 32+l32 is 32 rows on).
+  int64_t dma_goff[SPT];
+  uint32_t dma_loff[SPT];
+  int dma_key[SPT];
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    const int o = q * NT * 16 + tid * 16;
+    const int key = o / RB;
+    const int p = ((o % RB) / 16) ^ k_swizzle<D>(key);
+    dma_key[q] = key;
+    dma_goff[q] = (int64_t)key * kstride + p * 8;
+    dma_loff[q] = q * NT * 16 + wave * 1024;   // wave-uniform
+  }
+  uint32_t rd_off[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) rd_off[s] = l32 * RB + 16 * ((half * DS + s) ^ k_swizzle<D>(l32));
+
+  // Issue the DMA copies of stage st into ring slot st % NS.  Keys past the request read
+  // its last key instead (they are masked); nothing is read out of bounds.
   auto stage_issue = [&](int st) {
     const int ks = k0 + st * UK;
-    const uint32_t sbase = lds_base + (uint32_t)((st % NS) * SB);
+    const uint32_t sbase = lds_base + (uint32_t)((st & (NS - 1)) * SB);
+    const uint16_t* gb = kbase + (int64_t)ks * kstride;
+    if (ks + UK <= pr.L) {
 #pragma unroll
-    for (int q = 0; q < SPT; ++q) {
-      const int o = q * NT * 16 + tid * 16;          // byte offset in the stage
-      const int key = o / RB;
-      const int p = ((o % RB) / 16) ^ k_swizzle<D>(key);
-      const int kabs = min(ks + key, pr.L - 1);
-      lds_dma16(kbase + (int64_t)kabs * kstride + p * 8,
-                __builtin_amdgcn_readfirstlane(sbase + q * NT * 16 + wave * 1024));
+      for (int q = 0; q < SPT; ++q)
+        lds_dma16(gb + dma_goff[q], __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
+    } else {
+#pragma unroll
+      for (int q = 0; q < SPT; ++q) {
+        const int kabs = min(ks + dma_key[q], pr.L - 1);
+        lds_dma16(kbase + (int64_t)kabs * kstride + (dma_goff[q] - (int64_t)dma_key[q] * kstride),
+                  __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
+      }
     }
   };
   // Make stage st visible: wait for its copies (later stages may stay in flight),
@@ -276,15 +300,11 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
 
   f32x16 acc0[QT], acc1[QT];
 
-  // MFMAs of half h into acc.
-  auto mfma_half = [&](int h, f32x16 (&acc)[QT]) {
-    const int st = h / HPS, hh = h % HPS;
-    const int key = hh * 32 + l32;
-    const uint8_t* kb = lds + (st % NS) * SB + key * RB;
-    const int sw = k_swizzle<D>(key);
+  // MFMAs of half h into acc (LDS slot offset `so` bytes, runtime or constant).
+  auto mfma_half = [&](uint32_t so, f32x16 (&acc)[QT]) {
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + 16 * ((half * DS + s) ^ sw));
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + so + rd_off[s]);
 #pragma unroll
       for (int t = 0; t < QT; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][s], s == 0 ? f32x16{} : acc[t],
@@ -292,11 +312,11 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     }
   };
 
-  // Sum of 2^(x - Rs) over a lane's 16 values of half h (masked keys give 0).
+  // Sum of 2^(x - Rs) over a lane's 16 values (masked keys give 0), even/odd partials.
   auto half_sums = [&](f32x16 (&acc)[QT], float (&sum)[QT]) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      float a0 = 0.f, a1 = 0.f;   // same order as the interleaved path: even / odd elements
+      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
         a0 += fast_exp2(fmaf(acc[t][e], c, -Rs[t]));
@@ -320,34 +340,42 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
       }
   };
 
-  // Accumulate half h's sums; redo a half whose sum is out of range; handle block ends.
-  auto finish_half = [&](int h, f32x16 (&acc)[QT], float (&sum)[QT]) {
+  // Redo a tile whose sum left [0, 2^64] against the half's own maximum.
+  auto redo_tile = [&](int t, f32x16 (&acc)[QT]) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[t][e]);
+    if (mx == kNegInf) return lblk[t];   // no visible key in this half
+    const float rn = fmaxf(Rs[t], mx * c);
+    const float sc = fast_exp2(Rs[t] - rn);   // Rs = -inf gives 0 (sums were 0)
+    lblk[t] *= sc;
+    Lch[t] *= sc;
+    Rs[t] = rn;
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      a0 += fast_exp2(fmaf(acc[t][e], c, -rn));
+      a1 += fast_exp2(fmaf(acc[t][e + 1], c, -rn));
+    }
+    return lblk[t] + (a0 + a1);
+  };
+
+  // Accumulate half h's sums; handle block ends.
+  auto finish_half = [&](int h, f32x16 (&acc)[QT], const float (&sum)[QT]) {
+    float nl[QT];
+    bool ok = true;
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      float nl = lblk[t] + sum[t];
-      if (!(nl <= kSumLimit)) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[t][e]);
-        if (mx == kNegInf) {
-          nl = lblk[t];                    // no visible key in this half
-        } else {
-          const float rn = fmaxf(Rs[t], mx * c);
-          const float sc = fast_exp2(Rs[t] - rn);   // Rs = -inf gives 0 (sums were 0)
-          lblk[t] *= sc;
-          Lch[t] *= sc;
-          Rs[t] = rn;
-          float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-          for (int e = 0; e < 16; e += 2) {
-            a0 += fast_exp2(fmaf(acc[t][e], c, -rn));
-            a1 += fast_exp2(fmaf(acc[t][e + 1], c, -rn));
-          }
-          nl = lblk[t] + (a0 + a1);
-        }
-      }
-      lblk[t] = nl;
+      nl[t] = lblk[t] + sum[t];
+      ok = ok && (nl[t] <= kSumLimit);
     }
+    if (!ok) {
+#pragma unroll
+      for (int t = 0; t < QT; ++t)
+        if (!(nl[t] <= kSumLimit)) nl[t] = redo_tile(t, acc);
+    }
+#pragma unroll
+    for (int t = 0; t < QT; ++t) lblk[t] = nl[t];
     const int kh_end = k0 + (h + 1) * 32;
     if (kh_end % G == 0 || h == nh - 1) {
       const int bl = (k0 + h * 32) / G;   // request-local block
@@ -365,63 +393,70 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     }
   };
 
-  // One pipeline step: MFMAs of half h+1 (if any) interleaved with the sums of half h.
-  // `regs` holds the stage that half h+1 starts, when it starts one (its parity is
-  // static in the unrolled loop below).
-  auto step = [&](int h, f32x16 (&cur)[QT], f32x16 (&nxt)[QT]) {
-    const bool more = h + 1 < nh;
-    if (more && (h + 1) % HPS == 0) stage_enter((h + 1) / HPS);
-    const bool masked = (k0 + h * 32 + 31 > fast_limit);
-    float sum[QT];
-    if (!masked && more) {
-      // Interleaved: k-step s issues the LDS read for s+1, the MFMAs of half h+1
-      // for s, and 16/DS of each tile's exp-and-sum of half h.
-      constexpr int EPS = 16 / DS;   // elements per tile per k-step
-      const int st = (h + 1) / HPS, hh = (h + 1) % HPS;
-      const int key = hh * 32 + l32;
-      const uint8_t* kb = lds + (st % NS) * SB + key * RB;
-      const int sw = k_swizzle<D>(key);
-      float part[QT][2];
+  // Fast step (half h and h+1 unmasked, h+1 < nh): MFMAs of h+1 from LDS slot offset
+  // `so` interleaved with the exp-and-sum of h.
+  auto step_fast = [&](int h, uint32_t so, f32x16 (&cur)[QT], f32x16 (&nxt)[QT]) {
+    float part[QT][2];
 #pragma unroll
-      for (int t = 0; t < QT; ++t) { part[t][0] = 0.f; part[t][1] = 0.f; }
-      bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + 16 * ((half * DS) ^ sw));
+    for (int t = 0; t < QT; ++t) { part[t][0] = 0.f; part[t][1] = 0.f; }
+    bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + so + rd_off[0]);
 #pragma unroll
-      for (int ks = 0; ks < DS; ++ks) {
-        bf16x8 an;
-        if (ks + 1 < DS)
-          an = *reinterpret_cast<const bf16x8*>(kb + 16 * ((half * DS + ks + 1) ^ sw));
+    for (int ks = 0; ks < DS; ++ks) {
+      bf16x8 an;
+      if (ks + 1 < DS) an = *reinterpret_cast<const bf16x8*>(lds + so + rd_off[ks + 1]);
 #pragma unroll
-        for (int t = 0; t < QT; ++t)
-          nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][ks],
-                                                           ks == 0 ? f32x16{} : nxt[t], 0, 0, 0);
+      for (int t = 0; t < QT; ++t)
+        nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][ks],
+                                                         ks == 0 ? f32x16{} : nxt[t], 0, 0, 0);
 #pragma unroll
-        for (int t = 0; t < QT; ++t)
+      for (int t = 0; t < QT; ++t)
 #pragma unroll
-          for (int q = 0; q < EPS; ++q) {
-            const int e = ks * EPS + q;
-            part[t][e & 1] += fast_exp2(fmaf(cur[t][e], c, -Rs[t]));
-          }
-        if (ks + 1 < DS) a = an;
-      }
-#pragma unroll
-      for (int t = 0; t < QT; ++t) sum[t] = part[t][0] + part[t][1];
-    } else {
-      if (more) mfma_half(h + 1, nxt);
-      if (masked) mask_half(h, cur);
-      half_sums(cur, sum);
+        for (int q = 0; q < EPS; ++q) {
+          const int e = ks * EPS + q;
+          part[t][e & 1] += fast_exp2(fmaf(cur[t][e], c, -Rs[t]));
+        }
+      if (ks + 1 < DS) a = an;
     }
+    float sum[QT];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) sum[t] = part[t][0] + part[t][1];
     finish_half(h, cur, sum);
   };
 
-  // Prologue: stages 0 .. NS-2 in flight, stage 0 published.
+  // Generic step: any half (masked or the chunk's last), runtime LDS slot.
+  auto step_generic = [&](int h, f32x16 (&cur)[QT], f32x16 (&nxt)[QT]) {
+    const bool more = h + 1 < nh;
+    if (more && ((h + 1) & 1) == 0) stage_enter((h + 1) / 2);
+    if (more) mfma_half((uint32_t)((((h + 1) / 2) & (NS - 1)) * SB + ((h + 1) & 1) * 32 * RB), nxt);
+    if (k0 + h * 32 + 31 > fast_limit) mask_half(h, cur);
+    float sum[QT];
+    half_sums(cur, sum);
+    finish_half(h, cur, sum);
+  };
+
+  // Prologue: stages 0 .. NS-2 in flight, stage 0 published, MFMAs of half 0.
   for (int st = 0; st <= NS - 2 && st < nst; ++st) stage_issue(st);
   stage_enter(0);
   mfma_half(0, acc0);
 
-  for (int h = 0; h < nh; h += 2) {
-    step(h, acc0, acc1);
+  // Main loop, unrolled over the ring: halves h .. h+2NS-1 (stages h/2 .. h/2+NS-1, ring
+  // slots 0 .. NS-1) when every one of them and the next half are unmasked.
+  int h = 0;
+  while (h + 2 * NS < nh && k0 + (h + 2 * NS) * 32 + 31 <= fast_limit) {
+#pragma unroll
+    for (int j = 0; j < 2 * NS; ++j) {
+      f32x16 (&cur)[QT] = (j & 1) ? acc1 : acc0;
+      f32x16 (&nxt)[QT] = (j & 1) ? acc0 : acc1;
+      if ((j & 1) == 1) stage_enter((h + j + 1) / 2);
+      step_fast(h + j, (uint32_t)((((j + 1) / 2) & (NS - 1)) * SB + ((j + 1) & 1) * 32 * RB), cur, nxt);
+    }
+    h += 2 * NS;
+  }
+  // Tail: pairs of halves with static accumulator parity (h is even here).
+  for (; h < nh; h += 2) {
+    step_generic(h, acc0, acc1);
     if (h + 1 >= nh) break;
-    step(h + 1, acc1, acc0);
+    step_generic(h + 1, acc1, acc0);
   }
 
   // Chunk statistics: combine the two lanes of each query.
@@ -577,11 +612,11 @@ hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Total
   return hipGetLastError();
 }
 
-template <int D, int QT, int HPS, int NS>
+template <int D, int QT, int NS>
 static hipError_t launch_partial_t(const void* qwin, const void* k, const ScoreShape& s,
                                    const Totals& t, void* ws, const ScoreWs& L, float c,
                                    hipStream_t st) {
-  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, HPS, NS>), dim3((unsigned)t.items), dim3(512), 0,
+  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, NS>), dim3((unsigned)t.items), dim3(512), 0,
                      st, static_cast<const uint16_t*>(qwin), static_cast<const uint16_t*>(k),
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq, s.Hkv, s.G,
@@ -595,9 +630,9 @@ hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShap
                                 hipStream_t st) {
   if (t.items == 0) return hipSuccess;
   switch (s.d) {
-    case 64: return launch_partial_t<64, 2, 2, 8>(qwin, k, s, t, ws, L, c, st);
-    case 128: return launch_partial_t<128, 2, 2, 6>(qwin, k, s, t, ws, L, c, st);
-    case 256: return launch_partial_t<256, 1, 2, 4>(qwin, k, s, t, ws, L, c, st);
+    case 64: return launch_partial_t<64, 2, 8>(qwin, k, s, t, ws, L, c, st);
+    case 128: return launch_partial_t<128, 2, 4>(qwin, k, s, t, ws, L, c, st);
+    case 256: return launch_partial_t<256, 1, 4>(qwin, k, s, t, ws, L, c, st);
     default: return hipErrorInvalidValue;
   }
 }
