@@ -118,16 +118,20 @@ __global__ void up_score_plan_kernel(const int32_t* __restrict__ cu, ScoreShape 
 // lane reads one contiguous D-byte run per row.
 // ---------------------------------------------------------------------------
 
-// Combine two (reference, sum) pairs of the same quantity into one.
-__device__ __forceinline__ void combine_pair(float m1, float l1, float m2, float l2, float& m,
-                                             float& l) {
-  if (m1 == m2) { m = m1; l = l1 + l2; return; }   // common case, exact
-  m = fmaxf(m1, m2);
-  if (m == kNegInf) { l = 0.f; return; }
-  l = l1 * fast_exp2(m1 - m) + l2 * fast_exp2(m2 - m);
-}
-
 constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
+
+// Lanes l and l^32 hold the two key halves of one query.  v_permlane32_swap(x, x)
+// returns x of the low lane in [0] and of the high lane in [1], in both lanes.
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);   // same operand order in both lanes
+}
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // K rows live in LDS without padding; 16-byte granules of a row are XOR-swizzled
 // so that the 16 lanes of an LDS read phase (16 consecutive keys, same granule)
@@ -143,8 +147,7 @@ __device__ __forceinline__ int k_swizzle(int key) {
 // the next LDS read; completion is awaited explicitly (vmcnt) before the barrier
 // that publishes a stage.
 __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m0)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
 }
 
 // Wait until at most n vector-memory operations of this wave are outstanding and all
@@ -290,7 +293,9 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     if (st + NS - 1 <= nst - 1) stage_issue(st + NS - 1);
   };
 
-  // Per-lane softmax state (both lanes of a query keep their own).
+  // Softmax state.  Rs is one reference per query, identical in the two lanes that
+  // hold the query's keys; lblk / Lch are each lane's sums over its own keys of the
+  // current block / chunk, relative to Rs.
   float Rs[QT], lblk[QT], Lch[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) { Rs[t] = kNegInf; lblk[t] = 0.f; Lch[t] = 0.f; }
@@ -298,7 +303,14 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
   const int r_st = row0 + t_st * 32 + l32;
   const bool st_ok = (QT == 2 || half == 0) && (r_st < R);
 
+  int hcnt = G / 32;   // halves left in the current block
   f32x16 acc0[QT], acc1[QT];
+  float2 pend_v = make_float2(0.f, 0.f);   // block statistics waiting to be stored
+  int64_t pend_i = -1;
+  auto flush_pending = [&]() {
+    if (pend_i >= 0) ml[pend_i] = pend_v;
+    pend_i = -1;
+  };
 
   // MFMAs of half h into acc (LDS slot offset `so` bytes, runtime or constant).
   auto mfma_half = [&](uint32_t so, f32x16 (&acc)[QT]) {
@@ -340,56 +352,59 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
       }
   };
 
-  // Redo a tile whose sum left [0, 2^64] against the half's own maximum.
-  auto redo_tile = [&](int t, f32x16 (&acc)[QT]) {
-    float mx = kNegInf;
+  // Rebase the reference of every query whose half left [0, 2^64] (a sum overflowed,
+  // or the reference was unset) on the pair's maximum over this half; runs for the
+  // whole wave, the lanes whose sums were fine get the same sums back.
+  auto rebase = [&](f32x16 (&acc)[QT], float (&nl)[QT]) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[t][e]);
-    if (mx == kNegInf) return lblk[t];   // no visible key in this half
-    const float rn = fmaxf(Rs[t], mx * c);
-    const float sc = fast_exp2(Rs[t] - rn);   // Rs = -inf gives 0 (sums were 0)
-    lblk[t] *= sc;
-    Lch[t] *= sc;
-    Rs[t] = rn;
-    float a0 = 0.f, a1 = 0.f;
+    for (int t = 0; t < QT; ++t) {
+      float mx = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      a0 += fast_exp2(fmaf(acc[t][e], c, -rn));
-      a1 += fast_exp2(fmaf(acc[t][e + 1], c, -rn));
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[t][e]);
+      mx = pair_max(mx);
+      if (mx == kNegInf) { nl[t] = lblk[t]; continue; }   // no visible key for this query
+      const float rn = fmaxf(Rs[t], mx * c);
+      const float sc = fast_exp2(Rs[t] - rn);            // Rs = -inf gives 0 (sums were 0)
+      lblk[t] *= sc;
+      Lch[t] *= sc;
+      Rs[t] = rn;
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        a0 += fast_exp2(fmaf(acc[t][e], c, -rn));
+        a1 += fast_exp2(fmaf(acc[t][e + 1], c, -rn));
+      }
+      nl[t] = lblk[t] + (a0 + a1);
     }
-    return lblk[t] + (a0 + a1);
   };
 
   // Accumulate half h's sums; handle block ends.
   auto finish_half = [&](int h, f32x16 (&acc)[QT], const float (&sum)[QT]) {
     float nl[QT];
-    bool ok = true;
+    bool bad = false;
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       nl[t] = lblk[t] + sum[t];
-      ok = ok && (nl[t] <= kSumLimit);
+      bad = bad || !(nl[t] <= kSumLimit);
     }
-    if (!ok) {
-#pragma unroll
-      for (int t = 0; t < QT; ++t)
-        if (!(nl[t] <= kSumLimit)) nl[t] = redo_tile(t, acc);
-    }
+    if (__ballot(bad) != 0) rebase(acc, nl);   // wave-uniform branch, rare
 #pragma unroll
     for (int t = 0; t < QT; ++t) lblk[t] = nl[t];
-    const int kh_end = k0 + (h + 1) * 32;
-    if (kh_end % G == 0 || h == nh - 1) {
+    if (--hcnt == 0 || h == nh - 1) {
+      hcnt = G / 32;
       const int bl = (k0 + h * 32) / G;   // request-local block
-      float mst = 0.f, lst = 0.f;
+      float lst = 0.f, mst = 0.f;
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
-        const float mo = __shfl_xor(Rs[t], 32), lo = __shfl_xor(lblk[t], 32);
-        float m, l;
-        combine_pair(Rs[t], lblk[t], mo, lo, m, l);
-        if (t == t_st) { mst = m; lst = l; }
+        const float lp = pair_sum(lblk[t]);   // same value in both lanes
+        if (t == t_st) { mst = Rs[t]; lst = lp; }
         Lch[t] += lblk[t];
         lblk[t] = 0.f;
       }
-      if (st_ok) ml[pr.ml_off + ((int64_t)bl * Hkv + g) * R + r_st] = make_float2(mst, lst);
+      // The store is issued after the next stage barrier (flush_pending).
+      flush_pending();   // a block ended since the last barrier (G < 64): store it now
+      pend_v = make_float2(lst > 0.f ? mst : kNegInf, lst);
+      pend_i = st_ok ? pr.ml_off + ((int64_t)bl * Hkv + g) * R + r_st : -1;
     }
   };
 
@@ -399,14 +414,16 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     float part[QT][2];
 #pragma unroll
     for (int t = 0; t < QT; ++t) { part[t][0] = 0.f; part[t][1] = 0.f; }
-    bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + so + rd_off[0]);
+    // All A operands of half h+1 are requested up front, so MFMA s waits for read s only.
+    bf16x8 a[DS];
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(lds + so + rd_off[ks]);
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of everything below
 #pragma unroll
     for (int ks = 0; ks < DS; ++ks) {
-      bf16x8 an;
-      if (ks + 1 < DS) an = *reinterpret_cast<const bf16x8*>(lds + so + rd_off[ks + 1]);
 #pragma unroll
       for (int t = 0; t < QT; ++t)
-        nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][ks],
+        nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[t][ks],
                                                          ks == 0 ? f32x16{} : nxt[t], 0, 0, 0);
 #pragma unroll
       for (int t = 0; t < QT; ++t)
@@ -415,7 +432,6 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
           const int e = ks * EPS + q;
           part[t][e & 1] += fast_exp2(fmaf(cur[t][e], c, -Rs[t]));
         }
-      if (ks + 1 < DS) a = an;
     }
     float sum[QT];
 #pragma unroll
@@ -426,7 +442,10 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
   // Generic step: any half (masked or the chunk's last), runtime LDS slot.
   auto step_generic = [&](int h, f32x16 (&cur)[QT], f32x16 (&nxt)[QT]) {
     const bool more = h + 1 < nh;
-    if (more && ((h + 1) & 1) == 0) stage_enter((h + 1) / 2);
+    if (more && ((h + 1) & 1) == 0) {
+      stage_enter((h + 1) / 2);
+      flush_pending();
+    }
     if (more) mfma_half((uint32_t)((((h + 1) / 2) & (NS - 1)) * SB + ((h + 1) & 1) * 32 * RB), nxt);
     if (k0 + h * 32 + 31 > fast_limit) mask_half(h, cur);
     float sum[QT];
@@ -447,7 +466,10 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     for (int j = 0; j < 2 * NS; ++j) {
       f32x16 (&cur)[QT] = (j & 1) ? acc1 : acc0;
       f32x16 (&nxt)[QT] = (j & 1) ? acc0 : acc1;
-      if ((j & 1) == 1) stage_enter((h + j + 1) / 2);
+      if ((j & 1) == 1) {
+        stage_enter((h + j + 1) / 2);
+        flush_pending();
+      }
       step_fast(h + j, (uint32_t)((((j + 1) / 2) & (NS - 1)) * SB + ((j + 1) & 1) * 32 * RB), cur, nxt);
     }
     h += 2 * NS;
@@ -459,16 +481,16 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
     step_generic(h + 1, acc1, acc0);
   }
 
-  // Chunk statistics: combine the two lanes of each query.
+  flush_pending();
+  // Chunk statistics: the two lanes of each query share the reference; add their sums.
   float mst = 0.f, lst = 0.f;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    const float mo = __shfl_xor(Rs[t], 32), lo = __shfl_xor(Lch[t], 32);
-    float m, l;
-    combine_pair(Rs[t], Lch[t], mo, lo, m, l);
-    if (t == t_st) { mst = m; lst = l; }
+    const float lp = pair_sum(Lch[t]);
+    if (t == t_st) { mst = Rs[t]; lst = lp; }
   }
-  if (st_ok) cs[pr.cs_off + ((int64_t)ch * Hkv + g) * R + r_st] = make_float2(mst, lst);
+  if (st_ok)
+    cs[pr.cs_off + ((int64_t)ch * Hkv + g) * R + r_st] = make_float2(lst > 0.f ? mst : kNegInf, lst);
 }
 
 // ---------------------------------------------------------------------------
