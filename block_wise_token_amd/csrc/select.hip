@@ -5,13 +5,23 @@
 // selection runs on the GPU with no host round trip; [UP] "ablation" paragraph:
 // Top-k (a fixed count) is the alternative the ablation compares against.
 //
-// Order: 64-bit keys (~float bits of the score) << 32 | block index, sorted
-// ascending by a bitonic network in LDS, give score descending and ties by the
-// lower block index.  The running sum is exact: a float32 in [0, 1] is an integer
-// multiple of 2^-149 (below 2^150), so every score is widened to a 192-bit integer
-// and the prefix sums are integer adds -- associative, so the parallel scan gives
-// the same cut as a sequential exact sum would.  The cut is the first sorted
-// position whose running sum reaches p (float32 p widened the same way).
+// Order: score descending, ties by the lower block index.  The kept set is the
+// shortest prefix of that order whose exact running sum reaches p, so it is fixed
+// by one key, the cut: the (score, index) of the last kept block.  Nothing is
+// sorted.  The cut's score is found by a radix select over the float bits (a score
+// in [0, 1] has 30 significant bits: 7 exponent bits, 23 fraction bits), three
+// passes of 10-bit digits from the top.  Each pass histograms the candidates still
+// in play by digit -- a count and an exact sum per bin -- and takes the first bin,
+// walking digits downwards, whose cumulative sum reaches what is left of p.
+//
+// Sums are exact integers.  A float32 in [0, 1] is M * 2^sh units of 2^-149, with M
+// its 24-bit significand and sh = max(exponent - 1, 0).  The first digit fixes the
+// exponent, so a first-pass bin total is (sum of M) << sh, compared as a 192-bit
+// integer; after that every candidate shares sh and the remainder of p is carried
+// as a 64-bit count of 2^sh units.  Integer sums are order-independent, so the cut
+// equals the one a sequential exact running sum over the sorted order gives.
+// Among the blocks whose score equals the cut score (ties), the remainder decides
+// how many are kept, taken in ascending block index.
 #include "up_internal.h"
 
 namespace up {
@@ -21,30 +31,6 @@ struct U192 {
 };
 
 __device__ __forceinline__ U192 u192_zero() { return U192{0, 0, 0}; }
-
-// A score as an exact count of 2^-149 units.  Scores outside [0, 1] are clamped into
-// it and NaN counts as 0 (scores produced by up_block_scores are always in [0, 1]).
-__device__ __forceinline__ float clamp_score(float s) {
-  if (!(s > 0.f)) return 0.f;
-  return s > 1.f ? 1.f : s;
-}
-
-__device__ __forceinline__ U192 score_units(float s) {
-  const uint32_t bits = __float_as_uint(s);
-  const uint32_t e = bits >> 23, f = bits & 0x7FFFFFu;
-  uint64_t m;
-  int sh;
-  if (e == 0) { m = f; sh = 0; } else { m = f | 0x800000u; sh = (int)e - 1; }   // sh <= 126
-  U192 r = u192_zero();
-  if (sh < 64) {
-    r.lo = m << sh;
-    r.mid = sh ? (m >> (64 - sh)) : 0;
-  } else {
-    r.mid = m << (sh - 64);
-    r.hi = (sh == 64) ? 0 : (m >> (128 - sh));
-  }
-  return r;
-}
 
 __device__ __forceinline__ U192 u192_add(U192 a, U192 b) {
   U192 r;
@@ -58,10 +44,60 @@ __device__ __forceinline__ U192 u192_add(U192 a, U192 b) {
   return r;
 }
 
+// a - b for a >= b.
+__device__ __forceinline__ U192 u192_sub(U192 a, U192 b) {
+  U192 r;
+  r.lo = a.lo - b.lo;
+  const uint64_t b0 = a.lo < b.lo;
+  const uint64_t t = a.mid - b.mid;
+  const uint64_t b1 = a.mid < b.mid;
+  r.mid = t - b0;
+  const uint64_t b2 = t < b0;
+  r.hi = a.hi - b.hi - b1 - b2;
+  return r;
+}
+
 __device__ __forceinline__ bool u192_geq(U192 a, U192 b) {
   if (a.hi != b.hi) return a.hi > b.hi;
   if (a.mid != b.mid) return a.mid > b.mid;
   return a.lo >= b.lo;
+}
+
+// x << sh for x < 2^64 and 0 <= sh <= 127.
+__device__ __forceinline__ U192 u192_shl(uint64_t x, int sh) {
+  U192 r = u192_zero();
+  if (sh == 0) {
+    r.lo = x;
+  } else if (sh < 64) {
+    r.lo = x << sh;
+    r.mid = x >> (64 - sh);
+  } else if (sh == 64) {
+    r.mid = x;
+  } else if (sh < 128) {
+    r.mid = x << (sh - 64);
+    r.hi = x >> (128 - sh);
+  }
+  return r;
+}
+
+// ceil(a / 2^sh) for 0 <= sh <= 127, when the result is known to be below 2^64.
+__device__ __forceinline__ uint64_t u192_shr_ceil(U192 a, int sh) {
+  uint64_t q;
+  bool rem;
+  if (sh == 0) {
+    q = a.lo;
+    rem = false;
+  } else if (sh < 64) {
+    q = (a.lo >> sh) | (a.mid << (64 - sh));
+    rem = (a.lo << (64 - sh)) != 0;
+  } else if (sh == 64) {
+    q = a.mid;
+    rem = a.lo != 0;
+  } else {
+    q = (a.mid >> (sh - 64)) | (a.hi << (128 - sh));
+    rem = a.lo != 0 || (a.mid << (128 - sh)) != 0;
+  }
+  return q + (rem ? 1 : 0);
 }
 
 __device__ __forceinline__ U192 u192_shfl_up(U192 v, int d) {
@@ -72,175 +108,382 @@ __device__ __forceinline__ U192 u192_shfl_up(U192 v, int d) {
   return r;
 }
 
-// Sum of an int64 over the workgroup (1024 threads) in a fixed order: a butterfly
-// within each wave, then the 16 wave sums in wave order.
-__device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* wsum) {
+// Float bits of a score clamped into [0, 1] (NaN counts as 0); scores produced by
+// up_block_scores are always in [0, 1].  The bits are below 2^30.
+__device__ __forceinline__ uint32_t score_bits(float s) {
+  if (!(s > 0.f)) return 0u;
+  return __float_as_uint(s > 1.f ? 1.f : s);
+}
+
+// Significand M and shift sh of float bits u: the value is M * 2^sh units of 2^-149.
+__device__ __forceinline__ uint32_t sig_of(uint32_t u) {
+  const uint32_t e = u >> 23, f = u & 0x7FFFFFu;
+  return e ? (f | 0x800000u) : f;
+}
+__device__ __forceinline__ int shift_of_exp(uint32_t e) { return e ? (int)e - 1 : 0; }
+
+// Wave-wide inclusive scans with DPP row shifts and row broadcasts (no LDS round
+// trips): shifts by 1, 2, 4, 8 within each row of 16 lanes, then lane 15 of a row
+// into the next row, then lane 31 into rows 2 and 3.  Lanes with no source read 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp_in(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xf, true);
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_in64(uint64_t v) {
+  const uint32_t lo = dpp_in<CTRL, ROWMASK>((uint32_t)v);
+  const uint32_t hi = dpp_in<CTRL, ROWMASK>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ U192 dpp_in192(U192 v) {
+  return U192{dpp_in64<CTRL, ROWMASK>(v.lo), dpp_in64<CTRL, ROWMASK>(v.mid),
+              dpp_in64<CTRL, ROWMASK>(v.hi)};
+}
+
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
+  v += dpp_in<0x111, 0xf>(v);
+  v += dpp_in<0x112, 0xf>(v);
+  v += dpp_in<0x114, 0xf>(v);
+  v += dpp_in<0x118, 0xf>(v);
+  v += dpp_in<0x142, 0xa>(v);
+  v += dpp_in<0x143, 0xc>(v);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
+  v += dpp_in64<0x111, 0xf>(v);
+  v += dpp_in64<0x112, 0xf>(v);
+  v += dpp_in64<0x114, 0xf>(v);
+  v += dpp_in64<0x118, 0xf>(v);
+  v += dpp_in64<0x142, 0xa>(v);
+  v += dpp_in64<0x143, 0xc>(v);
+  return v;
+}
+__device__ __forceinline__ U192 wave_scan_u192(U192 v) {
+  v = u192_add(v, dpp_in192<0x111, 0xf>(v));
+  v = u192_add(v, dpp_in192<0x112, 0xf>(v));
+  v = u192_add(v, dpp_in192<0x114, 0xf>(v));
+  v = u192_add(v, dpp_in192<0x118, 0xf>(v));
+  v = u192_add(v, dpp_in192<0x142, 0xa>(v));
+  v = u192_add(v, dpp_in192<0x143, 0xc>(v));
+  return v;
+}
+
+constexpr int kSelPer = 16;                      // candidate slots per thread
+constexpr int kBins = 256;                       // digits of at most 8 bits
+constexpr int kCopies = 8;                       // lane l adds into histogram copy l % 8
+constexpr uint32_t kAbsent = 0xFFFFFFFFu;        // no block in this slot
+static_assert(kSelectMaxBlocks <= 1024 * kSelPer, "select slots");
+
+// Digit passes over the 30 score bits: the exponent (bits 29..23), then the
+// fraction in 8, 8 and 7 bits.
+__device__ __forceinline__ int digit_shift(int pass) {
+  return pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
+}
+
+template <int NW>
+struct SelLds {
+  uint32_t cnt[kBins * kCopies];
+  uint64_t sum[kBins * kCopies];
+  U192 wtot192[NW];
+  uint64_t wtot64[NW];
+  uint32_t wtot32[NW];
+  int64_t red[NW];
+  uint32_t tie_cnt[kSelPer * NW];
+  uint32_t tie_pre[kSelPer * NW];
+  int win;            // (thread) index of the bin holding the cut, from the top
+  uint32_t prefix;    // cut digits found so far
+  uint64_t rem;       // remainder of p in units of 2^sh of the cut's exponent
+  uint32_t rem_k;     // remainder of the count (Top-k)
+  uint32_t ties;      // blocks whose score equals the cut score
+  int keep_all;
+};
+
+// Inclusive scans over the workgroup in thread order: DPP within each wave, then
+// the totals of the lower waves (read as independent LDS loads).
+template <int NW, typename Lds>
+__device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, Lds& S) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_scan_u32(v);
+  if (lane == 63) S.wtot32[wave] = v;
+  __syncthreads();
+  uint32_t pre = 0;
 #pragma unroll
-  for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d);
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = v;
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = S.wtot32[w];
+    pre += w < wave ? t : 0u;
+  }
+  return pre + v;
+}
+template <int NW, typename Lds>
+__device__ __forceinline__ uint64_t block_scan_u64(uint64_t v, Lds& S) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_scan_u64(v);
+  if (lane == 63) S.wtot64[wave] = v;
+  __syncthreads();
+  uint64_t pre = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint64_t t = S.wtot64[w];
+    pre += w < wave ? t : 0ull;
+  }
+  return pre + v;
+}
+template <int NW, typename Lds>
+__device__ __forceinline__ U192 block_scan_u192(U192 v, Lds& S) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_scan_u192(v);
+  if (lane == 63) S.wtot192[wave] = v;
+  __syncthreads();
+  U192 pre = u192_zero();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const U192 t = S.wtot192[w];
+    if (w < wave) pre = u192_add(pre, t);
+  }
+  return u192_add(pre, v);
+}
+// Sum over the workgroup, the same value in every thread (integer: order-free).
+template <int NW, typename Lds>
+__device__ __forceinline__ int64_t block_sum_i64(int64_t v, Lds& S) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = (int64_t)wave_scan_u64((uint64_t)v);
+  if (lane == 63) S.red[wave] = v;
   __syncthreads();
   int64_t r = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) r += wsum[w];
-  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) r += S.red[w];
   return r;
 }
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelMaxPer = kSelectMaxBlocks / kSelThreads;   // sorted positions per thread
-
-__global__ __launch_bounds__(1024) void up_select_kernel(
+// NT threads per request; block a of the request lives in slot a / NT of thread a % NT.
+template <int NT>
+__global__ __launch_bounds__(NT) void up_select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ cu, int B, int n, int G,
-    int mode, float p, int topk, int NP, int64_t T_host, int64_t nb_tot_host,
+    int mode, float p, int topk, int64_t T_host, int64_t nb_tot_host, int direct,
     uint8_t* __restrict__ keep, int32_t* __restrict__ cu_out, int* __restrict__ err) {
-  extern __shared__ uint64_t keys[];            // NP sort keys
-  __shared__ int64_t red[kSelThreads / 64];
-  __shared__ U192 wave_tot[kSelThreads / 64];
-  __shared__ int cut_pos;
-
+  constexpr int NW = NT / 64;
+  constexpr int PER = kSelPer * 1024 / NT > kSelPer ? kSelPer : kSelPer * 1024 / NT;
+  constexpr int MAXB = NT * PER;
+  __shared__ SelLds<NW> S;
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
-  // First global block of this request: sum of the earlier requests' block counts.
-  int64_t part = 0;
-  for (int r = tid; r < i; r += kSelThreads) {
-    const int64_t Lr = (int64_t)cu[r + 1] - cu[r];
-    part += Lr > 0 ? (Lr + G - 1) / G : 0;
+  // A single request starts at block 0 and has the host's block count, so its scores
+  // are fetched before cu_seqlens is back; the device values are checked after.
+  uint32_t u[PER];
+  int64_t blk_off = 0;
+  if (direct) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int64_t a = (int64_t)q * NT + tid;
+      u[q] = a < nb_tot_host ? __float_as_uint(scores[a]) : kAbsent;
+    }
+  } else {
+    // First global block of this request: sum of the earlier requests' block counts.
+    int64_t part = 0;
+    for (int r = tid; r < i; r += NT) {
+      const int64_t Lr = (int64_t)cu[r + 1] - cu[r];
+      part += Lr > 0 ? (Lr + G - 1) / G : 0;
+    }
+    blk_off = block_sum_i64<NW>(part, S);
   }
-  const int64_t blk_off = block_sum_i64(part, red);
   const int64_t L = (int64_t)cu[i + 1] - cu[i];
   const int64_t nb = L > 0 ? (L + G - 1) / G : 0;
   const bool bad = (L < 0) || ((int64_t)cu[B] != T_host) || (blk_off + nb > nb_tot_host) ||
-                   (nb > NP) || (cu[0] != 0);
+                   (nb > MAXB) || (cu[0] != 0);
   if (bad) {
     if (tid == 0) {
       atomicOr(err, 1);
       cu_out[i + 1] = 0;
+      if (direct) cu_out[0] = 0;
     }
     return;
+  }
+  if (!direct) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int64_t a = (int64_t)q * NT + tid;
+      u[q] = a < nb ? __float_as_uint(scores[blk_off + a]) : kAbsent;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int64_t a = (int64_t)q * NT + tid;
+    u[q] = a < nb ? score_bits(__uint_as_float(u[q])) : kAbsent;
   }
   const int64_t W = L < n ? L : n;
   const int64_t wfirst = (L - W) / G;   // first block holding a window token
 
-  // Sort keys.  Element a of the bitonic network lives in thread a % 1024, slot
-  // a / 1024: partners at distance j >= 1024 are in the same thread, partners at
-  // 64 <= j < 1024 are exchanged through LDS, partners at j < 64 by wave shuffles.
-  const int PER = NP >= kSelThreads ? NP / kSelThreads : 1;
-  uint64_t kv[kSelMaxPer];
-#pragma unroll
-  for (int q = 0; q < kSelMaxPer; ++q) {
-    const int a = q * kSelThreads + tid;
-    uint64_t key = ~0ull;
-    if (q < PER && a < nb) {
-      const float s = clamp_score(scores[blk_off + a]);
-      key = ((uint64_t)(~__float_as_uint(s)) << 32) | (uint32_t)a;
-    }
-    kv[q] = key;
+  // How many of the top blocks the cut keeps, as a target the passes narrow down.
+  const int64_t kcount = mode == 1 ? (topk < nb ? topk : nb) : nb;
+  const bool all = mode == 1 ? (kcount >= nb) : !(p < 1.0f);
+  const bool none = mode == 1 && kcount == 0;
+  if (tid == 0) {
+    S.keep_all = all ? 1 : 0;
+    S.prefix = 0;
+    S.rem_k = (uint32_t)kcount;
+    S.rem = 0;
+    S.ties = 0;
   }
-  for (int k = 2; k <= NP; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= kSelThreads) {
-        const int jj = j / kSelThreads;
-        auto cx = [&](int q, int p) {   // q < p: slots q and p of this thread
-          const bool up = ((q * kSelThreads + tid) & k) == 0;
-          const uint64_t x = kv[q], y = kv[p];
-          if ((x > y) == up) { kv[q] = y; kv[p] = x; }
-        };
+  __syncthreads();
+  uint32_t ustar = kAbsent;   // the cut's score bits
+  uint32_t jtie = 0;          // ties at the cut score that are kept
+  const int copy = lane & (kCopies - 1);
+
+  if (!all && !none && nb > 0) {
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+      const int dsh = digit_shift(pass);
+      for (int e = tid; e < kBins * kCopies; e += NT) {
+        S.cnt[e] = 0;
+        S.sum[e] = 0;
+      }
+      if (tid == 0) S.win = kBins;
+      __syncthreads();
+      const uint32_t pre = S.prefix;
+      const int hsh = pass == 0 ? 30 : digit_shift(pass - 1);   // bits above this digit
 #pragma unroll
-        for (int q = 0; q < kSelMaxPer; ++q) {
-          if (jj == 1 && !(q & 1) && q + 1 < PER) cx(q, q + 1);
-          if (jj == 2 && !(q & 2) && q + 2 < PER) cx(q, q + 2);
-          if (jj == 4 && !(q & 4) && q + 4 < PER) cx(q, q + 4);
+      for (int q = 0; q < PER; ++q) {
+        const uint32_t x = u[q];
+        if (x != kAbsent && (pass == 0 || (x >> hsh) == pre)) {
+          const uint32_t dg = (x >> dsh) & ((1u << (hsh - dsh)) - 1u);
+          atomicAdd(&S.cnt[dg * kCopies + copy], 1u);
+          if (mode == 0)
+            atomicAdd((unsigned long long*)&S.sum[dg * kCopies + copy],
+                      (unsigned long long)sig_of(x));
         }
-      } else {
-        uint64_t y[kSelMaxPer];
-        if (j >= 64) {
+      }
+      __syncthreads();
+      // Thread t looks at digit kBins-1-t: ascending threads walk digits downwards.
+      const int dg = kBins - 1 - tid;
+      uint32_t c = 0;
+      uint64_t m = 0;
+      if (dg >= 0) {
 #pragma unroll
-          for (int q = 0; q < kSelMaxPer; ++q)
-            if (q < PER) keys[q * kSelThreads + tid] = kv[q];
+        for (int k = 0; k < kCopies; ++k) {
+          c += S.cnt[dg * kCopies + k];
+          if (mode == 0) m += S.sum[dg * kCopies + k];
+        }
+      }
+      if (mode == 0) {
+        if (pass == 0) {
+          const int sh = shift_of_exp((uint32_t)(dg >= 0 ? dg : 0));   // the digit is the exponent
+          const U192 v = u192_shl(m, sh);
+          const U192 inc = block_scan_u192<NW>(v, S);
+          // P: p as units of 2^-149 (p is a float32 in (0, 1)).
+          const uint32_t pb = __float_as_uint(p);
+          const U192 P = u192_shl(sig_of(pb), shift_of_exp(pb >> 23));
+          if (c > 0 && u192_geq(inc, P)) atomicMin(&S.win, tid);
           __syncthreads();
-#pragma unroll
-          for (int q = 0; q < kSelMaxPer; ++q)
-            if (q < PER) y[q] = keys[q * kSelThreads + (tid ^ j)];
-          __syncthreads();
+          if (tid == S.win) {
+            // What is left of p after every block of a higher exponent, in 2^sh units.
+            S.rem = u192_shr_ceil(u192_sub(P, u192_sub(inc, v)), sh);
+            S.prefix = (uint32_t)dg;
+            S.ties = c;
+          }
         } else {
-#pragma unroll
-          for (int q = 0; q < kSelMaxPer; ++q)
-            if (q < PER) y[q] = __shfl_xor(kv[q], j);
-        }
-#pragma unroll
-        for (int q = 0; q < kSelMaxPer; ++q) {
-          if (q < PER) {
-            const int a = q * kSelThreads + tid;
-            const bool lower = (a & j) == 0, up = (a & k) == 0;
-            const uint64_t x = kv[q];
-            kv[q] = (lower == up) ? (x < y[q] ? x : y[q]) : (x < y[q] ? y[q] : x);
+          const uint64_t inc = block_scan_u64<NW>(m, S);
+          const uint64_t target = S.rem;
+          if (c > 0 && inc >= target) atomicMin(&S.win, tid);
+          __syncthreads();
+          if (tid == S.win) {
+            S.rem = target - (inc - m);
+            S.prefix = (pre << (hsh - dsh)) | (uint32_t)dg;
+            S.ties = c;
           }
         }
-      }
-    }
-  }
-  // Re-distribute: thread t takes PER consecutive sorted positions.
-#pragma unroll
-  for (int q = 0; q < kSelMaxPer; ++q)
-    if (q < PER) keys[q * kSelThreads + tid] = kv[q];
-  __syncthreads();
-  U192 seg = u192_zero();
-#pragma unroll
-  for (int q = 0; q < kSelMaxPer; ++q) {
-    const int pos = tid * PER + q;
-    kv[q] = (q < PER && pos < nb) ? keys[pos] : ~0ull;
-    if (kv[q] != ~0ull) seg = u192_add(seg, score_units(__uint_as_float(~(uint32_t)(kv[q] >> 32))));
-  }
-
-  int64_t kstar = nb;
-  if (mode == 1) {
-    kstar = topk < nb ? topk : nb;
-  } else if (p < 1.0f) {
-    // Exclusive prefix of the segment sums: wave scan by shuffles, then wave totals.
-    U192 inc = seg;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const U192 o = u192_shfl_up(inc, d);
-      if (lane >= d) inc = u192_add(inc, o);
-    }
-    if (lane == 63) wave_tot[wave] = inc;
-    if (tid == 0) cut_pos = 0x7fffffff;
-    __syncthreads();
-    U192 wpre = u192_zero();
-    for (int w = 0; w < wave; ++w) wpre = u192_add(wpre, wave_tot[w]);
-    U192 excl = u192_shfl_up(inc, 1);
-    if (lane == 0) excl = u192_zero();
-    U192 run = u192_add(wpre, excl);
-    const U192 P = score_units(p);
-#pragma unroll
-    for (int q = 0; q < kSelMaxPer; ++q) {
-      if (kv[q] != ~0ull) {
-        run = u192_add(run, score_units(__uint_as_float(~(uint32_t)(kv[q] >> 32))));
-        if (u192_geq(run, P)) {
-          atomicMin(&cut_pos, tid * PER + q);
-          break;
+      } else {
+        const uint32_t inc = block_scan_u32<NW>(c, S);
+        const uint32_t target = S.rem_k;
+        if (c > 0 && inc >= target) atomicMin(&S.win, tid);
+        __syncthreads();
+        if (tid == S.win) {
+          S.rem_k = target - (inc - c);
+          S.prefix = pass == 0 ? (uint32_t)dg : ((pre << (hsh - dsh)) | (uint32_t)dg);
+          S.ties = c;
         }
       }
+      __syncthreads();
+      if (pass == 0 && S.win == kBins) {
+        // Every running sum stays below p: all blocks are kept.
+        if (tid == 0) S.keep_all = 1;
+        __syncthreads();
+        break;
+      }
+    }
+    if (!S.keep_all) {
+      ustar = S.prefix;
+      if (mode == 0) {
+        // The remainder is met by j ties of value sig(ustar) * 2^sh each.
+        const uint64_t t = sig_of(ustar);
+        const uint64_t r = S.rem;
+        jtie = t == 0 ? 1u : (uint32_t)((r + t - 1) / t);
+        if (jtie == 0) jtie = 1;
+      } else {
+        jtie = S.rem_k;
+      }
+    }
+  }
+  const bool keep_all = S.keep_all != 0;
+  const uint32_t ties = S.ties;
+
+  // When the cut splits a run of ties, rank them in ascending block index: slot-major,
+  // then wave, then lane, which is the order a = q * NT + tid.
+  uint32_t tie_rank[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) tie_rank[q] = 0;
+  if (ustar != kAbsent && jtie < ties) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const uint64_t msk = __ballot(u[q] == ustar);
+      tie_rank[q] = (uint32_t)__popcll(msk & ((1ull << lane) - 1));
+      if (lane == 0) S.tie_cnt[q * NW + wave] = (uint32_t)__popcll(msk);
     }
     __syncthreads();
-    if (cut_pos != 0x7fffffff) kstar = cut_pos + 1;
+    if (wave == 0) {
+      // Exclusive scan of the PER * NW tie counts, E per lane.
+      constexpr int E = (PER * NW + 63) / 64;
+      uint32_t loc[E], sl = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int idx = lane * E + e;
+        loc[e] = idx < PER * NW ? S.tie_cnt[idx] : 0u;
+        sl += loc[e];
+      }
+      uint32_t run = wave_scan_u32(sl) - sl;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int idx = lane * E + e;
+        if (idx < PER * NW) S.tie_pre[idx] = run;
+        run += loc[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) tie_rank[q] += S.tie_pre[q * NW + wave];
   }
 
   // Keep flags and kept-token count.
   int64_t cnt = 0;
 #pragma unroll
-  for (int q = 0; q < kSelMaxPer; ++q) {
-    if (kv[q] != ~0ull) {
-      const int pos = tid * PER + q;
-      const int64_t b = (int64_t)(uint32_t)kv[q];
-      const bool kept = (pos < kstar) || (b >= wfirst);
+  for (int q = 0; q < PER; ++q) {
+    const uint32_t x = u[q];
+    if (x != kAbsent) {
+      const int64_t b = (int64_t)q * NT + tid;
+      bool kept = keep_all || b >= wfirst;
+      if (!kept && ustar != kAbsent)
+        kept = x > ustar || (x == ustar && tie_rank[q] < jtie);
       keep[blk_off + b] = kept ? 1 : 0;
       if (kept) cnt += (L - b * G) < G ? (L - b * G) : G;
     }
   }
-  const int64_t total = block_sum_i64(cnt, red);
-  if (tid == 0) cu_out[i + 1] = (int32_t)total;
+  const int64_t total = block_sum_i64<NW>(cnt, S);
+  if (tid == 0) {
+    cu_out[i + 1] = (int32_t)total;
+    if (direct) cu_out[0] = 0;
+  }
 }
 
 // In-place inclusive scan of the per-request kept counts in cu_out[1..B]; cu_out[0] = 0.
@@ -272,15 +515,20 @@ hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, i
                          float p, int topk, int nb_max, int64_t T_host, int64_t nb_tot_host,
                          uint8_t* keep, int32_t* cu_out, int* err, hipStream_t st) {
   if (B == 0) return hipSuccess;
-  int NP = 1;
-  while (NP < nb_max) NP <<= 1;
-  const size_t lds = (size_t)(NP > kSelThreads ? NP : kSelThreads) * sizeof(uint64_t);
-  hipLaunchKernelGGL(up_select_kernel, dim3(B), dim3(kSelThreads), lds, st, scores, cu, B, n, G,
-                     mode, p, topk, NP, T_host, nb_tot_host, keep, cu_out, err);
+  // One request: its count is cu_out[1] itself, no scan launch needed.
+  const int direct = B == 1 ? 1 : 0;
+  if (nb_max <= 256 * kSelPer) {
+    hipLaunchKernelGGL(up_select_kernel<256>, dim3(B), dim3(256), 0, st, scores, cu, B, n, G,
+                       mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err);
+  } else {
+    hipLaunchKernelGGL(up_select_kernel<1024>, dim3(B), dim3(1024), 0, st, scores, cu, B, n, G,
+                       mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_select_finalize(int32_t* cu_out, int B, hipStream_t st) {
+  if (B == 1) return hipSuccess;   // written by the select kernel
   hipLaunchKernelGGL(up_select_finalize_kernel, dim3(1), dim3(1024), 0, st, cu_out, B);
   return hipGetLastError();
 }

@@ -75,7 +75,7 @@ hipError_t launch_normalize(const ScoreShape& s, const Totals& t, void* ws, cons
                             float* scores, hipStream_t st);
 
 // Selection (select.hip).  mode 0: Top-p with threshold p; mode 1: Top-k with k = topk.
-constexpr int kSelectMaxBlocks = 8192;
+constexpr int kSelectMaxBlocks = 16384;
 hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, int G, int mode,
                          float p, int topk, int nb_max, int64_t T_host, int64_t nb_tot_host,
                          uint8_t* keep, int32_t* cu_out, int* err, hipStream_t st);

@@ -106,7 +106,7 @@ def test_select_rejects_bad_arguments(L):
                             None) == UP_EINVAL
     assert L.up_topp_select(FAKE, FAKE, _p(cu), 1, 128, 64, ctypes.c_float(0.9), FAKE, None,
                             None) == UP_EINVAL
-    huge = _cu([64 * 8192 + 1])                                        # 8193 blocks
+    huge = _cu([64 * 16384 + 1])                                       # 16385 blocks
     assert L.up_topp_select(FAKE, FAKE, _p(huge), 1, 128, 64, ctypes.c_float(0.9), FAKE, FAKE,
                             None) == UP_EUNSUPPORTED
     assert L.up_topp_select(FAKE, FAKE, _p(np.array([0, 3, 2], np.int32)), 2, 128, 64,

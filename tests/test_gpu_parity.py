@@ -109,19 +109,38 @@ def test_select_is_bit_exact_on_oracle_scores():
     cu1 = np.array([0, 4096], np.int32)
     s1, _, _ = O.block_scores(qb, kb, cu1, 2, 1, 8, 128, 64)
     cases.append((s1, cu1, "ties"))
-    # block counts that use every exchange kind of the sort network (up to 8192 blocks)
-    big = [131072, 3000 * 64, 8192 * 64 - 5, 64 * 1500]
+    # large requests, up to the 16384-block limit (every slot of every thread in use)
+    big = [131072, 3000 * 64, 8192 * 64 - 5, 64 * 1500, 16384 * 64]
     cub = np.zeros(len(big) + 1, np.int32)
     cub[1:] = np.cumsum(big)
     sb = np.concatenate([rng.dirichlet(np.full(O.n_blocks(L, 64), 0.5)).astype(np.float32)
                          for L in big])
     cases.append((sb, cub, "large"))
+    # few distinct values: long tie runs at the cut, zeros, denormals, mixed exponents
+    vals = np.array([0.0, 2e-45, 1e-40, 3e-20, 0.125 / 4096, 0.25 / 4096, 0.5 / 4096], np.float32)
+    lens = [16384 * 64 - 17, 777 * 64, 64]
+    cut = np.zeros(len(lens) + 1, np.int32)
+    cut[1:] = np.cumsum(lens)
+    st = np.concatenate([rng.choice(vals, O.n_blocks(L, 64)) for L in lens]).astype(np.float32)
+    cases.append((st, cut, "tie runs"))
+    # a single block holding all the mass (score exactly 1.0) among zeros
+    s1b = np.zeros(9000, np.float32)
+    s1b[4321] = 1.0
+    cases.append((s1b, np.array([0, 9000 * 64], np.int32), "one-hot"))
     for s, c, name in cases:
         for p in (1e-6, 0.3, 0.9, 0.95, 0.99, 0.999, 1.0):
             say(f"[case] select {name} p={p} nb={s.size}")
             keep, cu_out = up.topp_select(torch.from_numpy(s).cuda(), i32_dev(c), c, 128, 64, p)
             torch.cuda.synchronize()
             ref_keep, ref_cu, _ = O.topp_select(s, c, 128, 64, p)
+            np.testing.assert_array_equal(keep.cpu().numpy(), ref_keep)
+            np.testing.assert_array_equal(cu_out.cpu().numpy(), ref_cu)
+        nbs = np.diff(np.array([0] + [O.n_blocks(int(L), 64) for L in np.diff(c)]).cumsum())
+        for k in (0, 1, 7, int(nbs.max()) // 3, int(nbs.max()) - 1, int(nbs.max()) + 5):
+            say(f"[case] topk select {name} k={k} nb={s.size}")
+            keep, cu_out = up.topk_select(torch.from_numpy(s).cuda(), i32_dev(c), c, 128, 64, k)
+            torch.cuda.synchronize()
+            ref_keep, ref_cu = O.topk_select(s, c, 128, 64, k)
             np.testing.assert_array_equal(keep.cpu().numpy(), ref_keep)
             np.testing.assert_array_equal(cu_out.cpu().numpy(), ref_cu)
     # exact boundaries: a running sum equal to p counts as reaching it
