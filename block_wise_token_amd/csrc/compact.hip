@@ -11,90 +11,138 @@
 // in order), and up_gather_kernel streams the runs with 16-byte loads and stores,
 // several workgroups per block.  The row-index list (idx_out) and positions come
 // out of the same pass.  Drop composition is a plain gather through idx.
+#include "up_dpp.h"
 #include "up_internal.h"
 
 namespace up {
 
-__device__ __forceinline__ int64_t wg_sum_i64(int64_t v, int64_t* wsum) {
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d);
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int64_t r = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) r += wsum[w];
-  __syncthreads();
-  return r;
-}
+// One workgroup.  Requests are taken 1024 at a time: their block counts are
+// scanned into block offsets (LDS), then the chunk's blocks -- contiguous in the
+// global block numbering -- are scanned in rounds of 1024 x 4, thread t taking 4
+// consecutive blocks.  A kept block's destination row is the number of kept tokens
+// before it in the whole batch, which equals cu_seqlens_out[i] + (kept tokens of
+// request i before it) exactly when cu_seqlens_out is the running sum of the kept
+// counts -- checked at every request's last block (cu_seqlens_out[i + 1] must equal
+// the running sum there).  Each block's request is found by binary search over the
+// chunk's offsets, for its source row and length.  Every write is bounded by the host
+// block count; hdr->valid = 1 only if all checks pass (the gather does nothing
+// otherwise).
+constexpr int kDstThreads = 1024;
+constexpr int kDstPer = 4;   // consecutive blocks per thread per round
 
-// Inclusive scan of an int64 over a 1024-thread workgroup; *total gets the sum.
-__device__ __forceinline__ int64_t wg_incl_scan_i64(int64_t v, int64_t* wsum, int64_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int64_t o = __shfl_up(v, d);
-    if (lane >= d) v += o;
-  }
-  if (lane == 63) wsum[wave] = v;
-  __syncthreads();
-  int64_t pre = 0, tot = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    if (w < wave) pre += wsum[w];
-    tot += wsum[w];
-  }
-  __syncthreads();
-  *total = tot;
-  return pre + v;
-}
-
-// One workgroup walks every request: validates cu_seqlens and cu_seqlens_out against
-// the host totals and the keep flags, and writes per global block its source row,
-// length and destination row (-1 when dropped).  hdr->valid = 1 only if all agree.
 __global__ __launch_bounds__(1024) void up_block_dst_kernel(
     const uint8_t* __restrict__ keep, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ cu_out, int B, int G, int64_t T_host, int64_t nb_tot_host,
     WsHeader* __restrict__ hdr, int32_t* __restrict__ dst, int32_t* __restrict__ src,
     int32_t* __restrict__ len, int* __restrict__ err) {
-  __shared__ int64_t wsum[16];
-  const int tid = threadIdx.x;
-  int64_t part = 0, neg = 0;
-  for (int r = tid; r < B; r += 1024) {
-    const int64_t L = (int64_t)cu[r + 1] - cu[r];
-    if (L < 0) neg += 1; else part += (L + G - 1) / G;
+  __shared__ int64_t wtot[2][16];
+  __shared__ int32_t req_boff[kDstThreads];   // chunk-relative first block of each request
+  __shared__ int32_t req_tok[kDstThreads];
+  __shared__ int32_t req_len[kDstThreads];
+  __shared__ int32_t req_oend[kDstThreads];   // cu_seqlens_out[i + 1]
+  __shared__ int bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t ends[4] = {0, 0, 0, 0};
+  if (tid == 0) {
+    bad = 0;
+    ends[0] = cu[0];
+    ends[1] = cu[B];
+    ends[2] = cu_out[0];
+    ends[3] = cu_out[B];
   }
-  const int64_t nbt = wg_sum_i64(part, wsum);
-  const int64_t nneg = wg_sum_i64(neg, wsum);
-  const bool ok = nneg == 0 && nbt == nb_tot_host && (int64_t)cu[B] == T_host && cu[0] == 0 &&
-                  cu_out[0] == 0;
-  if (!ok) {
-    if (tid == 0) { hdr->valid = 0; atomicOr(err, 1); }
-    return;
-  }
-  bool consistent = true;
-  int64_t boff = 0;
-  for (int i = 0; i < B; ++i) {
-    const int64_t L = (int64_t)cu[i + 1] - cu[i];
-    const int64_t nb = (L + G - 1) / G;
-    const int64_t tok = cu[i], out0 = cu_out[i];
-    int64_t carry = 0;
-    for (int64_t base = 0; base < nb; base += 1024) {
-      const int64_t b = base + tid;
-      const int64_t bl = (b < nb) ? ((L - b * G) < G ? (L - b * G) : G) : 0;
-      const bool kept = (b < nb) && keep[boff + b] != 0;
-      const int64_t kl = kept ? bl : 0;
-      int64_t tot;
-      const int64_t inc = wg_incl_scan_i64(kl, wsum, &tot);
-      if (b < nb) {
-        dst[boff + b] = kept ? (int32_t)(out0 + carry + inc - kl) : -1;
-        src[boff + b] = (int32_t)(tok + b * G);
-        len[boff + b] = (int32_t)bl;
-      }
-      carry += tot;
+  __syncthreads();
+  int64_t blk_base = 0;   // global index of the chunk's first block
+  int64_t kept_base = 0;  // kept tokens before the chunk
+  int par = 0;            // which wtot buffer the next scan uses
+  // Exclusive scan of v over the workgroup (in thread order) and its total.
+  auto scan = [&](int64_t v, int64_t& total) -> int64_t {
+    const uint64_t inc = wave_scan_u64((uint64_t)v);
+    if (lane == 63) wtot[par][wave] = (int64_t)inc;
+    __syncthreads();
+    int64_t pre = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int64_t t = wtot[par][w];
+      pre += w < wave ? t : 0;
+      all += t;
     }
-    if ((int64_t)cu_out[i + 1] - out0 != carry) consistent = false;
-    boff += nb;
+    par ^= 1;   // the next scan writes the other buffer: one barrier per scan suffices
+    total = all;
+    return pre + (int64_t)inc - v;
+  };
+  for (int base = 0; base < B; base += kDstThreads) {
+    const int r = base + tid;
+    int64_t nb_r = 0;
+    if (r < B) {
+      const int32_t t0 = cu[r], t1 = cu[r + 1];
+      const int64_t Lr = (int64_t)t1 - t0;
+      if (Lr < 0) atomicOr(&bad, 1);
+      nb_r = Lr > 0 ? (Lr + G - 1) / G : 0;
+      const int32_t o0 = cu_out[r], o1 = cu_out[r + 1];
+      req_tok[tid] = t0;
+      req_len[tid] = Lr > 0 ? (int32_t)Lr : 0;
+      req_oend[tid] = o1;
+      // An empty request keeps nothing: its two cu_seqlens_out entries must agree.
+      if (nb_r == 0 && o1 != o0) atomicOr(&bad, 1);
+    }
+    int64_t chunk_blocks;
+    const int64_t boff = scan(nb_r, chunk_blocks);
+    const int nreq = (B - base) < kDstThreads ? (B - base) : kDstThreads;
+    if (r < B) req_boff[tid] = (int32_t)(boff < INT32_MAX ? boff : INT32_MAX);
+    __syncthreads();
+    for (int64_t rb = 0; rb < chunk_blocks; rb += (int64_t)kDstThreads * kDstPer) {
+      const int64_t g0 = rb + (int64_t)tid * kDstPer;   // chunk-relative
+      // Request of block g0: the last request whose first block is <= g0.
+      int lo = 0, hi = nreq - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (req_boff[mid] <= g0) lo = mid; else hi = mid - 1;
+      }
+      int rr = lo;
+      int64_t kl[kDstPer];
+      int64_t tot = 0;
+      {
+        int q = rr;
+#pragma unroll
+        for (int j = 0; j < kDstPer; ++j) {
+          const int64_t g = g0 + j;
+          kl[j] = 0;
+          if (g < chunk_blocks && blk_base + g < nb_tot_host) {
+            while (q + 1 < nreq && req_boff[q + 1] <= g) ++q;
+            const int64_t b = g - req_boff[q];
+            const int64_t L = req_len[q];
+            if (keep[blk_base + g] != 0) kl[j] = (L - b * G) < G ? (L - b * G) : G;
+          }
+          tot += kl[j];
+        }
+      }
+      int64_t round_kept;
+      int64_t run = kept_base + scan(tot, round_kept);
+      int q = rr;
+#pragma unroll
+      for (int j = 0; j < kDstPer; ++j) {
+        const int64_t g = g0 + j;
+        if (g < chunk_blocks && blk_base + g < nb_tot_host) {
+          while (q + 1 < nreq && req_boff[q + 1] <= g) ++q;
+          const int64_t b = g - req_boff[q];
+          const int64_t L = req_len[q];
+          const int64_t bl = (L - b * G) < G ? (L - b * G) : G;
+          dst[blk_base + g] = kl[j] ? (int32_t)run : -1;
+          src[blk_base + g] = (int32_t)(req_tok[q] + b * G);
+          len[blk_base + g] = (int32_t)bl;
+          run += kl[j];
+          // The request's last block: the running sum must be cu_seqlens_out[i + 1].
+          if ((b + 1) * G >= L && (int64_t)req_oend[q] != run) atomicOr(&bad, 1);
+        }
+      }
+      kept_base += round_kept;
+    }
+    blk_base += chunk_blocks;
+    __syncthreads();   // before the next chunk overwrites the request tables
   }
   if (tid == 0) {
-    const bool v = consistent && (int64_t)cu_out[B] <= T_host;
+    const bool v = !bad && ends[0] == 0 && (int64_t)ends[1] == T_host && ends[2] == 0 &&
+                   (int64_t)ends[3] <= T_host && blk_base == nb_tot_host;
     hdr->valid = v ? 1 : 0;
     if (!v) atomicOr(err, 1);
   }

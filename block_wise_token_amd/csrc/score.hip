@@ -18,7 +18,7 @@
 //                            against the host-derived totals
 //   up_score_partial_kernel  Q K^T on bf16 MFMA (32x32x16), per-(row, block) (m_b, l_b)
 //                            and per-(row, key chunk) merged statistics
-//   up_row_stats_kernel      merge chunk statistics into per-row (m, l)
+//   up_row_stats_kernel      merge chunk statistics into per-row (m, 1 / l)
 //   up_block_mass_kernel     per-block mass, float64 sums in a fixed order
 //   up_normalize_kernel      per-request normalisation to scores that sum to one
 #include "up_internal.h"
@@ -535,13 +535,16 @@ __global__ __launch_bounds__(1024) void up_row_stats_kernel(
   if (wave == 0 && x < total_rows) {
     float Mt = kNegInf, St = 0.f;
     for (int w = 0; w < 16; ++w) merge_ml(Mt, St, part[w][lane].x, part[w][lane].y);
-    rs[x] = make_float2(Mt, St);
+    rs[x] = make_float2(Mt, St > 0.f ? 1.f / St : 0.f);   // (row max, 1 / row sum)
   }
 }
 
 // ---------------------------------------------------------------------------
-// Block masses: mass[b] = sum_{g, r} 2^(m_b - m) * l_b / l, float64, fixed order.
-// One workgroup per global block.
+// Block masses.  mass[b] = sum_{g, r} l_b * 2^(m_b - M) * (1 / l), where (M, 1 / l)
+// are the row's statistics: each term in float32, summed in float64 in a fixed
+// order.  One workgroup per global block.  (A last-workgroup-normalises variant
+// needs an agent-scope release per workgroup, an L2 writeback on every XCD, which
+// costs far more than the separate normalisation launch.)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int request_of_block(const ReqPlan* __restrict__ plan, int B,
                                                 int64_t x) {
@@ -553,16 +556,14 @@ __device__ __forceinline__ int request_of_block(const ReqPlan* __restrict__ plan
   return lo;
 }
 
-template <int NT>
-__device__ __forceinline__ double block_sum_f64(double v, double* red) {
-  red[threadIdx.x] = v;
-  __syncthreads();
+// Sum over a 256-thread workgroup in a fixed order (butterfly within each wave, then
+// the four wave sums in order); every thread gets the same value.
+__device__ __forceinline__ double wg256_sum_f64(double v, double* red) {
 #pragma unroll
-  for (int w = NT / 2; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  const double r = red[0];
+  for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const double r = (red[0] + red[1]) + (red[2] + red[3]);
   __syncthreads();
   return r;
 }
@@ -570,7 +571,7 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 __global__ __launch_bounds__(256) void up_block_mass_kernel(
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq,
     const float2* __restrict__ ml, const float2* __restrict__ rs, double* __restrict__ mass) {
-  __shared__ double red[256];
+  __shared__ double red[4];
   if (hdr->valid != 1) return;
   const int64_t blk = blockIdx.x;
   const int i = request_of_block(plan, B, blk);
@@ -580,13 +581,24 @@ __global__ __launch_bounds__(256) void up_block_mass_kernel(
   const int64_t terms = (int64_t)Hq * pr.W;           // Hkv * R
   const float2* mrow = ml + pr.ml_off + b * terms;
   const float2* rrow = rs + (int64_t)pr.win_off * Hq;
+  constexpr int U = 8;
   double acc = 0.0;
-  for (int64_t e = threadIdx.x; e < terms; e += 256) {
-    const float2 v = mrow[e];
-    const float2 w = rrow[e];
-    acc += (double)v.y * (double)fast_exp2(v.x - w.x) / (double)w.y;
+  int64_t e = threadIdx.x;
+  for (; e + (U - 1) * 256 < terms; e += U * 256) {
+    float2 v[U], w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = mrow[e + u * 256];
+      w[u] = rrow[e + u * 256];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += (double)(v[u].y * fast_exp2(v[u].x - w[u].x) * w[u].y);
   }
-  const double tot = block_sum_f64<256>(acc, red);
+  for (; e < terms; e += 256) {
+    const float2 v = mrow[e], w = rrow[e];
+    acc += (double)(v.y * fast_exp2(v.x - w.x) * w.y);
+  }
+  const double tot = wg256_sum_f64(acc, red);
   if (threadIdx.x == 0) mass[blk] = tot;
 }
 
@@ -597,14 +609,14 @@ __global__ __launch_bounds__(256) void up_block_mass_kernel(
 __global__ __launch_bounds__(256) void up_normalize_kernel(
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B,
     const double* __restrict__ mass, float* __restrict__ scores) {
-  __shared__ double red[256];
+  __shared__ double red[4];
   if (hdr->valid != 1) return;
   const int i = blockIdx.x;
   if (i >= B) return;
   const ReqPlan pr = plan[i];
   double acc = 0.0;
   for (int b = threadIdx.x; b < pr.nb; b += 256) acc += mass[pr.blk_off + b];
-  const double tot = block_sum_f64<256>(acc, red);
+  const double tot = wg256_sum_f64(acc, red);
   for (int b = threadIdx.x; b < pr.nb; b += 256)
     scores[pr.blk_off + b] = (float)(mass[pr.blk_off + b] / tot);
 }

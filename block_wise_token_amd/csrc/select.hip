@@ -22,6 +22,7 @@
 // equals the one a sequential exact running sum over the sorted order gives.
 // Among the blocks whose score equals the cut score (ties), the remainder decides
 // how many are kept, taken in ascending block index.
+#include "up_dpp.h"
 #include "up_internal.h"
 
 namespace up {
@@ -122,43 +123,12 @@ __device__ __forceinline__ uint32_t sig_of(uint32_t u) {
 }
 __device__ __forceinline__ int shift_of_exp(uint32_t e) { return e ? (int)e - 1 : 0; }
 
-// Wave-wide inclusive scans with DPP row shifts and row broadcasts (no LDS round
-// trips): shifts by 1, 2, 4, 8 within each row of 16 lanes, then lane 15 of a row
-// into the next row, then lane 31 into rows 2 and 3.  Lanes with no source read 0.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ uint32_t dpp_in(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xf, true);
-}
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ uint64_t dpp_in64(uint64_t v) {
-  const uint32_t lo = dpp_in<CTRL, ROWMASK>((uint32_t)v);
-  const uint32_t hi = dpp_in<CTRL, ROWMASK>((uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
 template <int CTRL, int ROWMASK>
 __device__ __forceinline__ U192 dpp_in192(U192 v) {
   return U192{dpp_in64<CTRL, ROWMASK>(v.lo), dpp_in64<CTRL, ROWMASK>(v.mid),
               dpp_in64<CTRL, ROWMASK>(v.hi)};
 }
 
-__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
-  v += dpp_in<0x111, 0xf>(v);
-  v += dpp_in<0x112, 0xf>(v);
-  v += dpp_in<0x114, 0xf>(v);
-  v += dpp_in<0x118, 0xf>(v);
-  v += dpp_in<0x142, 0xa>(v);
-  v += dpp_in<0x143, 0xc>(v);
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
-  v += dpp_in64<0x111, 0xf>(v);
-  v += dpp_in64<0x112, 0xf>(v);
-  v += dpp_in64<0x114, 0xf>(v);
-  v += dpp_in64<0x118, 0xf>(v);
-  v += dpp_in64<0x142, 0xa>(v);
-  v += dpp_in64<0x143, 0xc>(v);
-  return v;
-}
 __device__ __forceinline__ U192 wave_scan_u192(U192 v) {
   v = u192_add(v, dpp_in192<0x111, 0xf>(v));
   v = u192_add(v, dpp_in192<0x112, 0xf>(v));

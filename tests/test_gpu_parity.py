@@ -207,3 +207,86 @@ def test_inconsistent_device_cu_seqlens_raises_error_word():
     torch.cuda.synchronize()
     assert out.cpu().numpy().tolist() == [0, 9, -1, -1]
     assert up.device_error() & 2
+
+
+def test_inconsistent_compaction_inputs_write_nothing():
+    """expand_compact and select on device inputs that disagree with the host copy or
+    with each other: nothing is written and error bit 1 is raised."""
+    G, T, H = 64, 4096, 64
+    cu_h = np.array([0, T], np.int32)
+    rng = np.random.default_rng(5)
+    hid = bf16_dev(rng.integers(0, 1 << 15, (T, H)).astype(np.uint16))
+    pos = i32_dev(np.arange(T, dtype=np.int32))
+    keep = torch.ones(T // G, dtype=torch.uint8, device="cuda")
+    keep[3] = 0
+    good_out = i32_dev(np.array([0, T - G], np.int32))
+    cases = {
+        "cu_out disagrees with keep": (i32_dev(cu_h), i32_dev(np.array([0, T], np.int32))),
+        "device cu disagrees with host": (i32_dev(np.array([0, T - 5], np.int32)), good_out),
+        "cu_out[0] not zero": (i32_dev(cu_h), i32_dev(np.array([G, T], np.int32))),
+    }
+    up.device_error()
+    for name, (cu_d, cu_out_d) in cases.items():
+        say(f"[case] compaction: {name}")
+        idx_out = torch.full((T,), -9, dtype=torch.int32, device="cuda")
+        hid_out = torch.zeros((T, H), dtype=torch.bfloat16, device="cuda")
+        pos_out = torch.full((T,), -9, dtype=torch.int32, device="cuda")
+        up.expand_compact(hid, pos, keep, cu_d, cu_out_d, cu_h, G, idx_out=idx_out,
+                          hidden_out=hid_out, pos_out=pos_out)
+        torch.cuda.synchronize()
+        assert up.device_error() & 1, name
+        assert torch.all(idx_out == -9) and torch.all(pos_out == -9), name
+        assert torch.all(hid_out.view(torch.int16) == 0), name
+    # the consistent call on the same buffers compacts (one dropped block)
+    idx_out, hid_out, pos_out = up.expand_compact(hid, pos, keep, i32_dev(cu_h), good_out, cu_h,
+                                                  G)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    want = np.concatenate([np.arange(3 * G), np.arange(4 * G, T)]).astype(np.int32)
+    np.testing.assert_array_equal(idx_out[:T - G].cpu().numpy(), want)
+    np.testing.assert_array_equal(pos_out[:T - G].cpu().numpy(), want)
+    # select with a device cu_seqlens that disagrees with the host copy
+    say("[case] select: device cu disagrees with host")
+    sc = torch.full((T // G,), 1.0 / (T // G), device="cuda")
+    keep2 = torch.full((T // G,), 7, dtype=torch.uint8, device="cuda")
+    for fn, arg in ((up.topp_select, 0.9), (up.topk_select, 5)):
+        fn(sc, i32_dev(np.array([0, T - 5], np.int32)), cu_h, 128, G, arg, keep=keep2)
+        torch.cuda.synchronize()
+        assert up.device_error() & 1
+        assert torch.all(keep2 == 7)
+
+
+def test_many_short_requests_select_and_compact():
+    """2500 requests (more than one 1024-request chunk of the compaction scan), lengths
+    0..300 with empty ones, G = 32: select and compaction against the oracle."""
+    rng = np.random.default_rng(21)
+    B, G, n, H = 2500, 32, 64, 32
+    lens = rng.integers(0, 301, B)
+    lens[rng.integers(0, B, 200)] = 0
+    cu_h = np.zeros(B + 1, np.int32)
+    cu_h[1:] = np.cumsum(lens)
+    T = int(cu_h[-1])
+    nbs = [O.n_blocks(int(L), G) for L in lens]
+    s = np.concatenate([rng.dirichlet(np.full(k, 0.4)).astype(np.float32) if k else
+                        np.zeros(0, np.float32) for k in nbs])
+    say(f"[case] many short requests: B={B} T={T} blocks={s.size}")
+    cu_d = i32_dev(cu_h)
+    keep, cu_out = up.topp_select(torch.from_numpy(s).cuda(), cu_d, cu_h, n, G, 0.7)
+    torch.cuda.synchronize()
+    ref_keep, ref_cu, _ = O.topp_select(s, cu_h, n, G, 0.7)
+    np.testing.assert_array_equal(keep.cpu().numpy(), ref_keep)
+    np.testing.assert_array_equal(cu_out.cpu().numpy(), ref_cu)
+    hid_np = rng.integers(0, 1 << 15, (T, H)).astype(np.uint16)
+    pos_np = rng.integers(0, 1 << 30, T).astype(np.int32)
+    idx_out, hid_out, pos_out = up.expand_compact(bf16_dev(hid_np), i32_dev(pos_np), keep, cu_d,
+                                                  cu_out, cu_h, G)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    idx_ref = O.expand(ref_keep.astype(np.uint8), cu_h, G)
+    cnt = int(ref_cu[-1])
+    assert cnt == idx_ref.size
+    np.testing.assert_array_equal(idx_out[:cnt].cpu().numpy(), idx_ref)
+    h_ref, p_ref = O.compact_fast(hid_np, pos_np, idx_ref)
+    np.testing.assert_array_equal(hid_out[:cnt].view(torch.int16).cpu().numpy().view(np.uint16),
+                                  h_ref)
+    np.testing.assert_array_equal(pos_out[:cnt].cpu().numpy(), p_ref)
