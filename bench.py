@@ -10,6 +10,7 @@ tokens).  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -28,6 +29,28 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of this workload, scaled by the plain-copy calibration; None
+    if there is no summary or the kernel's source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    scale = None
+    for line in open(path):
+        parts = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
+        if line.startswith("scale "):
+            scale = float(parts["fetch"]), float(parts["write"])
+        elif parts.get("kernel") == kernel and scale:
+            src = os.path.join(ROOT, parts["source"])
+            if not os.path.exists(src):
+                return None
+            if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != parts["sha256"]:
+                return None
+            return (float(parts["fetch_kib"]) * scale[0] + float(parts["write_kib"]) * scale[1]) * 1024
+    return None
 
 
 def causal_pairs(L: int, W: int) -> int:
@@ -129,11 +152,13 @@ def main():
     gather_gbs = gather_bytes / (g_us * 1e-6) / 1e9
     roof_score = {"bound": "mfma", "achieved": round(score_tflops, 2),
                   "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                  "frac": round(score_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                  "frac": round(score_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "traffic": measured_traffic(args.workload, "up_score_partial_kernel"),
                   "kernel": "up_score_partial_kernel", "avg_us": round(s_us, 2),
                   "work_per_launch": score_flops}
     roof_gather = {"bound": "hbm", "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS,
-                   "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                   "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
+                   "traffic": measured_traffic(args.workload, "up_gather_kernel"),
                    "kernel": "up_gather_kernel", "avg_us": round(g_us, 2),
                    "work_per_launch": gather_bytes}
     dominant = roof_gather if g_us >= s_us else roof_score

@@ -48,7 +48,7 @@ def lib():
     L.up_expand_compact_workspace.argtypes = [vp, ci, ci]
     L.up_expand_compact.restype = ci
     L.up_expand_compact.argtypes = [vp, ci, ci, i32p, u8p, i32p, i32p, vp, ci, ci, i32p, vp, i32p,
-                                    vp, cs, vp]
+                                    i32p, i32p, vp, cs, vp]
     L.up_compose_drops.restype = ci
     L.up_compose_drops.argtypes = [i32p, ci, i32p, i32p, ci, i32p, vp]
     L.up_device_error.restype = ci
@@ -163,8 +163,10 @@ def topk_select(scores, cu_seqlens, cu_h, n, G, topk, keep=None, cu_out=None, st
 
 
 def expand_compact(hidden, pos, keep, cu_seqlens, cu_out, cu_h, G, idx_out=None, hidden_out=None,
-                   pos_out=None, workspace=None, stream=None):
-    """Kept-token rows: (idx_out, hidden_out, pos_out), each with capacity T rows."""
+                   pos_out=None, workspace=None, stream=None, prev_orig=None, orig_out=None):
+    """Kept-token rows: (idx_out, hidden_out, pos_out), each with capacity T rows.
+    With ``prev_orig`` given, ``orig_out[r] = prev_orig[idx_out[r]]`` is written in the
+    same pass (pass ``orig_out`` to choose the buffer)."""
     if not hidden.is_cuda or not hidden.is_contiguous():
         raise ValueError("hidden must be a contiguous device tensor")
     _dev(keep, torch.uint8, "keep_blocks")
@@ -183,13 +185,19 @@ def expand_compact(hidden, pos, keep, cu_seqlens, cu_out, cu_h, G, idx_out=None,
         hidden_out = torch.empty((T, H), dtype=hidden.dtype, device=dev)
     if pos_out is None and pos is not None:
         pos_out = torch.empty(T, dtype=torch.int32, device=dev)
+    if prev_orig is not None:
+        _dev(prev_orig, torch.int32, "prev_orig")
+        if orig_out is None:
+            orig_out = torch.empty(T, dtype=torch.int32, device=dev)
+    elif orig_out is not None:
+        raise ValueError("orig_out needs prev_orig")
     need = int(lib().up_expand_compact_workspace(h.ptr, h.B, G))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = lib().up_expand_compact(_ptr(hidden), H, eb, _ptr(pos), _ptr(keep), _ptr(cu_seqlens),
                                  _ptr(cu_out), h.ptr, h.B, G, _ptr(idx_out), _ptr(hidden_out),
-                                 _ptr(pos_out), _ptr(workspace), workspace.numel(),
-                                 _stream(stream))
+                                 _ptr(pos_out), _ptr(prev_orig), _ptr(orig_out), _ptr(workspace),
+                                 workspace.numel(), _stream(stream))
     _check(st, "up_expand_compact")
     return idx_out, hidden_out, pos_out
 
@@ -235,8 +243,10 @@ def profile_read(name: str):
 class LayerDecision:
     """One full-attention layer decision with every buffer allocated up front.
 
-    ``run()`` issues the four calls -- scores, Top-p, expand+compact, compose -- on
-    the current stream and allocates nothing.
+    ``run()`` issues the calls -- scores, Top-p, expand+compact with the drop
+    composition fused into the compaction pass -- on the current stream and
+    allocates nothing.  (``up_compose_drops`` is the standalone form of the last
+    step.)
     """
 
     def __init__(self, qwin, k, cu_seqlens, cu_h, hidden, pos, n, G, p, scale=0.0,
@@ -273,6 +283,5 @@ class LayerDecision:
                         cu_out=self.cu_out, stream=stream)
         expand_compact(self.hidden, self.pos, self.keep, self.cu, self.cu_out, self.h.arr, self.G,
                        idx_out=self.idx, hidden_out=self.hidden_out, pos_out=self.pos_out,
-                       workspace=self.ws_compact, stream=stream)
-        compose_drops(self.prev_orig, self.idx, self.cu_out[self.h.B:self.h.B + 1],
-                      capacity=self.h.T, out=self.orig, stream=stream)
+                       workspace=self.ws_compact, stream=stream, prev_orig=self.prev_orig,
+                       orig_out=self.orig)

@@ -119,7 +119,7 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
   s->B = B; s->Hq = Hq; s->Hkv = Hkv; s->d = d; s->n = n; s->G = G;
   s->qt = (d == 256) ? 1 : 2;
   s->kt = (d == 256) ? 1 : (G % 64 == 0 ? 2 : 1);
-  s->rows_wg = 8 * s->qt * 32;
+  s->rows_wg = score_rows_wg(d);
   const int64_t gs = Hq / Hkv;
   int64_t units = 0;
   for (int i = 0; i < B; ++i) {
@@ -129,12 +129,12 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
     const int64_t nrt = (gs * W + s->rows_wg - 1) / s->rows_wg;
     units += nb * Hkv * nrt;
   }
-  // Key-chunk length (blocks per workgroup).  One 8-wave workgroup fills a CU, so
-  // the score pass takes ceil(items / CUs) rounds of CB blocks each: pick the CB
-  // that minimises that product (ties: the larger CB, fewer workgroups).
+  // Key-chunk length (blocks per workgroup).  score_wgs_per_cu(d) workgroups fill a
+  // CU, so the score pass takes ceil(items / slots) rounds of CB blocks each: pick
+  // the CB that minimises that product (ties: the larger CB, fewer workgroups).
   (void)units;
   {
-    const int64_t cus = device_cus();
+    const int64_t cus = (int64_t)device_cus() * score_wgs_per_cu(d);
     int64_t best_cost = -1;
     int best_cb = 1;
     for (int cb = 256; cb >= 1; --cb) {
@@ -281,7 +281,8 @@ size_t up_expand_compact_workspace(const int32_t* cu_seqlens_h, int B, int G) {
 int up_expand_compact(const void* hidden, int H, int elem_bytes, const int32_t* pos,
                       const uint8_t* keep_blocks, const int32_t* cu_seqlens,
                       const int32_t* cu_seqlens_out, const int32_t* cu_seqlens_h, int B, int G,
-                      int32_t* idx_out, void* hidden_out, int32_t* pos_out, void* workspace,
+                      int32_t* idx_out, void* hidden_out, int32_t* pos_out,
+                      const int32_t* prev_orig, int32_t* orig_out, void* workspace,
                       size_t workspace_bytes, void* stream) {
   if (B < 0 || G <= 0 || H <= 0 || elem_bytes <= 0) return UP_EINVAL;
   if (!cu_ok(cu_seqlens_h, B)) return UP_EINVAL;
@@ -290,6 +291,7 @@ int up_expand_compact(const void* hidden, int H, int elem_bytes, const int32_t* 
   if (!hidden || !keep_blocks || !cu_seqlens || !cu_seqlens_out || !idx_out || !hidden_out)
     return UP_EINVAL;
   if (pos_out && !pos) return UP_EINVAL;
+  if (orig_out && !prev_orig) return UP_EINVAL;
   const int64_t row_bytes = (int64_t)H * elem_bytes;
   if (sp.T * row_bytes / row_bytes != sp.T) return UP_EUNSUPPORTED;
   const CompactWs L = compact_ws_layout(sp.nb_tot);
@@ -305,7 +307,7 @@ int up_expand_compact(const void* hidden, int H, int elem_bytes, const int32_t* 
   if (e != hipSuccess) return UP_EHIP;
   e = timed(7, hs, [&] {
     return launch_gather(hidden, row_bytes, pos, workspace, L, sp.nb_tot, G, idx_out, hidden_out,
-                         pos_out, hs);
+                         pos_out, prev_orig, orig_out, hs);
   });
   return e == hipSuccess ? UP_OK : UP_EHIP;
 }

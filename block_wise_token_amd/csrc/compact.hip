@@ -162,7 +162,8 @@ __global__ __launch_bounds__(NT) void up_gather_kernel(
     const WsHeader* __restrict__ hdr, const int32_t* __restrict__ dst,
     const int32_t* __restrict__ src, const int32_t* __restrict__ len, int split,
     int32_t* __restrict__ idx_out, uint8_t* __restrict__ hidden_out,
-    int32_t* __restrict__ pos_out) {
+    int32_t* __restrict__ pos_out, const int32_t* __restrict__ prev_orig,
+    int32_t* __restrict__ orig_out) {
   if (hdr->valid != 1) return;
   const int64_t blk = blockIdx.x / split;
   const int part = (int)(blockIdx.x % split);
@@ -187,6 +188,7 @@ __global__ __launch_bounds__(NT) void up_gather_kernel(
     for (int t = threadIdx.x; t < n; t += NT) {
       idx_out[d + t] = (int32_t)(s + t);
       if (pos_out) pos_out[d + t] = pos[s + t];
+      if (orig_out) orig_out[d + t] = prev_orig[s + t];   // drop composition, fused
     }
   }
 }
@@ -240,7 +242,8 @@ hipError_t launch_block_dst(const uint8_t* keep, const int32_t* cu, const int32_
 
 hipError_t launch_gather(const void* hidden, int64_t row_bytes, const int32_t* pos, void* ws,
                          const CompactWs& L, int64_t nb_tot, int G, int32_t* idx_out,
-                         void* hidden_out, int32_t* pos_out, hipStream_t st) {
+                         void* hidden_out, int32_t* pos_out, const int32_t* prev_orig,
+                         int32_t* orig_out, hipStream_t st) {
   if (nb_tot == 0) return hipSuccess;
   // Many small workgroups (4 KiB each, two 16-byte vectors per lane in flight)
   // stream fastest on MI355X: about 6.5 TB/s read+write for a plain 1 GiB copy.
@@ -260,13 +263,13 @@ hipError_t launch_gather(const void* hidden, int64_t row_bytes, const int32_t* p
   const uintptr_t al = reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(hidden_out);
   if (row_bytes % 16 == 0 && al % 16 == 0) {
     hipLaunchKernelGGL((up_gather_kernel<u32x4, NT, 2>), grid, dim3(NT), 0, st, h, row_bytes, pos,
-                       hdr, dst, src, len, split, idx_out, ho, pos_out);
+                       hdr, dst, src, len, split, idx_out, ho, pos_out, prev_orig, orig_out);
   } else if (row_bytes % 4 == 0 && al % 4 == 0) {
     hipLaunchKernelGGL((up_gather_kernel<uint32_t, NT, 4>), grid, dim3(NT), 0, st, h, row_bytes,
-                       pos, hdr, dst, src, len, split, idx_out, ho, pos_out);
+                       pos, hdr, dst, src, len, split, idx_out, ho, pos_out, prev_orig, orig_out);
   } else {
     hipLaunchKernelGGL((up_gather_kernel<uint8_t, NT, 4>), grid, dim3(NT), 0, st, h, row_bytes,
-                       pos, hdr, dst, src, len, split, idx_out, ho, pos_out);
+                       pos, hdr, dst, src, len, split, idx_out, ho, pos_out, prev_orig, orig_out);
   }
   return hipGetLastError();
 }

@@ -178,18 +178,18 @@ __device__ __forceinline__ void wait_vm_lgkm_barrier(int n) {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int D, int QT, int NS>
-__global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
+template <int D, int QT, int NS, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
     const uint16_t* __restrict__ qwin, const uint16_t* __restrict__ kmat,
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
     int G, int CB, float c, float2* __restrict__ ml, float2* __restrict__ cs) {
-  constexpr int NT = 512;
+  constexpr int NT = 64 * NW;
   constexpr int UK = 64;               // keys per LDS stage (two 32-key halves)
   constexpr int RB = 2 * D;            // LDS bytes per key row
   constexpr int SB = UK * RB;          // LDS bytes per stage
   constexpr int SPT = SB / (NT * 16);  // 16-byte DMA copies per lane per stage
   constexpr int DS = D / 16;           // MFMA k-steps over the head dimension
-  constexpr int ROWS = 8 * QT * 32;    // query rows per workgroup
+  constexpr int ROWS = NW * QT * 32;   // query rows per workgroup
   constexpr int EPS = 16 / DS;         // softmax elements per tile per k-step
   static_assert(SB % (NT * 16) == 0, "stage must be a whole number of DMA rounds");
   static_assert((NS - 2) * SPT <= 15, "vmcnt wait range");
@@ -412,13 +412,14 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
   // `so` interleaved with the exp-and-sum of h.
   auto step_fast = [&](int h, uint32_t so, f32x16 (&cur)[QT], f32x16 (&nxt)[QT]) {
     float part[QT][2];
-#pragma unroll
-    for (int t = 0; t < QT; ++t) { part[t][0] = 0.f; part[t][1] = 0.f; }
-    // All A operands of half h+1 are requested up front, so MFMA s waits for read s only.
+    // All A operands of half h+1 are requested up front, in the order the MFMAs use
+    // them (one scheduling region per read), so MFMA s waits for read s only.
     bf16x8 a[DS];
 #pragma unroll
-    for (int ks = 0; ks < DS; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(lds + so + rd_off[ks]);
-    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of everything below
+    for (int ks = 0; ks < DS; ++ks) {
+      a[ks] = *reinterpret_cast<const bf16x8*>(lds + so + rd_off[ks]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int ks = 0; ks < DS; ++ks) {
 #pragma unroll
@@ -430,7 +431,8 @@ __global__ __launch_bounds__(512, 1) void up_score_partial_kernel(
 #pragma unroll
         for (int q = 0; q < EPS; ++q) {
           const int e = ks * EPS + q;
-          part[t][e & 1] += fast_exp2(fmaf(cur[t][e], c, -Rs[t]));
+          const float v = fast_exp2(fmaf(cur[t][e], c, -Rs[t]));
+          if (e < 2) part[t][e] = v; else part[t][e & 1] += v;
         }
     }
     float sum[QT];
@@ -646,11 +648,13 @@ hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Total
   return hipGetLastError();
 }
 
-template <int D, int QT, int NS>
+template <int D, int QT, int NS, int NW>
 static hipError_t launch_partial_t(const void* qwin, const void* k, const ScoreShape& s,
                                    const Totals& t, void* ws, const ScoreWs& L, float c,
                                    hipStream_t st) {
-  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, NS>), dim3((unsigned)t.items), dim3(512), 0,
+  static_assert(NW * QT * 32 == score_rows_wg(D), "row tile of the kernel and of the plan");
+  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, NS, NW>), dim3((unsigned)t.items),
+                     dim3(64 * NW), 0,
                      st, static_cast<const uint16_t*>(qwin), static_cast<const uint16_t*>(k),
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq, s.Hkv, s.G,
@@ -664,9 +668,9 @@ hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShap
                                 hipStream_t st) {
   if (t.items == 0) return hipSuccess;
   switch (s.d) {
-    case 64: return launch_partial_t<64, 2, 8>(qwin, k, s, t, ws, L, c, st);
-    case 128: return launch_partial_t<128, 2, 4>(qwin, k, s, t, ws, L, c, st);
-    case 256: return launch_partial_t<256, 1, 4>(qwin, k, s, t, ws, L, c, st);
+    case 64: return launch_partial_t<64, 2, 8, 8>(qwin, k, s, t, ws, L, c, st);
+    case 128: return launch_partial_t<128, 2, 4, 8>(qwin, k, s, t, ws, L, c, st);
+    case 256: return launch_partial_t<256, 1, 4, 8>(qwin, k, s, t, ws, L, c, st);
     default: return hipErrorInvalidValue;
   }
 }

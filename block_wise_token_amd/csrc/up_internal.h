@@ -28,13 +28,20 @@ struct ReqPlan {
   int64_t cs_off;    // first chunk-statistics pair: [nch][Hkv][R]
 };
 
+// Launch shape of the score kernel per head dimension: query rows per workgroup
+// (waves x 32-row tiles per wave x 32) and workgroups resident per CU.  One 8-wave
+// workgroup per CU reads each key chunk once.  (Two 4-wave workgroups per CU, whose
+// barriers are independent, measured no faster at 128K tokens and read K twice.)
+constexpr int score_rows_wg(int d) { return d == 256 ? 8 * 1 * 32 : 8 * 2 * 32; }
+constexpr int score_wgs_per_cu(int) { return 1; }
+
 // Shape of the score pass, fixed by the host for one call.
 struct ScoreShape {
   int B, Hq, Hkv, d, n, G;
   int CB;        // blocks per key chunk (one workgroup's span of keys)
   int qt;        // 32-query column tiles per wave (1 or 2)
   int kt;        // 32-key row tiles per LDS stage (1 or 2)
-  int rows_wg;   // query rows per workgroup = 8 waves * qt * 32
+  int rows_wg;   // query rows per workgroup: score_rows_wg(d)
 };
 
 struct Totals {
@@ -91,7 +98,8 @@ hipError_t launch_block_dst(const uint8_t* keep, const int32_t* cu, const int32_
                             const CompactWs& L, int* err, hipStream_t st);
 hipError_t launch_gather(const void* hidden, int64_t row_bytes, const int32_t* pos, void* ws,
                          const CompactWs& L, int64_t nb_tot, int G, int32_t* idx_out,
-                         void* hidden_out, int32_t* pos_out, hipStream_t st);
+                         void* hidden_out, int32_t* pos_out, const int32_t* prev_orig,
+                         int32_t* orig_out, hipStream_t st);
 hipError_t launch_compose(const int32_t* prev, int prev_len, const int32_t* idx,
                           const int32_t* count, int capacity, int32_t* out, int* err,
                           hipStream_t st);

@@ -133,12 +133,16 @@ int up_topk_select(const float* scores, const int32_t* cu_seqlens,
  *   idx_out[r]    = packed input row of the r-th surviving token
  *   hidden_out[r] = hidden[idx_out[r]]   (a bit copy of row_bytes = H * elem_bytes)
  *   pos_out[r]    = pos[idx_out[r]]      (original positions, never renumbered)
+ *   orig_out[r]   = prev_orig[idx_out[r]] (drop composition, as up_compose_drops)
  * Rows r in [cu_seqlens_out[i], cu_seqlens_out[i+1]) belong to request i.
  *
  * hidden     : [T, H] rows of elem_bytes each (bf16: elem_bytes = 2).
  * pos        : int32 [T], or NULL (then pos_out is not written and may be NULL).
  * keep_blocks, cu_seqlens_out : as produced by up_topp_select.
  * idx_out    : int32 [T] capacity;  hidden_out: [T, H] capacity;  pos_out: int32 [T].
+ * prev_orig, orig_out : int32 [T] each, or both NULL.  When given, the composition
+ *              of up_compose_drops is written in the same pass (no extra launch);
+ *              orig_out without prev_orig is UP_EINVAL.
  * workspace  : at least up_expand_compact_workspace(...) bytes, 256-byte aligned.
  * ------------------------------------------------------------------------- */
 size_t up_expand_compact_workspace(const int32_t* cu_seqlens_h, int B, int G);
@@ -147,7 +151,8 @@ int up_expand_compact(const void* hidden, int H, int elem_bytes, const int32_t* 
                       const uint8_t* keep_blocks, const int32_t* cu_seqlens,
                       const int32_t* cu_seqlens_out, const int32_t* cu_seqlens_h, int B,
                       int G, int32_t* idx_out, void* hidden_out, int32_t* pos_out,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      const int32_t* prev_orig, int32_t* orig_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * 4. Drop composition  ([UP] "propagation" paragraph: a drop carries into every

@@ -117,15 +117,17 @@ def test_expand_compact_and_compose_reject_bad_arguments(L):
     cu = _cu([4096])
     f = L.up_expand_compact
 
-    def call(H=1024, eb=2, ws=FAKE, wsb=1 << 30, hidden=FAKE, pos=FAKE, pos_out=FAKE, G=64):
-        return f(hidden, H, eb, pos, FAKE, FAKE, FAKE, _p(cu), 1, G, FAKE, FAKE, pos_out, ws,
-                 ctypes.c_size_t(wsb), None)
+    def call(H=1024, eb=2, ws=FAKE, wsb=1 << 30, hidden=FAKE, pos=FAKE, pos_out=FAKE, G=64,
+             prev=None, orig=None):
+        return f(hidden, H, eb, pos, FAKE, FAKE, FAKE, _p(cu), 1, G, FAKE, FAKE, pos_out, prev,
+                 orig, ws, ctypes.c_size_t(wsb), None)
 
     assert call(H=0) == UP_EINVAL
     assert call(eb=0) == UP_EINVAL
     assert call(G=0) == UP_EINVAL
     assert call(hidden=None) == UP_EINVAL
     assert call(pos=None) == UP_EINVAL          # pos_out requested without pos
+    assert call(orig=FAKE) == UP_EINVAL         # orig_out requested without prev_orig
     assert call(wsb=8) == UP_EWORKSPACE
     assert call(ws=None) == UP_EWORKSPACE
     g = L.up_compose_drops

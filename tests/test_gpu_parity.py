@@ -290,3 +290,21 @@ def test_many_short_requests_select_and_compact():
     np.testing.assert_array_equal(hid_out[:cnt].view(torch.int16).cpu().numpy().view(np.uint16),
                                   h_ref)
     np.testing.assert_array_equal(pos_out[:cnt].cpu().numpy(), p_ref)
+
+
+def test_compose_drops_standalone_matches_oracle():
+    """up_compose_drops on its own (the decision fuses it into the compaction pass):
+    30000 survivors of 50000 rows through a scrambled original-index table."""
+    rng = np.random.default_rng(9)
+    prev_len, cnt, cap = 50000, 30000, 40000
+    prev = rng.permutation(1_000_000)[:prev_len].astype(np.int32)
+    idx = np.sort(rng.choice(prev_len, cnt, replace=False)).astype(np.int32)
+    idx_full = np.full(cap, -5, np.int32)
+    idx_full[:cnt] = idx
+    say("[case] compose_drops standalone")
+    up.device_error()
+    out = up.compose_drops(i32_dev(prev), i32_dev(idx_full), i32_dev(np.array([cnt], np.int32)),
+                           capacity=cap)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    np.testing.assert_array_equal(out[:cnt].cpu().numpy(), O.compose(prev, idx))
