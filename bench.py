@@ -145,7 +145,9 @@ def main():
     # Algorithmic work per launch.
     pairs = sum(causal_pairs(int(L), min(b.n, int(L))) for L in np.diff(b.cu_seqlens))
     score_flops = 2.0 * b.d * b.Hq * pairs                          # one Q K^T over causal pairs
-    gather_bytes = kept * (2 * row_bytes + 12)                        # rows read+written, pos r/w, idx w
+    # rows read + written, position read + written, index written, and the fused drop
+    # composition: previous original index read + composed index written
+    gather_bytes = kept * (2 * row_bytes + 12 + 8)
     s_us = kern["score_partial"]["avg_us"]
     g_us = kern["gather"]["avg_us"]
     score_tflops = score_flops / (s_us * 1e-6) / 1e12

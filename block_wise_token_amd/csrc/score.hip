@@ -94,24 +94,29 @@ __global__ void up_score_plan_kernel(const int32_t* __restrict__ cu, ScoreShape 
 // ---------------------------------------------------------------------------
 // Partial statistics on the matrix cores
 //
-// Workgroup = 8 waves = one (request, kv head g, query-row tile, key chunk).
-// Each wave holds QT tiles of 32 query rows of kv head g's group in VGPRs as the B
-// operand (rows r = j * gs + hh: window row j, head g*gs + hh).  Keys are staged
-// through LDS in stages of 32*HPS keys (double-buffered, padded rows; each stage's
-// global loads are issued two stages ahead) and read as the A operand, so
+// Workgroup = NW waves = one (request, kv head g, query-row tile, key chunk).  Each
+// wave holds QT tiles of 32 query rows of kv head g's group in VGPRs as the B
+// operand (rows r = j * gs + hh: window row j, head g*gs + hh).  Keys stream through
+// a ring of NS LDS stages of 64 keys: each stage is copied straight from global
+// memory into LDS (global_load_lds_dwordx4, no VGPR round trip) by all lanes, NS-2
+// stages ahead of use, and one barrier per stage publishes it and frees the slot the
+// previous stage used.  Rows are unpadded; their 16-byte granules are XOR-swizzled
+// so A-operand reads are free of bank conflicts.  Keys are the A operand, so
 // S^T = K Q^T lands with one query per lane column: lane l and lane l^32 together
 // hold the 32 keys of a half-stage for query l%32.
 //
-// The keys are processed in halves of 32.  The MFMAs of half h+1 are interleaved
-// (scheduling groups) with the exp/sum work of half h, on two accumulator sets.
+// The keys are processed in halves of 32: the MFMAs of half h+1 are issued between
+// the exp/sum instructions of half h, on two accumulator sets.  The main loop is
+// unrolled over the ring so every LDS offset is a compile-time constant.
 //
-// Softmax statistics per lane: a running reference Rs (log2 units) and the sums
-// l = sum 2^(x - Rs) over the lane's keys of the current block and chunk.  Any
-// reference gives the same (reference, sum) value, so there is no per-block max
-// pass: a half whose sum leaves [0, 2^64] (overflow, or NaN from an unset
-// reference) is redone against its own maximum and the earlier sums rescaled.
-// At a block end the two lanes of a query combine their pairs and one of them
-// stores (m_b, l_b); the chunk sums are combined and stored at the chunk end.
+// Softmax statistics: one running reference Rs per query (log2 units), the same in
+// both lanes of the query, and each lane's sums l = sum 2^(x - Rs) over its keys of
+// the current block and chunk.  Any reference gives the same (reference, sum) value,
+// so there is no per-block max pass; only when a half's sum leaves [0, 2^64]
+// (overflow, or the unset reference of a chunk's first half) does the wave rebase
+// the affected queries on the pair's maximum (a wave-uniform branch, rare).  At a
+// block end the partner lane's sum is added with v_permlane32_swap and one lane
+// stores (Rs, l_b); the chunk sums are stored likewise at the chunk end.
 //
 // The head dimension is contracted in a permuted order that both operands share:
 // lane half h, k-step s holds d-elements [h*D/2 + 8s, h*D/2 + 8s + 8), so every
