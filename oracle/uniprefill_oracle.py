@@ -179,6 +179,89 @@ def block_scores(qwin_bits: np.ndarray, k_bits: np.ndarray, cu_seqlens: np.ndarr
 
 
 # ---------------------------------------------------------------------------
+# Step 1b: block scores from the layer's own softmax statistics
+# ([UP] Triton kernels paragraph: the full-attention layer already runs an online
+# softmax over these rows, so its row statistics can be reused)
+# ---------------------------------------------------------------------------
+
+def row_lse(qwin_bits: np.ndarray, k_bits: np.ndarray, cu_seqlens: np.ndarray, Hq: int,
+            Hkv: int, d: int, n: int, scale: float | None = None) -> np.ndarray:
+    """Natural-log log-sum-exp of every window row's scaled logits over its causal
+    keys: lse = m + log(sum exp(s - m)), m the row maximum.  Float64 [sum W_i, Hq],
+    window rows in qwin order; these are the statistics a FlashAttention-style forward
+    keeps per query row.  Same masks and head map as ``window_probs``."""
+    if scale is None or scale <= 0:
+        scale = default_scale(d)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    gs = Hq // Hkv
+    out, qoff = [], 0
+    for i in range(cu.size - 1):
+        L = int(cu[i + 1] - cu[i])
+        W = window_size(L, n)
+        q = bf16_bits_to_f64(qwin_bits[qoff:qoff + W])
+        kk = bf16_bits_to_f64(k_bits[cu[i]:cu[i + 1]])
+        qoff += W
+        if W == 0:
+            continue
+        t = np.arange(L - W, L)
+        visible = np.arange(L)[None, :] <= t[:, None]
+        lse = np.empty((W, Hq), dtype=np.float64)
+        for h in range(Hq):
+            s_ = (q[:, h, :] @ kk[:, h // gs, :].T) * scale
+            s_ = np.where(visible, s_, -np.inf)
+            m = s_.max(axis=1)
+            lse[:, h] = m + np.log(np.exp(s_ - m[:, None]).sum(axis=1))
+        out.append(lse)
+    return np.concatenate(out) if out else np.zeros((0, Hq))
+
+
+def block_scores_given_lse(qwin_bits: np.ndarray, k_bits: np.ndarray, lse: np.ndarray,
+                           cu_seqlens: np.ndarray, Hq: int, Hkv: int, d: int, n: int, G: int,
+                           scale: float | None = None):
+    """Block scores when each window row's log-sum-exp is given rather than computed.
+
+    lse: [sum W_i, Hq] (window rows in qwin order, natural log).  A row's weights are
+    exp(s - lse_row) over its causal keys; block masses sum them over heads, rows and
+    the block's keys; each request's masses are divided by their sum.  With
+    lse = row_lse(...) the weights are the softmax probabilities and the result is
+    ``block_scores``'s.  A row with lse = +inf contributes nothing.
+
+    Returns (scores_f32 [NB_tot], scores_f64 [NB_tot], masses_f64 [NB_tot]).
+    """
+    if scale is None or scale <= 0:
+        scale = default_scale(d)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    lse = np.asarray(lse, dtype=np.float64)
+    gs = Hq // Hkv
+    out64, mass_all, qoff = [], [], 0
+    for i in range(cu.size - 1):
+        L = int(cu[i + 1] - cu[i])
+        W = window_size(L, n)
+        q = bf16_bits_to_f64(qwin_bits[qoff:qoff + W])
+        kk = bf16_bits_to_f64(k_bits[cu[i]:cu[i + 1]])
+        lrow = lse[qoff:qoff + W]
+        qoff += W
+        if L == 0:
+            continue
+        nb = n_blocks(L, G)
+        t = np.arange(L - W, L)
+        visible = np.arange(L)[None, :] <= t[:, None]
+        mass = np.zeros(nb, dtype=np.float64)
+        pad = nb * G - L
+        for h in range(Hq):
+            s_ = (q[:, h, :] @ kk[:, h // gs, :].T) * scale
+            P = np.where(visible, np.exp(s_ - lrow[:, h:h + 1]), 0.0)
+            if pad:
+                P = np.concatenate([P, np.zeros((W, pad))], axis=1)
+            mass += P.reshape(W, nb, G).sum(axis=(0, 2))
+        mass_all.append(mass)
+        out64.append(mass / mass.sum())
+    s64 = np.concatenate(out64) if out64 else np.zeros(0)
+    m64 = np.concatenate(mass_all) if mass_all else np.zeros(0)
+    return s64.astype(np.float32), s64, m64
+
+
+# ---------------------------------------------------------------------------
 # Step 2: Top-p selection  ([UP] Top-p selection paragraph)
 # ---------------------------------------------------------------------------
 

@@ -420,3 +420,103 @@ def test_topk_keeps_the_k_best_and_the_window():
     s2 = np.concatenate([s, np.array([0.5, 0.5], np.float32)])
     keep, cu_out = O.topk_select(s2, cu, n, G, 3)
     assert cu_out[-1] - cu_out[-2] == 100           # a short request keeps everything
+
+
+# ---------------------------------------------------------------------------
+# Block scores from given row statistics (the layer's own log-sum-exp)
+# ---------------------------------------------------------------------------
+
+def test_row_lse_matches_brute_force():
+    """row_lse against pure-Python float64 loops: log of the softmax denominator."""
+    rng = np.random.default_rng(31)
+    L, n, Hq, Hkv, d = 37, 12, 4, 2, 8
+    qb, kb = _rand_request(rng, L, Hq, Hkv, d, n)
+    qf, kf = O.bf16_bits_to_f64(qb), O.bf16_bits_to_f64(kb)
+    scale = O.default_scale(d)
+    lse = O.row_lse(qb, kb, np.array([0, L], np.int32), Hq, Hkv, d, n)
+    gs = Hq // Hkv
+    W = min(n, L)
+    for h in range(Hq):
+        for j in range(W):
+            t = L - W + j
+            logits = [scale * math.fsum(float(qf[j, h, x]) * float(kf[key, h // gs, x])
+                                        for x in range(d)) for key in range(t + 1)]
+            m = max(logits)
+            want = m + math.log(math.fsum(math.exp(v - m) for v in logits))
+            assert abs(lse[j, h] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_row_lse_closed_forms():
+    """Zero queries: every visible logit is 0, lse = ln(t + 1) exactly; a single
+    visible key (t = 0) has lse equal to its own logit."""
+    L, n = 300, 40
+    qb, kb = _zero_query_case(L, n, 64, Hq=2)
+    lse = O.row_lse(qb, kb, np.array([0, L], np.int32), 2, 1, 8, n)
+    t = np.arange(L - n, L)
+    np.testing.assert_allclose(lse, np.log(t + 1.0)[:, None].repeat(2, axis=1), rtol=1e-14)
+    rng = np.random.default_rng(2)
+    qb1, kb1 = _rand_request(rng, 1, 2, 1, 8, 4)
+    lse1 = O.row_lse(qb1, kb1, np.array([0, 1], np.int32), 2, 1, 8, 4)
+    s = (O.bf16_bits_to_f64(qb1)[0] @ O.bf16_bits_to_f64(kb1)[0, 0]) * O.default_scale(8)
+    np.testing.assert_allclose(lse1[0], s, rtol=1e-14)
+
+
+def test_given_lse_closed_form_zero_queries():
+    """Q = 0 with lse = ln(t + 1) written from the closed form (not from row_lse): the
+    scores are the exact Fraction closed form of the zero-query case."""
+    L, n, G, Hq = 1000, 100, 32, 2
+    qb, kb = _zero_query_case(L, n, G, Hq=Hq)
+    W = min(n, L)
+    nb = (L + G - 1) // G
+    t = [L - W + j for j in range(W)]
+    exact = []
+    for b in range(nb):
+        lo, hi = b * G, min((b + 1) * G, L)
+        exact.append(sum(Fraction(sum(1 for key in range(lo, hi) if key <= tj), tj + 1)
+                         for tj in t) / W)
+    lse = np.log(np.array(t, np.float64) + 1.0)[:, None].repeat(Hq, axis=1)
+    _, s64, m64 = O.block_scores_given_lse(qb, kb, lse, np.array([0, L], np.int32), Hq, 1, 8,
+                                           n, G)
+    np.testing.assert_allclose(s64, [float(x) for x in exact], rtol=1e-13)
+    np.testing.assert_allclose(m64.sum(), Hq * W, rtol=1e-13)   # every row's weights sum to 1
+
+
+def test_given_exact_lse_reproduces_block_scores():
+    """With each row's true log-sum-exp the weights are the softmax probabilities, so
+    the scores equal block_scores' (a packed batch: ragged, L < n, empty, MQA)."""
+    rng = np.random.default_rng(44)
+    lens, Hq, Hkv, d, n, G = [200, 9, 0, 130], 4, 1, 16, 24, 16
+    cu = np.zeros(len(lens) + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    reqs = [_rand_request(rng, L, Hq, Hkv, d, n) for L in lens]
+    qb = np.concatenate([q for q, _ in reqs])
+    kb = np.concatenate([k for _, k in reqs])
+    lse = O.row_lse(qb, kb, cu, Hq, Hkv, d, n)
+    assert lse.shape == (sum(min(n, L) for L in lens), Hq)
+    _, s_ref, m_ref = O.block_scores(qb, kb, cu, Hq, Hkv, d, n, G)
+    _, s_lse, m_lse = O.block_scores_given_lse(qb, kb, lse, cu, Hq, Hkv, d, n, G)
+    np.testing.assert_allclose(s_lse, s_ref, rtol=1e-12)
+    np.testing.assert_allclose(m_lse, m_ref, rtol=1e-12)
+
+
+def test_given_lse_is_linear_in_each_rows_weight():
+    """Masses are sum over rows of exp(-lse_row) * (row's unnormalised block sums):
+    shifting one row's lse by delta changes the masses by (e^-delta - 1) times that
+    row's contribution, which is the difference made by removing the row
+    (lse = +inf)."""
+    rng = np.random.default_rng(5)
+    L, Hq, Hkv, d, n, G = 150, 2, 1, 8, 20, 16
+    qb, kb = _rand_request(rng, L, Hq, Hkv, d, n)
+    cu = np.array([0, L], np.int32)
+    lse = O.row_lse(qb, kb, cu, Hq, Hkv, d, n)
+    _, _, m0 = O.block_scores_given_lse(qb, kb, lse, cu, Hq, Hkv, d, n, G)
+    j, h, delta = 7, 1, 0.75
+    gone = lse.copy()
+    gone[j, h] = np.inf
+    _, _, m_gone = O.block_scores_given_lse(qb, kb, gone, cu, Hq, Hkv, d, n, G)
+    shifted = lse.copy()
+    shifted[j, h] += delta
+    _, _, m_shift = O.block_scores_given_lse(qb, kb, shifted, cu, Hq, Hkv, d, n, G)
+    np.testing.assert_allclose(m_shift - m0, (math.exp(-delta) - 1.0) * (m0 - m_gone),
+                               rtol=1e-9, atol=1e-15)
+    np.testing.assert_allclose((m0 - m_gone).sum(), 1.0, rtol=1e-12)   # one row's weights sum to 1
