@@ -187,9 +187,51 @@ def main():
         "ms_per_step_instrumented": ms_step_instr,
     }
 
+    # The scope's next row: the same decision given each window row's log-sum-exp (what
+    # the layer's own attention keeps), here taken from the full pass's row_lse output.
+    # Reported beside the headline, which runs every step of the path itself.
+    result["given_lse"] = given_lse_leg(up, torch, dec, qwin, k, cu, b, hid, posd, p, args,
+                                        stream, score_flops)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, hidden, pos, p, cfg)
     print(json.dumps(result), flush=True)
+
+
+def given_lse_leg(up, torch, dec_full, qwin, k, cu, b, hid, posd, p, args, stream, score_flops):
+    lse = torch.empty((qwin.shape[0], b.Hq), dtype=torch.float32, device=qwin.device)
+    up.block_scores(qwin, k, cu, b.cu_seqlens, b.n, b.G, row_lse=lse)
+    dec = up.LayerDecision(qwin, k, cu, b.cu_seqlens, hid, posd, b.n, b.G, p, row_lse=lse)
+    for _ in range(args.warmup):
+        dec.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        dec.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    up.profile_reset()
+    up.profile_enable(True)
+    for _ in range(args.steps):
+        dec.run()
+    torch.cuda.synchronize()
+    up.profile_enable(False)
+    kern = {}
+    for name in ("score_plan", "score_partial_lse", "lse_finalize", "select", "block_dst", "gather"):
+        n_, t_ = up.profile_read(name)
+        if n_:
+            kern[name] = round(t_ * 1e3 / n_, 2)
+    up.profile_reset()
+    assert up.device_error() == 0
+    same = bool(torch.equal(dec.keep, dec_full.keep))
+    s_us = kern.get("score_partial_lse", float("nan"))
+    return {"ms_per_step": ms, "tokens_per_s": b.T / (ms * 1e-3), "kernels_avg_us": kern,
+            "score_tflops": round(score_flops / (s_us * 1e-6) / 1e12, 2),
+            "same_keep_as_full_pass": same,
+            "note": "scores from given window-row log-sum-exp (up_block_scores_lse); not the "
+                    "headline, which computes the row statistics itself"}
 
 
 def copy_reference(torch, nbytes, steps):

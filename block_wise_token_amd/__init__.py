@@ -10,6 +10,8 @@ from ._binding import (  # noqa: F401
     UniPrefillError,
     LayerDecision,
     block_scores,
+    block_scores_lse,
+    block_scores_lse_workspace_bytes,
     block_scores_workspace_bytes,
     compose_drops,
     device_error,

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libuniprefill.so")
 KERNEL_IDS = {
     "score_partial": 0, "row_stats": 1, "block_mass": 2, "normalize": 3, "select": 4,
     "select_finalize": 5, "block_dst": 6, "gather": 7, "compose": 8, "score_plan": 9,
+    "score_partial_lse": 10, "lse_finalize": 11,
 }
 
 _lib = None
@@ -39,7 +40,13 @@ def lib():
     L.up_block_scores_workspace.restype = cs
     L.up_block_scores_workspace.argtypes = [vp, ci, ci, ci, ci, ci, ci]
     L.up_block_scores.restype = ci
-    L.up_block_scores.argtypes = [vp, vp, i32p, vp, ci, ci, ci, ci, ci, ci, cf, f32p, vp, cs, vp]
+    L.up_block_scores.argtypes = [vp, vp, i32p, vp, ci, ci, ci, ci, ci, ci, cf, f32p, f32p, vp, cs,
+                                  vp]
+    L.up_block_scores_lse_workspace.restype = cs
+    L.up_block_scores_lse_workspace.argtypes = [vp, ci, ci, ci, ci, ci, ci]
+    L.up_block_scores_lse.restype = ci
+    L.up_block_scores_lse.argtypes = [vp, vp, f32p, i32p, vp, ci, ci, ci, ci, ci, ci, cf, f32p, vp,
+                                      cs, vp]
     L.up_topp_select.restype = ci
     L.up_topp_select.argtypes = [f32p, i32p, vp, ci, ci, ci, cf, u8p, i32p, vp]
     L.up_topk_select.restype = ci
@@ -115,9 +122,15 @@ def expand_compact_workspace_bytes(cu_h, G) -> int:
     return int(lib().up_expand_compact_workspace(h.ptr, h.B, G))
 
 
+def block_scores_lse_workspace_bytes(cu_h, Hq, Hkv, d, n, G) -> int:
+    h = _HostCu(cu_h)
+    return int(lib().up_block_scores_lse_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
+
+
 def block_scores(qwin, k, cu_seqlens, cu_h, n, G, scale=0.0, out=None, workspace=None,
-                 stream=None):
-    """Per-block importance scores (float32 [NB_tot]); see up_block_scores."""
+                 stream=None, row_lse=None):
+    """Per-block importance scores (float32 [NB_tot]); see up_block_scores.  With
+    ``row_lse`` (float32 [sum W, Hq]) each window row's log-sum-exp is written too."""
     _dev(qwin, torch.bfloat16, "qwin")
     _dev(k, torch.bfloat16, "k")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
@@ -129,10 +142,35 @@ def block_scores(qwin, k, cu_seqlens, cu_h, n, G, scale=0.0, out=None, workspace
     need = int(lib().up_block_scores_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qwin.device)
+    if row_lse is not None:
+        _dev(row_lse, torch.float32, "row_lse")
     st = lib().up_block_scores(_ptr(qwin), _ptr(k), _ptr(cu_seqlens), h.ptr, h.B, Hq, Hkv, d, n,
-                               G, float(scale), _ptr(out), _ptr(workspace),
+                               G, float(scale), _ptr(out), _ptr(row_lse), _ptr(workspace),
                                workspace.numel(), _stream(stream))
     _check(st, "up_block_scores")
+    return out
+
+
+def block_scores_lse(qwin, k, row_lse, cu_seqlens, cu_h, n, G, scale=0.0, out=None,
+                     workspace=None, stream=None):
+    """Block scores from given window-row log-sum-exp (float32 [sum W, Hq], natural
+    log); see up_block_scores_lse."""
+    _dev(qwin, torch.bfloat16, "qwin")
+    _dev(k, torch.bfloat16, "k")
+    _dev(row_lse, torch.float32, "row_lse")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    h = _HostCu(cu_h)
+    Hq, d = int(qwin.shape[1]), int(qwin.shape[2])
+    Hkv = int(k.shape[1])
+    if out is None:
+        out = torch.empty(h.nb_tot(G), dtype=torch.float32, device=qwin.device)
+    need = int(lib().up_block_scores_lse_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qwin.device)
+    st = lib().up_block_scores_lse(_ptr(qwin), _ptr(k), _ptr(row_lse), _ptr(cu_seqlens), h.ptr,
+                                   h.B, Hq, Hkv, d, n, G, float(scale), _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "up_block_scores_lse")
     return out
 
 
@@ -250,7 +288,7 @@ class LayerDecision:
     """
 
     def __init__(self, qwin, k, cu_seqlens, cu_h, hidden, pos, n, G, p, scale=0.0,
-                 prev_orig=None, topk=None):
+                 prev_orig=None, topk=None, row_lse=None):
         self.qwin, self.k, self.cu, self.hidden, self.pos = qwin, k, cu_seqlens, hidden, pos
         self.h = _HostCu(cu_h)
         self.n, self.G, self.p, self.scale, self.topk = n, G, p, scale, topk
@@ -259,8 +297,11 @@ class LayerDecision:
         nbt = self.h.nb_tot(G)
         Hq, d, Hkv = int(qwin.shape[1]), int(qwin.shape[2]), int(k.shape[1])
         self.scores = torch.empty(nbt, dtype=torch.float32, device=dev)
-        self.ws_scores = torch.empty(max(1, block_scores_workspace_bytes(self.h.arr, Hq, Hkv, d, n, G)),
-                                     dtype=torch.uint8, device=dev)
+        # With the layer's own row statistics the scores come from the given-lse pass.
+        self.row_lse = row_lse
+        ws_bytes = (block_scores_lse_workspace_bytes if row_lse is not None
+                    else block_scores_workspace_bytes)(self.h.arr, Hq, Hkv, d, n, G)
+        self.ws_scores = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
         self.keep = torch.empty(nbt, dtype=torch.uint8, device=dev)
         self.cu_out = torch.empty(B + 1, dtype=torch.int32, device=dev)
         self.idx = torch.empty(T, dtype=torch.int32, device=dev)
@@ -273,8 +314,12 @@ class LayerDecision:
         self.orig = torch.empty(T, dtype=torch.int32, device=dev)
 
     def run(self, stream=None):
-        block_scores(self.qwin, self.k, self.cu, self.h.arr, self.n, self.G, self.scale,
-                     out=self.scores, workspace=self.ws_scores, stream=stream)
+        if self.row_lse is None:
+            block_scores(self.qwin, self.k, self.cu, self.h.arr, self.n, self.G, self.scale,
+                         out=self.scores, workspace=self.ws_scores, stream=stream)
+        else:
+            block_scores_lse(self.qwin, self.k, self.row_lse, self.cu, self.h.arr, self.n, self.G,
+                             self.scale, out=self.scores, workspace=self.ws_scores, stream=stream)
         if self.topk is None:
             topp_select(self.scores, self.cu, self.h.arr, self.n, self.G, self.p, keep=self.keep,
                         cu_out=self.cu_out, stream=stream)

@@ -164,6 +164,7 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
     t->items += nch * Hkv * nrt;
     t->ml_pairs += nb * Hkv * R;
     t->cs_pairs += nch * Hkv * R;
+    t->pm_parts += nb * Hkv * nrt;
     if (nb > t->nb_max) t->nb_max = (int32_t)nb;
   }
   t->T = B > 0 ? cu_h[B] : 0;
@@ -204,8 +205,8 @@ size_t up_block_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int
 
 int up_block_scores(const void* qwin, const void* k, const int32_t* cu_seqlens,
                     const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d, int n, int G,
-                    float scale, float* scores, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+                    float scale, float* scores, float* row_lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   ScoreShape s;
   Totals t;
   const int st = plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t);
@@ -222,15 +223,58 @@ int up_block_scores(const void* qwin, const void* k, const int32_t* cu_seqlens,
   if (!err) return UP_EHIP;
   hipStream_t hs = as_stream(stream);
   hipError_t e;
-  e = timed(9, hs, [&] { return launch_score_plan(cu_seqlens, s, t, workspace, L, err, hs); });
+  e = timed(9, hs, [&] {
+    return launch_score_plan(cu_seqlens, s, t, workspace, L.plan, err, hs);
+  });
   if (e != hipSuccess) return UP_EHIP;
   e = timed(0, hs, [&] { return launch_score_partial(qwin, k, s, t, workspace, L, c, hs); });
   if (e != hipSuccess) return UP_EHIP;
-  e = timed(1, hs, [&] { return launch_row_stats(s, t, workspace, L, hs); });
+  e = timed(1, hs, [&] { return launch_row_stats(s, t, workspace, L, row_lse, hs); });
   if (e != hipSuccess) return UP_EHIP;
   e = timed(2, hs, [&] { return launch_block_mass(s, t, workspace, L, hs); });
   if (e != hipSuccess) return UP_EHIP;
   e = timed(3, hs, [&] { return launch_normalize(s, t, workspace, L, scores, hs); });
+  if (e != hipSuccess) return UP_EHIP;
+  return UP_OK;
+}
+
+size_t up_block_scores_lse_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d,
+                                     int n, int G) {
+  ScoreShape s;
+  Totals t;
+  if (plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t) != UP_OK) return 0;
+  return score_lse_ws_layout(B, t).total;
+}
+
+int up_block_scores_lse(const void* qwin, const void* k, const float* row_lse,
+                        const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B, int Hq,
+                        int Hkv, int d, int n, int G, float scale, float* scores,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  ScoreShape s;
+  Totals t;
+  const int st = plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t);
+  if (st != UP_OK) return st;
+  if (B == 0 || t.T == 0) return UP_OK;
+  if (!qwin || !k || !row_lse || !cu_seqlens || !scores) return UP_EINVAL;
+  if (!aligned(qwin, 16) || !aligned(k, 16) || !aligned(row_lse, 4)) return UP_EINVAL;
+  const ScoreLseWs L = score_lse_ws_layout(B, t);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, kWsAlign))
+    return UP_EWORKSPACE;
+  if (!(scale > 0.f) || std::isinf(scale)) scale = (float)(1.0 / std::sqrt((double)d));
+  const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
+  int* err = error_word();
+  if (!err) return UP_EHIP;
+  hipStream_t hs = as_stream(stream);
+  hipError_t e;
+  e = timed(9, hs, [&] {
+    return launch_score_plan(cu_seqlens, s, t, workspace, L.plan, err, hs);
+  });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(10, hs, [&] {
+    return launch_score_partial_lse(qwin, k, row_lse, s, t, workspace, L, c, hs);
+  });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(11, hs, [&] { return launch_lse_finalize(s, t, workspace, L, scores, hs); });
   if (e != hipSuccess) return UP_EHIP;
   return UP_OK;
 }
@@ -254,7 +298,7 @@ static int select_common(const float* scores, const int32_t* cu_seqlens,
                          keep_blocks, cu_seqlens_out, err, hs);
   });
   if (e != hipSuccess) return UP_EHIP;
-  e = timed(5, hs, [&] { return launch_select_finalize(cu_seqlens_out, B, hs); });
+  if (B > 1) e = timed(5, hs, [&] { return launch_select_finalize(cu_seqlens_out, B, hs); });
   return e == hipSuccess ? UP_OK : UP_EHIP;
 }
 

@@ -21,6 +21,7 @@
 //   up_row_stats_kernel      merge chunk statistics into per-row (m, 1 / l)
 //   up_block_mass_kernel     per-block mass, float64 sums in a fixed order
 //   up_normalize_kernel      per-request normalisation to scores that sum to one
+#include "up_dpp.h"
 #include "up_internal.h"
 
 #include <math.h>
@@ -67,7 +68,7 @@ __global__ void up_score_plan_kernel(const int32_t* __restrict__ cu, ScoreShape 
   if (threadIdx.x != 0) return;
   const int gs = s.Hq / s.Hkv;
   bool ok = (cu[0] == 0);
-  int64_t win = 0, blk = 0, items = 0, mlp = 0, csp = 0;
+  int64_t win = 0, blk = 0, items = 0, mlp = 0, csp = 0, pmp = 0;
   for (int i = 0; i < s.B; ++i) {
     const int32_t a = cu[i], b = cu[i + 1];
     int64_t L = (int64_t)b - a;
@@ -81,12 +82,13 @@ __global__ void up_score_plan_kernel(const int32_t* __restrict__ cu, ScoreShape 
     ReqPlan p;
     p.tok_off = a; p.L = (int32_t)L; p.W = (int32_t)W; p.win_off = (int32_t)win;
     p.blk_off = (int32_t)blk; p.nb = (int32_t)nb; p.nch = (int32_t)nch;
-    p.item_end = (int32_t)items; p.ml_off = mlp; p.cs_off = csp;
+    p.item_end = (int32_t)items; p.ml_off = mlp; p.cs_off = csp; p.pm_off = pmp;
     plan[i] = p;
-    win += W; blk += nb; mlp += nb * s.Hkv * R; csp += nch * s.Hkv * R;
+    win += W; blk += nb; mlp += nb * s.Hkv * R; csp += nch * s.Hkv * R; pmp += nb * s.Hkv * nrt;
   }
   ok = ok && (int64_t)cu[s.B] == host.T && win == host.win_rows && blk == host.nb_tot &&
-       items == host.items && mlp == host.ml_pairs && csp == host.cs_pairs;
+       items == host.items && mlp == host.ml_pairs && csp == host.cs_pairs &&
+       pmp == host.pm_parts;
   hdr->valid = ok ? 1 : 0;
   if (!ok) atomicOr(err, 1);
 }
@@ -183,11 +185,17 @@ __device__ __forceinline__ void wait_vm_lgkm_barrier(int n) {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int D, int QT, int NS, int NW>
+// LSE = true: the given-lse pass.  Each query's reference is its own log-sum-exp
+// (row_lse * log2 e), so 2^(x - Rs) are the softmax probabilities themselves and no
+// rebase ever happens; at a block end the workgroup sums the block's probabilities
+// (DPP within each wave, then the waves through LDS at the chunk end) and writes one
+// float partial per (block, kv head, row tile) to pm instead of per-row statistics.
+template <int D, int QT, int NS, int NW, bool LSE>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
     const uint16_t* __restrict__ qwin, const uint16_t* __restrict__ kmat,
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
-    int G, int CB, float c, float2* __restrict__ ml, float2* __restrict__ cs) {
+    int G, int CB, float c, float2* __restrict__ ml, float2* __restrict__ cs,
+    const float* __restrict__ row_lse, float* __restrict__ pm) {
   constexpr int NT = 64 * NW;
   constexpr int UK = 64;               // keys per LDS stage (two 32-key halves)
   constexpr int RB = 2 * D;            // LDS bytes per key row
@@ -200,6 +208,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   static_assert((NS - 2) * SPT <= 15, "vmcnt wait range");
   static_assert((NS & (NS - 1)) == 0, "ring length must be a power of two");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
+  __shared__ float blk_acc[LSE ? kMaxChunkBlocks * NW : 1];   // per (block, wave) sums
 
   if (hdr->valid != 1) return;
   const int x = blockIdx.x;
@@ -222,16 +231,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   // Query operand, resident for the whole chunk.
   bf16x8 qreg[QT][DS];
   int qpos[QT];
+  float lse_ref[QT];   // given-lse pass: the row's log-sum-exp in log2 units (+inf: no row)
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int r = row0 + t * 32 + l32;
+    lse_ref[t] = __builtin_inff();
     if (r < R) {
       const int j = r / gs, hh = r - j * gs;
-      const uint16_t* src =
-          qwin + ((int64_t)(pr.win_off + j) * Hq + g * gs + hh) * D + half * (D / 2);
+      const int64_t qrow = (int64_t)(pr.win_off + j) * Hq + g * gs + hh;
+      const uint16_t* src = qwin + qrow * D + half * (D / 2);
 #pragma unroll
       for (int s = 0; s < DS; ++s) qreg[t][s] = *reinterpret_cast<const bf16x8*>(src + s * 8);
       qpos[t] = pr.L - pr.W + j;
+      if (LSE) lse_ref[t] = row_lse[qrow] * 1.4426950408889634f;
     } else {
 #pragma unroll
       for (int s = 0; s < DS; ++s) qreg[t][s] = bf16x8{};
@@ -303,7 +315,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   // current block / chunk, relative to Rs.
   float Rs[QT], lblk[QT], Lch[QT];
 #pragma unroll
-  for (int t = 0; t < QT; ++t) { Rs[t] = kNegInf; lblk[t] = 0.f; Lch[t] = 0.f; }
+  for (int t = 0; t < QT; ++t) {
+    Rs[t] = LSE ? lse_ref[t] : kNegInf;
+    lblk[t] = 0.f;
+    Lch[t] = 0.f;
+  }
   const int t_st = (QT == 2) ? half : 0;          // the tile this lane stores
   const int r_st = row0 + t_st * 32 + l32;
   const bool st_ok = (QT == 2 || half == 0) && (r_st < R);
@@ -385,6 +401,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
 
   // Accumulate half h's sums; handle block ends.
   auto finish_half = [&](int h, f32x16 (&acc)[QT], const float (&sum)[QT]) {
+    if constexpr (LSE) {
+      // Probabilities already: accumulate; at a block end sum over the wave's 64 lanes
+      // (all its queries and keys) and leave the wave's total in LDS.
+#pragma unroll
+      for (int t = 0; t < QT; ++t) lblk[t] += sum[t];
+      if (--hcnt == 0 || h == nh - 1) {
+        hcnt = G / 32;
+        const int bl = (k0 + h * 32) / G;   // request-local block
+        float v = lblk[0];
+#pragma unroll
+        for (int t = 1; t < QT; ++t) v += lblk[t];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) lblk[t] = 0.f;
+        v = wave_scan_f32(v);
+        if (lane == 63) blk_acc[(bl - b0) * NW + wave] = v;
+      }
+      return;
+    }
     float nl[QT];
     bool bad = false;
 #pragma unroll
@@ -489,15 +523,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   }
 
   flush_pending();
-  // Chunk statistics: the two lanes of each query share the reference; add their sums.
-  float mst = 0.f, lst = 0.f;
+  if constexpr (LSE) {
+    // Block partials of this (kv head, row tile): the waves' totals in wave order.
+    __syncthreads();
+    for (int b = tid; b < b1 - b0; b += NT) {
+      float v = blk_acc[b * NW];
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    const float lp = pair_sum(Lch[t]);
-    if (t == t_st) { mst = Rs[t]; lst = lp; }
+      for (int w = 1; w < NW; ++w) v += blk_acc[b * NW + w];
+      pm[pr.pm_off + (int64_t)(g * nrt + rt) * pr.nb + b0 + b] = v;   // part-major
+    }
+  } else {
+    // Chunk statistics: the two lanes of each query share the reference; add their sums.
+    float mst = 0.f, lst = 0.f;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const float lp = pair_sum(Lch[t]);
+      if (t == t_st) { mst = Rs[t]; lst = lp; }
+    }
+    if (st_ok)
+      cs[pr.cs_off + ((int64_t)ch * Hkv + g) * R + r_st] =
+          make_float2(lst > 0.f ? mst : kNegInf, lst);
   }
-  if (st_ok)
-    cs[pr.cs_off + ((int64_t)ch * Hkv + g) * R + r_st] = make_float2(lst > 0.f ? mst : kNegInf, lst);
 }
 
 // ---------------------------------------------------------------------------
@@ -518,19 +564,23 @@ __device__ __forceinline__ int request_of_row(const ReqPlan* __restrict__ plan, 
 // of its lane's row, then wave 0 merges the 16 partial results in wave order.
 __global__ __launch_bounds__(1024) void up_row_stats_kernel(
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
-    const float2* __restrict__ cs, float2* __restrict__ rs, int64_t total_rows) {
+    const float2* __restrict__ cs, float2* __restrict__ rs, int64_t total_rows,
+    float* __restrict__ row_lse) {
   __shared__ float2 part[16][64];
   if (hdr->valid != 1) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t x = (int64_t)blockIdx.x * 64 + lane;
   float M = kNegInf, S = 0.f;
+  int64_t lse_at = -1;   // the row's index in the [sum W, Hq] window-row layout
   if (x < total_rows) {
     const int i = request_of_row(plan, B, Hq, x);
     if (i < B) {
       const ReqPlan pr = plan[i];
-      const int R = (Hq / Hkv) * pr.W;
+      const int gs = Hq / Hkv;
+      const int R = gs * pr.W;
       const int64_t local = x - (int64_t)pr.win_off * Hq;   // = g*R + r
       const int g = (int)(local / R), r = (int)(local % R);
+      lse_at = (int64_t)(pr.win_off + r / gs) * Hq + g * gs + r % gs;
       for (int chk = wave; chk < pr.nch; chk += 16) {
         const float2 v = cs[pr.cs_off + ((int64_t)chk * Hkv + g) * R + r];
         merge_ml(M, S, v.x, v.y);
@@ -543,6 +593,8 @@ __global__ __launch_bounds__(1024) void up_row_stats_kernel(
     float Mt = kNegInf, St = 0.f;
     for (int w = 0; w < 16; ++w) merge_ml(Mt, St, part[w][lane].x, part[w][lane].y);
     rs[x] = make_float2(Mt, St > 0.f ? 1.f / St : 0.f);   // (row max, 1 / row sum)
+    // Natural-log log-sum-exp of the row's scaled logits: (M + log2 l) * ln 2.
+    if (row_lse && lse_at >= 0) row_lse[lse_at] = (Mt + log2f(St)) * 0.6931471805599453f;
   }
 }
 
@@ -629,6 +681,58 @@ __global__ __launch_bounds__(256) void up_normalize_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Given-lse pass: scores[b] = (sum of the block's partials over kv heads and row
+// tiles) / (the request's total), float64 sums in a fixed order.  One workgroup per
+// request.  Partials are part-major ([Hkv * nrt][nb]), so the loads of one part are
+// coalesced across blocks and the parts of a block are independent loads; the
+// masses of the first kFinMass blocks stay in LDS for the second sweep.
+// ---------------------------------------------------------------------------
+constexpr int kFinThreads = 1024;
+constexpr int kFinMass = 4096;
+
+__global__ __launch_bounds__(kFinThreads) void up_lse_finalize_kernel(
+    const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
+    int rows_wg, const float* __restrict__ pm, float* __restrict__ scores) {
+  __shared__ double mass_lds[kFinMass];
+  __shared__ double red[kFinThreads / 64];
+  if (hdr->valid != 1) return;
+  const int i = blockIdx.x;
+  if (i >= B) return;
+  const ReqPlan pr = plan[i];
+  const int R = (Hq / Hkv) * pr.W;
+  const int parts = Hkv * ((R + rows_wg - 1) / rows_wg);
+  const float* base = pm + pr.pm_off;
+  const int64_t nb = pr.nb;
+  auto mass = [&](int64_t b) {
+    double m0 = 0.0, m1 = 0.0, m2 = 0.0, m3 = 0.0;
+    int q = 0;
+    for (; q + 3 < parts; q += 4) {
+      m0 += (double)base[(int64_t)q * nb + b];
+      m1 += (double)base[(int64_t)(q + 1) * nb + b];
+      m2 += (double)base[(int64_t)(q + 2) * nb + b];
+      m3 += (double)base[(int64_t)(q + 3) * nb + b];
+    }
+    for (; q < parts; ++q) m0 += (double)base[(int64_t)q * nb + b];
+    return (m0 + m1) + (m2 + m3);
+  };
+  double acc = 0.0;
+  for (int64_t b = threadIdx.x; b < nb; b += kFinThreads) {
+    const double m = mass(b);
+    if (b < kFinMass) mass_lds[b] = m;
+    acc += m;
+  }
+  // Fixed-order sum: butterfly within each wave, then the wave sums in order.
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) acc += __shfl_xor(acc, d);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  double tot = 0.0;
+  for (int w = 0; w < kFinThreads / 64; ++w) tot += red[w];
+  for (int64_t b = threadIdx.x; b < nb; b += kFinThreads)
+    scores[pr.blk_off + b] = (float)((b < kFinMass ? mass_lds[b] : mass(b)) / tot);
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
 ScoreWs score_ws_layout(int B, const Totals& t) {
@@ -643,52 +747,96 @@ ScoreWs score_ws_layout(int B, const Totals& t) {
   return L;
 }
 
+ScoreLseWs score_lse_ws_layout(int B, const Totals& t) {
+  ScoreLseWs L;
+  size_t off = align_up(sizeof(WsHeader));
+  L.plan = off; off = align_up(off + (size_t)B * sizeof(ReqPlan));
+  L.pm = off;   off = align_up(off + (size_t)t.pm_parts * sizeof(float));
+  L.total = off;
+  return L;
+}
+
 static inline char* wsb(void* ws) { return static_cast<char*>(ws); }
 
 hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Totals& t, void* ws,
-                             const ScoreWs& L, int* err, hipStream_t st) {
+                             size_t plan_off, int* err, hipStream_t st) {
   hipLaunchKernelGGL(up_score_plan_kernel, dim3(1), dim3(64), 0, st, cu, s, t,
                      reinterpret_cast<WsHeader*>(wsb(ws)),
-                     reinterpret_cast<ReqPlan*>(wsb(ws) + L.plan), err);
+                     reinterpret_cast<ReqPlan*>(wsb(ws) + plan_off), err);
   return hipGetLastError();
 }
 
-template <int D, int QT, int NS, int NW>
+// Output buffers of one launch of the score kernel (the unused ones are null).
+struct PartialOut {
+  size_t plan_off;
+  float2* ml;
+  float2* cs;
+  const float* row_lse;
+  float* pm;
+};
+
+template <int D, int QT, int NS, int NW, bool LSE>
 static hipError_t launch_partial_t(const void* qwin, const void* k, const ScoreShape& s,
-                                   const Totals& t, void* ws, const ScoreWs& L, float c,
+                                   const Totals& t, void* ws, const PartialOut& o, float c,
                                    hipStream_t st) {
   static_assert(NW * QT * 32 == score_rows_wg(D), "row tile of the kernel and of the plan");
-  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, NS, NW>), dim3((unsigned)t.items),
+  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, NS, NW, LSE>), dim3((unsigned)t.items),
                      dim3(64 * NW), 0,
                      st, static_cast<const uint16_t*>(qwin), static_cast<const uint16_t*>(k),
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
-                     reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq, s.Hkv, s.G,
-                     s.CB, c, reinterpret_cast<float2*>(wsb(ws) + L.ml),
-                     reinterpret_cast<float2*>(wsb(ws) + L.cs));
+                     reinterpret_cast<const ReqPlan*>(wsb(ws) + o.plan_off), s.B, s.Hq, s.Hkv,
+                     s.G, s.CB, c, o.ml, o.cs, o.row_lse, o.pm);
   return hipGetLastError();
+}
+
+template <bool LSE>
+static hipError_t launch_partial_d(const void* qwin, const void* k, const ScoreShape& s,
+                                   const Totals& t, void* ws, const PartialOut& o, float c,
+                                   hipStream_t st) {
+  if (t.items == 0) return hipSuccess;
+  if (s.CB > kMaxChunkBlocks) return hipErrorInvalidValue;
+  switch (s.d) {
+    case 64: return launch_partial_t<64, 2, 8, 8, LSE>(qwin, k, s, t, ws, o, c, st);
+    case 128: return launch_partial_t<128, 2, 4, 8, LSE>(qwin, k, s, t, ws, o, c, st);
+    case 256: return launch_partial_t<256, 1, 4, 8, LSE>(qwin, k, s, t, ws, o, c, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShape& s,
                                 const Totals& t, void* ws, const ScoreWs& L, float c,
                                 hipStream_t st) {
-  if (t.items == 0) return hipSuccess;
-  switch (s.d) {
-    case 64: return launch_partial_t<64, 2, 8, 8>(qwin, k, s, t, ws, L, c, st);
-    case 128: return launch_partial_t<128, 2, 4, 8>(qwin, k, s, t, ws, L, c, st);
-    case 256: return launch_partial_t<256, 1, 4, 8>(qwin, k, s, t, ws, L, c, st);
-    default: return hipErrorInvalidValue;
-  }
+  const PartialOut o{L.plan, reinterpret_cast<float2*>(wsb(ws) + L.ml),
+                     reinterpret_cast<float2*>(wsb(ws) + L.cs), nullptr, nullptr};
+  return launch_partial_d<false>(qwin, k, s, t, ws, o, c, st);
+}
+
+hipError_t launch_score_partial_lse(const void* qwin, const void* k, const float* row_lse,
+                                    const ScoreShape& s, const Totals& t, void* ws,
+                                    const ScoreLseWs& L, float c, hipStream_t st) {
+  const PartialOut o{L.plan, nullptr, nullptr, row_lse, reinterpret_cast<float*>(wsb(ws) + L.pm)};
+  return launch_partial_d<true>(qwin, k, s, t, ws, o, c, st);
+}
+
+hipError_t launch_lse_finalize(const ScoreShape& s, const Totals& t, void* ws,
+                               const ScoreLseWs& L, float* scores, hipStream_t st) {
+  if (s.B == 0 || t.nb_tot == 0) return hipSuccess;
+  hipLaunchKernelGGL(up_lse_finalize_kernel, dim3(s.B), dim3(kFinThreads), 0, st,
+                     reinterpret_cast<const WsHeader*>(wsb(ws)),
+                     reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq, s.Hkv,
+                     s.rows_wg, reinterpret_cast<const float*>(wsb(ws) + L.pm), scores);
+  return hipGetLastError();
 }
 
 hipError_t launch_row_stats(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
-                            hipStream_t st) {
+                            float* row_lse, hipStream_t st) {
   if (t.rows == 0) return hipSuccess;
   const unsigned grid = (unsigned)((t.rows + 63) / 64);
   hipLaunchKernelGGL(up_row_stats_kernel, dim3(grid), dim3(1024), 0, st,
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq, s.Hkv,
                      reinterpret_cast<const float2*>(wsb(ws) + L.cs),
-                     reinterpret_cast<float2*>(wsb(ws) + L.rs), t.rows);
+                     reinterpret_cast<float2*>(wsb(ws) + L.rs), t.rows, row_lse);
   return hipGetLastError();
 }
 

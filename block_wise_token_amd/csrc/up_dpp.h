@@ -40,6 +40,22 @@ __device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
   return v;
 }
 
+// Float inclusive scan in the same fixed pattern: lane 63 ends with the wave's sum,
+// always associated the same way (bitwise reproducible).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_in_f32(float v) {
+  return __uint_as_float(dpp_in<CTRL, ROWMASK>(__float_as_uint(v)));
+}
+__device__ __forceinline__ float wave_scan_f32(float v) {
+  v += dpp_in_f32<0x111, 0xf>(v);
+  v += dpp_in_f32<0x112, 0xf>(v);
+  v += dpp_in_f32<0x114, 0xf>(v);
+  v += dpp_in_f32<0x118, 0xf>(v);
+  v += dpp_in_f32<0x142, 0xa>(v);
+  v += dpp_in_f32<0x143, 0xc>(v);
+  return v;
+}
+
 // Value of lane 63 (the wave total after an inclusive scan).
 __device__ __forceinline__ uint64_t lane63_u64(uint64_t v) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);

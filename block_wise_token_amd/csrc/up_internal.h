@@ -26,6 +26,7 @@ struct ReqPlan {
   int32_t item_end;  // exclusive end of the request's work items of the score kernel
   int64_t ml_off;    // first (m, l) pair of the request: pairs are [nb][Hkv][R], R = gs * W
   int64_t cs_off;    // first chunk-statistics pair: [nch][Hkv][R]
+  int64_t pm_off;    // first block partial of the given-lse pass: [Hkv * nrt][nb]
 };
 
 // Launch shape of the score kernel per head dimension: query rows per workgroup
@@ -52,6 +53,7 @@ struct Totals {
   int64_t items;     // score work items (workgroups)
   int64_t ml_pairs;  // (m, l) pairs
   int64_t cs_pairs;  // chunk-statistics pairs
+  int64_t pm_parts;  // block partials of the given-lse pass
   int32_t nb_max;    // largest per-request block count
 };
 
@@ -68,14 +70,30 @@ struct ScoreWs {
 
 ScoreWs score_ws_layout(int B, const Totals& t);
 
+// Workspace of the given-lse score pass: plan and float block partials only.
+struct ScoreLseWs {
+  size_t plan, pm, total;
+};
+
+ScoreLseWs score_lse_ws_layout(int B, const Totals& t);
+
+// Largest key chunk (blocks per workgroup) the planner picks.
+constexpr int kMaxChunkBlocks = 256;
+
 // Launchers (score.hip).  Each returns the hipError_t of its launch.
 hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Totals& t,
-                             void* ws, const ScoreWs& L, int* err, hipStream_t st);
+                             void* ws, size_t plan_off, int* err, hipStream_t st);
 hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShape& s,
                                 const Totals& t, void* ws, const ScoreWs& L, float c_log2,
                                 hipStream_t st);
 hipError_t launch_row_stats(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
-                            hipStream_t st);
+                            float* row_lse, hipStream_t st);
+// The given-lse pass: row_lse [sum W_i, Hq] natural-log log-sum-exp of each window row.
+hipError_t launch_score_partial_lse(const void* qwin, const void* k, const float* row_lse,
+                                    const ScoreShape& s, const Totals& t, void* ws,
+                                    const ScoreLseWs& L, float c, hipStream_t st);
+hipError_t launch_lse_finalize(const ScoreShape& s, const Totals& t, void* ws,
+                               const ScoreLseWs& L, float* scores, hipStream_t st);
 hipError_t launch_block_mass(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
                              hipStream_t st);
 hipError_t launch_normalize(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,

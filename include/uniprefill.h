@@ -81,6 +81,9 @@ int up_abi_version(void);
  * Hq % Hkv == 0.  d in {64, 128, 256}.  G a multiple of 32 in [32, 1024].  n >= 1.
  * scale : softmax scale; <= 0 or NaN selects 1/sqrt(d) (as float32).
  * scores: float32 [NB_tot] output, NB_tot = sum_i nb_i.
+ * row_lse: float32 [sum_i W_i, Hq] output, or NULL: each window row's natural-log
+ *         log-sum-exp of scale * q.k over its causal keys, rows laid out like qwin
+ *         (the statistics up_block_scores_lse takes).
  * workspace: device buffer of at least up_block_scores_workspace(...) bytes,
  *         256-byte aligned; its contents on entry are ignored.
  * Precision: bf16 products accumulated in float32 on the matrix cores; softmax and
@@ -92,7 +95,33 @@ size_t up_block_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int
 int up_block_scores(const void* qwin, const void* k,
                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B,
                     int Hq, int Hkv, int d, int n, int G, float scale,
-                    float* scores, void* workspace, size_t workspace_bytes, void* stream);
+                    float* scores, float* row_lse, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 1b. Block scores from the layer's own softmax statistics  ([UP] "Triton kernels"
+ *     paragraph: the full-attention layer runs an online softmax over these rows,
+ *     so each window row's log-sum-exp already exists when the decision is made)
+ *
+ * Same result as up_block_scores, given each window row's log-sum-exp instead of
+ * computing it: the weights exp(scale * q.k - row_lse) are the softmax probabilities
+ * directly, so one pass sums them per block (no per-row statistics, no second
+ * reduction over rows):
+ *   mass[b]   = sum_h sum_j sum_{k in block b, k <= t} exp(scale * q.k - row_lse[j, h])
+ *   scores[b] = mass[b] / sum_{b'} mass[b']
+ * row_lse : float32 [sum_i W_i, Hq], natural log, window rows laid out like qwin (as
+ *           produced by up_block_scores, or kept by the layer's attention forward).
+ *           A row_lse far below the true value makes exp overflow; the result is then
+ *           meaningless (no fault).
+ * Other arguments as up_block_scores; workspace: up_block_scores_lse_workspace(...).
+ * ------------------------------------------------------------------------- */
+size_t up_block_scores_lse_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv,
+                                     int d, int n, int G);
+
+int up_block_scores_lse(const void* qwin, const void* k, const float* row_lse,
+                        const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B,
+                        int Hq, int Hkv, int d, int n, int G, float scale, float* scores,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * 2. Top-p selection  ([UP] "Top-p selection" paragraph: sort blocks by descending

@@ -63,6 +63,10 @@ def test_workspace_sizes(L):
     assert cw >= 3 * 2048 * 4
     vl = _cu([8192, 0, 65536, 77])
     assert L.up_block_scores_workspace(_p(vl), 4, 32, 8, 128, 128, 64) > 0
+    # the given-lse pass needs only the plan and one float per (block, kv head, row tile)
+    lw = L.up_block_scores_lse_workspace(_p(cu), 1, 32, 8, 128, 128, 64)
+    assert 2048 * 8 * 4 <= lw < ws // 100 and lw % 256 == 0
+    assert L.up_block_scores_lse_workspace(_p(cu), 1, 32, 8, 96, 128, 64) == 0
     bad = np.array([0, 10, 5], np.int32)
     assert L.up_expand_compact_workspace(_p(bad), 2, 64) == 0
 
@@ -75,8 +79,8 @@ def test_block_scores_rejects_bad_arguments(L):
     f = L.up_block_scores
 
     def call(cu_h=cu, B=1, Hq=8, Hkv=2, d=64, n=128, G=64, ws=FAKE, wsb=1 << 40, q=FAKE):
-        return f(q, FAKE, FAKE, _p(cu_h), B, Hq, Hkv, d, n, G, ctypes.c_float(0.0), FAKE, ws,
-                 ctypes.c_size_t(wsb), None)
+        return f(q, FAKE, FAKE, _p(cu_h), B, Hq, Hkv, d, n, G, ctypes.c_float(0.0), FAKE, None,
+                 ws, ctypes.c_size_t(wsb), None)
 
     assert call(Hkv=3) == UP_EINVAL
     assert call(Hq=0) == UP_EINVAL
@@ -145,3 +149,20 @@ def test_no_cpu_fallback_in_the_product_path():
             src = open(os.path.join(pkg, fn)).read()
             assert "oracle" not in src, fn
             assert "uniprefill_oracle" not in src, fn
+
+
+def test_block_scores_lse_rejects_bad_arguments(L):
+    cu = _cu([4096])
+    f = L.up_block_scores_lse
+
+    def call(lse=FAKE, B=1, Hkv=2, d=64, G=64, ws=FAKE, wsb=1 << 40):
+        return f(FAKE, FAKE, lse, FAKE, _p(cu), B, 8, Hkv, d, 128, G, ctypes.c_float(0.0), FAKE,
+                 ws, ctypes.c_size_t(wsb), None)
+
+    assert call(Hkv=3) == UP_EINVAL
+    assert call(d=80) == UP_EUNSUPPORTED
+    assert call(G=48) == UP_EUNSUPPORTED
+    assert call(lse=None) == UP_EINVAL
+    assert call(lse=ctypes.c_void_p(0x100002)) == UP_EINVAL      # row_lse not 4-byte aligned
+    assert call(wsb=16) == UP_EWORKSPACE
+    assert call(ws=None) == UP_EWORKSPACE
