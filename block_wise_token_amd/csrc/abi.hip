@@ -130,14 +130,25 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
     units += nb * Hkv * nrt;
   }
   // Key-chunk length (blocks per workgroup).  score_wgs_per_cu(d) workgroups fill a
-  // CU, so the score pass takes ceil(items / slots) rounds of CB blocks each: pick
-  // the CB that minimises that product (ties: the larger CB, fewer workgroups).
+  // CU, so the score pass takes ceil(items / slots) rounds, each costing CB blocks of
+  // work plus a workgroup's fixed cost (query load, ring fill, chunk-end stores),
+  // measured at about kChunkOverheadBlocks blocks: pick the CB that minimises
+  // rounds * (CB + overhead) (ties: the larger CB).  Chunks shorter than
+  // kMinChunkBlocks are considered only for requests that short.
   (void)units;
   {
+    constexpr int kChunkOverheadBlocks = 3;
+    constexpr int kMinChunkBlocks = 8;
     const int64_t cus = (int64_t)device_cus() * score_wgs_per_cu(d);
+    int64_t nb_max = 0;
+    for (int i = 0; i < B; ++i) {
+      const int64_t nb = ((int64_t)cu_h[i + 1] - cu_h[i] + G - 1) / G;
+      if (nb > nb_max) nb_max = nb;
+    }
+    const int cb_min = (int)(nb_max < kMinChunkBlocks ? (nb_max > 0 ? nb_max : 1) : kMinChunkBlocks);
     int64_t best_cost = -1;
-    int best_cb = 1;
-    for (int cb = 256; cb >= 1; --cb) {
+    int best_cb = cb_min;
+    for (int cb = kMaxChunkBlocks; cb >= cb_min; --cb) {
       int64_t items = 0;
       for (int i = 0; i < B; ++i) {
         const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
@@ -146,7 +157,7 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
         const int64_t nrt = (gs * W + s->rows_wg - 1) / s->rows_wg;
         items += (nb + cb - 1) / cb * Hkv * nrt;
       }
-      const int64_t cost = (items + cus - 1) / cus * cb;
+      const int64_t cost = (items + cus - 1) / cus * (cb + kChunkOverheadBlocks);
       if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_cb = cb; }
     }
     s->CB = best_cb;

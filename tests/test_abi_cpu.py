@@ -166,3 +166,16 @@ def test_block_scores_lse_rejects_bad_arguments(L):
     assert call(lse=ctypes.c_void_p(0x100002)) == UP_EINVAL      # row_lse not 4-byte aligned
     assert call(wsb=16) == UP_EWORKSPACE
     assert call(ws=None) == UP_EWORKSPACE
+
+
+def test_score_chunks_are_not_tiny_for_mixed_lengths(L):
+    """The score pass's key chunks must amortise a workgroup's fixed cost: for the
+    8-request pack (8K-64K tokens) the chunk statistics ([chunks][Hkv][rows] pairs)
+    stay a small fraction of the per-block statistics ([blocks][Hkv][rows] pairs),
+    which they would match with one-block chunks."""
+    lens = [56971, 44718, 37503, 23662, 25844, 10541, 12506, 9139]
+    cu = _cu(lens)
+    Hq, Hkv, d, n, G = 32, 8, 128, 128, 64
+    ws = L.up_block_scores_workspace(_p(cu), len(lens), Hq, Hkv, d, n, G)
+    per_block = sum((x + G - 1) // G for x in lens) * Hq * n * 8     # (m, l) pairs, bytes
+    assert per_block < ws < 1.2 * per_block
