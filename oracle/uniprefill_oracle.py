@@ -262,6 +262,31 @@ def block_scores_given_lse(qwin_bits: np.ndarray, k_bits: np.ndarray, lse: np.nd
 
 
 # ---------------------------------------------------------------------------
+# Paged key cache (scope: next; [UPA] continuous-batching operator, [CP] chunked
+# prefill reads earlier chunks' keys from the cache)
+# ---------------------------------------------------------------------------
+
+def gather_paged_keys(k_pages: np.ndarray, block_table: np.ndarray, cu_seqlens: np.ndarray,
+                      page_size: int) -> np.ndarray:
+    """Contiguous keys [T, Hkv, d] of a packed batch from a paged cache.
+
+    k_pages: [num_pages, page_size, Hkv, d] (any dtype, copied as is).
+    block_table: int [B, max_pages]; token t of request i lives in page
+    block_table[i, t // page_size], slot t % page_size (reading: the layout of a
+    paged KV cache with one page table per request, pages of page_size tokens).
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    out = []
+    for i in range(cu.size - 1):
+        L = int(cu[i + 1] - cu[i])
+        for t in range(L):
+            out.append(k_pages[int(block_table[i, t // page_size]), t % page_size])
+    if not out:
+        return np.zeros((0,) + k_pages.shape[2:], dtype=k_pages.dtype)
+    return np.stack(out)
+
+
+# ---------------------------------------------------------------------------
 # Step 2: Top-p selection  ([UP] Top-p selection paragraph)
 # ---------------------------------------------------------------------------
 

@@ -520,3 +520,38 @@ def test_given_lse_is_linear_in_each_rows_weight():
     np.testing.assert_allclose(m_shift - m0, (math.exp(-delta) - 1.0) * (m0 - m_gone),
                                rtol=1e-9, atol=1e-15)
     np.testing.assert_allclose((m0 - m_gone).sum(), 1.0, rtol=1e-12)   # one row's weights sum to 1
+
+
+# ---------------------------------------------------------------------------
+# Paged key cache
+# ---------------------------------------------------------------------------
+
+def test_gather_paged_keys_inverts_a_scatter():
+    """Pages built by scattering a contiguous K through a shuffled page table (pages
+    of 16 tokens, partial last pages, an empty request, unused pages) gather back to
+    that K exactly, and the scores computed on it are those of the contiguous K."""
+    rng = np.random.default_rng(12)
+    lens, ps, Hkv, d = [70, 0, 33, 16], 16, 2, 8
+    cu = np.zeros(len(lens) + 1, np.int64)
+    cu[1:] = np.cumsum(lens)
+    T = int(cu[-1])
+    k = synth.f32_to_bf16_bits(rng.standard_normal((T, Hkv, d), dtype=np.float32))
+    need = [(L + ps - 1) // ps for L in lens]
+    num_pages = sum(need) + 5
+    perm = rng.permutation(num_pages)
+    pages = np.zeros((num_pages, ps, Hkv, d), np.uint16)
+    table = np.full((len(lens), max(need)), -1, np.int64)
+    nxt = 0
+    for i, L in enumerate(lens):
+        for pg in range(need[i]):
+            table[i, pg] = perm[nxt]
+            nxt += 1
+            lo, hi = pg * ps, min((pg + 1) * ps, L)
+            pages[table[i, pg], :hi - lo] = k[cu[i] + lo:cu[i] + hi]
+    got = O.gather_paged_keys(pages, table, cu, ps)
+    np.testing.assert_array_equal(got, k)
+    q = synth.f32_to_bf16_bits(rng.standard_normal((sum(min(8, L) for L in lens), 4, d),
+                                                   dtype=np.float32))
+    a = O.block_scores(q, k, cu, 4, Hkv, d, 8, 16)[1]
+    b = O.block_scores(q, got, cu, 4, Hkv, d, 8, 16)[1]
+    np.testing.assert_array_equal(a, b)
