@@ -193,6 +193,9 @@ def main():
     result["given_lse"] = given_lse_leg(up, torch, dec, qwin, k, cu, b, hid, posd, p, args,
                                         stream, score_flops)
 
+    # Keys read through a block table from a paged cache (scope: next), score pass only.
+    result["paged_keys"] = paged_keys_leg(up, torch, qwin, k, cu, b, args)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, hidden, pos, p, cfg)
     print(json.dumps(result), flush=True)
@@ -232,6 +235,40 @@ def given_lse_leg(up, torch, dec_full, qwin, k, cu, b, hid, posd, p, args, strea
             "same_keep_as_full_pass": same,
             "note": "scores from given window-row log-sum-exp (up_block_scores_lse); not the "
                     "headline, which computes the row statistics itself"}
+
+
+def paged_keys_leg(up, torch, qwin, k, cu, b, args, page_size=16):
+    """Score pass with the keys scattered into shuffled pages of 16 tokens (the input
+    layout built here with torch indexing), timed against the contiguous pass."""
+    if b.B != 1 or b.T % page_size:
+        return None
+    npg = b.T // page_size
+    g = torch.Generator(device="cpu").manual_seed(7)
+    perm = torch.randperm(npg, generator=g).to(k.device)
+    pages = torch.empty((npg, page_size) + tuple(k.shape[1:]), dtype=k.dtype, device=k.device)
+    pages[perm] = k.view((npg, page_size) + tuple(k.shape[1:]))
+    table = perm.to(torch.int32).view(1, npg).contiguous()
+    out = {}
+    for name, fn in (("contiguous", lambda: up.block_scores(qwin, k, cu, b.cu_seqlens, b.n, b.G)),
+                     ("paged", lambda: up.block_scores_paged(qwin, pages, table, cu, b.cu_seqlens,
+                                                             b.n, b.G))):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        up.profile_reset()
+        up.profile_enable(True)
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        up.profile_enable(False)
+        n_, t_ = up.profile_read("score_partial")
+        out[name + "_score_us"] = round(t_ * 1e3 / n_, 2)
+        up.profile_reset()
+    same = bool(torch.equal(up.block_scores(qwin, k, cu, b.cu_seqlens, b.n, b.G),
+                            up.block_scores_paged(qwin, pages, table, cu, b.cu_seqlens, b.n, b.G)))
+    assert up.device_error() == 0
+    out.update({"page_size": page_size, "bit_identical": same})
+    return out
 
 
 def copy_reference(torch, nbytes, steps):

@@ -42,6 +42,9 @@ def lib():
     L.up_block_scores.restype = ci
     L.up_block_scores.argtypes = [vp, vp, i32p, vp, ci, ci, ci, ci, ci, ci, cf, f32p, f32p, vp, cs,
                                   vp]
+    L.up_block_scores_paged.restype = ci
+    L.up_block_scores_paged.argtypes = [vp, vp, ctypes.c_int64, ci, i32p, ci, i32p, vp, ci, ci, ci,
+                                        ci, ci, ci, cf, f32p, f32p, vp, cs, vp]
     L.up_block_scores_lse_workspace.restype = cs
     L.up_block_scores_lse_workspace.argtypes = [vp, ci, ci, ci, ci, ci, ci]
     L.up_block_scores_lse.restype = ci
@@ -148,6 +151,33 @@ def block_scores(qwin, k, cu_seqlens, cu_h, n, G, scale=0.0, out=None, workspace
                                G, float(scale), _ptr(out), _ptr(row_lse), _ptr(workspace),
                                workspace.numel(), _stream(stream))
     _check(st, "up_block_scores")
+    return out
+
+
+def block_scores_paged(qwin, k_pages, block_table, cu_seqlens, cu_h, n, G, scale=0.0, out=None,
+                       workspace=None, stream=None, row_lse=None):
+    """Block scores with keys in a paged cache: k_pages bf16 [num_pages, page_size, Hkv,
+    d], block_table int32 [B, max_pages]; see up_block_scores_paged."""
+    _dev(qwin, torch.bfloat16, "qwin")
+    _dev(k_pages, torch.bfloat16, "k_pages")
+    _dev(block_table, torch.int32, "block_table")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    h = _HostCu(cu_h)
+    Hq, d = int(qwin.shape[1]), int(qwin.shape[2])
+    num_pages, page_size, Hkv = int(k_pages.shape[0]), int(k_pages.shape[1]), int(k_pages.shape[2])
+    if out is None:
+        out = torch.empty(h.nb_tot(G), dtype=torch.float32, device=qwin.device)
+    need = int(lib().up_block_scores_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qwin.device)
+    if row_lse is not None:
+        _dev(row_lse, torch.float32, "row_lse")
+    st = lib().up_block_scores_paged(_ptr(qwin), _ptr(k_pages), num_pages, page_size,
+                                     _ptr(block_table), int(block_table.shape[1]), _ptr(cu_seqlens),
+                                     h.ptr, h.B, Hq, Hkv, d, n, G, float(scale), _ptr(out),
+                                     _ptr(row_lse), _ptr(workspace), workspace.numel(),
+                                     _stream(stream))
+    _check(st, "up_block_scores_paged")
     return out
 
 

@@ -214,10 +214,11 @@ size_t up_block_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int
   return score_ws_layout(B, t).total;
 }
 
-int up_block_scores(const void* qwin, const void* k, const int32_t* cu_seqlens,
-                    const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d, int n, int G,
-                    float scale, float* scores, float* row_lse, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+static int block_scores_common(const void* qwin, const void* k, const PagedK* paged,
+                               const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B,
+                               int Hq, int Hkv, int d, int n, int G, float scale, float* scores,
+                               float* row_lse, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   ScoreShape s;
   Totals t;
   const int st = plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t);
@@ -238,7 +239,14 @@ int up_block_scores(const void* qwin, const void* k, const int32_t* cu_seqlens,
     return launch_score_plan(cu_seqlens, s, t, workspace, L.plan, err, hs);
   });
   if (e != hipSuccess) return UP_EHIP;
-  e = timed(0, hs, [&] { return launch_score_partial(qwin, k, s, t, workspace, L, c, hs); });
+  PagedK pk;
+  if (paged) {
+    pk = *paged;
+    pk.err = err;
+  }
+  e = timed(0, hs, [&] {
+    return launch_score_partial(qwin, k, s, t, workspace, L, c, paged ? &pk : nullptr, hs);
+  });
   if (e != hipSuccess) return UP_EHIP;
   e = timed(1, hs, [&] { return launch_row_stats(s, t, workspace, L, row_lse, hs); });
   if (e != hipSuccess) return UP_EHIP;
@@ -247,6 +255,44 @@ int up_block_scores(const void* qwin, const void* k, const int32_t* cu_seqlens,
   e = timed(3, hs, [&] { return launch_normalize(s, t, workspace, L, scores, hs); });
   if (e != hipSuccess) return UP_EHIP;
   return UP_OK;
+}
+
+int up_block_scores(const void* qwin, const void* k, const int32_t* cu_seqlens,
+                    const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d, int n, int G,
+                    float scale, float* scores, float* row_lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return block_scores_common(qwin, k, nullptr, cu_seqlens, cu_seqlens_h, B, Hq, Hkv, d, n, G,
+                             scale, scores, row_lse, workspace, workspace_bytes, stream);
+}
+
+int up_block_scores_paged(const void* qwin, const void* k_pages, int64_t num_pages,
+                          int page_size, const int32_t* block_table, int max_pages,
+                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B, int Hq,
+                          int Hkv, int d, int n, int G, float scale, float* scores,
+                          float* row_lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (page_size < 16 || page_size > 1024 || (page_size & (page_size - 1)) != 0)
+    return UP_EUNSUPPORTED;
+  if (num_pages < 0 || max_pages < 0) return UP_EINVAL;
+  if (!cu_ok(cu_seqlens_h, B)) return UP_EINVAL;
+  int64_t need = 0;
+  for (int i = 0; i < B; ++i) {
+    const int64_t L = (int64_t)cu_seqlens_h[i + 1] - cu_seqlens_h[i];
+    const int64_t p = (L + page_size - 1) / page_size;
+    if (p > need) need = p;
+  }
+  if (need > max_pages) return UP_EINVAL;
+  if (need > 0 && (!block_table || num_pages == 0)) return UP_EINVAL;
+  if (k_pages && !aligned(k_pages, 16)) return UP_EINVAL;
+  PagedK pk;
+  pk.table = block_table;
+  pk.max_pages = max_pages;
+  pk.num_pages = num_pages;
+  int lp = 0;
+  while ((1 << lp) < page_size) ++lp;
+  pk.log2_page = lp;
+  return block_scores_common(qwin, k_pages, &pk, cu_seqlens, cu_seqlens_h, B, Hq, Hkv, d, n, G,
+                             scale, scores, row_lse, workspace, workspace_bytes, stream);
 }
 
 size_t up_block_scores_lse_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d,

@@ -190,12 +190,21 @@ __device__ __forceinline__ void wait_vm_lgkm_barrier(int n) {
 // rebase ever happens; at a block end the workgroup sums the block's probabilities
 // (DPP within each wave, then the waves through LDS at the chunk end) and writes one
 // float partial per (block, kv head, row tile) to pm instead of per-row statistics.
-template <int D, int QT, int NS, int NW, bool LSE>
+//
+// PAGED = true: keys come from a paged cache kmat = [num_pages][page][Hkv][D] through
+// the request's row of the block table (pages of 2^lps tokens, lps >= 4).  A 64-key
+// stage spans at most four pages; their indices are wave-uniform scalar loads made
+// one stage ahead.  Table slots are clamped to the row and page indices outside
+// [0, num_pages) read page 0 and raise error bit 8, so no input reaches memory out of
+// bounds.
+template <int D, int QT, int NS, int NW, bool LSE, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
     const uint16_t* __restrict__ qwin, const uint16_t* __restrict__ kmat,
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
     int G, int CB, float c, float2* __restrict__ ml, float2* __restrict__ cs,
-    const float* __restrict__ row_lse, float* __restrict__ pm) {
+    const float* __restrict__ row_lse, float* __restrict__ pm,
+    const int32_t* __restrict__ btab, int max_pages, int lps, int64_t num_pages,
+    int* __restrict__ err) {
   constexpr int NT = 64 * NW;
   constexpr int UK = 64;               // keys per LDS stage (two 32-key halves)
   constexpr int RB = 2 * D;            // LDS bytes per key row
@@ -260,7 +269,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   const int nh = (kend - k0 + 31) / 32;          // 32-key halves in this chunk
   const int nst = (nh + 1) / 2;                  // LDS stages
   const int64_t kstride = (int64_t)Hkv * D;
-  const uint16_t* kbase = kmat + ((int64_t)pr.tok_off * Hkv + g) * D;
+  const uint16_t* kbase =
+      PAGED ? kmat + (int64_t)g * D : kmat + ((int64_t)pr.tok_off * Hkv + g) * D;
+  const int32_t* trow = PAGED ? btab + (int64_t)i * max_pages : nullptr;
+  bool bad_page = false;
+  // Page indices of a stage's keys (up to four), and the stage they were loaded for.
+  int pf_stage = -1;
+  int pf_pg[4] = {0, 0, 0, 0};
+  auto load_pages = [&](int st, int (&pg)[4]) {
+    const int ks = k0 + st * UK;
+    const int s0 = ks >> lps;
+    const int slast = (min(ks + UK, pr.L) - 1) >> lps;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int slot = __builtin_amdgcn_readfirstlane(min(min(s0 + u, slast), max_pages - 1));
+      int p = trow[slot];
+      if (p < 0 || (int64_t)p >= num_pages) { bad_page = true; p = 0; }
+      pg[u] = p;
+    }
+  };
   const int fast_limit = pr.L - pr.W;   // keys <= this are visible to every window row
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8*)lds;   // LDS byte address
@@ -288,6 +315,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   auto stage_issue = [&](int st) {
     const int ks = k0 + st * UK;
     const uint32_t sbase = lds_base + (uint32_t)((st & (NS - 1)) * SB);
+    if constexpr (PAGED) {
+      int pg[4];
+      if (pf_stage == st) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pg[u] = pf_pg[u];
+      } else {
+        load_pages(st, pg);
+      }
+      const int s0 = ks >> lps;
+      const int pmask = (1 << lps) - 1;
+#pragma unroll
+      for (int q = 0; q < SPT; ++q) {
+        const int kabs = min(ks + dma_key[q], pr.L - 1);
+        const int u = (kabs >> lps) - s0;   // 0..3
+        const int p = u == 0 ? pg[0] : u == 1 ? pg[1] : u == 2 ? pg[2] : pg[3];
+        const int64_t row = ((int64_t)p << lps) + (kabs & pmask);
+        lds_dma16(kbase + row * kstride + (dma_goff[q] - (int64_t)dma_key[q] * kstride),
+                  __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
+      }
+      // The next stage's page indices, in flight while this stage's copies are.
+      if (st + 1 < nst) {
+        load_pages(st + 1, pf_pg);
+        pf_stage = st + 1;
+      }
+      return;
+    }
     const uint16_t* gb = kbase + (int64_t)ks * kstride;
     if (ks + UK <= pr.L) {
 #pragma unroll
@@ -523,6 +576,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   }
 
   flush_pending();
+  if (PAGED && bad_page && tid == 0) atomicOr(err, 8);
   if constexpr (LSE) {
     // Block partials of this (kv head, row tile): the waves' totals in wave order.
     __syncthreads();
@@ -766,56 +820,63 @@ hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Total
   return hipGetLastError();
 }
 
-// Output buffers of one launch of the score kernel (the unused ones are null).
+// Inputs and outputs of one launch of the score kernel (the unused ones are null).
 struct PartialOut {
   size_t plan_off;
   float2* ml;
   float2* cs;
   const float* row_lse;
   float* pm;
+  PagedK pk;
 };
 
-template <int D, int QT, int NS, int NW, bool LSE>
+template <int D, int QT, int NS, int NW, bool LSE, bool PAGED>
 static hipError_t launch_partial_t(const void* qwin, const void* k, const ScoreShape& s,
                                    const Totals& t, void* ws, const PartialOut& o, float c,
                                    hipStream_t st) {
   static_assert(NW * QT * 32 == score_rows_wg(D), "row tile of the kernel and of the plan");
-  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, NS, NW, LSE>), dim3((unsigned)t.items),
-                     dim3(64 * NW), 0,
+  hipLaunchKernelGGL((up_score_partial_kernel<D, QT, NS, NW, LSE, PAGED>),
+                     dim3((unsigned)t.items), dim3(64 * NW), 0,
                      st, static_cast<const uint16_t*>(qwin), static_cast<const uint16_t*>(k),
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + o.plan_off), s.B, s.Hq, s.Hkv,
-                     s.G, s.CB, c, o.ml, o.cs, o.row_lse, o.pm);
+                     s.G, s.CB, c, o.ml, o.cs, o.row_lse, o.pm, o.pk.table, o.pk.max_pages,
+                     o.pk.log2_page, o.pk.num_pages, o.pk.err);
   return hipGetLastError();
 }
 
-template <bool LSE>
+template <bool LSE, bool PAGED>
 static hipError_t launch_partial_d(const void* qwin, const void* k, const ScoreShape& s,
                                    const Totals& t, void* ws, const PartialOut& o, float c,
                                    hipStream_t st) {
   if (t.items == 0) return hipSuccess;
   if (s.CB > kMaxChunkBlocks) return hipErrorInvalidValue;
   switch (s.d) {
-    case 64: return launch_partial_t<64, 2, 8, 8, LSE>(qwin, k, s, t, ws, o, c, st);
-    case 128: return launch_partial_t<128, 2, 4, 8, LSE>(qwin, k, s, t, ws, o, c, st);
-    case 256: return launch_partial_t<256, 1, 4, 8, LSE>(qwin, k, s, t, ws, o, c, st);
+    case 64: return launch_partial_t<64, 2, 8, 8, LSE, PAGED>(qwin, k, s, t, ws, o, c, st);
+    case 128: return launch_partial_t<128, 2, 4, 8, LSE, PAGED>(qwin, k, s, t, ws, o, c, st);
+    case 256: return launch_partial_t<256, 1, 4, 8, LSE, PAGED>(qwin, k, s, t, ws, o, c, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShape& s,
                                 const Totals& t, void* ws, const ScoreWs& L, float c,
-                                hipStream_t st) {
-  const PartialOut o{L.plan, reinterpret_cast<float2*>(wsb(ws) + L.ml),
-                     reinterpret_cast<float2*>(wsb(ws) + L.cs), nullptr, nullptr};
-  return launch_partial_d<false>(qwin, k, s, t, ws, o, c, st);
+                                const PagedK* paged, hipStream_t st) {
+  PartialOut o{L.plan, reinterpret_cast<float2*>(wsb(ws) + L.ml),
+               reinterpret_cast<float2*>(wsb(ws) + L.cs), nullptr, nullptr, PagedK{}};
+  if (paged) {
+    o.pk = *paged;
+    return launch_partial_d<false, true>(qwin, k, s, t, ws, o, c, st);
+  }
+  return launch_partial_d<false, false>(qwin, k, s, t, ws, o, c, st);
 }
 
 hipError_t launch_score_partial_lse(const void* qwin, const void* k, const float* row_lse,
                                     const ScoreShape& s, const Totals& t, void* ws,
                                     const ScoreLseWs& L, float c, hipStream_t st) {
-  const PartialOut o{L.plan, nullptr, nullptr, row_lse, reinterpret_cast<float*>(wsb(ws) + L.pm)};
-  return launch_partial_d<true>(qwin, k, s, t, ws, o, c, st);
+  const PartialOut o{L.plan, nullptr, nullptr, row_lse, reinterpret_cast<float*>(wsb(ws) + L.pm),
+                     PagedK{}};
+  return launch_partial_d<true, false>(qwin, k, s, t, ws, o, c, st);
 }
 
 hipError_t launch_lse_finalize(const ScoreShape& s, const Totals& t, void* ws,

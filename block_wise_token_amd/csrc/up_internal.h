@@ -83,9 +83,19 @@ constexpr int kMaxChunkBlocks = 256;
 // Launchers (score.hip).  Each returns the hipError_t of its launch.
 hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Totals& t,
                              void* ws, size_t plan_off, int* err, hipStream_t st);
+// Paged key cache: k = [num_pages][2^log2_page][Hkv][d], table = int32 [B][max_pages].
+struct PagedK {
+  const int32_t* table = nullptr;
+  int max_pages = 0;
+  int log2_page = 0;
+  int64_t num_pages = 0;
+  int* err = nullptr;
+};
+
+// paged == nullptr: contiguous k = [T][Hkv][d].
 hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShape& s,
                                 const Totals& t, void* ws, const ScoreWs& L, float c_log2,
-                                hipStream_t st);
+                                const PagedK* paged, hipStream_t st);
 hipError_t launch_row_stats(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
                             float* row_lse, hipStream_t st);
 // The given-lse pass: row_lse [sum W_i, Hq] natural-log log-sum-exp of each window row.

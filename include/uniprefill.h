@@ -98,6 +98,23 @@ int up_block_scores(const void* qwin, const void* k,
                     float* scores, float* row_lse, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Same computation with the keys in a paged cache (the layout of a KV cache that
+ * serves continuous batching, [UPA]; chunked prefill reads earlier chunks' keys from
+ * it, [CP]):
+ * k_pages     : bf16 [num_pages, page_size, Hkv, d]; token t of request i is
+ *               k_pages[block_table[i * max_pages + t / page_size], t % page_size].
+ * page_size   : a power of two in [16, 1024] (UP_EUNSUPPORTED otherwise).
+ * block_table : int32 [B, max_pages]; max_pages >= ceil(L_i / page_size) for every
+ *               request (UP_EINVAL otherwise).
+ * A page index outside [0, num_pages) reads page 0 instead and raises device error
+ * bit 8.  Workspace: up_block_scores_workspace(...).  Other arguments as above. */
+int up_block_scores_paged(const void* qwin, const void* k_pages, int64_t num_pages,
+                          int page_size, const int32_t* block_table, int max_pages,
+                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B,
+                          int Hq, int Hkv, int d, int n, int G, float scale, float* scores,
+                          float* row_lse, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* ---------------------------------------------------------------------------
  * 1b. Block scores from the layer's own softmax statistics  ([UP] "Triton kernels"
  *     paragraph: the full-attention layer runs an online softmax over these rows,
@@ -204,7 +221,8 @@ int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
  * ------------------------------------------------------------------------- */
 
 /* Device error word: bit 1 = cu_seqlens inconsistent with the host copy,
- * bit 2 = index out of range in up_compose_drops, bit 4 = count above capacity.
+ * bit 2 = index out of range in up_compose_drops, bit 4 = count above capacity,
+ * bit 8 = page index outside the paged key cache (up_block_scores_paged).
  * Synchronises `stream`, copies the word to *code_h and clears it. */
 int up_device_error(int32_t* code_h, void* stream);
 

@@ -179,3 +179,20 @@ def test_score_chunks_are_not_tiny_for_mixed_lengths(L):
     ws = L.up_block_scores_workspace(_p(cu), len(lens), Hq, Hkv, d, n, G)
     per_block = sum((x + G - 1) // G for x in lens) * Hq * n * 8     # (m, l) pairs, bytes
     assert per_block < ws < 1.2 * per_block
+
+
+def test_block_scores_paged_rejects_bad_arguments(L):
+    cu = _cu([1000, 24])
+    f = L.up_block_scores_paged
+
+    def call(ps=16, maxp=63, table=FAKE, npages=100, B=2):
+        return f(FAKE, FAKE, ctypes.c_int64(npages), ps, table, maxp, FAKE, _p(cu), B, 8, 2, 64,
+                 128, 64, ctypes.c_float(0.0), FAKE, None, FAKE, ctypes.c_size_t(1 << 40), None)
+
+    assert call(ps=24) == UP_EUNSUPPORTED          # not a power of two
+    assert call(ps=8) == UP_EUNSUPPORTED           # below 16
+    assert call(ps=2048) == UP_EUNSUPPORTED
+    assert call(maxp=62) == UP_EINVAL              # 1000 tokens need 63 pages of 16
+    assert call(table=None) == UP_EINVAL
+    assert call(npages=0) == UP_EINVAL
+    assert call(npages=-1) == UP_EINVAL

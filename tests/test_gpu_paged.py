@@ -1,0 +1,113 @@
+"""GPU parity of the paged-key score pass (keys read through a block table).
+
+Keys are scattered into shuffled pages (with unused pages in between); the paged
+pass must give bit-identical scores and row statistics to the contiguous pass on
+the same keys (the same arithmetic on the same values) and meet the oracle on the
+keys it gathers from the pages; a page index outside the cache raises error bit 8
+without touching memory outside it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_wise_token_amd as up
+from oracle import uniprefill_oracle as O
+from workloads import synth
+from tests.gpu_helpers import GpuBatch, check_scores, i32_dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _batch(lengths, Hq, Hkv, d, n, G, seed):
+    reqs = [synth.gen_request(L, Hq, Hkv, d, n, G, 2,
+                              np.random.default_rng([seed, synth.TAG_VARLEN_REQUEST, i]))
+            for i, L in enumerate(lengths)]
+    return synth.pack(reqs, Hq, Hkv, d, n, G)
+
+
+def _paginate(k_bits, cu, ps, seed, spare=7):
+    """Scatter contiguous keys [T, Hkv, d] into shuffled pages; returns (pages, table)."""
+    rng = np.random.default_rng(seed)
+    lens = np.diff(np.asarray(cu, np.int64))
+    need = [int((L + ps - 1) // ps) for L in lens]
+    num_pages = sum(need) + spare
+    perm = rng.permutation(num_pages)
+    pages = rng.integers(0, 1 << 15, (num_pages, ps) + k_bits.shape[1:]).astype(np.uint16)
+    table = np.full((len(lens), max(1, max(need))), -1, np.int32)
+    nxt = 0
+    for i, L in enumerate(lens):
+        for pg in range(need[i]):
+            table[i, pg] = perm[nxt]
+            nxt += 1
+            lo, hi = pg * ps, min((pg + 1) * ps, int(L))
+            pages[table[i, pg], :hi - lo] = k_bits[cu[i] + lo:cu[i] + hi]
+    return pages, table
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+CASES = [
+    # lengths, Hq, Hkv, d, n, G, page size
+    ([4096], 8, 2, 64, 128, 64, 16),
+    ([1000], 4, 2, 64, 128, 64, 32),
+    ([300], 8, 2, 128, 128, 32, 64),
+    ([2000], 4, 2, 256, 128, 64, 16),
+    ([1500], 8, 1, 64, 64, 96, 256),              # G = 96: stages straddle 64-key pages
+    ([129, 0, 3000, 64, 1], 8, 2, 128, 128, 64, 16),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_paged_pass_matches_contiguous_and_oracle(case):
+    lengths, Hq, Hkv, d, n, G, ps = case
+    b = _batch(lengths, Hq, Hkv, d, n, G, seed=ps + d + len(lengths))
+    say(f"[case] paged keys {case}")
+    pages, table = _paginate(b.k, b.cu_seqlens, ps, seed=ps)
+    gb = GpuBatch(b)
+    lse_c = torch.empty((b.qwin.shape[0], Hq), dtype=torch.float32, device="cuda")
+    lse_p = torch.empty_like(lse_c)
+    s_c = up.block_scores(gb.qwin, gb.k, gb.cu, gb.cu_h, n, G, row_lse=lse_c)
+    s_p = up.block_scores_paged(gb.qwin, _bf16(pages), i32_dev(table), gb.cu, gb.cu_h, n, G,
+                                row_lse=lse_p)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    assert torch.equal(s_c, s_p)
+    assert torch.equal(lse_c, lse_p)
+    kk = O.gather_paged_keys(pages, table, b.cu_seqlens, ps)
+    _, s64, _ = O.block_scores(b.qwin, kk, b.cu_seqlens, Hq, Hkv, d, n, G)
+    worst = check_scores(s_p.cpu().numpy(), s64)
+    say(f"[ok] paged {case}: bit-identical to contiguous, worst rel err {worst:.2e}")
+
+
+def test_page_index_outside_the_cache_raises_error_bit():
+    b = _batch([1000], 8, 2, 64, 128, 64, seed=1)
+    pages, table = _paginate(b.k, b.cu_seqlens, 16, seed=3)
+    bad = table.copy()
+    bad[0, 5] = pages.shape[0] + 1000     # past the cache
+    bad[0, 9] = -3
+    gb = GpuBatch(b)
+    say("[case] paged keys with out-of-range page indices")
+    up.device_error()
+    up.block_scores_paged(gb.qwin, _bf16(pages), i32_dev(bad), gb.cu, gb.cu_h, 128, 64)
+    torch.cuda.synchronize()
+    assert up.device_error() & 8
+    s = up.block_scores_paged(gb.qwin, _bf16(pages), i32_dev(table), gb.cu, gb.cu_h, 128, 64)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0 and torch.isfinite(s).all()
+
+
+@pytest.mark.timeout(600)
+def test_paged_pass_at_128k_is_bit_identical():
+    cfg = synth.WORKLOADS["llama31_8b_128k"]
+    say("[setup] generating llama31_8b_128k")
+    b = synth.make_batch(cfg)
+    pages, table = _paginate(b.k, b.cu_seqlens, 16, seed=16)
+    gb = GpuBatch(b)
+    say("[case] paged keys at 128K, 16-token pages")
+    s_c = up.block_scores(gb.qwin, gb.k, gb.cu, gb.cu_h, b.n, b.G)
+    s_p = up.block_scores_paged(gb.qwin, _bf16(pages), i32_dev(table), gb.cu, gb.cu_h, b.n, b.G)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    assert torch.equal(s_c, s_p)
