@@ -193,6 +193,10 @@ def main():
     result["given_lse"] = given_lse_leg(up, torch, dec, qwin, k, cu, b, hid, posd, p, args,
                                         stream, score_flops)
 
+    # Independent decisions (a stream of requests) on two HIP streams: one request's
+    # HBM-bound compaction runs beside the next one's compute-bound scoring.
+    result["two_streams"] = two_streams_leg(up, torch, dec, qwin, k, cu, b, hid, posd, p, args)
+
     # Keys read through a block table from a paged cache (scope: next), score pass only.
     result["paged_keys"] = paged_keys_leg(up, torch, qwin, k, cu, b, args)
 
@@ -235,6 +239,28 @@ def given_lse_leg(up, torch, dec_full, qwin, k, cu, b, hid, posd, p, args, strea
             "same_keep_as_full_pass": same,
             "note": "scores from given window-row log-sum-exp (up_block_scores_lse); not the "
                     "headline, which computes the row statistics itself"}
+
+
+def two_streams_leg(up, torch, dec_a, qwin, k, cu, b, hid, posd, p, args):
+    """Throughput of independent decisions issued alternately on two streams (each
+    decision has its own buffers; both read the same resident inputs)."""
+    dec_b = up.LayerDecision(qwin, k, cu, b.cu_seqlens, hid, posd, b.n, b.G, p)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for j in range(2 * args.warmup):
+        (dec_a if j % 2 == 0 else dec_b).run(stream=sa if j % 2 == 0 else sb)
+    torch.cuda.synchronize()
+    n = 2 * args.steps
+    t0 = time.perf_counter()
+    for j in range(n):
+        (dec_a if j % 2 == 0 else dec_b).run(stream=sa if j % 2 == 0 else sb)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert up.device_error() == 0
+    same = bool(torch.equal(dec_a.keep, dec_b.keep))
+    return {"decisions": n, "ms_per_decision": dt * 1e3 / n, "tokens_per_s": b.T * n / dt,
+            "same_keep": same, "note": "two independent decisions in flight on two HIP "
+                                       "streams; wall clock; not the headline"}
 
 
 def paged_keys_leg(up, torch, qwin, k, cu, b, args, page_size=16):
