@@ -134,7 +134,9 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
   // work plus a workgroup's fixed cost (query load, ring fill, chunk-end stores),
   // measured at about kChunkOverheadBlocks blocks: pick the CB that minimises
   // rounds * (CB + overhead) (ties: the larger CB).  Chunks shorter than
-  // kMinChunkBlocks are considered only for requests that short.
+  // kMinChunkBlocks are considered only for requests that short.  The candidates are
+  // 8..256 in steps of about 1.25x (plus the shortest allowed and the longest
+  // request's block count), which keeps planning linear in B with a small constant.
   (void)units;
   {
     constexpr int kChunkOverheadBlocks = 3;
@@ -146,19 +148,32 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
       if (nb > nb_max) nb_max = nb;
     }
     const int cb_min = (int)(nb_max < kMinChunkBlocks ? (nb_max > 0 ? nb_max : 1) : kMinChunkBlocks);
+    static const int kCand[] = {256, 224, 192, 160, 128, 112, 96, 80, 64, 56, 48, 40, 32,
+                                28, 24, 20, 16, 14, 12, 10, 8};
+    int cands[sizeof(kCand) / sizeof(kCand[0]) + 2];
+    int nc = 0;
+    for (int cb : kCand)
+      if (cb >= cb_min) cands[nc++] = cb;
+    if (nb_max >= cb_min && nb_max < kMaxChunkBlocks) cands[nc++] = (int)nb_max;
+    cands[nc++] = cb_min;
+    // Per request: blocks and workgroups per key chunk (kv heads x row tiles).
+    std::vector<std::pair<int64_t, int64_t>> req(B);
+    for (int i = 0; i < B; ++i) {
+      const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
+      const int64_t W = L < n ? L : n;
+      req[i] = {(L + G - 1) / G, Hkv * ((gs * W + s->rows_wg - 1) / s->rows_wg)};
+    }
     int64_t best_cost = -1;
     int best_cb = cb_min;
-    for (int cb = kMaxChunkBlocks; cb >= cb_min; --cb) {
+    for (int ci = 0; ci < nc; ++ci) {
+      const int cb = cands[ci];
       int64_t items = 0;
-      for (int i = 0; i < B; ++i) {
-        const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
-        const int64_t W = L < n ? L : n;
-        const int64_t nb = (L + G - 1) / G;
-        const int64_t nrt = (gs * W + s->rows_wg - 1) / s->rows_wg;
-        items += (nb + cb - 1) / cb * Hkv * nrt;
-      }
+      for (const auto& r : req) items += (r.first + cb - 1) / cb * r.second;
       const int64_t cost = (items + cus - 1) / cus * (cb + kChunkOverheadBlocks);
-      if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_cb = cb; }
+      if (best_cost < 0 || cost < best_cost || (cost == best_cost && cb > best_cb)) {
+        best_cost = cost;
+        best_cb = cb;
+      }
     }
     s->CB = best_cb;
   }
