@@ -24,6 +24,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "prefill tokens/sec selected+compacted per layer at 128K; % MFMA peak, % HBM BW"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+# Kernel instances the headline decision launches (d = 128, contiguous keys, 16-byte rows),
+# as rocprofv3 names them.
+SCORE_KERNEL = "up_score_partial_kernel<128, 2, 4, 8, false, false>"
+GATHER_KERNEL = "up_gather_kernel<unsigned int __vector(4), 128, 2>"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
@@ -40,10 +44,15 @@ def measured_traffic(workload: str, kernel: str):
         return None
     scale = None
     for line in open(path):
-        parts = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
         if line.startswith("scale "):
+            parts = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
             scale = float(parts["fetch"]), float(parts["write"])
-        elif parts.get("kernel") == kernel and scale:
+            continue
+        if not line.startswith("kernel=") or " | " not in line:
+            continue
+        name, rest = line[len("kernel="):].split(" | ", 1)
+        parts = dict(kv.split("=", 1) for kv in rest.split() if "=" in kv)
+        if name.strip() == kernel and scale:
             src = os.path.join(ROOT, parts["source"])
             if not os.path.exists(src):
                 return None
@@ -66,6 +75,9 @@ def main():
     ap.add_argument("--workload", default="llama31_8b_128k")
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline decision (no given-lse, two-stream or paged "
+                         "legs): the mode the rocprofv3 summaries are taken in")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="BYTES",
                     help="only time a plain device-to-device copy of BYTES (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -155,12 +167,12 @@ def main():
     roof_score = {"bound": "mfma", "achieved": round(score_tflops, 2),
                   "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                   "frac": round(score_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                  "traffic": measured_traffic(args.workload, "up_score_partial_kernel"),
+                  "traffic": measured_traffic(args.workload, SCORE_KERNEL),
                   "kernel": "up_score_partial_kernel", "avg_us": round(s_us, 2),
                   "work_per_launch": score_flops}
     roof_gather = {"bound": "hbm", "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
-                   "traffic": measured_traffic(args.workload, "up_gather_kernel"),
+                   "traffic": measured_traffic(args.workload, GATHER_KERNEL),
                    "kernel": "up_gather_kernel", "avg_us": round(g_us, 2),
                    "work_per_launch": gather_bytes}
     dominant = roof_gather if g_us >= s_us else roof_score
@@ -190,15 +202,19 @@ def main():
     # The scope's next row: the same decision given each window row's log-sum-exp (what
     # the layer's own attention keeps), here taken from the full pass's row_lse output.
     # Reported beside the headline, which runs every step of the path itself.
-    result["given_lse"] = given_lse_leg(up, torch, dec, qwin, k, cu, b, hid, posd, p, args,
-                                        stream, score_flops)
+    if not args.headline_only:
+        result["given_lse"] = given_lse_leg(up, torch, dec, qwin, k, cu, b, hid, posd, p, args,
+                                            stream, score_flops)
 
     # Independent decisions (a stream of requests) on two HIP streams: one request's
     # HBM-bound compaction runs beside the next one's compute-bound scoring.
-    result["two_streams"] = two_streams_leg(up, torch, dec, qwin, k, cu, b, hid, posd, p, args)
+    if not args.headline_only:
+        result["two_streams"] = two_streams_leg(up, torch, dec, qwin, k, cu, b, hid, posd, p,
+                                                args)
 
     # Keys read through a block table from a paged cache (scope: next), score pass only.
-    result["paged_keys"] = paged_keys_leg(up, torch, qwin, k, cu, b, args)
+    if not args.headline_only:
+        result["paged_keys"] = paged_keys_leg(up, torch, qwin, k, cu, b, args)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, hidden, pos, p, cfg)
