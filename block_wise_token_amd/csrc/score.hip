@@ -378,6 +378,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   const bool st_ok = (QT == 2 || half == 0) && (r_st < R);
 
   int hcnt = G / 32;   // halves left in the current block
+  // Blocks end one at a time in order: the chunk-relative index of the next block to
+  // end, and (full pass) where its (m, l) pair goes, advanced by one block per end.
+  int blk_rel = 0;
+  int64_t ml_at = st_ok ? pr.ml_off + ((int64_t)b0 * Hkv + g) * R + r_st : -1;
+  const int64_t ml_step = (int64_t)Hkv * R;
   f32x16 acc0[QT], acc1[QT];
   float2 pend_v = make_float2(0.f, 0.f);   // block statistics waiting to be stored
   int64_t pend_i = -1;
@@ -461,14 +466,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
       for (int t = 0; t < QT; ++t) lblk[t] += sum[t];
       if (--hcnt == 0 || h == nh - 1) {
         hcnt = G / 32;
-        const int bl = (k0 + h * 32) / G;   // request-local block
+        const int bl = blk_rel++;   // chunk-relative block
         float v = lblk[0];
 #pragma unroll
         for (int t = 1; t < QT; ++t) v += lblk[t];
 #pragma unroll
         for (int t = 0; t < QT; ++t) lblk[t] = 0.f;
         v = wave_scan_f32(v);
-        if (lane == 63) blk_acc[(bl - b0) * NW + wave] = v;
+        if (lane == 63) blk_acc[bl * NW + wave] = v;
       }
       return;
     }
@@ -484,7 +489,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
     for (int t = 0; t < QT; ++t) lblk[t] = nl[t];
     if (--hcnt == 0 || h == nh - 1) {
       hcnt = G / 32;
-      const int bl = (k0 + h * 32) / G;   // request-local block
       float lst = 0.f, mst = 0.f;
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
@@ -496,7 +500,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
       // The store is issued after the next stage barrier (flush_pending).
       flush_pending();   // a block ended since the last barrier (G < 64): store it now
       pend_v = make_float2(lst > 0.f ? mst : kNegInf, lst);
-      pend_i = st_ok ? pr.ml_off + ((int64_t)bl * Hkv + g) * R + r_st : -1;
+      pend_i = ml_at;
+      if (st_ok) ml_at += ml_step;
     }
   };
 
