@@ -9,8 +9,10 @@
 // whole contiguous runs of G * row_bytes: up_block_dst_kernel assigns each kept
 // block its destination row (kept blocks in ascending order per request, requests
 // in order), and up_gather_kernel streams the runs with 16-byte loads and stores,
-// several workgroups per block.  The row-index list (idx_out) and positions come
-// out of the same pass.  Drop composition is a plain gather through idx.
+// several workgroups per block.  The row-index list (idx_out), the positions and,
+// when asked, the composed original indices (orig_out[r] = prev_orig[idx_out[r]])
+// come out of the same pass.  up_compose_kernel is the standalone composition: a
+// plain gather through idx.
 #include "up_dpp.h"
 #include "up_internal.h"
 

@@ -9,10 +9,11 @@
 // shortest prefix of that order whose exact running sum reaches p, so it is fixed
 // by one key, the cut: the (score, index) of the last kept block.  Nothing is
 // sorted.  The cut's score is found by a radix select over the float bits (a score
-// in [0, 1] has 30 significant bits: 7 exponent bits, 23 fraction bits), three
-// passes of 10-bit digits from the top.  Each pass histograms the candidates still
-// in play by digit -- a count and an exact sum per bin -- and takes the first bin,
-// walking digits downwards, whose cumulative sum reaches what is left of p.
+// in [0, 1] has 30 significant bits: 7 exponent bits, 23 fraction bits), four
+// passes from the top: the exponent, then fraction digits of 8, 8 and 7 bits.  Each
+// pass histograms the candidates still in play by digit -- a count and an exact sum
+// per bin, spread over eight copies against LDS atomic contention -- and takes the
+// first bin, walking digits downwards, whose cumulative sum reaches what is left of p.
 //
 // Sums are exact integers.  A float32 in [0, 1] is M * 2^sh units of 2^-149, with M
 // its 24-bit significand and sh = max(exponent - 1, 0).  The first digit fixes the
