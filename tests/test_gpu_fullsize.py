@@ -149,3 +149,30 @@ def test_four_layer_stack_composes_drops():
         pos = dec.pos_out[:cnt].clone()
         orig = dec.orig[:cnt].clone()
         orig_np = orig_next
+
+
+@pytest.mark.timeout(900)
+def test_largest_supported_request():
+    """One request of 16384 blocks of 64 tokens (1,048,576 tokens, the selection
+    limit): the full decision against the oracle (Hq=4, Hkv=2, d=64 keeps the oracle
+    to about half a minute)."""
+    L, Hq, Hkv, d, n, G, p = 16384 * 64, 4, 2, 64, 128, 64, 0.99
+    say(f"[setup] generating one request of {L} tokens")
+    req = synth.gen_request(L, Hq, Hkv, d, n, G, 16,
+                            np.random.default_rng([11, synth.TAG_VARLEN_REQUEST, 0]))
+    b = synth.pack([req], Hq, Hkv, d, n, G)
+    gb = GpuBatch(b, H=256, seed=11)
+    say("[case] largest request: decision")
+    res = run_decision(gb, p)
+    say("[case] largest request: oracle scores")
+    s32, s64, _ = O.block_scores(b.qwin, b.k, b.cu_seqlens, Hq, Hkv, d, n, G)
+    worst = check_scores(res["scores"], s64)
+    ref_keep, _, _ = O.topp_select(s32, b.cu_seqlens, n, G, p)
+    amb = ambiguous_blocks(s32, b.cu_seqlens, n, G, p)
+    ndiff = check_keep(res["keep"], ref_keep, amb)
+    own_keep, own_cu, _ = O.topp_select(res["scores"], b.cu_seqlens, n, G, p)
+    np.testing.assert_array_equal(res["keep"], own_keep)
+    np.testing.assert_array_equal(res["cu_out"], own_cu)
+    check_compaction(gb, res, sample_rows=4096, seed=5)
+    say(f"[ok] {L} tokens: worst rel err {worst:.2e}, ambiguous {len(amb)}, differing {ndiff}, "
+        f"kept {res['count']}/{b.T}")
