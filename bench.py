@@ -219,6 +219,7 @@ def main():
     # the layer's own attention keeps), here taken from the full pass's row_lse output.
     # Reported beside the headline, which runs every step of the path itself.
     if not args.headline_only:
+        result["median_flushed"] = median_flushed_leg(torch, dec, stream, T)
         result["given_lse"] = given_lse_leg(up, torch, dec, qwin, k, cu, b, hid, posd, p, args,
                                             stream, score_flops)
 
@@ -235,6 +236,28 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, hidden, pos, p, cfg)
     print(json.dumps(result), flush=True)
+
+
+def median_flushed_leg(torch, dec, stream, T, reps=100, warmup=20, flush_bytes=1 << 30):
+    """Median of individually timed decisions with a 1 GiB write between them, so
+    that no input is left in the 256 MB Infinity Cache from the previous rep."""
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        dec.run()
+    times = []
+    for _ in range(reps):
+        scratch.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dec.run()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    med = float(np.median(times))
+    del scratch
+    return {"reps": reps, "median_ms": med, "p10_ms": float(np.percentile(times, 10)),
+            "p90_ms": float(np.percentile(times, 90)), "tokens_per_s": T / (med * 1e-3),
+            "note": "1 GiB written between reps (Infinity Cache flushed); not the headline"}
 
 
 def given_lse_leg(up, torch, dec_full, qwin, k, cu, b, hid, posd, p, args, stream, score_flops):
@@ -349,11 +372,21 @@ def copy_reference(torch, nbytes, steps):
 def cpu_baseline(b, hidden, pos, p, cfg):
     """The oracle, untuned, timed on this host on one full decision of the same workload."""
     from oracle import uniprefill_oracle as O
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([d.get("num_threads", 1) for d in info] or [1])
+        blas = ", ".join(sorted({f"{d.get('internal_api')} {d.get('version')}" for d in info
+                                 if d.get("user_api") == "blas"})) or blas
     except Exception:  # threadpoolctl missing: report the affinity size
         threads = len(os.sched_getaffinity(0))
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     log("[bench] cpu baseline: oracle on one full decision ...")
     t0 = time.perf_counter()
     O.decide(b.qwin, b.k, b.cu_seqlens, hidden, pos, b.Hq, b.Hkv, b.d, b.n, b.G, p, fast=True)
@@ -362,7 +395,7 @@ def cpu_baseline(b, hidden, pos, p, cfg):
     return {"value": b.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"one full decision of {cfg and 'the same workload'} "
                       f"({b.T} tokens: scores, Top-p, expand, compact, compose), NumPy float64",
-            "seconds": dt, "cpu": platform.processor() or platform.machine()}
+            "seconds": dt, "cpu": cpu, "blas": blas}
 
 
 if __name__ == "__main__":
