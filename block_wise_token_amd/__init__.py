@@ -24,5 +24,11 @@ from ._binding import (  # noqa: F401
     profile_reset,
     topk_select,
     topp_select,
+    rope_attention,
+    rope_attention_workspace_bytes,
+    linear,
+    swiglu,
+    swiglu_ffn,
+    swiglu_ffn_workspace_bytes,
     KERNEL_IDS,
 )

@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(_HERE, "libuniprefill.so")
 KERNEL_IDS = {
     "score_partial": 0, "row_stats": 1, "block_mass": 2, "normalize": 3, "select": 4,
     "select_finalize": 5, "block_dst": 6, "gather": 7, "compose": 8, "score_plan": 9,
-    "score_partial_lse": 10, "lse_finalize": 11,
+    "score_partial_lse": 10, "lse_finalize": 11, "attn_plan": 12, "rope_layout": 13,
+    "attention": 14, "swiglu": 15, "gemm": 16,
 }
 
 _lib = None
@@ -69,6 +70,20 @@ def lib():
     L.up_profile_read.argtypes = [ci, vp, vp]
     L.up_profile_reset.restype = ci
     L.up_profile_reset.argtypes = []
+    i64 = ctypes.c_int64
+    L.up_rope_attention_workspace.restype = cs
+    L.up_rope_attention_workspace.argtypes = [vp, ci, ci, ci, ci]
+    L.up_rope_attention.restype = ci
+    L.up_rope_attention.argtypes = [vp, vp, vp, i32p, i32p, vp, ci, ci, ci, ci, cf, cf, vp, vp, cs,
+                                    vp]
+    L.up_linear.restype = ci
+    L.up_linear.argtypes = [vp, vp, vp, i64, ci, ci, vp, vp, cs, vp]
+    L.up_swiglu.restype = ci
+    L.up_swiglu.argtypes = [vp, i64, ci, vp, vp]
+    L.up_swiglu_ffn_workspace.restype = cs
+    L.up_swiglu_ffn_workspace.argtypes = [i64, ci, ci]
+    L.up_swiglu_ffn.restype = ci
+    L.up_swiglu_ffn.argtypes = [vp, vp, vp, vp, i64, ci, ci, vp, vp, cs, vp]
     _lib = L
     return L
 
@@ -360,3 +375,84 @@ class LayerDecision:
                        idx_out=self.idx, hidden_out=self.hidden_out, pos_out=self.pos_out,
                        workspace=self.ws_compact, stream=stream, prev_orig=self.prev_orig,
                        orig_out=self.orig)
+
+
+# ---- the layer on the surviving tokens ------------------------------------------
+
+def rope_attention_workspace_bytes(cu_h, Hq, Hkv, d) -> int:
+    h = _HostCu(cu_h)
+    return int(lib().up_rope_attention_workspace(h.ptr, h.B, Hq, Hkv, d))
+
+
+def rope_attention(q, k, v, pos, cu_seqlens, cu_h, scale=0.0, rope_theta=500000.0, out=None,
+                   workspace=None, stream=None):
+    """Rotary embedding at ``pos`` then causal GQA attention per request (bf16 [R, Hq, d]);
+    see up_rope_attention.  q [R, Hq, d], k and v [R, Hkv, d] bf16, pos int32 [R]."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(k, torch.bfloat16, "k")
+    _dev(v, torch.bfloat16, "v")
+    _dev(pos, torch.int32, "pos")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    h = _HostCu(cu_h)
+    Hq, d, Hkv = int(q.shape[1]), int(q.shape[2]), int(k.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    need = int(lib().up_rope_attention_workspace(h.ptr, h.B, Hq, Hkv, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().up_rope_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(cu_seqlens), h.ptr, h.B,
+                                 Hq, Hkv, d, float(scale), float(rope_theta), _ptr(out),
+                                 _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "up_rope_attention")
+    return out
+
+
+def linear(x, w, residual=None, out=None, workspace=None, stream=None):
+    """x [R, K] . w[N, K]^T (+ residual) in bf16 through hipBLASLt; see up_linear."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w, torch.bfloat16, "w")
+    R, K = int(x.shape[0]), int(x.shape[1])
+    N = int(w.shape[0])
+    if residual is not None:
+        _dev(residual, torch.bfloat16, "residual")
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.bfloat16, device=x.device)
+    nbytes = 0 if workspace is None else workspace.numel()
+    st = lib().up_linear(_ptr(x), _ptr(w), _ptr(residual), R, K, N, _ptr(out), _ptr(workspace),
+                         nbytes, _stream(stream))
+    _check(st, "up_linear")
+    return out
+
+
+def swiglu(gu, out=None, stream=None):
+    """silu(gu[:, :F]) * gu[:, F:] in bf16; see up_swiglu."""
+    _dev(gu, torch.bfloat16, "gu")
+    R, F = int(gu.shape[0]), int(gu.shape[1]) // 2
+    if out is None:
+        out = torch.empty((R, F), dtype=torch.bfloat16, device=gu.device)
+    _check(lib().up_swiglu(_ptr(gu), R, F, _ptr(out), _stream(stream)), "up_swiglu")
+    return out
+
+
+def swiglu_ffn_workspace_bytes(R, H, F) -> int:
+    return int(lib().up_swiglu_ffn_workspace(R, H, F))
+
+
+def swiglu_ffn(x, w_gu, w_down, residual=None, out=None, workspace=None, stream=None):
+    """SwiGLU FFN: swiglu(x . w_gu^T) . w_down^T (+ residual); see up_swiglu_ffn."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w_gu, torch.bfloat16, "w_gu")
+    _dev(w_down, torch.bfloat16, "w_down")
+    R, H = int(x.shape[0]), int(x.shape[1])
+    F = int(w_gu.shape[0]) // 2
+    if residual is not None:
+        _dev(residual, torch.bfloat16, "residual")
+    if out is None:
+        out = torch.empty((R, H), dtype=torch.bfloat16, device=x.device)
+    need = int(lib().up_swiglu_ffn_workspace(R, H, F))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib().up_swiglu_ffn(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(residual), R, H, F, _ptr(out),
+                             _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "up_swiglu_ffn")
+    return out

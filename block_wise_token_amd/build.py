@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libuniprefill.so")
-SOURCES = ["abi.hip", "score.hip", "select.hip", "compact.hip"]
+SOURCES = ["abi.hip", "score.hip", "select.hip", "compact.hip", "consumer.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are switched off for all device code.
@@ -50,7 +50,8 @@ def build(verbose: bool = True) -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    # hipBLASLt serves the plain GEMMs of the layer on the surviving tokens.
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-lhipblaslt", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -4,6 +4,7 @@
 #include "uniprefill.h"
 #include "up_internal.h"
 
+#include <climits>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -440,6 +441,138 @@ int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
     return launch_compose(prev_orig, prev_len, idx, count, capacity, orig_out, err, hs);
   });
   return e == hipSuccess ? UP_OK : UP_EHIP;
+}
+
+// ---- layer on the surviving tokens --------------------------------------------
+
+namespace {
+// Shape of an attention call; returns UP_OK or an error status.
+int plan_attention(const int32_t* cu_h, int B, int Hq, int Hkv, int d, AttnShape* s) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return UP_EINVAL;
+  if (!cu_ok(cu_h, B)) return UP_EINVAL;
+  if (d != 64 && d != 128) return UP_EUNSUPPORTED;
+  const int gsz = Hq / Hkv;
+  s->B = B; s->Hq = Hq; s->Hkv = Hkv; s->d = d;
+  s->HQ = gsz % 4 == 0 ? 4 : (gsz % 2 == 0 ? 2 : 1);
+  s->TT = 4 / s->HQ;
+  const int tok_tile = 64 * s->TT;
+  int64_t Rp = 0, tiles = 0;
+  for (int i = 0; i < B; ++i) {
+    const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
+    Rp += (L + 63) / 64 * 64;
+    tiles += (L + tok_tile - 1) / tok_tile;
+  }
+  s->R = B > 0 ? cu_h[B] : 0;
+  s->Rp = Rp;
+  s->tiles = tiles;
+  if (Rp > INT32_MAX || tiles > 65535) return UP_EUNSUPPORTED;
+  if ((int64_t)Hkv * (gsz / s->HQ) > 65535) return UP_EUNSUPPORTED;
+  return UP_OK;
+}
+
+// hipBLASLt workspace the library offers its GEMMs inside up_swiglu_ffn.
+constexpr size_t kGemmWs = size_t(32) << 20;
+
+struct FfnWs {
+  size_t gu, a, gemm, total;
+};
+FfnWs ffn_ws_layout(int64_t R, int F) {
+  FfnWs w;
+  size_t o = 0;
+  w.gu = o;
+  o += align_up((size_t)R * 2 * F * 2);
+  w.a = o;
+  o += align_up((size_t)R * F * 2);
+  w.gemm = o;
+  o += kGemmWs;
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+size_t up_rope_attention_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d) {
+  AttnShape s;
+  if (plan_attention(cu_seqlens_h, B, Hq, Hkv, d, &s) != UP_OK) return 0;
+  return attn_ws_layout(B, Hq, Hkv, d, s.Rp).total;
+}
+
+int up_rope_attention(const void* q, const void* k, const void* v, const int32_t* pos,
+                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B, int Hq,
+                      int Hkv, int d, float scale, float rope_theta, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  AttnShape s;
+  const int st = plan_attention(cu_seqlens_h, B, Hq, Hkv, d, &s);
+  if (st != UP_OK) return st;
+  if (!(rope_theta > 1.f) || std::isinf(rope_theta)) return UP_EINVAL;
+  if (B == 0 || s.R == 0) return UP_OK;
+  if (!q || !k || !v || !pos || !cu_seqlens || !out) return UP_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return UP_EINVAL;
+  const AttnWs L = attn_ws_layout(B, Hq, Hkv, d, s.Rp);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, kWsAlign))
+    return UP_EWORKSPACE;
+  if (!(scale > 0.f) || std::isinf(scale)) scale = (float)(1.0 / std::sqrt((double)d));
+  const float c = (float)((double)scale * 1.4426950408889634);
+  int* err = error_word();
+  if (!err) return UP_EHIP;
+  hipStream_t hs = as_stream(stream);
+  hipError_t e = timed(12, hs, [&] { return launch_attn_plan(cu_seqlens, s, workspace, L, err, hs); });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(13, hs, [&] {
+    return launch_rope_layout(q, k, v, pos, cu_seqlens, s, workspace, L,
+                              std::log2((double)rope_theta), hs);
+  });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(14, hs, [&] { return launch_attention(cu_seqlens, s, workspace, L, c, out, hs); });
+  return e == hipSuccess ? UP_OK : UP_EHIP;
+}
+
+int up_linear(const void* x, const void* w, const void* residual, int64_t R, int K, int N,
+              void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (R < 0 || K <= 0 || N <= 0) return UP_EINVAL;
+  if (R == 0) return UP_OK;
+  if (!x || !w || !y || (workspace_bytes > 0 && !workspace)) return UP_EINVAL;
+  if (workspace && !aligned(workspace, kWsAlign)) return UP_EWORKSPACE;
+  hipStream_t hs = as_stream(stream);
+  int r = 0;
+  const hipError_t e = timed(16, hs, [&] {
+    r = linear_gemm(x, w, residual, R, K, N, y, workspace, workspace_bytes, hs);
+    return hipSuccess;
+  });
+  if (e != hipSuccess || r == -1) return UP_EHIP;
+  return r == -2 ? UP_EUNSUPPORTED : UP_OK;
+}
+
+int up_swiglu(const void* gu, int64_t R, int F, void* a, void* stream) {
+  if (R < 0 || F <= 0) return UP_EINVAL;
+  if (F % 8 != 0) return UP_EUNSUPPORTED;
+  if (R == 0) return UP_OK;
+  if (!gu || !a || !aligned(gu, 16) || !aligned(a, 16)) return UP_EINVAL;
+  hipStream_t hs = as_stream(stream);
+  const hipError_t e = timed(15, hs, [&] { return launch_swiglu(gu, R, F, a, hs); });
+  return e == hipSuccess ? UP_OK : UP_EHIP;
+}
+
+size_t up_swiglu_ffn_workspace(int64_t R, int H, int F) {
+  if (R < 0 || H <= 0 || F <= 0) return 0;
+  return ffn_ws_layout(R, F).total;
+}
+
+int up_swiglu_ffn(const void* x, const void* w_gu, const void* w_down, const void* residual,
+                  int64_t R, int H, int F, void* y, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (R < 0 || H <= 0 || F <= 0) return UP_EINVAL;
+  if (F % 8 != 0) return UP_EUNSUPPORTED;
+  if (R == 0) return UP_OK;
+  if (!x || !w_gu || !w_down || !y) return UP_EINVAL;
+  const FfnWs L = ffn_ws_layout(R, F);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, kWsAlign))
+    return UP_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  int st = up_linear(x, w_gu, nullptr, R, H, 2 * F, ws + L.gu, ws + L.gemm, kGemmWs, stream);
+  if (st != UP_OK) return st;
+  st = up_swiglu(ws + L.gu, R, F, ws + L.a, stream);
+  if (st != UP_OK) return st;
+  return up_linear(ws + L.a, w_down, residual, R, F, H, y, ws + L.gemm, kGemmWs, stream);
 }
 
 int up_device_error(int32_t* code_h, void* stream) {

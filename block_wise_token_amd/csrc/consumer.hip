@@ -1,0 +1,735 @@
+// The layer that runs on the surviving tokens ([UP] "propagation" and "Sparsity
+// Propagation" paragraphs: after a drop every later sub-layer, attention and FFN,
+// computes on the kept tokens only; "scheduler" paragraph: the survivors keep their
+// original positions).
+//
+//   up_attn_plan_kernel    per-request padded offsets and workgroup tiles, checked
+//                          against the host's totals;
+//   up_rope_layout_kernel  rotary embedding of q and k at the carried positions
+//                          (float64 rotation, rounded once to bfloat16) into
+//                          head-major, 64-row padded copies, and v transposed to
+//                          [kv head][d][token] for the P V product;
+//   up_attention_kernel    causal GQA flash attention on the matrix cores;
+//   up_swiglu_kernel       silu(gate) * up for the FFN.
+// The FFN and projection GEMMs are plain bf16 GEMMs and go to hipBLASLt.
+#include "up_dpp.h"
+#include "up_internal.h"
+
+#include <hipblaslt/hipblaslt.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+namespace up {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// Plan: padded offsets po[i] (64-row aligned start of request i in the rotated
+// copies) and workgroup-tile offsets tp[i] (tiles of tok_tile tokens), both as
+// exclusive prefix sums; valid = 1 only when the device cu_seqlens gives the same
+// totals the host sized the launch with.
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void up_attn_plan_kernel(
+    const int32_t* __restrict__ cu, int B, int tok_tile, int64_t R_h, int64_t Rp_h,
+    int64_t tiles_h, WsHeader* __restrict__ hdr, int32_t* __restrict__ po,
+    int32_t* __restrict__ tp, int* __restrict__ err) {
+  constexpr int NWV = kPlanThreads / 64;
+  __shared__ uint64_t wsum[2][NWV];
+  __shared__ int bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  uint64_t carry_p = 0, carry_t = 0;
+  for (int base = 0; base < B; base += kPlanThreads) {
+    const int i = base + tid;
+    uint32_t lp = 0, nt = 0;
+    if (i < B) {
+      const int32_t a = cu[i], b = cu[i + 1];
+      if (b < a || (i == 0 && a != 0)) bad = 1;
+      const uint32_t L = b >= a ? (uint32_t)(b - a) : 0u;
+      lp = (L + 63u) & ~63u;
+      nt = (L + (uint32_t)tok_tile - 1u) / (uint32_t)tok_tile;
+    }
+    const uint64_t sp = wave_scan_u64(lp), sn = wave_scan_u64(nt);   // inclusive
+    if (lane == 63) {
+      wsum[0][wave] = sp;
+      wsum[1][wave] = sn;
+    }
+    __syncthreads();
+    uint64_t op = 0, on = 0, tot_p = 0, tot_n = 0;
+    for (int w = 0; w < NWV; ++w) {
+      if (w < wave) {
+        op += wsum[0][w];
+        on += wsum[1][w];
+      }
+      tot_p += wsum[0][w];
+      tot_n += wsum[1][w];
+    }
+    if (i < B) {
+      po[i] = (int32_t)(carry_p + op + sp - lp);
+      tp[i] = (int32_t)(carry_t + on + sn - nt);
+    }
+    carry_p += tot_p;
+    carry_t += tot_n;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    po[B] = (int32_t)carry_p;
+    tp[B] = (int32_t)carry_t;
+    const bool ok = !bad && (B == 0 || (int64_t)cu[B] == R_h) && (int64_t)carry_p == Rp_h &&
+                    (int64_t)carry_t == tiles_h;
+    hdr->valid = ok ? 1 : 0;
+    if (!ok) atomicOr(err, 1);
+  }
+}
+
+// Request holding padded row / tile x: the largest i in [0, B) with off[i] <= x
+// (empty requests share their successor's offset and are skipped).  off[B] > x.
+__device__ __forceinline__ int request_of(const int32_t* __restrict__ off, int B, int64_t x) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Rotary embedding and layout.  One workgroup per 64 padded rows.  Pair (i, i + d/2)
+// of a head turns by pos * theta^(-2i/d); the angle, its sine and cosine and the
+// rotation are float64, and the result is rounded to bfloat16 once (round to odd
+// into float32, then to nearest even into bfloat16, which is the correct rounding
+// of the float64 value).  Padding rows are zero.
+//   qr [Hq][Rp][d], kr [Hkv][Rp][d]    rotated copies
+//   vt [Hkv][d][Rp]                    v transposed; within each 16-token group
+//                                      token bits 2 and 3 are swapped, so the keys a
+//                                      lane contracts in one MFMA step are adjacent
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t bf16_of_f64(double x) {
+  const float f = __double2float_rz(x);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != x) u |= 1u;   // sticky bit: round to odd
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ double f64_of_bf16(uint16_t b) {
+  return (double)__uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ int swap_bits23(int t) {
+  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void up_rope_layout_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
+    const WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ po, int B, int Hq, int Hkv, int64_t Rp, double log2_theta,
+    uint16_t* __restrict__ qr, uint16_t* __restrict__ kr, uint16_t* __restrict__ vt) {
+  constexpr int PG = D / 8;          // groups of 4 pairs per row
+  constexpr int NU = 64 * PG / 256;  // (row, group) items per thread
+  constexpr int VRS = 2 * D + 4;     // LDS bytes per v row (padded against bank conflicts)
+  __shared__ __attribute__((aligned(16))) uint8_t vs[64 * VRS];
+  if (hdr->valid != 1) return;
+  const int64_t row0p = (int64_t)blockIdx.x * 64;
+  const int i = request_of(po, B, row0p);
+  const int t0 = (int)(row0p - po[i]);
+  const int L = cu[i + 1] - cu[i];
+  const int tid = threadIdx.x;
+
+  // q and k: each thread owns NU (row, 4-pair group) items and their 8 angles.
+  double cs[NU][4], sn[NU][4];
+  int64_t src_row[NU];   // packed token row, -1 for padding
+  int rr_of[NU], pg_of[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int item = tid + 256 * u;
+    const int rr = item / PG, pg = item % PG;
+    rr_of[u] = rr;
+    pg_of[u] = pg;
+    const int t = t0 + rr;
+    src_row[u] = t < L ? (int64_t)cu[i] + t : -1;
+    const double p = src_row[u] >= 0 ? (double)pos[src_row[u]] : 0.0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int ip = 4 * pg + m;
+      const double inv_freq = exp2(-(2.0 * ip / D) * log2_theta);
+      sincos(p * inv_freq, &sn[u][m], &cs[u][m]);
+    }
+  }
+  const int Hs = Hq + Hkv;
+  for (int hs = 0; hs < Hs; ++hs) {
+    const bool isq = hs < Hq;
+    const int hh = isq ? hs : hs - Hq;
+    const int H = isq ? Hq : Hkv;
+    const uint16_t* src = isq ? q : k;
+    uint16_t* dst = (isq ? qr : kr) + ((int64_t)hh * Rp + row0p) * D;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      ushort4 lo = make_ushort4(0, 0, 0, 0), hi = make_ushort4(0, 0, 0, 0);
+      if (src_row[u] >= 0) {
+        const uint16_t* s = src + (src_row[u] * H + hh) * D + 4 * pg_of[u];
+        const ushort4 xl = *reinterpret_cast<const ushort4*>(s);
+        const ushort4 xh = *reinterpret_cast<const ushort4*>(s + D / 2);
+        const uint16_t al[4] = {xl.x, xl.y, xl.z, xl.w};
+        const uint16_t ah[4] = {xh.x, xh.y, xh.z, xh.w};
+        uint16_t rl[4], rh[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const double a = f64_of_bf16(al[m]), b = f64_of_bf16(ah[m]);
+          rl[m] = bf16_of_f64(a * cs[u][m] - b * sn[u][m]);
+          rh[m] = bf16_of_f64(b * cs[u][m] + a * sn[u][m]);
+        }
+        lo = make_ushort4(rl[0], rl[1], rl[2], rl[3]);
+        hi = make_ushort4(rh[0], rh[1], rh[2], rh[3]);
+      }
+      uint16_t* d = dst + (int64_t)rr_of[u] * D + 4 * pg_of[u];
+      *reinterpret_cast<ushort4*>(d) = lo;
+      *reinterpret_cast<ushort4*>(d + D / 2) = hi;
+    }
+  }
+
+  // v: stage 64 rows of one kv head in LDS, then write 16-byte runs of 8 tokens per
+  // d-row in the swapped token order.
+  constexpr int RCH = D / 8;                 // 16-byte chunks per v row
+  constexpr int WCH = D * 8;                 // 16-byte output chunks per head (D rows x 8)
+  for (int g = 0; g < Hkv; ++g) {
+    __syncthreads();
+    for (int c = tid; c < 64 * RCH; c += 256) {
+      const int rr = c / RCH, ch = c % RCH;
+      const int t = t0 + rr;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (t < L) val = *reinterpret_cast<const uint4*>(v + (((int64_t)cu[i] + t) * Hkv + g) * D + 8 * ch);
+      uint32_t* dw = reinterpret_cast<uint32_t*>(vs + rr * VRS + 16 * ch);
+      dw[0] = val.x;
+      dw[1] = val.y;
+      dw[2] = val.z;
+      dw[3] = val.w;
+    }
+    __syncthreads();
+    for (int c = tid; c < WCH; c += 256) {
+      const int dv = c / 8, ch = c % 8;
+      uint16_t e[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int tok = swap_bits23(8 * ch + m);   // token stored at position 8 ch + m
+        e[m] = *reinterpret_cast<const uint16_t*>(vs + tok * VRS + 2 * dv);
+      }
+      uint4 o;
+      o.x = e[0] | ((uint32_t)e[1] << 16);
+      o.y = e[2] | ((uint32_t)e[3] << 16);
+      o.z = e[4] | ((uint32_t)e[5] << 16);
+      o.w = e[6] | ((uint32_t)e[7] << 16);
+      *reinterpret_cast<uint4*>(vt + ((int64_t)g * D + dv) * Rp + row0p + 8 * ch) = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Causal GQA flash attention on the matrix cores.
+//
+// Workgroup = 4 waves (one per SIMD) = HQ query heads x TT 64-token tiles of one kv
+// head (HQ * TT = 4), one wave per (head, tile), 64 query rows per wave in two
+// 32-row tiles held as the B operand in VGPRs.  Keys and values stream through a ring
+// of four LDS stages of 64 tokens (K tile [64][d] and V^T tile [d][64], 16-byte
+// granules XOR-swizzled), copied global -> LDS directly two stages ahead of use.
+//   S^T = K Q^T        (keys as rows: each lane column is one query, so a query's
+//                       softmax statistics are in-lane plus one lane-pair exchange)
+//   O^T += V^T P^T     (P^T straight from the S^T registers, rounded to bf16; the
+//                       keys a lane holds are the ones its V^T operand reads,
+//                       because v was stored in that order)
+// Softmax: one reference Rs per query in log2 units; P = 2^(x - Rs) with x the
+// scaled logit.  Rs moves only when a stage's maximum exceeds it by more than 32 (a
+// wave-uniform branch that rescales O and l), so P <= 2^32 and no per-stage
+// rescale of O is needed.  The stage after the current one has its S^T issued
+// before the current stage's softmax, so its MFMAs overlap that VALU work; a
+// wave's diagonal stage (its last) is masked before its maximum is taken.
+// Workgroups are ordered heaviest tile first; with the kv head in blockIdx.x the
+// workgroups of one kv head share an XCD's L2 when Hkv * quads is a multiple of 8.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t m0) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+}
+
+// vmcnt(N) and lgkmcnt(0), then a workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int D>
+__device__ __forceinline__ int k_swz(int key) {
+  return (D / 8 >= 16) ? (key & 15) : (key & 7);
+}
+__device__ __forceinline__ int v_swz(int row) { return row & 7; }
+
+constexpr float kRebase = 32.f;
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void up_attention_kernel(
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
+    const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
+    const int32_t* __restrict__ tp, int B, int Hq, int Hkv, int HQ, int TT, int64_t Rp,
+    float c, uint16_t* __restrict__ out) {
+  constexpr int NT = 256, NS = 4, UK = 64, QT = 2;
+  constexpr int DS = D / 16;             // MFMA k-steps over the head dimension
+  constexpr int DT = D / 32;             // 32-row tiles of O^T (head dimension)
+  constexpr int KRB = 2 * D;             // K tile row bytes
+  constexpr int KB = UK * KRB;           // K tile bytes
+  constexpr int VB = D * UK * 2;         // V^T tile bytes (rows of 128 bytes)
+  constexpr int SB = KB + VB;            // stage bytes
+  constexpr int KSPT = KB / (NT * 16);   // DMA copies per lane per stage, K
+  constexpr int VSPT = VB / (NT * 16);   // and V^T
+  constexpr int SPT = KSPT + VSPT;
+  static_assert(KB % (NT * 16) == 0 && VB % (NT * 16) == 0, "whole DMA rounds");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
+
+  if (hdr->valid != 1) return;
+  const int gsz = Hq / Hkv, quads = gsz / HQ;
+  const int g = blockIdx.x / quads, quad = blockIdx.x - g * quads;
+  const int f = blockIdx.y;
+  const int i = request_of(tp, B, f);
+  const int L = cu[i + 1] - cu[i];
+  const int nwt = tp[i + 1] - tp[i];
+  const int wt = nwt - 1 - (f - tp[i]);   // heaviest tile first
+  const int ntile = (L + 63) >> 6;        // 64-token tiles of the request
+  const int tile0 = wt * TT;
+  const int nst = min(tile0 + TT, ntile);   // key stages of this workgroup
+  const int64_t pbase = po[i];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5,
+            l32 = lane & 31;
+  const int head = g * gsz + quad * HQ + wave % HQ;
+  const int tw = tile0 + wave / HQ;   // this wave's 64-token tile (its diagonal stage)
+  const bool wact = tw < ntile;
+
+  // Query operand.  The head dimension is contracted in a permuted order shared by
+  // both operands: lane half h, k-step s covers d-elements [h D/2 + 8 s, +8).
+  bf16x8 qreg[QT][DS];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    if (wact) {
+      const uint16_t* src =
+          qr + ((int64_t)head * Rp + pbase + tw * 64 + t * 32 + l32) * D + half * (D / 2);
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qreg[t][s] = *reinterpret_cast<const bf16x8*>(src + s * 8);
+    } else {
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qreg[t][s] = bf16x8{};
+    }
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): only stage copies from here
+
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8*)lds;
+  // DMA: 16 bytes per lane per copy; copy q of the stage lands at LDS bytes
+  // [q NT 16 + 16 tid, +16), and reads the granule that the swizzle puts there.
+  const uint16_t* kbase = kr + ((int64_t)g * Rp + pbase) * D;
+  const uint16_t* vbase = vt + (int64_t)g * D * Rp + pbase;
+  auto issue = [&](int st) {
+    const uint32_t sb = lds_base + (uint32_t)((st & (NS - 1)) * SB);
+    const uint16_t* kst = kbase + (int64_t)st * UK * D;
+#pragma unroll
+    for (int q = 0; q < KSPT; ++q) {
+      const int o = q * NT * 16 + tid * 16;
+      const int key = o / KRB;
+      const int gr = ((o % KRB) / 16) ^ k_swz<D>(key);
+      lds_dma16(kst + key * D + gr * 8,
+                __builtin_amdgcn_readfirstlane(sb + q * NT * 16 + wave * 1024));
+    }
+    const uint16_t* vst = vbase + (int64_t)st * UK;
+#pragma unroll
+    for (int q = 0; q < VSPT; ++q) {
+      const int o = q * NT * 16 + tid * 16;
+      const int row = o / 128;
+      const int gr = ((o % 128) / 16) ^ v_swz(row);
+      lds_dma16(vst + (int64_t)row * Rp + gr * 8,
+                __builtin_amdgcn_readfirstlane(sb + KB + q * NT * 16 + wave * 1024));
+    }
+  };
+
+  // LDS read offsets within a stage for row tile 0; the swizzles depend on l32 only,
+  // so row tile kt of K is kt * 32 rows on and row tile dt of V^T dt * 32 rows on.
+  uint32_t krd[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) krd[s] = l32 * KRB + 16 * ((half * DS + s) ^ k_swz<D>(l32));
+  uint32_t vrd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) vrd[j] = KB + l32 * 128 + 16 * ((2 * j + half) ^ v_swz(l32));
+
+  float Rs[QT], lsum[QT];
+  f32x16 O[DT][QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    lsum[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[dt][t] = f32x16{};
+  }
+  int qtok[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) qtok[t] = tw * 64 + t * 32 + l32;
+
+  // The keys are consumed in halves of 32 (half-step hs = keys [32 hs, 32 hs + 32) of
+  // the request, stage hs / 2, row tile hs % 2 of that stage).
+  // S^T of half-step hs into acc[t].
+  auto s_mfma = [&](int hs, f32x16 (&acc)[QT]) {
+    const int kt = hs & 1;
+    const uint8_t* sl = lds + ((hs >> 1) & (NS - 1)) * SB;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sl + kt * 32 * KRB + krd[s]);
+#pragma unroll
+      for (int t = 0; t < QT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][s], s == 0 ? f32x16{} : acc[t],
+                                                         0, 0, 0);
+    }
+  };
+  // Causal mask of a half-step in the diagonal stage (keys past the query -> -inf).
+  auto mask = [&](int hs, f32x16 (&acc)[QT]) {
+#pragma unroll
+    for (int t = 0; t < QT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        // 32x32 result layout: register e of lane l is row 8(e/4) + 4(l/32) + e%4
+        // (the key) and column l%32 (the query).
+        const int key = hs * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (key > qtok[t]) acc[t][e] = kNegInf;
+      }
+  };
+  // Half-step maximum per query (log2 units) and, when it passes Rs + 32 anywhere in
+  // the wave, a new reference with O and l rescaled.
+  auto rebase = [&](f32x16 (&acc)[QT], bool init) {
+    float mx[QT];
+    bool need = init;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      float m0 = kNegInf, m1 = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        m0 = fmaxf(m0, acc[t][e]);
+        m1 = fmaxf(m1, acc[t][e + 1]);
+      }
+      mx[t] = pair_max(fmaxf(m0, m1)) * c;
+      if (!init) need |= mx[t] > Rs[t] + kRebase;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        if (init) {
+          Rs[t] = mx[t];
+          continue;
+        }
+        const float rn = fmaxf(Rs[t], mx[t]);
+        const float sc = __builtin_amdgcn_exp2f(Rs[t] - rn);
+        lsum[t] *= sc;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[dt][t] *= sc;
+        Rs[t] = rn;
+      }
+    }
+  };
+  // Softmax of half-step hs (S^T in acc) and O^T += V^T P^T over its 32 keys.
+  auto pv = [&](int hs, const f32x16 (&acc)[QT]) {
+    bf16x8 pb[2][QT];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      f32x16 p;
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(acc[t][e], c, -Rs[t]));
+        p[e + 1] = __builtin_amdgcn_exp2f(fmaf(acc[t][e + 1], c, -Rs[t]));
+        s0 += p[e];
+        s1 += p[e + 1];
+      }
+      lsum[t] += s0 + s1;
+      pb[0][t] = __builtin_convertvector(p.lo, bf16x8);
+      pb[1][t] = __builtin_convertvector(p.hi, bf16x8);
+    }
+    const int kt = hs & 1;
+    const uint8_t* sl = lds + ((hs >> 1) & (NS - 1)) * SB;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sl + dt * 32 * 128 + vrd[2 * kt + jj]);
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+          O[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[jj][t], O[dt][t], 0, 0, 0);
+      }
+  };
+
+  // Ring: stages st+1 and st+2 in flight while st is consumed; stage st+1 is waited
+  // for (and published by a barrier) before the second half of stage st, whose body
+  // issues the S^T of stage st+1's first half.
+  auto sync_for = [&](int st) {
+    if (st + 1 >= nst) return;
+    if (st + 2 < nst) wait_barrier<SPT>();
+    else wait_barrier<0>();
+    if (st + 3 < nst) issue(st + 3);
+  };
+
+  issue(0);
+  if (nst > 1) issue(1);
+  if (nst > 2) issue(2);
+  if (nst > 2) wait_barrier<2 * SPT>();
+  else if (nst > 1) wait_barrier<SPT>();
+  else wait_barrier<0>();
+
+  const int last_hs = 2 * tw + 1;   // the wave's last half-step (end of its diagonal stage)
+  f32x16 accA[QT], accB[QT];
+  if (wact) {
+    s_mfma(0, accA);
+    if (tw == 0) mask(0, accA);
+    rebase(accA, true);
+  }
+  // One half-step: cur holds S^T of half-step hs, nxt receives half-step hs+1's.
+  auto body = [&](int hs, f32x16 (&cur)[QT], f32x16 (&nxt)[QT]) {
+    if (!wact || hs > last_hs) return;
+    if (hs + 1 < 2 * tw) {          // next half-step is before the diagonal stage
+      s_mfma(hs + 1, nxt);
+      pv(hs, cur);
+      rebase(nxt, false);
+    } else if (hs + 1 <= last_hs) {   // next half-step is in the diagonal stage
+      s_mfma(hs + 1, nxt);
+      pv(hs, cur);
+      mask(hs + 1, nxt);
+      rebase(nxt, false);
+    } else {
+      pv(hs, cur);
+    }
+  };
+  for (int st = 0; st < nst; ++st) {
+    body(2 * st, accA, accB);
+    sync_for(st);
+    body(2 * st + 1, accB, accA);
+  }
+
+  if (!wact) return;
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const float inv = 1.f / pair_sum(lsum[t]);
+    if (qtok[t] >= L) continue;
+    uint16_t* dst = out + (((int64_t)cu[i] + qtok[t]) * Hq + head) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int eg = 0; eg < 4; ++eg) {
+        const int dv = dt * 32 + 8 * eg + 4 * half;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 o4 = {O[dt][t][4 * eg] * inv, O[dt][t][4 * eg + 1] * inv,
+                          O[dt][t][4 * eg + 2] * inv, O[dt][t][4 * eg + 3] * inv};
+        *reinterpret_cast<bf16x4*>(dst + dv) = __builtin_convertvector(o4, bf16x4);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU gate: a[r][j] = silu(gu[r][j]) * gu[r][F + j] in float32, rounded to
+// bfloat16.  Eight columns per thread, grid-stride.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void up_swiglu_kernel(const uint16_t* __restrict__ gu,
+                                                        int64_t R, int F,
+                                                        uint16_t* __restrict__ a) {
+  const int64_t per_row = F / 8;
+  const int64_t n = R * per_row;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
+       x += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = x / per_row, c8 = (x - r * per_row) * 8;
+    const bf16x8 gv = *reinterpret_cast<const bf16x8*>(gu + r * 2 * F + c8);
+    const bf16x8 uv = *reinterpret_cast<const bf16x8*>(gu + r * 2 * F + F + c8);
+    const f32x8 gf = __builtin_convertvector(gv, f32x8);
+    const f32x8 uf = __builtin_convertvector(uv, f32x8);
+    f32x8 o;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) o[m] = gf[m] / (1.f + __expf(-gf[m])) * uf[m];
+    *reinterpret_cast<bf16x8*>(a + r * F + c8) = __builtin_convertvector(o, bf16x8);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp) {
+  AttnWs w;
+  size_t o = 0;
+  w.hdr = o;
+  o += align_up(sizeof(WsHeader));
+  w.po = o;
+  o += align_up(sizeof(int32_t) * (size_t)(B + 1));
+  w.tp = o;
+  o += align_up(sizeof(int32_t) * (size_t)(B + 1));
+  w.qr = o;
+  o += align_up((size_t)Hq * Rp * d * 2);
+  w.kr = o;
+  o += align_up((size_t)Hkv * Rp * d * 2);
+  w.vt = o;
+  o += align_up((size_t)Hkv * Rp * d * 2);
+  w.total = o;
+  return w;
+}
+
+hipError_t launch_attn_plan(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
+                            int* err, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  hipLaunchKernelGGL(up_attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, cu, s.B, 64 * s.TT,
+                     s.R, s.Rp, s.tiles, reinterpret_cast<WsHeader*>(w + L.hdr),
+                     reinterpret_cast<int32_t*>(w + L.po), reinterpret_cast<int32_t*>(w + L.tp),
+                     err);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_layout(const void* q, const void* k, const void* v, const int32_t* pos,
+                              const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
+                              double log2_theta, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  const auto* hdr = reinterpret_cast<const WsHeader*>(w + L.hdr);
+  const auto* po = reinterpret_cast<const int32_t*>(w + L.po);
+  auto* qr = reinterpret_cast<uint16_t*>(w + L.qr);
+  auto* kr = reinterpret_cast<uint16_t*>(w + L.kr);
+  auto* vt = reinterpret_cast<uint16_t*>(w + L.vt);
+  const dim3 grid((unsigned)(s.Rp / 64));
+  auto kq = static_cast<const uint16_t*>(q);
+  auto kk = static_cast<const uint16_t*>(k);
+  auto kv = static_cast<const uint16_t*>(v);
+  if (s.d == 64)
+    hipLaunchKernelGGL(up_rope_layout_kernel<64>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr, cu,
+                       po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
+  else
+    hipLaunchKernelGGL(up_rope_layout_kernel<128>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr,
+                       cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
+                            float c, void* out, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  const auto* hdr = reinterpret_cast<const WsHeader*>(w + L.hdr);
+  const auto* po = reinterpret_cast<const int32_t*>(w + L.po);
+  const auto* tp = reinterpret_cast<const int32_t*>(w + L.tp);
+  const auto* qr = reinterpret_cast<const uint16_t*>(w + L.qr);
+  const auto* kr = reinterpret_cast<const uint16_t*>(w + L.kr);
+  const auto* vt = reinterpret_cast<const uint16_t*>(w + L.vt);
+  const dim3 grid((unsigned)(s.Hkv * (s.Hq / s.Hkv / s.HQ)), (unsigned)s.tiles);
+  auto o = static_cast<uint16_t*>(out);
+  if (s.d == 64)
+    hipLaunchKernelGGL(up_attention_kernel<64>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
+                       tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+  else
+    hipLaunchKernelGGL(up_attention_kernel<128>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
+                       tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const void* gu, int64_t R, int F, void* a, hipStream_t st) {
+  const int64_t n = R * (F / 8);
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256 * 64);
+  hipLaunchKernelGGL(up_swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(gu), R, F, static_cast<uint16_t*>(a));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// hipBLASLt GEMM: y[R][N] = x[R][K] w[N][K]^T (+ residual[R][N]), bf16 in and out,
+// float32 accumulation.  In hipBLASLt's column-major terms y^T = op_T(w) x^T.  One
+// handle per device; descriptors and the heuristic's first algorithm are cached per
+// (device, R, K, N, residual, workspace bytes).
+// ---------------------------------------------------------------------------
+namespace {
+struct GemmPlan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+  hipblasLtMatmulAlgo_t algo;
+  size_t ws_need = 0;
+};
+std::mutex g_blas_mu;
+hipblasLtHandle_t g_blas[64] = {};
+std::map<std::tuple<int, int64_t, int, int, bool, size_t>, GemmPlan> g_plans;
+}  // namespace
+
+int linear_gemm(const void* x, const void* w, const void* residual, int64_t R, int K, int N,
+                void* y, void* ws, size_t ws_bytes, hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  std::lock_guard<std::mutex> lk(g_blas_mu);
+  if (!g_blas[dev] && hipblasLtCreate(&g_blas[dev]) != HIPBLAS_STATUS_SUCCESS) {
+    g_blas[dev] = nullptr;
+    return -1;
+  }
+  const bool res = residual != nullptr;
+  const auto key = std::make_tuple(dev, R, K, N, res, ws_bytes);
+  auto it = g_plans.find(key);
+  if (it == g_plans.end()) {
+    GemmPlan p;
+    bool ok = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) ==
+              HIPBLAS_STATUS_SUCCESS;
+    const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+    ok = ok && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta,
+                                               sizeof(ta)) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb,
+                                               sizeof(tb)) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, K, R, K) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_16BF, N, R, N) == HIPBLAS_STATUS_SUCCESS;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS;
+    uint64_t wsmax = ws_bytes;
+    ok = ok && hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
+                                                     &wsmax, sizeof(wsmax)) ==
+                   HIPBLAS_STATUS_SUCCESS;
+    hipblasLtMatmulHeuristicResult_t hr[1];
+    int n = 0;
+    ok = ok && hipblasLtMatmulAlgoGetHeuristic(g_blas[dev], p.desc, p.la, p.lb, p.lc, p.lc, pref,
+                                               1, hr, &n) == HIPBLAS_STATUS_SUCCESS &&
+         n > 0;
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    if (!ok) {
+      if (p.la) hipblasLtMatrixLayoutDestroy(p.la);
+      if (p.lb) hipblasLtMatrixLayoutDestroy(p.lb);
+      if (p.lc) hipblasLtMatrixLayoutDestroy(p.lc);
+      if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
+      return -2;
+    }
+    p.algo = hr[0].algo;
+    p.ws_need = hr[0].workspaceSize;
+    it = g_plans.emplace(key, p).first;
+  }
+  const GemmPlan& p = it->second;
+  const float alpha = 1.f, beta = res ? 1.f : 0.f;
+  const hipblasStatus_t s =
+      hipblasLtMatmul(g_blas[dev], p.desc, &alpha, w, p.la, x, p.lb, &beta, res ? residual : y,
+                      p.lc, y, p.lc, &p.algo, p.ws_need ? ws : nullptr, p.ws_need, st);
+  return s == HIPBLAS_STATUS_SUCCESS ? 0 : -1;
+}
+
+}  // namespace up

@@ -132,4 +132,27 @@ hipError_t launch_compose(const int32_t* prev, int prev_len, const int32_t* idx,
                           const int32_t* count, int capacity, int32_t* out, int* err,
                           hipStream_t st);
 
+// Layer on the surviving tokens (consumer.hip).
+struct AttnShape {
+  int B, Hq, Hkv, d;
+  int HQ, TT;       // query heads and 64-token tiles per attention workgroup (HQ * TT = 4)
+  int64_t R, Rp;    // rows; padded rows (every request rounded up to 64)
+  int64_t tiles;    // attention workgroup tiles of 64 * TT tokens
+};
+struct AttnWs {
+  size_t hdr, po, tp, qr, kr, vt, total;
+};
+AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp);
+hipError_t launch_attn_plan(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
+                            int* err, hipStream_t st);
+hipError_t launch_rope_layout(const void* q, const void* k, const void* v, const int32_t* pos,
+                              const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
+                              double log2_theta, hipStream_t st);
+hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
+                            float c, void* out, hipStream_t st);
+hipError_t launch_swiglu(const void* gu, int64_t R, int F, void* a, hipStream_t st);
+// y = x w^T (+ residual) through hipBLASLt; 0 on success, -1 library error, -2 no algorithm.
+int linear_gemm(const void* x, const void* w, const void* residual, int64_t R, int K, int N,
+                void* y, void* ws, size_t ws_bytes, hipStream_t st);
+
 }  // namespace up

@@ -6,6 +6,8 @@
  *   2. up_topp_select    : Top-p cut over the sorted block scores
  *   3. up_expand_compact : kept blocks -> token indices; gather hidden rows and positions
  *   4. up_compose_drops  : map survivors back to original indices across layers
+ * and the layer that then runs on the survivors (5: up_rope_attention, up_linear,
+ * up_swiglu, up_swiglu_ffn).
  *
  * Pages cited (by title and paragraph / section):
  *   [UP]  "UniPrefill: 블록 단위 동적 희소화를 통한 범용적 롱 컨텍스트 프리필 가속화"
@@ -17,8 +19,9 @@
  * Conventions shared by every call
  *  - Pointers are DEVICE pointers unless their name ends in _h (host memory).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
- *    stream), never synchronises, never allocates device memory, and returns an
- *    up_status (0 = UP_OK, negative = error).  Arguments are validated on the
+ *    stream), never synchronises, never allocates device memory (except that the
+ *    first up_linear / up_swiglu_ffn call on a device lets hipBLASLt create its
+ *    handle), and returns an up_status (0 = UP_OK, negative = error).  Arguments are validated on the
  *    host before anything is launched; on error nothing is launched.
  *  - The caller owns every buffer.  Outputs are sized for the worst case
  *    (everything kept); the number of valid rows lives on the device, in
@@ -217,6 +220,66 @@ int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
                      const int32_t* count, int capacity, int32_t* orig_out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * 5. The layer on the surviving tokens  ([UP] "propagation" paragraph: after a
+ *    drop every later layer computes on the survivors only, so its GEMMs shrink
+ *    as well as its attention; [UP] "Sparsity Propagation" paragraph: FFN work
+ *    falls from O(N) to O(rho N) and attention shrinks with the kept fraction;
+ *    [UP] "scheduler" paragraph: survivors keep their original positions)
+ *
+ * These calls take the compacted rows of up_expand_compact (R = cu_seqlens_out[B]
+ * rows, request i owning [cu_seqlens_out[i], cu_seqlens_out[i+1])) and pos_out.
+ * ------------------------------------------------------------------------- */
+
+/* Rotary embedding at the carried positions, then causal GQA attention per request:
+ *   q' = rope(q, pos), k' = rope(k, pos)   element j pairs with element j + d/2 and
+ *        turns by pos * rope_theta^(-2j/d); computed in float64, rounded once to bf16
+ *   out[r, h] = sum_{r' <= r, same request} softmax_r'(scale q'[r, h] . k'[r', h / g]) v[r', h / g]
+ *   with g = Hq / Hkv.  Survivors are in ascending original order, so "r' <= r" is
+ *   causality over the original positions.
+ * q   : bf16 [R, Hq, d];  k, v : bf16 [R, Hkv, d];  out : bf16 [R, Hq, d] (16-byte aligned).
+ * pos : int32 [R] (pos_out: original positions).
+ * cu_seqlens / cu_seqlens_h : int32 [B+1] row offsets (cu_seqlens_out and its host copy).
+ * d in {64, 128} (UP_EUNSUPPORTED otherwise); scale <= 0 means 1/sqrt(d);
+ * rope_theta > 1 (e.g. 500000 for the Llama-3.1 shape).
+ * Probabilities enter the P.V product as bf16; softmax statistics and accumulation
+ * are float32.  Limits: sum of ceil(L_i / 64) padded rows < 2^31 and at most 65535
+ * workgroup tiles (about 4M rows at Hq / Hkv = 4).
+ * workspace : at least up_rope_attention_workspace(...) bytes, 256-byte aligned
+ *             (rotated q and k, transposed v, plan).
+ * A device cu_seqlens whose totals (rows, padded rows, workgroup tiles) differ from
+ * those of cu_seqlens_h raises error bit 1 and nothing is written. */
+size_t up_rope_attention_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d);
+
+int up_rope_attention(const void* q, const void* k, const void* v, const int32_t* pos,
+                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B, int Hq,
+                      int Hkv, int d, float scale, float rope_theta, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* y[R, N] = x[R, K] . w[N, K]^T (+ residual[R, N] when not NULL); bf16 in and out,
+ * float32 accumulation, through hipBLASLt (a plain GEMM).  residual may alias y.
+ * workspace may be NULL with workspace_bytes = 0; otherwise 256-byte aligned and
+ * offered to hipBLASLt.  The first call for a shape on a device creates the
+ * hipBLASLt handle and picks the algorithm (host work, cached); later calls only
+ * launch.  UP_EUNSUPPORTED if hipBLASLt has no algorithm for the shape. */
+int up_linear(const void* x, const void* w, const void* residual, int64_t R, int K, int N,
+              void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* SwiGLU gate: a[r, j] = silu(gu[r, j]) * gu[r, F + j], float32 math, bf16 result.
+ * gu : bf16 [R, 2F] (gate columns first);  a : bf16 [R, F];  F % 8 == 0. */
+int up_swiglu(const void* gu, int64_t R, int F, void* a, void* stream);
+
+/* SwiGLU FFN on R rows: y = swiglu(x . w_gu^T) . w_down^T (+ residual).
+ * x : bf16 [R, H];  w_gu : bf16 [2F, H] (gate rows first);  w_down : bf16 [H, F];
+ * residual : bf16 [R, H] or NULL (may alias y);  y : bf16 [R, H];  F % 8 == 0.
+ * The intermediate x . w_gu^T and the gated activation are stored as bf16 in the
+ * workspace: at least up_swiglu_ffn_workspace(R, H, F) bytes, 256-byte aligned. */
+size_t up_swiglu_ffn_workspace(int64_t R, int H, int F);
+
+int up_swiglu_ffn(const void* x, const void* w_gu, const void* w_down, const void* residual,
+                  int64_t R, int H, int F, void* y, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* ---------------------------------------------------------------------------
  * Diagnostics (not on the hot path)
  * ------------------------------------------------------------------------- */
 
@@ -231,7 +294,9 @@ int up_device_error(int32_t* code_h, void* stream);
  * library launches; up_profile_read() synchronises the recorded events and
  * returns, for kernel family `which` (0 score partials, 1 row statistics,
  * 2 block masses, 3 normalise, 4 select, 5 select finalise, 6 block
- * destinations, 7 gather, 8 compose, 9 plan), the number of launches and their
+ * destinations, 7 gather, 8 compose, 9 plan, 10 given-lse score partials,
+ * 11 given-lse finalise, 12 attention plan, 13 rotary layout, 14 attention,
+ * 15 SwiGLU gate, 16 hipBLASLt GEMM), the number of launches and their
  * summed duration in milliseconds; up_profile_reset() forgets them.
  * up_profile_enable(0) stops recording.  Not thread safe. */
 int up_profile_enable(int on);

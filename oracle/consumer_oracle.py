@@ -167,3 +167,35 @@ def ffn(x_bits, w_gu_bits, w_down_bits, F: int, residual_bits=None):
     if residual_bits is not None:
         y = y + bits_to_f64(residual_bits)
     return y, gu, a
+
+
+def rope_attention_rows(q_bits, k_bits, v_bits, pos, cu_seqlens, Hq: int, Hkv: int, d: int,
+                        scale: float, theta: float, rows) -> np.ndarray:
+    """The same attention as ``rope_attention`` for the listed rows only
+    (out [len(rows), Hq, d] float64): each row reads its request's keys up to itself.
+    Keys are rotated once per request, up to its last listed row."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    g = Hq // Hkv
+    out = np.zeros((len(rows), Hq, d))
+    q = q_bits.reshape(-1, Hq, d)
+    k = k_bits.reshape(-1, Hkv, d)
+    v = v_bits.reshape(-1, Hkv, d)
+    req = np.searchsorted(cu, rows, side="right") - 1
+    for i in np.unique(req):
+        a = int(cu[i])
+        sel = np.nonzero(req == i)[0]
+        last = int(rows[sel].max())
+        kr = rotate_bf16(k[a:last + 1], pos[a:last + 1], theta)      # [n_keys, Hkv, d]
+        vf = bits_to_f64(v[a:last + 1])
+        for n in sel:
+            r = int(rows[n])
+            qr = rotate_bf16(q[r:r + 1], pos[r:r + 1], theta)[0]       # [Hq, d]
+            nk = r - a + 1
+            for h in range(Hq):
+                s_ = (kr[:nk, h // g, :] @ qr[h]) * float(scale)
+                s_ = s_ - s_.max()
+                p = np.exp(s_)
+                p /= p.sum()
+                out[n, h] = p @ vf[:nk, h // g, :]
+    return out

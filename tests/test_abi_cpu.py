@@ -196,3 +196,59 @@ def test_block_scores_paged_rejects_bad_arguments(L):
     assert call(table=None) == UP_EINVAL
     assert call(npages=0) == UP_EINVAL
     assert call(npages=-1) == UP_EINVAL
+
+
+def test_rope_attention_workspace_and_arguments(L):
+    f = L.up_rope_attention_workspace
+    f.restype = ctypes.c_size_t
+    cu = _cu([100, 0, 64, 1])
+    Rp = 128 + 0 + 64 + 64
+    ws = f(_p(cu), 4, 8, 2, 128)
+    # rotated q (Hq) and k (Hkv), transposed v (Hkv), all over 64-row padded requests
+    assert ws >= (8 + 2 + 2) * Rp * 128 * 2 and ws % 256 == 0
+    assert f(_p(cu), 4, 8, 2, 256) == 0      # d unsupported
+    assert f(_p(cu), 4, 8, 3, 128) == 0      # Hq % Hkv
+    bad = _cu([5, 3])
+    bad[1] = 9; bad[2] = 4                   # decreasing offsets
+    assert f(_p(bad), 2, 8, 2, 128) == 0
+    a = L.up_rope_attention
+    a.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_float] * 2 + \
+                 [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    dummy = ctypes.c_void_p(4096)
+    args = lambda **kw: dict(dict(q=dummy, k=dummy, v=dummy, pos=dummy, cu=dummy, cu_h=_p(cu),
+                                  B=4, Hq=8, Hkv=2, d=128, scale=0.0, theta=500000.0, out=dummy,
+                                  ws=None, wsb=0, st=None), **kw)
+    call = lambda kw: a(*args(**kw).values())
+    assert call(dict(d=96)) == UP_EUNSUPPORTED
+    assert call(dict(theta=1.0)) == UP_EINVAL
+    assert call(dict(q=None)) == UP_EINVAL
+    assert call(dict(out=ctypes.c_void_p(4098))) == UP_EINVAL     # misaligned
+    assert call(dict()) == UP_EWORKSPACE                         # no workspace
+    assert call(dict(ws=ctypes.c_void_p(4096), wsb=ws - 1)) == UP_EWORKSPACE
+    assert call(dict(B=0, cu_h=_p(np.zeros(1, np.int32)))) == UP_OK   # nothing to do
+
+
+def test_linear_swiglu_ffn_reject_bad_arguments(L):
+    L.up_linear.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                            ctypes.c_size_t, ctypes.c_void_p]
+    d = ctypes.c_void_p(4096)
+    assert L.up_linear(d, d, None, -1, 16, 16, d, None, 0, None) == UP_EINVAL
+    assert L.up_linear(d, d, None, 8, 0, 16, d, None, 0, None) == UP_EINVAL
+    assert L.up_linear(None, d, None, 8, 16, 16, d, None, 0, None) == UP_EINVAL
+    assert L.up_linear(d, d, None, 8, 16, 16, d, None, 64, None) == UP_EINVAL   # bytes, no ptr
+    assert L.up_linear(d, d, None, 8, 16, 16, d, ctypes.c_void_p(4100), 64, None) == UP_EWORKSPACE
+    assert L.up_linear(d, d, None, 0, 16, 16, d, None, 0, None) == UP_OK
+    L.up_swiglu.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                            ctypes.c_void_p]
+    assert L.up_swiglu(d, 4, 12, d, None) == UP_EUNSUPPORTED                    # F % 8
+    assert L.up_swiglu(None, 4, 16, d, None) == UP_EINVAL
+    L.up_swiglu_ffn_workspace.restype = ctypes.c_size_t
+    L.up_swiglu_ffn_workspace.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+    w = L.up_swiglu_ffn_workspace(1000, 4096, 14336)
+    assert w >= 1000 * 3 * 14336 * 2 and w % 256 == 0
+    L.up_swiglu_ffn.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                        ctypes.c_void_p, ctypes.c_void_p,
+                                                        ctypes.c_size_t, ctypes.c_void_p]
+    assert L.up_swiglu_ffn(d, d, d, None, 1000, 4096, 14336, d, d, w - 1, None) == UP_EWORKSPACE
+    assert L.up_swiglu_ffn(d, d, d, None, 1000, 4096, 14330, d, d, w, None) == UP_EUNSUPPORTED

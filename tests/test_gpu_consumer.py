@@ -1,0 +1,182 @@
+"""GPU parity of the layer on the surviving tokens against the consumer oracle.
+
+Tolerances, derived from the arithmetic:
+  * attention: the rotated q and k are the same bfloat16 values on both sides; the
+    GPU rounds each probability to bfloat16 for the P.V product (relative error
+    <= 2^-9, so an output row moves by <= 2^-9 max|v|) and rounds the output to
+    bfloat16 (<= 2^-9 relative); logits and statistics in float32 add ~1e-5.  Bar:
+    |gpu - oracle| <= 2^-8 |oracle| + 2^-8 max|v| (per request and kv head);
+  * GEMM: float32 accumulation and one bfloat16 rounding of the result:
+    |gpu - oracle| <= 2^-8 |oracle| + 1e-5 sum_k |x_k w_k|;
+  * SwiGLU gate: float32 math and one bfloat16 rounding: <= 2^-8 relative to the
+    exact value (plus 1e-30);
+  * FFN: as the GEMM, with the gated activation allowed to move by 2^-7 relative
+    per element (its bfloat16 rounding and that of x.w_gu^T before it):
+    |gpu - oracle| <= 2^-8 |oracle| + 2^-7 sum_j |a_j w_j|.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_wise_token_amd as up
+from oracle import consumer_oracle as C
+from tests.gpu_helpers import bf16_dev, i32_dev, say
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+CASES = [
+    # lengths, Hq, Hkv, d, q_sigma
+    ([200], 8, 2, 128, 1.0),
+    ([64], 4, 1, 64, 1.0),                     # Hq / Hkv = 4, d = 64
+    ([1], 8, 2, 128, 1.0),                     # one row
+    ([300, 0, 65, 129, 1], 8, 2, 128, 1.0),    # varlen, empty and ragged requests
+    ([257], 8, 8, 128, 1.0),                   # one query head per kv head: 4 tiles per workgroup
+    ([190], 8, 4, 64, 1.0),                    # two query heads per kv head: 2 tiles per workgroup
+    ([150], 16, 2, 128, 1.0),                  # eight per kv head: two workgroups per kv head
+    ([700], 8, 2, 128, 12.0),                  # large logits: the reference rebases often
+    ([513], 4, 2, 64, 30.0),                   # very large logits, nearly one-hot rows
+]
+
+
+def _attention_case(lengths, Hq, Hkv, d, sigma, seed, theta=500000.0):
+    q, k, v, pos, cu = synth.gen_consumer_attention(lengths, Hq, Hkv, d, seed, q_sigma=sigma)
+    R = int(cu[-1])
+    scale = 1.0 / math.sqrt(d)
+    out = up.rope_attention(bf16_dev(q).view(R, Hq, d), bf16_dev(k).view(R, Hkv, d),
+                            bf16_dev(v).view(R, Hkv, d), i32_dev(pos), i32_dev(cu), cu,
+                            scale=scale, rope_theta=theta)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    return q, k, v, pos, cu, scale, _to_f64(out)
+
+
+def _check_attention(got, ref, vmax_rows, Hq, Hkv):
+    g = Hq // Hkv
+    vm = np.repeat(vmax_rows, g, axis=1)[:, :, None]          # [R, Hq, 1]
+    tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -8 * vm
+    err = np.abs(got - ref)
+    bad = err > tol
+    assert not bad.any(), (f"{int(bad.sum())} elements over the bar; worst excess "
+                           f"{float((err - tol).max()):.3e}")
+    return float((err / np.maximum(tol, 1e-30)).max())
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_rope_attention_matches_oracle(case):
+    lengths, Hq, Hkv, d, sigma = case
+    say(f"[case] rope_attention {case}")
+    q, k, v, pos, cu, scale, got = _attention_case(lengths, Hq, Hkv, d, sigma, seed=len(lengths) + d)
+    ref = C.rope_attention(q, k, v, pos, cu, Hq, Hkv, d, scale, 500000.0)
+    worst = _check_attention(got, ref, C.attention_vmax(v, cu, Hkv, d), Hq, Hkv)
+    say(f"[ok] {case}: worst error / bar {worst:.3f}")
+
+
+def test_rope_attention_uses_the_carried_positions():
+    """Renumbering the survivors 0..R-1 changes the output; the GPU follows the carried
+    positions (checked against the oracle at both)."""
+    lengths, Hq, Hkv, d = [256], 8, 2, 128
+    q, k, v, pos, cu = synth.gen_consumer_attention(lengths, Hq, Hkv, d, 5)
+    assert np.any(np.diff(pos) > 1)
+    R = int(cu[-1])
+    outs = {}
+    for name, p in (("carried", pos), ("renumbered", np.arange(R, dtype=np.int32))):
+        o = up.rope_attention(bf16_dev(q).view(R, Hq, d), bf16_dev(k).view(R, Hkv, d),
+                              bf16_dev(v).view(R, Hkv, d), i32_dev(p), i32_dev(cu), cu)
+        torch.cuda.synchronize()
+        ref = C.rope_attention(q, k, v, p, cu, Hq, Hkv, d, 1 / math.sqrt(d), 500000.0)
+        _check_attention(_to_f64(o), ref, C.attention_vmax(v, cu, Hkv, d), Hq, Hkv)
+        outs[name] = _to_f64(o)
+    assert np.abs(outs["carried"] - outs["renumbered"]).max() > 1e-2
+
+
+def test_rope_attention_is_deterministic_and_rejects_bad_cu():
+    lengths, Hq, Hkv, d = [1000, 37], 8, 2, 128
+    q, k, v, pos, cu = synth.gen_consumer_attention(lengths, Hq, Hkv, d, 9)
+    R = int(cu[-1])
+    args = (bf16_dev(q).view(R, Hq, d), bf16_dev(k).view(R, Hkv, d), bf16_dev(v).view(R, Hkv, d),
+            i32_dev(pos))
+    a = up.rope_attention(*args, i32_dev(cu), cu)
+    b = up.rope_attention(*args, i32_dev(cu), cu)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    # a device cu_seqlens whose totals disagree with the host copy (18 workgroup tiles
+    # and 1152 padded rows instead of 17 and 1088): nothing written, bit 1 raised
+    bad = cu.copy()
+    bad[1] = 970
+    pad = lambda c: sum(-(-int(L) // 64) * 64 for L in np.diff(c))
+    assert pad(bad) != pad(cu)
+    out = torch.full_like(a, 7.0)
+    up.rope_attention(*args, i32_dev(bad), cu, out=out)
+    torch.cuda.synchronize()
+    assert up.device_error() == 1
+    assert bool((out == 7.0).all())
+
+
+@pytest.mark.timeout(900)
+def test_rope_attention_at_128k_sampled_rows():
+    """The Llama-3.1-8B shape at 129600 survivors (p = 0.99 of 128K): sampled rows of the
+    GPU output against the oracle computed for those rows alone."""
+    R, Hq, Hkv, d = 129600, 32, 8, 128
+    say("[setup] generating 129600 survivors, Hq=32, Hkv=8, d=128")
+    q, k, v, pos, cu = synth.gen_consumer_attention([R], Hq, Hkv, d, 2026)
+    out = up.rope_attention(bf16_dev(q).view(R, Hq, d), bf16_dev(k).view(R, Hkv, d),
+                            bf16_dev(v).view(R, Hkv, d), i32_dev(pos), i32_dev(cu), cu)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    rows = [0, 1, 63, 64, 4095, 65536, 100003, R - 65, R - 2, R - 1]
+    got = out[rows].float().cpu().numpy().astype(np.float64)
+    say("[setup] oracle on sampled rows")
+    ref = C.rope_attention_rows(q, k, v, pos, cu, Hq, Hkv, d, 1 / math.sqrt(d), 500000.0, rows)
+    vmax = np.abs(C.bits_to_f64(v).reshape(R, Hkv, d)).max(axis=(0, 2))[None, :]
+    worst = _check_attention(got, ref, np.repeat(vmax, len(rows), axis=0), Hq, Hkv)
+    say(f"[ok] 128K sampled rows: worst error / bar {worst:.3f}")
+
+
+@pytest.mark.parametrize("R,K,N,res", [(300, 256, 512, False), (1, 128, 64, True),
+                                       (4099, 4096, 1024, True)])
+def test_linear_matches_oracle(R, K, N, res):
+    say(f"[case] linear R={R} K={K} N={N} residual={res}")
+    rng = np.random.default_rng(R + K)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((R, K)).astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32))
+    r = synth.f32_to_bf16_bits(rng.standard_normal((R, N)).astype(np.float32)) if res else None
+    y = up.linear(bf16_dev(x).view(R, K), bf16_dev(w).view(N, K),
+                  residual=None if r is None else bf16_dev(r).view(R, N))
+    torch.cuda.synchronize()
+    ref = C.linear(x, w) + (0 if r is None else C.bits_to_f64(r))
+    mag = np.abs(C.bits_to_f64(x)) @ np.abs(C.bits_to_f64(w)).T
+    err = np.abs(_to_f64(y) - ref)
+    assert (err <= 2.0 ** -8 * np.abs(ref) + 1e-5 * mag + 1e-30).all()
+
+
+def test_swiglu_matches_oracle():
+    rng = np.random.default_rng(3)
+    R, F = 517, 1032
+    gu = synth.f32_to_bf16_bits((rng.standard_normal((R, 2 * F)) * 3).astype(np.float32))
+    a = up.swiglu(bf16_dev(gu).view(R, 2 * F))
+    torch.cuda.synchronize()
+    g = C.bits_to_f64(gu)
+    exact = C.silu(g[:, :F]) * g[:, F:]
+    assert (np.abs(_to_f64(a) - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-30).all()
+
+
+@pytest.mark.parametrize("R,H,F", [(300, 256, 512), (64, 4096, 14336)])
+def test_swiglu_ffn_matches_oracle(R, H, F):
+    say(f"[case] swiglu_ffn R={R} H={H} F={F}")
+    x, wgu, wd, res = synth.gen_ffn(R, H, F, seed=R)
+    y = up.swiglu_ffn(bf16_dev(x).view(R, H), bf16_dev(wgu).view(2 * F, H), bf16_dev(wd).view(H, F),
+                      residual=bf16_dev(res).view(R, H))
+    torch.cuda.synchronize()
+    ref, _, a = C.ffn(x, wgu, wd, F, residual_bits=res)
+    mag = np.abs(a) @ np.abs(C.bits_to_f64(wd)).T
+    err = np.abs(_to_f64(y) - ref)
+    tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -7 * mag + 1e-30
+    assert (err <= tol).all(), f"worst excess {float((err - tol).max()):.3e}"

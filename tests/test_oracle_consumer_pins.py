@@ -216,3 +216,13 @@ def test_ffn_with_zero_gate_returns_the_residual():
     y, _, a = C.ffn(x, wgu, wd, F, residual_bits=res)
     assert np.all(a == 0)
     np.testing.assert_array_equal(y, C.bits_to_f64(res))
+
+
+def test_sampled_rows_equal_the_full_attention():
+    rng = np.random.default_rng(11)
+    lengths, Hq, Hkv, d = [70, 33], 4, 2, 16
+    q, k, v, pos, cu = _packed(rng, lengths, Hq, Hkv, d)
+    full = C.rope_attention(q, k, v, pos, cu, Hq, Hkv, d, 0.3, 10000.0)
+    rows = [0, 1, 69, 70, 71, 102]
+    part = C.rope_attention_rows(q, k, v, pos, cu, Hq, Hkv, d, 0.3, 10000.0, rows)
+    np.testing.assert_allclose(part, full[rows], rtol=1e-12, atol=1e-14)

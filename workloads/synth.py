@@ -246,3 +246,68 @@ def gen_layer(orig: np.ndarray, L0: int, needles: np.ndarray, Hq: int, Hkv: int,
             kc[nrow] += np.float32(2.0) * sd * u
         kb[r0:r1] = f32_to_bf16_bits(kc)
     return Request(L=L, qwin=f32_to_bf16_bits(q), k=kb, needles=needles)
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the layer on the surviving tokens
+# ---------------------------------------------------------------------------
+TAG_CONSUMER = 3
+
+
+def survivor_positions(lengths, rng, G: int = 64, drop_rate: float = 0.25) -> np.ndarray:
+    """Original positions of survivors: per request, ascending, in runs of G tokens
+    with whole dropped blocks (a drop_rate share of them) between the runs, the way a
+    block-wise drop leaves them.  int32 [sum(lengths)]."""
+    out = []
+    for L in lengths:
+        if L == 0:
+            continue
+        runs = (L + G - 1) // G
+        gaps = rng.binomial(3, drop_rate, size=runs) * G   # dropped tokens before each run
+        start = np.cumsum(gaps) + np.arange(runs) * G
+        p = (start[:, None] + np.arange(G)[None, :]).reshape(-1)[:L]
+        out.append(p)
+    return (np.concatenate(out) if out else np.zeros(0, np.int64)).astype(np.int32)
+
+
+def _normal_bits(rng: np.random.Generator, shape, sigma: float = 1.0) -> np.ndarray:
+    """Standard normal float32 draws times sigma, rounded to bfloat16 bits, drawn in
+    chunks of rows (the stream equals one draw of the whole array)."""
+    out = np.empty(shape, dtype=np.uint16)
+    flat = out.reshape(shape[0], -1)
+    per_row = flat.shape[1]
+    rows_per = max(1, CHUNK_ELEMS // max(per_row, 1))
+    for r0 in range(0, shape[0], rows_per):
+        r1 = min(shape[0], r0 + rows_per)
+        x = rng.standard_normal((r1 - r0, per_row), dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        flat[r0:r1] = f32_to_bf16_bits(x)
+    return out
+
+
+def gen_consumer_attention(lengths, Hq: int, Hkv: int, d: int, seed: int,
+                           q_sigma: float = 1.0, G: int = 64):
+    """q [R, Hq, d], k, v [R, Hkv, d] (bf16 bits, standard normal, q scaled by q_sigma),
+    carried positions pos [R] and row offsets cu [B+1] for the attention on the
+    survivors."""
+    rng = np.random.default_rng([seed, TAG_CONSUMER])
+    R = int(sum(lengths))
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    q = _normal_bits(rng, (R, Hq, d), q_sigma)
+    k = _normal_bits(rng, (R, Hkv, d))
+    v = _normal_bits(rng, (R, Hkv, d))
+    pos = survivor_positions(lengths, rng, G)
+    return q, k, v, pos, cu
+
+
+def gen_ffn(R: int, H: int, F: int, seed: int):
+    """x [R, H], w_gu [2F, H], w_down [H, F], residual [R, H] as bf16 bits; the weights
+    are scaled by 1/sqrt(fan-in) so activations stay of order one."""
+    rng = np.random.default_rng([seed, TAG_CONSUMER, 1])
+    x = _normal_bits(rng, (R, H))
+    wgu = _normal_bits(rng, (2 * F, H), 1.0 / np.sqrt(H))
+    wd = _normal_bits(rng, (H, F), 1.0 / np.sqrt(F))
+    res = _normal_bits(rng, (R, H))
+    return x, wgu, wd, res
