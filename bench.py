@@ -233,9 +233,101 @@ def main():
     if not args.headline_only:
         result["paged_keys"] = paged_keys_leg(up, torch, qwin, k, cu, b, args)
 
+    # The layer that then runs on the survivors (scope: next), against the same layer on
+    # every token.
+    if not args.headline_only and b.d in (64, 128):
+        result["consumer"] = consumer_leg(up, torch, dec, hid, b, cfg)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, hidden, pos, p, cfg)
     print(json.dumps(result), flush=True)
+
+
+def consumer_leg(up, torch, dec, hid, b, cfg, reps=2):
+    """One decoder layer with random weights -- q, k, v projections, rotary attention at
+    the carried positions, output projection plus residual, SwiGLU FFN plus residual --
+    on the survivors of the headline decision and on every token (no drop, positions
+    0..N-1).  Weights and inputs are seeded; nothing here is part of `value`."""
+    import math
+    H, Hq, Hkv, d = cfg["H"], b.Hq, b.Hkv, b.d
+    F = 14336 if H == 4096 else int(round(3.5 * H / 256)) * 256   # Llama-3.1-8B FFN width
+    dev = hid.device
+    g = torch.Generator(device=dev).manual_seed(20260)
+
+    def w(n, k_):
+        return (torch.randn(n, k_, generator=g, device=dev) / math.sqrt(k_)).to(torch.bfloat16)
+
+    Wq, Wk, Wv, Wo = w(Hq * d, H), w(Hkv * d, H), w(Hkv * d, H), w(H, Hq * d)
+    Wgu, Wd = w(2 * F, H), w(H, F)
+    N = b.T
+    kept = int(dec.cu_out[-1].item())
+    cu_all_h = b.cu_seqlens
+    cu_kept_h = dec.cu_out.cpu().numpy()
+    cu_all = torch.from_numpy(cu_all_h).to(dev)
+    pos_all = torch.from_numpy(synth_positions(cu_all_h)).to(dev)
+    buf = {name: torch.empty((N, cols), dtype=torch.bfloat16, device=dev)
+           for name, cols in (("q", Hq * d), ("k", Hkv * d), ("v", Hkv * d), ("att", Hq * d),
+                              ("h2", H), ("y", H))}
+    ws_att = torch.empty(max(up.rope_attention_workspace_bytes(cu_all_h, Hq, Hkv, d),
+                             up.rope_attention_workspace_bytes(cu_kept_h, Hq, Hkv, d)),
+                         dtype=torch.uint8, device=dev)
+    ws_ffn = torch.empty(up.swiglu_ffn_workspace_bytes(N, H, F), dtype=torch.uint8, device=dev)
+    ws_gemm = torch.empty(32 << 20, dtype=torch.uint8, device=dev)
+
+    def layer(x, pos, cu, cu_h, R):
+        q = up.linear(x, Wq, out=buf["q"][:R], workspace=ws_gemm)
+        k_ = up.linear(x, Wk, out=buf["k"][:R], workspace=ws_gemm)
+        v = up.linear(x, Wv, out=buf["v"][:R], workspace=ws_gemm)
+        att = up.rope_attention(q.view(R, Hq, d), k_.view(R, Hkv, d), v.view(R, Hkv, d), pos, cu,
+                                cu_h, out=buf["att"][:R].view(R, Hq, d), workspace=ws_att)
+        h2 = up.linear(att.view(R, Hq * d), Wo, residual=x, out=buf["h2"][:R], workspace=ws_gemm)
+        return up.swiglu_ffn(h2, Wgu, Wd, residual=h2, out=buf["y"][:R], workspace=ws_ffn)
+
+    stream = torch.cuda.current_stream()
+    cases = {"survivors": (dec.hidden_out[:kept], dec.pos_out[:kept], dec.cu_out, cu_kept_h, kept),
+             "all_tokens": (hid, pos_all, cu_all, cu_all_h, N)}
+    out = {}
+    for name, (x, pos, cu, cu_h, R) in cases.items():
+        layer(x, pos, cu, cu_h, R)                       # warm-up (GEMM plans, caches)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            layer(x, pos, cu, cu_h, R)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        up.profile_reset()
+        up.profile_enable(True)
+        layer(x, pos, cu, cu_h, R)
+        torch.cuda.synchronize()
+        up.profile_enable(False)
+        kt = {}
+        for kname in ("attn_plan", "rope_layout", "attention", "swiglu", "gemm"):
+            n, tot = up.profile_read(kname)
+            if n:
+                kt[kname] = round(tot * 1e3, 1)          # microseconds per layer
+        up.profile_reset()
+        assert up.device_error() == 0
+        pairs = sum(int(L) * (int(L) + 1) // 2 for L in np.diff(cu_h))
+        att_flops = 4.0 * d * Hq * pairs                  # Q K^T and P V over causal pairs
+        gemm_flops = 2.0 * R * H * (Hq * d + 2 * Hkv * d + Hq * d + 3 * F)
+        att_tf = att_flops / (kt["attention"] * 1e-6) / 1e12
+        out[name] = {"rows": R, "ms": round(ms, 3), "kernel_us": kt,
+                     "attention_tflops": round(att_tf, 1),
+                     "attention_frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "gemm_tflops": round(gemm_flops / (kt["gemm"] * 1e-6) / 1e12, 1)}
+        log(f"[bench] consumer {name}: {R} rows, {ms:.2f} ms/layer, attention {att_tf:.0f} TFLOP/s")
+    out["time_ratio"] = round(out["survivors"]["ms"] / out["all_tokens"]["ms"], 4)
+    out["rho"] = round(kept / N, 4)
+    out["note"] = ("one decoder layer (projections, rotary attention at the carried positions, "
+                   "SwiGLU FFN width %d) with random weights; not the headline" % F)
+    return out
+
+
+def synth_positions(cu_h):
+    from workloads import synth
+    return synth.positions(cu_h)
 
 
 def median_flushed_leg(torch, dec, stream, T, reps=100, warmup=20, flush_bytes=1 << 30):
