@@ -456,6 +456,15 @@ __global__ __launch_bounds__(256, 1) void up_attention_kernel(
   };
   // Softmax of half-step hs (S^T in acc) and O^T += V^T P^T over its 32 keys.
   auto pv = [&](int hs, const f32x16 (&acc)[QT]) {
+    // V^T operands first: their LDS latency runs under the softmax below.
+    const int kt = hs & 1;
+    const uint8_t* sl = lds + ((hs >> 1) & (NS - 1)) * SB;
+    bf16x8 va[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        va[dt][jj] = *reinterpret_cast<const bf16x8*>(sl + dt * 32 * 128 + vrd[2 * kt + jj]);
     bf16x8 pb[2][QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
@@ -472,17 +481,14 @@ __global__ __launch_bounds__(256, 1) void up_attention_kernel(
       pb[0][t] = __builtin_convertvector(p.lo, bf16x8);
       pb[1][t] = __builtin_convertvector(p.hi, bf16x8);
     }
-    const int kt = hs & 1;
-    const uint8_t* sl = lds + ((hs >> 1) & (NS - 1)) * SB;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sl + dt * 32 * 128 + vrd[2 * kt + jj]);
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int t = 0; t < QT; ++t)
-          O[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[jj][t], O[dt][t], 0, 0, 0);
-      }
+          O[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][jj], pb[jj][t], O[dt][t], 0, 0,
+                                                             0);
   };
 
   // Ring: stages st+1 and st+2 in flight while st is consumed; stage st+1 is waited
