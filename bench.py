@@ -233,6 +233,11 @@ def main():
     if not args.headline_only:
         result["paged_keys"] = paged_keys_leg(up, torch, qwin, k, cu, b, args)
 
+    # What a plain device-to-device copy of the gather's row bytes reaches on this machine:
+    # the practical ceiling the gather's HBM fraction is read against.
+    if not args.headline_only:
+        result["copy_ceiling"] = copy_ceiling_leg(torch, kept * row_bytes, g_us, gather_bytes)
+
     # The layer that then runs on the survivors (scope: next), against the same layer on
     # every token.
     if not args.headline_only and b.d in (64, 128):
@@ -442,6 +447,28 @@ def paged_keys_leg(up, torch, qwin, k, cu, b, args, page_size=16):
     assert up.device_error() == 0
     out.update({"page_size": page_size, "bit_identical": same})
     return out
+
+
+def copy_ceiling_leg(torch, nbytes, gather_us, gather_bytes, reps=20):
+    """torch's device-to-device copy of `nbytes` (read + write), timed like the gather."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    gather_gbs = gather_bytes / (gather_us * 1e-6) / 1e9
+    return {"bytes_read_plus_written": 2 * nbytes, "us": round(ms * 1e3, 1), "GB/s": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "gather_vs_copy": round(gather_gbs / gbs, 4),
+            "note": "torch copy_ of the kept rows' bytes; the gather moves these plus indices"}
 
 
 def copy_reference(torch, nbytes, steps):
