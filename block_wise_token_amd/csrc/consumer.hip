@@ -240,9 +240,10 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
 // ---------------------------------------------------------------------------
 // Causal GQA flash attention on the matrix cores.
 //
-// Workgroup = 4 waves (one per SIMD) = HQ query heads x TT 64-token tiles of one kv
-// head (HQ * TT = 4), one wave per (head, tile), 64 query rows per wave in two
-// 32-row tiles held as the B operand in VGPRs.  Keys and values stream through a ring
+// Workgroup = 8 waves (two per SIMD) = HQ query heads x TT 64-token tiles of one kv
+// head (HQ * TT = 4), two waves per (head, tile), 32 query rows per wave held as the B
+// operand in VGPRs (the kernel also builds with 64 rows per wave in 4 waves).  Keys
+// and values stream through a ring
 // of four LDS stages of 64 tokens (K tile [64][d] and V^T tile [d][64], 16-byte
 // granules XOR-swizzled), copied global -> LDS directly two stages ahead of use.
 //   S^T = K Q^T        (keys as rows: each lane column is one query, so a query's
@@ -290,14 +291,17 @@ __device__ __forceinline__ int v_swz(int row) { return row & 7; }
 
 constexpr float kRebase = 32.f;
 
-template <int D>
-__global__ __launch_bounds__(256, 1) void up_attention_kernel(
+// Rows per wave: QT tiles of 32; waves per workgroup: NW = 8 / QT, so that a (query
+// head, 64-token tile) pair is 2 / QT waves.
+template <int D, int QT>
+__global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
     const int32_t* __restrict__ tp, int B, int Hq, int Hkv, int HQ, int TT, int64_t Rp,
     float c, uint16_t* __restrict__ out) {
-  constexpr int NT = 256, NS = 4, UK = 64, QT = 2;
+  constexpr int NW = 8 / QT, NT = 64 * NW, NS = 4, UK = 64;
+  constexpr int WPP = 2 / QT;            // waves per (query head, 64-token tile) pair
   constexpr int DS = D / 16;             // MFMA k-steps over the head dimension
   constexpr int DT = D / 32;             // 32-row tiles of O^T (head dimension)
   constexpr int KRB = 2 * D;             // K tile row bytes
@@ -325,8 +329,9 @@ __global__ __launch_bounds__(256, 1) void up_attention_kernel(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5,
             l32 = lane & 31;
-  const int head = g * gsz + quad * HQ + wave % HQ;
-  const int tw = tile0 + wave / HQ;   // this wave's 64-token tile (its diagonal stage)
+  const int pair = wave / WPP, sub = wave % WPP;   // sub: which 32 * QT rows of the tile
+  const int head = g * gsz + quad * HQ + pair % HQ;
+  const int tw = tile0 + pair / HQ;   // this wave's 64-token tile (its diagonal stage)
   const bool wact = tw < ntile;
 
   // Query operand.  The head dimension is contracted in a permuted order shared by
@@ -336,7 +341,8 @@ __global__ __launch_bounds__(256, 1) void up_attention_kernel(
   for (int t = 0; t < QT; ++t) {
     if (wact) {
       const uint16_t* src =
-          qr + ((int64_t)head * Rp + pbase + tw * 64 + t * 32 + l32) * D + half * (D / 2);
+          qr + ((int64_t)head * Rp + pbase + tw * 64 + sub * 32 + t * 32 + l32) * D +
+          half * (D / 2);
 #pragma unroll
       for (int s = 0; s < DS; ++s) qreg[t][s] = *reinterpret_cast<const bf16x8*>(src + s * 8);
     } else {
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void up_attention_kernel(
   }
   int qtok[QT];
 #pragma unroll
-  for (int t = 0; t < QT; ++t) qtok[t] = tw * 64 + t * 32 + l32;
+  for (int t = 0; t < QT; ++t) qtok[t] = tw * 64 + sub * 32 + t * 32 + l32;
 
   // The keys are consumed in halves of 32 (half-step hs = keys [32 hs, 32 hs + 32) of
   // the request, stage hs / 2, row tile hs % 2 of that stage).
@@ -647,12 +653,16 @@ hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, con
   const auto* vt = reinterpret_cast<const uint16_t*>(w + L.vt);
   const dim3 grid((unsigned)(s.Hkv * (s.Hq / s.Hkv / s.HQ)), (unsigned)s.tiles);
   auto o = static_cast<uint16_t*>(out);
+  // 32 rows per wave, 8 waves: two waves per SIMD (225 VGPRs), so one wave's softmax
+  // runs beside the other's MFMAs.  (64 rows per wave in 4 waves, one per SIMD at
+  // 256 + 256 registers, measured 7% slower at 129,600 rows.)
+  constexpr int QT = 1;
   if (s.d == 64)
-    hipLaunchKernelGGL(up_attention_kernel<64>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
-                       tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+    hipLaunchKernelGGL((up_attention_kernel<64, QT>), grid, dim3(64 * (8 / QT)), 0, st, qr, kr, vt,
+                       hdr, cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
   else
-    hipLaunchKernelGGL(up_attention_kernel<128>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
-                       tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+    hipLaunchKernelGGL((up_attention_kernel<128, QT>), grid, dim3(64 * (8 / QT)), 0, st, qr, kr,
+                       vt, hdr, cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
   return hipGetLastError();
 }
 
