@@ -465,7 +465,7 @@ int plan_attention(const int32_t* cu_h, int B, int Hq, int Hkv, int d, AttnShape
   s->R = B > 0 ? cu_h[B] : 0;
   s->Rp = Rp;
   s->tiles = tiles;
-  if (Rp > INT32_MAX || tiles > 65535) return UP_EUNSUPPORTED;
+  if (Rp > INT32_MAX || tiles > 65535 || Hkv > kMaxAttnKvHeads) return UP_EUNSUPPORTED;
   if ((int64_t)Hkv * (gsz / s->HQ) > 65535) return UP_EUNSUPPORTED;
   return UP_OK;
 }

@@ -137,17 +137,21 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
     const WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ po, int B, int Hq, int Hkv, int64_t Rp, double log2_theta,
-    uint16_t* __restrict__ qr, uint16_t* __restrict__ kr, uint16_t* __restrict__ vt) {
+    uint16_t* __restrict__ qr, uint16_t* __restrict__ kr, uint16_t* __restrict__ vt,
+    float* __restrict__ kn) {
   constexpr int PG = D / 8;          // groups of 4 pairs per row
   constexpr int NU = 64 * PG / 256;  // (row, group) items per thread
   constexpr int VRS = 2 * D + 4;     // LDS bytes per v row (padded against bank conflicts)
   __shared__ __attribute__((aligned(16))) uint8_t vs[64 * VRS];
+  __shared__ uint32_t knorm2[kMaxAttnKvHeads];   // per kv head: max |k'|^2 of the tile (bits)
   if (hdr->valid != 1) return;
   const int64_t row0p = (int64_t)blockIdx.x * 64;
   const int i = request_of(po, B, row0p);
   const int t0 = (int)(row0p - po[i]);
   const int L = cu[i + 1] - cu[i];
   const int tid = threadIdx.x;
+  for (int h = tid; h < Hkv; h += 256) knorm2[h] = 0u;
+  __syncthreads();
 
   // q and k: each thread owns NU (row, 4-pair group) items and their 8 angles.
   double cs[NU][4], sn[NU][4];
@@ -176,6 +180,7 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
     const int H = isq ? Hq : Hkv;
     const uint16_t* src = isq ? q : k;
     uint16_t* dst = (isq ? qr : kr) + ((int64_t)hh * Rp + row0p) * D;
+    float rowmax = 0.f;   // keys: largest squared norm of this thread's rows
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       ushort4 lo = make_ushort4(0, 0, 0, 0), hi = make_ushort4(0, 0, 0, 0);
@@ -198,8 +203,25 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
       uint16_t* d = dst + (int64_t)rr_of[u] * D + 4 * pg_of[u];
       *reinterpret_cast<ushort4*>(d) = lo;
       *reinterpret_cast<ushort4*>(d + D / 2) = hi;
+      if (!isq) {
+        // squared norm of the rotated bf16 key row: the PG lanes of a row are adjacent
+        const uint16_t v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        float ss = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float f = __uint_as_float((uint32_t)v8[m] << 16);
+          ss = fmaf(f, f, ss);
+        }
+#pragma unroll
+        for (int off = PG / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+        rowmax = fmaxf(rowmax, ss);
+      }
     }
+    if (!isq) atomicMax(&knorm2[hh], __float_as_uint(rowmax));   // non-negative: bits order as values
   }
+  __syncthreads();
+  for (int h = tid; h < Hkv; h += 256)
+    kn[(int64_t)h * (Rp / 64) + blockIdx.x] = sqrtf(__uint_as_float(knorm2[h]));
 
   // v: stage 64 rows of one kv head in LDS, then write 16-byte runs of 8 tokens per
   // d-row in the swapped token order.
@@ -298,8 +320,8 @@ __global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
-    const int32_t* __restrict__ tp, int B, int Hq, int Hkv, int HQ, int TT, int64_t Rp,
-    float c, uint16_t* __restrict__ out) {
+    const int32_t* __restrict__ tp, const float* __restrict__ kn, int B, int Hq, int Hkv,
+    int HQ, int TT, int64_t Rp, float c, uint16_t* __restrict__ out) {
   constexpr int NW = 8 / QT, NT = 64 * NW, NS = 4, UK = 64;
   constexpr int WPP = 2 / QT;            // waves per (query head, 64-token tile) pair
   constexpr int DS = D / 16;             // MFMA k-steps over the head dimension
@@ -351,6 +373,30 @@ __global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
     }
   }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): only stage copies from here
+
+  // Largest query norm of the wave times c: with the largest key norm of a stage it
+  // bounds every logit of the stage (Cauchy-Schwarz).
+  float qbound;
+  {
+    float m = 0.f;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = (float)qreg[t][s][e];
+          ss = fmaf(f, f, ss);
+        }
+      m = fmaxf(m, pair_sum(ss));
+    }
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    // float32 norms and the MFMA's float32 sums are far inside this margin
+    qbound = __builtin_amdgcn_readfirstlane(sqrtf(m) * c * 1.001f);
+  }
+  const float* knrow = kn + (int64_t)g * (Rp / 64) + (pbase >> 6);
 
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8*)lds;
@@ -460,6 +506,15 @@ __global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
       }
     }
   };
+  // The exact check can be skipped for a stage whose logit bound is within 32 of every
+  // reference of the wave: no logit there can trigger a rebase.
+  auto bound_ok = [&](int hs) {
+    const float b = qbound * knrow[hs >> 1] - kRebase;
+    bool over = false;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) over |= b > Rs[t];
+    return __builtin_amdgcn_ballot_w64(over) == 0;
+  };
   // Softmax of half-step hs (S^T in acc) and O^T += V^T P^T over its 32 keys.
   auto pv = [&](int hs, const f32x16 (&acc)[QT]) {
     // V^T operands first: their LDS latency runs under the softmax below.
@@ -525,14 +580,16 @@ __global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
   auto body = [&](int hs, f32x16 (&cur)[QT], f32x16 (&nxt)[QT]) {
     if (!wact || hs > last_hs) return;
     if (hs + 1 < 2 * tw) {          // next half-step is before the diagonal stage
+      const bool skip = bound_ok(hs + 1);
       s_mfma(hs + 1, nxt);
       pv(hs, cur);
-      rebase(nxt, false);
+      if (!skip) rebase(nxt, false);
     } else if (hs + 1 <= last_hs) {   // next half-step is in the diagonal stage
+      const bool skip = bound_ok(hs + 1);
       s_mfma(hs + 1, nxt);
       pv(hs, cur);
       mask(hs + 1, nxt);
-      rebase(nxt, false);
+      if (!skip) rebase(nxt, false);
     } else {
       pv(hs, cur);
     }
@@ -606,6 +663,8 @@ AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp) {
   o += align_up((size_t)Hkv * Rp * d * 2);
   w.vt = o;
   o += align_up((size_t)Hkv * Rp * d * 2);
+  w.kn = o;
+  o += align_up((size_t)Hkv * (Rp / 64) * sizeof(float));
   w.total = o;
   return w;
 }
@@ -629,16 +688,17 @@ hipError_t launch_rope_layout(const void* q, const void* k, const void* v, const
   auto* qr = reinterpret_cast<uint16_t*>(w + L.qr);
   auto* kr = reinterpret_cast<uint16_t*>(w + L.kr);
   auto* vt = reinterpret_cast<uint16_t*>(w + L.vt);
+  auto* kn = reinterpret_cast<float*>(w + L.kn);
   const dim3 grid((unsigned)(s.Rp / 64));
   auto kq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(k);
   auto kv = static_cast<const uint16_t*>(v);
   if (s.d == 64)
     hipLaunchKernelGGL(up_rope_layout_kernel<64>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr, cu,
-                       po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
+                       po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt, kn);
   else
     hipLaunchKernelGGL(up_rope_layout_kernel<128>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr,
-                       cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
+                       cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt, kn);
   return hipGetLastError();
 }
 
@@ -651,6 +711,7 @@ hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, con
   const auto* qr = reinterpret_cast<const uint16_t*>(w + L.qr);
   const auto* kr = reinterpret_cast<const uint16_t*>(w + L.kr);
   const auto* vt = reinterpret_cast<const uint16_t*>(w + L.vt);
+  const auto* kn = reinterpret_cast<const float*>(w + L.kn);
   const dim3 grid((unsigned)(s.Hkv * (s.Hq / s.Hkv / s.HQ)), (unsigned)s.tiles);
   auto o = static_cast<uint16_t*>(out);
   // 32 rows per wave, 8 waves: two waves per SIMD (225 VGPRs), so one wave's softmax
@@ -659,10 +720,10 @@ hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, con
   constexpr int QT = 1;
   if (s.d == 64)
     hipLaunchKernelGGL((up_attention_kernel<64, QT>), grid, dim3(64 * (8 / QT)), 0, st, qr, kr, vt,
-                       hdr, cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+                       hdr, cu, po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
   else
     hipLaunchKernelGGL((up_attention_kernel<128, QT>), grid, dim3(64 * (8 / QT)), 0, st, qr, kr,
-                       vt, hdr, cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+                       vt, hdr, cu, po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
   return hipGetLastError();
 }
 

@@ -140,8 +140,10 @@ struct AttnShape {
   int64_t tiles;    // attention workgroup tiles of 64 * TT tokens
 };
 struct AttnWs {
-  size_t hdr, po, tp, qr, kr, vt, total;
+  size_t hdr, po, tp, qr, kr, vt, kn, total;
 };
+// Largest Hkv the attention's rotary layout pass supports (per-head LDS slots).
+constexpr int kMaxAttnKvHeads = 256;
 AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp);
 hipError_t launch_attn_plan(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
                             int* err, hipStream_t st);
