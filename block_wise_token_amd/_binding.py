@@ -14,7 +14,7 @@ KERNEL_IDS = {
     "score_partial": 0, "row_stats": 1, "block_mass": 2, "normalize": 3, "select": 4,
     "select_finalize": 5, "block_dst": 6, "gather": 7, "compose": 8, "score_plan": 9,
     "score_partial_lse": 10, "lse_finalize": 11, "attn_plan": 12, "rope_layout": 13,
-    "attention": 14, "swiglu": 15, "gemm": 16,
+    "attention": 14, "swiglu": 15, "gemm": 16, "select_fused": 17,
 }
 
 _lib = None
@@ -84,6 +84,11 @@ def lib():
     L.up_swiglu_ffn_workspace.argtypes = [i64, ci, ci]
     L.up_swiglu_ffn.restype = ci
     L.up_swiglu_ffn.argtypes = [vp, vp, vp, vp, i64, ci, ci, vp, vp, cs, vp]
+    L.up_layer_decision_workspace.restype = cs
+    L.up_layer_decision_workspace.argtypes = [vp, ci, ci, ci, ci, ci, ci]
+    L.up_layer_decision.restype = ci
+    L.up_layer_decision.argtypes = [vp, vp, i32p, vp, ci, ci, ci, ci, ci, ci, cf, cf, vp, ci, ci,
+                                    i32p, i32p, f32p, u8p, i32p, i32p, vp, i32p, i32p, vp, cs, vp]
     _lib = L
     return L
 
@@ -329,11 +334,12 @@ class LayerDecision:
     ``run()`` issues the calls -- scores, Top-p, expand+compact with the drop
     composition fused into the compaction pass -- on the current stream and
     allocates nothing.  (``up_compose_drops`` is the standalone form of the last
-    step.)
+    step.)  For a plain Top-p decision (no given row log-sum-exp, no Top-k) it is one
+    ``up_layer_decision`` call; ``separate=True`` issues the three calls instead.
     """
 
     def __init__(self, qwin, k, cu_seqlens, cu_h, hidden, pos, n, G, p, scale=0.0,
-                 prev_orig=None, topk=None, row_lse=None):
+                 prev_orig=None, topk=None, row_lse=None, separate=False):
         self.qwin, self.k, self.cu, self.hidden, self.pos = qwin, k, cu_seqlens, hidden, pos
         self.h = _HostCu(cu_h)
         self.n, self.G, self.p, self.scale, self.topk = n, G, p, scale, topk
@@ -357,8 +363,23 @@ class LayerDecision:
         self.prev_orig = prev_orig if prev_orig is not None else torch.arange(
             T, dtype=torch.int32, device=dev)
         self.orig = torch.empty(T, dtype=torch.int32, device=dev)
+        self.one_call = not separate and row_lse is None and topk is None and pos is not None
+        if self.one_call:
+            need = int(lib().up_layer_decision_workspace(self.h.ptr, B, Hq, Hkv, d, n, G))
+            self.ws_one = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+            self.dims = (Hq, Hkv, d, int(hidden.shape[1]), hidden.element_size())
 
     def run(self, stream=None):
+        if self.one_call:
+            Hq, Hkv, d, H, eb = self.dims
+            st = lib().up_layer_decision(
+                _ptr(self.qwin), _ptr(self.k), _ptr(self.cu), self.h.ptr, self.h.B, Hq, Hkv, d,
+                self.n, self.G, float(self.scale), float(self.p), _ptr(self.hidden), H, eb,
+                _ptr(self.pos), _ptr(self.prev_orig), _ptr(self.scores), _ptr(self.keep),
+                _ptr(self.cu_out), _ptr(self.idx), _ptr(self.hidden_out), _ptr(self.pos_out),
+                _ptr(self.orig), _ptr(self.ws_one), self.ws_one.numel(), _stream(stream))
+            _check(st, "up_layer_decision")
+            return
         if self.row_lse is None:
             block_scores(self.qwin, self.k, self.cu, self.h.arr, self.n, self.G, self.scale,
                          out=self.scores, workspace=self.ws_scores, stream=stream)

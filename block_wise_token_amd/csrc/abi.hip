@@ -230,17 +230,19 @@ size_t up_block_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int
   return score_ws_layout(B, t).total;
 }
 
+// stop_at_mass: leave the float64 block masses in the workspace and skip the
+// normalisation (the fused decision normalises inside its select kernel).
 static int block_scores_common(const void* qwin, const void* k, const PagedK* paged,
                                const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B,
                                int Hq, int Hkv, int d, int n, int G, float scale, float* scores,
                                float* row_lse, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               void* stream, bool stop_at_mass = false) {
   ScoreShape s;
   Totals t;
   const int st = plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t);
   if (st != UP_OK) return st;
   if (B == 0 || t.T == 0) return UP_OK;
-  if (!qwin || !k || !cu_seqlens || !scores) return UP_EINVAL;
+  if (!qwin || !k || !cu_seqlens || (!scores && !stop_at_mass)) return UP_EINVAL;
   if (!aligned(qwin, 16) || !aligned(k, 16)) return UP_EINVAL;
   const ScoreWs L = score_ws_layout(B, t);
   if (!workspace || workspace_bytes < L.total || !aligned(workspace, kWsAlign))
@@ -268,6 +270,7 @@ static int block_scores_common(const void* qwin, const void* k, const PagedK* pa
   if (e != hipSuccess) return UP_EHIP;
   e = timed(2, hs, [&] { return launch_block_mass(s, t, workspace, L, hs); });
   if (e != hipSuccess) return UP_EHIP;
+  if (stop_at_mass) return UP_OK;
   e = timed(3, hs, [&] { return launch_normalize(s, t, workspace, L, scores, hs); });
   if (e != hipSuccess) return UP_EHIP;
   return UP_OK;
@@ -443,6 +446,84 @@ int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
   return e == hipSuccess ? UP_OK : UP_EHIP;
 }
 
+// ---- the whole decision in one call ---------------------------------------------
+
+size_t up_layer_decision_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d,
+                                   int n, int G) {
+  ScoreShape s;
+  Totals t;
+  if (plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t) != UP_OK) return 0;
+  const SelPlan sp = sel_plan(cu_seqlens_h, B, G);
+  return score_ws_layout(B, t).total + compact_ws_layout(sp.nb_tot).total;
+}
+
+int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens,
+                      const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d, int n, int G,
+                      float scale, float p, const void* hidden, int H, int elem_bytes,
+                      const int32_t* pos, const int32_t* prev_orig, float* scores,
+                      uint8_t* keep_blocks, int32_t* cu_seqlens_out, int32_t* idx_out,
+                      void* hidden_out, int32_t* pos_out, int32_t* orig_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  ScoreShape s;
+  Totals t;
+  int st = plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t);
+  if (st != UP_OK) return st;
+  if (!(p > 0.f && p <= 1.f) || H <= 0 || elem_bytes <= 0) return UP_EINVAL;
+  const SelPlan sp = sel_plan(cu_seqlens_h, B, G);
+  if (sp.nb_max > kSelectMaxBlocks) return UP_EUNSUPPORTED;
+  if (B == 0) return UP_OK;
+  const ScoreWs LS = score_ws_layout(B, t);
+  const CompactWs LC = compact_ws_layout(sp.nb_tot);
+  if (!workspace || workspace_bytes < LS.total + LC.total || !aligned(workspace, kWsAlign))
+    return UP_EWORKSPACE;
+  if (!qwin || !k || !cu_seqlens || !scores || !keep_blocks || !cu_seqlens_out || !hidden ||
+      !idx_out || !hidden_out)
+    return UP_EINVAL;
+  if ((pos_out && !pos) || (orig_out && !prev_orig)) return UP_EINVAL;
+  const int64_t row_bytes = (int64_t)H * elem_bytes;
+  if (sp.T > 0 && sp.T * row_bytes / row_bytes != sp.T) return UP_EUNSUPPORTED;
+  char* cws = static_cast<char*>(workspace) + LS.total;
+  // One request of at most 4096 blocks can have its normalisation and block
+  // destinations done inside the select kernel (kFusedSelect).  That path is switched
+  // off: a benchmark run that first used it left the GPU faulted and no cause has been
+  // shown, so every shape takes the three calls in sequence.
+  if (!kFusedSelect || B != 1 || t.T == 0 || sp.nb_tot > kFusedSelectMaxBlocks) {
+    st = block_scores_common(qwin, k, nullptr, cu_seqlens, cu_seqlens_h, B, Hq, Hkv, d, n, G,
+                             scale, scores, nullptr, workspace, LS.total, stream);
+    if (st != UP_OK) return st;
+    st = select_common(scores, cu_seqlens, cu_seqlens_h, B, n, G, 0, p, 0, keep_blocks,
+                       cu_seqlens_out, stream);
+    if (st != UP_OK) return st;
+    return up_expand_compact(hidden, H, elem_bytes, pos, keep_blocks, cu_seqlens, cu_seqlens_out,
+                             cu_seqlens_h, B, G, idx_out, hidden_out, pos_out, prev_orig,
+                             orig_out, cws, LC.total, stream);
+  }
+  st = block_scores_common(qwin, k, nullptr, cu_seqlens, cu_seqlens_h, B, Hq, Hkv, d, n, G, scale,
+                           nullptr, nullptr, workspace, LS.total, stream, /*stop_at_mass=*/true);
+  if (st != UP_OK) return st;
+  int* err = error_word();
+  if (!err) return UP_EHIP;
+  hipStream_t hs = as_stream(stream);
+  FusedDecision fd;
+  fd.mass = reinterpret_cast<const double*>(static_cast<char*>(workspace) + LS.mass);
+  fd.scores = scores;
+  fd.shdr = static_cast<const WsHeader*>(workspace);
+  fd.chdr = reinterpret_cast<WsHeader*>(cws + LC.hdr);
+  fd.dst = reinterpret_cast<int32_t*>(cws + LC.dst);
+  fd.src = reinterpret_cast<int32_t*>(cws + LC.src);
+  fd.len = reinterpret_cast<int32_t*>(cws + LC.len);
+  hipError_t e = timed(17, hs, [&] {
+    return launch_select_fused(cu_seqlens, n, G, p, sp.T, sp.nb_tot, keep_blocks, cu_seqlens_out,
+                               err, fd, hs);
+  });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(7, hs, [&] {
+    return launch_gather(hidden, row_bytes, pos, cws, LC, sp.nb_tot, G, idx_out, hidden_out,
+                         pos_out, prev_orig, orig_out, hs);
+  });
+  return e == hipSuccess ? UP_OK : UP_EHIP;
+}
+
 // ---- layer on the surviving tokens --------------------------------------------
 
 namespace {
@@ -465,7 +546,7 @@ int plan_attention(const int32_t* cu_h, int B, int Hq, int Hkv, int d, AttnShape
   s->R = B > 0 ? cu_h[B] : 0;
   s->Rp = Rp;
   s->tiles = tiles;
-  if (Rp > INT32_MAX || tiles > 65535 || Hkv > kMaxAttnKvHeads) return UP_EUNSUPPORTED;
+  if (Rp > INT32_MAX || tiles > 65535) return UP_EUNSUPPORTED;
   if ((int64_t)Hkv * (gsz / s->HQ) > 65535) return UP_EUNSUPPORTED;
   return UP_OK;
 }

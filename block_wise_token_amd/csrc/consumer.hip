@@ -137,21 +137,17 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
     const WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ po, int B, int Hq, int Hkv, int64_t Rp, double log2_theta,
-    uint16_t* __restrict__ qr, uint16_t* __restrict__ kr, uint16_t* __restrict__ vt,
-    float* __restrict__ kn) {
+    uint16_t* __restrict__ qr, uint16_t* __restrict__ kr, uint16_t* __restrict__ vt) {
   constexpr int PG = D / 8;          // groups of 4 pairs per row
   constexpr int NU = 64 * PG / 256;  // (row, group) items per thread
   constexpr int VRS = 2 * D + 4;     // LDS bytes per v row (padded against bank conflicts)
   __shared__ __attribute__((aligned(16))) uint8_t vs[64 * VRS];
-  __shared__ uint32_t knorm2[kMaxAttnKvHeads];   // per kv head: max |k'|^2 of the tile (bits)
   if (hdr->valid != 1) return;
   const int64_t row0p = (int64_t)blockIdx.x * 64;
   const int i = request_of(po, B, row0p);
   const int t0 = (int)(row0p - po[i]);
   const int L = cu[i + 1] - cu[i];
   const int tid = threadIdx.x;
-  for (int h = tid; h < Hkv; h += 256) knorm2[h] = 0u;
-  __syncthreads();
 
   // q and k: each thread owns NU (row, 4-pair group) items and their 8 angles.
   double cs[NU][4], sn[NU][4];
@@ -180,7 +176,6 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
     const int H = isq ? Hq : Hkv;
     const uint16_t* src = isq ? q : k;
     uint16_t* dst = (isq ? qr : kr) + ((int64_t)hh * Rp + row0p) * D;
-    float rowmax = 0.f;   // keys: largest squared norm of this thread's rows
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       ushort4 lo = make_ushort4(0, 0, 0, 0), hi = make_ushort4(0, 0, 0, 0);
@@ -203,25 +198,8 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
       uint16_t* d = dst + (int64_t)rr_of[u] * D + 4 * pg_of[u];
       *reinterpret_cast<ushort4*>(d) = lo;
       *reinterpret_cast<ushort4*>(d + D / 2) = hi;
-      if (!isq) {
-        // squared norm of the rotated bf16 key row: the PG lanes of a row are adjacent
-        const uint16_t v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        float ss = 0.f;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const float f = __uint_as_float((uint32_t)v8[m] << 16);
-          ss = fmaf(f, f, ss);
-        }
-#pragma unroll
-        for (int off = PG / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-        rowmax = fmaxf(rowmax, ss);
-      }
     }
-    if (!isq) atomicMax(&knorm2[hh], __float_as_uint(rowmax));   // non-negative: bits order as values
   }
-  __syncthreads();
-  for (int h = tid; h < Hkv; h += 256)
-    kn[(int64_t)h * (Rp / 64) + blockIdx.x] = sqrtf(__uint_as_float(knorm2[h]));
 
   // v: stage 64 rows of one kv head in LDS, then write 16-byte runs of 8 tokens per
   // d-row in the swapped token order.
@@ -262,10 +240,9 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
 // ---------------------------------------------------------------------------
 // Causal GQA flash attention on the matrix cores.
 //
-// Workgroup = 8 waves (two per SIMD) = HQ query heads x TT 64-token tiles of one kv
-// head (HQ * TT = 4), two waves per (head, tile), 32 query rows per wave held as the B
-// operand in VGPRs (the kernel also builds with 64 rows per wave in 4 waves).  Keys
-// and values stream through a ring
+// Workgroup = 4 waves (one per SIMD) = HQ query heads x TT 64-token tiles of one kv
+// head (HQ * TT = 4), one wave per (head, tile), 64 query rows per wave in two
+// 32-row tiles held as the B operand in VGPRs.  Keys and values stream through a ring
 // of four LDS stages of 64 tokens (K tile [64][d] and V^T tile [d][64], 16-byte
 // granules XOR-swizzled), copied global -> LDS directly two stages ahead of use.
 //   S^T = K Q^T        (keys as rows: each lane column is one query, so a query's
@@ -305,29 +282,22 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// 16-byte granule swizzles.  The LDS serves a 16-byte read to 16 lanes per clock across
-// 64 banks; the 16 lanes of a group read 16 consecutive rows at one logical granule,
-// which the XOR spreads over 16 distinct bank groups: by row & 15 for 256-byte rows,
-// by (row >> 1) & 7 for 128-byte rows (odd rows sit half a bank cycle further on).
 template <int D>
 __device__ __forceinline__ int k_swz(int key) {
-  return (D / 8 >= 16) ? (key & 15) : ((key >> 1) & 7);
+  return (D / 8 >= 16) ? (key & 15) : (key & 7);
 }
-__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int v_swz(int row) { return row & 7; }
 
 constexpr float kRebase = 32.f;
 
-// Rows per wave: QT tiles of 32; waves per workgroup: NW = 8 / QT, so that a (query
-// head, 64-token tile) pair is 2 / QT waves.
-template <int D, int QT>
-__global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
+template <int D>
+__global__ __launch_bounds__(256, 1) void up_attention_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
-    const int32_t* __restrict__ tp, const float* __restrict__ kn, int B, int Hq, int Hkv,
-    int HQ, int TT, int64_t Rp, float c, uint16_t* __restrict__ out) {
-  constexpr int NW = 8 / QT, NT = 64 * NW, NS = 4, UK = 64;
-  constexpr int WPP = 2 / QT;            // waves per (query head, 64-token tile) pair
+    const int32_t* __restrict__ tp, int B, int Hq, int Hkv, int HQ, int TT, int64_t Rp,
+    float c, uint16_t* __restrict__ out) {
+  constexpr int NT = 256, NS = 4, UK = 64, QT = 2;
   constexpr int DS = D / 16;             // MFMA k-steps over the head dimension
   constexpr int DT = D / 32;             // 32-row tiles of O^T (head dimension)
   constexpr int KRB = 2 * D;             // K tile row bytes
@@ -355,9 +325,8 @@ __global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5,
             l32 = lane & 31;
-  const int pair = wave / WPP, sub = wave % WPP;   // sub: which 32 * QT rows of the tile
-  const int head = g * gsz + quad * HQ + pair % HQ;
-  const int tw = tile0 + pair / HQ;   // this wave's 64-token tile (its diagonal stage)
+  const int head = g * gsz + quad * HQ + wave % HQ;
+  const int tw = tile0 + wave / HQ;   // this wave's 64-token tile (its diagonal stage)
   const bool wact = tw < ntile;
 
   // Query operand.  The head dimension is contracted in a permuted order shared by
@@ -367,8 +336,7 @@ __global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
   for (int t = 0; t < QT; ++t) {
     if (wact) {
       const uint16_t* src =
-          qr + ((int64_t)head * Rp + pbase + tw * 64 + sub * 32 + t * 32 + l32) * D +
-          half * (D / 2);
+          qr + ((int64_t)head * Rp + pbase + tw * 64 + t * 32 + l32) * D + half * (D / 2);
 #pragma unroll
       for (int s = 0; s < DS; ++s) qreg[t][s] = *reinterpret_cast<const bf16x8*>(src + s * 8);
     } else {
@@ -377,30 +345,6 @@ __global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
     }
   }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): only stage copies from here
-
-  // Largest query norm of the wave times c: with the largest key norm of a stage it
-  // bounds every logit of the stage (Cauchy-Schwarz).
-  float qbound;
-  {
-    float m = 0.f;
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      float ss = 0.f;
-#pragma unroll
-      for (int s = 0; s < DS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = (float)qreg[t][s][e];
-          ss = fmaf(f, f, ss);
-        }
-      m = fmaxf(m, pair_sum(ss));
-    }
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    // float32 norms and the MFMA's float32 sums are far inside this margin
-    qbound = __builtin_amdgcn_readfirstlane(sqrtf(m) * c * 1.001f);
-  }
-  const float* knrow = kn + (int64_t)g * (Rp / 64) + (pbase >> 6);
 
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8*)lds;
@@ -449,7 +393,7 @@ __global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
   }
   int qtok[QT];
 #pragma unroll
-  for (int t = 0; t < QT; ++t) qtok[t] = tw * 64 + sub * 32 + t * 32 + l32;
+  for (int t = 0; t < QT; ++t) qtok[t] = tw * 64 + t * 32 + l32;
 
   // The keys are consumed in halves of 32 (half-step hs = keys [32 hs, 32 hs + 32) of
   // the request, stage hs / 2, row tile hs % 2 of that stage).
@@ -509,15 +453,6 @@ __global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
         Rs[t] = rn;
       }
     }
-  };
-  // The exact check can be skipped for a stage whose logit bound is within 32 of every
-  // reference of the wave: no logit there can trigger a rebase.
-  auto bound_ok = [&](int hs) {
-    const float b = qbound * knrow[hs >> 1] - kRebase;
-    bool over = false;
-#pragma unroll
-    for (int t = 0; t < QT; ++t) over |= b > Rs[t];
-    return __builtin_amdgcn_ballot_w64(over) == 0;
   };
   // Softmax of half-step hs (S^T in acc) and O^T += V^T P^T over its 32 keys.
   auto pv = [&](int hs, const f32x16 (&acc)[QT]) {
@@ -584,16 +519,14 @@ __global__ __launch_bounds__(64 * (8 / QT), 1) void up_attention_kernel(
   auto body = [&](int hs, f32x16 (&cur)[QT], f32x16 (&nxt)[QT]) {
     if (!wact || hs > last_hs) return;
     if (hs + 1 < 2 * tw) {          // next half-step is before the diagonal stage
-      const bool skip = bound_ok(hs + 1);
       s_mfma(hs + 1, nxt);
       pv(hs, cur);
-      if (!skip) rebase(nxt, false);
+      rebase(nxt, false);
     } else if (hs + 1 <= last_hs) {   // next half-step is in the diagonal stage
-      const bool skip = bound_ok(hs + 1);
       s_mfma(hs + 1, nxt);
       pv(hs, cur);
       mask(hs + 1, nxt);
-      if (!skip) rebase(nxt, false);
+      rebase(nxt, false);
     } else {
       pv(hs, cur);
     }
@@ -667,8 +600,6 @@ AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp) {
   o += align_up((size_t)Hkv * Rp * d * 2);
   w.vt = o;
   o += align_up((size_t)Hkv * Rp * d * 2);
-  w.kn = o;
-  o += align_up((size_t)Hkv * (Rp / 64) * sizeof(float));
   w.total = o;
   return w;
 }
@@ -692,17 +623,16 @@ hipError_t launch_rope_layout(const void* q, const void* k, const void* v, const
   auto* qr = reinterpret_cast<uint16_t*>(w + L.qr);
   auto* kr = reinterpret_cast<uint16_t*>(w + L.kr);
   auto* vt = reinterpret_cast<uint16_t*>(w + L.vt);
-  auto* kn = reinterpret_cast<float*>(w + L.kn);
   const dim3 grid((unsigned)(s.Rp / 64));
   auto kq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(k);
   auto kv = static_cast<const uint16_t*>(v);
   if (s.d == 64)
     hipLaunchKernelGGL(up_rope_layout_kernel<64>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr, cu,
-                       po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt, kn);
+                       po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
   else
     hipLaunchKernelGGL(up_rope_layout_kernel<128>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr,
-                       cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt, kn);
+                       cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
   return hipGetLastError();
 }
 
@@ -715,19 +645,14 @@ hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, con
   const auto* qr = reinterpret_cast<const uint16_t*>(w + L.qr);
   const auto* kr = reinterpret_cast<const uint16_t*>(w + L.kr);
   const auto* vt = reinterpret_cast<const uint16_t*>(w + L.vt);
-  const auto* kn = reinterpret_cast<const float*>(w + L.kn);
   const dim3 grid((unsigned)(s.Hkv * (s.Hq / s.Hkv / s.HQ)), (unsigned)s.tiles);
   auto o = static_cast<uint16_t*>(out);
-  // 32 rows per wave, 8 waves: two waves per SIMD (225 VGPRs), so one wave's softmax
-  // runs beside the other's MFMAs.  (64 rows per wave in 4 waves, one per SIMD at
-  // 256 + 256 registers, measured 7% slower at 129,600 rows.)
-  constexpr int QT = 1;
   if (s.d == 64)
-    hipLaunchKernelGGL((up_attention_kernel<64, QT>), grid, dim3(64 * (8 / QT)), 0, st, qr, kr, vt,
-                       hdr, cu, po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+    hipLaunchKernelGGL(up_attention_kernel<64>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
+                       tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
   else
-    hipLaunchKernelGGL((up_attention_kernel<128, QT>), grid, dim3(64 * (8 / QT)), 0, st, qr, kr,
-                       vt, hdr, cu, po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+    hipLaunchKernelGGL(up_attention_kernel<128>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
+                       tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
   return hipGetLastError();
 }
 

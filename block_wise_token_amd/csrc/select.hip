@@ -162,6 +162,8 @@ struct SelLds {
   int64_t red[NW];
   uint32_t tie_cnt[kSelPer * NW];
   uint32_t tie_pre[kSelPer * NW];
+  int64_t dtot[kSelPer * NW];   // fused decision: kept tokens per (slot, wave)
+  double red64[NW];             // fused decision: wave sums of the block masses
   int win;            // (thread) index of the bin holding the cut, from the top
   uint32_t prefix;    // cut digits found so far
   uint64_t rem;       // remainder of p in units of 2^sh of the cut's exponent
@@ -228,11 +230,20 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, Lds& S) {
 }
 
 // NT threads per request; block a of the request lives in slot a / NT of thread a % NT.
-template <int NT>
+//
+// FUSED (one request, NT = 256): the kernel also does the normalisation and the
+// block destinations of the compaction, so the decision needs neither the normalise
+// nor the block-destination launch.  It reads the float64 block masses, sums them in
+// the order the normalise kernel uses (per thread over blocks tid, tid + 256, ...,
+// then the lanes by butterfly, then the four waves in order) so the float32 scores it
+// writes are bit-identical, selects on them, and writes each block's destination row,
+// source row and length with the compaction header's valid flag.
+template <int NT, bool FUSED>
 __global__ __launch_bounds__(NT) void up_select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ cu, int B, int n, int G,
     int mode, float p, int topk, int64_t T_host, int64_t nb_tot_host, int direct,
-    uint8_t* __restrict__ keep, int32_t* __restrict__ cu_out, int* __restrict__ err) {
+    uint8_t* __restrict__ keep, int32_t* __restrict__ cu_out, int* __restrict__ err,
+    FusedDecision fd) {
   constexpr int NW = NT / 64;
   constexpr int PER = kSelPer * 1024 / NT > kSelPer ? kSelPer : kSelPer * 1024 / NT;
   constexpr int MAXB = NT * PER;
@@ -245,7 +256,40 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
   // are fetched before cu_seqlens is back; the device values are checked after.
   uint32_t u[PER];
   int64_t blk_off = 0;
-  if (direct) {
+  if constexpr (FUSED) {
+    if (fd.shdr->valid != 1) {   // the score pass did not run: no masses to select on
+      if (tid == 0) {
+        fd.chdr->valid = 0;
+        cu_out[0] = 0;
+        cu_out[1] = 0;
+      }
+      return;
+    }
+    double mv[PER];
+    double part = 0.0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int64_t a = (int64_t)q * NT + tid;
+      mv[q] = a < nb_tot_host ? fd.mass[a] : 0.0;
+      part += mv[q];
+    }
+#pragma unroll
+    for (int dd = 32; dd > 0; dd >>= 1) part += __shfl_xor(part, dd);
+    if (lane == 0) S.red64[wave] = part;
+    __syncthreads();
+    const double tot = (S.red64[0] + S.red64[1]) + (S.red64[2] + S.red64[3]);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int64_t a = (int64_t)q * NT + tid;
+      if (a < nb_tot_host) {
+        const float sc = (float)(mv[q] / tot);
+        fd.scores[a] = sc;
+        u[q] = __float_as_uint(sc);
+      } else {
+        u[q] = kAbsent;
+      }
+    }
+  } else if (direct) {
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int64_t a = (int64_t)q * NT + tid;
@@ -269,6 +313,7 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
       atomicOr(err, 1);
       cu_out[i + 1] = 0;
       if (direct) cu_out[0] = 0;
+      if constexpr (FUSED) fd.chdr->valid = 0;
     }
     return;
   }
@@ -438,22 +483,58 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
 
   // Keep flags and kept-token count.
   int64_t cnt = 0;
+  uint32_t kl[FUSED ? PER : 1];   // fused: kept tokens of each slot's block (<= G)
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const uint32_t x = u[q];
+    if constexpr (FUSED) kl[q] = 0;
     if (x != kAbsent) {
       const int64_t b = (int64_t)q * NT + tid;
       bool kept = keep_all || b >= wfirst;
       if (!kept && ustar != kAbsent)
         kept = x > ustar || (x == ustar && tie_rank[q] < jtie);
       keep[blk_off + b] = kept ? 1 : 0;
-      if (kept) cnt += (L - b * G) < G ? (L - b * G) : G;
+      if (kept) {
+        const int64_t bl = (L - b * G) < G ? (L - b * G) : G;
+        cnt += bl;
+        if constexpr (FUSED) kl[q] = (uint32_t)bl;
+      }
     }
   }
   const int64_t total = block_sum_i64<NW>(cnt, S);
   if (tid == 0) {
     cu_out[i + 1] = (int32_t)total;
     if (direct) cu_out[0] = 0;
+  }
+  if constexpr (FUSED) {
+    // Destination of block b = kept tokens of blocks 0..b-1.  Blocks are slot-major
+    // (b = q NT + tid): a wave scan per slot, then the slot and wave totals.
+    uint32_t incl[PER];   // within a wave: at most 64 blocks of <= 1024 tokens
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      incl[q] = wave_scan_u32(kl[q]);
+      if (lane == 63) S.dtot[q * NW + wave] = (int64_t)incl[q];
+    }
+    __syncthreads();
+    int64_t before = 0;   // kept tokens of all earlier slots
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      int64_t pre = before, slot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int64_t t = S.dtot[q * NW + w];
+        pre += w < wave ? t : 0;
+        slot += t;
+      }
+      const int64_t b = (int64_t)q * NT + tid;
+      if (b < nb) {
+        fd.dst[b] = kl[q] ? (int32_t)(pre + (int64_t)(incl[q] - kl[q])) : -1;
+        fd.src[b] = (int32_t)(b * G);
+        fd.len[b] = (int32_t)((L - b * G) < G ? (L - b * G) : G);
+      }
+      before += slot;
+    }
+    if (tid == 0) fd.chdr->valid = 1;
   }
 }
 
@@ -488,13 +569,25 @@ hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, i
   if (B == 0) return hipSuccess;
   // One request: its count is cu_out[1] itself, no scan launch needed.
   const int direct = B == 1 ? 1 : 0;
+  const FusedDecision none{};
   if (nb_max <= 256 * kSelPer) {
-    hipLaunchKernelGGL(up_select_kernel<256>, dim3(B), dim3(256), 0, st, scores, cu, B, n, G,
-                       mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err);
+    hipLaunchKernelGGL((up_select_kernel<256, false>), dim3(B), dim3(256), 0, st, scores, cu, B,
+                       n, G, mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err, none);
   } else {
-    hipLaunchKernelGGL(up_select_kernel<1024>, dim3(B), dim3(1024), 0, st, scores, cu, B, n, G,
-                       mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err);
+    hipLaunchKernelGGL((up_select_kernel<1024, false>), dim3(B), dim3(1024), 0, st, scores, cu,
+                       B, n, G, mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err,
+                       none);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_fused(const int32_t* cu, int n, int G, float p, int64_t T_host,
+                               int64_t nb_tot_host, uint8_t* keep, int32_t* cu_out, int* err,
+                               const FusedDecision& fd, hipStream_t st) {
+  static_assert(kFusedSelectMaxBlocks <= 256 * kSelPer, "fused select slots");
+  if (nb_tot_host > kFusedSelectMaxBlocks) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((up_select_kernel<256, true>), dim3(1), dim3(256), 0, st, nullptr, cu, 1, n,
+                     G, 0, p, 0, T_host, nb_tot_host, 1, keep, cu_out, err, fd);
   return hipGetLastError();
 }
 

@@ -115,6 +115,23 @@ hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, i
                          float p, int topk, int nb_max, int64_t T_host, int64_t nb_tot_host,
                          uint8_t* keep, int32_t* cu_out, int* err, hipStream_t st);
 hipError_t launch_select_finalize(int32_t* cu_out, int B, hipStream_t st);
+// The fused form of select for one request of at most 4096 blocks: masses in,
+// normalised scores, keep flags, cu_out and the compaction's block destinations out.
+struct FusedDecision {
+  const double* mass = nullptr;    // float64 block masses of the score pass
+  float* scores = nullptr;         // normalised scores (output)
+  const WsHeader* shdr = nullptr;  // score workspace header
+  WsHeader* chdr = nullptr;        // compaction workspace header (written)
+  int32_t* dst = nullptr;          // per block: destination row or -1
+  int32_t* src = nullptr;          // per block: first source row
+  int32_t* len = nullptr;          // per block: rows
+};
+constexpr int kFusedSelectMaxBlocks = 4096;
+// Whether up_layer_decision may use the fused select (off: see up_layer_decision).
+constexpr bool kFusedSelect = false;
+hipError_t launch_select_fused(const int32_t* cu, int n, int G, float p, int64_t T_host,
+                               int64_t nb_tot_host, uint8_t* keep, int32_t* cu_out, int* err,
+                               const FusedDecision& fd, hipStream_t st);
 
 // Expand + compact (compact.hip).
 struct CompactWs {
@@ -140,10 +157,8 @@ struct AttnShape {
   int64_t tiles;    // attention workgroup tiles of 64 * TT tokens
 };
 struct AttnWs {
-  size_t hdr, po, tp, qr, kr, vt, kn, total;
+  size_t hdr, po, tp, qr, kr, vt, total;
 };
-// Largest Hkv the attention's rotary layout pass supports (per-head LDS slots).
-constexpr int kMaxAttnKvHeads = 256;
 AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp);
 hipError_t launch_attn_plan(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
                             int* err, hipStream_t st);

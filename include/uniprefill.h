@@ -220,6 +220,28 @@ int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
                      const int32_t* count, int capacity, int32_t* orig_out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * 1-4 in one call  ([UP] "Triton kernels" paragraph: the method's steps run as a
+ *    GPU pipeline with no host round trip)
+ *
+ * The decision of up_block_scores + up_topp_select + up_expand_compact (with the
+ * drop composition when prev_orig / orig_out are given), with the same arguments,
+ * outputs and results, made as those three calls in sequence.  (A fused form that
+ * normalises and assigns block destinations inside the select kernel is built but
+ * switched off.)
+ * workspace : at least up_layer_decision_workspace(...) bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------- */
+size_t up_layer_decision_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d,
+                                   int n, int G);
+
+int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens,
+                      const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d, int n, int G,
+                      float scale, float p, const void* hidden, int H, int elem_bytes,
+                      const int32_t* pos, const int32_t* prev_orig, float* scores,
+                      uint8_t* keep_blocks, int32_t* cu_seqlens_out, int32_t* idx_out,
+                      void* hidden_out, int32_t* pos_out, int32_t* orig_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * 5. The layer on the surviving tokens  ([UP] "propagation" paragraph: after a
  *    drop every later layer computes on the survivors only, so its GEMMs shrink
  *    as well as its attention; [UP] "Sparsity Propagation" paragraph: FFN work
@@ -296,7 +318,8 @@ int up_device_error(int32_t* code_h, void* stream);
  * 2 block masses, 3 normalise, 4 select, 5 select finalise, 6 block
  * destinations, 7 gather, 8 compose, 9 plan, 10 given-lse score partials,
  * 11 given-lse finalise, 12 attention plan, 13 rotary layout, 14 attention,
- * 15 SwiGLU gate, 16 hipBLASLt GEMM), the number of launches and their
+ * 15 SwiGLU gate, 16 hipBLASLt GEMM, 17 select with normalisation and block
+ * destinations inside up_layer_decision), the number of launches and their
  * summed duration in milliseconds; up_profile_reset() forgets them.
  * up_profile_enable(0) stops recording.  Not thread safe. */
 int up_profile_enable(int on);
