@@ -252,3 +252,36 @@ def test_linear_swiglu_ffn_reject_bad_arguments(L):
                                                         ctypes.c_size_t, ctypes.c_void_p]
     assert L.up_swiglu_ffn(d, d, d, None, 1000, 4096, 14336, d, d, w - 1, None) == UP_EWORKSPACE
     assert L.up_swiglu_ffn(d, d, d, None, 1000, 4096, 14330, d, d, w, None) == UP_EUNSUPPORTED
+
+
+def test_layer_decision_workspace_and_arguments(L):
+    f = L.up_layer_decision_workspace
+    f.restype = ctypes.c_size_t
+    cu = _cu([131072])
+    ws = f(_p(cu), 1, 32, 8, 128, 128, 64)
+    # the score workspace plus the compaction workspace
+    L.up_block_scores_workspace.restype = ctypes.c_size_t
+    L.up_expand_compact_workspace.restype = ctypes.c_size_t
+    parts = (L.up_block_scores_workspace(_p(cu), 1, 32, 8, 128, 128, 64) +
+             L.up_expand_compact_workspace(_p(cu), 1, 64))
+    assert ws == parts and ws % 256 == 0
+    assert f(_p(cu), 1, 32, 8, 96, 128, 64) == 0      # d unsupported
+    a = L.up_layer_decision
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    a.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, cf, vp, ci, ci, vp, vp, vp, vp, vp,
+                  vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    d = ctypes.c_void_p(4096)
+    base = dict(qwin=d, k=d, cu=d, cu_h=_p(cu), B=1, Hq=32, Hkv=8, dd=128, n=128, G=64, scale=0.0,
+                p=0.99, hidden=d, H=4096, eb=2, pos=d, prev=None, scores=d, keep=d, cu_out=d,
+                idx=d, hout=d, pos_out=d, orig=None, ws=None, wsb=0, st=None)
+    call = lambda **kw: a(*dict(base, **kw).values())
+    assert call(p=0.0) == UP_EINVAL
+    assert call(p=1.5) == UP_EINVAL
+    assert call(H=0) == UP_EINVAL
+    assert call(dd=96) == UP_EUNSUPPORTED
+    assert call() == UP_EWORKSPACE                               # no workspace
+    assert call(ws=ctypes.c_void_p(4096), wsb=ws - 1) == UP_EWORKSPACE
+    assert call(ws=ctypes.c_void_p(4096), wsb=ws, scores=None) == UP_EINVAL
+    assert call(ws=ctypes.c_void_p(4096), wsb=ws, orig=d) == UP_EINVAL   # orig_out without prev_orig
+    assert call(ws=ctypes.c_void_p(4096), wsb=ws, pos=None) == UP_EINVAL  # pos_out without pos
+    assert call(B=0, cu_h=_p(np.zeros(1, np.int32))) == UP_OK
