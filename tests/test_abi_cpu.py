@@ -285,3 +285,18 @@ def test_layer_decision_workspace_and_arguments(L):
     assert call(ws=ctypes.c_void_p(4096), wsb=ws, orig=d) == UP_EINVAL   # orig_out without prev_orig
     assert call(ws=ctypes.c_void_p(4096), wsb=ws, pos=None) == UP_EINVAL  # pos_out without pos
     assert call(B=0, cu_h=_p(np.zeros(1, np.int32))) == UP_OK
+
+
+def test_rope_attention_rejects_more_than_65535_tiles(L):
+    """Workgroup tiles of 64 tokens (4 query heads per kv head) are the grid's y
+    dimension: 65535 tiles are accepted, one more is UP_EUNSUPPORTED."""
+    f = L.up_rope_attention_workspace
+    f.restype = ctypes.c_size_t
+    assert f(_p(_cu([64 * 65535])), 1, 8, 2, 128) > 0
+    assert f(_p(_cu([64 * 65535 + 1])), 1, 8, 2, 128) == 0
+    a = L.up_rope_attention
+    a.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_float] * 2 + \
+                 [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    d = ctypes.c_void_p(4096)
+    cu = _cu([64 * 65535 + 1])
+    assert a(d, d, d, d, d, _p(cu), 1, 8, 2, 128, 0.0, 500000.0, d, None, 0, None) == UP_EUNSUPPORTED

@@ -140,6 +140,31 @@ def test_rope_attention_at_128k_sampled_rows():
     say(f"[ok] 128K sampled rows: worst error / bar {worst:.3f}")
 
 
+@pytest.mark.timeout(900)
+def test_rope_attention_varlen_sampled_rows():
+    """Eight requests of 8K-64K survivors (the continuous-batching shape), Hq=8, Hkv=2,
+    d=128: sampled rows at the start, middle and end of every request against the
+    oracle computed for those rows."""
+    lengths = synth.varlen_lengths(11, 8, 8192, 65536)
+    Hq, Hkv, d = 8, 2, 128
+    say(f"[setup] varlen survivors {lengths}")
+    q, k, v, pos, cu = synth.gen_consumer_attention(lengths, Hq, Hkv, d, 77)
+    R = int(cu[-1])
+    out = up.rope_attention(bf16_dev(q).view(R, Hq, d), bf16_dev(k).view(R, Hkv, d),
+                            bf16_dev(v).view(R, Hkv, d), i32_dev(pos), i32_dev(cu), cu)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    rows = []
+    for i in range(len(lengths)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        rows += [a, a + 63, (a + b) // 2, b - 1]
+    got = out[rows].float().cpu().numpy().astype(np.float64)
+    ref = C.rope_attention_rows(q, k, v, pos, cu, Hq, Hkv, d, 1 / math.sqrt(d), 500000.0, rows)
+    vmax = C.attention_vmax(v, cu, Hkv, d)[rows]
+    worst = _check_attention(got, ref, vmax, Hq, Hkv)
+    say(f"[ok] varlen {R} rows: worst error / bar {worst:.3f}")
+
+
 @pytest.mark.parametrize("R,K,N,res", [(300, 256, 512, False), (1, 128, 64, True),
                                        (4099, 4096, 1024, True)])
 def test_linear_matches_oracle(R, K, N, res):
