@@ -282,11 +282,15 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// 16-byte granule swizzles.  The LDS serves a 16-byte read to 16 lanes per clock over
+// 64 banks; the 16 lanes of a group read 16 consecutive rows at one logical granule,
+// which the XOR spreads over 16 distinct bank groups: by row & 15 for 256-byte rows,
+// by (row >> 1) & 7 for 128-byte rows (odd rows sit half a bank cycle further on).
 template <int D>
 __device__ __forceinline__ int k_swz(int key) {
-  return (D / 8 >= 16) ? (key & 15) : (key & 7);
+  return (D / 8 >= 16) ? (key & 15) : ((key >> 1) & 7);
 }
-__device__ __forceinline__ int v_swz(int row) { return row & 7; }
+__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
 
 constexpr float kRebase = 32.f;
 
