@@ -229,6 +229,10 @@ def main():
         result["two_streams"] = two_streams_leg(up, torch, dec, qwin, k, cu, b, hid, posd, p,
                                                 args)
 
+    # Top-k instead of Top-p (scope: next), with k = the blocks the Top-p cut kept.
+    if not args.headline_only:
+        result["topk"] = topk_leg(up, torch, dec, qwin, k, cu, b, hid, posd, args, stream)
+
     # Keys read through a block table from a paged cache (scope: next), score pass only.
     if not args.headline_only:
         result["paged_keys"] = paged_keys_leg(up, torch, qwin, k, cu, b, args)
@@ -391,6 +395,38 @@ def given_lse_leg(up, torch, dec_full, qwin, k, cu, b, hid, posd, p, args, strea
             "same_keep_as_full_pass": same,
             "note": "scores from given window-row log-sum-exp (up_block_scores_lse); not the "
                     "headline, which computes the row statistics itself"}
+
+
+def topk_leg(up, torch, dec_p, qwin, k, cu, b, hid, posd, args, stream):
+    """The decision with a Top-k cut (k = the number of blocks the headline's Top-p cut
+    kept, so both keep the same number of blocks), timed like the headline."""
+    if b.B != 1:
+        return None
+    kblocks = int(dec_p.keep.sum().item())
+    dec = up.LayerDecision(qwin, k, cu, b.cu_seqlens, hid, posd, b.n, b.G, 1.0, topk=kblocks)
+    for _ in range(args.warmup):
+        dec.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        dec.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    up.profile_reset()
+    up.profile_enable(True)
+    dec.run()
+    torch.cuda.synchronize()
+    up.profile_enable(False)
+    n_, t_ = up.profile_read("select")
+    up.profile_reset()
+    assert up.device_error() == 0
+    same = bool(torch.equal(dec.keep, dec_p.keep))
+    del dec
+    return {"k_blocks": kblocks, "ms_per_step": ms, "tokens_per_s": b.T / (ms * 1e-3),
+            "select_us": round(t_ * 1e3 / max(n_, 1), 2), "same_keep_as_top_p": same,
+            "note": "Top-k cut with k = the Top-p cut's block count; not the headline"}
 
 
 def two_streams_leg(up, torch, dec_a, qwin, k, cu, b, hid, posd, p, args):
