@@ -117,6 +117,30 @@ def _dev(t: torch.Tensor, dtype, name: str):
     return t
 
 
+def _buf(t: torch.Tensor, dtype, min_numel: int, name: str):
+    """A contiguous device tensor of `dtype` with room for `min_numel` elements: the
+    library writes or reads that many through a plain pointer."""
+    _dev(t, dtype, name)
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {min_numel}")
+    return t
+
+
+def _rank(t: torch.Tensor, ndim: int, name: str):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return t
+
+
+def _check_scores_inputs(qwin, k, h, n, d_k_axis=2):
+    """qwin [sum W_i, Hq, d] and token-major keys with the same d."""
+    _rank(qwin, 3, "qwin")
+    if int(qwin.shape[0]) < h.win_rows(n):
+        raise ValueError(f"qwin has {int(qwin.shape[0])} rows, the window needs {h.win_rows(n)}")
+    if int(k.shape[d_k_axis]) != int(qwin.shape[2]):
+        raise ValueError("k and qwin differ in head dimension")
+
+
 class _HostCu:
     """Host copy of cu_seqlens as a C int32 array (kept alive with its pointer)."""
 
@@ -133,6 +157,9 @@ class _HostCu:
 
     def nb_tot(self, G: int) -> int:
         return int(sum((int(L) + G - 1) // G for L in np.diff(self.arr)))
+
+    def win_rows(self, n: int) -> int:
+        return int(sum(min(int(n), int(L)) for L in np.diff(self.arr)))
 
 
 def block_scores_workspace_bytes(cu_h, Hq, Hkv, d, n, G) -> int:
@@ -158,15 +185,20 @@ def block_scores(qwin, k, cu_seqlens, cu_h, n, G, scale=0.0, out=None, workspace
     _dev(k, torch.bfloat16, "k")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     h = _HostCu(cu_h)
+    _check_scores_inputs(qwin, _rank(k, 3, "k"), h, n)
+    if int(k.shape[0]) < h.T:
+        raise ValueError(f"k has {int(k.shape[0])} rows, cu_seqlens needs {h.T}")
     Hq, d = int(qwin.shape[1]), int(qwin.shape[2])
     Hkv = int(k.shape[1])
     if out is None:
         out = torch.empty(h.nb_tot(G), dtype=torch.float32, device=qwin.device)
+    _buf(out, torch.float32, h.nb_tot(G), "out")
     need = int(lib().up_block_scores_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qwin.device)
+    _buf(workspace, torch.uint8, need, "workspace")
     if row_lse is not None:
-        _dev(row_lse, torch.float32, "row_lse")
+        _buf(row_lse, torch.float32, h.win_rows(n) * Hq, "row_lse")
     st = lib().up_block_scores(_ptr(qwin), _ptr(k), _ptr(cu_seqlens), h.ptr, h.B, Hq, Hkv, d, n,
                                G, float(scale), _ptr(out), _ptr(row_lse), _ptr(workspace),
                                workspace.numel(), _stream(stream))
@@ -183,15 +215,21 @@ def block_scores_paged(qwin, k_pages, block_table, cu_seqlens, cu_h, n, G, scale
     _dev(block_table, torch.int32, "block_table")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     h = _HostCu(cu_h)
+    _check_scores_inputs(qwin, _rank(k_pages, 4, "k_pages"), h, n, d_k_axis=3)
+    _rank(block_table, 2, "block_table")
+    if int(block_table.shape[0]) < h.B:
+        raise ValueError("block_table needs one row per request")
     Hq, d = int(qwin.shape[1]), int(qwin.shape[2])
     num_pages, page_size, Hkv = int(k_pages.shape[0]), int(k_pages.shape[1]), int(k_pages.shape[2])
     if out is None:
         out = torch.empty(h.nb_tot(G), dtype=torch.float32, device=qwin.device)
+    _buf(out, torch.float32, h.nb_tot(G), "out")
     need = int(lib().up_block_scores_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qwin.device)
+    _buf(workspace, torch.uint8, need, "workspace")
     if row_lse is not None:
-        _dev(row_lse, torch.float32, "row_lse")
+        _buf(row_lse, torch.float32, h.win_rows(n) * Hq, "row_lse")
     st = lib().up_block_scores_paged(_ptr(qwin), _ptr(k_pages), num_pages, page_size,
                                      _ptr(block_table), int(block_table.shape[1]), _ptr(cu_seqlens),
                                      h.ptr, h.B, Hq, Hkv, d, n, G, float(scale), _ptr(out),
@@ -210,13 +248,19 @@ def block_scores_lse(qwin, k, row_lse, cu_seqlens, cu_h, n, G, scale=0.0, out=No
     _dev(row_lse, torch.float32, "row_lse")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     h = _HostCu(cu_h)
+    _check_scores_inputs(qwin, _rank(k, 3, "k"), h, n)
+    if int(k.shape[0]) < h.T:
+        raise ValueError(f"k has {int(k.shape[0])} rows, cu_seqlens needs {h.T}")
     Hq, d = int(qwin.shape[1]), int(qwin.shape[2])
     Hkv = int(k.shape[1])
+    _buf(row_lse, torch.float32, h.win_rows(n) * Hq, "row_lse")
     if out is None:
         out = torch.empty(h.nb_tot(G), dtype=torch.float32, device=qwin.device)
+    _buf(out, torch.float32, h.nb_tot(G), "out")
     need = int(lib().up_block_scores_lse_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qwin.device)
+    _buf(workspace, torch.uint8, need, "workspace")
     st = lib().up_block_scores_lse(_ptr(qwin), _ptr(k), _ptr(row_lse), _ptr(cu_seqlens), h.ptr,
                                    h.B, Hq, Hkv, d, n, G, float(scale), _ptr(out),
                                    _ptr(workspace), workspace.numel(), _stream(stream))
@@ -228,10 +272,14 @@ def _select(fn, scores, cu_seqlens, cu_h, n, G, arg, keep, cu_out, stream, what)
     _dev(scores, torch.float32, "scores")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     h = _HostCu(cu_h)
+    nbt = h.nb_tot(G)
+    _buf(scores, torch.float32, nbt, "scores")
     if keep is None:
-        keep = torch.empty(h.nb_tot(G), dtype=torch.uint8, device=scores.device)
+        keep = torch.empty(nbt, dtype=torch.uint8, device=scores.device)
     if cu_out is None:
         cu_out = torch.empty(h.B + 1, dtype=torch.int32, device=scores.device)
+    _buf(keep, torch.uint8, nbt, "keep_blocks")
+    _buf(cu_out, torch.int32, h.B + 1, "cu_seqlens_out")
     st = fn(_ptr(scores), _ptr(cu_seqlens), h.ptr, h.B, n, G, arg, _ptr(keep), _ptr(cu_out),
             _stream(stream))
     _check(st, what)
@@ -264,24 +312,37 @@ def expand_compact(hidden, pos, keep, cu_seqlens, cu_out, cu_h, G, idx_out=None,
         _dev(pos, torch.int32, "pos")
     h = _HostCu(cu_h)
     T = h.T
+    _rank(hidden, 2, "hidden")
+    if int(hidden.shape[0]) < T:
+        raise ValueError(f"hidden has {int(hidden.shape[0])} rows, cu_seqlens needs {T}")
     H = int(hidden.shape[1])
     eb = hidden.element_size()
     dev = hidden.device
+    _buf(keep, torch.uint8, h.nb_tot(G), "keep_blocks")
+    _buf(cu_out, torch.int32, h.B + 1, "cu_seqlens_out")
+    if pos is not None:
+        _buf(pos, torch.int32, T, "pos")
     if idx_out is None:
         idx_out = torch.empty(T, dtype=torch.int32, device=dev)
     if hidden_out is None:
         hidden_out = torch.empty((T, H), dtype=hidden.dtype, device=dev)
     if pos_out is None and pos is not None:
         pos_out = torch.empty(T, dtype=torch.int32, device=dev)
+    _buf(idx_out, torch.int32, T, "idx_out")
+    _buf(hidden_out, hidden.dtype, T * H, "hidden_out")
+    if pos_out is not None:
+        _buf(pos_out, torch.int32, T, "pos_out")
     if prev_orig is not None:
-        _dev(prev_orig, torch.int32, "prev_orig")
+        _buf(prev_orig, torch.int32, T, "prev_orig")
         if orig_out is None:
             orig_out = torch.empty(T, dtype=torch.int32, device=dev)
+        _buf(orig_out, torch.int32, T, "orig_out")
     elif orig_out is not None:
         raise ValueError("orig_out needs prev_orig")
     need = int(lib().up_expand_compact_workspace(h.ptr, h.B, G))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _buf(workspace, torch.uint8, need, "workspace")
     st = lib().up_expand_compact(_ptr(hidden), H, eb, _ptr(pos), _ptr(keep), _ptr(cu_seqlens),
                                  _ptr(cu_out), h.ptr, h.B, G, _ptr(idx_out), _ptr(hidden_out),
                                  _ptr(pos_out), _ptr(prev_orig), _ptr(orig_out), _ptr(workspace),
@@ -293,11 +354,12 @@ def expand_compact(hidden, pos, keep, cu_seqlens, cu_out, cu_h, G, idx_out=None,
 def compose_drops(prev_orig, idx, count, capacity=None, out=None, stream=None):
     """orig[r] = prev_orig[idx[r]] for r < *count (count: device int32 scalar view)."""
     _dev(prev_orig, torch.int32, "prev_orig")
-    _dev(idx, torch.int32, "idx")
-    _dev(count, torch.int32, "count")
+    _buf(count, torch.int32, 1, "count")
     cap = int(idx.numel()) if capacity is None else int(capacity)
+    _buf(idx, torch.int32, cap, "idx")
     if out is None:
         out = torch.empty(cap, dtype=torch.int32, device=idx.device)
+    _buf(out, torch.int32, cap, "out")
     st = lib().up_compose_drops(_ptr(prev_orig), int(prev_orig.numel()), _ptr(idx), _ptr(count),
                                 cap, _ptr(out), _stream(stream))
     _check(st, "up_compose_drops")
@@ -345,6 +407,20 @@ class LayerDecision:
         self.n, self.G, self.p, self.scale, self.topk = n, G, p, scale, topk
         dev = qwin.device
         T, B = self.h.T, self.h.B
+        # The one call hands these pointers straight to the library: check them here.
+        _dev(qwin, torch.bfloat16, "qwin")
+        _dev(k, torch.bfloat16, "k")
+        _check_scores_inputs(qwin, _rank(k, 3, "k"), self.h, n)
+        if int(k.shape[0]) < T:
+            raise ValueError(f"k has {int(k.shape[0])} rows, cu_seqlens needs {T}")
+        _buf(cu_seqlens, torch.int32, B + 1, "cu_seqlens")
+        _rank(_dev(hidden, hidden.dtype, "hidden"), 2, "hidden")
+        if int(hidden.shape[0]) < T:
+            raise ValueError(f"hidden has {int(hidden.shape[0])} rows, cu_seqlens needs {T}")
+        if pos is not None:
+            _buf(pos, torch.int32, T, "pos")
+        if prev_orig is not None:
+            _buf(prev_orig, torch.int32, T, "prev_orig")
         nbt = self.h.nb_tot(G)
         Hq, d, Hkv = int(qwin.shape[1]), int(qwin.shape[2]), int(k.shape[1])
         self.scores = torch.empty(nbt, dtype=torch.float32, device=dev)
@@ -415,12 +491,24 @@ def rope_attention(q, k, v, pos, cu_seqlens, cu_h, scale=0.0, rope_theta=500000.
     _dev(pos, torch.int32, "pos")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     h = _HostCu(cu_h)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _rank(t, 3, name)
     Hq, d, Hkv = int(q.shape[1]), int(q.shape[2]), int(k.shape[1])
+    R = h.T
+    if int(q.shape[0]) < R:
+        raise ValueError(f"q has {int(q.shape[0])} rows, cu_seqlens needs {R}")
+    if tuple(k.shape) != tuple(v.shape) or int(k.shape[0]) < R or int(k.shape[2]) != d:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} must both be "
+                         f"[>= {R}, Hkv, {d}]")
+    _buf(pos, torch.int32, R, "pos")
+    _buf(cu_seqlens, torch.int32, h.B + 1, "cu_seqlens")
     if out is None:
         out = torch.empty_like(q)
+    _buf(out, torch.bfloat16, R * Hq * d, "out")
     need = int(lib().up_rope_attention_workspace(h.ptr, h.B, Hq, Hkv, d))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _buf(workspace, torch.uint8, need, "workspace")
     st = lib().up_rope_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(cu_seqlens), h.ptr, h.B,
                                  Hq, Hkv, d, float(scale), float(rope_theta), _ptr(out),
                                  _ptr(workspace), workspace.numel(), _stream(stream))
@@ -430,14 +518,19 @@ def rope_attention(q, k, v, pos, cu_seqlens, cu_h, scale=0.0, rope_theta=500000.
 
 def linear(x, w, residual=None, out=None, workspace=None, stream=None):
     """x [R, K] . w[N, K]^T (+ residual) in bf16 through hipBLASLt; see up_linear."""
-    _dev(x, torch.bfloat16, "x")
-    _dev(w, torch.bfloat16, "w")
+    _rank(_dev(x, torch.bfloat16, "x"), 2, "x")
+    _rank(_dev(w, torch.bfloat16, "w"), 2, "w")
     R, K = int(x.shape[0]), int(x.shape[1])
     N = int(w.shape[0])
+    if int(w.shape[1]) != K:
+        raise ValueError(f"w {tuple(w.shape)} does not match x {tuple(x.shape)}")
     if residual is not None:
-        _dev(residual, torch.bfloat16, "residual")
+        _buf(residual, torch.bfloat16, R * N, "residual")
     if out is None:
         out = torch.empty((R, N), dtype=torch.bfloat16, device=x.device)
+    _buf(out, torch.bfloat16, R * N, "out")
+    if workspace is not None:
+        _dev(workspace, torch.uint8, "workspace")
     nbytes = 0 if workspace is None else workspace.numel()
     st = lib().up_linear(_ptr(x), _ptr(w), _ptr(residual), R, K, N, _ptr(out), _ptr(workspace),
                          nbytes, _stream(stream))
@@ -447,10 +540,13 @@ def linear(x, w, residual=None, out=None, workspace=None, stream=None):
 
 def swiglu(gu, out=None, stream=None):
     """silu(gu[:, :F]) * gu[:, F:] in bf16; see up_swiglu."""
-    _dev(gu, torch.bfloat16, "gu")
+    _rank(_dev(gu, torch.bfloat16, "gu"), 2, "gu")
+    if int(gu.shape[1]) % 2:
+        raise ValueError("gu must hold [gate | up] columns of equal width")
     R, F = int(gu.shape[0]), int(gu.shape[1]) // 2
     if out is None:
         out = torch.empty((R, F), dtype=torch.bfloat16, device=gu.device)
+    _buf(out, torch.bfloat16, R * F, "out")
     _check(lib().up_swiglu(_ptr(gu), R, F, _ptr(out), _stream(stream)), "up_swiglu")
     return out
 
@@ -461,18 +557,23 @@ def swiglu_ffn_workspace_bytes(R, H, F) -> int:
 
 def swiglu_ffn(x, w_gu, w_down, residual=None, out=None, workspace=None, stream=None):
     """SwiGLU FFN: swiglu(x . w_gu^T) . w_down^T (+ residual); see up_swiglu_ffn."""
-    _dev(x, torch.bfloat16, "x")
-    _dev(w_gu, torch.bfloat16, "w_gu")
-    _dev(w_down, torch.bfloat16, "w_down")
+    _rank(_dev(x, torch.bfloat16, "x"), 2, "x")
+    _rank(_dev(w_gu, torch.bfloat16, "w_gu"), 2, "w_gu")
+    _rank(_dev(w_down, torch.bfloat16, "w_down"), 2, "w_down")
     R, H = int(x.shape[0]), int(x.shape[1])
     F = int(w_gu.shape[0]) // 2
+    if int(w_gu.shape[0]) != 2 * F or int(w_gu.shape[1]) != H or tuple(w_down.shape) != (H, F):
+        raise ValueError(f"w_gu must be [2F, {H}] and w_down [{H}, F]; got "
+                         f"{tuple(w_gu.shape)} and {tuple(w_down.shape)}")
     if residual is not None:
-        _dev(residual, torch.bfloat16, "residual")
+        _buf(residual, torch.bfloat16, R * H, "residual")
     if out is None:
         out = torch.empty((R, H), dtype=torch.bfloat16, device=x.device)
+    _buf(out, torch.bfloat16, R * H, "out")
     need = int(lib().up_swiglu_ffn_workspace(R, H, F))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _buf(workspace, torch.uint8, need, "workspace")
     st = lib().up_swiglu_ffn(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(residual), R, H, F, _ptr(out),
                              _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "up_swiglu_ffn")
