@@ -237,6 +237,10 @@ def main():
     if not args.headline_only:
         result["paged_keys"] = paged_keys_leg(up, torch, qwin, k, cu, b, args)
 
+    # One tensor-parallel rank's share of the heads (8 ranks), score pass only.
+    if not args.headline_only:
+        result["tp8_share"] = tp_share_leg(up, torch, qwin, k, cu, b, args, s_us)
+
     # What a plain device-to-device copy of the gather's row bytes reaches on this machine:
     # the practical ceiling the gather's HBM fraction is read against.
     if not args.headline_only:
@@ -462,27 +466,84 @@ def paged_keys_leg(up, torch, qwin, k, cu, b, args, page_size=16):
     pages = torch.empty((npg, page_size) + tuple(k.shape[1:]), dtype=k.dtype, device=k.device)
     pages[perm] = k.view((npg, page_size) + tuple(k.shape[1:]))
     table = perm.to(torch.int32).view(1, npg).contiguous()
+    lse = torch.empty((qwin.shape[0], b.Hq), dtype=torch.float32, device=qwin.device)
+    up.block_scores(qwin, k, cu, b.cu_seqlens, b.n, b.G, row_lse=lse)
     out = {}
-    for name, fn in (("contiguous", lambda: up.block_scores(qwin, k, cu, b.cu_seqlens, b.n, b.G)),
-                     ("paged", lambda: up.block_scores_paged(qwin, pages, table, cu, b.cu_seqlens,
-                                                             b.n, b.G))):
+    legs = (
+        ("contiguous", "score_partial",
+         lambda: up.block_scores(qwin, k, cu, b.cu_seqlens, b.n, b.G)),
+        ("paged", "score_partial",
+         lambda: up.block_scores_paged(qwin, pages, table, cu, b.cu_seqlens, b.n, b.G)),
+        ("lse_contiguous", "score_partial_lse",
+         lambda: up.block_scores_lse(qwin, k, lse, cu, b.cu_seqlens, b.n, b.G)),
+        ("lse_paged", "score_partial_lse",
+         lambda: up.block_scores_lse_paged(qwin, pages, table, lse, cu, b.cu_seqlens, b.n, b.G)),
+    )
+    res = {}
+    for name, kname, fn in legs:
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
         up.profile_reset()
         up.profile_enable(True)
         for _ in range(args.steps):
-            fn()
+            res[name] = fn()
         torch.cuda.synchronize()
         up.profile_enable(False)
-        n_, t_ = up.profile_read("score_partial")
+        n_, t_ = up.profile_read(kname)
         out[name + "_score_us"] = round(t_ * 1e3 / n_, 2)
         up.profile_reset()
-    same = bool(torch.equal(up.block_scores(qwin, k, cu, b.cu_seqlens, b.n, b.G),
-                            up.block_scores_paged(qwin, pages, table, cu, b.cu_seqlens, b.n, b.G)))
     assert up.device_error() == 0
-    out.update({"page_size": page_size, "bit_identical": same})
+    out.update({"page_size": page_size,
+                "bit_identical": bool(torch.equal(res["contiguous"], res["paged"])),
+                "bit_identical_lse": bool(torch.equal(res["lse_contiguous"], res["lse_paged"]))})
     return out
+
+
+def tp_share_leg(up, torch, qwin, k, cu, b, args, score_us_full, tp=8):
+    """The score pass on one tensor-parallel rank's heads (Hq/tp query heads, Hkv/tp kv
+    heads: what each of tp GPUs would run on its own, at its real shape), timed like the
+    headline's score kernel; the all-gather of block masses that would follow is not
+    built (one GPU)."""
+    if b.Hq % tp or b.Hkv % tp:
+        return None
+    hq, hk = b.Hq // tp, b.Hkv // tp
+    q_r, k_r = qwin[:, :hq].contiguous(), k[:, :hk].contiguous()
+    pairs = sum(causal_pairs(int(L), min(b.n, int(L))) for L in np.diff(b.cu_seqlens))
+    flops = 2.0 * b.d * hq * pairs
+    out_s = torch.empty(int(sum((int(L) + b.G - 1) // b.G for L in np.diff(b.cu_seqlens))),
+                        dtype=torch.float32, device=qwin.device)
+    ws = torch.empty(max(1, up.block_scores_workspace_bytes(b.cu_seqlens, hq, hk, b.d, b.n, b.G)),
+                     dtype=torch.uint8, device=qwin.device)
+
+    def run():
+        up.block_scores(q_r, k_r, cu, b.cu_seqlens, b.n, b.G, out=out_s, workspace=ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    call_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    up.profile_reset()
+    up.profile_enable(True)
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    up.profile_enable(False)
+    n_, t_ = up.profile_read("score_partial")
+    s_us = t_ * 1e3 / n_
+    up.profile_reset()
+    assert up.device_error() == 0
+    tf = flops / (s_us * 1e-6) / 1e12
+    return {"tp": tp, "Hq": hq, "Hkv": hk, "score_kernel_us": round(s_us, 2),
+            "score_tflops": round(tf, 2), "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "block_scores_call_us": round(call_us, 2),
+            "full_heads_score_kernel_us": round(score_us_full, 2),
+            "note": "one rank's share of the heads; the cross-rank exchange is not built"}
 
 
 def copy_ceiling_leg(torch, nbytes, gather_us, gather_bytes, reps=20):

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     LayerDecision,
     block_scores,
     block_scores_lse,
+    block_scores_lse_paged,
     block_scores_paged,
     block_scores_lse_workspace_bytes,
     block_scores_workspace_bytes,

@@ -51,6 +51,9 @@ def lib():
     L.up_block_scores_lse.restype = ci
     L.up_block_scores_lse.argtypes = [vp, vp, f32p, i32p, vp, ci, ci, ci, ci, ci, ci, cf, f32p, vp,
                                       cs, vp]
+    L.up_block_scores_lse_paged.restype = ci
+    L.up_block_scores_lse_paged.argtypes = [vp, vp, ctypes.c_int64, ci, i32p, ci, f32p, i32p, vp,
+                                            ci, ci, ci, ci, ci, ci, cf, f32p, vp, cs, vp]
     L.up_topp_select.restype = ci
     L.up_topp_select.argtypes = [f32p, i32p, vp, ci, ci, ci, cf, u8p, i32p, vp]
     L.up_topk_select.restype = ci
@@ -265,6 +268,39 @@ def block_scores_lse(qwin, k, row_lse, cu_seqlens, cu_h, n, G, scale=0.0, out=No
                                    h.B, Hq, Hkv, d, n, G, float(scale), _ptr(out),
                                    _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "up_block_scores_lse")
+    return out
+
+
+def block_scores_lse_paged(qwin, k_pages, block_table, row_lse, cu_seqlens, cu_h, n, G,
+                           scale=0.0, out=None, workspace=None, stream=None):
+    """Block scores from given window-row log-sum-exp with the keys in a paged cache
+    (k_pages and block_table as for block_scores_paged); see up_block_scores_lse_paged."""
+    _dev(qwin, torch.bfloat16, "qwin")
+    _dev(k_pages, torch.bfloat16, "k_pages")
+    _dev(block_table, torch.int32, "block_table")
+    _dev(row_lse, torch.float32, "row_lse")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    h = _HostCu(cu_h)
+    _check_scores_inputs(qwin, _rank(k_pages, 4, "k_pages"), h, n, d_k_axis=3)
+    _rank(block_table, 2, "block_table")
+    if int(block_table.shape[0]) < h.B:
+        raise ValueError("block_table needs one row per request")
+    Hq, d = int(qwin.shape[1]), int(qwin.shape[2])
+    num_pages, page_size, Hkv = int(k_pages.shape[0]), int(k_pages.shape[1]), int(k_pages.shape[2])
+    _buf(row_lse, torch.float32, h.win_rows(n) * Hq, "row_lse")
+    if out is None:
+        out = torch.empty(h.nb_tot(G), dtype=torch.float32, device=qwin.device)
+    _buf(out, torch.float32, h.nb_tot(G), "out")
+    need = int(lib().up_block_scores_lse_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qwin.device)
+    _buf(workspace, torch.uint8, need, "workspace")
+    st = lib().up_block_scores_lse_paged(_ptr(qwin), _ptr(k_pages), num_pages, page_size,
+                                         _ptr(block_table), int(block_table.shape[1]),
+                                         _ptr(row_lse), _ptr(cu_seqlens), h.ptr, h.B, Hq, Hkv, d,
+                                         n, G, float(scale), _ptr(out), _ptr(workspace),
+                                         workspace.numel(), _stream(stream))
+    _check(st, "up_block_scores_lse_paged")
     return out
 
 

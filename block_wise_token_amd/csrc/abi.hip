@@ -284,12 +284,10 @@ int up_block_scores(const void* qwin, const void* k, const int32_t* cu_seqlens,
                              scale, scores, row_lse, workspace, workspace_bytes, stream);
 }
 
-int up_block_scores_paged(const void* qwin, const void* k_pages, int64_t num_pages,
-                          int page_size, const int32_t* block_table, int max_pages,
-                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B, int Hq,
-                          int Hkv, int d, int n, int G, float scale, float* scores,
-                          float* row_lse, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+// Host checks of a paged key cache's description; fills *pk (its error word is set later).
+static int paged_args(const void* k_pages, int64_t num_pages, int page_size,
+                      const int32_t* block_table, int max_pages, const int32_t* cu_seqlens_h,
+                      int B, PagedK* pk) {
   if (page_size < 16 || page_size > 1024 || (page_size & (page_size - 1)) != 0)
     return UP_EUNSUPPORTED;
   if (num_pages < 0 || max_pages < 0) return UP_EINVAL;
@@ -303,13 +301,25 @@ int up_block_scores_paged(const void* qwin, const void* k_pages, int64_t num_pag
   if (need > max_pages) return UP_EINVAL;
   if (need > 0 && (!block_table || num_pages == 0)) return UP_EINVAL;
   if (k_pages && !aligned(k_pages, 16)) return UP_EINVAL;
-  PagedK pk;
-  pk.table = block_table;
-  pk.max_pages = max_pages;
-  pk.num_pages = num_pages;
+  pk->table = block_table;
+  pk->max_pages = max_pages;
+  pk->num_pages = num_pages;
   int lp = 0;
   while ((1 << lp) < page_size) ++lp;
-  pk.log2_page = lp;
+  pk->log2_page = lp;
+  return UP_OK;
+}
+
+int up_block_scores_paged(const void* qwin, const void* k_pages, int64_t num_pages,
+                          int page_size, const int32_t* block_table, int max_pages,
+                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B, int Hq,
+                          int Hkv, int d, int n, int G, float scale, float* scores,
+                          float* row_lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  PagedK pk;
+  const int st = paged_args(k_pages, num_pages, page_size, block_table, max_pages, cu_seqlens_h,
+                            B, &pk);
+  if (st != UP_OK) return st;
   return block_scores_common(qwin, k_pages, &pk, cu_seqlens, cu_seqlens_h, B, Hq, Hkv, d, n, G,
                              scale, scores, row_lse, workspace, workspace_bytes, stream);
 }
@@ -322,10 +332,11 @@ size_t up_block_scores_lse_workspace(const int32_t* cu_seqlens_h, int B, int Hq,
   return score_lse_ws_layout(B, t).total;
 }
 
-int up_block_scores_lse(const void* qwin, const void* k, const float* row_lse,
-                        const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B, int Hq,
-                        int Hkv, int d, int n, int G, float scale, float* scores,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+static int block_scores_lse_common(const void* qwin, const void* k, const PagedK* paged,
+                                  const float* row_lse, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d,
+                                  int n, int G, float scale, float* scores, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   ScoreShape s;
   Totals t;
   const int st = plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t);
@@ -346,13 +357,41 @@ int up_block_scores_lse(const void* qwin, const void* k, const float* row_lse,
     return launch_score_plan(cu_seqlens, s, t, workspace, L.plan, err, hs);
   });
   if (e != hipSuccess) return UP_EHIP;
+  PagedK pk;
+  if (paged) {
+    pk = *paged;
+    pk.err = err;
+  }
   e = timed(10, hs, [&] {
-    return launch_score_partial_lse(qwin, k, row_lse, s, t, workspace, L, c, hs);
+    return launch_score_partial_lse(qwin, k, row_lse, s, t, workspace, L, c,
+                                    paged ? &pk : nullptr, hs);
   });
   if (e != hipSuccess) return UP_EHIP;
   e = timed(11, hs, [&] { return launch_lse_finalize(s, t, workspace, L, scores, hs); });
   if (e != hipSuccess) return UP_EHIP;
   return UP_OK;
+}
+
+int up_block_scores_lse(const void* qwin, const void* k, const float* row_lse,
+                        const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B, int Hq,
+                        int Hkv, int d, int n, int G, float scale, float* scores,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return block_scores_lse_common(qwin, k, nullptr, row_lse, cu_seqlens, cu_seqlens_h, B, Hq,
+                                 Hkv, d, n, G, scale, scores, workspace, workspace_bytes, stream);
+}
+
+int up_block_scores_lse_paged(const void* qwin, const void* k_pages, int64_t num_pages,
+                              int page_size, const int32_t* block_table, int max_pages,
+                              const float* row_lse, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d, int n,
+                              int G, float scale, float* scores, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  PagedK pk;
+  const int st = paged_args(k_pages, num_pages, page_size, block_table, max_pages, cu_seqlens_h,
+                            B, &pk);
+  if (st != UP_OK) return st;
+  return block_scores_lse_common(qwin, k_pages, &pk, row_lse, cu_seqlens, cu_seqlens_h, B, Hq,
+                                 Hkv, d, n, G, scale, scores, workspace, workspace_bytes, stream);
 }
 
 static int select_common(const float* scores, const int32_t* cu_seqlens,

@@ -878,9 +878,14 @@ hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShap
 
 hipError_t launch_score_partial_lse(const void* qwin, const void* k, const float* row_lse,
                                     const ScoreShape& s, const Totals& t, void* ws,
-                                    const ScoreLseWs& L, float c, hipStream_t st) {
-  const PartialOut o{L.plan, nullptr, nullptr, row_lse, reinterpret_cast<float*>(wsb(ws) + L.pm),
-                     PagedK{}};
+                                    const ScoreLseWs& L, float c, const PagedK* paged,
+                                    hipStream_t st) {
+  PartialOut o{L.plan, nullptr, nullptr, row_lse, reinterpret_cast<float*>(wsb(ws) + L.pm),
+               PagedK{}};
+  if (paged) {
+    o.pk = *paged;
+    return launch_partial_d<true, true>(qwin, k, s, t, ws, o, c, st);
+  }
   return launch_partial_d<true, false>(qwin, k, s, t, ws, o, c, st);
 }
 

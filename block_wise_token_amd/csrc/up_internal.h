@@ -98,10 +98,12 @@ hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShap
                                 const PagedK* paged, hipStream_t st);
 hipError_t launch_row_stats(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
                             float* row_lse, hipStream_t st);
-// The given-lse pass: row_lse [sum W_i, Hq] natural-log log-sum-exp of each window row.
+// The given-lse pass: row_lse [sum W_i, Hq] natural-log log-sum-exp of each window row;
+// paged == nullptr: contiguous k, as for launch_score_partial.
 hipError_t launch_score_partial_lse(const void* qwin, const void* k, const float* row_lse,
                                     const ScoreShape& s, const Totals& t, void* ws,
-                                    const ScoreLseWs& L, float c, hipStream_t st);
+                                    const ScoreLseWs& L, float c, const PagedK* paged,
+                                    hipStream_t st);
 hipError_t launch_lse_finalize(const ScoreShape& s, const Totals& t, void* ws,
                                const ScoreLseWs& L, float* scores, hipStream_t st);
 hipError_t launch_block_mass(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,

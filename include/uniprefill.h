@@ -143,6 +143,19 @@ int up_block_scores_lse(const void* qwin, const void* k, const float* row_lse,
                         int Hq, int Hkv, int d, int n, int G, float scale, float* scores,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* The given-lse pass over keys in a paged cache: the last chunk of a chunked prefill
+ * scores its window rows against every earlier chunk's keys where the cache holds
+ * them, with the log-sum-exp its own attention forward produced ([CP]; [UP] "Triton
+ * kernels" paragraph).  k_pages, page_size, block_table, max_pages and num_pages as
+ * for up_block_scores_paged (same checks, same device error bit 8); everything else as
+ * for up_block_scores_lse, whose workspace size applies. */
+int up_block_scores_lse_paged(const void* qwin, const void* k_pages, int64_t num_pages,
+                              int page_size, const int32_t* block_table, int max_pages,
+                              const float* row_lse, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d,
+                              int n, int G, float scale, float* scores, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * 2. Top-p selection  ([UP] "Top-p selection" paragraph: sort blocks by descending
  *    importance and keep them until the cumulative sum reaches p, e.g. 0.99;

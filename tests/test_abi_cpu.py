@@ -198,6 +198,23 @@ def test_block_scores_paged_rejects_bad_arguments(L):
     assert call(npages=-1) == UP_EINVAL
 
 
+def test_block_scores_lse_paged_rejects_bad_arguments(L):
+    cu = _cu([1000, 24])
+    f = L.up_block_scores_lse_paged
+
+    def call(ps=16, maxp=63, table=FAKE, npages=100, lse=FAKE, wsb=1 << 40):
+        return f(FAKE, FAKE, ctypes.c_int64(npages), ps, table, maxp, lse, FAKE, _p(cu), 2, 8, 2,
+                 64, 128, 64, ctypes.c_float(0.0), FAKE, FAKE, ctypes.c_size_t(wsb), None)
+
+    assert call(ps=24) == UP_EUNSUPPORTED
+    assert call(maxp=62) == UP_EINVAL
+    assert call(table=None) == UP_EINVAL
+    assert call(npages=0) == UP_EINVAL
+    assert call(lse=None) == UP_EINVAL
+    assert call(lse=ctypes.c_void_p(0x100002)) == UP_EINVAL
+    assert call(wsb=16) == UP_EWORKSPACE
+
+
 def test_rope_attention_workspace_and_arguments(L):
     f = L.up_rope_attention_workspace
     f.restype = ctypes.c_size_t

@@ -81,6 +81,32 @@ def test_paged_pass_matches_contiguous_and_oracle(case):
     say(f"[ok] paged {case}: bit-identical to contiguous, worst rel err {worst:.2e}")
 
 
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_paged_given_lse_pass_matches_contiguous_and_oracle(case):
+    """The given-lse pass over paged keys: bit-identical to the same pass over the
+    contiguous keys, and within the score bar of the oracle's given-lse scores on the
+    keys gathered from the pages, fed the oracle's own log-sum-exp."""
+    lengths, Hq, Hkv, d, n, G, ps = case
+    b = _batch(lengths, Hq, Hkv, d, n, G, seed=ps + d + len(lengths) + 11)
+    say(f"[case] paged keys, given lse {case}")
+    pages, table = _paginate(b.k, b.cu_seqlens, ps, seed=ps + 1)
+    kk = O.gather_paged_keys(pages, table, b.cu_seqlens, ps)
+    assert np.array_equal(kk, b.k)
+    lse32 = O.row_lse(b.qwin, kk, b.cu_seqlens, Hq, Hkv, d, n).astype(np.float32)
+    gb = GpuBatch(b)
+    lse = torch.from_numpy(lse32).cuda()
+    s_c = up.block_scores_lse(gb.qwin, gb.k, lse, gb.cu, gb.cu_h, n, G)
+    s_p = up.block_scores_lse_paged(gb.qwin, _bf16(pages), i32_dev(table), lse, gb.cu, gb.cu_h,
+                                    n, G)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    assert torch.equal(s_c, s_p)
+    _, s64, _ = O.block_scores_given_lse(b.qwin, kk, lse32.astype(np.float64), b.cu_seqlens,
+                                         Hq, Hkv, d, n, G)
+    worst = check_scores(s_p.cpu().numpy(), s64)
+    say(f"[ok] paged given-lse {case}: bit-identical to contiguous, worst rel err {worst:.2e}")
+
+
 def test_page_index_outside_the_cache_raises_error_bit():
     b = _batch([1000], 8, 2, 64, 128, 64, seed=1)
     pages, table = _paginate(b.k, b.cu_seqlens, 16, seed=3)
@@ -91,6 +117,11 @@ def test_page_index_outside_the_cache_raises_error_bit():
     say("[case] paged keys with out-of-range page indices")
     up.device_error()
     up.block_scores_paged(gb.qwin, _bf16(pages), i32_dev(bad), gb.cu, gb.cu_h, 128, 64)
+    torch.cuda.synchronize()
+    assert up.device_error() & 8
+    lse = torch.empty((b.qwin.shape[0], 8), dtype=torch.float32, device="cuda")
+    up.block_scores(gb.qwin, gb.k, gb.cu, gb.cu_h, 128, 64, row_lse=lse)
+    up.block_scores_lse_paged(gb.qwin, _bf16(pages), i32_dev(bad), lse, gb.cu, gb.cu_h, 128, 64)
     torch.cuda.synchronize()
     assert up.device_error() & 8
     s = up.block_scores_paged(gb.qwin, _bf16(pages), i32_dev(table), gb.cu, gb.cu_h, 128, 64)

@@ -63,6 +63,7 @@ SMALL_CASES = [
     ([1], 4, 2, 128, 128, 64, 0.99),              # a single token
     ([129, 0, 3000, 64, 1], 8, 2, 128, 128, 64, 0.97),   # varlen with an empty request
     ([5000], 16, 2, 128, 256, 64, 0.99),          # 8-query groups, n = 256: two row tiles
+    ([8192], 4, 1, 128, 128, 64, 0.99),           # one rank's heads of the Llama shape, TP = 8
 ]
 
 
