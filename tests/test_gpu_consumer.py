@@ -79,6 +79,21 @@ def test_rope_attention_matches_oracle(case):
     say(f"[ok] {case}: worst error / bar {worst:.3f}")
 
 
+def test_rope_attention_over_many_requests():
+    """120 short requests (0-150 survivors, some empty): the plan's padded offsets and
+    tile offsets over many requests and the tile-to-request search."""
+    rng = np.random.default_rng(44)
+    lengths = [int(x) for x in rng.integers(0, 151, 120)]
+    for j in rng.integers(0, 120, 10):
+        lengths[int(j)] = 0
+    Hq, Hkv, d = 8, 2, 64
+    say(f"[case] rope_attention over {len(lengths)} requests, {sum(lengths)} rows")
+    q, k, v, pos, cu, scale, got = _attention_case(lengths, Hq, Hkv, d, 1.0, seed=44)
+    ref = C.rope_attention(q, k, v, pos, cu, Hq, Hkv, d, scale, 500000.0)
+    worst = _check_attention(got, ref, C.attention_vmax(v, cu, Hkv, d), Hq, Hkv)
+    say(f"[ok] many requests: worst error / bar {worst:.3f}")
+
+
 def test_rope_attention_uses_the_carried_positions():
     """Renumbering the survivors 0..R-1 changes the output; the GPU follows the carried
     positions (checked against the oracle at both)."""

@@ -74,6 +74,18 @@ def test_small_cases_match_oracle(case):
     _full_check(batch, p, H=256, label=f"small {case}")
 
 
+def test_many_requests_full_decision():
+    """150 requests of 0-700 tokens (some empty) through the whole decision: more than
+    two 64-request rounds of the score pass's request lookup, the row-statistics and
+    block-mass searches over many requests, the per-request select with its
+    finalising scan."""
+    rng = np.random.default_rng(33)
+    lengths = rng.integers(0, 701, 150)
+    lengths[rng.integers(0, 150, 12)] = 0
+    batch = _batch([int(x) for x in lengths], 4, 2, 64, 64, 32, needles=1, seed=33)
+    _full_check(batch, 0.9, H=64, label="150 requests")
+
+
 def test_single_4k_workload():
     cfg = synth.WORKLOADS["single_4k_h8_d64"]
     _full_check(synth.make_batch(cfg), cfg["p"], H=cfg["H"], label="single_4k_h8_d64")
