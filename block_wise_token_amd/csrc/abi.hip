@@ -134,29 +134,26 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
   // CU, so the score pass takes ceil(items / slots) rounds, each costing CB blocks of
   // work plus a workgroup's fixed cost (query load, ring fill, chunk-end stores),
   // measured at about kChunkOverheadBlocks blocks: pick the CB that minimises
-  // rounds * (CB + overhead) (ties: the larger CB).  Chunks shorter than
-  // kMinChunkBlocks are considered only for requests that short.  The candidates are
-  // 8..256 in steps of about 1.25x (plus the shortest allowed and the longest
-  // request's block count), which keeps planning linear in B with a small constant.
+  // rounds * (CB + overhead) (ties: the larger CB).  Short requests that leave most
+  // CUs idle get chunks of a few blocks (a 4096-token request: 128 one-block
+  // workgroups rather than 16 of eight blocks, which takes half the time).  The
+  // candidates are 1..256 in steps of about 1.25x (plus the longest request's block
+  // count), which keeps planning linear in B with a small constant.
   (void)units;
   {
     constexpr int kChunkOverheadBlocks = 3;
-    constexpr int kMinChunkBlocks = 8;
     const int64_t cus = (int64_t)device_cus() * score_wgs_per_cu(d);
     int64_t nb_max = 0;
     for (int i = 0; i < B; ++i) {
       const int64_t nb = ((int64_t)cu_h[i + 1] - cu_h[i] + G - 1) / G;
       if (nb > nb_max) nb_max = nb;
     }
-    const int cb_min = (int)(nb_max < kMinChunkBlocks ? (nb_max > 0 ? nb_max : 1) : kMinChunkBlocks);
     static const int kCand[] = {256, 224, 192, 160, 128, 112, 96, 80, 64, 56, 48, 40, 32,
-                                28, 24, 20, 16, 14, 12, 10, 8};
-    int cands[sizeof(kCand) / sizeof(kCand[0]) + 2];
+                                28, 24, 20, 16, 14, 12, 10, 8, 6, 4, 3, 2, 1};
+    int cands[sizeof(kCand) / sizeof(kCand[0]) + 1];
     int nc = 0;
-    for (int cb : kCand)
-      if (cb >= cb_min) cands[nc++] = cb;
-    if (nb_max >= cb_min && nb_max < kMaxChunkBlocks) cands[nc++] = (int)nb_max;
-    cands[nc++] = cb_min;
+    for (int cb : kCand) cands[nc++] = cb;
+    if (nb_max > 1 && nb_max < kMaxChunkBlocks) cands[nc++] = (int)nb_max;
     // Per request: blocks and workgroups per key chunk (kv heads x row tiles).
     std::vector<std::pair<int64_t, int64_t>> req(B);
     for (int i = 0; i < B; ++i) {
@@ -165,7 +162,7 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
       req[i] = {(L + G - 1) / G, Hkv * ((gs * W + s->rows_wg - 1) / s->rows_wg)};
     }
     int64_t best_cost = -1;
-    int best_cb = cb_min;
+    int best_cb = 1;
     for (int ci = 0; ci < nc; ++ci) {
       const int cb = cands[ci];
       int64_t items = 0;

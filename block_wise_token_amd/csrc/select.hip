@@ -538,6 +538,100 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
   }
 }
 
+// Requests of at most 256 blocks (block a in thread a): instead of the digit passes,
+// every block finds its rank in the order (score descending, index ascending) by
+// comparing itself with each block of the request, the scores are placed in rank
+// order in LDS, and one exact integer scan over that order gives each rank the sum
+// of the scores ranked before it.  The block at rank r is in the shortest prefix that
+// reaches p exactly when that sum is still below p (Top-k: when r < k), which is the
+// cut the digit passes find, so both give the same keep flags.
+constexpr int kSmallSelBlocks = 256;
+
+__global__ __launch_bounds__(kSmallSelBlocks) void up_select_small_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ cu, int B, int n, int G,
+    int mode, float p, int topk, int64_t T_host, int64_t nb_tot_host, int direct,
+    uint8_t* __restrict__ keep, int32_t* __restrict__ cu_out, int* __restrict__ err) {
+  constexpr int NT = kSmallSelBlocks, NW = NT / 64;
+  struct Lds {
+    uint32_t u[NT];          // score bits by block
+    uint32_t sorted[NT];     // score bits by rank
+    uint8_t keep_rank[NT];   // kept, by rank
+    U192 wtot192[NW];
+    int64_t red[NW];
+  };
+  __shared__ Lds S;
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  int64_t blk_off = 0;
+  if (!direct) {
+    int64_t part = 0;
+    for (int r = tid; r < i; r += NT) {
+      const int64_t Lr = (int64_t)cu[r + 1] - cu[r];
+      part += Lr > 0 ? (Lr + G - 1) / G : 0;
+    }
+    blk_off = block_sum_i64<NW>(part, S);
+  }
+  const int64_t L = (int64_t)cu[i + 1] - cu[i];
+  const int64_t nb = L > 0 ? (L + G - 1) / G : 0;
+  const bool bad = (L < 0) || ((int64_t)cu[B] != T_host) || (blk_off + nb > nb_tot_host) ||
+                   (nb > NT) || (cu[0] != 0);
+  if (bad) {
+    if (tid == 0) {
+      atomicOr(err, 1);
+      cu_out[i + 1] = 0;
+      if (direct) cu_out[0] = 0;
+    }
+    return;
+  }
+  const bool mine = tid < nb;
+  const uint32_t u = mine ? score_bits(scores[blk_off + tid]) : 0u;
+  S.u[tid] = u;
+  __syncthreads();
+  uint32_t rank = 0;
+  if (mine) {
+    for (int j = 0; j < (int)nb; ++j) {
+      const uint32_t x = S.u[j];
+      rank += (x > u || (x == u && j < tid)) ? 1u : 0u;
+    }
+    S.sorted[rank] = u;
+  }
+  __syncthreads();
+  // Thread r holds rank r: the exact sum of the scores ranked before it, in units of
+  // 2^-149 (a score in [0, 1] is its significand times 2^sh, see sig_of).
+  const bool have = tid < nb;
+  const uint32_t x = have ? S.sorted[tid] : 0u;
+  const U192 v = have ? u192_shl(sig_of(x), shift_of_exp(x >> 23)) : u192_zero();
+  const U192 incl = block_scan_u192<NW>(v, S);
+  const U192 before = u192_sub(incl, v);
+  if (have) {
+    bool k;
+    if (mode == 1) {
+      k = (int64_t)tid < (int64_t)topk;
+    } else if (!(p < 1.0f)) {
+      k = true;
+    } else {
+      const uint32_t pb = __float_as_uint(p);
+      const U192 P = u192_shl(sig_of(pb), shift_of_exp(pb >> 23));
+      k = !u192_geq(before, P);
+    }
+    S.keep_rank[tid] = k ? 1 : 0;
+  }
+  __syncthreads();
+  const int64_t W = L < n ? L : n;
+  const int64_t wfirst = (L - W) / G;   // first block holding a window token
+  int64_t cnt = 0;
+  if (mine) {
+    const bool kept = S.keep_rank[rank] != 0 || (int64_t)tid >= wfirst;
+    keep[blk_off + tid] = kept ? 1 : 0;
+    if (kept) cnt = (L - (int64_t)tid * G) < G ? (L - (int64_t)tid * G) : G;
+  }
+  const int64_t total = block_sum_i64<NW>(cnt, S);
+  if (tid == 0) {
+    cu_out[i + 1] = (int32_t)total;
+    if (direct) cu_out[0] = 0;
+  }
+}
+
 // In-place inclusive scan of the per-request kept counts in cu_out[1..B]; cu_out[0] = 0.
 __global__ __launch_bounds__(1024) void up_select_finalize_kernel(int32_t* __restrict__ cu_out,
                                                                   int B) {
@@ -570,7 +664,10 @@ hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, i
   // One request: its count is cu_out[1] itself, no scan launch needed.
   const int direct = B == 1 ? 1 : 0;
   const FusedDecision none{};
-  if (nb_max <= 256 * kSelPer) {
+  if (nb_max <= kSmallSelBlocks) {
+    hipLaunchKernelGGL(up_select_small_kernel, dim3(B), dim3(kSmallSelBlocks), 0, st, scores, cu,
+                       B, n, G, mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err);
+  } else if (nb_max <= 256 * kSelPer) {
     hipLaunchKernelGGL((up_select_kernel<256, false>), dim3(B), dim3(256), 0, st, scores, cu, B,
                        n, G, mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err, none);
   } else {
