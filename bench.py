@@ -237,6 +237,11 @@ def main():
     if not args.headline_only:
         result["paged_keys"] = paged_keys_leg(up, torch, qwin, k, cu, b, args)
 
+    # The other cut thresholds of the 128K configuration.
+    if not args.headline_only and args.workload == "llama31_8b_128k" and args.p is None:
+        result["p_sweep"] = p_sweep_leg(up, torch, qwin, k, cu, b, hid, posd, args, stream,
+                                        row_bytes)
+
     # The decision captured once into a HIP graph and replayed.
     if not args.headline_only:
         result["graph"] = graph_leg(up, torch, dec, args, T)
@@ -548,6 +553,40 @@ def tp_share_leg(up, torch, qwin, k, cu, b, args, score_us_full, tp=8):
             "block_scores_call_us": round(call_us, 2),
             "full_heads_score_kernel_us": round(score_us_full, 2),
             "note": "one rank's share of the heads; the cross-rank exchange is not built"}
+
+
+def p_sweep_leg(up, torch, qwin, k, cu, b, hid, posd, args, stream, row_bytes):
+    """The same decision at the other cut thresholds of the 128K configuration: step
+    time, kept fraction and the gather's rate (fewer kept rows, fewer bytes)."""
+    out = {}
+    for p in (0.95, 0.999):
+        dec = up.LayerDecision(qwin, k, cu, b.cu_seqlens, hid, posd, b.n, b.G, p)
+        for _ in range(args.warmup):
+            dec.run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            dec.run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        up.profile_reset()
+        up.profile_enable(True)
+        for _ in range(args.steps):
+            dec.run()
+        torch.cuda.synchronize()
+        up.profile_enable(False)
+        n_, t_ = up.profile_read("gather")
+        g_us = t_ * 1e3 / n_
+        up.profile_reset()
+        assert up.device_error() == 0
+        kept = int(dec.cu_out[-1].item())
+        gbytes = kept * (2 * row_bytes + 12 + 8)
+        out[str(p)] = {"ms_per_step": round(ms, 4), "tokens_per_s": b.T / (ms * 1e-3),
+                       "rho": kept / b.T, "gather_us": round(g_us, 2),
+                       "gather_GBps": round(gbytes / (g_us * 1e-6) / 1e9, 1)}
+    return out
 
 
 def graph_leg(up, torch, dec_big, args, T_big, reps=50):

@@ -269,6 +269,44 @@ def test_inconsistent_compaction_inputs_write_nothing():
         assert torch.all(keep2 == 7)
 
 
+@pytest.mark.parametrize("dtype,H", [(torch.uint8, 33), (torch.float32, 3), (torch.bfloat16, 6),
+                                     (torch.float64, 5), (torch.int16, 4096)])
+def test_compaction_of_rows_of_any_width(dtype, H):
+    """Rows whose byte width is not a multiple of 16 (or of 4) take the gather's 4-byte
+    and 1-byte paths; every width must give the rows the oracle's expansion names, bit
+    for bit, with positions and composed indices."""
+    G, lens = 64, [1000, 0, 777, 64, 3000]
+    cu_h = np.zeros(len(lens) + 1, np.int32)
+    cu_h[1:] = np.cumsum(lens)
+    T = int(cu_h[-1])
+    nbs = [O.n_blocks(L, G) for L in lens]
+    rng = np.random.default_rng(H)
+    keep = (rng.random(sum(nbs)) < 0.6).astype(np.uint8)
+    cnt = [0] + [int(sum(min(G, L - b * G) for b in range(nb) if keep[sum(nbs[:i]) + b]))
+                 for i, (L, nb) in enumerate(zip(lens, nbs))]
+    cu_out = np.cumsum(cnt).astype(np.int32)
+    raw = rng.integers(0, 256, (T, H * torch.tensor([], dtype=dtype).element_size()),
+                       dtype=np.uint8)
+    hid = torch.from_numpy(raw).cuda().view(dtype).view(T, H)
+    pos = rng.integers(0, 1 << 30, T).astype(np.int32)
+    prev = rng.integers(0, 1 << 30, T).astype(np.int32)
+    say(f"[case] compaction of {H} x {dtype} rows ({hid.element_size() * H} bytes)")
+    orig = torch.empty(T, dtype=torch.int32, device="cuda")
+    idx_out, hid_out, pos_out = up.expand_compact(
+        hid, i32_dev(pos), torch.from_numpy(keep).cuda(), i32_dev(cu_h), i32_dev(cu_out), cu_h, G,
+        prev_orig=i32_dev(prev), orig_out=orig)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    idx_ref = O.expand(keep, cu_h, G)
+    n = int(cu_out[-1])
+    assert idx_ref.size == n
+    np.testing.assert_array_equal(idx_out[:n].cpu().numpy(), idx_ref)
+    got = hid_out[:n].contiguous().view(torch.uint8).view(n, -1).cpu().numpy()
+    np.testing.assert_array_equal(got, raw[idx_ref])
+    np.testing.assert_array_equal(pos_out[:n].cpu().numpy(), pos[idx_ref])
+    np.testing.assert_array_equal(orig[:n].cpu().numpy(), prev[idx_ref])
+
+
 def test_many_short_requests_select_and_compact():
     """2500 requests (more than one 1024-request chunk of the compaction scan), lengths
     0..300 with empty ones, G = 32: select and compaction against the oracle."""
