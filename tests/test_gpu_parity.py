@@ -64,6 +64,9 @@ SMALL_CASES = [
     ([129, 0, 3000, 64, 1], 8, 2, 128, 128, 64, 0.97),   # varlen with an empty request
     ([5000], 16, 2, 128, 256, 64, 0.99),          # 8-query groups, n = 256: two row tiles
     ([8192], 4, 1, 128, 128, 64, 0.99),           # one rank's heads of the Llama shape, TP = 8
+    ([20000], 8, 2, 128, 100, 1024, 0.7),         # G = 1024 (largest block), window not 32-aligned
+    ([7777], 4, 1, 64, 33, 512, 0.9),             # G = 512, n = 33
+    ([3000], 8, 2, 256, 128, 32, 0.9),            # d = 256 with G = 32
 ]
 
 
