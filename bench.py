@@ -237,6 +237,10 @@ def main():
     if not args.headline_only:
         result["paged_keys"] = paged_keys_leg(up, torch, qwin, k, cu, b, args)
 
+    # Every layer of a multi-layer workload, drops composed across layers.
+    if not args.headline_only and cfg.get("layers", 1) > 1:
+        result["stack"] = stack_leg(up, torch, cfg, b, hid, posd, p, args)
+
     # The other cut thresholds of the 128K configuration.
     if not args.headline_only and args.workload == "llama31_8b_128k" and args.p is None:
         result["p_sweep"] = p_sweep_leg(up, torch, qwin, k, cu, b, hid, posd, args, stream,
@@ -587,6 +591,56 @@ def p_sweep_leg(up, torch, qwin, k, cu, b, hid, posd, args, stream, row_bytes):
                        "rho": kept / b.T, "gather_us": round(g_us, 2),
                        "gather_GBps": round(gbytes / (g_us * 1e-6) / 1e9, 1)}
     return out
+
+
+def stack_leg(up, torch, cfg, b0, hid, posd, p, args):
+    """Every full-attention layer of a multi-layer workload: layer l scores fresh Q/K
+    drawn over the survivors of layer l-1, compacts them and composes the drops (the
+    original indices travel with the rows).  Each layer's decision is timed like the
+    headline."""
+    from workloads import synth
+    dev = hid.device
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    T0 = b0.T
+    orig = torch.arange(T0, dtype=torch.int32, device=dev)
+    orig_np = np.arange(T0, dtype=np.int32)
+    layers, total = [], 0.0
+    for layer in range(cfg["layers"]):
+        if layer == 0:
+            b = b0
+        else:
+            req = synth.gen_layer(orig_np, T0, b0.needles[0], cfg["Hq"], cfg["Hkv"], cfg["d"],
+                                  cfg["n"], cfg["G"], cfg["seed"], layer)
+            b = synth.pack([req], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["n"], cfg["G"])
+        L = b.T
+        cu = torch.from_numpy(b.cu_seqlens).to(dev)
+        dec = up.LayerDecision(bf16(b.qwin), bf16(b.k), cu, b.cu_seqlens, hid, posd, b.n, b.G, p,
+                               prev_orig=orig)
+        for _ in range(args.warmup):
+            dec.run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            dec.run()
+        e1.record()
+        torch.cuda.synchronize()
+        assert up.device_error() == 0
+        ms = e0.elapsed_time(e1) / args.steps
+        kept = int(dec.cu_out[-1].item())
+        layers.append({"layer": layer, "tokens": L, "kept": kept, "ms": round(ms, 4),
+                       "tokens_per_s": L / (ms * 1e-3)})
+        total += ms
+        hid, posd = dec.hidden_out[:kept].clone(), dec.pos_out[:kept].clone()
+        orig = dec.orig[:kept].clone()
+        orig_np = orig.cpu().numpy()
+        del dec
+    last_kept_orig_ok = bool(np.array_equal(orig_np[-b0.n:], np.arange(T0 - b0.n, T0)))
+    return {"layers": layers, "total_ms": round(total, 4), "final_tokens": int(orig_np.size),
+            "window_survives": last_kept_orig_ok,
+            "note": "each layer's decision timed on its own inputs; not the headline"}
 
 
 def graph_leg(up, torch, dec_big, args, T_big, reps=50):
