@@ -261,7 +261,7 @@ def main():
 
     # The layer that then runs on the survivors (scope: next), against the same layer on
     # every token.
-    if not args.headline_only and b.d in (64, 128):
+    if not args.headline_only and b.d in (64, 128, 256):
         result["consumer"] = consumer_leg(up, torch, dec, hid, b, cfg)
 
     if not args.no_cpu_baseline:
@@ -276,7 +276,8 @@ def consumer_leg(up, torch, dec, hid, b, cfg, reps=2):
     0..N-1).  Weights and inputs are seeded; nothing here is part of `value`."""
     import math
     H, Hq, Hkv, d = cfg["H"], b.Hq, b.Hkv, b.d
-    F = 14336 if H == 4096 else int(round(3.5 * H / 256)) * 256   # Llama-3.1-8B FFN width
+    # FFN width: Llama-3.1-8B's for H = 4096, Gemma-3-12B's for H = 3840.
+    F = {4096: 14336, 3840: 15360}.get(H, int(round(3.5 * H / 256)) * 256)
     dev = hid.device
     g = torch.Generator(device=dev).manual_seed(20260)
 

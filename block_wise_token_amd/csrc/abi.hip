@@ -567,12 +567,12 @@ namespace {
 int plan_attention(const int32_t* cu_h, int B, int Hq, int Hkv, int d, AttnShape* s) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return UP_EINVAL;
   if (!cu_ok(cu_h, B)) return UP_EINVAL;
-  if (d != 64 && d != 128) return UP_EUNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return UP_EUNSUPPORTED;
   const int gsz = Hq / Hkv;
   s->B = B; s->Hq = Hq; s->Hkv = Hkv; s->d = d;
   s->HQ = gsz % 4 == 0 ? 4 : (gsz % 2 == 0 ? 2 : 1);
   s->TT = 4 / s->HQ;
-  const int tok_tile = 64 * s->TT;
+  const int tok_tile = attn_tile_tokens(d) * s->TT;
   int64_t Rp = 0, tiles = 0;
   for (int i = 0; i < B; ++i) {
     const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];

@@ -562,6 +562,245 @@ __global__ __launch_bounds__(256, 1) void up_attention_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The same attention at d = 256.  A 64-token stage of K and V^T would take 64 KiB
+// there and the O accumulator of two 32-row query tiles 256 registers, so the tiling
+// is halved: each wave holds one 32-row query tile (tiles of 32 tokens; HQ heads x TT
+// tiles per workgroup, HQ * TT = 4) and the ring holds four stages of 32 keys (K
+// [32][256] and V^T [256][32], 32 KiB each).  A stage is one half-step, and a
+// half-step's body issues the next stage's S^T, so each stage is waited for and
+// published before the body that first reads it.  The 64-byte V^T rows keep granule
+// g of row r at g ^ ((r >> 2) & 3), which spreads the 16 rows one 16-lane group
+// reads over all 64 banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int v64_swz(int row) { return (row >> 2) & 3; }
+
+__global__ __launch_bounds__(256, 1) void up_attention_d256_kernel(
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
+    const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
+    const int32_t* __restrict__ tp, int B, int Hq, int Hkv, int HQ, int TT, int64_t Rp,
+    float c, uint16_t* __restrict__ out) {
+  constexpr int D = 256, NT = 256, NS = 4, UK = 32;
+  constexpr int DS = D / 16;             // MFMA k-steps over the head dimension
+  constexpr int DT = D / 32;             // 32-row tiles of O^T
+  constexpr int KRB = 2 * D;             // K tile row bytes
+  constexpr int KB = UK * KRB;           // K tile bytes
+  constexpr int VRB = 2 * UK;            // V^T tile row bytes
+  constexpr int VB = D * VRB;            // V^T tile bytes
+  constexpr int SB = KB + VB;            // stage bytes
+  constexpr int KSPT = KB / (NT * 16);   // DMA copies per lane per stage, K
+  constexpr int VSPT = VB / (NT * 16);   // and V^T
+  constexpr int SPT = KSPT + VSPT;
+  static_assert(KB % (NT * 16) == 0 && VB % (NT * 16) == 0, "whole DMA rounds");
+  static_assert(2 * SPT < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
+
+  if (hdr->valid != 1) return;
+  const int gsz = Hq / Hkv, quads = gsz / HQ;
+  const int g = blockIdx.x / quads, quad = blockIdx.x - g * quads;
+  const int f = blockIdx.y;
+  const int i = request_of(tp, B, f);
+  const int L = cu[i + 1] - cu[i];
+  const int nwt = tp[i + 1] - tp[i];
+  const int wt = nwt - 1 - (f - tp[i]);   // heaviest tile first
+  const int ntile = (L + 31) >> 5;        // 32-token tiles of the request
+  const int tile0 = wt * TT;
+  const int nst = min(tile0 + TT, ntile);   // 32-key stages of this workgroup
+  const int64_t pbase = po[i];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5,
+            l32 = lane & 31;
+  const int head = g * gsz + quad * HQ + wave % HQ;
+  const int tw = tile0 + wave / HQ;   // this wave's 32-token tile (its diagonal stage)
+  const bool wact = tw < ntile;
+
+  // Query operand (one 32-row tile), the head dimension in the permuted order both
+  // operands share: lane half h, k-step s covers d-elements [h D/2 + 8 s, +8).
+  bf16x8 qreg[DS];
+  if (wact) {
+    const uint16_t* src = qr + ((int64_t)head * Rp + pbase + tw * 32 + l32) * D + half * (D / 2);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(src + s * 8);
+  } else {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qreg[s] = bf16x8{};
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): only stage copies from here
+
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8*)lds;
+  const uint16_t* kbase = kr + ((int64_t)g * Rp + pbase) * D;
+  const uint16_t* vbase = vt + (int64_t)g * D * Rp + pbase;
+  auto issue = [&](int st) {
+    const uint32_t sb = lds_base + (uint32_t)((st & (NS - 1)) * SB);
+    const uint16_t* kst = kbase + (int64_t)st * UK * D;
+#pragma unroll
+    for (int q = 0; q < KSPT; ++q) {
+      const int o = q * NT * 16 + tid * 16;
+      const int key = o / KRB;
+      const int gr = ((o % KRB) / 16) ^ k_swz<D>(key);
+      lds_dma16(kst + key * D + gr * 8,
+                __builtin_amdgcn_readfirstlane(sb + q * NT * 16 + wave * 1024));
+    }
+    const uint16_t* vst = vbase + (int64_t)st * UK;
+#pragma unroll
+    for (int q = 0; q < VSPT; ++q) {
+      const int o = q * NT * 16 + tid * 16;
+      const int row = o / VRB;
+      const int gr = ((o % VRB) / 16) ^ v64_swz(row);
+      lds_dma16(vst + (int64_t)row * Rp + gr * 8,
+                __builtin_amdgcn_readfirstlane(sb + KB + q * NT * 16 + wave * 1024));
+    }
+  };
+
+  uint32_t krd[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) krd[s] = l32 * KRB + 16 * ((half * DS + s) ^ k_swz<D>(l32));
+  // V^T row dt * 32 + l32 has the swizzle of l32 (dt * 32 is a multiple of 16 rows).
+  uint32_t vrd[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) vrd[jj] = KB + l32 * VRB + 16 * ((2 * jj + half) ^ v64_swz(l32));
+
+  float Rs = 0.f, lsum = 0.f;
+  f32x16 O[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
+  const int qtok = tw * 32 + l32;
+
+  // S^T of stage (= half-step) hs into acc.
+  auto s_mfma = [&](int hs, f32x16& acc) {
+    const uint8_t* sl = lds + (hs & (NS - 1)) * SB;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sl + krd[s]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], s == 0 ? f32x16{} : acc, 0, 0, 0);
+    }
+  };
+  // Causal mask of the diagonal stage (keys past the query -> -inf).
+  auto mask = [&](int hs, f32x16& acc) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = hs * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+      if (key > qtok) acc[e] = kNegInf;
+    }
+  };
+  auto rebase = [&](const f32x16& acc, bool init) {
+    float m0 = kNegInf, m1 = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      m0 = fmaxf(m0, acc[e]);
+      m1 = fmaxf(m1, acc[e + 1]);
+    }
+    const float mx = pair_max(fmaxf(m0, m1)) * c;
+    const bool need = init || mx > Rs + kRebase;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      if (init) {
+        Rs = mx;
+      } else {
+        const float rn = fmaxf(Rs, mx);
+        const float sc = __builtin_amdgcn_exp2f(Rs - rn);
+        lsum *= sc;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[dt] *= sc;
+        Rs = rn;
+      }
+    }
+  };
+  // Softmax of stage hs (S^T in acc) and O^T += V^T P^T over its 32 keys.
+  auto pv = [&](int hs, const f32x16& acc) {
+    const uint8_t* sl = lds + (hs & (NS - 1)) * SB;
+    bf16x8 va[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        va[dt][jj] = *reinterpret_cast<const bf16x8*>(sl + dt * 32 * VRB + vrd[jj]);
+    f32x16 p;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      p[e] = __builtin_amdgcn_exp2f(fmaf(acc[e], c, -Rs));
+      p[e + 1] = __builtin_amdgcn_exp2f(fmaf(acc[e + 1], c, -Rs));
+      s0 += p[e];
+      s1 += p[e + 1];
+    }
+    lsum += s0 + s1;
+    const bf16x8 pb[2] = {__builtin_convertvector(p.lo, bf16x8),
+                          __builtin_convertvector(p.hi, bf16x8)};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][jj], pb[jj], O[dt], 0, 0, 0);
+  };
+
+  // Ring: while body(st) reads stages st and st+1, stages st+2 and st+3 are in flight.
+  // Before body(st): wait for stage st+1 (stage st+2, issued earlier, may stay in
+  // flight), publish it with a barrier -- after which every wave is done with stage
+  // st-1 -- and refill that slot with stage st+3.
+  auto sync_for = [&](int st) {
+    if (st + 1 >= nst) return;
+    if (st + 2 < nst) wait_barrier<SPT>();
+    else wait_barrier<0>();
+    if (st + 3 < nst) issue(st + 3);
+  };
+
+  issue(0);
+  if (nst > 1) issue(1);
+  if (nst > 2) issue(2);
+  if (nst > 2) wait_barrier<2 * SPT>();
+  else if (nst > 1) wait_barrier<SPT>();
+  else wait_barrier<0>();
+
+  f32x16 accA, accB;
+  if (wact) {
+    s_mfma(0, accA);
+    if (tw == 0) mask(0, accA);
+    rebase(accA, true);
+  }
+  // cur holds S^T of stage hs; nxt receives stage hs+1's (waited for by the caller).
+  auto body = [&](int hs, f32x16& cur, f32x16& nxt) {
+    if (!wact || hs > tw) return;
+    if (hs + 1 < tw) {
+      s_mfma(hs + 1, nxt);
+      pv(hs, cur);
+      rebase(nxt, false);
+    } else if (hs + 1 == tw) {
+      s_mfma(hs + 1, nxt);
+      pv(hs, cur);
+      mask(hs + 1, nxt);
+      rebase(nxt, false);
+    } else {
+      pv(hs, cur);
+    }
+  };
+  for (int st = 0; st < nst; st += 2) {
+    sync_for(st);
+    body(st, accA, accB);
+    if (st + 1 < nst) {
+      sync_for(st + 1);
+      body(st + 1, accB, accA);
+    }
+  }
+
+  if (!wact) return;
+  const float inv = 1.f / pair_sum(lsum);
+  if (qtok >= L) return;
+  uint16_t* dst = out + (((int64_t)cu[i] + qtok) * Hq + head) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int eg = 0; eg < 4; ++eg) {
+      const int dv = dt * 32 + 8 * eg + 4 * half;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      const f32x4 o4 = {O[dt][4 * eg] * inv, O[dt][4 * eg + 1] * inv, O[dt][4 * eg + 2] * inv,
+                        O[dt][4 * eg + 3] * inv};
+      *reinterpret_cast<bf16x4*>(dst + dv) = __builtin_convertvector(o4, bf16x4);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // SwiGLU gate: a[r][j] = silu(gu[r][j]) * gu[r][F + j] in float32, rounded to
 // bfloat16.  Eight columns per thread, grid-stride.
 // ---------------------------------------------------------------------------
@@ -611,7 +850,8 @@ AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp) {
 hipError_t launch_attn_plan(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
                             int* err, hipStream_t st) {
   char* w = static_cast<char*>(ws);
-  hipLaunchKernelGGL(up_attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, cu, s.B, 64 * s.TT,
+  hipLaunchKernelGGL(up_attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, cu, s.B,
+                     attn_tile_tokens(s.d) * s.TT,
                      s.R, s.Rp, s.tiles, reinterpret_cast<WsHeader*>(w + L.hdr),
                      reinterpret_cast<int32_t*>(w + L.po), reinterpret_cast<int32_t*>(w + L.tp),
                      err);
@@ -634,8 +874,11 @@ hipError_t launch_rope_layout(const void* q, const void* k, const void* v, const
   if (s.d == 64)
     hipLaunchKernelGGL(up_rope_layout_kernel<64>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr, cu,
                        po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
-  else
+  else if (s.d == 128)
     hipLaunchKernelGGL(up_rope_layout_kernel<128>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr,
+                       cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
+  else
+    hipLaunchKernelGGL(up_rope_layout_kernel<256>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr,
                        cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
   return hipGetLastError();
 }
@@ -654,8 +897,11 @@ hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, con
   if (s.d == 64)
     hipLaunchKernelGGL(up_attention_kernel<64>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
                        tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
-  else
+  else if (s.d == 128)
     hipLaunchKernelGGL(up_attention_kernel<128>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
+                       tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+  else
+    hipLaunchKernelGGL(up_attention_d256_kernel, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
                        tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
   return hipGetLastError();
 }

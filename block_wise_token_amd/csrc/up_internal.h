@@ -152,11 +152,14 @@ hipError_t launch_compose(const int32_t* prev, int prev_len, const int32_t* idx,
                           hipStream_t st);
 
 // Layer on the surviving tokens (consumer.hip).
+// Query tokens per wave in the attention kernel: 64 (two 32-row tiles) up to d = 128,
+// 32 at d = 256.
+constexpr int attn_tile_tokens(int d) { return d == 256 ? 32 : 64; }
 struct AttnShape {
   int B, Hq, Hkv, d;
-  int HQ, TT;       // query heads and 64-token tiles per attention workgroup (HQ * TT = 4)
+  int HQ, TT;       // query heads and per-wave token tiles per attention workgroup (HQ * TT = 4)
   int64_t R, Rp;    // rows; padded rows (every request rounded up to 64)
-  int64_t tiles;    // attention workgroup tiles of 64 * TT tokens
+  int64_t tiles;    // attention workgroup tiles of attn_tile_tokens(d) * TT tokens
 };
 struct AttnWs {
   size_t hdr, po, tp, qr, kr, vt, total;

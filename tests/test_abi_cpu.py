@@ -223,7 +223,8 @@ def test_rope_attention_workspace_and_arguments(L):
     ws = f(_p(cu), 4, 8, 2, 128)
     # rotated q (Hq) and k (Hkv), transposed v (Hkv), all over 64-row padded requests
     assert ws >= (8 + 2 + 2) * Rp * 128 * 2 and ws % 256 == 0
-    assert f(_p(cu), 4, 8, 2, 256) == 0      # d unsupported
+    assert f(_p(cu), 4, 8, 2, 192) == 0      # d unsupported
+    assert f(_p(cu), 4, 8, 2, 256) >= (8 + 2 + 2) * Rp * 256 * 2   # d = 256 supported
     assert f(_p(cu), 4, 8, 3, 128) == 0      # Hq % Hkv
     bad = _cu([5, 3])
     bad[1] = 9; bad[2] = 4                   # decreasing offsets
@@ -311,6 +312,9 @@ def test_rope_attention_rejects_more_than_65535_tiles(L):
     f.restype = ctypes.c_size_t
     assert f(_p(_cu([64 * 65535])), 1, 8, 2, 128) > 0
     assert f(_p(_cu([64 * 65535 + 1])), 1, 8, 2, 128) == 0
+    # at d = 256 a wave holds 32 query tokens, so a tile spans 32 of them
+    assert f(_p(_cu([32 * 65535])), 1, 8, 2, 256) > 0
+    assert f(_p(_cu([32 * 65535 + 1])), 1, 8, 2, 256) == 0
     a = L.up_rope_attention
     a.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_float] * 2 + \
                  [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]

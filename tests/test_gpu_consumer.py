@@ -43,6 +43,11 @@ CASES = [
     ([150], 16, 2, 128, 1.0),                  # eight per kv head: two workgroups per kv head
     ([700], 8, 2, 128, 12.0),                  # large logits: the reference rebases often
     ([513], 4, 2, 64, 30.0),                   # very large logits, nearly one-hot rows
+    ([200], 16, 8, 256, 1.0),                  # d = 256, Gemma-like GQA: 32-token tiles
+    ([300, 0, 65, 129, 1], 8, 2, 256, 1.0),    # d = 256, varlen with empty and ragged requests
+    ([130], 8, 8, 256, 1.0),                   # d = 256, one query head per kv head
+    ([190], 16, 4, 256, 1.0),                  # d = 256, four query heads per kv head
+    ([700], 4, 2, 256, 12.0),                  # d = 256, large logits: many rebases
 ]
 
 
@@ -136,17 +141,19 @@ def test_rope_attention_is_deterministic_and_rejects_bad_cu():
 
 
 @pytest.mark.timeout(900)
-def test_rope_attention_at_128k_sampled_rows():
-    """The Llama-3.1-8B shape at 129600 survivors (p = 0.99 of 128K): sampled rows of the
-    GPU output against the oracle computed for those rows alone."""
-    R, Hq, Hkv, d = 129600, 32, 8, 128
-    say("[setup] generating 129600 survivors, Hq=32, Hkv=8, d=128")
+@pytest.mark.parametrize("R,Hq,Hkv,d", [(129600, 32, 8, 128), (129344, 16, 8, 256)],
+                         ids=["llama_d128", "gemma_like_d256"])
+def test_rope_attention_at_128k_sampled_rows(R, Hq, Hkv, d):
+    """The Llama-3.1-8B shape at 129600 survivors and the Gemma-like d = 256 shape at
+    129344 (what p = 0.99 keeps of 128K in each): sampled rows of the GPU output against
+    the oracle computed for those rows alone."""
+    say(f"[setup] generating {R} survivors, Hq={Hq}, Hkv={Hkv}, d={d}")
     q, k, v, pos, cu = synth.gen_consumer_attention([R], Hq, Hkv, d, 2026)
     out = up.rope_attention(bf16_dev(q).view(R, Hq, d), bf16_dev(k).view(R, Hkv, d),
                             bf16_dev(v).view(R, Hkv, d), i32_dev(pos), i32_dev(cu), cu)
     torch.cuda.synchronize()
     assert up.device_error() == 0
-    rows = [0, 1, 63, 64, 4095, 65536, 100003, R - 65, R - 2, R - 1]
+    rows = [0, 1, 31, 32, 63, 64, 4095, 65536, 100003, R - 65, R - 33, R - 2, R - 1]
     got = out[rows].float().cpu().numpy().astype(np.float64)
     say("[setup] oracle on sampled rows")
     ref = C.rope_attention_rows(q, k, v, pos, cu, Hq, Hkv, d, 1 / math.sqrt(d), 500000.0, rows)
