@@ -149,55 +149,60 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
   const int L = cu[i + 1] - cu[i];
   const int tid = threadIdx.x;
 
-  // q and k: each thread owns NU (row, 4-pair group) items and their 8 angles.
-  double cs[NU][4], sn[NU][4];
-  int64_t src_row[NU];   // packed token row, -1 for padding
-  int rr_of[NU], pg_of[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int item = tid + 256 * u;
-    const int rr = item / PG, pg = item % PG;
-    rr_of[u] = rr;
-    pg_of[u] = pg;
-    const int t = t0 + rr;
-    src_row[u] = t < L ? (int64_t)cu[i] + t : -1;
-    const double p = src_row[u] >= 0 ? (double)pos[src_row[u]] : 0.0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int ip = 4 * pg + m;
-      const double inv_freq = exp2(-(2.0 * ip / D) * log2_theta);
-      sincos(p * inv_freq, &sn[u][m], &cs[u][m]);
-    }
-  }
+  // q and k: each thread owns NU (row, 4-pair group) items and their 8 angles, taken
+  // NC at a time so that the float64 angles of a chunk fit beside everything else.
+  constexpr int NC = NU < 4 ? NU : 4;
   const int Hs = Hq + Hkv;
-  for (int hs = 0; hs < Hs; ++hs) {
-    const bool isq = hs < Hq;
-    const int hh = isq ? hs : hs - Hq;
-    const int H = isq ? Hq : Hkv;
-    const uint16_t* src = isq ? q : k;
-    uint16_t* dst = (isq ? qr : kr) + ((int64_t)hh * Rp + row0p) * D;
+#pragma unroll 1
+  for (int u0 = 0; u0 < NU; u0 += NC) {
+    double cs[NC][4], sn[NC][4];
+    int64_t src_row[NC];   // packed token row, -1 for padding
+    int rr_of[NC], pg_of[NC];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      ushort4 lo = make_ushort4(0, 0, 0, 0), hi = make_ushort4(0, 0, 0, 0);
-      if (src_row[u] >= 0) {
-        const uint16_t* s = src + (src_row[u] * H + hh) * D + 4 * pg_of[u];
-        const ushort4 xl = *reinterpret_cast<const ushort4*>(s);
-        const ushort4 xh = *reinterpret_cast<const ushort4*>(s + D / 2);
-        const uint16_t al[4] = {xl.x, xl.y, xl.z, xl.w};
-        const uint16_t ah[4] = {xh.x, xh.y, xh.z, xh.w};
-        uint16_t rl[4], rh[4];
+    for (int u = 0; u < NC; ++u) {
+      const int item = tid + 256 * (u0 + u);
+      const int rr = item / PG, pg = item % PG;
+      rr_of[u] = rr;
+      pg_of[u] = pg;
+      const int t = t0 + rr;
+      src_row[u] = t < L ? (int64_t)cu[i] + t : -1;
+      const double p = src_row[u] >= 0 ? (double)pos[src_row[u]] : 0.0;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const double a = f64_of_bf16(al[m]), b = f64_of_bf16(ah[m]);
-          rl[m] = bf16_of_f64(a * cs[u][m] - b * sn[u][m]);
-          rh[m] = bf16_of_f64(b * cs[u][m] + a * sn[u][m]);
-        }
-        lo = make_ushort4(rl[0], rl[1], rl[2], rl[3]);
-        hi = make_ushort4(rh[0], rh[1], rh[2], rh[3]);
+      for (int m = 0; m < 4; ++m) {
+        const int ip = 4 * pg + m;
+        const double inv_freq = exp2(-(2.0 * ip / D) * log2_theta);
+        sincos(p * inv_freq, &sn[u][m], &cs[u][m]);
       }
-      uint16_t* d = dst + (int64_t)rr_of[u] * D + 4 * pg_of[u];
-      *reinterpret_cast<ushort4*>(d) = lo;
-      *reinterpret_cast<ushort4*>(d + D / 2) = hi;
+    }
+    for (int hs = 0; hs < Hs; ++hs) {
+      const bool isq = hs < Hq;
+      const int hh = isq ? hs : hs - Hq;
+      const int H = isq ? Hq : Hkv;
+      const uint16_t* src = isq ? q : k;
+      uint16_t* dst = (isq ? qr : kr) + ((int64_t)hh * Rp + row0p) * D;
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        ushort4 lo = make_ushort4(0, 0, 0, 0), hi = make_ushort4(0, 0, 0, 0);
+        if (src_row[u] >= 0) {
+          const uint16_t* sp = src + (src_row[u] * H + hh) * D + 4 * pg_of[u];
+          const ushort4 xl = *reinterpret_cast<const ushort4*>(sp);
+          const ushort4 xh = *reinterpret_cast<const ushort4*>(sp + D / 2);
+          const uint16_t al[4] = {xl.x, xl.y, xl.z, xl.w};
+          const uint16_t ah[4] = {xh.x, xh.y, xh.z, xh.w};
+          uint16_t rl[4], rh[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const double a = f64_of_bf16(al[m]), b = f64_of_bf16(ah[m]);
+            rl[m] = bf16_of_f64(a * cs[u][m] - b * sn[u][m]);
+            rh[m] = bf16_of_f64(b * cs[u][m] + a * sn[u][m]);
+          }
+          lo = make_ushort4(rl[0], rl[1], rl[2], rl[3]);
+          hi = make_ushort4(rh[0], rh[1], rh[2], rh[3]);
+        }
+        uint16_t* dd = dst + (int64_t)rr_of[u] * D + 4 * pg_of[u];
+        *reinterpret_cast<ushort4*>(dd) = lo;
+        *reinterpret_cast<ushort4*>(dd + D / 2) = hi;
+      }
     }
   }
 
