@@ -245,11 +245,11 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
 // ---------------------------------------------------------------------------
 // Causal GQA flash attention on the matrix cores.
 //
-// Workgroup = 4 waves (one per SIMD) = HQ query heads x TT 64-token tiles of one kv
-// head (HQ * TT = 4), one wave per (head, tile), 64 query rows per wave in two
-// 32-row tiles held as the B operand in VGPRs.  Keys and values stream through a ring
-// of four LDS stages of 64 tokens (K tile [64][d] and V^T tile [d][64], 16-byte
-// granules XOR-swizzled), copied global -> LDS directly two stages ahead of use.
+// Workgroup = 4 waves (one per SIMD) = HQ query heads x TT 32-token tiles of one kv
+// head (HQ * TT = 4), one wave per (head, tile), its 32 query rows held as the B
+// operand in VGPRs.  Keys and values stream through a ring of four LDS stages of 32
+// tokens (K tile [32][d] and V^T tile [d][32], 16-byte granules XOR-swizzled), copied
+// global -> LDS directly.
 //   S^T = K Q^T        (keys as rows: each lane column is one query, so a query's
 //                       softmax statistics are in-lane plus one lane-pair exchange)
 //   O^T += V^T P^T     (P^T straight from the S^T registers, rounded to bf16; the
@@ -257,12 +257,15 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
 //                       because v was stored in that order)
 // Softmax: one reference Rs per query in log2 units; P = 2^(x - Rs) with x the
 // scaled logit.  Rs moves only when a stage's maximum exceeds it by more than 32 (a
-// wave-uniform branch that rescales O and l), so P <= 2^32 and no per-stage
-// rescale of O is needed.  The stage after the current one has its S^T issued
-// before the current stage's softmax, so its MFMAs overlap that VALU work; a
-// wave's diagonal stage (its last) is masked before its maximum is taken.
-// Workgroups are ordered heaviest tile first; with the kv head in blockIdx.x the
-// workgroups of one kv head share an XCD's L2 when Hkv * quads is a multiple of 8.
+// wave-uniform branch that rescales O and l), so P <= 2^32 and no per-stage rescale
+// of O is needed.  A stage's body issues the next stage's S^T before its own softmax,
+// so those MFMAs overlap the VALU work; a wave's diagonal stage (its last) is masked
+// before its maximum is taken.  Up to d = 128 a workgroup takes 64 KiB of LDS and at
+// most 256 registers per lane, so two workgroups share a CU (two waves per SIMD); at
+// d = 256 the stage is 32 KiB and the O accumulator alone 128 registers, one
+// workgroup per CU.  Workgroups are ordered heaviest tile first; with the kv head in
+// blockIdx.x the workgroups of one kv head share an XCD's L2 when Hkv * quads is a
+// multiple of 8.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -289,303 +292,28 @@ __device__ __forceinline__ void wait_barrier() {
 
 // 16-byte granule swizzles.  The LDS serves a 16-byte read to 16 lanes per clock over
 // 64 banks; the 16 lanes of a group read 16 consecutive rows at one logical granule,
-// which the XOR spreads over 16 distinct bank groups: by row & 15 for 256-byte rows,
-// by (row >> 1) & 7 for 128-byte rows (odd rows sit half a bank cycle further on).
+// which the XOR spreads over 16 distinct bank groups: by row & 15 for K rows of 256
+// bytes or more, by (row >> 1) & 7 for 128-byte rows (odd rows sit half a bank cycle
+// further on).
 template <int D>
 __device__ __forceinline__ int k_swz(int key) {
   return (D / 8 >= 16) ? (key & 15) : ((key >> 1) & 7);
 }
-__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
 
 constexpr float kRebase = 32.f;
 
-template <int D>
-__global__ __launch_bounds__(256, 1) void up_attention_kernel(
-    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
-    const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
-    const int32_t* __restrict__ tp, int B, int Hq, int Hkv, int HQ, int TT, int64_t Rp,
-    float c, uint16_t* __restrict__ out) {
-  constexpr int NT = 256, NS = 4, UK = 64, QT = 2;
-  constexpr int DS = D / 16;             // MFMA k-steps over the head dimension
-  constexpr int DT = D / 32;             // 32-row tiles of O^T (head dimension)
-  constexpr int KRB = 2 * D;             // K tile row bytes
-  constexpr int KB = UK * KRB;           // K tile bytes
-  constexpr int VB = D * UK * 2;         // V^T tile bytes (rows of 128 bytes)
-  constexpr int SB = KB + VB;            // stage bytes
-  constexpr int KSPT = KB / (NT * 16);   // DMA copies per lane per stage, K
-  constexpr int VSPT = VB / (NT * 16);   // and V^T
-  constexpr int SPT = KSPT + VSPT;
-  static_assert(KB % (NT * 16) == 0 && VB % (NT * 16) == 0, "whole DMA rounds");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
-
-  if (hdr->valid != 1) return;
-  const int gsz = Hq / Hkv, quads = gsz / HQ;
-  const int g = blockIdx.x / quads, quad = blockIdx.x - g * quads;
-  const int f = blockIdx.y;
-  const int i = request_of(tp, B, f);
-  const int L = cu[i + 1] - cu[i];
-  const int nwt = tp[i + 1] - tp[i];
-  const int wt = nwt - 1 - (f - tp[i]);   // heaviest tile first
-  const int ntile = (L + 63) >> 6;        // 64-token tiles of the request
-  const int tile0 = wt * TT;
-  const int nst = min(tile0 + TT, ntile);   // key stages of this workgroup
-  const int64_t pbase = po[i];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5,
-            l32 = lane & 31;
-  const int head = g * gsz + quad * HQ + wave % HQ;
-  const int tw = tile0 + wave / HQ;   // this wave's 64-token tile (its diagonal stage)
-  const bool wact = tw < ntile;
-
-  // Query operand.  The head dimension is contracted in a permuted order shared by
-  // both operands: lane half h, k-step s covers d-elements [h D/2 + 8 s, +8).
-  bf16x8 qreg[QT][DS];
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    if (wact) {
-      const uint16_t* src =
-          qr + ((int64_t)head * Rp + pbase + tw * 64 + t * 32 + l32) * D + half * (D / 2);
-#pragma unroll
-      for (int s = 0; s < DS; ++s) qreg[t][s] = *reinterpret_cast<const bf16x8*>(src + s * 8);
-    } else {
-#pragma unroll
-      for (int s = 0; s < DS; ++s) qreg[t][s] = bf16x8{};
-    }
-  }
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): only stage copies from here
-
-  typedef __attribute__((address_space(3))) uint8_t lds_u8;
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8*)lds;
-  // DMA: 16 bytes per lane per copy; copy q of the stage lands at LDS bytes
-  // [q NT 16 + 16 tid, +16), and reads the granule that the swizzle puts there.
-  const uint16_t* kbase = kr + ((int64_t)g * Rp + pbase) * D;
-  const uint16_t* vbase = vt + (int64_t)g * D * Rp + pbase;
-  auto issue = [&](int st) {
-    const uint32_t sb = lds_base + (uint32_t)((st & (NS - 1)) * SB);
-    const uint16_t* kst = kbase + (int64_t)st * UK * D;
-#pragma unroll
-    for (int q = 0; q < KSPT; ++q) {
-      const int o = q * NT * 16 + tid * 16;
-      const int key = o / KRB;
-      const int gr = ((o % KRB) / 16) ^ k_swz<D>(key);
-      lds_dma16(kst + key * D + gr * 8,
-                __builtin_amdgcn_readfirstlane(sb + q * NT * 16 + wave * 1024));
-    }
-    const uint16_t* vst = vbase + (int64_t)st * UK;
-#pragma unroll
-    for (int q = 0; q < VSPT; ++q) {
-      const int o = q * NT * 16 + tid * 16;
-      const int row = o / 128;
-      const int gr = ((o % 128) / 16) ^ v_swz(row);
-      lds_dma16(vst + (int64_t)row * Rp + gr * 8,
-                __builtin_amdgcn_readfirstlane(sb + KB + q * NT * 16 + wave * 1024));
-    }
-  };
-
-  // LDS read offsets within a stage for row tile 0; the swizzles depend on l32 only,
-  // so row tile kt of K is kt * 32 rows on and row tile dt of V^T dt * 32 rows on.
-  uint32_t krd[DS];
-#pragma unroll
-  for (int s = 0; s < DS; ++s) krd[s] = l32 * KRB + 16 * ((half * DS + s) ^ k_swz<D>(l32));
-  uint32_t vrd[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) vrd[j] = KB + l32 * 128 + 16 * ((2 * j + half) ^ v_swz(l32));
-
-  float Rs[QT], lsum[QT];
-  f32x16 O[DT][QT];
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    lsum[t] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[dt][t] = f32x16{};
-  }
-  int qtok[QT];
-#pragma unroll
-  for (int t = 0; t < QT; ++t) qtok[t] = tw * 64 + t * 32 + l32;
-
-  // The keys are consumed in halves of 32 (half-step hs = keys [32 hs, 32 hs + 32) of
-  // the request, stage hs / 2, row tile hs % 2 of that stage).
-  // S^T of half-step hs into acc[t].
-  auto s_mfma = [&](int hs, f32x16 (&acc)[QT]) {
-    const int kt = hs & 1;
-    const uint8_t* sl = lds + ((hs >> 1) & (NS - 1)) * SB;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sl + kt * 32 * KRB + krd[s]);
-#pragma unroll
-      for (int t = 0; t < QT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t][s], s == 0 ? f32x16{} : acc[t],
-                                                         0, 0, 0);
-    }
-  };
-  // Causal mask of a half-step in the diagonal stage (keys past the query -> -inf).
-  auto mask = [&](int hs, f32x16 (&acc)[QT]) {
-#pragma unroll
-    for (int t = 0; t < QT; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        // 32x32 result layout: register e of lane l is row 8(e/4) + 4(l/32) + e%4
-        // (the key) and column l%32 (the query).
-        const int key = hs * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-        if (key > qtok[t]) acc[t][e] = kNegInf;
-      }
-  };
-  // Half-step maximum per query (log2 units) and, when it passes Rs + 32 anywhere in
-  // the wave, a new reference with O and l rescaled.
-  auto rebase = [&](f32x16 (&acc)[QT], bool init) {
-    float mx[QT];
-    bool need = init;
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      float m0 = kNegInf, m1 = kNegInf;
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        m0 = fmaxf(m0, acc[t][e]);
-        m1 = fmaxf(m1, acc[t][e + 1]);
-      }
-      mx[t] = pair_max(fmaxf(m0, m1)) * c;
-      if (!init) need |= mx[t] > Rs[t] + kRebase;
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int t = 0; t < QT; ++t) {
-        if (init) {
-          Rs[t] = mx[t];
-          continue;
-        }
-        const float rn = fmaxf(Rs[t], mx[t]);
-        const float sc = __builtin_amdgcn_exp2f(Rs[t] - rn);
-        lsum[t] *= sc;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) O[dt][t] *= sc;
-        Rs[t] = rn;
-      }
-    }
-  };
-  // Softmax of half-step hs (S^T in acc) and O^T += V^T P^T over its 32 keys.
-  auto pv = [&](int hs, const f32x16 (&acc)[QT]) {
-    // V^T operands first: their LDS latency runs under the softmax below.
-    const int kt = hs & 1;
-    const uint8_t* sl = lds + ((hs >> 1) & (NS - 1)) * SB;
-    bf16x8 va[DT][2];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        va[dt][jj] = *reinterpret_cast<const bf16x8*>(sl + dt * 32 * 128 + vrd[2 * kt + jj]);
-    bf16x8 pb[2][QT];
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      f32x16 p;
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(acc[t][e], c, -Rs[t]));
-        p[e + 1] = __builtin_amdgcn_exp2f(fmaf(acc[t][e + 1], c, -Rs[t]));
-        s0 += p[e];
-        s1 += p[e + 1];
-      }
-      lsum[t] += s0 + s1;
-      pb[0][t] = __builtin_convertvector(p.lo, bf16x8);
-      pb[1][t] = __builtin_convertvector(p.hi, bf16x8);
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int t = 0; t < QT; ++t)
-          O[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][jj], pb[jj][t], O[dt][t], 0, 0,
-                                                             0);
-  };
-
-  // Ring: stages st+1 and st+2 in flight while st is consumed; stage st+1 is waited
-  // for (and published by a barrier) before the second half of stage st, whose body
-  // issues the S^T of stage st+1's first half.
-  auto sync_for = [&](int st) {
-    if (st + 1 >= nst) return;
-    if (st + 2 < nst) wait_barrier<SPT>();
-    else wait_barrier<0>();
-    if (st + 3 < nst) issue(st + 3);
-  };
-
-  issue(0);
-  if (nst > 1) issue(1);
-  if (nst > 2) issue(2);
-  if (nst > 2) wait_barrier<2 * SPT>();
-  else if (nst > 1) wait_barrier<SPT>();
-  else wait_barrier<0>();
-
-  const int last_hs = 2 * tw + 1;   // the wave's last half-step (end of its diagonal stage)
-  f32x16 accA[QT], accB[QT];
-  if (wact) {
-    s_mfma(0, accA);
-    if (tw == 0) mask(0, accA);
-    rebase(accA, true);
-  }
-  // One half-step: cur holds S^T of half-step hs, nxt receives half-step hs+1's.
-  auto body = [&](int hs, f32x16 (&cur)[QT], f32x16 (&nxt)[QT]) {
-    if (!wact || hs > last_hs) return;
-    if (hs + 1 < 2 * tw) {          // next half-step is before the diagonal stage
-      s_mfma(hs + 1, nxt);
-      pv(hs, cur);
-      rebase(nxt, false);
-    } else if (hs + 1 <= last_hs) {   // next half-step is in the diagonal stage
-      s_mfma(hs + 1, nxt);
-      pv(hs, cur);
-      mask(hs + 1, nxt);
-      rebase(nxt, false);
-    } else {
-      pv(hs, cur);
-    }
-  };
-  for (int st = 0; st < nst; ++st) {
-    body(2 * st, accA, accB);
-    sync_for(st);
-    body(2 * st + 1, accB, accA);
-  }
-
-  if (!wact) return;
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    const float inv = 1.f / pair_sum(lsum[t]);
-    if (qtok[t] >= L) continue;
-    uint16_t* dst = out + (((int64_t)cu[i] + qtok[t]) * Hq + head) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int eg = 0; eg < 4; ++eg) {
-        const int dv = dt * 32 + 8 * eg + 4 * half;
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        const f32x4 o4 = {O[dt][t][4 * eg] * inv, O[dt][t][4 * eg + 1] * inv,
-                          O[dt][t][4 * eg + 2] * inv, O[dt][t][4 * eg + 3] * inv};
-        *reinterpret_cast<bf16x4*>(dst + dv) = __builtin_convertvector(o4, bf16x4);
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// The same attention at d = 256.  A 64-token stage of K and V^T would take 64 KiB
-// there and the O accumulator of two 32-row query tiles 256 registers, so the tiling
-// is halved: each wave holds one 32-row query tile (tiles of 32 tokens; HQ heads x TT
-// tiles per workgroup, HQ * TT = 4) and the ring holds four stages of 32 keys (K
-// [32][256] and V^T [256][32], 32 KiB each).  A stage is one half-step, and a
-// half-step's body issues the next stage's S^T, so each stage is waited for and
-// published before the body that first reads it.  The 64-byte V^T rows keep granule
-// g of row r at g ^ ((r >> 2) & 3), which spreads the 16 rows one 16-lane group
-// reads over all 64 banks.
-// ---------------------------------------------------------------------------
+// V^T tile rows are 64 bytes (32 tokens): granule g of row r sits at g ^ ((r >> 2) & 3),
+// which spreads the 16 rows one 16-lane group reads over all 64 banks.
 __device__ __forceinline__ int v64_swz(int row) { return (row >> 2) & 3; }
 
-__global__ __launch_bounds__(256, 1) void up_attention_d256_kernel(
+template <int D>
+__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
     const int32_t* __restrict__ tp, int B, int Hq, int Hkv, int HQ, int TT, int64_t Rp,
     float c, uint16_t* __restrict__ out) {
-  constexpr int D = 256, NT = 256, NS = 4, UK = 32;
+  constexpr int NT = 256, NS = 4, UK = 32;
   constexpr int DS = D / 16;             // MFMA k-steps over the head dimension
   constexpr int DT = D / 32;             // 32-row tiles of O^T
   constexpr int KRB = 2 * D;             // K tile row bytes
@@ -906,7 +634,7 @@ hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, con
     hipLaunchKernelGGL(up_attention_kernel<128>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
                        tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
   else
-    hipLaunchKernelGGL(up_attention_d256_kernel, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
+    hipLaunchKernelGGL(up_attention_kernel<256>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
                        tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
   return hipGetLastError();
 }

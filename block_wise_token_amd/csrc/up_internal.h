@@ -152,9 +152,8 @@ hipError_t launch_compose(const int32_t* prev, int prev_len, const int32_t* idx,
                           hipStream_t st);
 
 // Layer on the surviving tokens (consumer.hip).
-// Query tokens per wave in the attention kernel: 64 (two 32-row tiles) up to d = 128,
-// 32 at d = 256.
-constexpr int attn_tile_tokens(int d) { return d == 256 ? 32 : 64; }
+// Query tokens per wave in the attention kernel (one 32-row tile).
+constexpr int attn_tile_tokens(int) { return 32; }
 struct AttnShape {
   int B, Hq, Hkv, d;
   int HQ, TT;       // query heads and per-wave token tiles per attention workgroup (HQ * TT = 4)

@@ -278,9 +278,8 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
  * rope_theta > 1 (e.g. 500000 for the Llama-3.1 shape).
  * Probabilities enter the P.V product as bf16; softmax statistics and accumulation
  * are float32.  Limits: sum of ceil(L_i / 64) padded rows < 2^31 and at most 65535
- * workgroup tiles, a tile spanning 64 * 4 / m query tokens (32 * 4 / m at d = 256),
- * m = the largest of 4, 2, 1 dividing Hq / Hkv (about 4M rows at Hq / Hkv = 4 and
- * d <= 128).
+ * workgroup tiles, a tile spanning 32 * 4 / m query tokens, m = the largest of 4, 2, 1
+ * dividing Hq / Hkv (about 2M rows at Hq / Hkv = 4).
  * workspace : at least up_rope_attention_workspace(...) bytes, 256-byte aligned
  *             (rotated q and k, transposed v, plan).
  * A device cu_seqlens whose totals (rows, padded rows, workgroup tiles) differ from
