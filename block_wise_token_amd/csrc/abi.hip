@@ -117,6 +117,9 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
   if (!cu_ok(cu_h, B)) return UP_EINVAL;
   if (d != 64 && d != 128 && d != 256) return UP_EUNSUPPORTED;
   if (!block_size_supported(G)) return UP_EUNSUPPORTED;
+  // The score kernel addresses keys as 32-bit byte offsets within a page of up to 1024
+  // token rows of Hkv * d bf16 values.
+  if ((int64_t)Hkv * d * 2 * 1024 >= ((int64_t)1 << 31)) return UP_EUNSUPPORTED;
   s->B = B; s->Hq = Hq; s->Hkv = Hkv; s->d = d; s->n = n; s->G = G;
   s->qt = (d == 256) ? 1 : 2;
   s->kt = (d == 256) ? 1 : (G % 64 == 0 ? 2 : 1);

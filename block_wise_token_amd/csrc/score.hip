@@ -149,12 +149,22 @@ __device__ __forceinline__ int k_swizzle(int key) {
 }
 
 // Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
-// lane i of the wave writes LDS bytes [m0 + 16 i, m0 + 16 i + 16).  Issued from
-// inline assembly so that the compiler does not drain every outstanding load at
-// the next LDS read; completion is awaited explicitly (vmcnt) before the barrier
-// that publishes a stage.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t m0) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+// lane i of the wave writes LDS bytes [m0 + 16 i, m0 + 16 i + 16) and reads 16 bytes
+// at a wave-uniform 64-bit base (held in SGPRs) plus its own 32-bit byte offset, so a
+// lane spends no vector instructions on 64-bit address arithmetic.  Issued from
+// inline assembly so that the compiler does not drain every outstanding load at the
+// next LDS read; completion is awaited explicitly (vmcnt) before the barrier that
+// publishes a stage.
+__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t voff, uint32_t m0) {
+  // readfirstlane returns a signed int: both halves go through uint32_t before they
+  // are widened, so the low word is zero-extended, never sign-extended.
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t sa = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(reinterpret_cast<const void*>(sa)),
+               "{m0}"(m0)
+               : "memory");
 }
 
 // Wait until at most n vector-memory operations of this wave are outstanding and all
@@ -273,19 +283,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
       PAGED ? kmat + (int64_t)g * D : kmat + ((int64_t)pr.tok_off * Hkv + g) * D;
   const int32_t* trow = PAGED ? btab + (int64_t)i * max_pages : nullptr;
   bool bad_page = false;
-  // Page indices of a stage's keys (up to four), and the stage they were loaded for.
+  // A wave's copy q of a stage fetches 1024 bytes: 1024 / RB consecutive keys, aligned
+  // to their count (2, 4 or 8), so inside one page (pages hold at least 16 keys; keys
+  // past the request read its last key, still inside that page).  Its page index is
+  // therefore wave-uniform: one scalar load per copy, made one stage ahead.
   int pf_stage = -1;
-  int pf_pg[4] = {0, 0, 0, 0};
-  auto load_pages = [&](int st, int (&pg)[4]) {
+  int pf_pg[SPT];
+  auto load_pages = [&](int st, int (&pg)[SPT]) {
     const int ks = k0 + st * UK;
-    const int s0 = ks >> lps;
-    const int slast = (min(ks + UK, pr.L) - 1) >> lps;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int slot = __builtin_amdgcn_readfirstlane(min(min(s0 + u, slast), max_pages - 1));
+    for (int q = 0; q < SPT; ++q) {
+      const int key0 = __builtin_amdgcn_readfirstlane((q * NT * 16 + wave * 1024) / RB);
+      const int slot =
+          __builtin_amdgcn_readfirstlane(min(min(ks + key0, pr.L - 1) >> lps, max_pages - 1));
       int p = trow[slot];
       if (p < 0 || (int64_t)p >= num_pages) { bad_page = true; p = 0; }
-      pg[u] = p;
+      pg[q] = p;
     }
   };
   const int fast_limit = pr.L - pr.W;   // keys <= this are visible to every window row
@@ -294,7 +307,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
 
   // Per-lane constants: where this lane's DMA copies come from and land, and where its
   // A-operand reads are (granule half*DS+s of key l32, swizzled; key 32+l32 is 32 rows on).
-  int64_t dma_goff[SPT];
+  // Byte offsets are 32-bit: a stage spans 64 keys of kstride2 bytes (the host keeps
+  // 64 * kstride2 below 2^31).
+  const uint32_t kstride2 = (uint32_t)(kstride * 2);
+  uint32_t dma_voff[SPT];   // from the stage's first key (full stages, contiguous keys)
+  uint32_t dma_gran[SPT];   // the swizzled 16-byte granule within the key's row
   uint32_t dma_loff[SPT];
   int dma_key[SPT];
 #pragma unroll
@@ -303,7 +320,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
     const int key = o / RB;
     const int p = ((o % RB) / 16) ^ k_swizzle<D>(key);
     dma_key[q] = key;
-    dma_goff[q] = (int64_t)key * kstride + p * 8;
+    dma_gran[q] = (uint32_t)p * 16;
+    dma_voff[q] = (uint32_t)key * kstride2 + dma_gran[q];
     dma_loff[q] = q * NT * 16 + wave * 1024;   // wave-uniform
   }
   uint32_t rd_off[DS];
@@ -316,23 +334,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
     const int ks = k0 + st * UK;
     const uint32_t sbase = lds_base + (uint32_t)((st & (NS - 1)) * SB);
     if constexpr (PAGED) {
-      int pg[4];
+      int pg[SPT];
       if (pf_stage == st) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) pg[u] = pf_pg[u];
+        for (int q = 0; q < SPT; ++q) pg[q] = pf_pg[q];
       } else {
         load_pages(st, pg);
       }
-      const int s0 = ks >> lps;
       const int pmask = (1 << lps) - 1;
 #pragma unroll
       for (int q = 0; q < SPT; ++q) {
         const int kabs = min(ks + dma_key[q], pr.L - 1);
-        const int u = (kabs >> lps) - s0;   // 0..3
-        const int p = u == 0 ? pg[0] : u == 1 ? pg[1] : u == 2 ? pg[2] : pg[3];
-        const int64_t row = ((int64_t)p << lps) + (kabs & pmask);
-        lds_dma16(kbase + row * kstride + (dma_goff[q] - (int64_t)dma_key[q] * kstride),
-                  __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
+        lds_dma16_s(kbase + ((int64_t)pg[q] << lps) * kstride,
+                    (uint32_t)(kabs & pmask) * kstride2 + dma_gran[q],
+                    __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
       }
       // The next stage's page indices, in flight while this stage's copies are.
       if (st + 1 < nst) {
@@ -345,13 +360,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
     if (ks + UK <= pr.L) {
 #pragma unroll
       for (int q = 0; q < SPT; ++q)
-        lds_dma16(gb + dma_goff[q], __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
+        lds_dma16_s(gb, dma_voff[q], __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
     } else {
 #pragma unroll
       for (int q = 0; q < SPT; ++q) {
         const int kabs = min(ks + dma_key[q], pr.L - 1);
-        lds_dma16(kbase + (int64_t)kabs * kstride + (dma_goff[q] - (int64_t)dma_key[q] * kstride),
-                  __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
+        lds_dma16_s(gb, (uint32_t)(kabs - ks) * kstride2 + dma_gran[q],
+                    __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
       }
     }
   };
@@ -581,7 +596,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   }
 
   flush_pending();
-  if (PAGED && bad_page && tid == 0) atomicOr(err, 8);
+  // Each wave checks only the page indices of its own copies: every wave reports.
+  if (PAGED && bad_page && (tid & 63) == 0) atomicOr(err, 8);
   if constexpr (LSE) {
     // Block partials of this (kv head, row tile): the waves' totals in wave order.
     __syncthreads();

@@ -82,6 +82,7 @@ int up_abi_version(void);
  * k     : bf16 [T, Hkv, d]; T = cu_seqlens[B].  Key (t, g) at ((t * Hkv) + g) * d.
  * cu_seqlens / cu_seqlens_h : int32 [B+1], cu[0] = 0, non-decreasing.
  * Hq % Hkv == 0.  d in {64, 128, 256}.  G a multiple of 32 in [32, 1024].  n >= 1.
+ * Hkv * d < 2^20 (1024 key rows stay below 2 GiB; UP_EUNSUPPORTED otherwise).
  * scale : softmax scale; <= 0 or NaN selects 1/sqrt(d) (as float32).
  * scores: float32 [NB_tot] output, NB_tot = sum_i nb_i.
  * row_lse: float32 [sum_i W_i, Hq] output, or NULL: each window row's natural-log

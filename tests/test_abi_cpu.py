@@ -88,6 +88,7 @@ def test_block_scores_rejects_bad_arguments(L):
     assert call(d=80) == UP_EUNSUPPORTED
     assert call(G=48) == UP_EUNSUPPORTED
     assert call(G=2048) == UP_EUNSUPPORTED
+    assert call(Hq=4096, Hkv=4096, d=256) == UP_EUNSUPPORTED   # 1024 key rows reach 2 GiB
     assert call(cu_h=np.array([0, 5, 3], np.int32), B=2) == UP_EINVAL
     assert call(cu_h=np.array([1, 5], np.int32)) == UP_EINVAL
     assert call(q=None) == UP_EINVAL
