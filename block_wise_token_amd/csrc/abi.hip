@@ -125,14 +125,6 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
   s->kt = (d == 256) ? 1 : (G % 64 == 0 ? 2 : 1);
   s->rows_wg = score_rows_wg(d);
   const int64_t gs = Hq / Hkv;
-  int64_t units = 0;
-  for (int i = 0; i < B; ++i) {
-    const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
-    const int64_t W = L < n ? L : n;
-    const int64_t nb = (L + G - 1) / G;
-    const int64_t nrt = (gs * W + s->rows_wg - 1) / s->rows_wg;
-    units += nb * Hkv * nrt;
-  }
   // Key-chunk length (blocks per workgroup).  score_wgs_per_cu(d) workgroups fill a
   // CU, so the score pass takes ceil(items / slots) rounds, each costing CB blocks of
   // work plus a workgroup's fixed cost (query load, ring fill, chunk-end stores),
@@ -142,7 +134,6 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
   // workgroups rather than 16 of eight blocks, which takes half the time).  The
   // candidates are 1..256 in steps of about 1.25x (plus the longest request's block
   // count), which keeps planning linear in B with a small constant.
-  (void)units;
   {
     constexpr int kChunkOverheadBlocks = 3;
     const int64_t cus = (int64_t)device_cus() * score_wgs_per_cu(d);

@@ -362,3 +362,46 @@ def test_compose_drops_standalone_matches_oracle():
     torch.cuda.synchronize()
     assert up.device_error() == 0
     np.testing.assert_array_equal(out[:cnt].cpu().numpy(), O.compose(prev, idx))
+
+
+def _random_configs(count=24, seed=2026):
+    """Seeded draws over the supported argument space: 1-5 requests of 0-4000 tokens
+    (empty and one-token requests included), GQA group sizes 1, 2, 3, 4 and 8, every
+    head dimension, window sizes 1-300, every block size 32-1024 in steps of 32, p in
+    [0.3, 1] and, for a quarter of the cases, a Top-k cut with k anywhere from 0 to past
+    the longest request's block count."""
+    rng = np.random.default_rng(seed)
+    heads = [(8, 2), (4, 1), (4, 4), (12, 4), (6, 2), (16, 2), (2, 1), (3, 3)]
+    out = []
+    while len(out) < count:
+        B = int(rng.integers(1, 6))
+        lengths = [int(x) for x in rng.integers(0, 4001, B)]
+        for j in range(B):
+            r = rng.random()
+            if r < 0.1:
+                lengths[j] = 0
+            elif r < 0.2:
+                lengths[j] = int(rng.integers(1, 40))
+        Hq, Hkv = heads[int(rng.integers(len(heads)))]
+        d = int(rng.choice([64, 128, 256]))
+        n = int(rng.integers(1, 301))
+        G = 32 * int(rng.integers(1, 33))
+        p = 1.0 if rng.random() < 0.1 else float(np.float32(rng.uniform(0.3, 0.999)))
+        nb_max = max((L + G - 1) // G for L in lengths)
+        topk = int(rng.integers(0, nb_max + 4)) if rng.random() < 0.25 else None
+        # keep the float64 oracle to about a second per case
+        if sum(L * Hq * min(L, n) * d for L in lengths) > 1.2e9:
+            continue
+        out.append((lengths, Hq, Hkv, d, n, G, p, topk, int(rng.integers(1 << 30))))
+    return out
+
+
+RANDOM_CASES = _random_configs()
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"r{i}" for i in range(len(RANDOM_CASES))])
+def test_random_configurations_match_oracle(case):
+    lengths, Hq, Hkv, d, n, G, p, topk, seed = case
+    batch = _batch(lengths, Hq, Hkv, d, n, G, needles=int(seed % 4), seed=seed,
+                   recency=int(seed % 3) * 16)
+    _full_check(batch, p, H=int(8 + seed % 57), topk=topk, label=f"random {case}")
