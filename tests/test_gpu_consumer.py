@@ -84,6 +84,40 @@ def test_rope_attention_matches_oracle(case):
     say(f"[ok] {case}: worst error / bar {worst:.3f}")
 
 
+def _random_attention_configs(count=16, seed=909):
+    """Seeded draws: 1-4 requests of 0-900 survivors, GQA group sizes 1, 2, 3, 4, 6 and
+    8 (3 and 6 take one query head per tile row group), every head dimension, logit
+    scales from plain to nearly one-hot, and rotary bases 1e4, 5e5 and 1e6."""
+    rng = np.random.default_rng(seed)
+    heads = [(8, 2), (4, 1), (8, 8), (16, 2), (12, 4), (12, 2), (6, 2), (4, 2)]
+    out = []
+    while len(out) < count:
+        B = int(rng.integers(1, 5))
+        lengths = [int(x) for x in rng.integers(0, 901, B)]
+        Hq, Hkv = heads[int(rng.integers(len(heads)))]
+        d = int(rng.choice([64, 128, 256]))
+        if sum(L * L for L in lengths) * Hq * d > 1.5e9:   # keeps the oracle near a second
+            continue
+        out.append((lengths, Hq, Hkv, d, float(rng.choice([1.0, 4.0, 15.0])),
+                    float(rng.choice([1e4, 5e5, 1e6])), int(rng.integers(1 << 30))))
+    return out
+
+
+RANDOM_ATTENTION = _random_attention_configs()
+
+
+@pytest.mark.parametrize("case", RANDOM_ATTENTION,
+                         ids=[f"r{i}" for i in range(len(RANDOM_ATTENTION))])
+def test_random_attention_configurations_match_oracle(case):
+    lengths, Hq, Hkv, d, sigma, theta, seed = case
+    say(f"[case] random rope_attention {case}")
+    q, k, v, pos, cu, scale, got = _attention_case(lengths, Hq, Hkv, d, sigma, seed=seed,
+                                                   theta=theta)
+    ref = C.rope_attention(q, k, v, pos, cu, Hq, Hkv, d, scale, theta)
+    worst = _check_attention(got, ref, C.attention_vmax(v, cu, Hkv, d), Hq, Hkv)
+    say(f"[ok] random {case}: worst error / bar {worst:.3f}")
+
+
 def test_rope_attention_over_many_requests():
     """120 short requests (0-150 survivors, some empty): the plan's padded offsets and
     tile offsets over many requests and the tile-to-request search."""
