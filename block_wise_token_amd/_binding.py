@@ -113,6 +113,10 @@ def _ptr(t: torch.Tensor | None):
 def _dev(t: torch.Tensor, dtype, name: str):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        # the library launches on the current device and stream
+        raise ValueError(f"{name} is on {t.device}, the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
@@ -188,6 +192,7 @@ def block_scores(qwin, k, cu_seqlens, cu_h, n, G, scale=0.0, out=None, workspace
     _dev(k, torch.bfloat16, "k")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     h = _HostCu(cu_h)
+    _buf(cu_seqlens, torch.int32, h.B + 1, "cu_seqlens")
     _check_scores_inputs(qwin, _rank(k, 3, "k"), h, n)
     if int(k.shape[0]) < h.T:
         raise ValueError(f"k has {int(k.shape[0])} rows, cu_seqlens needs {h.T}")
@@ -218,6 +223,7 @@ def block_scores_paged(qwin, k_pages, block_table, cu_seqlens, cu_h, n, G, scale
     _dev(block_table, torch.int32, "block_table")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     h = _HostCu(cu_h)
+    _buf(cu_seqlens, torch.int32, h.B + 1, "cu_seqlens")
     _check_scores_inputs(qwin, _rank(k_pages, 4, "k_pages"), h, n, d_k_axis=3)
     _rank(block_table, 2, "block_table")
     if int(block_table.shape[0]) < h.B:
@@ -251,6 +257,7 @@ def block_scores_lse(qwin, k, row_lse, cu_seqlens, cu_h, n, G, scale=0.0, out=No
     _dev(row_lse, torch.float32, "row_lse")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     h = _HostCu(cu_h)
+    _buf(cu_seqlens, torch.int32, h.B + 1, "cu_seqlens")
     _check_scores_inputs(qwin, _rank(k, 3, "k"), h, n)
     if int(k.shape[0]) < h.T:
         raise ValueError(f"k has {int(k.shape[0])} rows, cu_seqlens needs {h.T}")
@@ -281,6 +288,7 @@ def block_scores_lse_paged(qwin, k_pages, block_table, row_lse, cu_seqlens, cu_h
     _dev(row_lse, torch.float32, "row_lse")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     h = _HostCu(cu_h)
+    _buf(cu_seqlens, torch.int32, h.B + 1, "cu_seqlens")
     _check_scores_inputs(qwin, _rank(k_pages, 4, "k_pages"), h, n, d_k_axis=3)
     _rank(block_table, 2, "block_table")
     if int(block_table.shape[0]) < h.B:
@@ -308,6 +316,7 @@ def _select(fn, scores, cu_seqlens, cu_h, n, G, arg, keep, cu_out, stream, what)
     _dev(scores, torch.float32, "scores")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     h = _HostCu(cu_h)
+    _buf(cu_seqlens, torch.int32, h.B + 1, "cu_seqlens")
     nbt = h.nb_tot(G)
     _buf(scores, torch.float32, nbt, "scores")
     if keep is None:
@@ -339,14 +348,14 @@ def expand_compact(hidden, pos, keep, cu_seqlens, cu_out, cu_h, G, idx_out=None,
     """Kept-token rows: (idx_out, hidden_out, pos_out), each with capacity T rows.
     With ``prev_orig`` given, ``orig_out[r] = prev_orig[idx_out[r]]`` is written in the
     same pass (pass ``orig_out`` to choose the buffer)."""
-    if not hidden.is_cuda or not hidden.is_contiguous():
-        raise ValueError("hidden must be a contiguous device tensor")
+    _dev(hidden, hidden.dtype, "hidden")
     _dev(keep, torch.uint8, "keep_blocks")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     _dev(cu_out, torch.int32, "cu_seqlens_out")
     if pos is not None:
         _dev(pos, torch.int32, "pos")
     h = _HostCu(cu_h)
+    _buf(cu_seqlens, torch.int32, h.B + 1, "cu_seqlens")
     T = h.T
     _rank(hidden, 2, "hidden")
     if int(hidden.shape[0]) < T:

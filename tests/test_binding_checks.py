@@ -76,7 +76,8 @@ def test_block_scores_rejects_short_buffers(bad):
         k = k[:-1].contiguous()
     else:
         k = torch.zeros(1300, HKV, D * 2, dtype=BF)
-    with pytest.raises(ValueError):
+    name = {"qwin_rows": "qwin has", "k_rows": "k has", "k_dim": "head dimension"}.get(bad, bad)
+    with pytest.raises(ValueError, match=name):
         bd.block_scores(qwin, k, cu, cu_h, n, g, **kw)
 
 
@@ -121,11 +122,20 @@ def test_expand_compact_rejects_short_buffers(bad):
              workspace=torch.zeros(WS, dtype=U8))
     t[bad] = t[bad][:-1].contiguous()
     cu, cu_out = torch.tensor(CU), torch.zeros(3, dtype=I32)
-    with pytest.raises(ValueError):
+    name = {"keep": "keep_blocks"}.get(bad, bad)
+    with pytest.raises(ValueError, match=name):
         bd.expand_compact(t["hidden"], t["pos"], t["keep"], cu, cu_out, CU, G,
                           idx_out=t["idx_out"], hidden_out=t["hidden_out"], pos_out=t["pos_out"],
                           workspace=t["workspace"], prev_orig=t["prev_orig"],
                           orig_out=t["orig_out"])
+
+
+def test_expand_compact_accepts_exact_sizes():
+    T, H = 1300, 32
+    with pytest.raises(_Reached, match="up_expand_compact"):
+        bd.expand_compact(torch.zeros(T, H, dtype=BF), torch.zeros(T, dtype=I32),
+                          torch.zeros(NBT, dtype=U8), torch.tensor(CU), torch.zeros(3, dtype=I32),
+                          CU, G, prev_orig=torch.zeros(T, dtype=I32))
 
 
 def test_compose_drops_checks_capacity():
@@ -163,7 +173,8 @@ def test_rope_attention_rejects_mismatched_buffers(bad):
         t["v"] = torch.zeros(R, 2, 128, dtype=BF)
     else:
         t[bad] = t[bad][:-1].contiguous()
-    with pytest.raises(ValueError):
+    name = {"q": "q has", "k": "must both be", "v_shape": "must both be"}.get(bad, bad)
+    with pytest.raises(ValueError, match=name):
         bd.rope_attention(t["q"], t["k"], t["v"], t["pos"], torch.tensor(ATT_CU), ATT_CU,
                           out=t["out"], workspace=t["workspace"])
 
@@ -197,3 +208,24 @@ def test_linear_and_ffn_shape_checks():
         bd.swiglu_ffn(x, wgu, wd, workspace=torch.zeros(WS - 1, dtype=U8))
     with pytest.raises(_Reached, match="up_swiglu_ffn"):
         bd.swiglu_ffn(x, wgu, wd)
+
+
+def test_short_device_cu_seqlens_is_refused():
+    """Every call reads B + 1 entries through the device cu_seqlens pointer."""
+    qwin, k, _, cu_h, n, g = _scores_args()
+    short = torch.tensor(CU[:-1])
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        bd.block_scores(qwin, k, short, cu_h, n, g)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        bd.block_scores_lse(qwin, k, torch.zeros(256 * HQ, dtype=F32), short, cu_h, n, g)
+    pages = torch.zeros(30, 64, HKV, D, dtype=BF)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        bd.block_scores_paged(qwin, pages, torch.zeros(2, 20, dtype=I32), short, cu_h, n, g)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        bd.block_scores_lse_paged(qwin, pages, torch.zeros(2, 20, dtype=I32),
+                                  torch.zeros(256 * HQ, dtype=F32), short, cu_h, n, g)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        bd.topp_select(torch.zeros(NBT, dtype=F32), short, CU, N, G, 0.9)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        bd.expand_compact(torch.zeros(1300, 8, dtype=BF), None, torch.zeros(NBT, dtype=U8), short,
+                          torch.zeros(3, dtype=I32), CU, G)
