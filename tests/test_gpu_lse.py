@@ -65,8 +65,15 @@ def test_given_lse_pass_matches_oracle(case):
     lengths, Hq, Hkv, d, n, G, p = case
     b = _batch(lengths, Hq, Hkv, d, n, G, seed=len(lengths) * 7 + d)
     say(f"[case] given-lse pass {case}")
+    _check_given_lse(b, p, H=128, label=str(case))
+
+
+def _check_given_lse(b, p, H, label):
+    """The decision from the oracle's log-sum-exp (float32) against the oracle's
+    given-lse scores, its cut and the compaction."""
+    Hq, Hkv, d, n, G = b.Hq, b.Hkv, b.d, b.n, b.G
     lse32 = _lse_f32(b)
-    gb = GpuBatch(b, H=128)
+    gb = GpuBatch(b, H=H)
     dec = up.LayerDecision(gb.qwin, gb.k, gb.cu, gb.cu_h, gb.hidden, gb.pos, n, G, p,
                            row_lse=torch.from_numpy(lse32).cuda())
     dec.run()
@@ -86,7 +93,7 @@ def test_given_lse_pass_matches_oracle(case):
     res = dict(scores=s_gpu, keep=keep, cu_out=dec.cu_out.cpu().numpy(), count=cnt, dec=dec)
     np.testing.assert_array_equal(res["cu_out"], own_cu)
     check_compaction(gb, res)
-    say(f"[ok] given-lse {case}: worst rel err {worst:.2e}, ambiguous {len(amb)}, "
+    say(f"[ok] given-lse {label}: worst rel err {worst:.2e}, ambiguous {len(amb)}, "
         f"differing {ndiff}")
 
 
@@ -123,3 +130,42 @@ def test_given_lse_pass_at_128k():
     _, s64, _ = O.block_scores(b.qwin, b.k, b.cu_seqlens, b.Hq, b.Hkv, b.d, b.n, b.G)
     worst = check_scores(s_lse.cpu().numpy(), s64)
     say(f"[ok] 128K given-lse vs oracle: worst rel err {worst:.2e}")
+
+
+def _random_lse_configs(count=12, seed=4242):
+    """Seeded draws: 1-4 requests of 0-3000 tokens, GQA group sizes 1-8, every head
+    dimension, windows of 1-260, block sizes 32-1024 and p in [0.3, 1]."""
+    rng = np.random.default_rng(seed)
+    heads = [(8, 2), (4, 1), (4, 4), (12, 4), (16, 2), (6, 3)]
+    out = []
+    while len(out) < count:
+        B = int(rng.integers(1, 5))
+        lengths = [int(x) for x in rng.integers(0, 3001, B)]
+        Hq, Hkv = heads[int(rng.integers(len(heads)))]
+        d = int(rng.choice([64, 128, 256]))
+        n = int(rng.integers(1, 261))
+        if sum(L * Hq * min(L, n) * d for L in lengths) > 1.0e9:
+            continue
+        out.append((lengths, Hq, Hkv, d, n, 32 * int(rng.integers(1, 33)),
+                    float(np.float32(rng.uniform(0.3, 1.0))), int(rng.integers(1 << 30))))
+    return out
+
+
+RANDOM_LSE = _random_lse_configs()
+
+
+@pytest.mark.parametrize("case", RANDOM_LSE, ids=[f"r{i}" for i in range(len(RANDOM_LSE))])
+def test_random_configurations_row_lse_and_given_lse(case):
+    """Per seeded draw: the full pass's row log-sum-exp output against the oracle's, and
+    the decision from the oracle's log-sum-exp against the oracle's given-lse scores."""
+    lengths, Hq, Hkv, d, n, G, p, seed = case
+    b = _batch(lengths, Hq, Hkv, d, n, G, seed=seed)
+    say(f"[case] random lse {case}")
+    gb = GpuBatch(b)
+    lse = torch.empty((b.qwin.shape[0], Hq), dtype=torch.float32, device="cuda")
+    up.block_scores(gb.qwin, gb.k, gb.cu, gb.cu_h, n, G, row_lse=lse)
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    ref = O.row_lse(b.qwin, b.k, b.cu_seqlens, Hq, Hkv, d, n)
+    np.testing.assert_allclose(lse.cpu().numpy().astype(np.float64), ref, rtol=1e-5, atol=1e-4)
+    _check_given_lse(b, p, H=int(8 + seed % 41), label=f"random {case}")
