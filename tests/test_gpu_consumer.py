@@ -261,3 +261,41 @@ def test_swiglu_ffn_matches_oracle(R, H, F):
     err = np.abs(_to_f64(y) - ref)
     tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -7 * mag + 1e-30
     assert (err <= tol).all(), f"worst excess {float((err - tol).max()):.3e}"
+
+
+def _random_dense_shapes(seed=515):
+    """Seeded draws for the dense calls: GEMMs of 1-3000 rows with K and N multiples of 8
+    up to 2048 (half with a residual), gates of 1-2000 rows with F a multiple of 8 up to
+    3000, and FFNs of 1-700 rows with H a multiple of 64 and F a multiple of 8."""
+    rng = np.random.default_rng(seed)
+    lin = [(int(rng.integers(1, 3001)), 8 * int(rng.integers(1, 257)), 8 * int(rng.integers(1, 257)),
+            bool(rng.random() < 0.5)) for _ in range(8)]
+    gate = [(int(rng.integers(1, 2001)), 8 * int(rng.integers(1, 376))) for _ in range(6)]
+    ffn = [(int(rng.integers(1, 701)), 64 * int(rng.integers(1, 17)), 8 * int(rng.integers(1, 257)))
+           for _ in range(4)]
+    return lin, gate, ffn
+
+
+RANDOM_LIN, RANDOM_GATE, RANDOM_FFN = _random_dense_shapes()
+
+
+@pytest.mark.parametrize("R,K,N,res", RANDOM_LIN, ids=[f"r{i}" for i in range(len(RANDOM_LIN))])
+def test_random_linear_shapes(R, K, N, res):
+    test_linear_matches_oracle(R, K, N, res)
+
+
+@pytest.mark.parametrize("R,F", RANDOM_GATE, ids=[f"r{i}" for i in range(len(RANDOM_GATE))])
+def test_random_swiglu_shapes(R, F):
+    say(f"[case] swiglu R={R} F={F}")
+    rng = np.random.default_rng(R * 7 + F)
+    gu = synth.f32_to_bf16_bits((rng.standard_normal((R, 2 * F)) * 3).astype(np.float32))
+    a = up.swiglu(bf16_dev(gu).view(R, 2 * F))
+    torch.cuda.synchronize()
+    g = C.bits_to_f64(gu)
+    exact = C.silu(g[:, :F]) * g[:, F:]
+    assert (np.abs(_to_f64(a) - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-30).all()
+
+
+@pytest.mark.parametrize("R,H,F", RANDOM_FFN, ids=[f"r{i}" for i in range(len(RANDOM_FFN))])
+def test_random_swiglu_ffn_shapes(R, H, F):
+    test_swiglu_ffn_matches_oracle(R, H, F)
