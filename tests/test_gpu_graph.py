@@ -129,3 +129,44 @@ def test_rope_attention_replays_match_eager():
         assert up.device_error() == 0
         assert torch.equal(out, want), f"replay {r} differs"
     say(f"[ok] rotary attention: {REPLAYS} replays equal the eager call")
+
+
+def test_paged_score_passes_replay_match_eager():
+    """Both paged score passes (row statistics computed, and given) in one graph, as a
+    serving loop over a paged cache would capture them."""
+    from tests.test_gpu_paged import _bf16, _paginate
+    say("[case] graph replay: paged score passes")
+    b = _batch([3000, 0, 1234], 8, 2, 128, 128, 64, seed=17)
+    gb = GpuBatch(b)
+    pages, table = _paginate(b.k, b.cu_seqlens, 32, seed=5)
+    pg, tb = _bf16(pages), i32_dev(table)
+    nbt = int(sum((int(L) + 63) // 64 for L in np.diff(b.cu_seqlens)))
+    lse = torch.empty((b.qwin.shape[0], 8), dtype=torch.float32, device="cuda")
+    s_full = torch.empty(nbt, dtype=torch.float32, device="cuda")
+    s_given = torch.empty_like(s_full)
+    ws = torch.empty(up.block_scores_workspace_bytes(b.cu_seqlens, 8, 2, 128, 128, 64),
+                     dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(max(1, up.block_scores_lse_workspace_bytes(b.cu_seqlens, 8, 2, 128, 128, 64)),
+                      dtype=torch.uint8, device="cuda")
+
+    def run():
+        up.block_scores_paged(gb.qwin, pg, tb, gb.cu, gb.cu_h, 128, 64, out=s_full, workspace=ws,
+                              row_lse=lse)
+        up.block_scores_lse_paged(gb.qwin, pg, tb, lse, gb.cu, gb.cu_h, 128, 64, out=s_given,
+                                  workspace=ws2)
+    run()
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    want = (s_full.clone(), lse.clone(), s_given.clone())
+    g = _capture(run)
+    for r in range(REPLAYS):
+        s_full.fill_(-1.0)
+        lse.fill_(-1.0)
+        s_given.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert up.device_error() == 0
+        for got, w, name in zip((s_full, lse, s_given), want, ("scores", "row_lse", "given")):
+            assert torch.equal(got, w), f"replay {r}: {name} differs"
+    say(f"[ok] paged score passes: {REPLAYS} replays equal the eager calls")
