@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     UniPrefillError,
     LayerDecision,
     block_scores,
+    block_scores_chunks,
     block_scores_lse,
     block_scores_lse_paged,
     block_scores_paged,

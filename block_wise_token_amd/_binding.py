@@ -43,6 +43,8 @@ def lib():
     L.up_block_scores.restype = ci
     L.up_block_scores.argtypes = [vp, vp, i32p, vp, ci, ci, ci, ci, ci, ci, cf, f32p, f32p, vp, cs,
                                   vp]
+    L.up_block_scores_chunks.restype = ci
+    L.up_block_scores_chunks.argtypes = [vp, ci, ci, ci, ci, ci, ci, vp]
     L.up_block_scores_paged.restype = ci
     L.up_block_scores_paged.argtypes = [vp, vp, ctypes.c_int64, ci, i32p, ci, i32p, vp, ci, ci, ci,
                                         ci, ci, ci, cf, f32p, f32p, vp, cs, vp]
@@ -167,6 +169,17 @@ class _HostCu:
 
     def win_rows(self, n: int) -> int:
         return int(sum(min(int(n), int(L)) for L in np.diff(self.arr)))
+
+
+def block_scores_chunks(cu_h, Hq, Hkv, d, n, G) -> np.ndarray:
+    """Per-request statistics-chunk length in blocks (int32 [B]); see
+    up_block_scores_chunks.  Host only."""
+    h = _HostCu(cu_h)
+    out = np.zeros(max(h.B, 0), dtype=np.int32)
+    _check(lib().up_block_scores_chunks(h.ptr, h.B, Hq, Hkv, d, n, G,
+                                        out.ctypes.data_as(ctypes.c_void_p)),
+           "up_block_scores_chunks")
+    return out
 
 
 def block_scores_workspace_bytes(cu_h, Hq, Hkv, d, n, G) -> int:

@@ -125,61 +125,63 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
   s->kt = (d == 256) ? 1 : (G % 64 == 0 ? 2 : 1);
   s->rows_wg = score_rows_wg(d);
   const int64_t gs = Hq / Hkv;
-  // Key-chunk length (blocks per workgroup).  score_wgs_per_cu(d) workgroups fill a
-  // CU, so the score pass takes ceil(items / slots) rounds, each costing CB blocks of
-  // work plus a workgroup's fixed cost (query load, ring fill, chunk-end stores),
-  // measured at about kChunkOverheadBlocks blocks: pick the CB that minimises
-  // rounds * (CB + overhead) (ties: the larger CB).  Short requests that leave most
-  // CUs idle get chunks of a few blocks (a 4096-token request: 128 one-block
-  // workgroups rather than 16 of eight blocks, which takes half the time).  The
-  // candidates are 1..256 in steps of about 1.25x (plus the longest request's block
-  // count), which keeps planning linear in B with a small constant.
+  // Statistics chunks per request (from the request alone, stat_chunk_blocks), then a
+  // target work-item length TB for load balance: every request's items are whole runs
+  // of its statistics chunks (chunks_per_item).  TB minimises the estimated time,
+  // rounds of the device's CUs times the mean item cost (blocks plus a workgroup's
+  // fixed cost), ties going to the longer item; it never changes a result.  For a
+  // lone request on 256 CUs it picks one chunk per item.
+  const int64_t cus = (int64_t)device_cus() * score_wgs_per_cu(d);
+  struct Req { int64_t nb, per; int cbs; int64_t nch; };
+  std::vector<Req> req(B);
+  for (int i = 0; i < B; ++i) {
+    const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
+    const int64_t W = L < n ? L : n;
+    Req r;
+    r.nb = (L + G - 1) / G;
+    r.per = Hkv * ((gs * W + s->rows_wg - 1) / s->rows_wg);   // items per chunk position
+    r.cbs = stat_chunk_blocks(r.nb, r.per);
+    r.nch = (r.nb + r.cbs - 1) / r.cbs;
+    req[i] = r;
+  }
   {
-    constexpr int kChunkOverheadBlocks = 3;
-    const int64_t cus = (int64_t)device_cus() * score_wgs_per_cu(d);
-    int64_t nb_max = 0;
-    for (int i = 0; i < B; ++i) {
-      const int64_t nb = ((int64_t)cu_h[i + 1] - cu_h[i] + G - 1) / G;
-      if (nb > nb_max) nb_max = nb;
-    }
-    static const int kCand[] = {256, 224, 192, 160, 128, 112, 96, 80, 64, 56, 48, 40, 32,
-                                28, 24, 20, 16, 14, 12, 10, 8, 6, 4, 3, 2, 1};
-    int cands[sizeof(kCand) / sizeof(kCand[0]) + 1];
-    int nc = 0;
-    for (int cb : kCand) cands[nc++] = cb;
-    if (nb_max > 1 && nb_max < kMaxChunkBlocks) cands[nc++] = (int)nb_max;
-    // Per request: blocks and workgroups per key chunk (kv heads x row tiles).
-    std::vector<std::pair<int64_t, int64_t>> req(B);
-    for (int i = 0; i < B; ++i) {
-      const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
-      const int64_t W = L < n ? L : n;
-      req[i] = {(L + G - 1) / G, Hkv * ((gs * W + s->rows_wg - 1) / s->rows_wg)};
-    }
-    int64_t best_cost = -1;
-    int best_cb = 1;
-    for (int ci = 0; ci < nc; ++ci) {
-      const int cb = cands[ci];
-      int64_t items = 0;
-      for (const auto& r : req) items += (r.first + cb - 1) / cb * r.second;
-      const int64_t cost = (items + cus - 1) / cus * (cb + kChunkOverheadBlocks);
-      if (best_cost < 0 || cost < best_cost || (cost == best_cost && cb > best_cb)) {
+    static const int kTb[] = {256, 224, 192, 160, 128, 112, 96, 80, 64, 56, 48, 40, 32,
+                              28, 24, 20, 16, 14, 12, 10, 8, 6, 4, 3, 2, 1};
+    double best_cost = -1.0;
+    int best_tb = 1;
+    for (int tb : kTb) {
+      int64_t items = 0, work = 0;
+      for (const Req& r : req) {
+        if (r.nb == 0) continue;
+        const int cps = chunks_per_item(r.cbs, r.nch, tb);
+        const int64_t n_it = (r.nch + cps - 1) / cps;
+        const int64_t len = std::min<int64_t>((int64_t)cps * r.cbs, r.nb);
+        items += n_it * r.per;
+        work += n_it * r.per * (len + kChunkOverheadBlocks);
+      }
+      const double cost = items ? (double)((items + cus - 1) / cus) * ((double)work / items) : 0.0;
+      if (best_cost < 0 || cost < best_cost * (1.0 - 1e-9) ||
+          (cost <= best_cost * (1.0 + 1e-9) && tb > best_tb)) {
         best_cost = cost;
-        best_cb = cb;
+        best_tb = tb;
       }
     }
-    s->CB = best_cb;
+    s->TB = best_tb;
   }
   *t = Totals{};
   for (int i = 0; i < B; ++i) {
     const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
     const int64_t W = L < n ? L : n;
-    const int64_t nb = (L + G - 1) / G;
-    const int64_t nch = (nb + s->CB - 1) / s->CB;
+    const Req& r = req[i];
+    const int64_t nb = r.nb;
+    const int64_t nch = r.nch;
+    const int cps = chunks_per_item(r.cbs, nch, s->TB);
+    const int64_t n_it = (nch + cps - 1) / cps;
     const int64_t R = gs * W;
     const int64_t nrt = (R + s->rows_wg - 1) / s->rows_wg;
     t->win_rows += W;
     t->nb_tot += nb;
-    t->items += nch * Hkv * nrt;
+    t->items += n_it * Hkv * nrt;
     t->ml_pairs += nb * Hkv * R;
     t->cs_pairs += nch * Hkv * R;
     t->pm_parts += nb * Hkv * nrt;
@@ -219,6 +221,23 @@ size_t up_block_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int
   Totals t;
   if (plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t) != UP_OK) return 0;
   return score_ws_layout(B, t).total;
+}
+
+int up_block_scores_chunks(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d, int n,
+                           int G, int32_t* chunk_blocks_h) {
+  ScoreShape s;
+  Totals t;
+  const int st = plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t);
+  if (st != UP_OK) return st;
+  if (B > 0 && !chunk_blocks_h) return UP_EINVAL;
+  const int64_t gs = Hq / Hkv;
+  for (int i = 0; i < B; ++i) {
+    const int64_t L = (int64_t)cu_seqlens_h[i + 1] - cu_seqlens_h[i];
+    const int64_t W = L < n ? L : n;
+    const int64_t nrt = (gs * W + s.rows_wg - 1) / s.rows_wg;
+    chunk_blocks_h[i] = stat_chunk_blocks((L + G - 1) / G, Hkv * nrt);
+  }
+  return UP_OK;
 }
 
 // stop_at_mass: leave the float64 block masses in the workspace and skip the
@@ -456,8 +475,8 @@ int up_expand_compact(const void* hidden, int H, int elem_bytes, const int32_t* 
   });
   if (e != hipSuccess) return UP_EHIP;
   e = timed(7, hs, [&] {
-    return launch_gather(hidden, row_bytes, pos, workspace, L, sp.nb_tot, G, idx_out, hidden_out,
-                         pos_out, prev_orig, orig_out, hs);
+    return launch_gather(hidden, row_bytes, pos, workspace, L, sp.nb_tot, G, sp.T, idx_out,
+                         hidden_out, pos_out, prev_orig, orig_out, err, hs);
   });
   return e == hipSuccess ? UP_OK : UP_EHIP;
 }
@@ -513,10 +532,9 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
   const int64_t row_bytes = (int64_t)H * elem_bytes;
   if (sp.T > 0 && sp.T * row_bytes / row_bytes != sp.T) return UP_EUNSUPPORTED;
   char* cws = static_cast<char*>(workspace) + LS.total;
-  // One request of at most 4096 blocks can have its normalisation and block
-  // destinations done inside the select kernel (kFusedSelect).  That path is switched
-  // off: a benchmark run that first used it left the GPU faulted and no cause has been
-  // shown, so every shape takes the three calls in sequence.
+  // One request of at most 4096 blocks has its normalisation and block destinations
+  // done inside the select kernel (kFusedSelect): the score pass stops at the float64
+  // masses and the normalise and block-destination launches are not needed.
   if (!kFusedSelect || B != 1 || t.T == 0 || sp.nb_tot > kFusedSelectMaxBlocks) {
     st = block_scores_common(qwin, k, nullptr, cu_seqlens, cu_seqlens_h, B, Hq, Hkv, d, n, G,
                              scale, scores, nullptr, workspace, LS.total, stream);
@@ -548,8 +566,8 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
   });
   if (e != hipSuccess) return UP_EHIP;
   e = timed(7, hs, [&] {
-    return launch_gather(hidden, row_bytes, pos, cws, LC, sp.nb_tot, G, idx_out, hidden_out,
-                         pos_out, prev_orig, orig_out, hs);
+    return launch_gather(hidden, row_bytes, pos, cws, LC, sp.nb_tot, G, sp.T, idx_out,
+                         hidden_out, pos_out, prev_orig, orig_out, err, hs);
   });
   return e == hipSuccess ? UP_OK : UP_EHIP;
 }

@@ -165,7 +165,7 @@ __global__ __launch_bounds__(NT) void up_gather_kernel(
     const int32_t* __restrict__ src, const int32_t* __restrict__ len, int split,
     int32_t* __restrict__ idx_out, uint8_t* __restrict__ hidden_out,
     int32_t* __restrict__ pos_out, const int32_t* __restrict__ prev_orig,
-    int32_t* __restrict__ orig_out) {
+    int32_t* __restrict__ orig_out, int64_t cap, int64_t T_in, int* __restrict__ err) {
   if (hdr->valid != 1) return;
   const int64_t blk = blockIdx.x / split;
   const int part = (int)(blockIdx.x % split);
@@ -173,6 +173,12 @@ __global__ __launch_bounds__(NT) void up_gather_kernel(
   if (d < 0) return;
   const int64_t s = src[blk];
   const int n = len[blk];
+  // The header says the run table is consistent; a run that would still land outside
+  // the outputs (capacity cap rows) or read outside the input (T_in rows) is refused.
+  if (n < 0 || s < 0 || (int64_t)d + n > cap || s + n > T_in) {
+    if (part == 0 && threadIdx.x == 0) atomicOr(err, 16);
+    return;
+  }
   const int64_t nvec = (int64_t)n * row_bytes / (int64_t)sizeof(V);
   const int64_t lo = nvec * part / split, hi = nvec * (part + 1) / split;
   const V* sp = reinterpret_cast<const V*>(hidden + s * row_bytes);
@@ -243,9 +249,9 @@ hipError_t launch_block_dst(const uint8_t* keep, const int32_t* cu, const int32_
 }
 
 hipError_t launch_gather(const void* hidden, int64_t row_bytes, const int32_t* pos, void* ws,
-                         const CompactWs& L, int64_t nb_tot, int G, int32_t* idx_out,
+                         const CompactWs& L, int64_t nb_tot, int G, int64_t T, int32_t* idx_out,
                          void* hidden_out, int32_t* pos_out, const int32_t* prev_orig,
-                         int32_t* orig_out, hipStream_t st) {
+                         int32_t* orig_out, int* err, hipStream_t st) {
   if (nb_tot == 0) return hipSuccess;
   // Many small workgroups (4 KiB each, two 16-byte vectors per lane in flight)
   // stream fastest on MI355X: about 6.5 TB/s read+write for a plain 1 GiB copy.
@@ -265,13 +271,13 @@ hipError_t launch_gather(const void* hidden, int64_t row_bytes, const int32_t* p
   const uintptr_t al = reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(hidden_out);
   if (row_bytes % 16 == 0 && al % 16 == 0) {
     hipLaunchKernelGGL((up_gather_kernel<u32x4, NT, 2>), grid, dim3(NT), 0, st, h, row_bytes, pos,
-                       hdr, dst, src, len, split, idx_out, ho, pos_out, prev_orig, orig_out);
+                       hdr, dst, src, len, split, idx_out, ho, pos_out, prev_orig, orig_out, T, T, err);
   } else if (row_bytes % 4 == 0 && al % 4 == 0) {
     hipLaunchKernelGGL((up_gather_kernel<uint32_t, NT, 4>), grid, dim3(NT), 0, st, h, row_bytes,
-                       pos, hdr, dst, src, len, split, idx_out, ho, pos_out, prev_orig, orig_out);
+                       pos, hdr, dst, src, len, split, idx_out, ho, pos_out, prev_orig, orig_out, T, T, err);
   } else {
     hipLaunchKernelGGL((up_gather_kernel<uint8_t, NT, 4>), grid, dim3(NT), 0, st, h, row_bytes,
-                       pos, hdr, dst, src, len, split, idx_out, ho, pos_out, prev_orig, orig_out);
+                       pos, hdr, dst, src, len, split, idx_out, ho, pos_out, prev_orig, orig_out, T, T, err);
   }
   return hipGetLastError();
 }

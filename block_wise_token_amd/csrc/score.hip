@@ -62,41 +62,95 @@ __device__ __forceinline__ int request_of_item(const ReqPlan* __restrict__ plan,
 // ---------------------------------------------------------------------------
 // Plan
 // ---------------------------------------------------------------------------
-__global__ void up_score_plan_kernel(const int32_t* __restrict__ cu, ScoreShape s, Totals host,
-                                     WsHeader* __restrict__ hdr, ReqPlan* __restrict__ plan,
-                                     int* __restrict__ err) {
-  if (threadIdx.x != 0) return;
+// One workgroup of kPlanThreads; requests are taken kPlanThreads at a time, thread t
+// planning request base + t, and the per-request counts are scanned into offsets
+// (DPP within each wave, the wave totals through LDS, a carry between rounds).
+constexpr int kPlanThreads = 256;
+
+__global__ __launch_bounds__(kPlanThreads) void up_score_plan_kernel(
+    const int32_t* __restrict__ cu, ScoreShape s, Totals host, WsHeader* __restrict__ hdr,
+    ReqPlan* __restrict__ plan, int* __restrict__ err) {
+  constexpr int NW = kPlanThreads / 64;
+  constexpr int NV = 6;   // scanned quantities: W, nb, items, ml, cs, pm
+  __shared__ int64_t wtot[NV][NW];
+  __shared__ int bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gs = s.Hq / s.Hkv;
-  bool ok = (cu[0] == 0);
-  int64_t win = 0, blk = 0, items = 0, mlp = 0, csp = 0, pmp = 0;
-  for (int i = 0; i < s.B; ++i) {
-    const int32_t a = cu[i], b = cu[i + 1];
-    int64_t L = (int64_t)b - a;
-    if (L < 0) { ok = false; L = 0; }
-    const int64_t W = L < s.n ? L : s.n;
-    const int64_t nb = (L + s.G - 1) / s.G;
-    const int64_t nch = (nb + s.CB - 1) / s.CB;
-    const int64_t R = gs * W;
-    const int64_t nrt = (R + s.rows_wg - 1) / s.rows_wg;
-    items += nch * s.Hkv * nrt;
-    ReqPlan p;
-    p.tok_off = a; p.L = (int32_t)L; p.W = (int32_t)W; p.win_off = (int32_t)win;
-    p.blk_off = (int32_t)blk; p.nb = (int32_t)nb; p.nch = (int32_t)nch;
-    p.item_end = (int32_t)items; p.ml_off = mlp; p.cs_off = csp; p.pm_off = pmp;
-    plan[i] = p;
-    win += W; blk += nb; mlp += nb * s.Hkv * R; csp += nch * s.Hkv * R; pmp += nb * s.Hkv * nrt;
+  if (tid == 0) bad = cu[0] != 0;
+  __syncthreads();
+  int64_t carry[NV] = {0, 0, 0, 0, 0, 0};
+  for (int base = 0; base < s.B; base += kPlanThreads) {
+    const int i = base + tid;
+    int64_t v[NV] = {0, 0, 0, 0, 0, 0};
+    ReqPlan p{};
+    if (i < s.B) {
+      const int32_t a = cu[i], b = cu[i + 1];
+      int64_t L = (int64_t)b - a;
+      if (L < 0) { atomicOr(&bad, 1); L = 0; }
+      const int64_t W = L < s.n ? L : s.n;
+      const int64_t nb = (L + s.G - 1) / s.G;
+      const int64_t R = gs * W;
+      const int64_t nrt = (R + s.rows_wg - 1) / s.rows_wg;
+      const int cbs = stat_chunk_blocks(nb, s.Hkv * nrt);
+      const int64_t nch = (nb + cbs - 1) / cbs;
+      const int cps = chunks_per_item(cbs, nch, s.TB);
+      v[0] = W;
+      v[1] = nb;
+      v[2] = (nch + cps - 1) / cps * s.Hkv * nrt;
+      v[3] = nb * s.Hkv * R;
+      v[4] = nch * s.Hkv * R;
+      v[5] = nb * s.Hkv * nrt;
+      p.tok_off = a; p.L = (int32_t)L; p.W = (int32_t)W; p.nb = (int32_t)nb;
+      p.nch = (int32_t)nch; p.cbs = cbs; p.cps = cps;
+    }
+    int64_t inc[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      inc[q] = (int64_t)wave_scan_u64((uint64_t)v[q]);
+      if (lane == 63) wtot[q][wave] = inc[q];
+    }
+    __syncthreads();
+    int64_t pre[NV], tot[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      pre[q] = carry[q];
+      tot[q] = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int64_t t = wtot[q][w];
+        pre[q] += w < wave ? t : 0;
+        tot[q] += t;
+      }
+    }
+    __syncthreads();   // the next round overwrites wtot
+    if (i < s.B) {
+      p.win_off = (int32_t)(pre[0] + inc[0] - v[0]);
+      p.blk_off = (int32_t)(pre[1] + inc[1] - v[1]);
+      p.item_end = (int32_t)(pre[2] + inc[2]);            // inclusive
+      p.ml_off = pre[3] + inc[3] - v[3];
+      p.cs_off = pre[4] + inc[4] - v[4];
+      p.pm_off = pre[5] + inc[5] - v[5];
+      plan[i] = p;
+    }
+#pragma unroll
+    for (int q = 0; q < NV; ++q) carry[q] += tot[q];
   }
-  ok = ok && (int64_t)cu[s.B] == host.T && win == host.win_rows && blk == host.nb_tot &&
-       items == host.items && mlp == host.ml_pairs && csp == host.cs_pairs &&
-       pmp == host.pm_parts;
-  hdr->valid = ok ? 1 : 0;
-  if (!ok) atomicOr(err, 1);
+  __syncthreads();
+  if (tid == 0) {
+    const bool ok = !bad && (int64_t)cu[s.B] == host.T && carry[0] == host.win_rows &&
+                    carry[1] == host.nb_tot && carry[2] == host.items &&
+                    carry[3] == host.ml_pairs && carry[4] == host.cs_pairs &&
+                    carry[5] == host.pm_parts;
+    hdr->valid = ok ? 1 : 0;
+    if (!ok) atomicOr(err, 1);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Partial statistics on the matrix cores
 //
-// Workgroup = NW waves = one (request, kv head g, query-row tile, key chunk).  Each
+// Workgroup = NW waves = one (request, kv head g, query-row tile, work item: a run of
+// the request's statistics chunks, see stat_chunk_blocks).  Each
 // wave holds QT tiles of 32 query rows of kv head g's group in VGPRs as the B
 // operand (rows r = j * gs + hh: window row j, head g*gs + hh).  Keys stream through
 // a ring of NS LDS stages of 64 keys: each stage is copied straight from global
@@ -113,12 +167,14 @@ __global__ void up_score_plan_kernel(const int32_t* __restrict__ cu, ScoreShape 
 //
 // Softmax statistics: one running reference Rs per query (log2 units), the same in
 // both lanes of the query, and each lane's sums l = sum 2^(x - Rs) over its keys of
-// the current block and chunk.  Any reference gives the same (reference, sum) value,
-// so there is no per-block max pass; only when a half's sum leaves [0, 2^64]
-// (overflow, or the unset reference of a chunk's first half) does the wave rebase
-// the affected queries on the pair's maximum (a wave-uniform branch, rare).  At a
-// block end the partner lane's sum is added with v_permlane32_swap and one lane
-// stores (Rs, l_b); the chunk sums are stored likewise at the chunk end.
+// the current block and statistics chunk.  Any reference gives the same (reference,
+// sum) value, so there is no per-block max pass; only when a half's sum leaves
+// [0, 2^64] (overflow, or the unset reference of a statistics chunk's first half)
+// does the wave rebase the affected queries on the pair's maximum (a wave-uniform
+// branch, rare).  At a block end the partner lane's sum is added with
+// v_permlane32_swap and one lane stores (Rs, l_b); at a statistics chunk's end its
+// sums are stored likewise and the reference is reset, so every stored value depends
+// only on the keys of its own chunk, whatever work item the chunk ran in.
 //
 // The head dimension is contracted in a permuted order that both operands share:
 // lane half h, k-step s holds d-elements [h*D/2 + 8s, h*D/2 + 8s + 8), so every
@@ -211,7 +267,7 @@ template <int D, int QT, int NS, int NW, bool LSE, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
     const uint16_t* __restrict__ qwin, const uint16_t* __restrict__ kmat,
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
-    int G, int CB, float c, float2* __restrict__ ml, float2* __restrict__ cs,
+    int G, float c, float2* __restrict__ ml, float2* __restrict__ cs,
     const float* __restrict__ row_lse, float* __restrict__ pm,
     const int32_t* __restrict__ btab, int max_pages, int lps, int64_t num_pages,
     int* __restrict__ err) {
@@ -241,7 +297,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   const int g = xl % Hkv;
   xl /= Hkv;
   const int rt = xl % nrt;
-  const int ch = xl / nrt;
+  const int it = xl / nrt;              // work item within the (request, kv head, row tile)
+  const int ch0 = it * pr.cps;          // its first statistics chunk
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -272,8 +329,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   // Q is in registers before any K copy is issued: the waits below count K copies only.
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
 
-  const int b0 = ch * CB;
-  const int b1 = min(pr.nb, b0 + CB);
+  const int b0 = ch0 * pr.cbs;
+  const int b1 = min(pr.nb, b0 + pr.cps * pr.cbs);
   const int k0 = b0 * G;
   const int kend = min(b1 * G, pr.L);
   const int nh = (kend - k0 + 31) / 32;          // 32-key halves in this chunk
@@ -393,9 +450,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
   const bool st_ok = (QT == 2 || half == 0) && (r_st < R);
 
   int hcnt = G / 32;   // halves left in the current block
-  // Blocks end one at a time in order: the chunk-relative index of the next block to
+  // Blocks end one at a time in order: the item-relative index of the next block to
   // end, and (full pass) where its (m, l) pair goes, advanced by one block per end.
   int blk_rel = 0;
+  int ccnt = pr.cbs;   // blocks left in the current statistics chunk
+  int chk = ch0;       // the current statistics chunk
   int64_t ml_at = st_ok ? pr.ml_off + ((int64_t)b0 * Hkv + g) * R + r_st : -1;
   const int64_t ml_step = (int64_t)Hkv * R;
   f32x16 acc0[QT], acc1[QT];
@@ -517,6 +576,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
       pend_v = make_float2(lst > 0.f ? mst : kNegInf, lst);
       pend_i = ml_at;
       if (st_ok) ml_at += ml_step;
+      if (--ccnt == 0 || h == nh - 1) {
+        // End of a statistics chunk: store its merged pair (the two lanes of a query
+        // share the reference; add their sums), then restart the reference so the next
+        // chunk's statistics depend on its own keys only.
+        float mc = 0.f, lc = 0.f;
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+          const float lp = pair_sum(Lch[t]);
+          if (t == t_st) { mc = Rs[t]; lc = lp; }
+          Rs[t] = kNegInf;
+          Lch[t] = 0.f;
+        }
+        if (st_ok)
+          cs[pr.cs_off + ((int64_t)chk * Hkv + g) * R + r_st] =
+              make_float2(lc > 0.f ? mc : kNegInf, lc);
+        ++chk;
+        ccnt = pr.cbs;
+      }
     }
   };
 
@@ -607,17 +684,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
       for (int w = 1; w < NW; ++w) v += blk_acc[b * NW + w];
       pm[pr.pm_off + (int64_t)(g * nrt + rt) * pr.nb + b0 + b] = v;   // part-major
     }
-  } else {
-    // Chunk statistics: the two lanes of each query share the reference; add their sums.
-    float mst = 0.f, lst = 0.f;
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      const float lp = pair_sum(Lch[t]);
-      if (t == t_st) { mst = Rs[t]; lst = lp; }
-    }
-    if (st_ok)
-      cs[pr.cs_off + ((int64_t)ch * Hkv + g) * R + r_st] =
-          make_float2(lst > 0.f ? mst : kNegInf, lst);
   }
 }
 
@@ -835,7 +901,7 @@ static inline char* wsb(void* ws) { return static_cast<char*>(ws); }
 
 hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Totals& t, void* ws,
                              size_t plan_off, int* err, hipStream_t st) {
-  hipLaunchKernelGGL(up_score_plan_kernel, dim3(1), dim3(64), 0, st, cu, s, t,
+  hipLaunchKernelGGL(up_score_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, cu, s, t,
                      reinterpret_cast<WsHeader*>(wsb(ws)),
                      reinterpret_cast<ReqPlan*>(wsb(ws) + plan_off), err);
   return hipGetLastError();
@@ -861,7 +927,7 @@ static hipError_t launch_partial_t(const void* qwin, const void* k, const ScoreS
                      st, static_cast<const uint16_t*>(qwin), static_cast<const uint16_t*>(k),
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + o.plan_off), s.B, s.Hq, s.Hkv,
-                     s.G, s.CB, c, o.ml, o.cs, o.row_lse, o.pm, o.pk.table, o.pk.max_pages,
+                     s.G, c, o.ml, o.cs, o.row_lse, o.pm, o.pk.table, o.pk.max_pages,
                      o.pk.log2_page, o.pk.num_pages, o.pk.err);
   return hipGetLastError();
 }
@@ -871,7 +937,6 @@ static hipError_t launch_partial_d(const void* qwin, const void* k, const ScoreS
                                    const Totals& t, void* ws, const PartialOut& o, float c,
                                    hipStream_t st) {
   if (t.items == 0) return hipSuccess;
-  if (s.CB > kMaxChunkBlocks) return hipErrorInvalidValue;
   switch (s.d) {
     case 64: return launch_partial_t<64, 2, 8, 8, LSE, PAGED>(qwin, k, s, t, ws, o, c, st);
     case 128: return launch_partial_t<128, 2, 4, 8, LSE, PAGED>(qwin, k, s, t, ws, o, c, st);

@@ -383,6 +383,11 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
           if (mode == 0) m += S.sum[dg * kCopies + k];
         }
       }
+      // The winning bin is read into a register right after the barrier that follows
+      // the atomicMin: thread 0 resets S.win at the start of the next pass, which it can
+      // reach once every wave has passed the pass's last barrier, so S.win must not be
+      // read after that barrier.
+      int win = kBins;
       if (mode == 0) {
         if (pass == 0) {
           const int sh = shift_of_exp((uint32_t)(dg >= 0 ? dg : 0));   // the digit is the exponent
@@ -393,7 +398,8 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
           const U192 P = u192_shl(sig_of(pb), shift_of_exp(pb >> 23));
           if (c > 0 && u192_geq(inc, P)) atomicMin(&S.win, tid);
           __syncthreads();
-          if (tid == S.win) {
+          win = S.win;
+          if (tid == win) {
             // What is left of p after every block of a higher exponent, in 2^sh units.
             S.rem = u192_shr_ceil(u192_sub(P, u192_sub(inc, v)), sh);
             S.prefix = (uint32_t)dg;
@@ -404,7 +410,8 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
           const uint64_t target = S.rem;
           if (c > 0 && inc >= target) atomicMin(&S.win, tid);
           __syncthreads();
-          if (tid == S.win) {
+          win = S.win;
+          if (tid == win) {
             S.rem = target - (inc - m);
             S.prefix = (pre << (hsh - dsh)) | (uint32_t)dg;
             S.ties = c;
@@ -415,14 +422,15 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
         const uint32_t target = S.rem_k;
         if (c > 0 && inc >= target) atomicMin(&S.win, tid);
         __syncthreads();
-        if (tid == S.win) {
+        win = S.win;
+        if (tid == win) {
           S.rem_k = target - (inc - c);
           S.prefix = pass == 0 ? (uint32_t)dg : ((pre << (hsh - dsh)) | (uint32_t)dg);
           S.ties = c;
         }
       }
       __syncthreads();
-      if (pass == 0 && S.win == kBins) {
+      if (pass == 0 && win == kBins) {
         // Every running sum stays below p: all blocks are kept.
         if (tid == 0) S.keep_all = 1;
         __syncthreads();
@@ -517,6 +525,7 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
     }
     __syncthreads();
     int64_t before = 0;   // kept tokens of all earlier slots
+    bool dst_bad = false;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       int64_t pre = before, slot = 0;
@@ -528,13 +537,23 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
       }
       const int64_t b = (int64_t)q * NT + tid;
       if (b < nb) {
-        fd.dst[b] = kl[q] ? (int32_t)(pre + (int64_t)(incl[q] - kl[q])) : -1;
+        const int64_t dd = pre + (int64_t)(incl[q] - kl[q]);
+        // A kept run must lie inside the kept-token count (which is at most T).
+        if (kl[q] && (dd < 0 || dd + kl[q] > total)) dst_bad = true;
+        fd.dst[b] = kl[q] ? (int32_t)dd : -1;
         fd.src[b] = (int32_t)(b * G);
         fd.len[b] = (int32_t)((L - b * G) < G ? (L - b * G) : G);
       }
       before += slot;
     }
-    if (tid == 0) fd.chdr->valid = 1;
+    // The slot totals must add up to the kept count, and every run must fit; only
+    // then may the gather use the destinations.
+    const int64_t nbad = block_sum_i64<NW>((dst_bad || before != total) ? 1 : 0, S);
+    if (tid == 0) {
+      const bool ok = nbad == 0 && total <= T_host;
+      fd.chdr->valid = ok ? 1 : 0;
+      if (!ok) atomicOr(err, 1);
+    }
   }
 }
 

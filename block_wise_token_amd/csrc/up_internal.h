@@ -22,12 +22,52 @@ struct ReqPlan {
   int32_t win_off;   // first window row of the request in qwin
   int32_t blk_off;   // first global block
   int32_t nb;        // blocks: ceil(L / G)
-  int32_t nch;       // key chunks: ceil(nb / CB)
+  int32_t nch;       // statistics chunks: ceil(nb / cbs)
   int32_t item_end;  // exclusive end of the request's work items of the score kernel
+  int32_t cbs;       // blocks per statistics chunk (a function of this request alone)
+  int32_t cps;       // statistics chunks per work item (load balance only)
   int64_t ml_off;    // first (m, l) pair of the request: pairs are [nb][Hkv][R], R = gs * W
   int64_t cs_off;    // first chunk-statistics pair: [nch][Hkv][R]
   int64_t pm_off;    // first block partial of the given-lse pass: [Hkv * nrt][nb]
 };
+
+// Largest work item (blocks per workgroup) of the score kernel.
+constexpr int kMaxChunkBlocks = 256;
+
+// Statistics chunks.  The score kernel restarts each query's softmax reference at
+// the first key of every statistics chunk and stores one merged pair per (row,
+// chunk); the row statistics merge the chunks in chunk order.  So a request's scores
+// depend on how its keys are cut into chunks, and that cut is made from the request
+// alone -- its block count and the call's per-chunk work (kv heads x row tiles) --
+// never from the other requests of a batch or from the device: the same request gets
+// bit-identical scores alone, packed with others, or on another GPU.  The cut is the
+// one a lone request would take to fill kStatCus compute units in one round: with
+// per = items per chunk position, floor(kStatCus / per) chunks, each ceil(nb / that)
+// blocks (1 to kMaxChunkBlocks).  More rounds would only add a workgroup's fixed cost
+// per round.  Work items (one workgroup each) are whole runs of statistics chunks,
+// sized by the planner for load balance; that choice moves work between workgroups
+// but never changes a result.
+constexpr int kStatCus = 256;
+constexpr int kChunkOverheadBlocks = 3;   // a workgroup's fixed cost, in blocks of work
+
+// nb < 2^31 (the host refuses larger requests): 32-bit divisions.
+__host__ __device__ inline int stat_chunk_blocks(int64_t nb, int64_t items_per_chunk) {
+  const uint32_t slots = items_per_chunk >= kStatCus || items_per_chunk <= 0
+                             ? 1u : (uint32_t)kStatCus / (uint32_t)items_per_chunk;
+  uint32_t cb = nb > 0 ? ((uint32_t)nb - 1u) / slots + 1u : 1u;
+  if (cb > (uint32_t)kMaxChunkBlocks) cb = kMaxChunkBlocks;
+  return (int)cb;
+}
+
+// Statistics chunks per work item for a target item length of tb blocks: at least
+// one, at most the request's chunks, and no item longer than kMaxChunkBlocks.
+__host__ __device__ inline int chunks_per_item(int cbs, int64_t nch, int tb) {
+  int c = tb / cbs;
+  const int cmax = kMaxChunkBlocks / cbs;   // cbs <= kMaxChunkBlocks, so cmax >= 1
+  if (c > cmax) c = cmax;
+  if (c > nch) c = (int)nch;
+  return c < 1 ? 1 : c;
+}
 
 // Launch shape of the score kernel per head dimension: query rows per workgroup
 // (waves x 32-row tiles per wave x 32) and workgroups resident per CU.  One 8-wave
@@ -39,7 +79,7 @@ constexpr int score_wgs_per_cu(int) { return 1; }
 // Shape of the score pass, fixed by the host for one call.
 struct ScoreShape {
   int B, Hq, Hkv, d, n, G;
-  int CB;        // blocks per key chunk (one workgroup's span of keys)
+  int TB;        // target work-item length in blocks (chunks_per_item)
   int qt;        // 32-query column tiles per wave (1 or 2)
   int kt;        // 32-key row tiles per LDS stage (1 or 2)
   int rows_wg;   // query rows per workgroup: score_rows_wg(d)
@@ -76,9 +116,6 @@ struct ScoreLseWs {
 };
 
 ScoreLseWs score_lse_ws_layout(int B, const Totals& t);
-
-// Largest key chunk (blocks per workgroup) the planner picks.
-constexpr int kMaxChunkBlocks = 256;
 
 // Launchers (score.hip).  Each returns the hipError_t of its launch.
 hipError_t launch_score_plan(const int32_t* cu, const ScoreShape& s, const Totals& t,
@@ -129,8 +166,9 @@ struct FusedDecision {
   int32_t* len = nullptr;          // per block: rows
 };
 constexpr int kFusedSelectMaxBlocks = 4096;
-// Whether up_layer_decision may use the fused select (off: see up_layer_decision).
-constexpr bool kFusedSelect = false;
+// Whether up_layer_decision uses the fused select for one request of at most
+// kFusedSelectMaxBlocks blocks.
+constexpr bool kFusedSelect = true;
 hipError_t launch_select_fused(const int32_t* cu, int n, int G, float p, int64_t T_host,
                                int64_t nb_tot_host, uint8_t* keep, int32_t* cu_out, int* err,
                                const FusedDecision& fd, hipStream_t st);
@@ -143,10 +181,12 @@ CompactWs compact_ws_layout(int64_t nb_tot);
 hipError_t launch_block_dst(const uint8_t* keep, const int32_t* cu, const int32_t* cu_out, int B,
                             int G, int64_t T_host, int64_t nb_tot_host, void* ws,
                             const CompactWs& L, int* err, hipStream_t st);
+// T: rows of hidden and the capacity of every output (a run outside is refused, error
+// bit 16).
 hipError_t launch_gather(const void* hidden, int64_t row_bytes, const int32_t* pos, void* ws,
-                         const CompactWs& L, int64_t nb_tot, int G, int32_t* idx_out,
+                         const CompactWs& L, int64_t nb_tot, int G, int64_t T, int32_t* idx_out,
                          void* hidden_out, int32_t* pos_out, const int32_t* prev_orig,
-                         int32_t* orig_out, hipStream_t st);
+                         int32_t* orig_out, int* err, hipStream_t st);
 hipError_t launch_compose(const int32_t* prev, int prev_len, const int32_t* idx,
                           const int32_t* count, int capacity, int32_t* out, int* err,
                           hipStream_t st);

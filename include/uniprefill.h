@@ -102,6 +102,18 @@ int up_block_scores(const void* qwin, const void* k,
                     float* scores, float* row_lse, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Statistics chunks of the score pass (host only; launches nothing).  The pass
+ * restarts each query's softmax reference at the first key of every statistics
+ * chunk, so its float32 results depend on where the chunks start.  Request i's chunks
+ * are chunk_blocks_h[i] blocks long (its first chunk starts at its block 0), chosen
+ * from that request's block count and the call's shape (Hq, Hkv, d, n) alone: a request
+ * gets bit-identical scores and row statistics whatever other requests share the
+ * batch and whatever GPU runs it ([UPA]: the operator serves continuous batching,
+ * where requests are independent).  chunk_blocks_h: host int32 [B], written.
+ * Returns UP_OK or the argument error up_block_scores would return. */
+int up_block_scores_chunks(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d, int n,
+                           int G, int32_t* chunk_blocks_h);
+
 /* Same computation with the keys in a paged cache (the layout of a KV cache that
  * serves continuous batching, [UPA]; chunked prefill reads earlier chunks' keys from
  * it, [CP]):

@@ -118,8 +118,24 @@ def run_decision(gb: GpuBatch, p: float, topk=None, prev_orig=None) -> dict:
                 cu_out=dec.cu_out.cpu().numpy(), count=cnt, dec=dec)
 
 
-def check_compaction(gb: GpuBatch, res: dict, sample_rows: int | None = None, seed: int = 0):
-    """idx/hidden/pos/orig bit-exact against the oracle given the GPU's kept set."""
+def check_rows(hidden_out: torch.Tensor, src_np: np.ndarray, idx: np.ndarray, chunk=16384):
+    """Every compacted row bit-exact: hidden_out[r] == src_np[idx[r]] for all r, copied
+    back and compared chunk by chunk (bounded host memory at full size)."""
+    cnt = int(idx.size)
+    flat = hidden_out.view(torch.int16)
+    for r0 in range(0, cnt, chunk):
+        r1 = min(cnt, r0 + chunk)
+        got = flat[r0:r1].cpu().numpy().view(np.uint16)
+        want = src_np[idx[r0:r1]]
+        if not np.array_equal(got, want):
+            bad = np.nonzero((got != want).any(axis=1))[0]
+            raise AssertionError(f"compacted rows differ at {(bad[:8] + r0).tolist()} "
+                                 f"({bad.size} rows in [{r0}, {r1}))")
+
+
+def check_compaction(gb: GpuBatch, res: dict):
+    """idx/hidden/pos/orig bit-exact against the oracle given the GPU's kept set; every
+    compacted row is compared."""
     b = gb.b
     dec = res["dec"]
     keep = res["keep"]
@@ -137,14 +153,7 @@ def check_compaction(gb: GpuBatch, res: dict, sample_rows: int | None = None, se
     np.testing.assert_array_equal(orig, prev[idx_ref])
     if gb.hidden is None:
         return
-    if sample_rows is None or sample_rows >= cnt:
-        rows = np.arange(cnt)
-    else:
-        rng = np.random.default_rng(seed)
-        rows = np.unique(np.concatenate([[0, cnt - 1], rng.integers(0, cnt, sample_rows)]))
-    got = dec.hidden_out.view(torch.int16)[torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16)
-    want = gb.hidden_np[idx_ref[rows]]
-    np.testing.assert_array_equal(got, want)
+    check_rows(dec.hidden_out[:cnt], gb.hidden_np, idx_ref)
 
 
 def _counts(keep, cu, G):
@@ -157,3 +166,41 @@ def _counts(keep, cu, G):
         out[i + 1] = out[i] + sum(min((b + 1) * G, L) - b * G for b in range(nb) if keep[boff + b])
         boff += nb
     return None, out, None
+
+
+def check_packed_equals_alone(gb: GpuBatch, res: dict, p: float, requests=None):
+    """Requests are independent ([UPA]: a continuous-batching operator): each request
+    decided alone gives bit-identical scores and keep flags to its slice of the packed
+    decision, the same kept-token count, and the same compacted rows.  Returns the
+    number of requests checked."""
+    b = gb.b
+    cu = b.cu_seqlens.astype(np.int64)
+    boff = 0
+    checked = 0
+    dec = res["dec"]
+    for i in range(b.B):
+        L = int(cu[i + 1] - cu[i])
+        nb = O.n_blocks(L, b.G)
+        if (requests is None or i in requests) and L > 0:
+            from workloads import synth
+            wo = int(sum(min(b.n, int(cu[r + 1] - cu[r])) for r in range(i)))
+            W = min(b.n, L)
+            one = synth.Batch(cu_seqlens=np.array([0, L], np.int32), qwin=b.qwin[wo:wo + W],
+                              k=b.k[cu[i]:cu[i + 1]], Hq=b.Hq, Hkv=b.Hkv, d=b.d, n=b.n, G=b.G)
+            hid = gb.hidden_np[cu[i]:cu[i + 1]] if gb.hidden_np is not None else None
+            r1 = run_decision(GpuBatch(one, H=None, hidden=hid), p)
+            assert np.array_equal(r1["scores"].view(np.uint32),
+                                  res["scores"][boff:boff + nb].view(np.uint32)), \
+                f"request {i} (L={L}): scores differ between alone and packed"
+            assert np.array_equal(r1["keep"], res["keep"][boff:boff + nb]), \
+                f"request {i} (L={L}): keep flags differ between alone and packed"
+            o0, o1 = int(res["cu_out"][i]), int(res["cu_out"][i + 1])
+            assert r1["count"] == o1 - o0
+            if hid is not None and r1["count"]:
+                a = r1["dec"].hidden_out[:r1["count"]]
+                c = dec.hidden_out[o0:o1]
+                assert torch.equal(a.view(torch.int16), c.view(torch.int16)), \
+                    f"request {i}: compacted rows differ between alone and packed"
+            checked += 1
+        boff += nb
+    return checked

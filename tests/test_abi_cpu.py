@@ -182,6 +182,29 @@ def test_score_chunks_are_not_tiny_for_mixed_lengths(L):
     assert per_block < ws < 1.2 * per_block
 
 
+def test_statistics_chunks_depend_on_the_request_alone(L):
+    """A request's statistics chunks (where the score pass restarts its softmax
+    reference) come from its own length and the call's shape only: the same whether it
+    is scored alone or packed with others, so its scores can be bit-identical."""
+    lens = [56971, 44718, 37503, 23662, 25844, 10541, 12506, 9139, 0, 1, 700]
+    Hq, Hkv, d, n, G = 32, 8, 128, 128, 64
+    packed = (ctypes.c_int32 * len(lens))()
+    assert L.up_block_scores_chunks(_p(_cu(lens)), len(lens), Hq, Hkv, d, n, G, packed) == UP_OK
+    for i, x in enumerate(lens):
+        alone = (ctypes.c_int32 * 1)()
+        assert L.up_block_scores_chunks(_p(_cu([x])), 1, Hq, Hkv, d, n, G, alone) == UP_OK
+        assert alone[0] == packed[i], (i, x)
+        assert 1 <= packed[i] <= 256
+    # a lone 128K request of the Llama-3.1-8B shape: 64-block chunks (256 workgroups)
+    one = (ctypes.c_int32 * 1)()
+    assert L.up_block_scores_chunks(_p(_cu([131072])), 1, Hq, Hkv, d, n, G, one) == UP_OK
+    assert one[0] == 64
+    # the same argument checks as the score pass
+    assert L.up_block_scores_chunks(_p(_cu([100])), 1, 32, 7, d, n, G, one) == UP_EINVAL
+    assert L.up_block_scores_chunks(_p(_cu([100])), 1, 32, 8, 96, n, G, one) == UP_EUNSUPPORTED
+    assert L.up_block_scores_chunks(_p(_cu([100])), 1, 32, 8, d, n, G, None) == UP_EINVAL
+
+
 def test_block_scores_paged_rejects_bad_arguments(L):
     cu = _cu([1000, 24])
     f = L.up_block_scores_paged

@@ -1,10 +1,10 @@
 """GPU: up_layer_decision (the whole decision in one call) against the three separate
 calls on the same inputs: every output must be bit-identical (scores, keep flags,
-cu_seqlens_out, indices, rows, positions, composed original indices).  The one call
-currently makes the three calls itself: its fused select path (normalisation and
-block destinations inside the select kernel) is switched off, see
-test_fused_select_path.  (The other GPU tests reach the one call through
-LayerDecision and compare it with the oracle.)"""
+cu_seqlens_out, indices, rows, positions, composed original indices).  For one
+request of at most 4096 blocks the one call normalises and assigns block destinations
+inside the select kernel (the fused path); otherwise it makes the three calls.  (The
+other GPU tests reach the one call through LayerDecision and compare it with the
+oracle.)"""
 import numpy as np
 import pytest
 import torch
@@ -107,10 +107,69 @@ def test_one_call_with_inconsistent_device_cu_writes_nothing():
     assert bool((dec.hidden_out == 3.0).all())
 
 
-@pytest.mark.skip(reason="the fused select path of up_layer_decision is switched off "
-                         "(kFusedSelect = false): a benchmark run that first used it, together "
-                         "with the 8-wave attention kernel, left the GPU faulted and no cause "
-                         "has been shown; the path stays off the GPU until one is")
+def _fused_launches(gb, p):
+    """Launches of the fused select kernel in one up_layer_decision call."""
+    b = gb.b
+    dec = up.LayerDecision(gb.qwin, gb.k, gb.cu, gb.cu_h, gb.hidden, gb.pos, b.n, b.G, p)
+    up.profile_reset()
+    up.profile_enable(True)
+    dec.run()
+    torch.cuda.synchronize()
+    up.profile_enable(False)
+    n, _ = up.profile_read("select_fused")
+    up.profile_reset()
+    assert up.device_error() == 0
+    return n
+
+
 def test_fused_select_path():
-    """Would compare the fused select path (masses normalised and block destinations
-    assigned inside the select kernel) with the separate calls, bit for bit."""
+    """One request of at most 4096 blocks: up_layer_decision normalises the block
+    masses and assigns the compaction's block destinations inside the select kernel
+    (one launch instead of three); every output is bit-identical to the separate
+    calls (see test_one_call_equals_the_separate_calls for the case list)."""
+    b = _batch([4096], 8, 2, 64, 128, 64, seed=5)
+    gb = GpuBatch(b, H=64)
+    assert _fused_launches(gb, 0.99) == 1
+    big = _batch([262208], 8, 2, 64, 128, 64, seed=6)   # 4097 blocks: the separate calls
+    assert _fused_launches(GpuBatch(big, H=64), 0.95) == 0
+    a, c = _both(gb, 0.99)
+    _assert_same(a, c)
+
+
+@pytest.mark.timeout(600)
+def test_fused_select_beside_another_stream():
+    """Regression test of the select kernel's pass loop: a wave must not read the
+    shared winning-bin index after the pass's last barrier (the next pass resets it).
+    Waves of one select workgroup drift apart most when they share SIMDs with another
+    kernel's waves, so fused decisions run here while independent decisions on a
+    second stream keep the CUs busy with score passes; every repetition's outputs must
+    equal the separate calls' bit for bit."""
+    cfg = synth.WORKLOADS["llama31_8b_128k"]
+    say("[setup] generating llama31_8b_128k")
+    b = synth.make_batch(cfg)
+    gb = GpuBatch(b, H=cfg["H"])
+    ref = up.LayerDecision(gb.qwin, gb.k, gb.cu, gb.cu_h, gb.hidden, gb.pos, b.n, b.G,
+                           cfg["p"], separate=True)
+    ref.run()
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    kept = int(ref.cu_out[-1].item())
+    da = up.LayerDecision(gb.qwin, gb.k, gb.cu, gb.cu_h, gb.hidden, gb.pos, b.n, b.G, cfg["p"])
+    db = up.LayerDecision(gb.qwin, gb.k, gb.cu, gb.cu_h, gb.hidden, gb.pos, b.n, b.G, cfg["p"])
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    say("[case] fused decisions on two streams, 40 repetitions")
+    for rep in range(40):
+        da.hidden_out.zero_()
+        torch.cuda.synchronize()
+        for j in range(3):
+            db.run(stream=sb)
+            da.run(stream=sa)
+        torch.cuda.synchronize()
+        assert up.device_error() == 0, f"device error at repetition {rep}"
+        for name in ("scores", "keep", "cu_out"):
+            assert torch.equal(getattr(da, name), getattr(ref, name)), (rep, name)
+        for name in ("idx", "pos_out", "orig"):
+            assert torch.equal(getattr(da, name)[:kept], getattr(ref, name)[:kept]), (rep, name)
+        assert torch.equal(da.hidden_out[:kept].view(torch.int16),
+                           ref.hidden_out[:kept].view(torch.int16)), rep
+    say("[ok] 40 repetitions identical")

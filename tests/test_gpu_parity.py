@@ -11,7 +11,8 @@ import block_wise_token_amd as up
 from oracle import uniprefill_oracle as O
 from workloads import synth
 from tests.gpu_helpers import (GpuBatch, ambiguous_blocks, bf16_dev, check_compaction, check_keep,
-                               check_scores, i32_dev, run_decision, say)
+                               check_packed_equals_alone, check_scores, i32_dev, run_decision,
+                               say)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +25,7 @@ def _batch(lengths, Hq, Hkv, d, n, G, needles=2, seed=0, recency=0):
     return synth.pack(reqs, Hq, Hkv, d, n, G)
 
 
-def _full_check(batch, p, H=None, sample_rows=None, topk=None, label=""):
+def _full_check(batch, p, H=None, topk=None, label=""):
     say(f"[case] {label} B={batch.B} T={batch.T} Hq={batch.Hq} Hkv={batch.Hkv} d={batch.d} "
         f"n={batch.n} G={batch.G} p={p} topk={topk} H={H}")
     gb = GpuBatch(batch, H=H)
@@ -45,7 +46,7 @@ def _full_check(batch, p, H=None, sample_rows=None, topk=None, label=""):
         own_keep, own_cu = O.topk_select(res["scores"], batch.cu_seqlens, batch.n, batch.G, topk)
     np.testing.assert_array_equal(res["keep"], own_keep)
     np.testing.assert_array_equal(res["cu_out"], own_cu)
-    check_compaction(gb, res, sample_rows=sample_rows)
+    check_compaction(gb, res)
     say(f"[ok] {label} worst score rel err {worst:.2e}; ambiguous {len(amb)}, differing {ndiff}; "
         f"kept {res['count']}/{batch.T}")
     return res, gb
@@ -86,7 +87,10 @@ def test_many_requests_full_decision():
     lengths = rng.integers(0, 701, 150)
     lengths[rng.integers(0, 150, 12)] = 0
     batch = _batch([int(x) for x in lengths], 4, 2, 64, 64, 32, needles=1, seed=33)
-    _full_check(batch, 0.9, H=64, label="150 requests")
+    res, gb = _full_check(batch, 0.9, H=64, label="150 requests")
+    # every request decided alone: bit-identical scores, keep flags and rows
+    n = check_packed_equals_alone(gb, res, 0.9)
+    say(f"[ok] 150 requests: {n} non-empty requests alone == packed, bitwise")
 
 
 def test_single_4k_workload():
@@ -97,14 +101,14 @@ def test_single_4k_workload():
 @pytest.mark.parametrize("p", [0.95, 0.99, 0.999, 1.0])
 def test_llama_32k_workload(p):
     cfg = synth.WORKLOADS["llama31_8b_32k"]
-    _full_check(synth.make_batch(cfg), p, H=cfg["H"], sample_rows=4096,
+    _full_check(synth.make_batch(cfg), p, H=cfg["H"],
                 label=f"llama31_8b_32k p={p}")
 
 
 def test_topk_matches_oracle():
     cfg = synth.WORKLOADS["llama31_8b_32k"]
     for k in (1, 100, 511, 4096):
-        _full_check(synth.make_batch(cfg), 0.99, H=64, topk=k, sample_rows=256, label=f"topk k={k}")
+        _full_check(synth.make_batch(cfg), 0.99, H=64, topk=k, label=f"topk k={k}")
 
 
 def test_select_is_bit_exact_on_oracle_scores():

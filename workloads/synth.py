@@ -249,6 +249,42 @@ def gen_layer(orig: np.ndarray, L0: int, needles: np.ndarray, Hq: int, Hkv: int,
 
 
 # ---------------------------------------------------------------------------
+# Planted large logits: keys that stand far above everything a subset of the window
+# rows has seen so far, at chosen token positions (inputs that make a running
+# softmax reference move by a large step in the middle of the keys)
+# ---------------------------------------------------------------------------
+TAG_PLANTED = 4
+
+
+def gen_planted_request(L: int, Hq: int, Hkv: int, d: int, n: int, plants, seed: int,
+                        beta: float = 8.0, gap: float = 62.0) -> Request:
+    """Gaussian queries and keys, with m = len(plants) orthonormal directions v_s
+    removed from every query.  Window rows [s * r, (s + 1) * r) (r = W // (m + 1)) then
+    get beta * v_s added in every head, and the key at token plants[s] is replaced, in
+    every kv head, by alpha * v_s with alpha = gap * sqrt(d) / beta: its scaled logit
+    against those rows is about ``gap`` (natural units, at scale 1/sqrt(d)) while
+    every other key gives them a logit of order one, and every other row gets about
+    0 from it.  Rows outside every subset see plain Gaussian keys.  Draws from
+    default_rng([seed, TAG_PLANTED]); positions must lie before the window."""
+    rng = np.random.default_rng([seed, TAG_PLANTED])
+    W = min(n, L)
+    m = len(plants)
+    q = rng.standard_normal((W, Hq, d), dtype=np.float32)
+    k = rng.standard_normal((L, Hkv, d), dtype=np.float32)
+    V = np.linalg.qr(rng.standard_normal((d, m)))[0].T.astype(np.float32)   # [m, d]
+    q -= np.einsum("whm,md->whd", np.einsum("whd,md->whm", q, V), V)
+    r = max(1, W // (m + 1))
+    alpha = np.float32(gap * np.sqrt(d) / beta)
+    for s_, t in enumerate(plants):
+        if not 0 <= t < L - W:
+            raise ValueError(f"plant {t} is not before the window of a {L}-token request")
+        q[s_ * r:(s_ + 1) * r] += np.float32(beta) * V[s_]
+        k[t] = alpha * V[s_]
+    return Request(L=L, qwin=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k),
+                   needles=np.zeros(0, np.int64), sink=False)
+
+
+# ---------------------------------------------------------------------------
 # Inputs of the layer on the surviving tokens
 # ---------------------------------------------------------------------------
 TAG_CONSUMER = 3
