@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     compose_drops,
     device_error,
     expand_compact,
+    expand_compact_noalloc,
     expand_compact_workspace_bytes,
     lib,
     profile_enable,

@@ -65,6 +65,9 @@ def lib():
     L.up_expand_compact.restype = ci
     L.up_expand_compact.argtypes = [vp, ci, ci, i32p, u8p, i32p, i32p, vp, ci, ci, i32p, vp, i32p,
                                     i32p, i32p, vp, cs, vp]
+    L.up_expand_compact_noalloc.restype = ci
+    L.up_expand_compact_noalloc.argtypes = [vp, ci, ci, i32p, u8p, i32p, i32p, vp, ci, ci, i32p,
+                                            vp, i32p, i32p, i32p, vp]
     L.up_compose_drops.restype = ci
     L.up_compose_drops.argtypes = [i32p, ci, i32p, i32p, ci, i32p, vp]
     L.up_device_error.restype = ci
@@ -406,6 +409,44 @@ def expand_compact(hidden, pos, keep, cu_seqlens, cu_out, cu_h, G, idx_out=None,
                                  _ptr(pos_out), _ptr(prev_orig), _ptr(orig_out), _ptr(workspace),
                                  workspace.numel(), _stream(stream))
     _check(st, "up_expand_compact")
+    return idx_out, hidden_out, pos_out
+
+
+def expand_compact_noalloc(hidden, pos, keep, cu_seqlens, cu_out, cu_h, G, idx_out, hidden_out,
+                           pos_out=None, stream=None, prev_orig=None, orig_out=None):
+    """up_expand_compact_noalloc: expand_compact with the run table in the library's
+    own device array; every output is the caller's (nothing is allocated here or in
+    the library).  At most 65,536 blocks per call; calls overlapping on one GPU race."""
+    _dev(hidden, hidden.dtype, "hidden")
+    _dev(keep, torch.uint8, "keep_blocks")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    _dev(cu_out, torch.int32, "cu_seqlens_out")
+    h = _HostCu(cu_h)
+    _buf(cu_seqlens, torch.int32, h.B + 1, "cu_seqlens")
+    T = h.T
+    _rank(hidden, 2, "hidden")
+    if int(hidden.shape[0]) < T:
+        raise ValueError(f"hidden has {int(hidden.shape[0])} rows, cu_seqlens needs {T}")
+    H = int(hidden.shape[1])
+    _buf(keep, torch.uint8, h.nb_tot(G), "keep_blocks")
+    _buf(cu_out, torch.int32, h.B + 1, "cu_seqlens_out")
+    _buf(idx_out, torch.int32, T, "idx_out")
+    _buf(hidden_out, hidden.dtype, T * H, "hidden_out")
+    if pos is not None:
+        _buf(pos, torch.int32, T, "pos")
+        _buf(pos_out, torch.int32, T, "pos_out")
+    elif pos_out is not None:
+        raise ValueError("pos_out needs pos")
+    if prev_orig is not None:
+        _buf(prev_orig, torch.int32, T, "prev_orig")
+        _buf(orig_out, torch.int32, T, "orig_out")
+    elif orig_out is not None:
+        raise ValueError("orig_out needs prev_orig")
+    st = lib().up_expand_compact_noalloc(_ptr(hidden), H, hidden.element_size(), _ptr(pos),
+                                         _ptr(keep), _ptr(cu_seqlens), _ptr(cu_out), h.ptr, h.B,
+                                         G, _ptr(idx_out), _ptr(hidden_out), _ptr(pos_out),
+                                         _ptr(prev_orig), _ptr(orig_out), _stream(stream))
+    _check(st, "up_expand_compact_noalloc")
     return idx_out, hidden_out, pos_out
 
 

@@ -481,6 +481,40 @@ int up_expand_compact(const void* hidden, int H, int elem_bytes, const int32_t* 
   return e == hipSuccess ? UP_OK : UP_EHIP;
 }
 
+int up_expand_compact_noalloc(const void* hidden, int H, int elem_bytes, const int32_t* pos,
+                              const uint8_t* keep_blocks, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_out, const int32_t* cu_seqlens_h,
+                              int B, int G, int32_t* idx_out, void* hidden_out,
+                              int32_t* pos_out, const int32_t* prev_orig, int32_t* orig_out,
+                              void* stream) {
+  if (B < 0 || G <= 0 || H <= 0 || elem_bytes <= 0) return UP_EINVAL;
+  if (!cu_ok(cu_seqlens_h, B)) return UP_EINVAL;
+  const SelPlan sp = sel_plan(cu_seqlens_h, B, G);
+  if (sp.nb_tot > kStaticCompactBlocks) return UP_EUNSUPPORTED;
+  if (B == 0 || sp.T == 0) return UP_OK;
+  if (!hidden || !keep_blocks || !cu_seqlens || !cu_seqlens_out || !idx_out || !hidden_out)
+    return UP_EINVAL;
+  if (pos_out && !pos) return UP_EINVAL;
+  if (orig_out && !prev_orig) return UP_EINVAL;
+  const int64_t row_bytes = (int64_t)H * elem_bytes;
+  if (sp.T * row_bytes / row_bytes != sp.T) return UP_EUNSUPPORTED;
+  const CompactWs L = compact_ws_layout(sp.nb_tot);
+  size_t cap = 0;
+  void* ws = static_compact_scratch(&cap);
+  if (!ws) return UP_EHIP;
+  if (L.total > cap) return UP_EUNSUPPORTED;
+  int* err = error_word();
+  if (!err) return UP_EHIP;
+  // Launched directly (no per-kernel timing: its events would be allocations).
+  hipStream_t hs = as_stream(stream);
+  hipError_t e = launch_block_dst(keep_blocks, cu_seqlens, cu_seqlens_out, B, G, sp.T, sp.nb_tot,
+                                  ws, L, err, hs);
+  if (e != hipSuccess) return UP_EHIP;
+  e = launch_gather(hidden, row_bytes, pos, ws, L, sp.nb_tot, G, sp.T, idx_out, hidden_out,
+                    pos_out, prev_orig, orig_out, err, hs);
+  return e == hipSuccess ? UP_OK : UP_EHIP;
+}
+
 int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
                      const int32_t* count, int capacity, int32_t* orig_out, void* stream) {
   if (capacity < 0 || prev_len < 0) return UP_EINVAL;

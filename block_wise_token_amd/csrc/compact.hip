@@ -16,6 +16,8 @@
 #include "up_dpp.h"
 #include "up_internal.h"
 
+#include <mutex>
+
 namespace up {
 
 // One workgroup.  Requests are taken 1024 at a time: their block counts are
@@ -222,6 +224,34 @@ __global__ __launch_bounds__(256) void up_compose_kernel(const int32_t* __restri
   } else {
     out[r] = prev[j];
   }
+}
+
+// ---------------------------------------------------------------------------
+// Run table of up_expand_compact_noalloc: a file-scope device array, one per GPU,
+// held until the process ends.  Host code never uses the array's name as an address
+// (on the host it is only a stand-in symbol); its device address is looked up once
+// per device with hipGetSymbolAddress and that pointer is what the kernels get.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = 256 + 3 * (size_t)kStaticCompactBlocks * 4;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+void* static_compact_scratch(size_t* bytes) {
+  *bytes = kStaticScratchBytes;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 CompactWs compact_ws_layout(int64_t nb_tot) {

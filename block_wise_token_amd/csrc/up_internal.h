@@ -178,6 +178,10 @@ struct CompactWs {
   size_t hdr, dst, src, len, total;
 };
 CompactWs compact_ws_layout(int64_t nb_tot);
+// The run table of up_expand_compact_noalloc: the current device's address of the
+// library's device array (looked up once per device), or null; *bytes = its size.
+constexpr int64_t kStaticCompactBlocks = 65536;
+void* static_compact_scratch(size_t* bytes);
 hipError_t launch_block_dst(const uint8_t* keep, const int32_t* cu, const int32_t* cu_out, int B,
                             int G, int64_t T_host, int64_t nb_tot_host, void* ws,
                             const CompactWs& L, int* err, hipStream_t st);

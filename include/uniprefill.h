@@ -229,6 +229,24 @@ int up_expand_compact(const void* hidden, int H, int elem_bytes, const int32_t* 
                       const int32_t* prev_orig, int32_t* orig_out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* The same operation with no workspace argument, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the per-block run table lives in a device array of the library
+ * (786,688 bytes per GPU, held until the process ends), so the call allocates
+ * nothing.  At most 65,536 blocks in the batch (nb_tot = sum_i ceil(L_i / G));
+ * more is UP_EUNSUPPORTED, with nothing launched.  Every call on one GPU uses that
+ * GPU's one array: calls that overlap on the same GPU (different streams without
+ * ordering, or host threads) race and must be ordered by the caller; calls on
+ * different GPUs do not interact.  No state is carried from one call to the next
+ * (each call rewrites the whole table before the copy reads it).  Other arguments,
+ * outputs and results are those of up_expand_compact. */
+int up_expand_compact_noalloc(const void* hidden, int H, int elem_bytes, const int32_t* pos,
+                              const uint8_t* keep_blocks, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_out, const int32_t* cu_seqlens_h,
+                              int B, int G, int32_t* idx_out, void* hidden_out,
+                              int32_t* pos_out, const int32_t* prev_orig, int32_t* orig_out,
+                              void* stream);
+
 /* ---------------------------------------------------------------------------
  * 4. Drop composition  ([UP] "propagation" paragraph: a drop carries into every
  *    later layer; [UP] "scheduler" paragraph: the drop history maps survivors to
@@ -251,9 +269,9 @@ int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
  *
  * The decision of up_block_scores + up_topp_select + up_expand_compact (with the
  * drop composition when prev_orig / orig_out are given), with the same arguments,
- * outputs and results, made as those three calls in sequence.  (A fused form that
- * normalises and assigns block destinations inside the select kernel is built but
- * switched off.)
+ * outputs and results, bit for bit.  For one request of at most 4096 blocks the
+ * select kernel also normalises the block masses and assigns the compaction's block
+ * destinations (two launches fewer); otherwise the three calls run in sequence.
  * workspace : at least up_layer_decision_workspace(...) bytes, 256-byte aligned.
  * ------------------------------------------------------------------------- */
 size_t up_layer_decision_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d,
@@ -332,9 +350,11 @@ int up_swiglu_ffn(const void* x, const void* w_gu, const void* w_down, const voi
  * Diagnostics (not on the hot path)
  * ------------------------------------------------------------------------- */
 
-/* Device error word: bit 1 = cu_seqlens inconsistent with the host copy,
- * bit 2 = index out of range in up_compose_drops, bit 4 = count above capacity,
- * bit 8 = page index outside the paged key cache (up_block_scores_paged).
+/* Device error word: bit 1 = cu_seqlens inconsistent with the host copy (or a
+ * selection whose kept counts disagree with its flags), bit 2 = index out of range in
+ * up_compose_drops, bit 4 = count above capacity, bit 8 = page index outside the paged
+ * key cache (up_block_scores_paged), bit 16 = a compaction run whose destination or
+ * source rows fall outside the buffers (the run is not copied).
  * Synchronises `stream`, copies the word to *code_h and clears it. */
 int up_device_error(int32_t* code_h, void* stream);
 
