@@ -330,12 +330,33 @@ def consumer_leg(up, torch, dec, hid, b, cfg, reps=2):
         torch.cuda.synchronize()
         up.profile_enable(False)
         kt = {}
-        for kname in ("attn_plan", "rope_layout", "attention", "swiglu", "gemm"):
+        for kname in ("attn_plan", "rope_layout", "attention", "swiglu"):
             n, tot = up.profile_read(kname)
             if n:
                 kt[kname] = round(tot * 1e3, 1)          # microseconds per layer
         up.profile_reset()
         assert up.device_error() == 0
+        # The GEMMs (libuniprefill_layer.so, hipBLASLt): the layer's six, timed together.
+        a_ffn = torch.empty((R, F), dtype=torch.bfloat16, device=dev)
+        gu = torch.empty((R, 2 * F), dtype=torch.bfloat16, device=dev)
+
+        def gemms():
+            up.linear(x, Wq, out=buf["q"][:R], workspace=ws_gemm)
+            up.linear(x, Wk, out=buf["k"][:R], workspace=ws_gemm)
+            up.linear(x, Wv, out=buf["v"][:R], workspace=ws_gemm)
+            up.linear(buf["att"][:R], Wo, residual=x, out=buf["h2"][:R], workspace=ws_gemm)
+            up.linear(buf["h2"][:R], Wgu, out=gu, workspace=ws_gemm)
+            up.linear(a_ffn, Wd, out=buf["y"][:R], workspace=ws_gemm)
+        gemms()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(reps):
+            gemms()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        kt["gemm"] = round(g0.elapsed_time(g1) / reps * 1e3, 1)
+        del gu, a_ffn
         pairs = sum(int(L) * (int(L) + 1) // 2 for L in np.diff(cu_h))
         att_flops = 4.0 * d * Hq * pairs                  # Q K^T and P V over causal pairs
         gemm_flops = 2.0 * R * H * (Hq * d + 2 * Hkv * d + Hq * d + 3 * F)

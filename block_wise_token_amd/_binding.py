@@ -84,20 +84,40 @@ def lib():
     L.up_rope_attention.restype = ci
     L.up_rope_attention.argtypes = [vp, vp, vp, i32p, i32p, vp, ci, ci, ci, ci, cf, cf, vp, vp, cs,
                                     vp]
-    L.up_linear.restype = ci
-    L.up_linear.argtypes = [vp, vp, vp, i64, ci, ci, vp, vp, cs, vp]
     L.up_swiglu.restype = ci
     L.up_swiglu.argtypes = [vp, i64, ci, vp, vp]
-    L.up_swiglu_ffn_workspace.restype = cs
-    L.up_swiglu_ffn_workspace.argtypes = [i64, ci, ci]
-    L.up_swiglu_ffn.restype = ci
-    L.up_swiglu_ffn.argtypes = [vp, vp, vp, vp, i64, ci, ci, vp, vp, cs, vp]
     L.up_layer_decision_workspace.restype = cs
     L.up_layer_decision_workspace.argtypes = [vp, ci, ci, ci, ci, ci, ci]
     L.up_layer_decision.restype = ci
     L.up_layer_decision.argtypes = [vp, vp, i32p, vp, ci, ci, ci, ci, ci, ci, cf, cf, vp, ci, ci,
                                     i32p, i32p, f32p, u8p, i32p, i32p, vp, i32p, i32p, vp, cs, vp]
     _lib = L
+    return L
+
+
+LAYER_LIB_PATH = os.path.join(_HERE, "libuniprefill_layer.so")
+_layer = None
+
+
+def layer_lib():
+    """Load libuniprefill_layer.so (the layer's hipBLASLt GEMMs; it loads
+    libuniprefill.so itself, which lib() loads first so both share one copy)."""
+    global _layer
+    if _layer is not None:
+        return _layer
+    lib()
+    if not os.path.exists(LAYER_LIB_PATH):
+        raise UniPrefillError(f"{LAYER_LIB_PATH} is missing: build it with "
+                              "`python -m block_wise_token_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LAYER_LIB_PATH)
+    vp, ci, cs, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int64
+    L.up_linear.restype = ci
+    L.up_linear.argtypes = [vp, vp, vp, i64, ci, ci, vp, vp, cs, vp]
+    L.up_swiglu_ffn_workspace.restype = cs
+    L.up_swiglu_ffn_workspace.argtypes = [i64, ci, ci]
+    L.up_swiglu_ffn.restype = ci
+    L.up_swiglu_ffn.argtypes = [vp, vp, vp, vp, i64, ci, ci, vp, vp, cs, vp]
+    _layer = L
     return L
 
 
@@ -631,7 +651,7 @@ def linear(x, w, residual=None, out=None, workspace=None, stream=None):
     if workspace is not None:
         _dev(workspace, torch.uint8, "workspace")
     nbytes = 0 if workspace is None else workspace.numel()
-    st = lib().up_linear(_ptr(x), _ptr(w), _ptr(residual), R, K, N, _ptr(out), _ptr(workspace),
+    st = layer_lib().up_linear(_ptr(x), _ptr(w), _ptr(residual), R, K, N, _ptr(out), _ptr(workspace),
                          nbytes, _stream(stream))
     _check(st, "up_linear")
     return out
@@ -651,7 +671,7 @@ def swiglu(gu, out=None, stream=None):
 
 
 def swiglu_ffn_workspace_bytes(R, H, F) -> int:
-    return int(lib().up_swiglu_ffn_workspace(R, H, F))
+    return int(layer_lib().up_swiglu_ffn_workspace(R, H, F))
 
 
 def swiglu_ffn(x, w_gu, w_down, residual=None, out=None, workspace=None, stream=None):
@@ -669,11 +689,11 @@ def swiglu_ffn(x, w_gu, w_down, residual=None, out=None, workspace=None, stream=
     if out is None:
         out = torch.empty((R, H), dtype=torch.bfloat16, device=x.device)
     _buf(out, torch.bfloat16, R * H, "out")
-    need = int(lib().up_swiglu_ffn_workspace(R, H, F))
+    need = int(layer_lib().up_swiglu_ffn_workspace(R, H, F))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _buf(workspace, torch.uint8, need, "workspace")
-    st = lib().up_swiglu_ffn(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(residual), R, H, F, _ptr(out),
+    st = layer_lib().up_swiglu_ffn(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(residual), R, H, F, _ptr(out),
                              _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "up_swiglu_ffn")
     return out

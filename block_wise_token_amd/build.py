@@ -17,7 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libuniprefill.so")
+# The GEMMs of the layer on the survivors (hipBLASLt) live in a library of their own.
+LAYER_LIB = os.path.join(PKG, "libuniprefill_layer.so")
 SOURCES = ["abi.hip", "score.hip", "select.hip", "compact.hip", "consumer.hip"]
+LAYER_SOURCES = ["gemm.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are switched off for all device code.
@@ -45,19 +48,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    # hipBLASLt serves the plain GEMMs of the layer on the surviving tokens.
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-lhipblaslt", "-o", tmp]
+def _link(objs, out, extra):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *extra, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(out)} failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + LAYER_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    # The decision library: HIP runtime only.
+    _link([objs[s] for s in SOURCES], LIB, ["-Wl,-soname,libuniprefill.so"])
+    # The layer's GEMMs: hipBLASLt, and libuniprefill.so (found next to it) for the gate.
+    _link([objs[s] for s in LAYER_SOURCES], LAYER_LIB,
+          ["-L", PKG, "-luniprefill", "-lhipblaslt", "-Wl,-rpath,$ORIGIN",
+           "-Wl,-soname,libuniprefill_layer.so"])
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {LAYER_LIB}")
     return LIB
 
 

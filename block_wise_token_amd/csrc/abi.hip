@@ -633,24 +633,6 @@ int plan_attention(const int32_t* cu_h, int B, int Hq, int Hkv, int d, AttnShape
   return UP_OK;
 }
 
-// hipBLASLt workspace the library offers its GEMMs inside up_swiglu_ffn.
-constexpr size_t kGemmWs = size_t(32) << 20;
-
-struct FfnWs {
-  size_t gu, a, gemm, total;
-};
-FfnWs ffn_ws_layout(int64_t R, int F) {
-  FfnWs w;
-  size_t o = 0;
-  w.gu = o;
-  o += align_up((size_t)R * 2 * F * 2);
-  w.a = o;
-  o += align_up((size_t)R * F * 2);
-  w.gemm = o;
-  o += kGemmWs;
-  w.total = o;
-  return w;
-}
 }  // namespace
 
 size_t up_rope_attention_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d) {
@@ -689,22 +671,6 @@ int up_rope_attention(const void* q, const void* k, const void* v, const int32_t
   return e == hipSuccess ? UP_OK : UP_EHIP;
 }
 
-int up_linear(const void* x, const void* w, const void* residual, int64_t R, int K, int N,
-              void* y, void* workspace, size_t workspace_bytes, void* stream) {
-  if (R < 0 || K <= 0 || N <= 0) return UP_EINVAL;
-  if (R == 0) return UP_OK;
-  if (!x || !w || !y || (workspace_bytes > 0 && !workspace)) return UP_EINVAL;
-  if (workspace && !aligned(workspace, kWsAlign)) return UP_EWORKSPACE;
-  hipStream_t hs = as_stream(stream);
-  int r = 0;
-  const hipError_t e = timed(16, hs, [&] {
-    r = linear_gemm(x, w, residual, R, K, N, y, workspace, workspace_bytes, hs);
-    return hipSuccess;
-  });
-  if (e != hipSuccess || r == -1) return UP_EHIP;
-  return r == -2 ? UP_EUNSUPPORTED : UP_OK;
-}
-
 int up_swiglu(const void* gu, int64_t R, int F, void* a, void* stream) {
   if (R < 0 || F <= 0) return UP_EINVAL;
   if (F % 8 != 0) return UP_EUNSUPPORTED;
@@ -713,29 +679,6 @@ int up_swiglu(const void* gu, int64_t R, int F, void* a, void* stream) {
   hipStream_t hs = as_stream(stream);
   const hipError_t e = timed(15, hs, [&] { return launch_swiglu(gu, R, F, a, hs); });
   return e == hipSuccess ? UP_OK : UP_EHIP;
-}
-
-size_t up_swiglu_ffn_workspace(int64_t R, int H, int F) {
-  if (R < 0 || H <= 0 || F <= 0) return 0;
-  return ffn_ws_layout(R, F).total;
-}
-
-int up_swiglu_ffn(const void* x, const void* w_gu, const void* w_down, const void* residual,
-                  int64_t R, int H, int F, void* y, void* workspace, size_t workspace_bytes,
-                  void* stream) {
-  if (R < 0 || H <= 0 || F <= 0) return UP_EINVAL;
-  if (F % 8 != 0) return UP_EUNSUPPORTED;
-  if (R == 0) return UP_OK;
-  if (!x || !w_gu || !w_down || !y) return UP_EINVAL;
-  const FfnWs L = ffn_ws_layout(R, F);
-  if (!workspace || workspace_bytes < L.total || !aligned(workspace, kWsAlign))
-    return UP_EWORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  int st = up_linear(x, w_gu, nullptr, R, H, 2 * F, ws + L.gu, ws + L.gemm, kGemmWs, stream);
-  if (st != UP_OK) return st;
-  st = up_swiglu(ws + L.gu, R, F, ws + L.a, stream);
-  if (st != UP_OK) return st;
-  return up_linear(ws + L.a, w_down, residual, R, F, H, y, ws + L.gemm, kGemmWs, stream);
 }
 
 int up_device_error(int32_t* code_h, void* stream) {

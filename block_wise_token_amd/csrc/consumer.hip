@@ -11,11 +11,11 @@
 //                          [kv head][d][token] for the P V product;
 //   up_attention_kernel    causal GQA flash attention on the matrix cores;
 //   up_swiglu_kernel       silu(gate) * up for the FFN.
-// The FFN and projection GEMMs are plain bf16 GEMMs and go to hipBLASLt.
+// The FFN and projection GEMMs are plain bf16 GEMMs; they are served by hipBLASLt in
+// the separate layer library (gemm.hip).
 #include "up_dpp.h"
 #include "up_internal.h"
 
-#include <hipblaslt/hipblaslt.h>
 
 #include <algorithm>
 #include <map>
@@ -646,79 +646,6 @@ hipError_t launch_swiglu(const void* gu, int64_t R, int F, void* a, hipStream_t 
   hipLaunchKernelGGL(up_swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
                      static_cast<const uint16_t*>(gu), R, F, static_cast<uint16_t*>(a));
   return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// hipBLASLt GEMM: y[R][N] = x[R][K] w[N][K]^T (+ residual[R][N]), bf16 in and out,
-// float32 accumulation.  In hipBLASLt's column-major terms y^T = op_T(w) x^T.  One
-// handle per device; descriptors and the heuristic's first algorithm are cached per
-// (device, R, K, N, residual, workspace bytes).
-// ---------------------------------------------------------------------------
-namespace {
-struct GemmPlan {
-  hipblasLtMatmulDesc_t desc = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
-  hipblasLtMatmulAlgo_t algo;
-  size_t ws_need = 0;
-};
-std::mutex g_blas_mu;
-hipblasLtHandle_t g_blas[64] = {};
-std::map<std::tuple<int, int64_t, int, int, bool, size_t>, GemmPlan> g_plans;
-}  // namespace
-
-int linear_gemm(const void* x, const void* w, const void* residual, int64_t R, int K, int N,
-                void* y, void* ws, size_t ws_bytes, hipStream_t st) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  std::lock_guard<std::mutex> lk(g_blas_mu);
-  if (!g_blas[dev] && hipblasLtCreate(&g_blas[dev]) != HIPBLAS_STATUS_SUCCESS) {
-    g_blas[dev] = nullptr;
-    return -1;
-  }
-  const bool res = residual != nullptr;
-  const auto key = std::make_tuple(dev, R, K, N, res, ws_bytes);
-  auto it = g_plans.find(key);
-  if (it == g_plans.end()) {
-    GemmPlan p;
-    bool ok = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) ==
-              HIPBLAS_STATUS_SUCCESS;
-    const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
-    ok = ok && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta,
-                                               sizeof(ta)) == HIPBLAS_STATUS_SUCCESS;
-    ok = ok && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb,
-                                               sizeof(tb)) == HIPBLAS_STATUS_SUCCESS;
-    ok = ok && hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS;
-    ok = ok && hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, K, R, K) == HIPBLAS_STATUS_SUCCESS;
-    ok = ok && hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_16BF, N, R, N) == HIPBLAS_STATUS_SUCCESS;
-    hipblasLtMatmulPreference_t pref = nullptr;
-    ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS;
-    uint64_t wsmax = ws_bytes;
-    ok = ok && hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
-                                                     &wsmax, sizeof(wsmax)) ==
-                   HIPBLAS_STATUS_SUCCESS;
-    hipblasLtMatmulHeuristicResult_t hr[1];
-    int n = 0;
-    ok = ok && hipblasLtMatmulAlgoGetHeuristic(g_blas[dev], p.desc, p.la, p.lb, p.lc, p.lc, pref,
-                                               1, hr, &n) == HIPBLAS_STATUS_SUCCESS &&
-         n > 0;
-    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-    if (!ok) {
-      if (p.la) hipblasLtMatrixLayoutDestroy(p.la);
-      if (p.lb) hipblasLtMatrixLayoutDestroy(p.lb);
-      if (p.lc) hipblasLtMatrixLayoutDestroy(p.lc);
-      if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
-      return -2;
-    }
-    p.algo = hr[0].algo;
-    p.ws_need = hr[0].workspaceSize;
-    it = g_plans.emplace(key, p).first;
-  }
-  const GemmPlan& p = it->second;
-  const float alpha = 1.f, beta = res ? 1.f : 0.f;
-  const hipblasStatus_t s =
-      hipblasLtMatmul(g_blas[dev], p.desc, &alpha, w, p.la, x, p.lb, &beta, res ? residual : y,
-                      p.lc, y, p.lc, &p.algo, p.ws_need ? ws : nullptr, p.ws_need, st);
-  return s == HIPBLAS_STATUS_SUCCESS ? 0 : -1;
 }
 
 }  // namespace up

@@ -216,8 +216,5 @@ hipError_t launch_rope_layout(const void* q, const void* k, const void* v, const
 hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
                             float c, void* out, hipStream_t st);
 hipError_t launch_swiglu(const void* gu, int64_t R, int F, void* a, hipStream_t st);
-// y = x w^T (+ residual) through hipBLASLt; 0 on success, -1 library error, -2 no algorithm.
-int linear_gemm(const void* x, const void* w, const void* residual, int64_t R, int K, int N,
-                void* y, void* ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace up

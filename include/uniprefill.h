@@ -6,8 +6,8 @@
  *   2. up_topp_select    : Top-p cut over the sorted block scores
  *   3. up_expand_compact : kept blocks -> token indices; gather hidden rows and positions
  *   4. up_compose_drops  : map survivors back to original indices across layers
- * and the layer that then runs on the survivors (5: up_rope_attention, up_linear,
- * up_swiglu, up_swiglu_ffn).
+ * and the layer that then runs on the survivors (5: up_rope_attention, up_swiglu;
+ * its GEMMs up_linear and up_swiglu_ffn are in libuniprefill_layer.so).
  *
  * Pages cited (by title and paragraph / section):
  *   [UP]  "UniPrefill: 블록 단위 동적 희소화를 통한 범용적 롱 컨텍스트 프리필 가속화"
@@ -19,9 +19,8 @@
  * Conventions shared by every call
  *  - Pointers are DEVICE pointers unless their name ends in _h (host memory).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
- *    stream), never synchronises, never allocates device memory (except that the
- *    first up_linear / up_swiglu_ffn call on a device lets hipBLASLt create its
- *    handle), and returns an up_status (0 = UP_OK, negative = error).  Arguments are validated on the
+ *    stream), never synchronises, never allocates device memory, and returns an
+ *    up_status (0 = UP_OK, negative = error).  Arguments are validated on the
  *    host before anything is launched; on error nothing is launched.
  *  - The caller owns every buffer.  Outputs are sized for the worst case
  *    (everything kept); the number of valid rows lives on the device, in
@@ -322,29 +321,13 @@ int up_rope_attention(const void* q, const void* k, const void* v, const int32_t
                       int Hkv, int d, float scale, float rope_theta, void* out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
-/* y[R, N] = x[R, K] . w[N, K]^T (+ residual[R, N] when not NULL); bf16 in and out,
- * float32 accumulation, through hipBLASLt (a plain GEMM).  residual may alias y.
- * workspace may be NULL with workspace_bytes = 0; otherwise 256-byte aligned and
- * offered to hipBLASLt.  The first call for a shape on a device creates the
- * hipBLASLt handle and picks the algorithm (host work, cached); later calls only
- * launch.  UP_EUNSUPPORTED if hipBLASLt has no algorithm for the shape. */
-int up_linear(const void* x, const void* w, const void* residual, int64_t R, int K, int N,
-              void* y, void* workspace, size_t workspace_bytes, void* stream);
-
 /* SwiGLU gate: a[r, j] = silu(gu[r, j]) * gu[r, F + j], float32 math, bf16 result.
  * gu : bf16 [R, 2F] (gate columns first);  a : bf16 [R, F];  F % 8 == 0. */
 int up_swiglu(const void* gu, int64_t R, int F, void* a, void* stream);
 
-/* SwiGLU FFN on R rows: y = swiglu(x . w_gu^T) . w_down^T (+ residual).
- * x : bf16 [R, H];  w_gu : bf16 [2F, H] (gate rows first);  w_down : bf16 [H, F];
- * residual : bf16 [R, H] or NULL (may alias y);  y : bf16 [R, H];  F % 8 == 0.
- * The intermediate x . w_gu^T and the gated activation are stored as bf16 in the
- * workspace: at least up_swiglu_ffn_workspace(R, H, F) bytes, 256-byte aligned. */
-size_t up_swiglu_ffn_workspace(int64_t R, int H, int F);
-
-int up_swiglu_ffn(const void* x, const void* w_gu, const void* w_down, const void* residual,
-                  int64_t R, int H, int F, void* y, void* workspace, size_t workspace_bytes,
-                  void* stream);
+/* The layer's GEMMs (up_linear, up_swiglu_ffn) are plain bf16 GEMMs served by
+ * hipBLASLt; they live in a separate library, libuniprefill_layer.so, declared in
+ * include/uniprefill_layer.h, so that this library links no vendor GEMM library. */
 
 /* ---------------------------------------------------------------------------
  * Diagnostics (not on the hot path)

@@ -270,7 +270,32 @@ def test_rope_attention_workspace_and_arguments(L):
     assert call(dict(B=0, cu_h=_p(np.zeros(1, np.int32)))) == UP_OK   # nothing to do
 
 
-def test_linear_swiglu_ffn_reject_bad_arguments(L):
+@pytest.fixture(scope="module")
+def LL():
+    from block_wise_token_amd._binding import layer_lib
+    return layer_lib()
+
+
+LAYER_HEADER = os.path.join(ROOT, "include", "uniprefill_layer.h")
+
+
+def test_layer_library_exports_its_header_and_decision_library_links_no_blas(LL):
+    text = re.sub(r"/\*.*?\*/", "", open(LAYER_HEADER).read(), flags=re.S)
+    syms = sorted(set(re.findall(r"\b(up_[a-z0-9_]+)\s*\(", text)))
+    assert syms == ["up_linear", "up_swiglu_ffn", "up_swiglu_ffn_workspace"]
+    for s_ in syms:
+        assert hasattr(LL, s_)
+    # the decision library needs no vendor GEMM library
+    import subprocess
+    from block_wise_token_amd._binding import LIB_PATH
+    out = subprocess.run(["readelf", "-d", LIB_PATH], capture_output=True, text=True).stdout
+    needed = re.findall(r"NEEDED.*\[(.*?)\]", out)
+    assert needed and not [n for n in needed if "blas" in n.lower()], needed
+
+
+def test_linear_swiglu_ffn_reject_bad_arguments(L, LL):
+    L_gate = L
+    L = LL
     L.up_linear.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                             ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                             ctypes.c_size_t, ctypes.c_void_p]
@@ -281,10 +306,10 @@ def test_linear_swiglu_ffn_reject_bad_arguments(L):
     assert L.up_linear(d, d, None, 8, 16, 16, d, None, 64, None) == UP_EINVAL   # bytes, no ptr
     assert L.up_linear(d, d, None, 8, 16, 16, d, ctypes.c_void_p(4100), 64, None) == UP_EWORKSPACE
     assert L.up_linear(d, d, None, 0, 16, 16, d, None, 0, None) == UP_OK
-    L.up_swiglu.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
-                            ctypes.c_void_p]
-    assert L.up_swiglu(d, 4, 12, d, None) == UP_EUNSUPPORTED                    # F % 8
-    assert L.up_swiglu(None, 4, 16, d, None) == UP_EINVAL
+    L_gate.up_swiglu.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    assert L_gate.up_swiglu(d, 4, 12, d, None) == UP_EUNSUPPORTED               # F % 8
+    assert L_gate.up_swiglu(None, 4, 16, d, None) == UP_EINVAL
     L.up_swiglu_ffn_workspace.restype = ctypes.c_size_t
     L.up_swiglu_ffn_workspace.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
     w = L.up_swiglu_ffn_workspace(1000, 4096, 14336)

@@ -40,6 +40,7 @@ def stub(monkeypatch):
             raise ValueError(f"{name} must be contiguous")
         return t
     monkeypatch.setattr(bd, "lib", lambda: _StubLib())
+    monkeypatch.setattr(bd, "layer_lib", lambda: _StubLib())
     monkeypatch.setattr(bd, "_dev", dev)
     monkeypatch.setattr(bd, "_stream", lambda s=None: 0)
 
