@@ -185,7 +185,10 @@ def main():
     roof_score.update({"traffic": measured_traffic(args.workload, SCORE_KERNEL)
                        if b.d == 128 else None,
                        "kernel": "up_score_partial_kernel", "avg_us": round(s_us, 2),
-                       "flop_per_byte": round(score_flops / score_bytes, 1)})
+                       "flop_per_byte": round(score_flops / score_bytes, 1),
+                       "variant": "one pass: a single Q K^T over the causal keys keeps a "
+                                  "per-(row, block) reference and sum; row statistics and "
+                                  "block masses follow from them (no second Q K^T)"})
     roof_gather = {"bound": "hbm", "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
                    "traffic": measured_traffic(args.workload, GATHER_KERNEL),
@@ -768,7 +771,8 @@ def copy_reference(torch, nbytes, steps):
 
 
 def cpu_baseline(b, hidden, pos, p, cfg):
-    """The oracle, untuned, timed on this host on one full decision of the same workload."""
+    """The oracle, untuned, timed on this host on whole decisions of the same workload,
+    repeated until about ten seconds of CPU work have been done (at most 16)."""
     from oracle import uniprefill_oracle as O
     blas = "unknown"
     try:
@@ -785,14 +789,17 @@ def cpu_baseline(b, hidden, pos, p, cfg):
             cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
     except (OSError, StopIteration):
         pass
-    log("[bench] cpu baseline: oracle on one full decision ...")
-    t0 = time.perf_counter()
-    O.decide(b.qwin, b.k, b.cu_seqlens, hidden, pos, b.Hq, b.Hkv, b.d, b.n, b.G, p, fast=True)
-    dt = time.perf_counter() - t0
-    log(f"[bench] cpu baseline: {dt:.1f}s")
-    return {"value": b.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full decision of {cfg and 'the same workload'} "
-                      f"({b.T} tokens: scores, Top-p, expand, compact, compose), NumPy float64",
+    log("[bench] cpu baseline: oracle on full decisions ...")
+    reps, dt = 0, 0.0
+    while reps == 0 or (dt < 10.0 and reps < 16):
+        t0 = time.perf_counter()
+        O.decide(b.qwin, b.k, b.cu_seqlens, hidden, pos, b.Hq, b.Hkv, b.d, b.n, b.G, p, fast=True)
+        dt += time.perf_counter() - t0
+        reps += 1
+    log(f"[bench] cpu baseline: {reps} decisions in {dt:.1f}s")
+    return {"value": reps * b.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full decisions of {cfg and 'the same workload'} "
+                      f"({b.T} tokens each: scores, Top-p, expand, compact, compose), NumPy float64",
             "seconds": dt, "cpu": cpu, "blas": blas}
 
 
