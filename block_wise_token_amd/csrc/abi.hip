@@ -618,7 +618,7 @@ int plan_attention(const int32_t* cu_h, int B, int Hq, int Hkv, int d, AttnShape
   s->B = B; s->Hq = Hq; s->Hkv = Hkv; s->d = d;
   s->HQ = gsz % 4 == 0 ? 4 : (gsz % 2 == 0 ? 2 : 1);
   s->TT = 4 / s->HQ;
-  const int tok_tile = attn_tile_tokens(d) * s->TT;
+  const int tok_tile = attn_tile_tokens(d, Hkv) * s->TT;
   int64_t Rp = 0, tiles = 0;
   for (int i = 0; i < B; ++i) {
     const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];

@@ -13,6 +13,7 @@
 //   up_swiglu_kernel       silu(gate) * up for the FFN.
 // The FFN and projection GEMMs are plain bf16 GEMMs; they are served by hipBLASLt in
 // the separate layer library (gemm.hip).
+#include "attn_geom.h"
 #include "up_dpp.h"
 #include "up_internal.h"
 
@@ -92,17 +93,7 @@ __global__ __launch_bounds__(kPlanThreads) void up_attn_plan_kernel(
   }
 }
 
-// Request holding padded row / tile x: the largest i in [0, B) with off[i] <= x
-// (empty requests share their successor's offset and are skipped).  off[B] > x.
-__device__ __forceinline__ int request_of(const int32_t* __restrict__ off, int B, int64_t x) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= x) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
+using attn::request_of;
 
 // ---------------------------------------------------------------------------
 // Rotary embedding and layout.  One workgroup per 64 padded rows.  Pair (i, i + d/2)
@@ -114,6 +105,8 @@ __device__ __forceinline__ int request_of(const int32_t* __restrict__ off, int B
 //   vt [Hkv][d][Rp]                    v transposed; within each 16-token group
 //                                      token bits 2 and 3 are swapped, so the keys a
 //                                      lane contracts in one MFMA step are adjacent
+//   kn [Hkv][Rp / 64]                  (when kn is given) the largest norm of the 64
+//                                      rotated bf16 key rows of each kv head and tile
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint16_t bf16_of_f64(double x) {
   const float f = __double2float_rz(x);
@@ -127,9 +120,7 @@ __device__ __forceinline__ double f64_of_bf16(uint16_t b) {
   return (double)__uint_as_float((uint32_t)b << 16);
 }
 
-__device__ __forceinline__ int swap_bits23(int t) {
-  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
-}
+using attn::swap_bits23;
 
 template <int D>
 __global__ __launch_bounds__(256) void up_rope_layout_kernel(
@@ -137,17 +128,24 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
     const WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ po, int B, int Hq, int Hkv, int64_t Rp, double log2_theta,
-    uint16_t* __restrict__ qr, uint16_t* __restrict__ kr, uint16_t* __restrict__ vt) {
+    uint16_t* __restrict__ qr, uint16_t* __restrict__ kr, uint16_t* __restrict__ vt,
+    float* __restrict__ kn) {
   constexpr int PG = D / 8;          // groups of 4 pairs per row
   constexpr int NU = 64 * PG / 256;  // (row, group) items per thread
   constexpr int VRS = 2 * D + 4;     // LDS bytes per v row (padded against bank conflicts)
   __shared__ __attribute__((aligned(16))) uint8_t vs[64 * VRS];
+  __shared__ uint32_t knorm2[kMaxAttnKvHeads];   // per kv head: largest |k'|^2 (float bits)
   if (hdr->valid != 1) return;
   const int64_t row0p = (int64_t)blockIdx.x * 64;
   const int i = request_of(po, B, row0p);
   const int t0 = (int)(row0p - po[i]);
   const int L = cu[i + 1] - cu[i];
   const int tid = threadIdx.x;
+  const bool norms = kn != nullptr;   // the host passes kn only when Hkv <= kMaxAttnKvHeads
+  if (norms) {
+    for (int h = tid; h < Hkv; h += 256) knorm2[h] = 0u;
+    __syncthreads();
+  }
 
   // q and k: each thread owns NU (row, 4-pair group) items and their 8 angles, taken
   // NC at a time so that the float64 angles of a chunk fit beside everything else.
@@ -180,6 +178,7 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
       const int H = isq ? Hq : Hkv;
       const uint16_t* src = isq ? q : k;
       uint16_t* dst = (isq ? qr : kr) + ((int64_t)hh * Rp + row0p) * D;
+      float rowmax = 0.f;   // keys: largest squared norm of this thread's rows
 #pragma unroll
       for (int u = 0; u < NC; ++u) {
         ushort4 lo = make_ushort4(0, 0, 0, 0), hi = make_ushort4(0, 0, 0, 0);
@@ -202,8 +201,28 @@ __global__ __launch_bounds__(256) void up_rope_layout_kernel(
         uint16_t* dd = dst + (int64_t)rr_of[u] * D + 4 * pg_of[u];
         *reinterpret_cast<ushort4*>(dd) = lo;
         *reinterpret_cast<ushort4*>(dd + D / 2) = hi;
+        if (norms && !isq) {
+          // squared norm of the rotated bf16 key row: its PG items sit in adjacent lanes
+          const uint16_t v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          float ss = 0.f;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const float f = __uint_as_float((uint32_t)v8[m] << 16);
+            ss = fmaf(f, f, ss);
+          }
+#pragma unroll
+          for (int off = PG / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+          rowmax = fmaxf(rowmax, ss);
+        }
       }
+      // non-negative floats order as their bit patterns
+      if (norms && !isq) atomicMax(&knorm2[hh], __float_as_uint(rowmax));
     }
+  }
+  if (norms) {
+    __syncthreads();
+    for (int h = tid; h < Hkv; h += 256)
+      kn[(int64_t)h * (Rp / 64) + blockIdx.x] = sqrtf(__uint_as_float(knorm2[h]));
   }
 
   // v: stage 64 rows of one kv head in LDS, then write 16-byte runs of 8 tokens per
@@ -534,6 +553,233 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The same attention with 8 waves per workgroup sharing one ring of 64-key stages
+// (d = 64 and 128, at most kMaxAttnKvHeads kv heads).  Workgroup = HQ query heads x
+// TT 64-token tiles of one kv head (HQ * TT = 4), two waves per (head, tile), 32
+// query rows per wave; two waves per SIMD, one workgroup per CU (128 KiB of LDS at
+// d = 128).  Every K and V^T stage is copied once for 256 query rows instead of 128,
+// and a stage costs one barrier per 64 keys instead of per 32.  A 64-key stage is two
+// half-steps of 32 keys (row tiles kt = 0, 1 of the K tile and granules 4 kt .. 4 kt
+// + 3 of the V^T rows).  Before a half-step's rebase check the wave compares a bound
+// on its logits -- the largest query norm of the wave times the stage's largest key
+// norm (kn, from the layout pass) times c -- with its references: when no logit can
+// exceed a reference by the rebase margin the check cannot fire and is skipped, so the
+// results are those of the unconditional check.  All addresses come from attn_geom.h.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
+    const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
+    const int32_t* __restrict__ tp, const float* __restrict__ kn, int B, int Hq, int Hkv,
+    int HQ, int TT, int64_t Rp, float c, uint16_t* __restrict__ out) {
+  using G = attn::W8<D>;
+  constexpr int NS = G::NS, DS = G::DS, DT = G::DT, SB = G::SB, SPT = G::SPT;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
+
+  if (hdr->valid != 1) return;
+  const attn::Wg w = attn::wg_of(blockIdx.x, blockIdx.y, Hq, Hkv, HQ, TT, B, cu, po, tp);
+  const int nst = w.nst;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5,
+            l32 = lane & 31;
+  const attn::Wv wv = attn::wave_of(w, wave, Hq, Hkv, HQ);
+  const int tw = wv.tw;
+  const bool wact = wv.act;
+
+  // Query operand: lane half h, k-step s covers d-elements [h D/2 + 8 s, +8).
+  bf16x8 qreg[DS];
+  if (wact) {
+    const uint16_t* src = qr + attn::q_src<D>(w, wv, l32, half, Rp);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(src + s * 8);
+  } else {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qreg[s] = bf16x8{};
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): only stage copies from here
+
+  // Largest query norm of the wave times c (float32 norms and the MFMA's float32 sums
+  // are far inside the 0.1% margin).
+  float qbound;
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = (float)qreg[s][e];
+        ss = fmaf(f, f, ss);
+      }
+    float m = pair_sum(ss);
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    qbound = __builtin_amdgcn_readfirstlane(sqrtf(m) * c * 1.001f);
+  }
+
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8*)lds;
+  auto issue = [&](int st) {
+    const uint32_t sb = lds_base + (uint32_t)((st & (NS - 1)) * SB);
+    const uint16_t* kst = kr + attn::k_stage<D>(w, st, Rp);
+#pragma unroll
+    for (int q = 0; q < G::KSPT; ++q)
+      lds_dma16(kst + G::k_src(q, tid), __builtin_amdgcn_readfirstlane(sb + G::k_dst(q, wave)));
+    const uint16_t* vst = vt + attn::v_stage<D>(w, st, Rp);
+#pragma unroll
+    for (int q = 0; q < G::VSPT; ++q)
+      lds_dma16(vst + G::v_src(q, tid, Rp),
+                __builtin_amdgcn_readfirstlane(sb + G::v_dst(q, wave)));
+  };
+
+  uint32_t krd[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) krd[s] = G::k_rd(l32, half, s);
+  uint32_t vrd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) vrd[j] = G::v_rd(l32, 2 * j + half);
+
+  float Rs = 0.f, lsum = 0.f;
+  f32x16 O[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
+  const int qtok = attn::query_token(wv, l32);
+
+  // S^T of half-step hs (keys [32 hs, 32 hs + 32): stage hs / 2, row tile hs % 2).
+  auto s_mfma = [&](int hs, f32x16& acc) {
+    const uint8_t* sl = lds + ((hs >> 1) & (NS - 1)) * SB + (hs & 1) * 32 * G::KRB;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sl + krd[s]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], s == 0 ? f32x16{} : acc, 0, 0, 0);
+    }
+  };
+  auto mask = [&](int hs, f32x16& acc) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (attn::acc_key(hs, e, half) > qtok) acc[e] = kNegInf;
+  };
+  auto rebase = [&](const f32x16& acc, bool init) {
+    float m0 = kNegInf, m1 = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      m0 = fmaxf(m0, acc[e]);
+      m1 = fmaxf(m1, acc[e + 1]);
+    }
+    const float mx = pair_max(fmaxf(m0, m1)) * c;
+    const bool need = init || mx > Rs + kRebase;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      if (init) {
+        Rs = mx;
+      } else {
+        const float rn = fmaxf(Rs, mx);
+        const float sc = __builtin_amdgcn_exp2f(Rs - rn);
+        lsum *= sc;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[dt] *= sc;
+        Rs = rn;
+      }
+    }
+  };
+  // True when no logit of half-step hs can exceed the wave's references by kRebase.
+  auto bound_ok = [&](int hs) {
+    const float b = qbound * kn[attn::kn_index(w, hs >> 1, Rp)] - kRebase;
+    return __builtin_amdgcn_ballot_w64(b > Rs) == 0;
+  };
+  auto pv = [&](int hs, const f32x16& acc) {
+    const int kt = hs & 1;
+    const uint8_t* sl = lds + ((hs >> 1) & (NS - 1)) * SB;
+    bf16x8 va[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        va[dt][jj] = *reinterpret_cast<const bf16x8*>(sl + dt * 32 * G::VRB + vrd[2 * kt + jj]);
+    f32x16 p;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      p[e] = __builtin_amdgcn_exp2f(fmaf(acc[e], c, -Rs));
+      p[e + 1] = __builtin_amdgcn_exp2f(fmaf(acc[e + 1], c, -Rs));
+      s0 += p[e];
+      s1 += p[e + 1];
+    }
+    lsum += s0 + s1;
+    const bf16x8 pb[2] = {__builtin_convertvector(p.lo, bf16x8),
+                          __builtin_convertvector(p.hi, bf16x8)};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][jj], pb[jj], O[dt], 0, 0, 0);
+  };
+
+  // Ring: stages st+1 and st+2 in flight while st is consumed; stage st+1 is waited
+  // for (and published by a barrier, after which every wave is done with stage st-1)
+  // before the second half of stage st, whose body issues the S^T of stage st+1's
+  // first half; then stage st-1's slot is refilled with stage st+3.
+  auto sync_for = [&](int st) {
+    if (st + 1 >= nst) return;
+    if (st + 2 < nst) wait_barrier<SPT>();
+    else wait_barrier<0>();
+    if (st + 3 < nst) issue(st + 3);
+  };
+
+  issue(0);
+  if (nst > 1) issue(1);
+  if (nst > 2) issue(2);
+  if (nst > 2) wait_barrier<2 * SPT>();
+  else if (nst > 1) wait_barrier<SPT>();
+  else wait_barrier<0>();
+
+  const int last_hs = 2 * tw + 1;   // the wave's last half-step (end of its diagonal stage)
+  f32x16 accA, accB;
+  if (wact) {
+    s_mfma(0, accA);
+    if (tw == 0) mask(0, accA);
+    rebase(accA, true);
+  }
+  // cur holds S^T of half-step hs; nxt receives half-step hs+1's.
+  auto body = [&](int hs, f32x16& cur, f32x16& nxt) {
+    if (!wact || hs > last_hs) return;
+    if (hs + 1 < 2 * tw) {            // next half-step is before the diagonal stage
+      const bool skip = bound_ok(hs + 1);
+      s_mfma(hs + 1, nxt);
+      pv(hs, cur);
+      if (!skip) rebase(nxt, false);
+    } else if (hs + 1 <= last_hs) {   // next half-step is in the diagonal stage
+      const bool skip = bound_ok(hs + 1);
+      s_mfma(hs + 1, nxt);
+      pv(hs, cur);
+      mask(hs + 1, nxt);
+      if (!skip) rebase(nxt, false);
+    } else {
+      pv(hs, cur);
+    }
+  };
+  for (int st = 0; st < nst; ++st) {
+    body(2 * st, accA, accB);
+    sync_for(st);
+    body(2 * st + 1, accB, accA);
+  }
+
+  if (!wact) return;
+  const float inv = 1.f / pair_sum(lsum);
+  if (qtok >= w.L) return;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int eg = 0; eg < 4; ++eg) {
+      const int dv = dt * 32 + 8 * eg + 4 * half;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      const f32x4 o4 = {O[dt][4 * eg] * inv, O[dt][4 * eg + 1] * inv, O[dt][4 * eg + 2] * inv,
+                        O[dt][4 * eg + 3] * inv};
+      *reinterpret_cast<bf16x4*>(out + attn::out_index<D>(cu, w, wv, l32, Hq, dv)) =
+          __builtin_convertvector(o4, bf16x4);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // SwiGLU gate: a[r][j] = silu(gu[r][j]) * gu[r][F + j] in float32, rounded to
 // bfloat16.  Eight columns per thread, grid-stride.
 // ---------------------------------------------------------------------------
@@ -576,6 +822,8 @@ AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp) {
   o += align_up((size_t)Hkv * Rp * d * 2);
   w.vt = o;
   o += align_up((size_t)Hkv * Rp * d * 2);
+  w.kn = o;
+  if (attn_w8(d, Hkv)) o += align_up((size_t)Hkv * (Rp / 64) * sizeof(float));
   w.total = o;
   return w;
 }
@@ -584,7 +832,7 @@ hipError_t launch_attn_plan(const int32_t* cu, const AttnShape& s, void* ws, con
                             int* err, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   hipLaunchKernelGGL(up_attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, cu, s.B,
-                     attn_tile_tokens(s.d) * s.TT,
+                     attn_tile_tokens(s.d, s.Hkv) * s.TT,
                      s.R, s.Rp, s.tiles, reinterpret_cast<WsHeader*>(w + L.hdr),
                      reinterpret_cast<int32_t*>(w + L.po), reinterpret_cast<int32_t*>(w + L.tp),
                      err);
@@ -600,19 +848,20 @@ hipError_t launch_rope_layout(const void* q, const void* k, const void* v, const
   auto* qr = reinterpret_cast<uint16_t*>(w + L.qr);
   auto* kr = reinterpret_cast<uint16_t*>(w + L.kr);
   auto* vt = reinterpret_cast<uint16_t*>(w + L.vt);
+  auto* kn = attn_w8(s.d, s.Hkv) ? reinterpret_cast<float*>(w + L.kn) : nullptr;
   const dim3 grid((unsigned)(s.Rp / 64));
   auto kq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(k);
   auto kv = static_cast<const uint16_t*>(v);
   if (s.d == 64)
     hipLaunchKernelGGL(up_rope_layout_kernel<64>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr, cu,
-                       po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
+                       po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt, kn);
   else if (s.d == 128)
     hipLaunchKernelGGL(up_rope_layout_kernel<128>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr,
-                       cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
+                       cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt, kn);
   else
     hipLaunchKernelGGL(up_rope_layout_kernel<256>, grid, dim3(256), 0, st, kq, kk, kv, pos, hdr,
-                       cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt);
+                       cu, po, s.B, s.Hq, s.Hkv, s.Rp, log2_theta, qr, kr, vt, kn);
   return hipGetLastError();
 }
 
@@ -627,6 +876,16 @@ hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, con
   const auto* vt = reinterpret_cast<const uint16_t*>(w + L.vt);
   const dim3 grid((unsigned)(s.Hkv * (s.Hq / s.Hkv / s.HQ)), (unsigned)s.tiles);
   auto o = static_cast<uint16_t*>(out);
+  if (attn_w8(s.d, s.Hkv)) {
+    const auto* kn = reinterpret_cast<const float*>(w + L.kn);
+    if (s.d == 64)
+      hipLaunchKernelGGL(up_attention_w8_kernel<64>, grid, dim3(512), 0, st, qr, kr, vt, hdr, cu,
+                         po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+    else
+      hipLaunchKernelGGL(up_attention_w8_kernel<128>, grid, dim3(512), 0, st, qr, kr, vt, hdr, cu,
+                         po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+    return hipGetLastError();
+  }
   if (s.d == 64)
     hipLaunchKernelGGL(up_attention_kernel<64>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
                        tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);

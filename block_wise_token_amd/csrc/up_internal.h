@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "attn_geom.h"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -196,16 +198,19 @@ hipError_t launch_compose(const int32_t* prev, int prev_len, const int32_t* idx,
                           hipStream_t st);
 
 // Layer on the surviving tokens (consumer.hip).
-// Query tokens per wave in the attention kernel (one 32-row tile).
-constexpr int attn_tile_tokens(int) { return 32; }
+// The 8-wave attention kernel (64-token tiles per query-head pair) serves d = 64 and
+// 128 up to attn::kMaxKvHeads kv heads; the 4-wave kernel (32-token tiles) the rest.
+constexpr int kMaxAttnKvHeads = attn::kMaxKvHeads;
+constexpr bool attn_w8(int d, int Hkv) { return attn::w8_serves(d, Hkv); }
+constexpr int attn_tile_tokens(int d, int Hkv) { return attn_w8(d, Hkv) ? 64 : 32; }
 struct AttnShape {
   int B, Hq, Hkv, d;
-  int HQ, TT;       // query heads and per-wave token tiles per attention workgroup (HQ * TT = 4)
+  int HQ, TT;       // query heads and per-head token tiles per attention workgroup (HQ * TT = 4)
   int64_t R, Rp;    // rows; padded rows (every request rounded up to 64)
-  int64_t tiles;    // attention workgroup tiles of attn_tile_tokens(d) * TT tokens
+  int64_t tiles;    // attention workgroup tiles of attn_tile_tokens(d, Hkv) * TT tokens
 };
 struct AttnWs {
-  size_t hdr, po, tp, qr, kr, vt, total;
+  size_t hdr, po, tp, qr, kr, vt, kn, total;   // kn: 8-wave kernel only (else empty)
 };
 AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp);
 hipError_t launch_attn_plan(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,

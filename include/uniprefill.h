@@ -308,10 +308,12 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
  * rope_theta > 1 (e.g. 500000 for the Llama-3.1 shape).
  * Probabilities enter the P.V product as bf16; softmax statistics and accumulation
  * are float32.  Limits: sum of ceil(L_i / 64) padded rows < 2^31 and at most 65535
- * workgroup tiles, a tile spanning 32 * 4 / m query tokens, m = the largest of 4, 2, 1
- * dividing Hq / Hkv (about 2M rows at Hq / Hkv = 4).
+ * workgroup tiles, a tile spanning t * 4 / m query tokens, m = the largest of 4, 2, 1
+ * dividing Hq / Hkv, t = 64 for d = 64 and 128 with Hkv <= 256, else 32 (about 4M
+ * rows at d = 128 and Hq / Hkv = 4).
  * workspace : at least up_rope_attention_workspace(...) bytes, 256-byte aligned
- *             (rotated q and k, transposed v, plan).
+ *             (rotated q and k, transposed v, plan; for d = 64 and 128 with
+ *             Hkv <= 256 also the largest key norm of each 64-row tile per kv head).
  * A device cu_seqlens whose totals (rows, padded rows, workgroup tiles) differ from
  * those of cu_seqlens_h raises error bit 1 and nothing is written. */
 size_t up_rope_attention_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d);

@@ -355,19 +355,23 @@ def test_layer_decision_workspace_and_arguments(L):
 
 
 def test_rope_attention_rejects_more_than_65535_tiles(L):
-    """Workgroup tiles of 32 tokens (4 query heads per kv head, one 32-row tile per
-    wave) are the grid's y dimension: 65535 tiles are accepted, one more is
-    UP_EUNSUPPORTED; with one query head per kv head a tile spans 4 x 32 tokens."""
+    """Workgroup tiles are the grid's y dimension: 65535 tiles are accepted, one more is
+    UP_EUNSUPPORTED.  With 4 query heads per kv head a tile is one token tile per
+    head: 64 tokens for the 8-wave kernel (d = 64, 128 with at most 256 kv heads), 32
+    for the 4-wave kernel (d = 256, or more kv heads); with one query head per kv head
+    a tile spans 4 token tiles."""
     f = L.up_rope_attention_workspace
     f.restype = ctypes.c_size_t
-    for d in (64, 128, 256):
-        assert f(_p(_cu([32 * 65535])), 1, 8, 2, d) > 0
-        assert f(_p(_cu([32 * 65535 + 1])), 1, 8, 2, d) == 0
-    assert f(_p(_cu([128 * 65535])), 1, 2, 2, 128) > 0
-    assert f(_p(_cu([128 * 65535 + 1])), 1, 2, 2, 128) == 0
+    for d, tok in ((64, 64), (128, 64), (256, 32)):
+        assert f(_p(_cu([tok * 65535])), 1, 8, 2, d) > 0
+        assert f(_p(_cu([tok * 65535 + 1])), 1, 8, 2, d) == 0
+    assert f(_p(_cu([256 * 65535])), 1, 2, 2, 128) > 0
+    assert f(_p(_cu([256 * 65535 + 1])), 1, 2, 2, 128) == 0
+    assert f(_p(_cu([32 * 65535])), 1, 2048, 512, 128) > 0     # 512 kv heads: 4-wave kernel
+    assert f(_p(_cu([32 * 65535 + 1])), 1, 2048, 512, 128) == 0
     a = L.up_rope_attention
     a.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_float] * 2 + \
                  [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     d = ctypes.c_void_p(4096)
-    cu = _cu([32 * 65535 + 1])
+    cu = _cu([64 * 65535 + 1])
     assert a(d, d, d, d, d, _p(cu), 1, 8, 2, 128, 0.0, 500000.0, d, None, 0, None) == UP_EUNSUPPORTED
