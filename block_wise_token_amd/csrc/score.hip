@@ -783,20 +783,47 @@ __global__ __launch_bounds__(256) void up_block_mass_kernel(
   const float2* rrow = rs + (int64_t)pr.win_off * Hq;
   constexpr int U = 8;
   double acc = 0.0;
-  int64_t e = threadIdx.x;
-  for (; e + (U - 1) * 256 < terms; e += U * 256) {
-    float2 v[U], w[U];
+  if ((terms & 1) == 0 && (((uintptr_t)mrow | (uintptr_t)rrow) & 15) == 0) {
+    // two consecutive terms per 16-byte load; thread t sums terms 2t, 2t + 1, then
+    // those 512 on, in that order
+    const float4* m4 = reinterpret_cast<const float4*>(mrow);
+    const float4* r4 = reinterpret_cast<const float4*>(rrow);
+    const int64_t pairs = terms >> 1;
+    int64_t e = threadIdx.x;
+    for (; e + (U - 1) * 256 < pairs; e += U * 256) {
+      float4 v[U], w[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v[u] = mrow[e + u * 256];
-      w[u] = rrow[e + u * 256];
+      for (int u = 0; u < U; ++u) {
+        v[u] = m4[e + u * 256];
+        w[u] = r4[e + u * 256];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        acc += (double)(v[u].y * fast_exp2(v[u].x - w[u].x) * w[u].y);
+        acc += (double)(v[u].w * fast_exp2(v[u].z - w[u].z) * w[u].w);
+      }
     }
+    for (; e < pairs; e += 256) {
+      const float4 v = m4[e], w = r4[e];
+      acc += (double)(v.y * fast_exp2(v.x - w.x) * w.y);
+      acc += (double)(v.w * fast_exp2(v.z - w.z) * w.w);
+    }
+  } else {
+    int64_t e = threadIdx.x;
+    for (; e + (U - 1) * 256 < terms; e += U * 256) {
+      float2 v[U], w[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc += (double)(v[u].y * fast_exp2(v[u].x - w[u].x) * w[u].y);
-  }
-  for (; e < terms; e += 256) {
-    const float2 v = mrow[e], w = rrow[e];
-    acc += (double)(v.y * fast_exp2(v.x - w.x) * w.y);
+      for (int u = 0; u < U; ++u) {
+        v[u] = mrow[e + u * 256];
+        w[u] = rrow[e + u * 256];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc += (double)(v[u].y * fast_exp2(v[u].x - w[u].x) * w[u].y);
+    }
+    for (; e < terms; e += 256) {
+      const float2 v = mrow[e], w = rrow[e];
+      acc += (double)(v.y * fast_exp2(v.x - w.x) * w.y);
+    }
   }
   const double tot = wg256_sum_f64(acc, red);
   if (threadIdx.x == 0) mass[blk] = tot;

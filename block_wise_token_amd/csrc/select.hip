@@ -169,6 +169,7 @@ struct SelLds {
   uint64_t rem;       // remainder of p in units of 2^sh of the cut's exponent
   uint32_t rem_k;     // remainder of the count (Top-k)
   uint32_t ties;      // blocks whose score equals the cut score
+  uint32_t full;      // the cut's score bits, when a pass leaves one candidate
   int keep_all;
 };
 
@@ -349,6 +350,7 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
   const int copy = lane & (kCopies - 1);
 
   if (!all && !none && nb > 0) {
+    bool early = false;   // a pass left a single candidate
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
       const int dsh = digit_shift(pass);
@@ -436,9 +438,23 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
         __syncthreads();
         break;
       }
+      // One candidate left in the winning bin: it is the cut (the remainder it has to
+      // meet is at most its own value, so one tie is kept), and the later passes would
+      // only recover its remaining digits.  S.ties and S.prefix are written by the next
+      // pass's winner only after that pass's first barrier, which every wave reaches
+      // after these reads; the branch is the same in every wave.
+      if (pass < 3 && S.ties == 1) {
+        const uint32_t pfx = S.prefix;
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+          if (u[q] != kAbsent && (u[q] >> dsh) == pfx) S.full = u[q];
+        __syncthreads();
+        early = true;
+        break;
+      }
     }
     if (!S.keep_all) {
-      ustar = S.prefix;
+      ustar = early ? S.full : S.prefix;
       if (mode == 0) {
         // The remainder is met by j ties of value sig(ustar) * 2^sh each.
         const uint64_t t = sig_of(ustar);
