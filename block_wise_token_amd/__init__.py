@@ -28,6 +28,8 @@ from ._binding import (  # noqa: F401
     topk_select,
     topp_select,
     rope_attention,
+    rope_attention_scores,
+    rope_attention_scores_workspace_bytes,
     rope_attention_workspace_bytes,
     linear,
     swiglu,

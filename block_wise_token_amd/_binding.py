@@ -81,6 +81,11 @@ def lib():
     i64 = ctypes.c_int64
     L.up_rope_attention_workspace.restype = cs
     L.up_rope_attention_workspace.argtypes = [vp, ci, ci, ci, ci]
+    L.up_rope_attention_scores_workspace.restype = cs
+    L.up_rope_attention_scores_workspace.argtypes = [vp, ci, ci, ci, ci, ci, ci]
+    L.up_rope_attention_scores.restype = ci
+    L.up_rope_attention_scores.argtypes = [vp, vp, vp, i32p, i32p, vp, ci, ci, ci, ci, cf, cf, ci,
+                                           ci, vp, f32p, f32p, vp, cs, vp]
     L.up_rope_attention.restype = ci
     L.up_rope_attention.argtypes = [vp, vp, vp, i32p, i32p, vp, ci, ci, ci, ci, cf, cf, vp, vp, cs,
                                     vp]
@@ -633,6 +638,55 @@ def rope_attention(q, k, v, pos, cu_seqlens, cu_h, scale=0.0, rope_theta=500000.
                                  _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "up_rope_attention")
     return out
+
+
+def rope_attention_scores_workspace_bytes(cu_h, Hq, Hkv, d, n, G) -> int:
+    h = _HostCu(cu_h)
+    return int(lib().up_rope_attention_scores_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
+
+
+def rope_attention_scores(q, k, v, pos, cu_seqlens, cu_h, n, G, scale=0.0, rope_theta=500000.0,
+                          out=None, scores=None, row_lse=None, workspace=None, stream=None):
+    """The rotary attention of ``rope_attention`` and the block scores of its window rows
+    from the same probabilities; see up_rope_attention_scores.  Returns (out, scores)."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(k, torch.bfloat16, "k")
+    _dev(v, torch.bfloat16, "v")
+    _dev(pos, torch.int32, "pos")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    h = _HostCu(cu_h)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _rank(t, 3, name)
+    Hq, d, Hkv = int(q.shape[1]), int(q.shape[2]), int(k.shape[1])
+    R = h.T
+    if int(q.shape[0]) < R:
+        raise ValueError(f"q has {int(q.shape[0])} rows, cu_seqlens needs {R}")
+    if tuple(k.shape) != tuple(v.shape) or int(k.shape[0]) < R or int(k.shape[2]) != d:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} must both be "
+                         f"[>= {R}, Hkv, {d}]")
+    _buf(pos, torch.int32, R, "pos")
+    _buf(cu_seqlens, torch.int32, h.B + 1, "cu_seqlens")
+    nb = h.nb_tot(G)
+    if out is None:
+        out = torch.empty_like(q)
+    _buf(out, torch.bfloat16, R * Hq * d, "out")
+    if scores is None:
+        scores = torch.empty(max(nb, 1), dtype=torch.float32, device=q.device)
+    _buf(scores, torch.float32, nb, "scores")
+    if row_lse is not None:
+        W = int(sum(min(int(L), n) for L in np.diff(h.arr)))
+        _buf(row_lse, torch.float32, W * Hq, "row_lse")
+    need = int(lib().up_rope_attention_scores_workspace(h.ptr, h.B, Hq, Hkv, d, n, G))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _buf(workspace, torch.uint8, need, "workspace")
+    st = lib().up_rope_attention_scores(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(cu_seqlens), h.ptr, h.B, Hq, Hkv, d,
+        float(scale), float(rope_theta), int(n), int(G), _ptr(out), _ptr(scores),
+        _ptr(row_lse) if row_lse is not None else None, _ptr(workspace), workspace.numel(),
+        _stream(stream))
+    _check(st, "up_rope_attention_scores")
+    return out, scores
 
 
 def linear(x, w, residual=None, out=None, workspace=None, stream=None):

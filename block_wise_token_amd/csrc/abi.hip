@@ -671,6 +671,68 @@ int up_rope_attention(const void* q, const void* k, const void* v, const int32_t
   return e == hipSuccess ? UP_OK : UP_EHIP;
 }
 
+size_t up_rope_attention_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv,
+                                          int d, int n, int G) {
+  AttnShape a;
+  ScoreShape s;
+  Totals t;
+  if (plan_attention(cu_seqlens_h, B, Hq, Hkv, d, &a) != UP_OK) return 0;
+  if (plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t) != UP_OK) return 0;
+  return align_up(attn_ws_layout(B, Hq, Hkv, d, a.Rp).total) + score_ws_layout(B, t).total;
+}
+
+int up_rope_attention_scores(const void* q, const void* k, const void* v, const int32_t* pos,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B,
+                             int Hq, int Hkv, int d, float scale, float rope_theta, int n, int G,
+                             void* out, float* scores, float* row_lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  AttnShape a;
+  int st = plan_attention(cu_seqlens_h, B, Hq, Hkv, d, &a);
+  if (st != UP_OK) return st;
+  ScoreShape s;
+  Totals t;
+  st = plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t);
+  if (st != UP_OK) return st;
+  if (!(rope_theta > 1.f) || std::isinf(rope_theta)) return UP_EINVAL;
+  if (B == 0 || a.R == 0) return UP_OK;
+  if (!q || !k || !v || !pos || !cu_seqlens || !out || !scores) return UP_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(scores, 4) || (row_lse && !aligned(row_lse, 4)))
+    return UP_EINVAL;
+  const AttnWs LA = attn_ws_layout(B, Hq, Hkv, d, a.Rp);
+  const size_t soff = align_up(LA.total);
+  const ScoreWs LS = score_ws_layout(B, t);
+  if (!workspace || workspace_bytes < soff + LS.total || !aligned(workspace, kWsAlign))
+    return UP_EWORKSPACE;
+  if (!(scale > 0.f) || std::isinf(scale)) scale = (float)(1.0 / std::sqrt((double)d));
+  const float c = (float)((double)scale * 1.4426950408889634);
+  int* err = error_word();
+  if (!err) return UP_EHIP;
+  hipStream_t hs = as_stream(stream);
+  char* sws = static_cast<char*>(workspace) + soff;
+  hipError_t e = timed(9, hs, [&] {
+    return launch_score_plan(cu_seqlens, s, t, sws, LS.plan, err, hs);
+  });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(12, hs, [&] { return launch_attn_plan(cu_seqlens, a, workspace, LA, err, hs); });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(13, hs, [&] {
+    return launch_rope_layout(q, k, v, pos, cu_seqlens, a, workspace, LA,
+                              std::log2((double)rope_theta), hs);
+  });
+  if (e != hipSuccess) return UP_EHIP;
+  const AttnScoreOut so{reinterpret_cast<WsHeader*>(sws),
+                        reinterpret_cast<const ReqPlan*>(sws + LS.plan),
+                        reinterpret_cast<float2*>(sws + LS.ml),
+                        reinterpret_cast<float2*>(sws + LS.rs), row_lse, G};
+  e = timed(14, hs, [&] { return launch_attention(cu_seqlens, a, workspace, LA, c, out, hs, &so); });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(2, hs, [&] { return launch_block_mass(s, t, sws, LS, hs); });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(3, hs, [&] { return launch_normalize(s, t, sws, LS, scores, hs); });
+  return e == hipSuccess ? UP_OK : UP_EHIP;
+}
+
 int up_swiglu(const void* gu, int64_t R, int F, void* a, void* stream) {
   if (R < 0 || F <= 0) return UP_EINVAL;
   if (F % 8 != 0) return UP_EUNSUPPORTED;

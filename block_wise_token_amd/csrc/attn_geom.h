@@ -170,5 +170,18 @@ UP_HD int64_t out_index(const int32_t* cu, const Wg& w, const Wv& v, int l32, in
   return (((int64_t)cu[w.i] + query_token(v, l32)) * Hq + v.head) * D + dv;
 }
 
+// Window-row block statistics (the attention's fused form of the block scores).  The
+// window is the last W = min(n, L) tokens of a request; window row wr of query head
+// head (kv head g, gs = Hq / Hkv query heads per kv head) is term
+// g gs W + wr gs + (head - g gs) of the request's [Hkv][gs W] rows.
+UP_HD int64_t win_term(int g, int gs, int W, int wr, int head) {
+  return (int64_t)g * gs * W + (int64_t)wr * gs + (head - g * gs);
+}
+// A wave's 32-key half-step hs closes a G-key block at its end, or is the wave's last.
+UP_HD bool stats_flush(int hs, int last, int G) { return ((hs + 1) * 32) % G == 0 || hs == last; }
+UP_HD int stats_block(int hs, int G) { return (hs * 32) / G; }
+// First block wholly after a wave whose last half-step is `last`.
+UP_HD int stats_tail_first(int last, int G) { return ((last + 1) * 32 - 1) / G + 1; }
+
 }  // namespace attn
 }  // namespace up

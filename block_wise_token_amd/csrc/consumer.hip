@@ -321,17 +321,74 @@ __device__ __forceinline__ int k_swz(int key) {
 
 constexpr float kRebase = 32.f;
 
+// Window-row block statistics (the fused form of the block scores).  A wave whose
+// rows reach the last W = min(n, L) tokens of its request sums, per lane, the
+// probabilities 2^(x - Rs) of each G-key block beside its softmax (bsum, rescaled with
+// l and O when Rs moves); at a block's end (or at the wave's last 32-key half-step) the
+// two lanes of a window row add their halves and one of them stores (Rs, block sum)
+// for that (row, block).  Blocks wholly after the wave's diagonal tile hold no key the
+// row may see: they get (-inf, 0).  At the end the row's (Rs, 1 / l) and, when asked,
+// its natural-log log-sum-exp are stored.  Pairs and rows use the score pass's layouts:
+// pair (b, e) at ml_off + b Hq W + e and row e at win_off Hq + e, with
+// e = g gs W + w gs + (head - g gs) for window row w of query head head (gs = Hq / Hkv).
+struct WinStats {
+  bool wave = false;   // some row of the wave is a window row (wave-uniform)
+  bool row = false;    // this lane's row is a window row
+  float bsum = 0.f;
+  float2* pair0 = nullptr;   // this row's pair of block 0
+  float2* rsp = nullptr;
+  float* lsep = nullptr;
+  int64_t terms = 0;
+  int nb = 0, G = 64;
+
+  __device__ __forceinline__ void init(const AttnScoreOut& so, int i, int L, int g, int head,
+                                       int Hq, int Hkv, bool wact, int last_row_tok, int qtok) {
+    if (!wact || so.hdr->valid != 1) return;
+    const ReqPlan pr = so.plan[i];
+    const int wfirst = L - pr.W;
+    wave = last_row_tok >= wfirst;
+    if (!wave) return;
+    const int gs = Hq / Hkv;
+    row = qtok >= wfirst && qtok < L;
+    const int wr = row ? qtok - wfirst : 0;
+    terms = (int64_t)Hq * pr.W;
+    const int64_t e = attn::win_term(g, gs, pr.W, wr, head);
+    pair0 = so.ml + pr.ml_off + e;
+    rsp = so.rs + (int64_t)pr.win_off * Hq + e;
+    lsep = so.row_lse ? so.row_lse + ((int64_t)pr.win_off + wr) * Hq + head : nullptr;
+    nb = pr.nb;
+    G = so.G;
+  }
+  // After the P V of half-step hs (keys [32 hs, 32 hs + 32)); last = the wave's last.
+  // A half-step wholly past the request's last key (the padded end of its last 64-token
+  // tile) can lie in block nb: nothing is stored for it (its probabilities are zero).
+  __device__ __forceinline__ void flush(int hs, int last, float Rs, int half) {
+    if (!wave || !attn::stats_flush(hs, last, G)) return;
+    const float tot = pair_sum(bsum);
+    const int b = attn::stats_block(hs, G);
+    if (row && half == 0 && b < nb) pair0[(int64_t)b * terms] = make_float2(Rs, tot);
+    bsum = 0.f;
+  }
+  __device__ __forceinline__ void finish(int last, float Rs, float l, int half) {
+    if (!wave || !row || half != 0) return;
+    for (int b = attn::stats_tail_first(last, G); b < nb; ++b)
+      pair0[(int64_t)b * terms] = make_float2(kNegInf, 0.f);
+    *rsp = make_float2(Rs, 1.f / l);
+    if (lsep) *lsep = (Rs + log2f(l)) * 0.6931471805599453f;
+  }
+};
+
 // V^T tile rows are 64 bytes (32 tokens): granule g of row r sits at g ^ ((r >> 2) & 3),
 // which spreads the 16 rows one 16-lane group reads over all 64 banks.
 __device__ __forceinline__ int v64_swz(int row) { return (row >> 2) & 3; }
 
-template <int D>
+template <int D, bool ST>
 __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
     const int32_t* __restrict__ tp, int B, int Hq, int Hkv, int HQ, int TT, int64_t Rp,
-    float c, uint16_t* __restrict__ out) {
+    float c, uint16_t* __restrict__ out, AttnScoreOut so) {
   constexpr int NT = 256, NS = 4, UK = 32;
   constexpr int DS = D / 16;             // MFMA k-steps over the head dimension
   constexpr int DT = D / 32;             // 32-row tiles of O^T
@@ -347,7 +404,11 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
   static_assert(2 * SPT < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
 
-  if (hdr->valid != 1) return;
+  if (hdr->valid != 1) {
+    if constexpr (ST)
+      if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) so.hdr->valid = 0;
+    return;
+  }
   const int gsz = Hq / Hkv, quads = gsz / HQ;
   const int g = blockIdx.x / quads, quad = blockIdx.x - g * quads;
   const int f = blockIdx.y;
@@ -418,6 +479,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
   const int qtok = tw * 32 + l32;
+  WinStats ws;
+  if constexpr (ST) ws.init(so, i, L, g, head, Hq, Hkv, wact, tw * 32 + 31, qtok);
 
   // S^T of stage (= half-step) hs into acc.
   auto s_mfma = [&](int hs, f32x16& acc) {
@@ -452,6 +515,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
         const float rn = fmaxf(Rs, mx);
         const float sc = __builtin_amdgcn_exp2f(Rs - rn);
         lsum *= sc;
+        if constexpr (ST) ws.bsum *= sc;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) O[dt] *= sc;
         Rs = rn;
@@ -477,6 +541,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
       s1 += p[e + 1];
     }
     lsum += s0 + s1;
+    if constexpr (ST) ws.bsum += s0 + s1;
     const bf16x8 pb[2] = {__builtin_convertvector(p.lo, bf16x8),
                           __builtin_convertvector(p.hi, bf16x8)};
 #pragma unroll
@@ -516,14 +581,17 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
     if (hs + 1 < tw) {
       s_mfma(hs + 1, nxt);
       pv(hs, cur);
+      if constexpr (ST) ws.flush(hs, tw, Rs, half);
       rebase(nxt, false);
     } else if (hs + 1 == tw) {
       s_mfma(hs + 1, nxt);
       pv(hs, cur);
+      if constexpr (ST) ws.flush(hs, tw, Rs, half);
       mask(hs + 1, nxt);
       rebase(nxt, false);
     } else {
       pv(hs, cur);
+      if constexpr (ST) ws.flush(hs, tw, Rs, half);
     }
   };
   for (int st = 0; st < nst; st += 2) {
@@ -536,7 +604,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
   }
 
   if (!wact) return;
-  const float inv = 1.f / pair_sum(lsum);
+  const float lt = pair_sum(lsum), inv = 1.f / lt;
+  if constexpr (ST) ws.finish(tw, Rs, lt, half);
   if (qtok >= L) return;
   uint16_t* dst = out + (((int64_t)cu[i] + qtok) * Hq + head) * D;
 #pragma unroll
@@ -566,18 +635,24 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
 // exceed a reference by the rebase margin the check cannot fire and is skipped, so the
 // results are those of the unconditional check.  All addresses come from attn_geom.h.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool ST>
 __global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
     const int32_t* __restrict__ tp, const float* __restrict__ kn, int B, int Hq, int Hkv,
-    int HQ, int TT, int64_t Rp, float c, uint16_t* __restrict__ out) {
+    int HQ, int TT, int64_t Rp, float c, uint16_t* __restrict__ out, AttnScoreOut so) {
   using G = attn::W8<D>;
   constexpr int NS = G::NS, DS = G::DS, DT = G::DT, SB = G::SB, SPT = G::SPT;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
 
-  if (hdr->valid != 1) return;
+  if (hdr->valid != 1) {
+    // no attention: the block statistics are not written either, so the block masses
+    // after this kernel must not run on them
+    if constexpr (ST)
+      if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) so.hdr->valid = 0;
+    return;
+  }
   const attn::Wg w = attn::wg_of(blockIdx.x, blockIdx.y, Hq, Hkv, HQ, TT, B, cu, po, tp);
   const int nst = w.nst;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5,
@@ -643,6 +718,9 @@ __global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
   const int qtok = attn::query_token(wv, l32);
+  WinStats ws;
+  if constexpr (ST) ws.init(so, w.i, w.L, w.g, wv.head, Hq, Hkv, wact, attn::query_token(wv, 31),
+                            qtok);
 
   // S^T of half-step hs (keys [32 hs, 32 hs + 32): stage hs / 2, row tile hs % 2).
   auto s_mfma = [&](int hs, f32x16& acc) {
@@ -674,6 +752,7 @@ __global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
         const float rn = fmaxf(Rs, mx);
         const float sc = __builtin_amdgcn_exp2f(Rs - rn);
         lsum *= sc;
+        if constexpr (ST) ws.bsum *= sc;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) O[dt] *= sc;
         Rs = rn;
@@ -704,6 +783,7 @@ __global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
       s1 += p[e + 1];
     }
     lsum += s0 + s1;
+    if constexpr (ST) ws.bsum += s0 + s1;
     const bf16x8 pb[2] = {__builtin_convertvector(p.lo, bf16x8),
                           __builtin_convertvector(p.hi, bf16x8)};
 #pragma unroll
@@ -745,15 +825,18 @@ __global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
       const bool skip = bound_ok(hs + 1);
       s_mfma(hs + 1, nxt);
       pv(hs, cur);
+      if constexpr (ST) ws.flush(hs, last_hs, Rs, half);
       if (!skip) rebase(nxt, false);
     } else if (hs + 1 <= last_hs) {   // next half-step is in the diagonal stage
       const bool skip = bound_ok(hs + 1);
       s_mfma(hs + 1, nxt);
       pv(hs, cur);
+      if constexpr (ST) ws.flush(hs, last_hs, Rs, half);
       mask(hs + 1, nxt);
       if (!skip) rebase(nxt, false);
     } else {
       pv(hs, cur);
+      if constexpr (ST) ws.flush(hs, last_hs, Rs, half);
     }
   };
   for (int st = 0; st < nst; ++st) {
@@ -763,7 +846,8 @@ __global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
   }
 
   if (!wact) return;
-  const float inv = 1.f / pair_sum(lsum);
+  const float lt = pair_sum(lsum), inv = 1.f / lt;
+  if constexpr (ST) ws.finish(last_hs, Rs, lt, half);
   if (qtok >= w.L) return;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -865,8 +949,34 @@ hipError_t launch_rope_layout(const void* q, const void* k, const void* v, const
   return hipGetLastError();
 }
 
+template <bool ST>
+static void launch_attention_kernels(const AttnShape& s, dim3 grid, hipStream_t st,
+                                     const uint16_t* qr, const uint16_t* kr, const uint16_t* vt,
+                                     const WsHeader* hdr, const int32_t* cu, const int32_t* po,
+                                     const int32_t* tp, const float* kn, float c, uint16_t* o,
+                                     const AttnScoreOut& so) {
+  if (attn_w8(s.d, s.Hkv)) {
+    if (s.d == 64)
+      hipLaunchKernelGGL((up_attention_w8_kernel<64, ST>), grid, dim3(512), 0, st, qr, kr, vt,
+                         hdr, cu, po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so);
+    else
+      hipLaunchKernelGGL((up_attention_w8_kernel<128, ST>), grid, dim3(512), 0, st, qr, kr, vt,
+                         hdr, cu, po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so);
+    return;
+  }
+  if (s.d == 64)
+    hipLaunchKernelGGL((up_attention_kernel<64, ST>), grid, dim3(256), 0, st, qr, kr, vt, hdr,
+                       cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so);
+  else if (s.d == 128)
+    hipLaunchKernelGGL((up_attention_kernel<128, ST>), grid, dim3(256), 0, st, qr, kr, vt, hdr,
+                       cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so);
+  else
+    hipLaunchKernelGGL((up_attention_kernel<256, ST>), grid, dim3(256), 0, st, qr, kr, vt, hdr,
+                       cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so);
+}
+
 hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
-                            float c, void* out, hipStream_t st) {
+                            float c, void* out, hipStream_t st, const AttnScoreOut* so) {
   char* w = static_cast<char*>(ws);
   const auto* hdr = reinterpret_cast<const WsHeader*>(w + L.hdr);
   const auto* po = reinterpret_cast<const int32_t*>(w + L.po);
@@ -874,27 +984,14 @@ hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, con
   const auto* qr = reinterpret_cast<const uint16_t*>(w + L.qr);
   const auto* kr = reinterpret_cast<const uint16_t*>(w + L.kr);
   const auto* vt = reinterpret_cast<const uint16_t*>(w + L.vt);
+  const auto* kn = attn_w8(s.d, s.Hkv) ? reinterpret_cast<const float*>(w + L.kn) : nullptr;
   const dim3 grid((unsigned)(s.Hkv * (s.Hq / s.Hkv / s.HQ)), (unsigned)s.tiles);
   auto o = static_cast<uint16_t*>(out);
-  if (attn_w8(s.d, s.Hkv)) {
-    const auto* kn = reinterpret_cast<const float*>(w + L.kn);
-    if (s.d == 64)
-      hipLaunchKernelGGL(up_attention_w8_kernel<64>, grid, dim3(512), 0, st, qr, kr, vt, hdr, cu,
-                         po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
-    else
-      hipLaunchKernelGGL(up_attention_w8_kernel<128>, grid, dim3(512), 0, st, qr, kr, vt, hdr, cu,
-                         po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
-    return hipGetLastError();
-  }
-  if (s.d == 64)
-    hipLaunchKernelGGL(up_attention_kernel<64>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
-                       tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
-  else if (s.d == 128)
-    hipLaunchKernelGGL(up_attention_kernel<128>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
-                       tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+  if (so)
+    launch_attention_kernels<true>(s, grid, st, qr, kr, vt, hdr, cu, po, tp, kn, c, o, *so);
   else
-    hipLaunchKernelGGL(up_attention_kernel<256>, grid, dim3(256), 0, st, qr, kr, vt, hdr, cu, po,
-                       tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o);
+    launch_attention_kernels<false>(s, grid, st, qr, kr, vt, hdr, cu, po, tp, kn, c, o,
+                                    AttnScoreOut{});
   return hipGetLastError();
 }
 

@@ -218,8 +218,22 @@ hipError_t launch_attn_plan(const int32_t* cu, const AttnShape& s, void* ws, con
 hipError_t launch_rope_layout(const void* q, const void* k, const void* v, const int32_t* pos,
                               const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
                               double log2_theta, hipStream_t st);
+// Block statistics of the window rows, written by the attention kernel when given
+// (the fused form of the block scores): per request the same (reference, block sum)
+// pairs [nb][Hkv][gs * W] and row statistics (row max, 1 / row sum) [W][Hq] that the
+// score pass leaves in its workspace, so the block masses and the normalisation run
+// on them unchanged.  hdr and plan are the score pass's plan.
+struct AttnScoreOut {
+  WsHeader* hdr;
+  const ReqPlan* plan;
+  float2* ml;
+  float2* rs;
+  float* row_lse;   // optional: natural-log log-sum-exp per window row, [sum W][Hq]
+  int G;
+};
 hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
-                            float c, void* out, hipStream_t st);
+                            float c, void* out, hipStream_t st,
+                            const AttnScoreOut* so = nullptr);
 hipError_t launch_swiglu(const void* gu, int64_t R, int F, void* a, hipStream_t st);
 
 }  // namespace up

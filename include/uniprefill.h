@@ -323,6 +323,40 @@ int up_rope_attention(const void* q, const void* k, const void* v, const int32_t
                       int Hkv, int d, float scale, float rope_theta, void* out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* The same attention, and the block scores of its window rows from the probabilities
+ * it computes anyway ([UP] "Triton kernels" paragraph: online softmax and block
+ * reduction in the GPU pipeline; "drop" paragraph: the scoring happens at the
+ * full-attention layer, whose attention already runs that softmax).  Per request the
+ * window is its last W = min(n, L) rows; for every window row and query head the
+ * attention kernel keeps, beside its softmax, the sum of the probabilities of each
+ * block of G keys and stores it with the softmax reference it was taken against,
+ * then the row's own maximum and sum; the block masses and the normalisation follow
+ * as in up_block_scores.  So
+ *   scores[blk_off(i) + b] = (sum over window rows w and query heads h of
+ *       P_{w,h}(block b)) / (the same sum over all blocks of request i),
+ * P_{w,h}(block b) the softmax probability mass that window row w of head h puts on
+ * the keys of block b, computed from the rotated bf16 operands q', k' of the
+ * attention (the scores up_block_scores gives for window queries q'[last W rows]
+ * and keys k').  out is exactly up_rope_attention's output.
+ * q, k, v, pos, cu_seqlens, cu_seqlens_h, d, scale, rope_theta, out: as up_rope_attention
+ * (scale also scales the scores' logits).
+ * n >= 1 window rows, G block size (a multiple of 32 in [32, 1024], else UP_EUNSUPPORTED).
+ * scores  : float32 [sum_i ceil(L_i / G)], blocks of request i from blk_off(i) = sum of
+ *           the earlier requests' block counts (as up_block_scores).
+ * row_lse : optional float32 [sum_i W_i, Hq] natural-log log-sum-exp of each window
+ *           row's scaled logits (NULL to skip).
+ * workspace : at least up_rope_attention_scores_workspace(...) bytes, 256-byte aligned.
+ * Errors: as up_rope_attention and up_block_scores; when either plan finds the device
+ * cu_seqlens inconsistent, error bit 1 is raised and the scores are not written. */
+size_t up_rope_attention_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv,
+                                          int d, int n, int G);
+
+int up_rope_attention_scores(const void* q, const void* k, const void* v, const int32_t* pos,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B,
+                             int Hq, int Hkv, int d, float scale, float rope_theta, int n, int G,
+                             void* out, float* scores, float* row_lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* SwiGLU gate: a[r, j] = silu(gu[r, j]) * gu[r, F + j], float32 math, bf16 result.
  * gu : bf16 [R, 2F] (gate columns first);  a : bf16 [R, F];  F % 8 == 0. */
 int up_swiglu(const void* gu, int64_t R, int F, void* a, void* stream);

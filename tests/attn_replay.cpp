@@ -2,7 +2,7 @@
 // consumer.hip, up_attention_w8_kernel), built with g++ against the same index
 // functions the kernel calls (attn_geom.h).  No GPU code runs here.
 //
-//   attn_replay D Hq Hkv L0,L1,...
+//   attn_replay D Hq Hkv L0,L1,... [n G]
 //
 // Part 1 (per head dimension, every lane): the global-to-LDS copies of a stage fill
 // the stage's K and V^T tiles exactly once, inside the stage; every K operand read
@@ -16,6 +16,12 @@
 // the mask leaving exactly the causal keys; and every global access (K and V^T copies,
 // query loads, key-norm entries, output stores) inside its buffer and inside the
 // request's padded rows; every output element of every real row written once.
+// Part 3 (with n and G): the window-row block statistics the kernels store when asked
+// (up_rope_attention_scores): for every window row and query head, with the wave's
+// half-steps as either kernel runs them (64-token tiles of two 32-key half-steps in the
+// 8-wave kernel, 32-token tiles in the 4-wave kernel), every block of the request gets
+// exactly one (reference, sum) pair, inside the request's pairs, and the row's
+// statistics and log-sum-exp land inside their arrays.
 // Prints "ok" and exits 0, or prints the first violation and exits 1.
 #include <cstdint>
 #include <cstdio>
@@ -300,11 +306,66 @@ void part2(int Hq, int Hkv, const std::vector<int>& lens) {
               D, Hq, Hkv, B, (long long)R, (long long)Rp, (long long)tiles, gx, (long long)tiles);
 }
 
+void part3(int Hq, int Hkv, const std::vector<int>& lens, int n, int G, int tile_tokens) {
+  const int B = (int)lens.size();
+  const int gs = Hq / Hkv;
+  CHECK(G >= 32 && G % 32 == 0 && n > 0, G, n);
+  // The score plan's layout: per request nb = ceil(L / G), W = min(n, L), pairs
+  // [nb][Hq W] from ml_off, rows [W][Hq] from win_off Hq.
+  int64_t ml_off = 0, win_off = 0;
+  for (int i = 0; i < B; ++i) {
+    const int L = lens[i];
+    const int W = L < n ? L : n;
+    const int nb = (L + G - 1) / G;
+    const int64_t terms = (int64_t)Hq * W;
+    std::vector<uint8_t> seen((size_t)(nb * terms), 0), rows((size_t)terms, 0);
+    for (int head = 0; head < Hq; ++head) {
+      const int g = head / gs;
+      for (int wr = 0; wr < W; ++wr) {
+        const int qtok = L - W + wr;
+        const int tw = qtok / tile_tokens;
+        const int last = (tw + 1) * (tile_tokens / 32) - 1;   // the wave's last half-step
+        const int64_t e = up::attn::win_term(g, gs, W, wr, head);
+        CHECK(e >= 0 && e < terms, i, head, wr);
+        CHECK(rows[(size_t)e] == 0, i, head, wr);
+        rows[(size_t)e] = 1;
+        // the wave reaches every key the row may see
+        CHECK((int64_t)(last + 1) * 32 > qtok, i, qtok, last);
+        for (int hs = 0; hs <= last; ++hs) {
+          if (!up::attn::stats_flush(hs, last, G)) continue;
+          const int b = up::attn::stats_block(hs, G);
+          if (b >= nb) {
+            CHECK((int64_t)hs * 32 >= L, i, hs, b);   // only half-steps past the last key
+            continue;
+          }
+          uint8_t& c = seen[(size_t)(b * terms + e)];
+          CHECK(c == 0, i, b, e);
+          c = 1;
+        }
+        for (int b = up::attn::stats_tail_first(last, G); b < nb; ++b) {
+          CHECK((int64_t)b * G > qtok, i, b, qtok);   // wholly after the row: no key it sees
+          uint8_t& c = seen[(size_t)(b * terms + e)];
+          CHECK(c == 0, i, b, e);
+          c = 1;
+        }
+        const int64_t lse = (win_off + wr) * Hq + head;
+        CHECK(lse >= win_off * Hq && lse < (win_off + W) * Hq, i, wr, head);
+      }
+    }
+    for (size_t x = 0; x < seen.size(); ++x) CHECK(seen[x] == 1, i, (long long)x);
+    for (size_t x = 0; x < rows.size(); ++x) CHECK(rows[x] == 1, i, (long long)x);
+    ml_off += nb * terms;
+    win_off += W;
+  }
+  std::printf("statistics tile=%d Hq=%d Hkv=%d B=%d n=%d G=%d pairs=%lld: ok\n", tile_tokens, Hq,
+              Hkv, B, n, G, (long long)ml_off);
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
-  if (argc != 5) {
-    std::printf("usage: attn_replay D Hq Hkv L0,L1,...\n");
+  if (argc != 5 && argc != 7) {
+    std::printf("usage: attn_replay D Hq Hkv L0,L1,... [n G]\n");
     return 2;
   }
   const int D = std::atoi(argv[1]), Hq = std::atoi(argv[2]), Hkv = std::atoi(argv[3]);
@@ -317,13 +378,18 @@ int main(int argc, char** argv) {
     if (q == std::string::npos) break;
     p = q + 1;
   }
+  if (argc == 7) {
+    const int n = std::atoi(argv[5]), G = std::atoi(argv[6]);
+    // the 8-wave kernel's 64-token tiles (d = 64, 128) and the 4-wave kernel's 32
+    part3(Hq, Hkv, lens, n, G, up::attn::w8_serves(D, Hkv) ? 64 : 32);
+  }
   if (D == 64) {
     part1<64>();
     part2<64>(Hq, Hkv, lens);
   } else if (D == 128) {
     part1<128>();
     part2<128>(Hq, Hkv, lens);
-  } else {
+  } else if (argc != 7) {
     std::printf("the 8-wave kernel serves d = 64 and 128\n");
     return 2;
   }

@@ -375,3 +375,34 @@ def test_rope_attention_rejects_more_than_65535_tiles(L):
     d = ctypes.c_void_p(4096)
     cu = _cu([64 * 65535 + 1])
     assert a(d, d, d, d, d, _p(cu), 1, 8, 2, 128, 0.0, 500000.0, d, None, 0, None) == UP_EUNSUPPORTED
+
+
+def test_rope_attention_scores_sizes_and_rejections(L):
+    """up_rope_attention_scores: the workspace holds the attention's and the score
+    pass's; unsupported block sizes and head dimensions, a missing scores pointer and a
+    short workspace are refused before any launch."""
+    f = L.up_rope_attention_scores_workspace
+    f.restype = ctypes.c_size_t
+    cu = _cu([131072])
+    att = L.up_rope_attention_workspace
+    att.restype = ctypes.c_size_t
+    sw = L.up_block_scores_workspace(_p(cu), 1, 32, 8, 128, 128, 64)
+    assert f(_p(cu), 1, 32, 8, 128, 128, 64) >= att(_p(cu), 1, 32, 8, 128) + sw
+    assert f(_p(cu), 1, 32, 8, 128, 128, 48) == 0      # G not a multiple of 32
+    assert f(_p(cu), 1, 32, 8, 96, 128, 64) == 0       # d unsupported
+    assert f(_p(cu), 1, 32, 8, 128, 0, 64) == 0        # n = 0
+    a = L.up_rope_attention_scores
+    a.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_float] * 2 + \
+                 [ctypes.c_int] * 2 + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]
+    c4 = _cu([4096])
+
+    def call(n=128, G=64, scores=FAKE, ws=FAKE, wsb=1 << 40, d=128):
+        return a(FAKE, FAKE, FAKE, FAKE, FAKE, _p(c4), 1, 8, 2, d, 0.0, 500000.0, n, G, FAKE,
+                 scores, None, ws, ctypes.c_size_t(wsb), None)
+
+    assert call(n=0) == UP_EINVAL
+    assert call(G=48) == UP_EUNSUPPORTED
+    assert call(d=80) == UP_EUNSUPPORTED
+    assert call(scores=None) == UP_EINVAL
+    assert call(wsb=16) == UP_EWORKSPACE
+    assert call(ws=None) == UP_EWORKSPACE

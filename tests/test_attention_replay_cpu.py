@@ -32,9 +32,11 @@ def replay(tmp_path_factory):
     return exe
 
 
-def _run(exe, d, Hq, Hkv, lengths):
-    r = subprocess.run([exe, str(d), str(Hq), str(Hkv), ",".join(str(x) for x in lengths)],
-                       capture_output=True, text=True, timeout=300)
+def _run(exe, d, Hq, Hkv, lengths, n=None, G=None):
+    args = [exe, str(d), str(Hq), str(Hkv), ",".join(str(x) for x in lengths)]
+    if n is not None:
+        args += [str(n), str(G)]
+    r = subprocess.run(args, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
 
 
@@ -79,3 +81,17 @@ def test_replay_of_many_small_requests(replay):
         lengths[int(j)] = 0
     _run(replay, 64, 8, 2, lengths)
     _run(replay, 128, 12, 4, lengths)
+
+
+def test_replay_of_the_window_statistics(replay):
+    """The block statistics of up_rope_attention_scores: every (window row, block) pair
+    written once, inside the request's pairs, for both kernels' tilings and every block
+    size the GPU tests use (and the 128K decision's shape)."""
+    from tests import test_gpu_attention_scores as T
+    for lengths, Hq, Hkv, d, n, G, _ in T.CASES:
+        _run(replay, d, Hq, Hkv, lengths, n, G)
+    _run(replay, 128, 32, 8, [32768], 128, 64)
+    _run(replay, 128, 32, 8, [131072], 128, 64)
+    for G in (32, 96, 160, 1024):
+        _run(replay, 64, 8, 2, [980, 1, 63, 64, 65, 4000], 128, G)
+        _run(replay, 256, 16, 8, [980, 1, 63, 64, 65, 4000], 100, G)
