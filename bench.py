@@ -369,11 +369,90 @@ def consumer_leg(up, torch, dec, hid, b, cfg, reps=2):
                      "attention_frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "gemm_tflops": round(gemm_flops / (kt["gemm"] * 1e-6) / 1e12, 1)}
         log(f"[bench] consumer {name}: {R} rows, {ms:.2f} ms/layer, attention {att_tf:.0f} TFLOP/s")
+    out["scores_in_attention"] = scores_in_attention_leg(up, torch, buf, b, pos_all, cu_all,
+                                                         cu_all_h, ws_att, reps)
     out["time_ratio"] = round(out["survivors"]["ms"] / out["all_tokens"]["ms"], 4)
     out["rho"] = round(kept / N, 4)
     out["note"] = ("one decoder layer (projections, rotary attention at the carried positions, "
                    "SwiGLU FFN width %d) with random weights; not the headline" % F)
     return out
+
+
+def scores_in_attention_leg(up, torch, buf, b, pos_all, cu_all, cu_all_h, ws_att, reps):
+    """The full-attention layer's attention on every token, alone and with the block
+    scores of its window rows taken inside it (up_rope_attention_scores), against the
+    separate score pass over the same q and k (up_block_scores); per-kernel HIP events,
+    microseconds per call."""
+    Hq, Hkv, d, n, G = b.Hq, b.Hkv, b.d, b.n, b.G
+    R = b.T
+    dev = buf["q"].device
+    q = buf["q"][:R].view(R, Hq, d)
+    k_ = buf["k"][:R].view(R, Hkv, d)
+    v = buf["v"][:R].view(R, Hkv, d)
+    att = buf["att"][:R].view(R, Hq, d)
+    nb = int(sum((int(L) + G - 1) // G for L in np.diff(cu_all_h)))
+    sc = torch.empty(nb, dtype=torch.float32, device=dev)
+    ws_as = torch.empty(up.rope_attention_scores_workspace_bytes(cu_all_h, Hq, Hkv, d, n, G),
+                        dtype=torch.uint8, device=dev)
+    win = np.concatenate([np.arange(max(int(cu_all_h[i + 1]) - n, int(cu_all_h[i])),
+                                    int(cu_all_h[i + 1]))
+                          for i in range(len(cu_all_h) - 1)])
+    qwin = q[torch.from_numpy(win).to(dev)].contiguous()
+    ws_bs = torch.empty(up.block_scores_workspace_bytes(cu_all_h, Hq, Hkv, d, n, G),
+                        dtype=torch.uint8, device=dev)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, names):
+        """(microseconds per whole call on the caller's stream, per-kernel averages)."""
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        call_us = e0.elapsed_time(e1) * 1e3 / reps
+        up.profile_reset()
+        up.profile_enable(True)
+        fn()
+        torch.cuda.synchronize()
+        up.profile_enable(False)
+        res = {}
+        for nm in names:
+            cnt, ms = up.profile_read(nm)
+            if cnt:
+                res[nm] = round(ms * 1e3 / cnt, 2)
+        up.profile_reset()
+        assert up.device_error() == 0
+        return call_us, res
+
+    def plain_call():
+        up.rope_attention(q, k_, v, pos_all, cu_all, cu_all_h, out=att, workspace=ws_att)
+
+    def fused_call():
+        up.rope_attention_scores(q, k_, v, pos_all, cu_all, cu_all_h, n, G, out=att, scores=sc,
+                                 workspace=ws_as)
+
+    plain_names = ("attn_plan", "rope_layout", "attention")
+    fused_names = ("score_plan", "attn_plan", "rope_layout", "attention", "attention_window",
+                   "block_mass", "normalize")
+    runs = [(timed(plain_call, plain_names), timed(fused_call, fused_names)) for _ in range(2)]
+    plain_us, plain = min((r[0] for r in runs), key=lambda x: x[0])   # alternated, best of two
+    fused_us, fused = min((r[1] for r in runs), key=lambda x: x[0])
+    sep_us, sep = timed(lambda: up.block_scores(qwin, k_, cu_all, cu_all_h, n, G, out=sc,
+                                                workspace=ws_bs),
+                        ("score_plan", "score_partial", "row_stats", "block_mass", "normalize"))
+    return {"attention_call_us": round(plain_us, 1), "attention_with_scores_call_us":
+            round(fused_us, 1), "extra_us": round(fused_us - plain_us, 1),
+            "separate_score_pass_call_us": round(sep_us, 1),
+            "kernels_us": {"attention": plain, "attention_with_scores": fused,
+                           "separate_score_pass": sep},
+            "note": "block scores of the window rows taken inside the layer's attention on "
+                    "every token (the window tiles on a second stream beside the others): "
+                    "extra_us is what the scores add to the attention call; the separate "
+                    "pass re-reads K and recomputes the window's Q K^T"}
 
 
 def synth_positions(cu_h):
@@ -704,29 +783,41 @@ def graph_leg(up, torch, dec_big, args, T_big, reps=50):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             dec.run()
+        g10 = torch.cuda.CUDAGraph()   # ten decisions in one graph
+        with torch.cuda.graph(g10):
+            for _ in range(10):
+                dec.run()
         torch.cuda.synchronize()
+        n10 = max(n // 10, 1)
         res = {}
-        for mode in ("eager", "graph", "eager", "graph"):
+        for mode in ("eager", "graph", "graph10", "eager", "graph", "graph10"):
             stream = torch.cuda.current_stream()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             e0.record(stream)
-            for _ in range(n):
-                g.replay() if mode == "graph" else dec.run()
+            if mode == "graph10":
+                for _ in range(n10):
+                    g10.replay()
+            else:
+                for _ in range(n):
+                    g.replay() if mode == "graph" else dec.run()
             e1.record(stream)
             torch.cuda.synchronize()
-            wall = (time.perf_counter() - t0) * 1e3 / n
-            res.setdefault(mode, []).append((e0.elapsed_time(e1) / n, wall))
+            k = 10 * n10 if mode == "graph10" else n
+            wall = (time.perf_counter() - t0) * 1e3 / k
+            res.setdefault(mode, []).append((e0.elapsed_time(e1) / k, wall))
         assert up.device_error() == 0
         same = bool(torch.equal(dec.keep, want_keep))
         out[name] = {"tokens": T, "decisions": n,
                      "eager_ms": round(min(x[0] for x in res["eager"]), 4),
                      "graph_ms": round(min(x[0] for x in res["graph"]), 4),
+                     "graph10_ms": round(min(x[0] for x in res["graph10"]), 4),
                      "eager_wall_ms": round(min(x[1] for x in res["eager"]), 4),
                      "graph_wall_ms": round(min(x[1] for x in res["graph"]), 4),
                      "same_keep": same}
-    out["note"] = ("one decision per graph, replayed back to back; best of two rounds; "
+    out["note"] = ("graph: one decision per graph, replayed back to back; graph10: ten "
+                   "decisions per graph (per-decision time); best of two rounds; "
                    "not the headline")
     return out
 

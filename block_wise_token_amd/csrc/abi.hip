@@ -610,8 +610,9 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
 
 namespace {
 // Shape of an attention call; returns UP_OK or an error status.
-int plan_attention(const int32_t* cu_h, int B, int Hq, int Hkv, int d, AttnShape* s) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return UP_EINVAL;
+int plan_attention(const int32_t* cu_h, int B, int Hq, int Hkv, int d, AttnShape* s,
+                   int n = 0) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0 || n < 0) return UP_EINVAL;
   if (!cu_ok(cu_h, B)) return UP_EINVAL;
   if (d != 64 && d != 128 && d != 256) return UP_EUNSUPPORTED;
   const int gsz = Hq / Hkv;
@@ -619,12 +620,16 @@ int plan_attention(const int32_t* cu_h, int B, int Hq, int Hkv, int d, AttnShape
   s->HQ = gsz % 4 == 0 ? 4 : (gsz % 2 == 0 ? 2 : 1);
   s->TT = 4 / s->HQ;
   const int tok_tile = attn_tile_tokens(d, Hkv) * s->TT;
-  int64_t Rp = 0, tiles = 0;
+  int64_t Rp = 0, tiles = 0, wtiles = 0;
   for (int i = 0; i < B; ++i) {
     const int64_t L = (int64_t)cu_h[i + 1] - cu_h[i];
+    const int64_t nt = (L + tok_tile - 1) / tok_tile;
     Rp += (L + 63) / 64 * 64;
-    tiles += (L + tok_tile - 1) / tok_tile;
+    tiles += nt;
+    if (n > 0 && L > 0) wtiles += nt - (L - std::min<int64_t>(L, n)) / tok_tile;
   }
+  s->n = n;
+  s->wtiles = wtiles;
   s->R = B > 0 ? cu_h[B] : 0;
   s->Rp = Rp;
   s->tiles = tiles;
@@ -671,12 +676,44 @@ int up_rope_attention(const void* q, const void* k, const void* v, const int32_t
   return e == hipSuccess ? UP_OK : UP_EHIP;
 }
 
+// A second stream per device for the statistics launch of up_rope_attention_scores,
+// forked from and joined back into the caller's stream with events; created at the
+// first such call on the device and kept until the process ends.  The fork and join
+// are enqueued under a lock, so calls from several host threads stay ordered.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+SideStream* side_stream_locked() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    hipStream_t s = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+      if (a) (void)hipEventDestroy(a);
+      (void)hipStreamDestroy(s);
+      return nullptr;
+    }
+    ss.s = s;
+    ss.fork = a;
+    ss.join = b;
+  }
+  return &ss;
+}
+
 size_t up_rope_attention_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv,
                                           int d, int n, int G) {
   AttnShape a;
   ScoreShape s;
   Totals t;
-  if (plan_attention(cu_seqlens_h, B, Hq, Hkv, d, &a) != UP_OK) return 0;
+  if (plan_attention(cu_seqlens_h, B, Hq, Hkv, d, &a, n) != UP_OK) return 0;
   if (plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t) != UP_OK) return 0;
   return align_up(attn_ws_layout(B, Hq, Hkv, d, a.Rp).total) + score_ws_layout(B, t).total;
 }
@@ -687,7 +724,7 @@ int up_rope_attention_scores(const void* q, const void* k, const void* v, const 
                              void* out, float* scores, float* row_lse, void* workspace,
                              size_t workspace_bytes, void* stream) {
   AttnShape a;
-  int st = plan_attention(cu_seqlens_h, B, Hq, Hkv, d, &a);
+  int st = plan_attention(cu_seqlens_h, B, Hq, Hkv, d, &a, n);
   if (st != UP_OK) return st;
   ScoreShape s;
   Totals t;
@@ -725,8 +762,29 @@ int up_rope_attention_scores(const void* q, const void* k, const void* v, const 
                         reinterpret_cast<const ReqPlan*>(sws + LS.plan),
                         reinterpret_cast<float2*>(sws + LS.ml),
                         reinterpret_cast<float2*>(sws + LS.rs), row_lse, G};
-  e = timed(14, hs, [&] { return launch_attention(cu_seqlens, a, workspace, LA, c, out, hs, &so); });
-  if (e != hipSuccess) return UP_EHIP;
+  // The tiles that hold window rows run the attention with block statistics on a second
+  // stream, beside the plain attention over the other tiles on the caller's stream.
+  {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SideStream* ss = side_stream_locked();
+    if (!ss) return UP_EHIP;
+    if (hipEventRecord(ss->fork, hs) != hipSuccess ||
+        hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+      return UP_EHIP;
+    e = timed(18, ss->s, [&] {
+      return launch_attention(cu_seqlens, a, workspace, LA, c, out, ss->s, &so,
+                              attn::kSlotsWindow);
+    });
+    if (e != hipSuccess) return UP_EHIP;
+    e = timed(14, hs, [&] {
+      return launch_attention(cu_seqlens, a, workspace, LA, c, out, hs, nullptr,
+                              attn::kSlotsRest);
+    });
+    if (e != hipSuccess) return UP_EHIP;
+    if (hipEventRecord(ss->join, ss->s) != hipSuccess ||
+        hipStreamWaitEvent(hs, ss->join, 0) != hipSuccess)
+      return UP_EHIP;
+  }
   e = timed(2, hs, [&] { return launch_block_mass(s, t, sws, LS, hs); });
   if (e != hipSuccess) return UP_EHIP;
   e = timed(3, hs, [&] { return launch_normalize(s, t, sws, LS, scores, hs); });

@@ -103,21 +103,52 @@ struct W8 {
   }
 };
 
+// Launch layouts of the tile slots (blockIdx.y).  A request's slots are its workgroup
+// tiles, heaviest (last) first; tp is the prefix of the requests' slot counts.  With
+// window block statistics, the first k_i slots of request i hold its window rows (wp is
+// the prefix of k_i): one launch takes those (kSlotsWindow) and another the rest
+// (kSlotsRest); kSlotsAll takes every slot.
+constexpr int kSlotsAll = 0, kSlotsWindow = 1, kSlotsRest = 2;
+
+// Slot by of a launch in the given layout -> request i and slot j of the request.
+UP_HD void slot_of(int mode, int by, int B, const int32_t* tp, const int32_t* wp, int& i,
+                   int& j) {
+  if (mode == kSlotsAll) {
+    i = request_of(tp, B, by);
+    j = by - tp[i];
+  } else if (mode == kSlotsWindow) {
+    i = request_of(wp, B, by);
+    j = by - wp[i];
+  } else {
+    // the rest: request i's slots start at tp[i] - wp[i] and skip its k_i window slots
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tp[mid] - wp[mid] <= by) lo = mid;
+      else hi = mid - 1;
+    }
+    i = lo;
+    j = by - (tp[i] - wp[i]) + (wp[i + 1] - wp[i]);
+  }
+}
+
 // Workgroup (blockIdx.x = kv head x query-head quad, blockIdx.y = tile slot).
 struct Wg {
   int g, quad, i, L, wt, ntile, tile0, nst;
   int64_t pbase;
 };
 UP_HD Wg wg_of(int bx, int by, int Hq, int Hkv, int HQ, int TT, int B, const int32_t* cu,
-               const int32_t* po, const int32_t* tp) {
+               const int32_t* po, const int32_t* tp, int mode = kSlotsAll,
+               const int32_t* wp = nullptr) {
   Wg w;
   const int gsz = Hq / Hkv, quads = gsz / HQ;
   w.g = bx / quads;
   w.quad = bx - w.g * quads;
-  w.i = request_of(tp, B, by);
+  int j = 0;
+  slot_of(mode, by, B, tp, wp, w.i, j);
   w.L = cu[w.i + 1] - cu[w.i];
   const int nwt = tp[w.i + 1] - tp[w.i];
-  w.wt = nwt - 1 - (by - tp[w.i]);   // heaviest tile first
+  w.wt = nwt - 1 - j;   // heaviest tile first
   w.ntile = (w.L + 63) >> 6;         // 64-token tiles of the request
   w.tile0 = w.wt * TT;
   w.nst = w.tile0 + TT < w.ntile ? w.tile0 + TT : w.ntile;   // key stages of the workgroup

@@ -39,55 +39,68 @@ constexpr float kNegInf = -__builtin_inff();
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 
+// With n > 0 also the window slots: k_i = the tiles of request i that hold some of its
+// last W = min(n, L) rows (its first slots, heaviest first), wp = their prefix.
 __global__ __launch_bounds__(kPlanThreads) void up_attn_plan_kernel(
-    const int32_t* __restrict__ cu, int B, int tok_tile, int64_t R_h, int64_t Rp_h,
-    int64_t tiles_h, WsHeader* __restrict__ hdr, int32_t* __restrict__ po,
-    int32_t* __restrict__ tp, int* __restrict__ err) {
+    const int32_t* __restrict__ cu, int B, int tok_tile, int n, int64_t R_h, int64_t Rp_h,
+    int64_t tiles_h, int64_t wtiles_h, WsHeader* __restrict__ hdr, int32_t* __restrict__ po,
+    int32_t* __restrict__ tp, int32_t* __restrict__ wp, int* __restrict__ err) {
   constexpr int NWV = kPlanThreads / 64;
-  __shared__ uint64_t wsum[2][NWV];
+  __shared__ uint64_t wsum[3][NWV];
   __shared__ int bad;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) bad = 0;
   __syncthreads();
-  uint64_t carry_p = 0, carry_t = 0;
+  uint64_t carry_p = 0, carry_t = 0, carry_w = 0;
   for (int base = 0; base < B; base += kPlanThreads) {
     const int i = base + tid;
-    uint32_t lp = 0, nt = 0;
+    uint32_t lp = 0, nt = 0, nw = 0;
     if (i < B) {
       const int32_t a = cu[i], b = cu[i + 1];
       if (b < a || (i == 0 && a != 0)) bad = 1;
       const uint32_t L = b >= a ? (uint32_t)(b - a) : 0u;
       lp = (L + 63u) & ~63u;
       nt = (L + (uint32_t)tok_tile - 1u) / (uint32_t)tok_tile;
+      if (n > 0 && L > 0) {
+        const uint32_t W = L < (uint32_t)n ? L : (uint32_t)n;
+        nw = nt - (L - W) / (uint32_t)tok_tile;
+      }
     }
     const uint64_t sp = wave_scan_u64(lp), sn = wave_scan_u64(nt);   // inclusive
+    const uint64_t sw = wave_scan_u64(nw);
     if (lane == 63) {
       wsum[0][wave] = sp;
       wsum[1][wave] = sn;
+      wsum[2][wave] = sw;
     }
     __syncthreads();
-    uint64_t op = 0, on = 0, tot_p = 0, tot_n = 0;
+    uint64_t op = 0, on = 0, ow = 0, tot_p = 0, tot_n = 0, tot_w = 0;
     for (int w = 0; w < NWV; ++w) {
       if (w < wave) {
         op += wsum[0][w];
         on += wsum[1][w];
+        ow += wsum[2][w];
       }
       tot_p += wsum[0][w];
       tot_n += wsum[1][w];
+      tot_w += wsum[2][w];
     }
     if (i < B) {
       po[i] = (int32_t)(carry_p + op + sp - lp);
       tp[i] = (int32_t)(carry_t + on + sn - nt);
+      wp[i] = (int32_t)(carry_w + ow + sw - nw);
     }
     carry_p += tot_p;
     carry_t += tot_n;
+    carry_w += tot_w;
     __syncthreads();
   }
   if (tid == 0) {
     po[B] = (int32_t)carry_p;
     tp[B] = (int32_t)carry_t;
+    wp[B] = (int32_t)carry_w;
     const bool ok = !bad && (B == 0 || (int64_t)cu[B] == R_h) && (int64_t)carry_p == Rp_h &&
-                    (int64_t)carry_t == tiles_h;
+                    (int64_t)carry_t == tiles_h && (int64_t)carry_w == wtiles_h;
     hdr->valid = ok ? 1 : 0;
     if (!ok) atomicOr(err, 1);
   }
@@ -340,13 +353,16 @@ struct WinStats {
   float* lsep = nullptr;
   int64_t terms = 0;
   int nb = 0, G = 64;
+  int pend = 0;   // statistics stores since the newest stage copies (wave-uniform)
 
+  // The wave's rows are the tokens [first_row_tok, first_row_tok + 32); it keeps
+  // statistics when one of them is a window row, so every flush has lanes that store.
   __device__ __forceinline__ void init(const AttnScoreOut& so, int i, int L, int g, int head,
-                                       int Hq, int Hkv, bool wact, int last_row_tok, int qtok) {
+                                       int Hq, int Hkv, bool wact, int first_row_tok, int qtok) {
     if (!wact || so.hdr->valid != 1) return;
     const ReqPlan pr = so.plan[i];
     const int wfirst = L - pr.W;
-    wave = last_row_tok >= wfirst;
+    wave = first_row_tok + 31 >= wfirst && first_row_tok < L;
     if (!wave) return;
     const int gs = Hq / Hkv;
     row = qtok >= wfirst && qtok < L;
@@ -366,7 +382,12 @@ struct WinStats {
     if (!wave || !attn::stats_flush(hs, last, G)) return;
     const float tot = pair_sum(bsum);
     const int b = attn::stats_block(hs, G);
-    if (row && half == 0 && b < nb) pair0[(int64_t)b * terms] = make_float2(Rs, tot);
+    if (b < nb) {
+      // a window wave always has lanes with row && half == 0, so the store is issued
+      if (row && half == 0) pair0[(int64_t)b * terms] = make_float2(Rs, tot);
+      ++pend;
+      asm volatile("" ::: "memory");   // the store stays ahead of the next wait
+    }
     bsum = 0.f;
   }
   __device__ __forceinline__ void finish(int last, float Rs, float l, int half) {
@@ -388,7 +409,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
     const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
     const int32_t* __restrict__ tp, int B, int Hq, int Hkv, int HQ, int TT, int64_t Rp,
-    float c, uint16_t* __restrict__ out, AttnScoreOut so) {
+    float c, uint16_t* __restrict__ out, AttnScoreOut so, int mode,
+    const int32_t* __restrict__ wp) {
   constexpr int NT = 256, NS = 4, UK = 32;
   constexpr int DS = D / 16;             // MFMA k-steps over the head dimension
   constexpr int DT = D / 32;             // 32-row tiles of O^T
@@ -411,11 +433,11 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
   }
   const int gsz = Hq / Hkv, quads = gsz / HQ;
   const int g = blockIdx.x / quads, quad = blockIdx.x - g * quads;
-  const int f = blockIdx.y;
-  const int i = request_of(tp, B, f);
+  int i = 0, j = 0;
+  attn::slot_of(mode, blockIdx.y, B, tp, wp, i, j);
   const int L = cu[i + 1] - cu[i];
   const int nwt = tp[i + 1] - tp[i];
-  const int wt = nwt - 1 - (f - tp[i]);   // heaviest tile first
+  const int wt = nwt - 1 - j;             // heaviest tile first
   const int ntile = (L + 31) >> 5;        // 32-token tiles of the request
   const int tile0 = wt * TT;
   const int nst = min(tile0 + TT, ntile);   // 32-key stages of this workgroup
@@ -480,7 +502,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
   const int qtok = tw * 32 + l32;
   WinStats ws;
-  if constexpr (ST) ws.init(so, i, L, g, head, Hq, Hkv, wact, tw * 32 + 31, qtok);
+  if constexpr (ST) ws.init(so, i, L, g, head, Hq, Hkv, wact, tw * 32, qtok);
 
   // S^T of stage (= half-step) hs into acc.
   auto s_mfma = [&](int hs, f32x16& acc) {
@@ -557,9 +579,24 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
   // st-1 -- and refill that slot with stage st+3.
   auto sync_for = [&](int st) {
     if (st + 1 >= nst) return;
-    if (st + 2 < nst) wait_barrier<SPT>();
-    else wait_barrier<0>();
-    if (st + 3 < nst) issue(st + 3);
+    if (st + 2 < nst) {
+      // Stores share the vector-memory count with the stage copies and complete in issue
+      // order with them: the block-statistics stores issued since the newest copies are
+      // younger than them, so the wait leaves those stores and the newest stage in flight.
+      if constexpr (ST) {
+        if (ws.pend == 2) wait_barrier<SPT + 2>();
+        else if (ws.pend == 1) wait_barrier<SPT + 1>();
+        else wait_barrier<SPT>();
+      } else {
+        wait_barrier<SPT>();
+      }
+    } else {
+      wait_barrier<0>();
+    }
+    if (st + 3 < nst) {
+      issue(st + 3);
+      if constexpr (ST) ws.pend = 0;
+    }
   };
 
   issue(0);
@@ -641,7 +678,8 @@ __global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
     const uint16_t* __restrict__ vt, const WsHeader* __restrict__ hdr,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ po,
     const int32_t* __restrict__ tp, const float* __restrict__ kn, int B, int Hq, int Hkv,
-    int HQ, int TT, int64_t Rp, float c, uint16_t* __restrict__ out, AttnScoreOut so) {
+    int HQ, int TT, int64_t Rp, float c, uint16_t* __restrict__ out, AttnScoreOut so, int mode,
+    const int32_t* __restrict__ wp) {
   using G = attn::W8<D>;
   constexpr int NS = G::NS, DS = G::DS, DT = G::DT, SB = G::SB, SPT = G::SPT;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
@@ -653,7 +691,8 @@ __global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
       if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) so.hdr->valid = 0;
     return;
   }
-  const attn::Wg w = attn::wg_of(blockIdx.x, blockIdx.y, Hq, Hkv, HQ, TT, B, cu, po, tp);
+  const attn::Wg w = attn::wg_of(blockIdx.x, blockIdx.y, Hq, Hkv, HQ, TT, B, cu, po, tp, mode,
+                                 wp);
   const int nst = w.nst;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5,
             l32 = lane & 31;
@@ -719,7 +758,7 @@ __global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
   const int qtok = attn::query_token(wv, l32);
   WinStats ws;
-  if constexpr (ST) ws.init(so, w.i, w.L, w.g, wv.head, Hq, Hkv, wact, attn::query_token(wv, 31),
+  if constexpr (ST) ws.init(so, w.i, w.L, w.g, wv.head, Hq, Hkv, wact, attn::query_token(wv, 0),
                             qtok);
 
   // S^T of half-step hs (keys [32 hs, 32 hs + 32): stage hs / 2, row tile hs % 2).
@@ -799,9 +838,24 @@ __global__ __launch_bounds__(512, 1) void up_attention_w8_kernel(
   // first half; then stage st-1's slot is refilled with stage st+3.
   auto sync_for = [&](int st) {
     if (st + 1 >= nst) return;
-    if (st + 2 < nst) wait_barrier<SPT>();
-    else wait_barrier<0>();
-    if (st + 3 < nst) issue(st + 3);
+    if (st + 2 < nst) {
+      // Stores share the vector-memory count with the stage copies and complete in issue
+      // order with them: the block-statistics stores issued since the newest copies are
+      // younger than them, so the wait leaves those stores and the newest stage in flight.
+      if constexpr (ST) {
+        if (ws.pend == 2) wait_barrier<SPT + 2>();
+        else if (ws.pend == 1) wait_barrier<SPT + 1>();
+        else wait_barrier<SPT>();
+      } else {
+        wait_barrier<SPT>();
+      }
+    } else {
+      wait_barrier<0>();
+    }
+    if (st + 3 < nst) {
+      issue(st + 3);
+      if constexpr (ST) ws.pend = 0;
+    }
   };
 
   issue(0);
@@ -900,6 +954,8 @@ AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp) {
   o += align_up(sizeof(int32_t) * (size_t)(B + 1));
   w.tp = o;
   o += align_up(sizeof(int32_t) * (size_t)(B + 1));
+  w.wp = o;
+  o += align_up(sizeof(int32_t) * (size_t)(B + 1));
   w.qr = o;
   o += align_up((size_t)Hq * Rp * d * 2);
   w.kr = o;
@@ -916,10 +972,10 @@ hipError_t launch_attn_plan(const int32_t* cu, const AttnShape& s, void* ws, con
                             int* err, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   hipLaunchKernelGGL(up_attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, cu, s.B,
-                     attn_tile_tokens(s.d, s.Hkv) * s.TT,
-                     s.R, s.Rp, s.tiles, reinterpret_cast<WsHeader*>(w + L.hdr),
+                     attn_tile_tokens(s.d, s.Hkv) * s.TT, s.n, s.R, s.Rp, s.tiles, s.wtiles,
+                     reinterpret_cast<WsHeader*>(w + L.hdr),
                      reinterpret_cast<int32_t*>(w + L.po), reinterpret_cast<int32_t*>(w + L.tp),
-                     err);
+                     reinterpret_cast<int32_t*>(w + L.wp), err);
   return hipGetLastError();
 }
 
@@ -953,45 +1009,54 @@ template <bool ST>
 static void launch_attention_kernels(const AttnShape& s, dim3 grid, hipStream_t st,
                                      const uint16_t* qr, const uint16_t* kr, const uint16_t* vt,
                                      const WsHeader* hdr, const int32_t* cu, const int32_t* po,
-                                     const int32_t* tp, const float* kn, float c, uint16_t* o,
-                                     const AttnScoreOut& so) {
+                                     const int32_t* tp, const int32_t* wp, const float* kn,
+                                     float c, uint16_t* o, const AttnScoreOut& so, int mode) {
   if (attn_w8(s.d, s.Hkv)) {
     if (s.d == 64)
       hipLaunchKernelGGL((up_attention_w8_kernel<64, ST>), grid, dim3(512), 0, st, qr, kr, vt,
-                         hdr, cu, po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so);
+                         hdr, cu, po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so, mode,
+                         wp);
     else
       hipLaunchKernelGGL((up_attention_w8_kernel<128, ST>), grid, dim3(512), 0, st, qr, kr, vt,
-                         hdr, cu, po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so);
+                         hdr, cu, po, tp, kn, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so, mode,
+                         wp);
     return;
   }
   if (s.d == 64)
     hipLaunchKernelGGL((up_attention_kernel<64, ST>), grid, dim3(256), 0, st, qr, kr, vt, hdr,
-                       cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so);
+                       cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so, mode, wp);
   else if (s.d == 128)
     hipLaunchKernelGGL((up_attention_kernel<128, ST>), grid, dim3(256), 0, st, qr, kr, vt, hdr,
-                       cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so);
+                       cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so, mode, wp);
   else
     hipLaunchKernelGGL((up_attention_kernel<256, ST>), grid, dim3(256), 0, st, qr, kr, vt, hdr,
-                       cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so);
+                       cu, po, tp, s.B, s.Hq, s.Hkv, s.HQ, s.TT, s.Rp, c, o, so, mode, wp);
 }
 
 hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
-                            float c, void* out, hipStream_t st, const AttnScoreOut* so) {
+                            float c, void* out, hipStream_t st, const AttnScoreOut* so,
+                            int mode) {
   char* w = static_cast<char*>(ws);
   const auto* hdr = reinterpret_cast<const WsHeader*>(w + L.hdr);
   const auto* po = reinterpret_cast<const int32_t*>(w + L.po);
   const auto* tp = reinterpret_cast<const int32_t*>(w + L.tp);
+  const auto* wp = reinterpret_cast<const int32_t*>(w + L.wp);
   const auto* qr = reinterpret_cast<const uint16_t*>(w + L.qr);
   const auto* kr = reinterpret_cast<const uint16_t*>(w + L.kr);
   const auto* vt = reinterpret_cast<const uint16_t*>(w + L.vt);
   const auto* kn = attn_w8(s.d, s.Hkv) ? reinterpret_cast<const float*>(w + L.kn) : nullptr;
-  const dim3 grid((unsigned)(s.Hkv * (s.Hq / s.Hkv / s.HQ)), (unsigned)s.tiles);
+  const int64_t slots = mode == attn::kSlotsAll      ? s.tiles
+                        : mode == attn::kSlotsWindow ? s.wtiles
+                                                     : s.tiles - s.wtiles;
+  if (slots == 0) return hipSuccess;
+  const dim3 grid((unsigned)(s.Hkv * (s.Hq / s.Hkv / s.HQ)), (unsigned)slots);
   auto o = static_cast<uint16_t*>(out);
   if (so)
-    launch_attention_kernels<true>(s, grid, st, qr, kr, vt, hdr, cu, po, tp, kn, c, o, *so);
+    launch_attention_kernels<true>(s, grid, st, qr, kr, vt, hdr, cu, po, tp, wp, kn, c, o, *so,
+                                   mode);
   else
-    launch_attention_kernels<false>(s, grid, st, qr, kr, vt, hdr, cu, po, tp, kn, c, o,
-                                    AttnScoreOut{});
+    launch_attention_kernels<false>(s, grid, st, qr, kr, vt, hdr, cu, po, tp, wp, kn, c, o,
+                                    AttnScoreOut{}, mode);
   return hipGetLastError();
 }
 

@@ -208,9 +208,11 @@ struct AttnShape {
   int HQ, TT;       // query heads and per-head token tiles per attention workgroup (HQ * TT = 4)
   int64_t R, Rp;    // rows; padded rows (every request rounded up to 64)
   int64_t tiles;    // attention workgroup tiles of attn_tile_tokens(d, Hkv) * TT tokens
+  int n;            // window rows whose block statistics are kept (0: none)
+  int64_t wtiles;   // workgroup tiles holding window rows (0 when n = 0)
 };
 struct AttnWs {
-  size_t hdr, po, tp, qr, kr, vt, kn, total;   // kn: 8-wave kernel only (else empty)
+  size_t hdr, po, tp, wp, qr, kr, vt, kn, total;   // kn: 8-wave kernel only (else empty)
 };
 AttnWs attn_ws_layout(int B, int Hq, int Hkv, int d, int64_t Rp);
 hipError_t launch_attn_plan(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
@@ -231,9 +233,11 @@ struct AttnScoreOut {
   float* row_lse;   // optional: natural-log log-sum-exp per window row, [sum W][Hq]
   int G;
 };
+// mode: attn::kSlotsAll, or kSlotsWindow (with so: the statistics kernel over the
+// window tiles) and kSlotsRest (the plain kernel over the others).
 hipError_t launch_attention(const int32_t* cu, const AttnShape& s, void* ws, const AttnWs& L,
                             float c, void* out, hipStream_t st,
-                            const AttnScoreOut* so = nullptr);
+                            const AttnScoreOut* so = nullptr, int mode = attn::kSlotsAll);
 hipError_t launch_swiglu(const void* gu, int64_t R, int F, void* a, hipStream_t st);
 
 }  // namespace up

@@ -337,7 +337,11 @@ int up_rope_attention(const void* q, const void* k, const void* v, const int32_t
  * P_{w,h}(block b) the softmax probability mass that window row w of head h puts on
  * the keys of block b, computed from the rotated bf16 operands q', k' of the
  * attention (the scores up_block_scores gives for window queries q'[last W rows]
- * and keys k').  out is exactly up_rope_attention's output.
+ * and keys k').  out is exactly up_rope_attention's output.  The workgroup tiles that
+ * hold window rows run a statistics-keeping instance of the attention kernel on a
+ * second stream of the library's (one per device, created at the first call and kept;
+ * it joins back into `stream` with events before the block masses), beside the plain
+ * kernel over the other tiles on `stream`.
  * q, k, v, pos, cu_seqlens, cu_seqlens_h, d, scale, rope_theta, out: as up_rope_attention
  * (scale also scales the scores' logits).
  * n >= 1 window rows, G block size (a multiple of 32 in [32, 1024], else UP_EUNSUPPORTED).
@@ -385,7 +389,9 @@ int up_device_error(int32_t* code_h, void* stream);
  * destinations, 7 gather, 8 compose, 9 plan, 10 given-lse score partials,
  * 11 given-lse finalise, 12 attention plan, 13 rotary layout, 14 attention,
  * 15 SwiGLU gate, 16 hipBLASLt GEMM, 17 select with normalisation and block
- * destinations inside up_layer_decision), the number of launches and their
+ * destinations inside up_layer_decision, 18 the attention over the window tiles with
+ * block statistics inside up_rope_attention_scores, timed on its second stream), the
+ * number of launches and their
  * summed duration in milliseconds; up_profile_reset() forgets them.
  * up_profile_enable(0) stops recording.  Not thread safe. */
 int up_profile_enable(int on);

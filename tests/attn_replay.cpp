@@ -306,6 +306,46 @@ void part2(int Hq, int Hkv, const std::vector<int>& lens) {
               D, Hq, Hkv, B, (long long)R, (long long)Rp, (long long)tiles, gx, (long long)tiles);
 }
 
+// Part 4 (with n): the two launches of up_rope_attention_scores.  For a workgroup tile
+// of tok_tile tokens, the window launch (slot layout kSlotsWindow) and the rest
+// (kSlotsRest) together cover every (request, slot) exactly once; the window launch
+// takes exactly the slots whose tokens reach the request's last W = min(n, L) rows.
+void part4(const std::vector<int>& lens, int n, int tok_tile) {
+  const int B = (int)lens.size();
+  std::vector<int32_t> tp(B + 1, 0), wp(B + 1, 0);
+  for (int i = 0; i < B; ++i) {
+    const int L = lens[i];
+    const int nt = (L + tok_tile - 1) / tok_tile;
+    const int W = L < n ? L : n;
+    const int nw = (n > 0 && L > 0) ? nt - (L - W) / tok_tile : 0;
+    tp[i + 1] = tp[i] + nt;
+    wp[i + 1] = wp[i] + nw;
+  }
+  const int64_t tiles = tp[B], wtiles = wp[B];
+  std::vector<uint8_t> seen((size_t)tiles, 0);
+  for (int mode : {up::attn::kSlotsWindow, up::attn::kSlotsRest}) {
+    const int64_t slots = mode == up::attn::kSlotsWindow ? wtiles : tiles - wtiles;
+    for (int by = 0; by < slots; ++by) {
+      int i = -1, j = -1;
+      up::attn::slot_of(mode, by, B, tp.data(), wp.data(), i, j);
+      CHECK(i >= 0 && i < B, mode, by, i);
+      const int nt = tp[i + 1] - tp[i];
+      CHECK(j >= 0 && j < nt, mode, by, j);
+      const int L = lens[i];
+      const int W = L < n ? L : n;
+      const int wt = nt - 1 - j;                    // the tile: tokens [wt tok, (wt+1) tok)
+      const bool window = (int64_t)(wt + 1) * tok_tile > L - W;
+      CHECK(window == (mode == up::attn::kSlotsWindow), mode, by, wt);
+      uint8_t& c = seen[(size_t)(tp[i] + j)];
+      CHECK(c == 0, mode, by, j);
+      c = 1;
+    }
+  }
+  for (size_t x = 0; x < seen.size(); ++x) CHECK(seen[x] == 1, (long long)x);
+  std::printf("slot layouts tile=%d B=%d n=%d tiles=%lld window=%lld: ok\n", tok_tile, B, n,
+              (long long)tiles, (long long)wtiles);
+}
+
 void part3(int Hq, int Hkv, const std::vector<int>& lens, int n, int G, int tile_tokens) {
   const int B = (int)lens.size();
   const int gs = Hq / Hkv;
@@ -381,7 +421,11 @@ int main(int argc, char** argv) {
   if (argc == 7) {
     const int n = std::atoi(argv[5]), G = std::atoi(argv[6]);
     // the 8-wave kernel's 64-token tiles (d = 64, 128) and the 4-wave kernel's 32
-    part3(Hq, Hkv, lens, n, G, up::attn::w8_serves(D, Hkv) ? 64 : 32);
+    const int tile = up::attn::w8_serves(D, Hkv) ? 64 : 32;
+    part3(Hq, Hkv, lens, n, G, tile);
+    const int gsz = Hq / Hkv;
+    const int HQ = gsz % 4 == 0 ? 4 : (gsz % 2 == 0 ? 2 : 1);
+    part4(lens, n, tile * (4 / HQ));
   }
   if (D == 64) {
     part1<64>();

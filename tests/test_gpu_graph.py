@@ -131,6 +131,41 @@ def test_rope_attention_replays_match_eager():
     say(f"[ok] rotary attention: {REPLAYS} replays equal the eager call")
 
 
+def test_rope_attention_scores_replays_match_eager():
+    """The attention with the window rows' block scores: its window tiles run on the
+    library's second stream, forked from and joined back into the captured stream with
+    events, so the graph holds both branches."""
+    lengths, Hq, Hkv, d, n, G = [300, 0, 65, 129], 8, 2, 128, 128, 64
+    say("[case] graph replay: rotary attention with block scores")
+    q, k, v, pos, cu = synth.gen_consumer_attention(lengths, Hq, Hkv, d, 8)
+    R = int(cu[-1])
+    args = (bf16_dev(q).view(R, Hq, d), bf16_dev(k).view(R, Hkv, d), bf16_dev(v).view(R, Hkv, d),
+            i32_dev(pos), i32_dev(cu), cu, n, G)
+    ws = torch.empty(up.rope_attention_scores_workspace_bytes(cu, Hq, Hkv, d, n, G),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((R, Hq, d), dtype=torch.bfloat16, device="cuda")
+    nb = sum((L + G - 1) // G for L in lengths)
+    sc = torch.empty(nb, dtype=torch.float32, device="cuda")
+
+    def run():
+        up.rope_attention_scores(*args, out=out, scores=sc, workspace=ws)
+    run()
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    want_out, want_sc = out.clone(), sc.clone()
+    g = _capture(run)
+    for r in range(REPLAYS):
+        out.fill_(0.5)
+        sc.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert up.device_error() == 0
+        assert torch.equal(out, want_out), f"replay {r}: out differs"
+        assert torch.equal(sc, want_sc), f"replay {r}: scores differ"
+    say(f"[ok] rotary attention with block scores: {REPLAYS} replays equal the eager call")
+
+
 def test_paged_score_passes_replay_match_eager():
     """Both paged score passes (row statistics computed, and given) in one graph, as a
     serving loop over a paged cache would capture them."""
