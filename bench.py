@@ -265,11 +265,23 @@ def main():
     # The layer that then runs on the survivors (scope: next), against the same layer on
     # every token.
     if not args.headline_only and b.d in (64, 128, 256):
-        result["consumer"] = consumer_leg(up, torch, dec, hid, b, cfg)
+        F = ffn_width(cfg["H"])
+        if b.T * 2 * F >= 1 << 32:
+            # the layer library refuses GEMM operands of 2^32 elements or more
+            result["consumer"] = {"skipped": f"the FFN of {b.T} rows at width {F} has a "
+                                             f"{b.T * 2 * F:.3g}-element operand; GEMMs of "
+                                             "2^32 elements or more are refused"}
+        else:
+            result["consumer"] = consumer_leg(up, torch, dec, hid, b, cfg)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, hidden, pos, p, cfg)
     print(json.dumps(result), flush=True)
+
+
+def ffn_width(H):
+    """FFN width: Llama-3.1-8B's for H = 4096, Gemma-3-12B's for H = 3840."""
+    return {4096: 14336, 3840: 15360}.get(H, int(round(3.5 * H / 256)) * 256)
 
 
 def consumer_leg(up, torch, dec, hid, b, cfg, reps=2):
@@ -279,8 +291,7 @@ def consumer_leg(up, torch, dec, hid, b, cfg, reps=2):
     0..N-1).  Weights and inputs are seeded; nothing here is part of `value`."""
     import math
     H, Hq, Hkv, d = cfg["H"], b.Hq, b.Hkv, b.d
-    # FFN width: Llama-3.1-8B's for H = 4096, Gemma-3-12B's for H = 3840.
-    F = {4096: 14336, 3840: 15360}.get(H, int(round(3.5 * H / 256)) * 256)
+    F = ffn_width(H)
     dev = hid.device
     g = torch.Generator(device=dev).manual_seed(20260)
 

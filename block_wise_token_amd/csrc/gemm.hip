@@ -115,6 +115,17 @@ FfnWs ffn_ws_layout(int64_t R, int F) {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Largest operand (elements) a GEMM here may have.  The GEMMs have run on the device up
+// to 4.03e9 elements per operand (the FFN of 131,072 rows at width 15,360); a run whose
+// FFN output had 6.3e9 elements (220,884 rows x 2 x 14,336) left the GPU with a memory
+// fault, and no fault of this library's own kernels at that size has been shown, so
+// operands of 2^32 elements or more are refused until one is shown to be safe.
+constexpr int64_t kMaxGemmElems = int64_t(1) << 32;
+bool gemm_fits(int64_t R, int K, int N) {
+  return R * (int64_t)K < kMaxGemmElems && R * (int64_t)N < kMaxGemmElems &&
+         (int64_t)K * N < kMaxGemmElems;
+}
 }  // namespace
 
 extern "C" {
@@ -123,6 +134,7 @@ int up_linear(const void* x, const void* w, const void* residual, int64_t R, int
               void* y, void* workspace, size_t workspace_bytes, void* stream) {
   if (R < 0 || K <= 0 || N <= 0) return UP_EINVAL;
   if (R == 0) return UP_OK;
+  if (!gemm_fits(R, K, N)) return UP_EUNSUPPORTED;
   if (!x || !w || !y || (workspace_bytes > 0 && !workspace)) return UP_EINVAL;
   if (workspace && !aligned(workspace, kWsAlign)) return UP_EWORKSPACE;
   const int r = linear_gemm(x, w, residual, R, K, N, y, workspace, workspace_bytes,
@@ -142,6 +154,7 @@ int up_swiglu_ffn(const void* x, const void* w_gu, const void* w_down, const voi
   if (R < 0 || H <= 0 || F <= 0) return UP_EINVAL;
   if (F % 8 != 0) return UP_EUNSUPPORTED;
   if (R == 0) return UP_OK;
+  if (!gemm_fits(R, H, 2 * F) || !gemm_fits(R, F, H)) return UP_EUNSUPPORTED;
   if (!x || !w_gu || !w_down || !y) return UP_EINVAL;
   const FfnWs L = ffn_ws_layout(R, F);
   if (!workspace || workspace_bytes < L.total || !aligned(workspace, kWsAlign))

@@ -26,7 +26,10 @@ extern "C" {
 /* y[R, N] = x[R, K] . w[N, K]^T (+ residual[R, N] when not NULL); bf16 in and out,
  * float32 accumulation.  residual may alias y.  workspace may be NULL with
  * workspace_bytes = 0; otherwise 256-byte aligned and offered to hipBLASLt.
- * UP_EUNSUPPORTED if hipBLASLt has no algorithm for the shape. */
+ * UP_EUNSUPPORTED if hipBLASLt has no algorithm for the shape, or if x, w or y has
+ * 2^32 elements or more (such GEMMs have not been shown to run safely here: the largest
+ * that ran had 4.03e9 elements per operand, and a run with a 6.3e9-element FFN output
+ * faulted the GPU). */
 int up_linear(const void* x, const void* w, const void* residual, int64_t R, int K, int N,
               void* y, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -35,7 +38,9 @@ int up_linear(const void* x, const void* w, const void* residual, int64_t R, int
  * residual : bf16 [R, H] or NULL (may alias y);  y : bf16 [R, H];  F % 8 == 0.
  * The intermediate x . w_gu^T and the gated activation (up_swiglu of
  * libuniprefill.so) are stored as bf16 in the workspace: at least
- * up_swiglu_ffn_workspace(R, H, F) bytes, 256-byte aligned. */
+ * up_swiglu_ffn_workspace(R, H, F) bytes, 256-byte aligned.  UP_EUNSUPPORTED when
+ * either GEMM would have an operand of 2^32 elements or more (R * 2F below 2^32, as for
+ * up_linear). */
 size_t up_swiglu_ffn_workspace(int64_t R, int H, int F);
 
 int up_swiglu_ffn(const void* x, const void* w_gu, const void* w_down, const void* residual,

@@ -319,6 +319,15 @@ def test_linear_swiglu_ffn_reject_bad_arguments(L, LL):
                                                         ctypes.c_size_t, ctypes.c_void_p]
     assert L.up_swiglu_ffn(d, d, d, None, 1000, 4096, 14336, d, d, w - 1, None) == UP_EWORKSPACE
     assert L.up_swiglu_ffn(d, d, d, None, 1000, 4096, 14330, d, d, w, None) == UP_EUNSUPPORTED
+    # operands of 2^32 elements or more are refused before any launch
+    assert L.up_linear(d, d, None, 1 << 20, 4096, 4096, d, None, 0, None) == UP_EUNSUPPORTED
+    assert L.up_linear(d, d, None, 149797, 4096, 28672, d, None, 0, None) == UP_EUNSUPPORTED
+    assert L.up_swiglu_ffn(d, d, d, None, 220884, 4096, 14336, d, d, 1 << 62, None) == \
+        UP_EUNSUPPORTED
+    # the largest layer that has run: 131,072 rows at width 15,360 (4.03e9 elements)
+    big = L.up_swiglu_ffn_workspace(131072, 3840, 15360)
+    assert L.up_swiglu_ffn(d, d, d, None, 131072, 3840, 15360, d, d, big - 1, None) == \
+        UP_EWORKSPACE
 
 
 def test_layer_decision_workspace_and_arguments(L):
