@@ -21,6 +21,10 @@ LIB = os.path.join(PKG, "libuniprefill.so")
 LAYER_LIB = os.path.join(PKG, "libuniprefill_layer.so")
 SOURCES = ["abi.hip", "score.hip", "select.hip", "compact.hip", "consumer.hip"]
 LAYER_SOURCES = ["gemm.hip"]
+# A measurement program (not linked into either library): the sustained clock and matrix
+# rate of the score kernel's instruction mix.
+PROBE_SRC = "probe_mfma_mix.hip"
+PROBE_BIN = os.path.join(PKG, "probe_mfma_mix")
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are switched off for all device code.
@@ -48,9 +52,10 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _link(objs, out, extra):
+def _link(objs, out, extra, shared=True):
     tmp = out + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *extra, "-o", tmp]
+    kind = ["-shared", "-fPIC"] if shared else []
+    cmd = [hipcc(), *kind, f"--offload-arch={ARCH}", *objs, *extra, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link of {os.path.basename(out)} failed:\n" + r.stdout + r.stderr)
@@ -68,8 +73,9 @@ def build(verbose: bool = True) -> str:
     _link([objs[s] for s in LAYER_SOURCES], LAYER_LIB,
           ["-L", PKG, "-luniprefill", "-lhipblaslt", "-Wl,-rpath,$ORIGIN",
            "-Wl,-soname,libuniprefill_layer.so"])
+    _link([_compile(PROBE_SRC)], PROBE_BIN, [], shared=False)
     if verbose:
-        print(f"built {LIB} and {LAYER_LIB}")
+        print(f"built {LIB}, {LAYER_LIB} and {PROBE_BIN}")
     return LIB
 
 
