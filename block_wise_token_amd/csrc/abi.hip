@@ -771,19 +771,24 @@ int up_rope_attention_scores(const void* q, const void* k, const void* v, const 
     if (hipEventRecord(ss->fork, hs) != hipSuccess ||
         hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
       return UP_EHIP;
+    // From here the second stream may hold work of this call: whatever fails below, the
+    // caller's stream is joined to it before returning, so no kernel of a failed call
+    // can still be reading the caller's buffers once the error is reported.
     e = timed(18, ss->s, [&] {
       return launch_attention(cu_seqlens, a, workspace, LA, c, out, ss->s, &so,
                               attn::kSlotsWindow);
     });
-    if (e != hipSuccess) return UP_EHIP;
-    e = timed(14, hs, [&] {
-      return launch_attention(cu_seqlens, a, workspace, LA, c, out, hs, nullptr,
-                              attn::kSlotsRest);
-    });
-    if (e != hipSuccess) return UP_EHIP;
+    if (e == hipSuccess)
+      e = timed(14, hs, [&] {
+        return launch_attention(cu_seqlens, a, workspace, LA, c, out, hs, nullptr,
+                                attn::kSlotsRest);
+      });
     if (hipEventRecord(ss->join, ss->s) != hipSuccess ||
-        hipStreamWaitEvent(hs, ss->join, 0) != hipSuccess)
+        hipStreamWaitEvent(hs, ss->join, 0) != hipSuccess) {
+      (void)hipStreamSynchronize(ss->s);   // no join could be enqueued: drain it instead
       return UP_EHIP;
+    }
+    if (e != hipSuccess) return UP_EHIP;
   }
   e = timed(2, hs, [&] { return launch_block_mass(s, t, sws, LS, hs); });
   if (e != hipSuccess) return UP_EHIP;

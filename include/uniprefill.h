@@ -351,7 +351,10 @@ int up_rope_attention(const void* q, const void* k, const void* v, const int32_t
  *           row's scaled logits (NULL to skip).
  * workspace : at least up_rope_attention_scores_workspace(...) bytes, 256-byte aligned.
  * Errors: as up_rope_attention and up_block_scores; when either plan finds the device
- * cu_seqlens inconsistent, error bit 1 is raised and the scores are not written. */
+ * cu_seqlens inconsistent, error bit 1 is raised and the scores are not written.  A
+ * launch error after the fork still joins `stream` to the second stream before
+ * UP_EHIP is returned (if even the join cannot be enqueued, the second stream is
+ * synchronised), so no kernel of the failed call outlives the report. */
 size_t up_rope_attention_scores_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv,
                                           int d, int n, int G);
 
