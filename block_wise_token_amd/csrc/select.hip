@@ -230,7 +230,9 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, Lds& S) {
   return r;
 }
 
-// NT threads per request; block a of the request lives in slot a / NT of thread a % NT.
+// NT threads per request; block a of the request lives in slot a / NT of thread a % NT,
+// PER slots per thread (the launch takes the fewest that hold the request: every phase
+// loops over the slots, so empty ones cost time).
 //
 // FUSED (one request, NT = 256): the kernel also does the normalisation and the
 // block destinations of the compaction, so the decision needs neither the normalise
@@ -239,15 +241,15 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, Lds& S) {
 // then the lanes by butterfly, then the four waves in order) so the float32 scores it
 // writes are bit-identical, selects on them, and writes each block's destination row,
 // source row and length with the compaction header's valid flag.
-template <int NT, bool FUSED>
+template <int NT, int PER, bool FUSED>
 __global__ __launch_bounds__(NT) void up_select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ cu, int B, int n, int G,
     int mode, float p, int topk, int64_t T_host, int64_t nb_tot_host, int direct,
     uint8_t* __restrict__ keep, int32_t* __restrict__ cu_out, int* __restrict__ err,
     FusedDecision fd) {
   constexpr int NW = NT / 64;
-  constexpr int PER = kSelPer * 1024 / NT > kSelPer ? kSelPer : kSelPer * 1024 / NT;
   constexpr int MAXB = NT * PER;
+  static_assert(PER >= 1 && PER <= kSelPer, "slots per thread");
   __shared__ SelLds<NW> S;
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
@@ -692,6 +694,33 @@ __global__ __launch_bounds__(1024) void up_select_finalize_kernel(int32_t* __res
   }
 }
 
+// Slots per thread of a 256-thread select for a request of nb blocks: the fewest of
+// 1, 2, 4, 8, 16 that hold it (nb <= 256 * kSelPer).
+static int sel_slots(int64_t nb) {
+  int per = 1;
+  while (per < kSelPer && (int64_t)256 * per < nb) per *= 2;
+  return per;
+}
+
+template <bool FUSED>
+static void launch_select256(int per, int B, hipStream_t st, const float* scores,
+                             const int32_t* cu, int n, int G, int mode, float p, int topk,
+                             int64_t T_host, int64_t nb_tot_host, int direct, uint8_t* keep,
+                             int32_t* cu_out, int* err, const FusedDecision& fd) {
+#define UP_SEL_LAUNCH(P)                                                                   \
+  hipLaunchKernelGGL((up_select_kernel<256, P, FUSED>), dim3(B), dim3(256), 0, st, scores, \
+                     cu, B, n, G, mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out,  \
+                     err, fd)
+  switch (per) {
+    case 1: UP_SEL_LAUNCH(1); break;
+    case 2: UP_SEL_LAUNCH(2); break;
+    case 4: UP_SEL_LAUNCH(4); break;
+    case 8: UP_SEL_LAUNCH(8); break;
+    default: UP_SEL_LAUNCH(kSelPer); break;
+  }
+#undef UP_SEL_LAUNCH
+}
+
 hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, int G, int mode,
                          float p, int topk, int nb_max, int64_t T_host, int64_t nb_tot_host,
                          uint8_t* keep, int32_t* cu_out, int* err, hipStream_t st) {
@@ -703,12 +732,12 @@ hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, i
     hipLaunchKernelGGL(up_select_small_kernel, dim3(B), dim3(kSmallSelBlocks), 0, st, scores, cu,
                        B, n, G, mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err);
   } else if (nb_max <= 256 * kSelPer) {
-    hipLaunchKernelGGL((up_select_kernel<256, false>), dim3(B), dim3(256), 0, st, scores, cu, B,
-                       n, G, mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err, none);
+    launch_select256<false>(sel_slots(nb_max), B, st, scores, cu, n, G, mode, p, topk, T_host,
+                            nb_tot_host, direct, keep, cu_out, err, none);
   } else {
-    hipLaunchKernelGGL((up_select_kernel<1024, false>), dim3(B), dim3(1024), 0, st, scores, cu,
-                       B, n, G, mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err,
-                       none);
+    hipLaunchKernelGGL((up_select_kernel<1024, kSelPer, false>), dim3(B), dim3(1024), 0, st,
+                       scores, cu, B, n, G, mode, p, topk, T_host, nb_tot_host, direct, keep,
+                       cu_out, err, none);
   }
   return hipGetLastError();
 }
@@ -718,8 +747,8 @@ hipError_t launch_select_fused(const int32_t* cu, int n, int G, float p, int64_t
                                const FusedDecision& fd, hipStream_t st) {
   static_assert(kFusedSelectMaxBlocks <= 256 * kSelPer, "fused select slots");
   if (nb_tot_host > kFusedSelectMaxBlocks) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((up_select_kernel<256, true>), dim3(1), dim3(256), 0, st, nullptr, cu, 1, n,
-                     G, 0, p, 0, T_host, nb_tot_host, 1, keep, cu_out, err, fd);
+  launch_select256<true>(sel_slots(nb_tot_host), 1, st, nullptr, cu, n, G, 0, p, 0, T_host,
+                         nb_tot_host, 1, keep, cu_out, err, fd);
   return hipGetLastError();
 }
 
