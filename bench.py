@@ -766,22 +766,28 @@ def stack_leg(up, torch, cfg, b0, hid, posd, p, args):
 
 def graph_leg(up, torch, dec_big, args, T_big, reps=50):
     """Decisions replayed from a HIP graph (torch.cuda.CUDAGraph) against the same calls
-    launched one by one: at the headline size and at the small single-request size
+    launched one by one: at the bench's workload and at the small single-request size
     (4096 tokens, where the host's launch cost matters)."""
     from workloads import synth
-    cfg = synth.WORKLOADS["single_4k_h8_d64"]
-    sb = synth.make_batch(cfg)
-    dev = dec_big.qwin.device
+    legs = [(args.workload, dec_big, T_big, args.steps)]
+    small_name = "single_4k_h8_d64"
+    if args.workload != small_name:
+        cfg = synth.WORKLOADS[small_name]
+        sb = synth.make_batch(cfg)
+        dev = dec_big.qwin.device
 
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-    hid = bf16(synth.gen_hidden(sb.T, cfg["H"], cfg["seed"]))
-    small = up.LayerDecision(bf16(sb.qwin), bf16(sb.k), torch.from_numpy(sb.cu_seqlens).to(dev),
-                             sb.cu_seqlens, hid, torch.from_numpy(synth.positions(sb.cu_seqlens)).to(dev),
-                             sb.n, sb.G, cfg["p"])
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        hid = bf16(synth.gen_hidden(sb.T, cfg["H"], cfg["seed"]))
+        small = up.LayerDecision(bf16(sb.qwin), bf16(sb.k), torch.from_numpy(sb.cu_seqlens).to(dev),
+                                 sb.cu_seqlens, hid,
+                                 torch.from_numpy(synth.positions(sb.cu_seqlens)).to(dev),
+                                 sb.n, sb.G, cfg["p"])
+        legs.append((small_name, small, sb.T, reps))
+    else:
+        legs = [(small_name, dec_big, T_big, reps)]
     out = {}
-    for name, dec, T, n in (("llama31_8b_128k", dec_big, T_big, args.steps),
-                            ("single_4k_h8_d64", small, sb.T, reps)):
+    for name, dec, T, n in legs:
         dec.run()
         torch.cuda.synchronize()
         want_keep = dec.keep.clone()
