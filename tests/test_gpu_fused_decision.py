@@ -60,6 +60,7 @@ CASES = [
     ([3000], 8, 2, 128, 128, 64, 1.0, False),         # p = 1 keeps everything
     ([20000], 8, 2, 64, 128, 64, 0.97, True),         # exact ties at the cut
     ([5000], 16, 2, 128, 256, 32, 0.99, False),       # G = 32
+    ([50000], 8, 2, 64, 128, 64, 0.99, False),        # 782 blocks: four select slots per thread
     ([262144], 8, 2, 64, 128, 64, 0.95, False),       # exactly 4096 blocks: the fused limit
     ([262208], 8, 2, 64, 128, 64, 0.95, False),       # 4097 blocks: the separate calls
     ([129, 0, 3000, 64, 1], 8, 2, 128, 128, 64, 0.97, False),   # several requests

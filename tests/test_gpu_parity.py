@@ -143,6 +143,10 @@ def test_select_is_bit_exact_on_oracle_scores():
     cut[1:] = np.cumsum(lens)
     st = np.concatenate([rng.choice(vals, O.n_blocks(L, 64)) for L in lens]).astype(np.float32)
     cases.append((st, cut, "tie runs"))
+    # one request per slot count of the 256-thread select (2, 4, 8 and 16 per thread)
+    for nb in (300, 777, 1500, 4096):
+        sm = rng.dirichlet(np.full(nb, 0.4)).astype(np.float32)
+        cases.append((sm, np.array([0, nb * 64 - 9], np.int32), f"one request of {nb} blocks"))
     # a single block holding all the mass (score exactly 1.0) among zeros
     s1b = np.zeros(9000, np.float32)
     s1b[4321] = 1.0
