@@ -140,7 +140,7 @@ __device__ __forceinline__ U192 wave_scan_u192(U192 v) {
   return v;
 }
 
-constexpr int kSelPer = 16;                      // candidate slots per thread
+constexpr int kSelPer = 16;                      // most candidate slots per thread
 constexpr int kBins = 256;                       // digits of at most 8 bits
 constexpr int kCopies = 8;                       // lane l adds into histogram copy l % 8
 constexpr uint32_t kAbsent = 0xFFFFFFFFu;        // no block in this slot
