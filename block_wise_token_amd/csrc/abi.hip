@@ -559,8 +559,10 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
   const CompactWs LC = compact_ws_layout(sp.nb_tot);
   if (!workspace || workspace_bytes < LS.total + LC.total || !aligned(workspace, kWsAlign))
     return UP_EWORKSPACE;
-  if (!qwin || !k || !cu_seqlens || !scores || !keep_blocks || !cu_seqlens_out || !hidden ||
-      !idx_out || !hidden_out)
+  // With every request empty (T = 0) only cu_seqlens and cu_seqlens_out hold data; the
+  // other buffers have no elements and may be NULL, as in the separate calls.
+  if (!cu_seqlens || !cu_seqlens_out) return UP_EINVAL;
+  if (t.T > 0 && (!qwin || !k || !scores || !keep_blocks || !hidden || !idx_out || !hidden_out))
     return UP_EINVAL;
   if ((pos_out && !pos) || (orig_out && !prev_orig)) return UP_EINVAL;
   const int64_t row_bytes = (int64_t)H * elem_bytes;

@@ -271,6 +271,8 @@ int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
  * outputs and results, bit for bit.  For one request of at most 4096 blocks the
  * select kernel also normalises the block masses and assigns the compaction's block
  * destinations (two launches fewer); otherwise the three calls run in sequence.
+ * When every request is empty (T = 0) only cu_seqlens_out is written (all zeros); the
+ * buffers sized by T or by the block count may then be NULL.
  * workspace : at least up_layer_decision_workspace(...) bytes, 256-byte aligned.
  * ------------------------------------------------------------------------- */
 size_t up_layer_decision_workspace(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, int d,

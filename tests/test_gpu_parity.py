@@ -198,6 +198,26 @@ def test_zero_queries_give_exact_ties_on_gpu():
     check_compaction(gb, res)
 
 
+@pytest.mark.parametrize("lengths", [[0], [0, 0, 0]])
+@pytest.mark.parametrize("separate", [False, True])
+def test_all_empty_batch_decides_nothing(lengths, separate):
+    """Every request empty (T = 0): the decision writes cu_seqlens_out = 0 and nothing
+    else, through the one-call entry and through the three separate calls (the
+    zero-length buffers are passed as whatever torch gives for empty tensors)."""
+    say(f"[case] all-empty batch {lengths} separate={separate}")
+    batch = _batch(lengths, 8, 2, 128, 128, 64, seed=11)
+    assert batch.T == 0
+    gb = GpuBatch(batch, H=64)
+    b = gb.b
+    dec = up.LayerDecision(gb.qwin, gb.k, gb.cu, gb.cu_h, gb.hidden, gb.pos, b.n, b.G, 0.9,
+                           separate=separate)
+    dec.cu_out.fill_(-7)
+    dec.run()
+    torch.cuda.synchronize()
+    assert up.device_error() == 0
+    assert dec.cu_out.cpu().tolist() == [0] * (len(lengths) + 1)
+
+
 def test_runs_are_bitwise_reproducible():
     cfg = synth.WORKLOADS["single_4k_h8_d64"]
     batch = synth.make_batch(cfg)
