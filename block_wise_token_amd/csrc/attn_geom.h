@@ -1,10 +1,10 @@
-// Index arithmetic of the 8-wave attention kernel (consumer.hip): which request,
-// heads and token tiles a workgroup and its waves take, where every global-to-LDS
-// copy reads and lands, and where every operand read and output store goes.  The
-// kernel calls these functions and nothing else for its addresses; a host replay
-// (tests/attn_replay.cpp, built with g++) calls the same functions for every
-// workgroup, wave, lane and stage of a launch and checks each access against its
-// buffer, the ring's stage hand-over and the operand layouts.
+// Index arithmetic of the attention kernels (consumer.hip: the 8-wave kernel W8 and
+// the 4-wave kernel W4): which request, heads and token tiles a workgroup and its
+// waves take, where every global-to-LDS copy reads and lands, and where every operand
+// read and output store goes.  The kernels call these functions and nothing else for
+// their addresses; a host replay (tests/attn_replay.cpp, built with g++) calls the same
+// functions for every workgroup, wave, lane and stage of a launch and checks each
+// access against its buffer, the ring's stage hand-over and the operand layouts.
 #pragma once
 #include <cstdint>
 
@@ -45,6 +45,9 @@ UP_HD int k_swz(int key) {
   return (D / 8 >= 16) ? (key & 15) : ((key >> 1) & 7);
 }
 UP_HD int v128_swz(int row) { return (row >> 1) & 7; }
+// V^T rows of 64 bytes (32 tokens): granule g of row r sits at g ^ ((r >> 2) & 3), which
+// spreads the 16 rows one 16-lane group reads over all 64 banks.
+UP_HD int v64_swz(int row) { return (row >> 2) & 3; }
 
 // Token stored at position t of the transposed v: inside each 16-token group bits 2
 // and 3 are swapped, so that the 8 keys a lane half contracts in one MFMA step (the
@@ -103,6 +106,55 @@ struct W8 {
   }
 };
 
+// Four waves (one per SIMD at d = 256) share one ring of NS stages of 32 keys: the K
+// tile [32][D] and the V^T tile [D][32] (row bytes 64).  Each wave holds one query head's
+// 32-token tile.
+template <int D>
+struct W4 {
+  static constexpr int NW = 4, NT = 64 * NW, NS = 4, UK = 32;
+  static constexpr int DS = D / 16;        // MFMA k-steps over the head dimension
+  static constexpr int DT = D / 32;        // 32-row tiles of O^T
+  static constexpr int KRB = 2 * D;        // K tile row bytes
+  static constexpr int KB = UK * KRB;      // K tile bytes
+  static constexpr int VRB = 2 * UK;       // V^T tile row bytes
+  static constexpr int VB = D * VRB;       // V^T tile bytes
+  static constexpr int SB = KB + VB;       // stage bytes
+  static constexpr int KSPT = KB / (NT * 16);   // 16-byte copies per lane per stage, K
+  static constexpr int VSPT = VB / (NT * 16);   // and V^T
+  static constexpr int SPT = KSPT + VSPT;
+  static_assert(KB % (NT * 16) == 0 && VB % (NT * 16) == 0, "whole copy rounds");
+  static_assert(2 * SPT < 64, "vmcnt range");
+  static_assert(NS * SB <= 160 * 1024, "LDS");
+
+  // Copy q of a stage, thread tid: as in W8 (element offsets from the stage's first K
+  // row, or from its first token of V^T row 0).
+  UP_HD static int k_src(int q, int tid) {
+    const int o = q * NT * 16 + tid * 16;
+    const int key = o / KRB;
+    const int gr = ((o % KRB) / 16) ^ k_swz<D>(key);
+    return key * D + gr * 8;
+  }
+  UP_HD static int64_t v_src(int q, int tid, int64_t Rp) {
+    const int o = q * NT * 16 + tid * 16;
+    const int row = o / VRB;
+    const int gr = ((o % VRB) / 16) ^ v64_swz(row);
+    return (int64_t)row * Rp + gr * 8;
+  }
+  UP_HD static uint32_t k_dst(int q, int wave) { return (uint32_t)(q * NT * 16 + wave * 1024); }
+  UP_HD static uint32_t v_dst(int q, int wave) {
+    return (uint32_t)(KB + q * NT * 16 + wave * 1024);
+  }
+  // Operand reads, stage bytes: K row l32 (the stage's key l32), lane half h, k-step s
+  // reads d-elements [h D/2 + 8 s, +8); V^T granule j of row l32 (row tile dt adds
+  // dt 32 VRB).
+  UP_HD static uint32_t k_rd(int l32, int half, int s) {
+    return (uint32_t)(l32 * KRB + 16 * ((half * DS + s) ^ k_swz<D>(l32)));
+  }
+  UP_HD static uint32_t v_rd(int l32, int j) {
+    return (uint32_t)(KB + l32 * VRB + 16 * (j ^ v64_swz(l32)));
+  }
+};
+
 // Launch layouts of the tile slots (blockIdx.y).  A request's slots are its workgroup
 // tiles, heaviest (last) first; tp is the prefix of the requests' slot counts.  With
 // window block statistics, the first k_i slots of request i hold its window rows (wp is
@@ -139,7 +191,7 @@ struct Wg {
 };
 UP_HD Wg wg_of(int bx, int by, int Hq, int Hkv, int HQ, int TT, int B, const int32_t* cu,
                const int32_t* po, const int32_t* tp, int mode = kSlotsAll,
-               const int32_t* wp = nullptr) {
+               const int32_t* wp = nullptr, int tile_shift = 6) {
   Wg w;
   const int gsz = Hq / Hkv, quads = gsz / HQ;
   w.g = bx / quads;
@@ -149,7 +201,7 @@ UP_HD Wg wg_of(int bx, int by, int Hq, int Hkv, int HQ, int TT, int B, const int
   w.L = cu[w.i + 1] - cu[w.i];
   const int nwt = tp[w.i + 1] - tp[w.i];
   w.wt = nwt - 1 - j;   // heaviest tile first
-  w.ntile = (w.L + 63) >> 6;         // 64-token tiles of the request
+  w.ntile = (w.L + (1 << tile_shift) - 1) >> tile_shift;   // tiles of the request
   w.tile0 = w.wt * TT;
   w.nst = w.tile0 + TT < w.ntile ? w.tile0 + TT : w.ntile;   // key stages of the workgroup
   w.pbase = po[w.i];
@@ -173,6 +225,36 @@ UP_HD Wv wave_of(const Wg& w, int wave, int Hq, int Hkv, int HQ) {
 }
 // Request-local token of a wave's query row (lane column l32).
 UP_HD int query_token(const Wv& v, int l32) { return v.tw * 64 + v.sub * 32 + l32; }
+
+// The 4-wave kernel's waves: query head HQ-major within the quad, one 32-token tile
+// each (wg_of with tile_shift 5).
+UP_HD Wv wave4_of(const Wg& w, int wave, int Hq, int Hkv, int HQ) {
+  Wv v;
+  const int gsz = Hq / Hkv;
+  v.sub = 0;
+  v.head = w.g * gsz + w.quad * HQ + wave % HQ;
+  v.tw = w.tile0 + wave / HQ;
+  v.act = v.tw < w.ntile;
+  return v;
+}
+UP_HD int query_token4(const Wv& v, int l32) { return v.tw * 32 + l32; }
+template <int D>
+UP_HD int64_t q_src4(const Wg& w, const Wv& v, int l32, int half, int64_t Rp) {
+  return ((int64_t)v.head * Rp + w.pbase + v.tw * 32 + l32) * D + half * (D / 2);
+}
+// Element offsets of the 32-key K and V^T stage st of kv head g.
+template <int D>
+UP_HD int64_t k_stage4(const Wg& w, int st, int64_t Rp) {
+  return ((int64_t)w.g * Rp + w.pbase) * D + (int64_t)st * 32 * D;
+}
+template <int D>
+UP_HD int64_t v_stage4(const Wg& w, int st, int64_t Rp) {
+  return (int64_t)w.g * D * Rp + w.pbase + (int64_t)st * 32;
+}
+template <int D>
+UP_HD int64_t out_index4(const int32_t* cu, const Wg& w, const Wv& v, int l32, int Hq, int dv) {
+  return (((int64_t)cu[w.i] + query_token4(v, l32)) * Hq + v.head) * D + dv;
+}
 // Element offset of a query row's operand in the rotated copy qr [Hq][Rp][D].
 template <int D>
 UP_HD int64_t q_src(const Wg& w, const Wv& v, int l32, int half, int64_t Rp) {

@@ -322,16 +322,6 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// 16-byte granule swizzles.  The LDS serves a 16-byte read to 16 lanes per clock over
-// 64 banks; the 16 lanes of a group read 16 consecutive rows at one logical granule,
-// which the XOR spreads over 16 distinct bank groups: by row & 15 for K rows of 256
-// bytes or more, by (row >> 1) & 7 for 128-byte rows (odd rows sit half a bank cycle
-// further on).
-template <int D>
-__device__ __forceinline__ int k_swz(int key) {
-  return (D / 8 >= 16) ? (key & 15) : ((key >> 1) & 7);
-}
-
 constexpr float kRebase = 32.f;
 
 // Window-row block statistics (the fused form of the block scores).  A wave whose
@@ -399,10 +389,6 @@ struct WinStats {
   }
 };
 
-// V^T tile rows are 64 bytes (32 tokens): granule g of row r sits at g ^ ((r >> 2) & 3),
-// which spreads the 16 rows one 16-lane group reads over all 64 banks.
-__device__ __forceinline__ int v64_swz(int row) { return (row >> 2) & 3; }
-
 template <int D, bool ST>
 __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
@@ -411,19 +397,9 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
     const int32_t* __restrict__ tp, int B, int Hq, int Hkv, int HQ, int TT, int64_t Rp,
     float c, uint16_t* __restrict__ out, AttnScoreOut so, int mode,
     const int32_t* __restrict__ wp) {
-  constexpr int NT = 256, NS = 4, UK = 32;
-  constexpr int DS = D / 16;             // MFMA k-steps over the head dimension
-  constexpr int DT = D / 32;             // 32-row tiles of O^T
-  constexpr int KRB = 2 * D;             // K tile row bytes
-  constexpr int KB = UK * KRB;           // K tile bytes
-  constexpr int VRB = 2 * UK;            // V^T tile row bytes
-  constexpr int VB = D * VRB;            // V^T tile bytes
-  constexpr int SB = KB + VB;            // stage bytes
-  constexpr int KSPT = KB / (NT * 16);   // DMA copies per lane per stage, K
-  constexpr int VSPT = VB / (NT * 16);   // and V^T
-  constexpr int SPT = KSPT + VSPT;
-  static_assert(KB % (NT * 16) == 0 && VB % (NT * 16) == 0, "whole DMA rounds");
-  static_assert(2 * SPT < 64, "vmcnt range");
+  using G = attn::W4<D>;
+  constexpr int NS = G::NS, DS = G::DS, DT = G::DT, VRB = G::VRB, SB = G::SB, KSPT = G::KSPT,
+                VSPT = G::VSPT, SPT = G::SPT;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SB];
 
   if (hdr->valid != 1) {
@@ -431,29 +407,23 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
       if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) so.hdr->valid = 0;
     return;
   }
-  const int gsz = Hq / Hkv, quads = gsz / HQ;
-  const int g = blockIdx.x / quads, quad = blockIdx.x - g * quads;
-  int i = 0, j = 0;
-  attn::slot_of(mode, blockIdx.y, B, tp, wp, i, j);
-  const int L = cu[i + 1] - cu[i];
-  const int nwt = tp[i + 1] - tp[i];
-  const int wt = nwt - 1 - j;             // heaviest tile first
-  const int ntile = (L + 31) >> 5;        // 32-token tiles of the request
-  const int tile0 = wt * TT;
-  const int nst = min(tile0 + TT, ntile);   // 32-key stages of this workgroup
-  const int64_t pbase = po[i];
+  // 32-token tiles (tile_shift 5): a workgroup's stages are 32 keys each.
+  const attn::Wg w = attn::wg_of(blockIdx.x, blockIdx.y, Hq, Hkv, HQ, TT, B, cu, po, tp, mode,
+                                 wp, 5);
+  const int i = w.i, L = w.L, g = w.g, nst = w.nst;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5,
             l32 = lane & 31;
-  const int head = g * gsz + quad * HQ + wave % HQ;
-  const int tw = tile0 + wave / HQ;   // this wave's 32-token tile (its diagonal stage)
-  const bool wact = tw < ntile;
+  const attn::Wv wv = attn::wave4_of(w, wave, Hq, Hkv, HQ);
+  const int head = wv.head;
+  const int tw = wv.tw;   // this wave's 32-token tile (its diagonal stage)
+  const bool wact = wv.act;
 
   // Query operand (one 32-row tile), the head dimension in the permuted order both
   // operands share: lane half h, k-step s covers d-elements [h D/2 + 8 s, +8).
   bf16x8 qreg[DS];
   if (wact) {
-    const uint16_t* src = qr + ((int64_t)head * Rp + pbase + tw * 32 + l32) * D + half * (D / 2);
+    const uint16_t* src = qr + attn::q_src4<D>(w, wv, l32, half, Rp);
 #pragma unroll
     for (int s = 0; s < DS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(src + s * 8);
   } else {
@@ -464,43 +434,32 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
 
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8*)lds;
-  const uint16_t* kbase = kr + ((int64_t)g * Rp + pbase) * D;
-  const uint16_t* vbase = vt + (int64_t)g * D * Rp + pbase;
   auto issue = [&](int st) {
     const uint32_t sb = lds_base + (uint32_t)((st & (NS - 1)) * SB);
-    const uint16_t* kst = kbase + (int64_t)st * UK * D;
+    const uint16_t* kst = kr + attn::k_stage4<D>(w, st, Rp);
 #pragma unroll
-    for (int q = 0; q < KSPT; ++q) {
-      const int o = q * NT * 16 + tid * 16;
-      const int key = o / KRB;
-      const int gr = ((o % KRB) / 16) ^ k_swz<D>(key);
-      lds_dma16(kst + key * D + gr * 8,
-                __builtin_amdgcn_readfirstlane(sb + q * NT * 16 + wave * 1024));
-    }
-    const uint16_t* vst = vbase + (int64_t)st * UK;
+    for (int q = 0; q < KSPT; ++q)
+      lds_dma16(kst + G::k_src(q, tid), __builtin_amdgcn_readfirstlane(sb + G::k_dst(q, wave)));
+    const uint16_t* vst = vt + attn::v_stage4<D>(w, st, Rp);
 #pragma unroll
-    for (int q = 0; q < VSPT; ++q) {
-      const int o = q * NT * 16 + tid * 16;
-      const int row = o / VRB;
-      const int gr = ((o % VRB) / 16) ^ v64_swz(row);
-      lds_dma16(vst + (int64_t)row * Rp + gr * 8,
-                __builtin_amdgcn_readfirstlane(sb + KB + q * NT * 16 + wave * 1024));
-    }
+    for (int q = 0; q < VSPT; ++q)
+      lds_dma16(vst + G::v_src(q, tid, Rp),
+                __builtin_amdgcn_readfirstlane(sb + G::v_dst(q, wave)));
   };
 
   uint32_t krd[DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) krd[s] = l32 * KRB + 16 * ((half * DS + s) ^ k_swz<D>(l32));
+  for (int s = 0; s < DS; ++s) krd[s] = G::k_rd(l32, half, s);
   // V^T row dt * 32 + l32 has the swizzle of l32 (dt * 32 is a multiple of 16 rows).
   uint32_t vrd[2];
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) vrd[jj] = KB + l32 * VRB + 16 * ((2 * jj + half) ^ v64_swz(l32));
+  for (int jj = 0; jj < 2; ++jj) vrd[jj] = G::v_rd(l32, 2 * jj + half);
 
   float Rs = 0.f, lsum = 0.f;
   f32x16 O[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
-  const int qtok = tw * 32 + l32;
+  const int qtok = attn::query_token4(wv, l32);
   WinStats ws;
   if constexpr (ST) ws.init(so, i, L, g, head, Hq, Hkv, wact, tw * 32, qtok);
 
@@ -517,8 +476,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
   auto mask = [&](int hs, f32x16& acc) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int key = hs * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-      if (key > qtok) acc[e] = kNegInf;
+      if (attn::acc_key(hs, e, half) > qtok) acc[e] = kNegInf;
     }
   };
   auto rebase = [&](const f32x16& acc, bool init) {
@@ -644,7 +602,6 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
   const float lt = pair_sum(lsum), inv = 1.f / lt;
   if constexpr (ST) ws.finish(tw, Rs, lt, half);
   if (qtok >= L) return;
-  uint16_t* dst = out + (((int64_t)cu[i] + qtok) * Hq + head) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -654,7 +611,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void up_attention_kernel(
       typedef float f32x4 __attribute__((ext_vector_type(4)));
       const f32x4 o4 = {O[dt][4 * eg] * inv, O[dt][4 * eg + 1] * inv, O[dt][4 * eg + 2] * inv,
                         O[dt][4 * eg + 3] * inv};
-      *reinterpret_cast<bf16x4*>(dst + dv) = __builtin_convertvector(o4, bf16x4);
+      *reinterpret_cast<bf16x4*>(out + attn::out_index4<D>(cu, w, wv, l32, Hq, dv)) =
+          __builtin_convertvector(o4, bf16x4);
     }
 }
 

@@ -1,9 +1,11 @@
-// Host replay of the 8-wave attention kernel's addressing (block_wise_token_amd/csrc/
-// consumer.hip, up_attention_w8_kernel), built with g++ against the same index
-// functions the kernel calls (attn_geom.h).  No GPU code runs here.
+// Host replay of the attention kernels' addressing (block_wise_token_amd/csrc/
+// consumer.hip: up_attention_w8_kernel for d = 64 and 128 up to 256 kv heads,
+// up_attention_kernel, the 4-wave kernel, otherwise), built with g++ against the same
+// index functions the kernels call (attn_geom.h).  No GPU code runs here.
 //
 //   attn_replay D Hq Hkv L0,L1,... [n G]
 //
+// Parts 1 and 2 run for the kernel that serves the shape (W8 or W4).
 // Part 1 (per head dimension, every lane): the global-to-LDS copies of a stage fill
 // the stage's K and V^T tiles exactly once, inside the stage; every K operand read
 // returns the key and head-dimension elements the query operand of the same lane and
@@ -306,6 +308,224 @@ void part2(int Hq, int Hkv, const std::vector<int>& lens) {
               D, Hq, Hkv, B, (long long)R, (long long)Rp, (long long)tiles, gx, (long long)tiles);
 }
 
+// Parts 1 and 2 for the 4-wave kernel (W4): 32-key stages of a 32-key K tile and a
+// V^T tile of 32 tokens per row; a wave holds one query head's 32-token tile.
+template <int D>
+void part1_w4() {
+  using G = up::attn::W4<D>;
+  const int ngran = G::SB / 16;
+  std::vector<Gran> map(ngran);
+  std::vector<int> kcov(32 * D / 8, 0), vcov(D * 32 / 8, 0);
+  for (int q = 0; q < G::KSPT; ++q)
+    for (int tid = 0; tid < G::NT; ++tid) {
+      const int wave = tid / 64, lane = tid % 64;
+      const uint32_t dst = G::k_dst(q, wave) + 16u * lane;
+      CHECK(dst % 16 == 0 && dst + 16 <= (uint32_t)G::KB, q, tid, dst);
+      const int src = G::k_src(q, tid);
+      CHECK(src % 8 == 0 && src >= 0 && src + 8 <= 32 * D, q, tid, src);
+      CHECK(map[dst / 16].kind == -1, q, tid, dst);
+      map[dst / 16] = Gran{0, src / D, src % D};
+      kcov[src / 8]++;
+    }
+  for (int q = 0; q < G::VSPT; ++q)
+    for (int tid = 0; tid < G::NT; ++tid) {
+      const int wave = tid / 64, lane = tid % 64;
+      const uint32_t dst = G::v_dst(q, wave) + 16u * lane;
+      CHECK(dst % 16 == 0 && dst >= (uint32_t)G::KB && dst + 16 <= (uint32_t)G::SB, q, tid, dst);
+      const int64_t Rp = 1 << 20;
+      const int64_t src = G::v_src(q, tid, Rp);
+      const int row = (int)(src / Rp), tok = (int)(src % Rp);
+      CHECK(row >= 0 && row < D && tok % 8 == 0 && tok + 8 <= 32, q, tid, src);
+      CHECK(map[dst / 16].kind == -1, q, tid, dst);
+      map[dst / 16] = Gran{1, row, tok};
+      vcov[(row * 32 + tok) / 8]++;
+    }
+  for (int g = 0; g < ngran; ++g) CHECK(map[g].kind != -1, g);
+  for (size_t x = 0; x < kcov.size(); ++x) CHECK(kcov[x] == 1, (long long)x);
+  for (size_t x = 0; x < vcov.size(); ++x) CHECK(vcov[x] == 1, (long long)x);
+  for (int lane = 0; lane < 64; ++lane) {
+    const int half = lane >> 5, l32 = lane & 31;
+    // S^T = K Q^T: A row l32 = the stage's key l32; k-step s = d-elements [h D/2 + 8 s, +8)
+    for (int s = 0; s < G::DS; ++s) {
+      const uint32_t off = G::k_rd(l32, half, s);
+      CHECK(off % 16 == 0 && off + 16 <= (uint32_t)G::KB, lane, s);
+      const Gran& gr = map[off / 16];
+      CHECK(gr.kind == 0 && gr.a == l32 && gr.b == half * (D / 2) + 8 * s, lane, s);
+    }
+    // O^T += V^T P^T: element t of pb[jj] is P of register 8 jj + t; granule 2 jj + h of
+    // V^T row dt 32 + l32 must hold v of the same keys, in the stored token order.
+    for (int dt = 0; dt < G::DT; ++dt)
+      for (int jj = 0; jj < 2; ++jj) {
+        const uint32_t off = dt * 32 * G::VRB + G::v_rd(l32, 2 * jj + half);
+        CHECK(off % 16 == 0 && off >= (uint32_t)G::KB && off + 16 <= (uint32_t)G::SB, lane, dt, jj);
+        const Gran& gr = map[off / 16];
+        CHECK(gr.kind == 1 && gr.a == dt * 32 + l32, lane, dt, jj);
+        for (int t = 0; t < 8; ++t) {
+          const int key_v = up::attn::swap_bits23(gr.b + t);
+          const int key_p = up::attn::acc_key(0, 8 * jj + t, half);
+          CHECK(key_v == key_p, lane, dt, t);
+        }
+      }
+  }
+}
+
+template <int D>
+void part2_w4(int Hq, int Hkv, const std::vector<int>& lens) {
+  using G = up::attn::W4<D>;
+  const int B = (int)lens.size();
+  CHECK(Hq % Hkv == 0 && !up::attn::w8_serves(D, Hkv), Hq, Hkv);
+  const int gsz = Hq / Hkv;
+  const int HQ = gsz % 4 == 0 ? 4 : (gsz % 2 == 0 ? 2 : 1);
+  const int TT = 4 / HQ;
+  const int tok_tile = 32 * TT;
+  std::vector<int32_t> cu(B + 1, 0), po(B + 1, 0), tp(B + 1, 0);
+  for (int i = 0; i < B; ++i) {
+    cu[i + 1] = cu[i] + lens[i];
+    po[i + 1] = po[i] + (lens[i] + 63) / 64 * 64;
+    tp[i + 1] = tp[i] + (lens[i] + tok_tile - 1) / tok_tile;
+  }
+  const int64_t R = cu[B], Rp = po[B], tiles = tp[B];
+  const int gx = Hkv * (gsz / HQ);
+  const int64_t nq = (int64_t)Hq * Rp * D, nk = (int64_t)Hkv * Rp * D, nv = nk;
+  const int64_t nout = R * Hq * D;
+  int64_t klo = INT64_MAX, khi = INT64_MIN, vlo = INT64_MAX, vhi = INT64_MIN;
+  for (int tid = 0; tid < G::NT; ++tid) {
+    for (int q = 0; q < G::KSPT; ++q) {
+      const int64_t o = G::k_src(q, tid);
+      klo = std::min(klo, o);
+      khi = std::max(khi, o + 8);
+    }
+    for (int q = 0; q < G::VSPT; ++q) {
+      const int64_t o = G::v_src(q, tid, Rp);
+      vlo = std::min(vlo, o);
+      vhi = std::max(vhi, o + 8);
+    }
+  }
+  CHECK(klo == 0 && khi == 32LL * D, klo, khi);
+  CHECK(vlo == 0 && vhi == (int64_t)(D - 1) * Rp + 32, vlo, vhi);
+  std::vector<uint8_t> written((size_t)(R * Hq * (D / 4)), 0);
+  std::vector<int> slot_stage(G::NS), last_read, ready;
+  for (int by = 0; by < tiles; ++by)
+    for (int bx = 0; bx < gx; ++bx) {
+      const up::attn::Wg w = up::attn::wg_of(bx, by, Hq, Hkv, HQ, TT, B, cu.data(), po.data(),
+                                             tp.data(), up::attn::kSlotsAll, nullptr, 5);
+      CHECK(w.i >= 0 && w.i < B && lens[w.i] > 0, bx, by, w.i);
+      CHECK(by >= tp[w.i] && by < tp[w.i + 1], bx, by, w.i);
+      CHECK(w.g >= 0 && w.g < Hkv && w.quad >= 0 && w.quad < gsz / HQ, bx, by);
+      CHECK(w.nst >= 1 && w.nst <= w.ntile && w.tile0 < w.ntile, bx, by, w.nst);
+      CHECK(w.ntile == (lens[w.i] + 31) / 32, bx, by, w.ntile);
+      CHECK(w.pbase == po[w.i] && w.pbase % 64 == 0, bx, by);
+      const int nst = w.nst;
+      // every 32-key stage lies inside the request's padded rows and inside kr / vt
+      CHECK(w.pbase + 32LL * nst <= po[w.i + 1], bx, by, nst);
+      for (int st = 0; st < nst; ++st) {
+        const int64_t kb = up::attn::k_stage4<D>(w, st, Rp), vb = up::attn::v_stage4<D>(w, st, Rp);
+        CHECK(kb + klo >= 0 && kb + khi <= nk, bx, by, st);
+        CHECK(vb + vlo >= 0 && vb + vhi <= nv, bx, by, st);
+      }
+      up::attn::Wv wv[4];
+      for (int wave = 0; wave < 4; ++wave) {
+        wv[wave] = up::attn::wave4_of(w, wave, Hq, Hkv, HQ);
+        const up::attn::Wv& v = wv[wave];
+        CHECK(v.head >= w.g * gsz && v.head < (w.g + 1) * gsz, bx, by, wave);
+        CHECK(v.act == (v.tw < w.ntile), bx, by, wave);
+        if (!v.act) continue;
+        CHECK(v.tw < nst && v.tw >= w.tile0, bx, by, wave);
+        for (int lane = 0; lane < 64; ++lane) {
+          const int half = lane >> 5, l32 = lane & 31;
+          const int64_t qs = up::attn::q_src4<D>(w, v, l32, half, Rp);
+          CHECK(qs >= 0 && qs + D / 2 <= nq, bx, by, wave);
+          const int qtok = up::attn::query_token4(v, l32);
+          CHECK(w.pbase + qtok < po[w.i + 1], bx, by, qtok);
+          CHECK(32 * v.tw <= qtok && qtok < 32 * (v.tw + 1), bx, by, qtok);
+          if (qtok >= w.L) continue;
+          for (int dt = 0; dt < G::DT; ++dt)
+            for (int eg = 0; eg < 4; ++eg) {
+              const int dv = dt * 32 + 8 * eg + 4 * half;
+              const int64_t oi = up::attn::out_index4<D>(cu.data(), w, v, l32, Hq, dv);
+              CHECK(oi >= 0 && oi + 4 <= nout && oi % 4 == 0, bx, by, oi);
+              uint8_t& c = written[(size_t)(oi / 4)];
+              CHECK(c == 0, bx, by, oi);
+              c = 1;
+            }
+        }
+      }
+      // The ring in the kernel's program order (a stage is one 32-key half-step).
+      std::fill(slot_stage.begin(), slot_stage.end(), -1);
+      last_read.assign(nst, -1);
+      ready.assign(nst, -1);
+      int phase = 0;
+      std::vector<int> inflight;
+      auto issue = [&](int st) {
+        const int slot = st % G::NS;
+        const int old = slot_stage[slot];
+        if (old >= 0) CHECK(last_read[old] < phase, bx, by, st);
+        slot_stage[slot] = st;
+        inflight.push_back(st);
+      };
+      auto wait_barrier = [&](int n) {
+        CHECK(n % G::SPT == 0, n);
+        const size_t keep = (size_t)(n / G::SPT);
+        CHECK(inflight.size() >= keep, bx, by, n);
+        while (inflight.size() > keep) {
+          ready[inflight.front()] = phase + 1;
+          inflight.erase(inflight.begin());
+        }
+        ++phase;
+      };
+      auto read = [&](int st) {
+        CHECK(st >= 0 && st < nst, bx, by, st);
+        CHECK(slot_stage[st % G::NS] == st, bx, by, st);
+        CHECK(ready[st] >= 0 && ready[st] <= phase, bx, by, st);
+        if (phase > last_read[st]) last_read[st] = phase;
+      };
+      // sync_for(st): wait for stage st + 1 (st + 2 may stay in flight), barrier, refill
+      // the slot of stage st - 1 with stage st + 3.  (The statistics stores the kernel
+      // counts in the same wait are not stages: the wait still drains stage st + 1.)
+      auto sync_for = [&](int st) {
+        if (st + 1 >= nst) return;
+        if (st + 2 < nst) wait_barrier(G::SPT);
+        else wait_barrier(0);
+        if (st + 3 < nst) issue(st + 3);
+      };
+      issue(0);
+      if (nst > 1) issue(1);
+      if (nst > 2) issue(2);
+      if (nst > 2) wait_barrier(2 * G::SPT);
+      else if (nst > 1) wait_barrier(G::SPT);
+      else wait_barrier(0);
+      for (int wave = 0; wave < 4; ++wave)
+        if (wv[wave].act) read(0);
+      std::vector<int> pv_count(4, 0), s_count(4, 1);
+      auto body = [&](int wave, int hs) {
+        const up::attn::Wv& v = wv[wave];
+        if (!v.act || hs > v.tw) return;
+        if (hs + 1 <= v.tw) {
+          read(hs + 1);
+          s_count[wave]++;
+        }
+        read(hs);
+        pv_count[wave]++;
+      };
+      for (int st = 0; st < nst; st += 2) {
+        sync_for(st);
+        for (int wave = 0; wave < 4; ++wave) body(wave, st);
+        if (st + 1 < nst) {
+          sync_for(st + 1);
+          for (int wave = 0; wave < 4; ++wave) body(wave, st + 1);
+        }
+      }
+      CHECK(inflight.empty(), bx, by, (long long)inflight.size());
+      for (int wave = 0; wave < 4; ++wave)
+        if (wv[wave].act)
+          CHECK(pv_count[wave] == wv[wave].tw + 1 && s_count[wave] == wv[wave].tw + 1, bx, by,
+                wave);
+    }
+  for (size_t x = 0; x < written.size(); ++x) CHECK(written[x] == 1, (long long)x);
+  std::printf("launch (4-wave) D=%d Hq=%d Hkv=%d B=%d rows=%lld padded=%lld tiles=%lld grid=%dx%lld: ok\n",
+              D, Hq, Hkv, B, (long long)R, (long long)Rp, (long long)tiles, gx, (long long)tiles);
+}
+
 // Part 4 (with n): the two launches of up_rope_attention_scores.  For a workgroup tile
 // of tok_tile tokens, the window launch (slot layout kSlotsWindow) and the rest
 // (kSlotsRest) together cover every (request, slot) exactly once; the window launch
@@ -427,14 +647,25 @@ int main(int argc, char** argv) {
     const int HQ = gsz % 4 == 0 ? 4 : (gsz % 2 == 0 ? 2 : 1);
     part4(lens, n, tile * (4 / HQ));
   }
-  if (D == 64) {
-    part1<64>();
-    part2<64>(Hq, Hkv, lens);
+  if (up::attn::w8_serves(D, Hkv)) {
+    if (D == 64) {
+      part1<64>();
+      part2<64>(Hq, Hkv, lens);
+    } else {
+      part1<128>();
+      part2<128>(Hq, Hkv, lens);
+    }
+  } else if (D == 64) {
+    part1_w4<64>();
+    part2_w4<64>(Hq, Hkv, lens);
   } else if (D == 128) {
-    part1<128>();
-    part2<128>(Hq, Hkv, lens);
-  } else if (argc != 7) {
-    std::printf("the 8-wave kernel serves d = 64 and 128\n");
+    part1_w4<128>();
+    part2_w4<128>(Hq, Hkv, lens);
+  } else if (D == 256) {
+    part1_w4<256>();
+    part2_w4<256>(Hq, Hkv, lens);
+  } else {
+    std::printf("head dimensions are 64, 128 and 256\n");
     return 2;
   }
   std::printf("ok\n");

@@ -1,10 +1,12 @@
-"""CPU: host replay of the 8-wave attention kernel's addressing (tests/attn_replay.cpp,
-built here with g++ against the index functions the kernel itself calls,
-block_wise_token_amd/csrc/attn_geom.h).
+"""CPU: host replay of the attention kernels' addressing (tests/attn_replay.cpp, built
+here with g++ against the index functions the kernels themselves call,
+block_wise_token_amd/csrc/attn_geom.h): the 8-wave kernel (d = 64 and 128, up to 256 kv
+heads) and the 4-wave kernel (d = 256, and more kv heads).
 
 For every launch shape below -- the layer-on-the-survivors shapes of the 128K Llama
-decision (129,600 survivors and all 131,072 rows, Hq = 32, Hkv = 8, d = 128), the
-shapes the GPU attention tests launch at d = 64 and 128, and edge shapes -- the replay
+decision (129,600 survivors and all 131,072 rows, Hq = 32, Hkv = 8, d = 128) and of the
+Gemma-like d = 256 layer (129,344 and 131,072 rows, Hq = 16, Hkv = 8), every shape the
+GPU attention tests launch, and edge shapes -- the replay
 checks every copy, operand read, key-norm read and output store against its buffer,
 the ring's stage hand-over against the waits and barriers, the causal mask and the
 operand layouts, and that every output element is written once (the program's own
@@ -41,12 +43,12 @@ def _run(exe, d, Hq, Hkv, lengths, n=None, G=None):
 
 
 def _gpu_test_shapes():
-    """(lengths, Hq, Hkv, d) of the GPU attention tests that take the 8-wave kernel."""
+    """(lengths, Hq, Hkv, d) of every GPU attention test launch (either kernel)."""
     from tests import test_gpu_consumer as T
     shapes = [(c[0], c[1], c[2], c[3]) for c in T.CASES]
     shapes += [(c[0], c[1], c[2], c[3]) for c in T.RANDOM_ATTENTION]
     shapes += [([256], 8, 2, 128), ([1000, 37], 8, 2, 128)]
-    return [s for s in shapes if s[3] in (64, 128) and sum(s[0]) > 0]
+    return [s for s in shapes if sum(s[0]) > 0]
 
 
 @pytest.mark.parametrize("rows", [129600, 131072])
@@ -54,9 +56,15 @@ def test_replay_at_the_128k_layer_shapes(replay, rows):
     _run(replay, 128, 32, 8, [rows])
 
 
+@pytest.mark.parametrize("rows", [129344, 131072])
+def test_replay_at_the_gemma_like_d256_layer_shapes(replay, rows):
+    """The 4-wave kernel at the Gemma-like layer's shapes (d = 256, Hq = 16, Hkv = 8)."""
+    _run(replay, 256, 16, 8, [rows])
+
+
 def test_replay_of_the_gpu_test_shapes(replay):
     shapes = _gpu_test_shapes()
-    assert len(shapes) >= 10
+    assert len(shapes) >= 10 and any(s[3] == 256 for s in shapes)
     for lengths, Hq, Hkv, d in shapes:
         _run(replay, d, Hq, Hkv, lengths)
 
@@ -68,6 +76,11 @@ def test_replay_of_the_gpu_test_shapes(replay):
     ([8192, 16384, 65536, 24576, 49152, 32768, 12288, 12244], 32, 8, 128),   # varlen pack
     ([700, 1], 256, 256, 128),                       # the largest kv-head count served
     ([20000], 8, 1, 128),                            # MQA
+    ([1], 4, 2, 256),                                # the 4-wave kernel: one row
+    ([31, 32, 33, 95, 96, 97], 8, 8, 256),           # 32-token tile edges, 4 tiles per workgroup
+    ([0, 0, 5, 0], 12, 2, 256),                      # empty requests around one row, HQ = 2
+    ([700, 1], 512, 512, 128),                       # more kv heads than the 8-wave kernel serves
+    ([3000], 2048, 512, 64),                         # four query heads per kv head, 512 kv heads
 ])
 def test_replay_edge_shapes(replay, shape):
     lengths, Hq, Hkv, d = shape
