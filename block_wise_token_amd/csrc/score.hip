@@ -210,7 +210,12 @@ __device__ __forceinline__ int k_swizzle(int key) {
 // lane spends no vector instructions on 64-bit address arithmetic.  Issued from
 // inline assembly so that the compiler does not drain every outstanding load at the
 // next LDS read; completion is awaited explicitly (vmcnt) before the barrier that
-// publishes a stage.
+// publishes a stage.  NTL marks the copies non-temporal: the d = 256 pass reads twice
+// the key bytes per flop of d = 128, and with non-temporal copies its decision step is
+// faster (the pass 171-174 -> 139-140 us, the next compaction 293 -> 317 us, the step
+// 497 -> 489 us at 128K tokens); at d = 128 the same policy made the step slower, so
+// only the d = 256 instances take it.
+template <bool NTL = false>
 __device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t voff, uint32_t m0) {
   // readfirstlane returns a signed int: both halves go through uint32_t before they
   // are widened, so the low word is zero-extended, never sign-extended.
@@ -218,9 +223,14 @@ __device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t voff, uin
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   const uint64_t sa = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(reinterpret_cast<const void*>(sa)),
-               "{m0}"(m0)
-               : "memory");
+  if constexpr (NTL)
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(reinterpret_cast<const void*>(sa)),
+                 "{m0}"(m0)
+                 : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(reinterpret_cast<const void*>(sa)),
+                 "{m0}"(m0)
+                 : "memory");
 }
 
 // Wait until at most n vector-memory operations of this wave are outstanding and all
@@ -417,12 +427,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
     if (ks + UK <= pr.L) {
 #pragma unroll
       for (int q = 0; q < SPT; ++q)
-        lds_dma16_s(gb, dma_voff[q], __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
+        lds_dma16_s<D == 256>(gb, dma_voff[q], __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
     } else {
 #pragma unroll
       for (int q = 0; q < SPT; ++q) {
         const int kabs = min(ks + dma_key[q], pr.L - 1);
-        lds_dma16_s(gb, (uint32_t)(kabs - ks) * kstride2 + dma_gran[q],
+        lds_dma16_s<D == 256>(gb, (uint32_t)(kabs - ks) * kstride2 + dma_gran[q],
                     __builtin_amdgcn_readfirstlane(sbase + dma_loff[q]));
       }
     }
