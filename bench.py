@@ -257,7 +257,7 @@ def main():
     if not args.headline_only:
         result["tp8_share"] = tp_share_leg(up, torch, qwin, k, cu, b, args, s_us)
 
-    # What a plain device-to-device copy of the gather's row bytes reaches on this machine:
+    # What a plain device-to-device copy of the gather's row bytes reaches on this GPU:
     # the practical ceiling the gather's HBM fraction is read against.
     if not args.headline_only:
         result["copy_ceiling"] = copy_ceiling_leg(torch, kept * row_bytes, g_us, gather_bytes)
