@@ -236,7 +236,8 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, Lds& S) {
 //
 // FUSED (one request, NT = 256): the kernel also does the normalisation and the
 // block destinations of the compaction, so the decision needs neither the normalise
-// nor the block-destination launch.  It reads the float64 block masses, sums them in
+// nor the block-destination launch.  It reads the float64 partial block masses (each
+// block's partials summed over kv heads in order), sums them in
 // the order the normalise kernel uses (per thread over blocks tid, tid + 256, ...,
 // then the lanes by butterfly, then the four waves in order) so the float32 scores it
 // writes are bit-identical, selects on them, and writes each block's destination row,
@@ -268,14 +269,30 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
       }
       return;
     }
+    // Each block's partial masses (kv-head-major) summed over kv heads in order, as the
+    // normalisation sums them; the loads of four heads are in flight together.
     double mv[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) mv[q] = 0.0;
+    for (int g0 = 0; g0 < fd.parts; g0 += 4) {
+      double t[4][PER];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int64_t a = (int64_t)q * NT + tid;
+          t[gg][q] = (g0 + gg < fd.parts && a < nb_tot_host)
+                         ? fd.mass[(int64_t)(g0 + gg) * nb_tot_host + a] : 0.0;
+        }
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+          if (g0 + gg < fd.parts) mv[q] = (g0 + gg == 0) ? t[gg][q] : mv[q] + t[gg][q];
+    }
     double part = 0.0;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int64_t a = (int64_t)q * NT + tid;
-      mv[q] = a < nb_tot_host ? fd.mass[a] : 0.0;
-      part += mv[q];
-    }
+    for (int q = 0; q < PER; ++q) part += mv[q];
 #pragma unroll
     for (int dd = 32; dd > 0; dd >>= 1) part += __shfl_xor(part, dd);
     if (lane == 0) S.red64[wave] = part;
