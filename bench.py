@@ -454,7 +454,7 @@ def scores_in_attention_leg(up, torch, buf, b, pos_all, cu_all, cu_all_h, ws_att
     fused_us, fused = min((r[1] for r in runs), key=lambda x: x[0])
     sep_us, sep = timed(lambda: up.block_scores(qwin, k_, cu_all, cu_all_h, n, G, out=sc,
                                                 workspace=ws_bs),
-                        ("score_plan", "score_partial", "stats_mass", "normalize"))
+                        ("score_plan", "score_partial", "row_stats", "block_mass", "normalize"))
     return {"attention_call_us": round(plain_us, 1), "attention_with_scores_call_us":
             round(fused_us, 1), "extra_us": round(fused_us - plain_us, 1),
             "separate_score_pass_call_us": round(sep_us, 1),

@@ -11,11 +11,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libuniprefill.so")
 
 KERNEL_IDS = {
-    "score_partial": 0, "block_mass": 2, "normalize": 3, "select": 4,
+    "score_partial": 0, "row_stats": 1, "block_mass": 2, "normalize": 3, "select": 4,
     "select_finalize": 5, "block_dst": 6, "gather": 7, "compose": 8, "score_plan": 9,
     "score_partial_lse": 10, "lse_finalize": 11, "attn_plan": 12, "rope_layout": 13,
     "attention": 14, "swiglu": 15, "gemm": 16, "select_fused": 17, "attention_window": 18,
-    "stats_mass": 19,
 }
 
 _lib = None

@@ -185,15 +185,11 @@ int plan_scores(const int32_t* cu_h, int B, int Hq, int Hkv, int d, int n, int G
     t->ml_pairs += nb * Hkv * R;
     t->cs_pairs += nch * Hkv * R;
     t->pm_parts += nb * Hkv * nrt;
-    t->mass_items += (nb + kMassBlocks - 1) / kMassBlocks * Hkv;
     if (nb > t->nb_max) t->nb_max = (int32_t)nb;
   }
   t->T = B > 0 ? cu_h[B] : 0;
   t->rows = t->win_rows * Hq;
-  t->mass_parts = t->nb_tot * Hkv;
-  if (t->items >= (int64_t)1 << 31 || t->rows >= (int64_t)1 << 31 ||
-      t->mass_items >= (int64_t)1 << 31)
-    return UP_EUNSUPPORTED;
+  if (t->items >= (int64_t)1 << 31 || t->rows >= (int64_t)1 << 31) return UP_EUNSUPPORTED;
   if ((int64_t)t->win_rows * Hq * d >= ((int64_t)1 << 40)) return UP_EUNSUPPORTED;
   return UP_OK;
 }
@@ -244,7 +240,7 @@ int up_block_scores_chunks(const int32_t* cu_seqlens_h, int B, int Hq, int Hkv, 
   return UP_OK;
 }
 
-// stop_at_mass: leave the float64 partial block masses in the workspace and skip the
+// stop_at_mass: leave the float64 block masses in the workspace and skip the
 // normalisation (the fused decision normalises inside its select kernel).
 static int block_scores_common(const void* qwin, const void* k, const PagedK* paged,
                                const int32_t* cu_seqlens, const int32_t* cu_seqlens_h, int B,
@@ -280,10 +276,12 @@ static int block_scores_common(const void* qwin, const void* k, const PagedK* pa
     return launch_score_partial(qwin, k, s, t, workspace, L, c, paged ? &pk : nullptr, hs);
   });
   if (e != hipSuccess) return UP_EHIP;
-  e = timed(19, hs, [&] { return launch_stats_mass(s, t, workspace, L, row_lse, hs); });
+  e = timed(1, hs, [&] { return launch_row_stats(s, t, workspace, L, row_lse, hs); });
+  if (e != hipSuccess) return UP_EHIP;
+  e = timed(2, hs, [&] { return launch_block_mass(s, t, workspace, L, hs); });
   if (e != hipSuccess) return UP_EHIP;
   if (stop_at_mass) return UP_OK;
-  e = timed(3, hs, [&] { return launch_normalize(s, t, workspace, L, scores, true, hs); });
+  e = timed(3, hs, [&] { return launch_normalize(s, t, workspace, L, scores, hs); });
   if (e != hipSuccess) return UP_EHIP;
   return UP_OK;
 }
@@ -591,8 +589,7 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
   if (!err) return UP_EHIP;
   hipStream_t hs = as_stream(stream);
   FusedDecision fd;
-  fd.mass = reinterpret_cast<const double*>(static_cast<char*>(workspace) + LS.part);
-  fd.parts = Hkv;
+  fd.mass = reinterpret_cast<const double*>(static_cast<char*>(workspace) + LS.mass);
   fd.scores = scores;
   fd.shdr = static_cast<const WsHeader*>(workspace);
   fd.chdr = reinterpret_cast<WsHeader*>(cws + LC.hdr);
@@ -795,9 +792,9 @@ int up_rope_attention_scores(const void* q, const void* k, const void* v, const 
     }
     if (e != hipSuccess) return UP_EHIP;
   }
-  e = timed(2, hs, [&] { return launch_block_mass(s, t, sws, LS, hs); });
+  e = timed(2, hs, [&] { return launch_block_mass_pairs(s, t, sws, LS, hs); });
   if (e != hipSuccess) return UP_EHIP;
-  e = timed(3, hs, [&] { return launch_normalize(s, t, sws, LS, scores, false, hs); });
+  e = timed(3, hs, [&] { return launch_normalize(s, t, sws, LS, scores, hs); });
   return e == hipSuccess ? UP_OK : UP_EHIP;
 }
 

@@ -18,11 +18,12 @@
 //                            against the host-derived totals
 //   up_score_partial_kernel  Q K^T on bf16 MFMA (32x32x16), per-(row, block) (m_b, l_b)
 //                            and per-(row, key chunk) merged statistics
-//   up_stats_mass_kernel     merge chunk statistics into per-row (m, 1 / l) and sum the
-//                            per-(block, kv head) masses, float64 sums in a fixed order
+//   up_row_stats_kernel      merge chunk statistics into per-row (m, 1 / l), and each
+//                            (row, chunk)'s weight of its block sums
+//   up_block_mass_kernel     per-block mass, float64 sums in a fixed order
 //   up_normalize_kernel      per-request normalisation to scores that sum to one
-// (up_block_mass_kernel serves the attention's fused form, whose row statistics come
-// from the attention kernel itself.)
+// (up_block_mass_pairs_kernel serves the attention's fused form, whose row statistics
+// come from the attention kernel itself.)
 #include "up_dpp.h"
 #include "up_internal.h"
 
@@ -73,17 +74,17 @@ __global__ __launch_bounds__(kPlanThreads) void up_score_plan_kernel(
     const int32_t* __restrict__ cu, ScoreShape s, Totals host, WsHeader* __restrict__ hdr,
     ReqPlan* __restrict__ plan, int* __restrict__ err) {
   constexpr int NW = kPlanThreads / 64;
-  constexpr int NV = 7;   // scanned quantities: W, nb, items, ml, cs, pm, mass items
+  constexpr int NV = 6;   // scanned quantities: W, nb, items, ml, cs, pm
   __shared__ int64_t wtot[NV][NW];
   __shared__ int bad;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gs = s.Hq / s.Hkv;
   if (tid == 0) bad = cu[0] != 0;
   __syncthreads();
-  int64_t carry[NV] = {0, 0, 0, 0, 0, 0, 0};
+  int64_t carry[NV] = {0, 0, 0, 0, 0, 0};
   for (int base = 0; base < s.B; base += kPlanThreads) {
     const int i = base + tid;
-    int64_t v[NV] = {0, 0, 0, 0, 0, 0, 0};
+    int64_t v[NV] = {0, 0, 0, 0, 0, 0};
     ReqPlan p{};
     if (i < s.B) {
       const int32_t a = cu[i], b = cu[i + 1];
@@ -102,7 +103,6 @@ __global__ __launch_bounds__(kPlanThreads) void up_score_plan_kernel(
       v[3] = nb * s.Hkv * R;
       v[4] = nch * s.Hkv * R;
       v[5] = nb * s.Hkv * nrt;
-      v[6] = (nb + kMassBlocks - 1) / kMassBlocks * s.Hkv;
       p.tok_off = a; p.L = (int32_t)L; p.W = (int32_t)W; p.nb = (int32_t)nb;
       p.nch = (int32_t)nch; p.cbs = cbs; p.cps = cps;
     }
@@ -133,7 +133,6 @@ __global__ __launch_bounds__(kPlanThreads) void up_score_plan_kernel(
       p.ml_off = pre[3] + inc[3] - v[3];
       p.cs_off = pre[4] + inc[4] - v[4];
       p.pm_off = pre[5] + inc[5] - v[5];
-      p.mitem_end = (int32_t)(pre[6] + inc[6]);           // inclusive
       plan[i] = p;
     }
 #pragma unroll
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(kPlanThreads) void up_score_plan_kernel(
     const bool ok = !bad && (int64_t)cu[s.B] == host.T && carry[0] == host.win_rows &&
                     carry[1] == host.nb_tot && carry[2] == host.items &&
                     carry[3] == host.ml_pairs && carry[4] == host.cs_pairs &&
-                    carry[5] == host.pm_parts && carry[6] == host.mass_items;
+                    carry[5] == host.pm_parts;
     hdr->valid = ok ? 1 : 0;
     if (!ok) atomicOr(err, 1);
   }
@@ -723,232 +722,115 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void up_score_partial_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Row statistics and block masses in one launch.
+// Row statistics and chunk weights.
 //
 // The score kernel leaves, per (row, block), the block's sum l_b relative to the
 // reference of its statistics chunk (the chunk's final reference Rc, stored with the
-// chunk's statistics), except for the blocks that ended before a mid-chunk rebase,
-// whose reference is in mref; per (row, chunk) first_cur says which blocks those are.
-//
-// Workgroup = one (request, kv head g, mass item: kMassBlocks consecutive blocks of the
-// request).  It first merges, for every row r of kv head g's group, the row's statistics
-// chunks in chunk order into (M_r, 1 / L_r) -- each workgroup of the same (request, g)
-// repeats this small merge, which takes the place of a launch of its own -- and the
-// weight w_c(r) = 2^(Rc(r) - M_r) / L_r of every chunk c its blocks lie in; then, for
-// each of its blocks b, sums the terms l_b(r) w_c(r) over the group's rows: term in
-// float32, sum in float64 (each lane over its rows in order, then a butterfly over the
-// wave).  It writes one partial mass per (kv head, block); the normalisation sums a
-// block's partials over the kv heads in order.  Rows are taken in slabs whose
-// statistics and weights sit in LDS.
+// chunk's statistics), except for the blocks that ended before a mid-chunk rebase, whose
+// reference is in mref; per (row, chunk) first_cur says which blocks those are.  Here
+// every (request, kv head, row)'s chunks are merged into (M, 1 / L), and every (row,
+// chunk) gets the weight w = 2^(Rc - M) / L that turns its block sums into
+// probabilities: w = -1 - first_cur (negative) for a (row, chunk) with a mid-chunk
+// rebase, whose terms the block-mass kernel forms one by one.
+// Output layout: rs[win_off*Hq + g*R + r] (the request's Hq*W rows, g-major); the
+// weights in the chunk statistics' layout.
 // ---------------------------------------------------------------------------
-constexpr int kMassThreads = 1024;
-constexpr int kMassWaves = kMassThreads / 64;
-constexpr int kMassBpw = kMassBlocks / kMassWaves;   // blocks per wave
-constexpr int kMassSlab = 2048;                      // most rows per LDS slab
-constexpr int kMassWts = 12288;                      // LDS weights: slab rows x chunks
-constexpr int kMassPre = 2;        // 16-byte loads per lane and block issued up front
-constexpr int kMassCsUnroll = 8;   // chunk statistics per lane loaded together
-static_assert(kMassBlocks % kMassWaves == 0, "mass item split over the waves");
-static_assert(kMassWts >= 4 * kMassBlocks, "at least four rows per slab");
-
-// Number of requests whose stats-mass workgroups end at or before x (wave-wide ballot).
-__device__ __forceinline__ int request_of_mitem(const ReqPlan* __restrict__ plan, int B, int x) {
-  const int lane = threadIdx.x & 63;
-  int cnt = 0;
-  for (int base = 0; base < B; base += 64) {
-    const int i = base + lane;
-    const bool pred = (i < B) && (plan[i].mitem_end <= x);
-    cnt += __popcll(__ballot(pred));
+__device__ __forceinline__ int request_of_row(const ReqPlan* __restrict__ plan, int B, int Hq,
+                                              int64_t x) {
+  int lo = 0, hi = B;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)(plan[mid].win_off + plan[mid].W) * Hq <= x) lo = mid + 1; else hi = mid;
   }
-  return cnt;
+  return lo;
 }
 
-__global__ __launch_bounds__(kMassThreads) void up_stats_mass_kernel(
+// Workgroup = 64 rows (one per lane) x 16 waves; wave w merges chunks w, w+16, ...
+// of its lane's row, wave 0 merges the 16 partial results in wave order, then wave w
+// writes the weights of the same chunks.
+__global__ __launch_bounds__(1024) void up_row_stats_kernel(
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
-    int64_t nb_tot, const float2* __restrict__ cs, const int32_t* __restrict__ crb,
-    const float* __restrict__ ml, const float* __restrict__ mref, double* __restrict__ part,
-    float* __restrict__ row_lse) {
-  __shared__ __attribute__((aligned(16))) float2 rst[kMassSlab];   // (M_r, 1 / L_r)
-  // w_c(r) of the item's chunks, [chunk][slab row]; negative (-1 - first_cur) for a
-  // (row, chunk) with a mid-chunk rebase, whose terms are formed one by one.
-  __shared__ __attribute__((aligned(16))) float wts[kMassWts];
+    const float2* __restrict__ cs, const int32_t* __restrict__ crb, float2* __restrict__ rs,
+    float* __restrict__ wt, int64_t total_rows, float* __restrict__ row_lse) {
+  __shared__ float2 part[16][64];
   if (hdr->valid != 1) return;
-  const int x = blockIdx.x;
-  const int i = request_of_mitem(plan, B, x);
-  if (i >= B) return;
-  const ReqPlan pr = plan[i];
-  const int gs = Hq / Hkv;
-  const int R = gs * pr.W;
-  const int xl = x - (i > 0 ? plan[i - 1].mitem_end : 0);
-  const int g = xl % Hkv;
-  const int mi = xl / Hkv;
-  const int b0 = mi * kMassBlocks;
-  const int nbl = min(kMassBlocks, pr.nb - b0);   // blocks of this item, >= 1
-  const int cf = b0 / pr.cbs;                     // first chunk of the item
-  const int ncw = (b0 + nbl - 1) / pr.cbs - cf + 1;   // chunks of the item (<= kMassBlocks)
-  const int slab = min(kMassSlab, (kMassWts / ncw) & ~3);   // rows per slab, >= 4
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block indices in SGPRs
-  const int64_t cstep = (int64_t)Hkv * R;
-  const float2* csg = cs + pr.cs_off + (int64_t)g * R;   // chunk c at + c * cstep
-  const int32_t* crg = crb + pr.cs_off + (int64_t)g * R;
-  // Wave w sums blocks b0 + w + kMassWaves * u (request-relative bb[u], chunk slot
-  // cc[u], chunk-relative index jj[u]); the sums of block b start at mlb.
-  const float* mlb[kMassBpw];
-  bool has[kMassBpw];
-  int bb[kMassBpw], cc[kMassBpw], jj[kMassBpw];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t x = (int64_t)blockIdx.x * 64 + lane;
+  float M = kNegInf, S = 0.f;
+  int64_t lse_at = -1;   // the row's index in the [sum W, Hq] window-row layout
+  int64_t c0 = -1;       // the row's pair of chunk 0; chunk chk at c0 + chk * cstep
+  int64_t cstep = 0;
+  int nch = 0;
+  if (x < total_rows) {
+    const int i = request_of_row(plan, B, Hq, x);
+    if (i < B) {
+      const ReqPlan pr = plan[i];
+      const int gs = Hq / Hkv;
+      const int R = gs * pr.W;
+      const int64_t local = x - (int64_t)pr.win_off * Hq;   // = g*R + r
+      const int g = (int)(local / R), r = (int)(local % R);
+      lse_at = (int64_t)(pr.win_off + r / gs) * Hq + g * gs + r % gs;
+      c0 = pr.cs_off + (int64_t)g * R + r;
+      cstep = (int64_t)Hkv * R;
+      nch = pr.nch;
+      // chunks wave, wave + 16, ... in order; four loads in flight
+      int chk = wave;
+      for (; chk + 48 < nch; chk += 64) {
+        float2 v[4];
 #pragma unroll
-  for (int u = 0; u < kMassBpw; ++u) {
-    const int bl = wave + kMassWaves * u;
-    has[u] = bl < nbl;
-    bb[u] = b0 + (has[u] ? bl : 0);
-    cc[u] = bb[u] / pr.cbs - cf;
-    jj[u] = bb[u] - (cf + cc[u]) * pr.cbs;
-    mlb[u] = ml + pr.ml_off + ((int64_t)bb[u] * Hkv + g) * R;
-  }
-  // Four rows per 16-byte load when every block's run of sums is 16-byte aligned.
-  const bool vec = (R & 3) == 0 && (pr.ml_off & 3) == 0;
-  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  double acc[kMassBpw];
+        for (int q = 0; q < 4; ++q) v[q] = cs[c0 + (chk + 16 * q) * cstep];
 #pragma unroll
-  for (int u = 0; u < kMassBpw; ++u) acc[u] = 0.0;
-
-  // The first slab's loads of sums (kMassPre per lane and block: all of them for up to
-  // 256 * kMassPre rows) are issued first and stay in flight while the statistics merge.
-  float4 pre[kMassPre][kMassBpw];
-  {
-    const int nq0 = vec ? (min(slab, R) >> 2) : 0;   // 16-byte loads in slab 0
-#pragma unroll
-    for (int k = 0; k < kMassPre; ++k)
-#pragma unroll
-      for (int u = 0; u < kMassBpw; ++u)
-        pre[k][u] = (lane + 64 * k < nq0 && has[u])
-                        ? reinterpret_cast<const float4*>(mlb[u])[lane + 64 * k] : zero4;
-  }
-  const int nh0 = (pr.nch + 1) >> 1;
-  const int c_lo = (tid & 1) ? nh0 : 0, c_hi = (tid & 1) ? pr.nch : nh0;
-  for (int s0 = 0; s0 < R; s0 += slab) {
-    const int sn = min(slab, R - s0);
-    if (s0 > 0) __syncthreads();   // the previous slab's statistics are no longer read
-    // Lanes 2r and 2r + 1 merge the first and the second half of row r's chunks; both
-    // then combine the halves in that order (the same value in both lanes) and share
-    // the item's chunk weights.
-    for (int r2 = tid; r2 < 2 * sn; r2 += kMassThreads) {
-      const int r = r2 >> 1;
-      const float2* pc = csg + s0 + r;
-      float M = kNegInf, S = 0.f;
-      int chk = c_lo;
-      for (; chk + kMassCsUnroll <= c_hi; chk += kMassCsUnroll) {
-        float2 v[kMassCsUnroll];
-#pragma unroll
-        for (int q = 0; q < kMassCsUnroll; ++q) v[q] = pc[(int64_t)(chk + q) * cstep];
-#pragma unroll
-        for (int q = 0; q < kMassCsUnroll; ++q) merge_ml(M, S, v[q].x, v[q].y);
+        for (int q = 0; q < 4; ++q) merge_ml(M, S, v[q].x, v[q].y);
       }
-      for (; chk < c_hi; ++chk) {
-        const float2 v = pc[(int64_t)chk * cstep];
+      for (; chk < nch; chk += 16) {
+        const float2 v = cs[c0 + chk * cstep];
         merge_ml(M, S, v.x, v.y);
       }
-      const float Mo = __shfl_xor(M, 1), So = __shfl_xor(S, 1);
-      float Mt = (tid & 1) ? Mo : M, St = (tid & 1) ? So : S;   // first half
-      merge_ml(Mt, St, (tid & 1) ? M : Mo, (tid & 1) ? S : So);   // then the second
-      const float inv = St > 0.f ? 1.f / St : 0.f;
-      if ((tid & 1) == 0) {
-        rst[r] = make_float2(Mt, inv);
-        if (row_lse && mi == 0) {
-          // Natural-log log-sum-exp of the row's scaled logits: (M + log2 L) * ln 2.
-          const int rr = s0 + r;
-          row_lse[(int64_t)(pr.win_off + rr / gs) * Hq + g * gs + rr % gs] =
-              (Mt + log2f(St)) * 0.6931471805599453f;
-        }
-      }
-      for (int q = tid & 1; q < ncw; q += 2) {
-        const int64_t ci = (int64_t)(cf + q) * cstep + s0 + r;
-        const int fc = crg[ci];
-        wts[q * sn + r] = fc > 0 ? -1.f - (float)fc : fast_exp2(csg[ci].x - Mt) * inv;
-      }
-    }
-    // LDS writes done, then the workgroup barrier; loads of sums stay in flight.
-    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
-    // Terms with a non-negative weight, in row order; a (row, chunk) with a mid-chunk
-    // rebase contributes nothing here (its weight is clamped to 0) and is added after
-    // the slab's other terms, also in row order.
-    float wmin = 0.f;
-    if (vec) {
-      const int nq = sn >> 2;
-      int e = lane;
-      auto add4 = [&](int u, float4 v, int q) {
-        const float4 w = *reinterpret_cast<const float4*>(&wts[cc[u] * sn + 4 * q]);
-        wmin = fminf(wmin, fminf(fminf(w.x, w.y), fminf(w.z, w.w)));
-        acc[u] += (double)(v.x * fmaxf(w.x, 0.f));
-        acc[u] += (double)(v.y * fmaxf(w.y, 0.f));
-        acc[u] += (double)(v.z * fmaxf(w.z, 0.f));
-        acc[u] += (double)(v.w * fmaxf(w.w, 0.f));
-      };
-      if (s0 == 0) {
-#pragma unroll
-        for (int k = 0; k < kMassPre; ++k) {
-          if (e < nq) {
-#pragma unroll
-            for (int u = 0; u < kMassBpw; ++u)
-              if (has[u]) add4(u, pre[k][u], e);
-          }
-          e += 64;
-        }
-      }
-      for (; e < nq; e += 64) {
-        float4 v[kMassBpw];
-#pragma unroll
-        for (int u = 0; u < kMassBpw; ++u)
-          v[u] = has[u] ? reinterpret_cast<const float4*>(mlb[u] + s0)[e] : zero4;
-#pragma unroll
-        for (int u = 0; u < kMassBpw; ++u)
-          if (has[u]) add4(u, v[u], e);
-      }
-    } else {
-      for (int e = lane; e < sn; e += 64) {
-#pragma unroll
-        for (int u = 0; u < kMassBpw; ++u) {
-          if (!has[u]) continue;
-          const float w = wts[cc[u] * sn + e];
-          wmin = fminf(wmin, w);
-          acc[u] += (double)(mlb[u][s0 + e] * fmaxf(w, 0.f));
-        }
-      }
-    }
-    if (__ballot(wmin < 0.f) != 0) {   // wave-uniform, rare
-      for (int e = lane; e < sn; e += 64) {
-#pragma unroll 1
-        for (int u = 0; u < kMassBpw; ++u) {
-          if (!has[u]) continue;
-          const float w = wts[cc[u] * sn + e];
-          if (w >= 0.f) continue;
-          const int fc = (int)(-w) - 1;   // first block under the chunk's final reference
-          const int64_t at = (mlb[u] - ml) + s0 + e;
-          const float ref = jj[u] < fc ? mref[at] : csg[(int64_t)(cf + cc[u]) * cstep + s0 + e].x;
-          const float2 st = rst[e];
-          acc[u] += (double)(ml[at] * fast_exp2(ref - st.x) * st.y);
-        }
-      }
     }
   }
+  part[wave][lane] = make_float2(M, S);
+  __syncthreads();
+  if (wave == 0 && c0 >= 0) {
+    float Mt = kNegInf, St = 0.f;
+    for (int w = 0; w < 16; ++w) merge_ml(Mt, St, part[w][lane].x, part[w][lane].y);
+    const float2 st = make_float2(Mt, St > 0.f ? 1.f / St : 0.f);   // (row max, 1 / row sum)
+    rs[x] = st;
+    part[0][lane] = st;
+    // Natural-log log-sum-exp of the row's scaled logits: (M + log2 l) * ln 2.
+    if (row_lse) row_lse[lse_at] = (Mt + log2f(St)) * 0.6931471805599453f;
+  }
+  __syncthreads();
+  if (c0 >= 0) {
+    const float2 st = part[0][lane];
+    auto weight = [&](int fc, float rc) {
+      return fc > 0 ? -1.f - (float)fc : fast_exp2(rc - st.x) * st.y;
+    };
+    int chk = wave;
+    for (; chk + 48 < nch; chk += 64) {
+      int fc[4];
+      float rc[4];
 #pragma unroll
-  for (int u = 0; u < kMassBpw; ++u) {
-    double v = acc[u];
+      for (int q = 0; q < 4; ++q) {
+        fc[q] = crb[c0 + (chk + 16 * q) * cstep];
+        rc[q] = cs[c0 + (chk + 16 * q) * cstep].x;
+      }
 #pragma unroll
-    for (int dd = 32; dd > 0; dd >>= 1) v += __shfl_xor(v, dd);
-    // kv-head-major: part[g][global block]
-    if (lane == 0 && has[u]) part[(int64_t)g * nb_tot + pr.blk_off + bb[u]] = v;
+      for (int q = 0; q < 4; ++q) wt[c0 + (chk + 16 * q) * cstep] = weight(fc[q], rc[q]);
+    }
+    for (; chk < nch; chk += 16) {
+      const int64_t ci = c0 + chk * cstep;
+      wt[ci] = weight(crb[ci], cs[ci].x);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Block masses.  mass[b] = sum_{g, r} l_b * 2^(m_b - M) * (1 / l), where (M, 1 / l)
-// are the row's statistics: each term in float32, summed in float64 in a fixed
-// order.  One workgroup per global block.  (A last-workgroup-normalises variant
-// needs an agent-scope release per workgroup, an L2 writeback on every XCD, which
-// costs far more than the separate normalisation launch.)
+// Block masses.  mass[b] = sum_{g, r} l_b(r) w_c(r) over the block's Hq * W (row)
+// terms, c the block's statistics chunk: each term in float32, summed in float64 in a
+// fixed order (per thread over its terms, the terms of rebased (row, chunk)s after the
+// others, then the workgroup).  One workgroup per global block.  (A
+// last-workgroup-normalises variant needs an agent-scope release per workgroup, an L2
+// writeback on every XCD, which costs far more than the separate normalisation launch.)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int request_of_block(const ReqPlan* __restrict__ plan, int B,
                                                 int64_t x) {
@@ -973,6 +855,77 @@ __device__ __forceinline__ double wg256_sum_f64(double v, double* red) {
 }
 
 __global__ __launch_bounds__(256) void up_block_mass_kernel(
+    const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq,
+    const float* __restrict__ lb, const float* __restrict__ mref, const float* __restrict__ wt,
+    const float2* __restrict__ cs, const float2* __restrict__ rs, double* __restrict__ mass) {
+  __shared__ double red[4];
+  if (hdr->valid != 1) return;
+  const int64_t blk = blockIdx.x;
+  const int i = request_of_block(plan, B, blk);
+  if (i >= B) return;
+  const ReqPlan pr = plan[i];
+  const int64_t b = blk - pr.blk_off;
+  const int64_t c = b / pr.cbs;                    // the block's statistics chunk
+  const int j = (int)(b - c * pr.cbs);             // its index within the chunk
+  const int64_t terms = (int64_t)Hq * pr.W;        // Hkv * R
+  const int64_t lo = pr.ml_off + b * terms;        // the block's sums (and mref)
+  const int64_t wo = pr.cs_off + c * terms;        // its chunk's weights (and statistics)
+  const float* lrow = lb + lo;
+  const float* wrow = wt + wo;
+  constexpr int U = 4;
+  double acc = 0.0;
+  float wmin = 0.f;
+  if ((terms & 3) == 0 && ((lo | wo) & 3) == 0) {
+    // four terms per 16-byte load; thread t takes quads t, t + 256, ... in order
+    const float4* l4 = reinterpret_cast<const float4*>(lrow);
+    const float4* w4 = reinterpret_cast<const float4*>(wrow);
+    const int64_t quads = terms >> 2;
+    int64_t e = threadIdx.x;
+    auto add4 = [&](float4 l, float4 w) {
+      wmin = fminf(wmin, fminf(fminf(w.x, w.y), fminf(w.z, w.w)));
+      acc += (double)(l.x * fmaxf(w.x, 0.f));
+      acc += (double)(l.y * fmaxf(w.y, 0.f));
+      acc += (double)(l.z * fmaxf(w.z, 0.f));
+      acc += (double)(l.w * fmaxf(w.w, 0.f));
+    };
+    for (; e + (U - 1) * 256 < quads; e += U * 256) {
+      float4 v[U], w[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        v[u] = l4[e + u * 256];
+        w[u] = w4[e + u * 256];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) add4(v[u], w[u]);
+    }
+    for (; e < quads; e += 256) add4(l4[e], w4[e]);
+  } else {
+    for (int64_t e = threadIdx.x; e < terms; e += 256) {
+      const float w = wrow[e];
+      wmin = fminf(wmin, w);
+      acc += (double)(lrow[e] * fmaxf(w, 0.f));
+    }
+  }
+  if (__syncthreads_or(wmin < 0.f)) {
+    // Rows whose chunk had a mid-chunk rebase (rare): each term with the reference its
+    // block ended under, in the thread's order.
+    const float2* srow = rs + (int64_t)pr.win_off * Hq;
+    for (int64_t e = threadIdx.x; e < terms; e += 256) {
+      const float w = wrow[e];
+      if (!(w < 0.f)) continue;
+      const int fc = (int)(-w) - 1;   // first block under the chunk's final reference
+      const float ref = j < fc ? mref[lo + e] : cs[wo + e].x;
+      const float2 st = srow[e];
+      acc += (double)(lrow[e] * fast_exp2(ref - st.x) * st.y);
+    }
+  }
+  const double tot = wg256_sum_f64(acc, red);
+  if (threadIdx.x == 0) mass[blk] = tot;
+}
+
+// The attention's fused form: mass[b] = sum_{g, r} l_b * 2^(m_b - M) * (1 / l) from
+// (reference, sum) pairs per (row, block) and the row statistics (M, 1 / l).
+__global__ __launch_bounds__(256) void up_block_mass_pairs_kernel(
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq,
     const float2* __restrict__ ml, const float2* __restrict__ rs, double* __restrict__ mass) {
   __shared__ double red[4];
@@ -1035,28 +988,21 @@ __global__ __launch_bounds__(256) void up_block_mass_kernel(
 
 // ---------------------------------------------------------------------------
 // Normalise: scores[b] = mass[b] / sum of the request's masses.  One workgroup
-// per request; the sum has a fixed order.  A block's mass is the sum of its `parts`
-// partials in order (kv-head-major, [parts][nb_tot]: one per kv head from the
-// stats-mass kernel, or the block-mass kernel's single value).
+// per request; the sum has a fixed order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void up_normalize_kernel(
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B,
-    const double* __restrict__ mass, int parts, int64_t nb_tot, float* __restrict__ scores) {
+    const double* __restrict__ mass, float* __restrict__ scores) {
   __shared__ double red[4];
   if (hdr->valid != 1) return;
   const int i = blockIdx.x;
   if (i >= B) return;
   const ReqPlan pr = plan[i];
-  auto block_mass = [&](int64_t b) {
-    double v = mass[b];
-    for (int q = 1; q < parts; ++q) v += mass[(int64_t)q * nb_tot + b];
-    return v;
-  };
   double acc = 0.0;
-  for (int b = threadIdx.x; b < pr.nb; b += 256) acc += block_mass(pr.blk_off + b);
+  for (int b = threadIdx.x; b < pr.nb; b += 256) acc += mass[pr.blk_off + b];
   const double tot = wg256_sum_f64(acc, red);
   for (int b = threadIdx.x; b < pr.nb; b += 256)
-    scores[pr.blk_off + b] = (float)(block_mass(pr.blk_off + b) / tot);
+    scores[pr.blk_off + b] = (float)(mass[pr.blk_off + b] / tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -1121,9 +1067,9 @@ ScoreWs score_ws_layout(int B, const Totals& t) {
   L.ml = off;   off = align_up(off + (size_t)t.ml_pairs * sizeof(float2));
   L.cs = off;   off = align_up(off + (size_t)t.cs_pairs * sizeof(float2));
   L.crb = off;  off = align_up(off + (size_t)t.cs_pairs * sizeof(int32_t));
+  L.wt = off;   off = align_up(off + (size_t)t.cs_pairs * sizeof(float));
   L.rs = off;   off = align_up(off + (size_t)t.rows * sizeof(float2));
   L.mass = off; off = align_up(off + (size_t)t.nb_tot * sizeof(double));
-  L.part = off; off = align_up(off + (size_t)t.mass_parts * sizeof(double));
   L.total = off;
   return L;
 }
@@ -1224,24 +1170,39 @@ hipError_t launch_lse_finalize(const ScoreShape& s, const Totals& t, void* ws,
   return hipGetLastError();
 }
 
-hipError_t launch_stats_mass(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
-                             float* row_lse, hipStream_t st) {
-  if (t.mass_items == 0) return hipSuccess;
-  hipLaunchKernelGGL(up_stats_mass_kernel, dim3((unsigned)t.mass_items), dim3(kMassThreads), 0, st,
+hipError_t launch_row_stats(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
+                            float* row_lse, hipStream_t st) {
+  if (t.rows == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((t.rows + 63) / 64);
+  hipLaunchKernelGGL(up_row_stats_kernel, dim3(grid), dim3(1024), 0, st,
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq, s.Hkv,
-                     t.nb_tot, reinterpret_cast<const float2*>(wsb(ws) + L.cs),
+                     reinterpret_cast<const float2*>(wsb(ws) + L.cs),
                      reinterpret_cast<const int32_t*>(wsb(ws) + L.crb),
-                     reinterpret_cast<const float*>(wsb(ws) + L.ml),
-                     reinterpret_cast<const float*>(wsb(ws) + L.ml) + t.ml_pairs,
-                     reinterpret_cast<double*>(wsb(ws) + L.part), row_lse);
+                     reinterpret_cast<float2*>(wsb(ws) + L.rs),
+                     reinterpret_cast<float*>(wsb(ws) + L.wt), t.rows, row_lse);
   return hipGetLastError();
 }
 
 hipError_t launch_block_mass(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
                              hipStream_t st) {
   if (t.nb_tot == 0) return hipSuccess;
+  // the pair region holds the block sums in its first half and mref in its second
+  const float* lb = reinterpret_cast<const float*>(wsb(ws) + L.ml);
   hipLaunchKernelGGL(up_block_mass_kernel, dim3((unsigned)t.nb_tot), dim3(256), 0, st,
+                     reinterpret_cast<const WsHeader*>(wsb(ws)),
+                     reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq, lb,
+                     lb + t.ml_pairs, reinterpret_cast<const float*>(wsb(ws) + L.wt),
+                     reinterpret_cast<const float2*>(wsb(ws) + L.cs),
+                     reinterpret_cast<const float2*>(wsb(ws) + L.rs),
+                     reinterpret_cast<double*>(wsb(ws) + L.mass));
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mass_pairs(const ScoreShape& s, const Totals& t, void* ws,
+                                   const ScoreWs& L, hipStream_t st) {
+  if (t.nb_tot == 0) return hipSuccess;
+  hipLaunchKernelGGL(up_block_mass_pairs_kernel, dim3((unsigned)t.nb_tot), dim3(256), 0, st,
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B, s.Hq,
                      reinterpret_cast<const float2*>(wsb(ws) + L.ml),
@@ -1251,13 +1212,12 @@ hipError_t launch_block_mass(const ScoreShape& s, const Totals& t, void* ws, con
 }
 
 hipError_t launch_normalize(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
-                            float* scores, bool from_parts, hipStream_t st) {
+                            float* scores, hipStream_t st) {
   if (s.B == 0 || t.nb_tot == 0) return hipSuccess;
   hipLaunchKernelGGL(up_normalize_kernel, dim3(s.B), dim3(256), 0, st,
                      reinterpret_cast<const WsHeader*>(wsb(ws)),
                      reinterpret_cast<const ReqPlan*>(wsb(ws) + L.plan), s.B,
-                     reinterpret_cast<const double*>(wsb(ws) + (from_parts ? L.part : L.mass)),
-                     from_parts ? s.Hkv : 1, t.nb_tot, scores);
+                     reinterpret_cast<const double*>(wsb(ws) + L.mass), scores);
   return hipGetLastError();
 }
 

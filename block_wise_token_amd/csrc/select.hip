@@ -236,14 +236,13 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, Lds& S) {
 //
 // FUSED (one request, NT = 256): the kernel also does the normalisation and the
 // block destinations of the compaction, so the decision needs neither the normalise
-// nor the block-destination launch.  It reads the float64 partial block masses (each
-// block's partials summed over kv heads in order), sums them in
+// nor the block-destination launch.  It reads the float64 block masses, sums them in
 // the order the normalise kernel uses (per thread over blocks tid, tid + 256, ...,
 // then the lanes by butterfly, then the four waves in order) so the float32 scores it
 // writes are bit-identical, selects on them, and writes each block's destination row,
 // source row and length with the compaction header's valid flag.
-template <int NT, int PER, bool FUSED, int NL = NT>
-__global__ __launch_bounds__(NL) void up_select_kernel(
+template <int NT, int PER, bool FUSED>
+__global__ __launch_bounds__(NT) void up_select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ cu, int B, int n, int G,
     int mode, float p, int topk, int64_t T_host, int64_t nb_tot_host, int direct,
     uint8_t* __restrict__ keep, int32_t* __restrict__ cu_out, int* __restrict__ err,
@@ -251,8 +250,6 @@ __global__ __launch_bounds__(NL) void up_select_kernel(
   constexpr int NW = NT / 64;
   constexpr int MAXB = NT * PER;
   static_assert(PER >= 1 && PER <= kSelPer, "slots per thread");
-  static_assert(NL == NT || (FUSED && NL % NT == 0), "extra launch threads load masses only");
-  constexpr int PA = (MAXB + NL - 1) / NL;   // blocks per thread while all NL threads load
   __shared__ SelLds<NW> S;
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
@@ -271,66 +268,14 @@ __global__ __launch_bounds__(NL) void up_select_kernel(
       }
       return;
     }
-    // Each block's partial masses (kv-head-major) summed over kv heads in order, as the
-    // normalisation sums them; the loads of four heads are in flight together.
     double mv[PER];
-    if constexpr (NL > NT) {
-      // All NL threads sum the partials of blocks tid, tid + NL, ... into LDS (more loads
-      // in flight than NT threads hold); then the threads beyond NT leave and the others
-      // take their blocks' masses from LDS.  (A barrier counts the waves still running.)
-      __shared__ double smass[MAXB];
-      constexpr int GB = 8;   // kv heads whose loads are in flight together
-      for (int g0 = 0; g0 < fd.parts; g0 += GB) {
-        double t[GB][PA];
-#pragma unroll
-        for (int gg = 0; gg < GB; ++gg)
-#pragma unroll
-          for (int q = 0; q < PA; ++q) {
-            const int64_t a = (int64_t)q * NL + tid;
-            t[gg][q] = (g0 + gg < fd.parts && a < nb_tot_host)
-                           ? fd.mass[(int64_t)(g0 + gg) * nb_tot_host + a] : 0.0;
-          }
-#pragma unroll
-        for (int q = 0; q < PA; ++q) {
-          const int64_t a = (int64_t)q * NL + tid;
-          if (a >= MAXB) continue;
-          double m = g0 == 0 ? t[0][q] : smass[a] + t[0][q];
-#pragma unroll
-          for (int gg = 1; gg < GB; ++gg)
-            if (g0 + gg < fd.parts) m += t[gg][q];
-          smass[a] = m;
-        }
-      }
-      __syncthreads();
-      if (tid >= NT) return;
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const int64_t a = (int64_t)q * NT + tid;
-        mv[q] = a < nb_tot_host ? smass[a] : 0.0;
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < PER; ++q) mv[q] = 0.0;
-      for (int g0 = 0; g0 < fd.parts; g0 += 4) {
-        double t[4][PER];
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg)
-#pragma unroll
-          for (int q = 0; q < PER; ++q) {
-            const int64_t a = (int64_t)q * NT + tid;
-            t[gg][q] = (g0 + gg < fd.parts && a < nb_tot_host)
-                           ? fd.mass[(int64_t)(g0 + gg) * nb_tot_host + a] : 0.0;
-          }
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg)
-#pragma unroll
-          for (int q = 0; q < PER; ++q)
-            if (g0 + gg < fd.parts) mv[q] = (g0 + gg == 0) ? t[gg][q] : mv[q] + t[gg][q];
-      }
-    }
     double part = 0.0;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) part += mv[q];
+    for (int q = 0; q < PER; ++q) {
+      const int64_t a = (int64_t)q * NT + tid;
+      mv[q] = a < nb_tot_host ? fd.mass[a] : 0.0;
+      part += mv[q];
+    }
 #pragma unroll
     for (int dd = 32; dd > 0; dd >>= 1) part += __shfl_xor(part, dd);
     if (lane == 0) S.red64[wave] = part;
@@ -762,11 +707,10 @@ static void launch_select256(int per, int B, hipStream_t st, const float* scores
                              const int32_t* cu, int n, int G, int mode, float p, int topk,
                              int64_t T_host, int64_t nb_tot_host, int direct, uint8_t* keep,
                              int32_t* cu_out, int* err, const FusedDecision& fd) {
-  // The fused select of up to 2048 blocks loads its partial masses with 1024 threads.
-#define UP_SEL_LAUNCH(P)                                                                  \
-  hipLaunchKernelGGL((up_select_kernel<256, P, FUSED, (FUSED && P <= 8) ? 1024 : 256>),  \
-                     dim3(B), dim3((FUSED && P <= 8) ? 1024 : 256), 0, st, scores, cu, B, n, \
-                     G, mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out, err, fd)
+#define UP_SEL_LAUNCH(P)                                                                   \
+  hipLaunchKernelGGL((up_select_kernel<256, P, FUSED>), dim3(B), dim3(256), 0, st, scores, \
+                     cu, B, n, G, mode, p, topk, T_host, nb_tot_host, direct, keep, cu_out,  \
+                     err, fd)
   switch (per) {
     case 1: UP_SEL_LAUNCH(1); break;
     case 2: UP_SEL_LAUNCH(2); break;

@@ -28,7 +28,6 @@ struct ReqPlan {
   int32_t item_end;  // exclusive end of the request's work items of the score kernel
   int32_t cbs;       // blocks per statistics chunk (a function of this request alone)
   int32_t cps;       // statistics chunks per work item (load balance only)
-  int32_t mitem_end; // exclusive end of the request's workgroups of the stats-mass kernel
   int64_t ml_off;    // first (m, l) pair of the request: pairs are [nb][Hkv][R], R = gs * W
   int64_t cs_off;    // first chunk-statistics pair: [nch][Hkv][R]
   int64_t pm_off;    // first block partial of the given-lse pass: [Hkv * nrt][nb]
@@ -36,10 +35,6 @@ struct ReqPlan {
 
 // Largest work item (blocks per workgroup) of the score kernel.
 constexpr int kMaxChunkBlocks = 256;
-
-// Blocks per workgroup of the stats-mass kernel (row statistics and block masses in
-// one launch): one workgroup per (request, kv head, run of kMassBlocks blocks).
-constexpr int kMassBlocks = 64;
 
 // Statistics chunks.  The score kernel restarts each query's softmax reference at
 // the first key of every statistics chunk and stores one merged pair per (row,
@@ -101,8 +96,6 @@ struct Totals {
   int64_t ml_pairs;  // (m, l) pairs
   int64_t cs_pairs;  // chunk-statistics pairs
   int64_t pm_parts;  // block partials of the given-lse pass
-  int64_t mass_items;  // workgroups of the stats-mass kernel: Hkv * ceil(nb / kMassBlocks)
-  int64_t mass_parts;  // partial block masses: nb_tot * Hkv
   int32_t nb_max;    // largest per-request block count
 };
 
@@ -116,11 +109,10 @@ struct WsHeader {
 // ml: per (row, block) float32 block sums, then as many float32 references (mref) of
 // blocks that ended before a mid-chunk rebase -- or, for the attention's fused form,
 // (reference, sum) pairs; cs: per (row, chunk) statistics; crb: per (row, chunk) the
-// first block under the chunk's final reference; part: float64 partial block masses
-// [Hkv][nb_tot] of the stats-mass kernel; rs and mass: row statistics and block masses
-// of the attention's fused form.
+// first block under the chunk's final reference; wt: per (row, chunk) weight of the
+// chunk's block sums in the block masses; rs: per row (max, 1 / sum); mass: per block.
 struct ScoreWs {
-  size_t plan, ml, cs, crb, rs, mass, part, total;
+  size_t plan, ml, cs, crb, wt, rs, mass, total;
 };
 
 ScoreWs score_ws_layout(int B, const Totals& t);
@@ -148,10 +140,10 @@ struct PagedK {
 hipError_t launch_score_partial(const void* qwin, const void* k, const ScoreShape& s,
                                 const Totals& t, void* ws, const ScoreWs& L, float c_log2,
                                 const PagedK* paged, hipStream_t st);
-// Row statistics and per-(block, kv head) partial masses from the score kernel's
-// statistics, in one launch (row_lse: optional natural-log log-sum-exp per window row).
-hipError_t launch_stats_mass(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
-                             float* row_lse, hipStream_t st);
+// Row statistics (and each (row, chunk)'s weight) from the score kernel's chunk
+// statistics (row_lse: optional natural-log log-sum-exp per window row).
+hipError_t launch_row_stats(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
+                            float* row_lse, hipStream_t st);
 // The given-lse pass: row_lse [sum W_i, Hq] natural-log log-sum-exp of each window row;
 // paged == nullptr: contiguous k, as for launch_score_partial.
 hipError_t launch_score_partial_lse(const void* qwin, const void* k, const float* row_lse,
@@ -160,12 +152,14 @@ hipError_t launch_score_partial_lse(const void* qwin, const void* k, const float
                                     hipStream_t st);
 hipError_t launch_lse_finalize(const ScoreShape& s, const Totals& t, void* ws,
                                const ScoreLseWs& L, float* scores, hipStream_t st);
+// Block masses of the score pass (block sums and chunk weights) ...
 hipError_t launch_block_mass(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
                              hipStream_t st);
-// from_parts: the masses are the stats-mass kernel's partials, summed over kv heads in
-// order; otherwise the block-mass kernel's masses.
+// ... and of the attention's fused form ((reference, sum) pairs and row statistics).
+hipError_t launch_block_mass_pairs(const ScoreShape& s, const Totals& t, void* ws,
+                                   const ScoreWs& L, hipStream_t st);
 hipError_t launch_normalize(const ScoreShape& s, const Totals& t, void* ws, const ScoreWs& L,
-                            float* scores, bool from_parts, hipStream_t st);
+                            float* scores, hipStream_t st);
 
 // Selection (select.hip).  mode 0: Top-p with threshold p; mode 1: Top-k with k = topk.
 constexpr int kSelectMaxBlocks = 16384;
@@ -176,8 +170,7 @@ hipError_t launch_select_finalize(int32_t* cu_out, int B, hipStream_t st);
 // The fused form of select for one request of at most 4096 blocks: masses in,
 // normalised scores, keep flags, cu_out and the compaction's block destinations out.
 struct FusedDecision {
-  const double* mass = nullptr;    // float64 partial block masses [parts][nb] of the score pass
-  int parts = 1;                   // partials per block, summed in order
+  const double* mass = nullptr;    // float64 block masses of the score pass
   float* scores = nullptr;         // normalised scores (output)
   const WsHeader* shdr = nullptr;  // score workspace header
   WsHeader* chdr = nullptr;        // compaction workspace header (written)
