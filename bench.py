@@ -187,8 +187,9 @@ def main():
                        "kernel": "up_score_partial_kernel", "avg_us": round(s_us, 2),
                        "flop_per_byte": round(score_flops / score_bytes, 1),
                        "variant": "one pass: a single Q K^T over the causal keys keeps a "
-                                  "per-(row, block) reference and sum; row statistics and "
-                                  "block masses follow from them (no second Q K^T)"})
+                                  "per-(row, block) sum relative to its statistics chunk's "
+                                  "reference; row statistics and block masses follow from "
+                                  "them (no second Q K^T)"})
     roof_gather = {"bound": "hbm", "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
                    "traffic": measured_traffic(args.workload, GATHER_KERNEL),
