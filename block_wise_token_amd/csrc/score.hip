@@ -16,7 +16,7 @@
 // Kernels (all launched on the caller's stream, in this order):
 //   up_score_plan_kernel     per-request offsets from the device cu_seqlens, checked
 //                            against the host-derived totals
-//   up_score_partial_kernel  Q K^T on bf16 MFMA (32x32x16), per-(row, block) (m_b, l_b)
+//   up_score_partial_kernel  Q K^T on bf16 MFMA (32x32x16), per-(row, block) block sums
 //                            and per-(row, key chunk) merged statistics
 //   up_row_stats_kernel      merge chunk statistics into per-row (m, 1 / l), and each
 //                            (row, chunk)'s weight of its block sums
