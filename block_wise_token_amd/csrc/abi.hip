@@ -537,7 +537,8 @@ size_t up_layer_decision_workspace(const int32_t* cu_seqlens_h, int B, int Hq, i
   Totals t;
   if (plan_scores(cu_seqlens_h, B, Hq, Hkv, d, n, G, &s, &t) != UP_OK) return 0;
   const SelPlan sp = sel_plan(cu_seqlens_h, B, G);
-  return score_ws_layout(B, t).total + compact_ws_layout(sp.nb_tot).total;
+  return score_ws_layout(B, t).total + compact_ws_layout(sp.nb_tot).total +
+         align_up((size_t)sp.nb_tot * sizeof(int32_t));
 }
 
 int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens,
@@ -557,7 +558,10 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
   if (B == 0) return UP_OK;
   const ScoreWs LS = score_ws_layout(B, t);
   const CompactWs LC = compact_ws_layout(sp.nb_tot);
-  if (!workspace || workspace_bytes < LS.total + LC.total || !aligned(workspace, kWsAlign))
+  // After the score and compaction workspaces: the fused select's per-block request index.
+  const size_t rq_bytes = align_up((size_t)sp.nb_tot * sizeof(int32_t));
+  if (!workspace || workspace_bytes < LS.total + LC.total + rq_bytes ||
+      !aligned(workspace, kWsAlign))
     return UP_EWORKSPACE;
   // With every request empty (T = 0) only cu_seqlens and cu_seqlens_out hold data; the
   // other buffers have no elements and may be NULL, as in the separate calls.
@@ -568,10 +572,11 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
   const int64_t row_bytes = (int64_t)H * elem_bytes;
   if (sp.T > 0 && sp.T * row_bytes / row_bytes != sp.T) return UP_EUNSUPPORTED;
   char* cws = static_cast<char*>(workspace) + LS.total;
-  // One request of at most 4096 blocks has its normalisation and block destinations
-  // done inside the select kernel (kFusedSelect): the score pass stops at the float64
-  // masses and the normalise and block-destination launches are not needed.
-  if (!kFusedSelect || B != 1 || t.T == 0 || sp.nb_tot > kFusedSelectMaxBlocks) {
+  // Requests of at most 4096 blocks each have their normalisation and block
+  // destinations done inside the select kernel (kFusedSelect; several requests also take
+  // the fused finalize): the score pass stops at the float64 masses and the normalise
+  // and block-destination launches are not needed.
+  if (!kFusedSelect || t.T == 0 || sp.nb_max > kFusedSelectMaxBlocks) {
     st = block_scores_common(qwin, k, nullptr, cu_seqlens, cu_seqlens_h, B, Hq, Hkv, d, n, G,
                              scale, scores, nullptr, workspace, LS.total, stream);
     if (st != UP_OK) return st;
@@ -590,6 +595,8 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
   hipStream_t hs = as_stream(stream);
   FusedDecision fd;
   fd.mass = reinterpret_cast<const double*>(static_cast<char*>(workspace) + LS.mass);
+  fd.splan = reinterpret_cast<const ReqPlan*>(static_cast<char*>(workspace) + LS.plan);
+  fd.rq = reinterpret_cast<int32_t*>(cws + LC.total);
   fd.scores = scores;
   fd.shdr = static_cast<const WsHeader*>(workspace);
   fd.chdr = reinterpret_cast<WsHeader*>(cws + LC.hdr);
@@ -597,8 +604,8 @@ int up_layer_decision(const void* qwin, const void* k, const int32_t* cu_seqlens
   fd.src = reinterpret_cast<int32_t*>(cws + LC.src);
   fd.len = reinterpret_cast<int32_t*>(cws + LC.len);
   hipError_t e = timed(17, hs, [&] {
-    return launch_select_fused(cu_seqlens, n, G, p, sp.T, sp.nb_tot, keep_blocks, cu_seqlens_out,
-                               err, fd, hs);
+    return launch_select_fused(cu_seqlens, B, n, G, p, sp.nb_max, sp.T, sp.nb_tot, keep_blocks,
+                               cu_seqlens_out, err, fd, hs);
   });
   if (e != hipSuccess) return UP_EHIP;
   e = timed(7, hs, [&] {

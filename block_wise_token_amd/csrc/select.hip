@@ -262,18 +262,29 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
   if constexpr (FUSED) {
     if (fd.shdr->valid != 1) {   // the score pass did not run: no masses to select on
       if (tid == 0) {
-        fd.chdr->valid = 0;
-        cu_out[0] = 0;
-        cu_out[1] = 0;
+        if (direct) {
+          fd.chdr->valid = 0;
+          cu_out[0] = 0;
+          cu_out[1] = 0;
+        } else {
+          cu_out[i + 1] = -1;   // the fused finalize then writes nothing
+        }
       }
       return;
+    }
+    // One request: its blocks start at 0, host's count.  Several: the score plan's
+    // offsets (valid: the header says the plan matches the host totals).
+    int64_t mnb = nb_tot_host;
+    if (!direct) {
+      blk_off = fd.splan[i].blk_off;
+      mnb = fd.splan[i].nb;
     }
     double mv[PER];
     double part = 0.0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int64_t a = (int64_t)q * NT + tid;
-      mv[q] = a < nb_tot_host ? fd.mass[a] : 0.0;
+      mv[q] = a < mnb ? fd.mass[blk_off + a] : 0.0;
       part += mv[q];
     }
 #pragma unroll
@@ -284,9 +295,9 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int64_t a = (int64_t)q * NT + tid;
-      if (a < nb_tot_host) {
+      if (a < mnb) {
         const float sc = (float)(mv[q] / tot);
-        fd.scores[a] = sc;
+        fd.scores[blk_off + a] = sc;
         u[q] = __float_as_uint(sc);
       } else {
         u[q] = kAbsent;
@@ -307,20 +318,21 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
     }
     blk_off = block_sum_i64<NW>(part, S);
   }
-  const int64_t L = (int64_t)cu[i + 1] - cu[i];
+  const int64_t cu_lo = cu[i];
+  const int64_t L = (int64_t)cu[i + 1] - cu_lo;
   const int64_t nb = L > 0 ? (L + G - 1) / G : 0;
   const bool bad = (L < 0) || ((int64_t)cu[B] != T_host) || (blk_off + nb > nb_tot_host) ||
                    (nb > MAXB) || (cu[0] != 0);
   if (bad) {
     if (tid == 0) {
       atomicOr(err, 1);
-      cu_out[i + 1] = 0;
+      cu_out[i + 1] = (FUSED && !direct) ? -1 : 0;
       if (direct) cu_out[0] = 0;
-      if constexpr (FUSED) fd.chdr->valid = 0;
+      if (FUSED && direct) fd.chdr->valid = 0;
     }
     return;
   }
-  if (!direct) {
+  if (!direct && !FUSED) {
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int64_t a = (int64_t)q * NT + tid;
@@ -555,12 +567,14 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
       }
       const int64_t b = (int64_t)q * NT + tid;
       if (b < nb) {
+        // Relative to the request's first output row (one request: absolute).
         const int64_t dd = pre + (int64_t)(incl[q] - kl[q]);
         // A kept run must lie inside the kept-token count (which is at most T).
         if (kl[q] && (dd < 0 || dd + kl[q] > total)) dst_bad = true;
-        fd.dst[b] = kl[q] ? (int32_t)dd : -1;
-        fd.src[b] = (int32_t)(b * G);
-        fd.len[b] = (int32_t)((L - b * G) < G ? (L - b * G) : G);
+        fd.dst[blk_off + b] = kl[q] ? (int32_t)dd : -1;
+        fd.src[blk_off + b] = (int32_t)(cu_lo + b * G);
+        fd.len[blk_off + b] = (int32_t)((L - b * G) < G ? (L - b * G) : G);
+        if (!direct) fd.rq[blk_off + b] = i;
       }
       before += slot;
     }
@@ -569,7 +583,11 @@ __global__ __launch_bounds__(NT) void up_select_kernel(
     const int64_t nbad = block_sum_i64<NW>((dst_bad || before != total) ? 1 : 0, S);
     if (tid == 0) {
       const bool ok = nbad == 0 && total <= T_host;
-      fd.chdr->valid = ok ? 1 : 0;
+      if (direct) {
+        fd.chdr->valid = ok ? 1 : 0;
+      } else if (!ok) {
+        cu_out[i + 1] = -1;   // the fused finalize refuses the batch
+      }
       if (!ok) atomicOr(err, 1);
     }
   }
@@ -694,6 +712,68 @@ __global__ __launch_bounds__(1024) void up_select_finalize_kernel(int32_t* __res
   }
 }
 
+// The fused decision over several requests: scan the per-request kept counts the
+// select workgroups left in cu_out[1..B] into cu_seqlens_out, then make every kept
+// block's destination absolute (its request's first output row plus its destination
+// within the request) and write the compaction header.  A request whose checks failed
+// left -1: then cu_seqlens_out is all zeros and the header invalid (the gather moves
+// nothing).
+__global__ __launch_bounds__(1024) void up_select_finalize_fused_kernel(
+    int32_t* __restrict__ cu_out, int B, int64_t T_host, int64_t nb_tot_host, int* __restrict__ err,
+    FusedDecision fd) {
+  __shared__ int64_t buf[1024];
+  __shared__ int64_t carry;
+  __shared__ int bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    carry = 0;
+    bad = 0;
+    cu_out[0] = 0;   // request 0's first output row (read below)
+  }
+  __syncthreads();
+  for (int base = 0; base < B; base += 1024) {
+    const int idx = base + tid;
+    const int64_t c = idx < B ? cu_out[idx + 1] : 0;
+    if (c < 0) atomicOr(&bad, 1);
+    buf[tid] = c < 0 ? 0 : c;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int64_t v = tid >= d ? buf[tid - d] : 0;
+      __syncthreads();
+      buf[tid] += v;
+      __syncthreads();
+    }
+    if (idx < B) cu_out[idx + 1] = (int32_t)(carry + buf[tid]);
+    __syncthreads();
+    if (tid == 1023) carry += buf[1023];
+    __syncthreads();
+  }
+  const int64_t total = carry;
+  const bool ok_counts = !bad && total <= T_host;
+  // Absolute destinations; a run must fit inside the kept count.
+  bool run_bad = false;
+  if (ok_counts) {
+    for (int64_t b = tid; b < nb_tot_host; b += 1024) {
+      const int32_t d = fd.dst[b];
+      if (d < 0) continue;
+      const int r = fd.rq[b];
+      if (r < 0 || r >= B) { run_bad = true; continue; }
+      const int64_t ad = (int64_t)cu_out[r] + d;
+      if (ad + fd.len[b] > total) run_bad = true;
+      fd.dst[b] = (int32_t)ad;
+    }
+  }
+  const int any = __syncthreads_or(run_bad ? 1 : 0);
+  const bool ok = ok_counts && !any;
+  if (!ok) {
+    for (int idx = tid; idx <= B; idx += 1024) cu_out[idx] = 0;
+  }
+  if (tid == 0) {
+    fd.chdr->valid = ok ? 1 : 0;
+    if (!ok) atomicOr(err, 1);
+  }
+}
+
 // Slots per thread of a 256-thread select for a request of nb blocks: the fewest of
 // 1, 2, 4, 8, 16 that hold it (nb <= 256 * kSelPer).
 static int sel_slots(int64_t nb) {
@@ -742,13 +822,17 @@ hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, i
   return hipGetLastError();
 }
 
-hipError_t launch_select_fused(const int32_t* cu, int n, int G, float p, int64_t T_host,
-                               int64_t nb_tot_host, uint8_t* keep, int32_t* cu_out, int* err,
-                               const FusedDecision& fd, hipStream_t st) {
+hipError_t launch_select_fused(const int32_t* cu, int B, int n, int G, float p, int nb_max,
+                               int64_t T_host, int64_t nb_tot_host, uint8_t* keep,
+                               int32_t* cu_out, int* err, const FusedDecision& fd,
+                               hipStream_t st) {
   static_assert(kFusedSelectMaxBlocks <= 256 * kSelPer, "fused select slots");
-  if (nb_tot_host > kFusedSelectMaxBlocks) return hipErrorInvalidValue;
-  launch_select256<true>(sel_slots(nb_tot_host), 1, st, nullptr, cu, n, G, 0, p, 0, T_host,
-                         nb_tot_host, 1, keep, cu_out, err, fd);
+  if (B < 1 || nb_max > kFusedSelectMaxBlocks) return hipErrorInvalidValue;
+  launch_select256<true>(sel_slots(nb_max), B, st, nullptr, cu, n, G, 0, p, 0, T_host,
+                         nb_tot_host, B == 1 ? 1 : 0, keep, cu_out, err, fd);
+  if (B > 1)
+    hipLaunchKernelGGL(up_select_finalize_fused_kernel, dim3(1), dim3(1024), 0, st, cu_out, B,
+                       T_host, nb_tot_host, err, fd);
   return hipGetLastError();
 }
 

@@ -167,24 +167,32 @@ hipError_t launch_select(const float* scores, const int32_t* cu, int B, int n, i
                          float p, int topk, int nb_max, int64_t T_host, int64_t nb_tot_host,
                          uint8_t* keep, int32_t* cu_out, int* err, hipStream_t st);
 hipError_t launch_select_finalize(int32_t* cu_out, int B, hipStream_t st);
-// The fused form of select for one request of at most 4096 blocks: masses in,
-// normalised scores, keep flags, cu_out and the compaction's block destinations out.
+// The fused form of select for requests of at most 4096 blocks: masses in, normalised
+// scores, keep flags, cu_out and the compaction's block destinations out.  One request:
+// the select kernel writes everything, absolute destinations and the compaction
+// header included.  Several: each request's workgroup writes its kept count to
+// cu_out[i + 1] (-1 if its checks failed), destinations relative to the request's first
+// output row and the request index of each block; the fused finalize kernel then scans
+// the counts, makes the destinations absolute and writes the header.
 struct FusedDecision {
   const double* mass = nullptr;    // float64 block masses of the score pass
   float* scores = nullptr;         // normalised scores (output)
   const WsHeader* shdr = nullptr;  // score workspace header
+  const ReqPlan* splan = nullptr;  // score pass plan (several requests)
   WsHeader* chdr = nullptr;        // compaction workspace header (written)
   int32_t* dst = nullptr;          // per block: destination row or -1
   int32_t* src = nullptr;          // per block: first source row
   int32_t* len = nullptr;          // per block: rows
+  int32_t* rq = nullptr;           // per block: its request (several requests)
 };
 constexpr int kFusedSelectMaxBlocks = 4096;
-// Whether up_layer_decision uses the fused select for one request of at most
+// Whether up_layer_decision uses the fused select when no request has more than
 // kFusedSelectMaxBlocks blocks.
 constexpr bool kFusedSelect = true;
-hipError_t launch_select_fused(const int32_t* cu, int n, int G, float p, int64_t T_host,
-                               int64_t nb_tot_host, uint8_t* keep, int32_t* cu_out, int* err,
-                               const FusedDecision& fd, hipStream_t st);
+hipError_t launch_select_fused(const int32_t* cu, int B, int n, int G, float p, int nb_max,
+                               int64_t T_host, int64_t nb_tot_host, uint8_t* keep,
+                               int32_t* cu_out, int* err, const FusedDecision& fd,
+                               hipStream_t st);
 
 // Expand + compact (compact.hip).
 struct CompactWs {

@@ -268,7 +268,7 @@ int up_compose_drops(const int32_t* prev_orig, int prev_len, const int32_t* idx,
  *
  * The decision of up_block_scores + up_topp_select + up_expand_compact (with the
  * drop composition when prev_orig / orig_out are given), with the same arguments,
- * outputs and results, bit for bit.  For one request of at most 4096 blocks the
+ * outputs and results, bit for bit.  When no request has more than 4096 blocks the
  * select kernel also normalises the block masses and assigns the compaction's block
  * destinations (two launches fewer); otherwise the three calls run in sequence.
  * When every request is empty (T = 0) only cu_seqlens_out is written (all zeros); the

@@ -335,11 +335,13 @@ def test_layer_decision_workspace_and_arguments(L):
     f.restype = ctypes.c_size_t
     cu = _cu([131072])
     ws = f(_p(cu), 1, 32, 8, 128, 128, 64)
-    # the score workspace plus the compaction workspace
+    # the score workspace, the compaction workspace and one int32 per block (the fused
+    # select's request index), 256-byte aligned
     L.up_block_scores_workspace.restype = ctypes.c_size_t
     L.up_expand_compact_workspace.restype = ctypes.c_size_t
+    nb = 131072 // 64
     parts = (L.up_block_scores_workspace(_p(cu), 1, 32, 8, 128, 128, 64) +
-             L.up_expand_compact_workspace(_p(cu), 1, 64))
+             L.up_expand_compact_workspace(_p(cu), 1, 64) + (nb * 4 + 255) // 256 * 256)
     assert ws == parts and ws % 256 == 0
     assert f(_p(cu), 1, 32, 8, 96, 128, 64) == 0      # d unsupported
     a = L.up_layer_decision

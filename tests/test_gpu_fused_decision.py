@@ -1,10 +1,11 @@
 """GPU: up_layer_decision (the whole decision in one call) against the three separate
 calls on the same inputs: every output must be bit-identical (scores, keep flags,
-cu_seqlens_out, indices, rows, positions, composed original indices).  For one
-request of at most 4096 blocks the one call normalises and assigns block destinations
-inside the select kernel (the fused path); otherwise it makes the three calls.  (The
-other GPU tests reach the one call through LayerDecision and compare it with the
-oracle.)"""
+cu_seqlens_out, indices, rows, positions, composed original indices).  When no request
+has more than 4096 blocks the one call normalises and assigns block destinations
+inside the select kernel (the fused path; several requests also take a finalize
+launch that scans the kept counts and makes the destinations absolute); otherwise it
+makes the three calls.  (The other GPU tests reach the one call through LayerDecision
+and compare it with the oracle.)"""
 import numpy as np
 import pytest
 import torch
@@ -64,18 +65,26 @@ CASES = [
     ([262144], 8, 2, 64, 128, 64, 0.95, False),       # exactly 4096 blocks: the fused limit
     ([262208], 8, 2, 64, 128, 64, 0.95, False),       # 4097 blocks: the separate calls
     ([129, 0, 3000, 64, 1], 8, 2, 128, 128, 64, 0.97, False),   # several requests
+    ([262144, 700, 0, 9000], 8, 2, 64, 128, 64, 0.95, False),   # 4096 blocks beside others
+    ([262208, 700, 9000], 8, 2, 64, 128, 64, 0.95, False),      # one of 4097: separate calls
+    ([40000, 40000, 12345], 8, 2, 64, 128, 64, 0.99, True),     # ties, several requests
+    ([0, 0, 5000, 0], 4, 2, 64, 128, 64, 0.9, False),           # empty requests around one
+    (list(np.random.default_rng(77).integers(0, 400, 1500)), 4, 2, 64, 128, 64, 0.9,
+     False),                                                    # 1500 requests: scan > 1024
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
 def test_one_call_equals_the_separate_calls(case):
     lengths, Hq, Hkv, d, n, G, p, zq = case
-    say(f"[case] one call vs separate {case}")
+    lengths = [int(x) for x in lengths]
+    shown = lengths if len(lengths) <= 8 else f"{len(lengths)} requests"
+    say(f"[case] one call vs separate {shown} Hq={Hq} Hkv={Hkv} d={d} n={n} G={G} p={p}")
     b = _batch(lengths, Hq, Hkv, d, n, G, seed=len(lengths) + G, zero_q=zq)
     gb = GpuBatch(b, H=64)
     a, c = _both(gb, p)
     kept = _assert_same(a, c)
-    say(f"[ok] {case}: {kept} of {b.T} tokens kept")
+    say(f"[ok] {shown}: {kept} of {b.T} tokens kept")
 
 
 @pytest.mark.timeout(600)
@@ -108,6 +117,25 @@ def test_one_call_with_inconsistent_device_cu_writes_nothing():
     assert bool((dec.hidden_out == 3.0).all())
 
 
+def test_one_call_with_inconsistent_device_cu_writes_nothing_several_requests():
+    """As above for a pack of three requests (the fused finalize path): the second call's
+    device cu_seqlens disagrees with the host copy, so it raises error bit 1, writes
+    cu_seqlens_out = 0 and moves no row."""
+    b = _batch([3000, 5000, 200], 8, 2, 64, 128, 64, seed=4)
+    gb = GpuBatch(b, H=64)
+    dec = up.LayerDecision(gb.qwin, gb.k, gb.cu, gb.cu_h, gb.hidden, gb.pos, b.n, b.G, 0.9)
+    dec.run()
+    torch.cuda.synchronize()
+    assert up.device_error() == 0 and int(dec.cu_out[-1].item()) > 0
+    dec.cu.copy_(torch.tensor([0, 3000, 7900, 8200], dtype=torch.int32))
+    dec.hidden_out.fill_(3.0)
+    dec.run()
+    torch.cuda.synchronize()
+    assert up.device_error() & 1
+    assert dec.cu_out.cpu().numpy().tolist() == [0, 0, 0, 0]
+    assert bool((dec.hidden_out == 3.0).all())
+
+
 def _fused_launches(gb, p):
     """Launches of the fused select kernel in one up_layer_decision call."""
     b = gb.b
@@ -124,10 +152,11 @@ def _fused_launches(gb, p):
 
 
 def test_fused_select_path():
-    """One request of at most 4096 blocks: up_layer_decision normalises the block
+    """Requests of at most 4096 blocks each: up_layer_decision normalises the block
     masses and assigns the compaction's block destinations inside the select kernel
-    (one launch instead of three); every output is bit-identical to the separate
-    calls (see test_one_call_equals_the_separate_calls for the case list)."""
+    (one launch instead of three for one request, two instead of four for several);
+    every output is bit-identical to the separate calls (see
+    test_one_call_equals_the_separate_calls for the case list)."""
     b = _batch([4096], 8, 2, 64, 128, 64, seed=5)
     gb = GpuBatch(b, H=64)
     assert _fused_launches(gb, 0.99) == 1
@@ -135,6 +164,13 @@ def test_fused_select_path():
     assert _fused_launches(GpuBatch(big, H=64), 0.95) == 0
     a, c = _both(gb, 0.99)
     _assert_same(a, c)
+    # several requests of at most 4096 blocks each: the fused path too
+    many = GpuBatch(_batch([3000, 0, 262144, 64], 8, 2, 64, 128, 64, seed=7), H=64)
+    assert _fused_launches(many, 0.95) == 1
+    a, c = _both(many, 0.95)
+    _assert_same(a, c)
+    mixed = _batch([3000, 262208, 64], 8, 2, 64, 128, 64, seed=8)   # one of 4097 blocks
+    assert _fused_launches(GpuBatch(mixed, H=64), 0.95) == 0
 
 
 @pytest.mark.timeout(600)
