@@ -746,45 +746,57 @@ __device__ __forceinline__ int request_of_row(const ReqPlan* __restrict__ plan, 
 }
 
 // Workgroup = 64 rows (one per lane) x 16 waves; wave w merges chunks w, w+16, ...
-// of its lane's row, wave 0 merges the 16 partial results in wave order, then wave w
-// writes the weights of the same chunks.
+// of its lane's row in that order, wave 0 merges the 16 partial results in wave order,
+// then wave w writes the weights of the same chunks.  The row's plan entry is read
+// while the header's flag is in flight (a lone request needs no search; every index
+// stays inside the plan) and used only once the flag says the plan is valid; a wave
+// issues up to four chunks' loads at once and keeps its first four for the weights.
 __global__ __launch_bounds__(1024) void up_row_stats_kernel(
     const WsHeader* __restrict__ hdr, const ReqPlan* __restrict__ plan, int B, int Hq, int Hkv,
     const float2* __restrict__ cs, const int32_t* __restrict__ crb, float2* __restrict__ rs,
     float* __restrict__ wt, int64_t total_rows, float* __restrict__ row_lse) {
   __shared__ float2 part[16][64];
-  if (hdr->valid != 1) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t x = (int64_t)blockIdx.x * 64 + lane;
+  const int valid = hdr->valid;
+  int i = B;
+  ReqPlan pr{};
+  if (B == 1) {
+    pr = plan[0];
+    i = x < total_rows ? 0 : 1;
+  } else if (x < total_rows) {
+    i = request_of_row(plan, B, Hq, x);
+    if (i < B) pr = plan[i];
+  }
+  if (valid != 1) return;
   float M = kNegInf, S = 0.f;
   int64_t lse_at = -1;   // the row's index in the [sum W, Hq] window-row layout
   int64_t c0 = -1;       // the row's pair of chunk 0; chunk chk at c0 + chk * cstep
   int64_t cstep = 0;
   int nch = 0;
-  if (x < total_rows) {
-    const int i = request_of_row(plan, B, Hq, x);
-    if (i < B) {
-      const ReqPlan pr = plan[i];
-      const int gs = Hq / Hkv;
-      const int R = gs * pr.W;
-      const int64_t local = x - (int64_t)pr.win_off * Hq;   // = g*R + r
-      const int g = (int)(local / R), r = (int)(local % R);
-      lse_at = (int64_t)(pr.win_off + r / gs) * Hq + g * gs + r % gs;
-      c0 = pr.cs_off + (int64_t)g * R + r;
-      cstep = (int64_t)Hkv * R;
-      nch = pr.nch;
-      // chunks wave, wave + 16, ... in order; four loads in flight
-      int chk = wave;
-      for (; chk + 48 < nch; chk += 64) {
-        float2 v[4];
+  float rc0[4];          // the reference and rebase mark of chunks wave + 16 q
+  int fc0[4];
+  if (i < B) {
+    const int gs = Hq / Hkv;
+    const int R = gs * pr.W;
+    const int64_t local = x - (int64_t)pr.win_off * Hq;   // = g*R + r
+    const int g = (int)(local / R), r = (int)(local % R);
+    lse_at = (int64_t)(pr.win_off + r / gs) * Hq + g * gs + r % gs;
+    c0 = pr.cs_off + (int64_t)g * R + r;
+    cstep = (int64_t)Hkv * R;
+    nch = pr.nch;
+    for (int base = wave; base < nch; base += 64) {
+      float2 v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = cs[c0 + (chk + 16 * q) * cstep];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) merge_ml(M, S, v[q].x, v[q].y);
+      for (int q = 0; q < 4; ++q) {
+        const int chk = base + 16 * q;
+        v[q] = chk < nch ? cs[c0 + chk * cstep] : make_float2(kNegInf, 0.f);
+        if (base == wave) fc0[q] = chk < nch ? crb[c0 + chk * cstep] : 0;
       }
-      for (; chk < nch; chk += 16) {
-        const float2 v = cs[c0 + chk * cstep];
-        merge_ml(M, S, v.x, v.y);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (base + 16 * q < nch) merge_ml(M, S, v[q].x, v[q].y);
+        if (base == wave) rc0[q] = v[q].x;
       }
     }
   }
@@ -805,21 +817,14 @@ __global__ __launch_bounds__(1024) void up_row_stats_kernel(
     auto weight = [&](int fc, float rc) {
       return fc > 0 ? -1.f - (float)fc : fast_exp2(rc - st.x) * st.y;
     };
-    int chk = wave;
-    for (; chk + 48 < nch; chk += 64) {
-      int fc[4];
-      float rc[4];
+    for (int base = wave; base < nch; base += 64) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        fc[q] = crb[c0 + (chk + 16 * q) * cstep];
-        rc[q] = cs[c0 + (chk + 16 * q) * cstep].x;
+        const int64_t chk = base + 16 * q;
+        if (chk >= nch) continue;
+        const int64_t ci = c0 + chk * cstep;
+        wt[ci] = base == wave ? weight(fc0[q], rc0[q]) : weight(crb[ci], cs[ci].x);
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) wt[c0 + (chk + 16 * q) * cstep] = weight(fc[q], rc[q]);
-    }
-    for (; chk < nch; chk += 16) {
-      const int64_t ci = c0 + chk * cstep;
-      wt[ci] = weight(crb[ci], cs[ci].x);
     }
   }
 }
@@ -859,11 +864,15 @@ __global__ __launch_bounds__(256) void up_block_mass_kernel(
     const float* __restrict__ lb, const float* __restrict__ mref, const float* __restrict__ wt,
     const float2* __restrict__ cs, const float2* __restrict__ rs, double* __restrict__ mass) {
   __shared__ double red[4];
-  if (hdr->valid != 1) return;
   const int64_t blk = blockIdx.x;
-  const int i = request_of_block(plan, B, blk);
-  if (i >= B) return;
-  const ReqPlan pr = plan[i];
+  // The plan entry is read while the header's flag is in flight (a lone request needs no
+  // search; every index stays inside the plan) and used only once the flag says the
+  // plan is valid.
+  const int valid = hdr->valid;
+  const int i = B == 1 ? 0 : request_of_block(plan, B, blk);
+  ReqPlan pr{};
+  if (i < B) pr = plan[i];
+  if (valid != 1 || i >= B) return;
   const int64_t b = blk - pr.blk_off;
   const int64_t c = b / pr.cbs;                    // the block's statistics chunk
   const int j = (int)(b - c * pr.cbs);             // its index within the chunk
