@@ -76,11 +76,12 @@ __global__ __launch_bounds__(kPlanThreads) void up_score_plan_kernel(
   constexpr int NW = kPlanThreads / 64;
   constexpr int NV = 6;   // scanned quantities: W, nb, items, ml, cs, pm
   __shared__ int64_t wtot[NV][NW];
-  __shared__ int bad;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gs = s.Hq / s.Hkv;
-  if (tid == 0) bad = cu[0] != 0;
-  __syncthreads();
+  // Every check is one workgroup vote at the end, so the first and last entries of
+  // cu_seqlens are read together with the requests' own.
+  bool bad = tid == 0 && cu[0] != 0;
+  const int32_t cu_end = tid == 0 ? cu[s.B] : 0;
   int64_t carry[NV] = {0, 0, 0, 0, 0, 0};
   for (int base = 0; base < s.B; base += kPlanThreads) {
     const int i = base + tid;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kPlanThreads) void up_score_plan_kernel(
     if (i < s.B) {
       const int32_t a = cu[i], b = cu[i + 1];
       int64_t L = (int64_t)b - a;
-      if (L < 0) { atomicOr(&bad, 1); L = 0; }
+      if (L < 0) { bad = true; L = 0; }
       const int64_t W = L < s.n ? L : s.n;
       const int64_t nb = (L + s.G - 1) / s.G;
       const int64_t R = gs * W;
@@ -138,9 +139,9 @@ __global__ __launch_bounds__(kPlanThreads) void up_score_plan_kernel(
 #pragma unroll
     for (int q = 0; q < NV; ++q) carry[q] += tot[q];
   }
-  __syncthreads();
+  const int any_bad = __syncthreads_or(bad ? 1 : 0);
   if (tid == 0) {
-    const bool ok = !bad && (int64_t)cu[s.B] == host.T && carry[0] == host.win_rows &&
+    const bool ok = !any_bad && (int64_t)cu_end == host.T && carry[0] == host.win_rows &&
                     carry[1] == host.nb_tot && carry[2] == host.items &&
                     carry[3] == host.ml_pairs && carry[4] == host.cs_pairs &&
                     carry[5] == host.pm_parts;
