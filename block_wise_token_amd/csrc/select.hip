@@ -234,13 +234,16 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, Lds& S) {
 // PER slots per thread (the launch takes the fewest that hold the request: every phase
 // loops over the slots, so empty ones cost time).
 //
-// FUSED (one request, NT = 256): the kernel also does the normalisation and the
-// block destinations of the compaction, so the decision needs neither the normalise
-// nor the block-destination launch.  It reads the float64 block masses, sums them in
-// the order the normalise kernel uses (per thread over blocks tid, tid + 256, ...,
-// then the lanes by butterfly, then the four waves in order) so the float32 scores it
-// writes are bit-identical, selects on them, and writes each block's destination row,
-// source row and length with the compaction header's valid flag.
+// FUSED (NT = 256, requests of at most 4096 blocks): the kernel also does the
+// normalisation and the block destinations of the compaction, so the decision needs
+// neither the normalise nor the block-destination launch.  It reads the float64 block
+// masses, sums them in the order the normalise kernel uses (per thread over blocks tid,
+// tid + 256, ..., then the lanes by butterfly, then the four waves in order) so the
+// float32 scores it writes are bit-identical, selects on them, and writes each block's
+// destination row, source row and length.  One request (direct): absolute
+// destinations and the compaction header's valid flag.  Several: destinations relative
+// to the request's first output row, each block's request index and the kept count
+// (-1 when a check failed); up_select_finalize_fused_kernel completes them.
 template <int NT, int PER, bool FUSED>
 __global__ __launch_bounds__(NT) void up_select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ cu, int B, int n, int G,
