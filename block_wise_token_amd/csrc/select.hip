@@ -724,46 +724,62 @@ __global__ __launch_bounds__(1024) void up_select_finalize_kernel(int32_t* __res
 __global__ __launch_bounds__(1024) void up_select_finalize_fused_kernel(
     int32_t* __restrict__ cu_out, int B, int64_t T_host, int64_t nb_tot_host, int* __restrict__ err,
     FusedDecision fd) {
-  __shared__ int64_t buf[1024];
-  __shared__ int64_t carry;
-  __shared__ int bad;
+  constexpr int kOffs = 4096;   // request offsets kept in LDS for packs below this size
+  struct FinLds {
+    uint64_t wtot64[16];
+  };
+  __shared__ FinLds S;
+  __shared__ int32_t offs[kOffs];
   const int tid = threadIdx.x;
+  const bool lds_offs = B < kOffs;
   if (tid == 0) {
-    carry = 0;
-    bad = 0;
     cu_out[0] = 0;   // request 0's first output row (read below)
+    if (lds_offs) offs[0] = 0;
   }
-  __syncthreads();
+  // Counts 1024 at a time: wave scans, then the lower waves' totals.
+  bool bad_c = false;
+  int64_t carry = 0;   // the same in every thread
   for (int base = 0; base < B; base += 1024) {
     const int idx = base + tid;
     const int64_t c = idx < B ? cu_out[idx + 1] : 0;
-    if (c < 0) atomicOr(&bad, 1);
-    buf[tid] = c < 0 ? 0 : c;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-      const int64_t v = tid >= d ? buf[tid - d] : 0;
-      __syncthreads();
-      buf[tid] += v;
-      __syncthreads();
+    if (c < 0) bad_c = true;
+    const uint64_t inc = block_scan_u64<16>((uint64_t)(c < 0 ? 0 : c), S);
+    if (idx < B) {
+      const int32_t o = (int32_t)(carry + (int64_t)inc);
+      cu_out[idx + 1] = o;
+      if (lds_offs) offs[idx + 1] = o;
     }
-    if (idx < B) cu_out[idx + 1] = (int32_t)(carry + buf[tid]);
-    __syncthreads();
-    if (tid == 1023) carry += buf[1023];
-    __syncthreads();
+    uint64_t round = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) round += S.wtot64[w];
+    carry += (int64_t)round;
+    __syncthreads();   // the next round rewrites S
   }
   const int64_t total = carry;
-  const bool ok_counts = !bad && total <= T_host;
-  // Absolute destinations; a run must fit inside the kept count.
+  const bool ok_counts = !__syncthreads_or(bad_c ? 1 : 0) && total <= T_host;
+  // Absolute destinations; a run must fit inside the kept count.  A thread takes four
+  // blocks at a time, their loads issued together.
   bool run_bad = false;
   if (ok_counts) {
-    for (int64_t b = tid; b < nb_tot_host; b += 1024) {
-      const int32_t d = fd.dst[b];
-      if (d < 0) continue;
-      const int r = fd.rq[b];
-      if (r < 0 || r >= B) { run_bad = true; continue; }
-      const int64_t ad = (int64_t)cu_out[r] + d;
-      if (ad + fd.len[b] > total) run_bad = true;
-      fd.dst[b] = (int32_t)ad;
+    constexpr int U = 4;
+    for (int64_t b0 = tid; b0 < nb_tot_host; b0 += U * 1024) {
+      int32_t d[U], r[U], ln[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t b = b0 + (int64_t)u * 1024;
+        const bool in = b < nb_tot_host;
+        d[u] = in ? fd.dst[b] : -1;
+        r[u] = in ? fd.rq[b] : 0;
+        ln[u] = in ? fd.len[b] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (d[u] < 0) continue;
+        if (r[u] < 0 || r[u] >= B) { run_bad = true; continue; }
+        const int64_t ad = (int64_t)(lds_offs ? offs[r[u]] : cu_out[r[u]]) + d[u];
+        if (ad + ln[u] > total) run_bad = true;
+        fd.dst[b0 + (int64_t)u * 1024] = (int32_t)ad;
+      }
     }
   }
   const int any = __syncthreads_or(run_bad ? 1 : 0);
