@@ -693,25 +693,24 @@ __global__ __launch_bounds__(kSmallSelBlocks) void up_select_small_kernel(
 // In-place inclusive scan of the per-request kept counts in cu_out[1..B]; cu_out[0] = 0.
 __global__ __launch_bounds__(1024) void up_select_finalize_kernel(int32_t* __restrict__ cu_out,
                                                                   int B) {
-  __shared__ int64_t buf[1024];
-  __shared__ int64_t carry;
+  struct FinLds {
+    uint64_t wtot64[16];
+  };
+  __shared__ FinLds S;
   const int tid = threadIdx.x;
-  if (tid == 0) { carry = 0; cu_out[0] = 0; }
-  __syncthreads();
+  if (tid == 0) cu_out[0] = 0;
+  // Counts 1024 at a time: wave scans, then the lower waves' totals.
+  int64_t carry = 0;   // the same in every thread
   for (int base = 0; base < B; base += 1024) {
     const int idx = base + tid;
-    buf[tid] = idx < B ? cu_out[idx + 1] : 0;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-      const int64_t v = tid >= d ? buf[tid - d] : 0;
-      __syncthreads();
-      buf[tid] += v;
-      __syncthreads();
-    }
-    if (idx < B) cu_out[idx + 1] = (int32_t)(carry + buf[tid]);
-    __syncthreads();
-    if (tid == 1023) carry += buf[1023];
-    __syncthreads();
+    const int64_t c = idx < B ? cu_out[idx + 1] : 0;
+    const uint64_t inc = block_scan_u64<16>((uint64_t)c, S);
+    if (idx < B) cu_out[idx + 1] = (int32_t)(carry + (int64_t)inc);
+    uint64_t round = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) round += S.wtot64[w];
+    carry += (int64_t)round;
+    __syncthreads();   // the next round rewrites S
   }
 }
 
